@@ -1,0 +1,146 @@
+"""fp64 CPU oracle for the Mamba-1 selective scan and the single-token update.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
+and the CPU-baseline leg of ``bench.py``.  The GPU library never imports,
+links or calls anything here, and this package imports nothing from it.
+
+The arithmetic lives in ``oracle.c`` (plain C, fp64, libm's exp/expm1/log1p,
+no fast-math).  This module only marshals numpy arrays to it; every input is
+first up-converted to float64, which is exact for the bf16 and fp32 values
+the GPU sees.
+
+Pages followed (titles and sections; each step is cited in ``oracle.c``):
+  "Mamba 模型" (gaos6e.github.io) -- the full-step flowchart, nodes H to M;
+  "Mamba 与状态空间模型" (world.lapla.si, plate F56) -- sections 03, 06, 07;
+  "Mamba 状态空间模型架构深度解析" (pnsm.cn) -- ZOH, diagonal A;
+  "Mamba模型：高效序列建模的新突破" (mhpn.cn) -- section 3.1, ZOH B-bar.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+DISCRETIZATIONS = {"zoh": 0, "delta_b": 1}
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc -O2 (no fast-math) into liboracle.so."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math",
+               "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm", "-lpthread"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build(force=True)
+            lib = ctypes.CDLL(_LIB)
+            dp = ctypes.POINTER(ctypes.c_double)
+            i64 = ctypes.c_int64
+            lib.oracle_scan.argtypes = [i64, i64, i64, i64] + [dp] * 9 + [ctypes.c_int, dp, dp, ctypes.c_int]
+            lib.oracle_scan.restype = ctypes.c_int
+            lib.oracle_state_update.argtypes = [i64, i64, i64, dp] + [dp] * 8 + [ctypes.c_int, dp, ctypes.c_int]
+            lib.oracle_state_update.restype = ctypes.c_int
+            lib.oracle_softplus.argtypes = [ctypes.c_double]
+            lib.oracle_softplus.restype = ctypes.c_double
+            _lib = lib
+    return _lib
+
+
+def default_threads() -> int:
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit() and int(env) > 0:
+        return int(env)
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _f64(a, shape=None):
+    if a is None:
+        return None
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+    if shape is not None and a.shape != tuple(shape):
+        raise ValueError("expected shape %s, got %s" % (tuple(shape), a.shape))
+    return a
+
+
+def _ptr(a):
+    if a is None:
+        return ctypes.POINTER(ctypes.c_double)()
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def softplus(x: float) -> float:
+    return _load().oracle_softplus(float(x))
+
+
+def scan(u, delta_raw, z, Bt, Ct, A, Dskip=None, delta_bias=None, h0=None,
+         discretization: str = "zoh", nthreads: int | None = None):
+    """Selective scan over (B, D, L).  Returns (y (B,D,L), final_state (B,D,N)), float64."""
+    u = _f64(u)
+    if u.ndim != 3:
+        raise ValueError("u must be (B, D, L)")
+    B, D, L = u.shape
+    Bt = _f64(Bt)
+    if Bt.ndim != 3 or Bt.shape[0] != B or Bt.shape[2] != L:
+        raise ValueError("Bt must be (B, N, L)")
+    N = Bt.shape[1]
+    delta_raw = _f64(delta_raw, (B, D, L))
+    z = _f64(z, (B, D, L))
+    Ct = _f64(Ct, (B, N, L))
+    A = _f64(A, (D, N))
+    Dskip = _f64(Dskip, (D,))
+    delta_bias = _f64(delta_bias, (D,))
+    h0 = _f64(h0, (B, D, N))
+    y = np.empty((B, D, L), dtype=np.float64)
+    hN = np.empty((B, D, N), dtype=np.float64)
+    rc = _load().oracle_scan(B, D, N, L, _ptr(u), _ptr(delta_raw), _ptr(z), _ptr(Bt), _ptr(Ct),
+                             _ptr(A), _ptr(Dskip), _ptr(delta_bias), _ptr(h0),
+                             DISCRETIZATIONS[discretization], _ptr(y), _ptr(hN),
+                             nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError("oracle_scan failed with %d" % rc)
+    return y, hN
+
+
+def state_update(state, u, delta_raw, z, Bt, Ct, A, Dskip=None, delta_bias=None,
+                 discretization: str = "zoh", nthreads: int | None = None):
+    """One decoding step.  state (B,D,N); u, delta_raw, z (B,D); Bt, Ct (B,N).
+
+    Returns (y (B,D), new_state (B,D,N)) as float64; the input is not modified.
+    """
+    st = np.array(state, dtype=np.float64, copy=True, order="C")
+    if st.ndim != 3:
+        raise ValueError("state must be (B, D, N)")
+    B, D, N = st.shape
+    u = _f64(u, (B, D))
+    delta_raw = _f64(delta_raw, (B, D))
+    z = _f64(z, (B, D))
+    Bt = _f64(Bt, (B, N))
+    Ct = _f64(Ct, (B, N))
+    A = _f64(A, (D, N))
+    Dskip = _f64(Dskip, (D,))
+    delta_bias = _f64(delta_bias, (D,))
+    y = np.empty((B, D), dtype=np.float64)
+    rc = _load().oracle_state_update(B, D, N, _ptr(st), _ptr(u), _ptr(delta_raw), _ptr(z),
+                                     _ptr(Bt), _ptr(Ct), _ptr(A), _ptr(Dskip), _ptr(delta_bias),
+                                     DISCRETIZATIONS[discretization], _ptr(y),
+                                     nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError("oracle_state_update failed with %d" % rc)
+    return y, st

@@ -1,0 +1,178 @@
+/*
+ * oracle.c -- plain fp64 CPU reference for the Mamba-1 selective scan (S6)
+ * forward and the single-token state update.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark load this library.  The GPU path shares no
+ * code, header, table or helper with it.
+ *
+ * What it computes, step by step, with the passage each step follows:
+ *
+ *   Pages cited:
+ *     [P1] "Mamba 模型" (gaos6e.github.io, AI-Agent-Engineer notes):
+ *          the full-step flowchart (nodes H to M) and its step notes.
+ *     [P3] "Mamba 与状态空间模型" (world.lapla.si, plate F56):
+ *          sections 03, 06 and 07.
+ *     [P4] "Mamba 状态空间模型架构深度解析：从 S4 到 Mamba-3" (pnsm.cn):
+ *          "状态空间模型（SSM）基础" (ZOH) and "Mamba-1：选择性状态空间"
+ *          (diagonal A, one independent SSM per channel).
+ *     [P5] "Mamba模型：高效序列建模的新突破" (mhpn.cn), section 3.1:
+ *          the zero-order-hold formulas for A-bar and B-bar.
+ *
+ *   For every channel (b, d) independently ([P4] diagonal A):
+ *     h(-1) = h0[b,d,:]  (zero for a fresh scan)
+ *     for l = 0 .. L-1:
+ *       delta  = softplus(delta_raw[b,d,l] + bias[d])          [P1] node H
+ *       for n = 0 .. N-1:
+ *         Abar = exp(delta * A[d,n])                            [P1] node I, [P5] 3.1
+ *         Bbar = (Abar - 1) / A[d,n] * B[b,n,l]   (ZOH)         [P5] 3.1, [P4]
+ *                (limit delta * B[b,n,l] when A[d,n] == 0)
+ *              or delta * B[b,n,l]                (simplified)  [P3] "模型省略了什么"
+ *         h[n] = Abar * h[n] + Bbar * u[b,d,l]                  [P1] node J
+ *       y = sum_n C[b,n,l] * h[n] + Dskip[d] * u[b,d,l]         [P1] node K
+ *       y = y * z * sigmoid(z)          (skipped when z is NULL) [P1] nodes L, M
+ *     final_state[b,d,:] = h
+ *
+ *   Readings where the pages leave a point open (each is listed in the design
+ *   notes): the bias is added before softplus; the readout uses the updated
+ *   state h_t; the D-term is inside the gate; B_t and C_t are shared by all D
+ *   channels of a batch row; softplus is the exact function with no
+ *   threshold, evaluated as max(x,0) + log1p(exp(-|x|)).
+ *
+ * Layout: all arrays are dense row-major float64.
+ *   u, delta_raw, z : (B, D, L)      Bt, Ct : (B, N, L)
+ *   A : (D, N)      Dskip, bias : (D)      h0, final_state : (B, D, N)
+ *   y : (B, D, L)
+ *
+ * Threads split the channel list only; each channel's time loop is sequential.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+enum { ORACLE_ZOH = 0, ORACLE_DELTA_B = 1 };
+
+/* softplus(x) = log(1 + e^x), written so that neither branch overflows. */
+double oracle_softplus(double x) { return fmax(x, 0.0) + log1p(exp(-fabs(x))); }
+
+/* z * sigmoid(z), written as z / (1 + e^-z): e^-z may overflow to +inf for very
+ * negative z, and the quotient then goes to -0, which is the right limit. */
+static double silu(double z) { return z / (1.0 + exp(-z)); }
+
+/* Input coefficient multiplying B * u for one (delta, a) pair. */
+static double bbar_coef(double delta, double a, int mode) {
+  if (mode == ORACLE_DELTA_B) return delta;
+  if (a == 0.0) return delta;           /* lim_{a->0} (e^{delta a} - 1)/a */
+  return expm1(delta * a) / a;          /* (Abar - 1)/a, with no cancellation */
+}
+
+typedef struct {
+  int64_t B, D, N, L;
+  const double *u, *delta_raw, *z, *Bt, *Ct, *A, *Dskip, *bias, *h0;
+  int mode;
+  double *y, *final_state;
+  int64_t ch_begin, ch_end; /* range of flattened channel ids b*D + d */
+} job_t;
+
+static void scan_one_channel(const job_t* j, int64_t ch, double* h) {
+  const int64_t b = ch / j->D, d = ch % j->D;
+  const int64_t N = j->N, L = j->L;
+  const double* u = j->u + ch * L;
+  const double* dr = j->delta_raw + ch * L;
+  const double* z = j->z ? j->z + ch * L : NULL;
+  const double* Bb = j->Bt + b * N * L;
+  const double* Cb = j->Ct + b * N * L;
+  const double* Ad = j->A + d * N;
+  const double Dd = j->Dskip ? j->Dskip[d] : 0.0;
+  const double bias = j->bias ? j->bias[d] : 0.0;
+  double* y = j->y + ch * L;
+
+  for (int64_t n = 0; n < N; ++n) h[n] = j->h0 ? j->h0[ch * N + n] : 0.0;
+
+  for (int64_t l = 0; l < L; ++l) {
+    const double delta = oracle_softplus(dr[l] + bias);
+    const double x = u[l];
+    double acc = 0.0;
+    for (int64_t n = 0; n < N; ++n) {
+      const double a = Ad[n];
+      const double abar = exp(delta * a);
+      const double bbar = bbar_coef(delta, a, j->mode) * Bb[n * L + l];
+      h[n] = abar * h[n] + bbar * x;
+      acc += Cb[n * L + l] * h[n];
+    }
+    double out = acc + Dd * x;
+    if (z) out *= silu(z[l]);
+    y[l] = out;
+  }
+  if (j->final_state)
+    for (int64_t n = 0; n < N; ++n) j->final_state[ch * N + n] = h[n];
+}
+
+static void* run_job(void* arg) {
+  const job_t* j = (const job_t*)arg;
+  double* h = (double*)malloc(sizeof(double) * (size_t)(j->N > 0 ? j->N : 1));
+  if (!h) return (void*)1;
+  for (int64_t ch = j->ch_begin; ch < j->ch_end; ++ch) scan_one_channel(j, ch, h);
+  free(h);
+  return NULL;
+}
+
+/* Returns 0 on success, -1 on bad arguments, -2 on allocation/thread failure. */
+int oracle_scan(int64_t B, int64_t D, int64_t N, int64_t L,
+                const double* u, const double* delta_raw, const double* z,
+                const double* Bt, const double* Ct, const double* A,
+                const double* Dskip, const double* bias, const double* h0,
+                int mode, double* y, double* final_state, int nthreads) {
+  if (B < 0 || D < 0 || N < 0 || L < 0) return -1;
+  if (!u || !delta_raw || !Bt || !Ct || !A || !y) return -1;
+  if (mode != ORACLE_ZOH && mode != ORACLE_DELTA_B) return -1;
+  const int64_t nch = B * D;
+  if (nch == 0) return 0;
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > nch) nthreads = (int)nch;
+
+  job_t* jobs = (job_t*)calloc((size_t)nthreads, sizeof(job_t));
+  pthread_t* tids = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+  if (!jobs || !tids) { free(jobs); free(tids); return -2; }
+  int rc = 0, started = 0;
+  for (int t = 0; t < nthreads; ++t) {
+    job_t* j = &jobs[t];
+    j->B = B; j->D = D; j->N = N; j->L = L;
+    j->u = u; j->delta_raw = delta_raw; j->z = z; j->Bt = Bt; j->Ct = Ct;
+    j->A = A; j->Dskip = Dskip; j->bias = bias; j->h0 = h0; j->mode = mode;
+    j->y = y; j->final_state = final_state;
+    j->ch_begin = nch * t / nthreads;
+    j->ch_end = nch * (t + 1) / nthreads;
+  }
+  if (nthreads == 1) {
+    if (run_job(&jobs[0])) rc = -2;
+  } else {
+    for (int t = 0; t < nthreads; ++t) {
+      if (pthread_create(&tids[t], NULL, run_job, &jobs[t]) != 0) { rc = -2; break; }
+      ++started;
+    }
+    for (int t = 0; t < started; ++t) {
+      void* ret = NULL;
+      pthread_join(tids[t], &ret);
+      if (ret) rc = -2;
+    }
+  }
+  free(jobs);
+  free(tids);
+  return rc;
+}
+
+/* One decoding step: the scan above with L = 1, starting from `state`
+ * ([P1] "为什么 Mamba 推理更省": state <- update(state, x_t)).  `state` is
+ * updated in place; inputs are (B, D) / (B, N). */
+int oracle_state_update(int64_t B, int64_t D, int64_t N, double* state,
+                        const double* u, const double* delta_raw, const double* z,
+                        const double* Bt, const double* Ct, const double* A,
+                        const double* Dskip, const double* bias, int mode,
+                        double* y, int nthreads) {
+  if (!state) return -1;
+  return oracle_scan(B, D, N, 1, u, delta_raw, z, Bt, Ct, A, Dskip, bias,
+                     state, mode, y, state, nthreads);
+}
