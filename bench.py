@@ -1,0 +1,276 @@
+"""Benchmark of the MI355X selective scan (one GPU).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Default workload: the Mamba-2.8B-shaped layer scan, B=4 D=5120 N=16 L=2048,
+bf16 inputs/outputs, fp32 state and arithmetic, final state returned.  A
+step is one call of mamba_scan_fwd over one batch (inputs resident in HBM;
+two input sets alternate so the 256 MB last-level cache cannot hold a step's
+inputs from the previous step).  Prints one JSON line.
+
+Other workloads: --workload long_b1 (B=1 D=4096 L=131072, chunked along L),
+mamba130m_layer, tiny_fp32, decode48 (48 layers x 128 steps of
+mamba_state_update at B=128 D=4096, the 48-layer step replayed as a graph).
+
+--copy-calibration runs only a plain device copy of known size (used to
+scale rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "scan HBM GB/s (% of MI355X peak) + B·D·L elems/s at Mamba-2.8B layer shape"
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, AMD published
+CUS, SIMDS_PER_CU, LANES_PER_SIMD, CLOCK_GHZ = 256, 4, 16, 2.4
+# fp32 VALU lane-operations per second without packed math: 256 x 4 x 16 x 2.4e9
+VALU_PEAK_TOPS = CUS * SIMDS_PER_CU * LANES_PER_SIMD * CLOCK_GHZ / 1e3
+# Algorithmic fp32 operations of one ZOH state update (delta*A, exp, (e-1)/A,
+# B*u, *coef, e*h + input, C*h accumulate): 6 VALU + 1 transcendental; the
+# transcendental occupies the VALU issue slot it is issued in.
+OPS_PER_UPDATE = 7
+MEASURED_TRANS_SLOTS = None     # filled from the rate probe, see DESIGN
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def to_dev(a, dev):
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+    return torch.from_numpy(a.astype(np.float32, copy=False)).to(dev)
+
+
+def cpu_threads():
+    env = os.environ.get("OMP_NUM_THREADS")
+    n = int(env) if env and env.isdigit() and int(env) > 0 else (os.cpu_count() or 1)
+    return max(1, min(16, n))
+
+
+# ----------------------------------------------------------------------------- CPU oracle baseline
+def cpu_baseline_scan(cfg, x, seconds: float):
+    """Time the fp64 oracle (as it stands) on whole channels of the same workload."""
+    import oracle
+    from selective_state_space_75_amd import workloads as W
+    nth = cpu_threads()
+    f64 = lambda a: W.as_f32(a).astype(np.float64)  # noqa: E731
+
+    def run(nch):
+        b = 0
+        ds = list(range(nch))
+        args = (f64(x["u"][b:b + 1, ds]), f64(x["delta_raw"][b:b + 1, ds]), f64(x["z"][b:b + 1, ds]),
+                f64(x["Bt"][b:b + 1]), f64(x["Ct"][b:b + 1]), x["A"][ds].astype(np.float64),
+                x["Dskip"][ds].astype(np.float64), x["delta_bias"][ds].astype(np.float64))
+        t0 = time.perf_counter()
+        oracle.scan(*args, nthreads=nth)
+        return time.perf_counter() - t0
+
+    probe = min(cfg.D, 4 * nth)
+    t_probe = run(probe)
+    nch = int(min(cfg.D, max(probe, probe * seconds / max(t_probe, 1e-6))))
+    nch = max(nth, (nch // nth) * nth) if nch >= nth else nch
+    t = run(nch) if nch != probe else t_probe
+    frac = nch / float(cfg.B * cfg.D)
+    gbs = cfg.algorithmic_bytes() * frac / t / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": nth, "kind": "oracle",
+            "sample": "%d of %d channels (batch row 0, full L=%d, N=%d), fp64 C oracle, %.1f s wall; "
+                      "GB/s = the workload's algorithmic bytes x sampled fraction / time"
+                      % (nch, cfg.B * cfg.D, cfg.L, cfg.N, t),
+            "elems_per_s": round(cfg.elements * frac / t, 1)}
+
+
+# ----------------------------------------------------------------------------- scan benchmark
+def bench_scan(args, dev):
+    import torch
+    import selective_state_space_75_amd as m
+    from selective_state_space_75_amd import workloads as W
+    cfg = W.SCAN_CONFIGS[args.workload]
+    log("workload %s: B=%d D=%d N=%d L=%d %s" % (cfg.name, cfg.B, cfg.D, cfg.N, cfg.L, cfg.dtype))
+    x = W.scan_inputs(cfg)
+    sets = []
+    for k in range(args.sets):
+        if k == 0:
+            xs = x
+        else:
+            xs = W.scan_inputs(W.ScanConfig(cfg.name, cfg.B, cfg.D, cfg.N, cfg.L, cfg.dtype, cfg.seed + 100 * k,
+                                            cfg.dskip, cfg.final_state))
+        t = {k2: to_dev(xs[k2], dev) for k2 in ("u", "delta_raw", "z", "Bt", "Ct", "A", "Dskip", "delta_bias")}
+        sets.append(t)
+    odt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    ys = [torch.empty((cfg.B, cfg.D, cfg.L), dtype=odt, device=dev) for _ in sets]
+    hs = [torch.empty((cfg.B, cfg.D, cfg.N), dtype=torch.float32, device=dev) for _ in sets]
+    wsb = m.workspace_size(cfg.B, cfg.D, cfg.N, cfg.L)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        t = sets[i % len(sets)]
+        m.scan_fwd(t["u"], t["delta_raw"], t["z"], t["Bt"], t["Ct"], t["A"], t["Dskip"], t["delta_bias"],
+                   return_final_state=cfg.final_state, y=ys[i % len(sets)], final_state=hs[i % len(sets)],
+                   workspace=ws if wsb else None, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_launch_ms = [a.elapsed_time(b) for a, b in ev]
+    ms_step = wall * 1e3 / args.steps
+    kern_ms = float(np.mean(per_launch_ms))
+    nbytes = cfg.algorithmic_bytes()
+    gbs = nbytes / (ms_step * 1e-3) / 1e9
+    ops = cfg.updates * OPS_PER_UPDATE
+    achieved_tops = ops / (kern_ms * 1e-3) / 1e12
+    line = {
+        "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "io_dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": cfg.name, "B": cfg.B, "D": cfg.D, "N": cfg.N, "L": cfg.L,
+                   "final_state": cfg.final_state, "global_batch": cfg.B, "seq_len": cfg.L,
+                   "parallelism": "none (1 GPU)"},
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "elems_per_s": round(cfg.elements / (ms_step * 1e-3), 1),
+        "kernel_ms_mean": round(kern_ms, 5), "kernel_ms_min": round(float(np.min(per_launch_ms)), 5),
+        "algorithmic_bytes": nbytes,
+        "roofline": {"bound": "alu", "achieved": round(achieved_tops, 3), "peak": round(VALU_PEAK_TOPS, 2),
+                     "unit": "TOP/s", "frac": round(achieved_tops / VALU_PEAK_TOPS, 4), "traffic": None,
+                     "ops_per_update": OPS_PER_UPDATE, "updates_per_launch": cfg.updates,
+                     "hbm_achieved_gbs_kernel": round(nbytes / (kern_ms * 1e-3) / 1e9, 2)},
+    }
+    return line, cfg, x
+
+
+# ----------------------------------------------------------------------------- decode benchmark
+def bench_decode(args, dev):
+    import torch
+    import selective_state_space_75_amd as m
+    from selective_state_space_75_amd import workloads as W
+    cfg = W.DECODE_CONFIGS["decode48"]
+    log("decode48: %d layers x %d steps, B=%d D=%d N=%d" % (cfg.layers, cfg.steps, cfg.B, cfg.D, cfg.N))
+    layers = []
+    pool = 4   # distinct per-layer token inputs cycled over steps (inputs are ~4% of the bytes)
+    for l in range(cfg.layers):
+        A, Dskip, bias, st0 = W.decode_layer_params(cfg, l)
+        toks = []
+        for s in range(pool):
+            si = W.decode_step_inputs(cfg, l, s)
+            toks.append({k: to_dev(v, dev) for k, v in si.items()})
+        layers.append({"A": to_dev(A, dev), "Dskip": to_dev(Dskip, dev), "bias": to_dev(bias, dev),
+                       "state": to_dev(st0, dev), "toks": toks,
+                       "y": torch.empty((cfg.B, cfg.D), dtype=torch.bfloat16, device=dev)})
+        if l % 12 == 11:
+            log("  layer %d ready" % (l + 1))
+    stream = torch.cuda.Stream(dev)
+    graphs = []
+    torch.cuda.synchronize()
+    for s in range(pool):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for L_ in layers:
+                tk = L_["toks"][s]
+                m.state_update(L_["state"], tk["u"], tk["delta_raw"], tk["z"], tk["Bt"], tk["Ct"], L_["A"],
+                               L_["Dskip"], L_["bias"], y=L_["y"], stream=stream)
+        graphs.append(g)
+    # capture does not execute; restore the states it did not touch anyway
+    for i in range(args.warmup):
+        graphs[i % pool].replay()
+    torch.cuda.synchronize()
+    steps = cfg.steps
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(torch.cuda.current_stream(dev))
+    for s in range(steps):
+        graphs[s % pool].replay()
+    ev1.record(torch.cuda.current_stream(dev))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    per_ls = cfg.bytes_per_layer_step()
+    total = per_ls * cfg.layers * steps
+    gbs = total / (wall) / 1e9
+    kern_us = gpu_ms * 1e3 / (cfg.layers * steps)
+    line = {
+        "metric": "decode state-update HBM GB/s, 48 layers x 128 steps (B=128, D=4096, N=16)",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / steps, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "io_dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "decode48", "layers": cfg.layers, "steps": steps, "B": cfg.B, "D": cfg.D,
+                   "N": cfg.N, "order": "step-major, 48-layer step replayed as a HIP graph"},
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "tokens_per_s": round(cfg.B * steps / wall, 1),
+        "layer_step_us_mean": round(kern_us, 3),
+        "roofline": {"bound": "hbm", "achieved": round(per_ls / (kern_us * 1e-6) / 1e9, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(per_ls / (kern_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": None, "bytes_per_layer_step": per_ls},
+    }
+    return line
+
+
+def copy_calibration(args, dev):
+    import torch
+    n = args.copy_mb * (1 << 20) // 4
+    a = torch.randn(n, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(args.steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n * 4, "copy_calibration_bytes_written": n * 4,
+                      "launches": args.steps}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mamba2.8b_layer")
+    ap.add_argument("--sets", type=int, default=2, help="distinct input sets cycled over steps")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--copy-mb", type=int, default=1024)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        copy_calibration(args, dev)
+        return
+    if args.workload == "decode48":
+        line = bench_decode(args, dev)
+    else:
+        line, cfg, x = bench_scan(args, dev)
+        if not args.no_cpu_baseline:
+            log("cpu baseline (oracle) ...")
+            line["cpu_baseline"] = cpu_baseline_scan(cfg, x, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,143 @@
+/*
+ * mamba_scan.h -- C ABI of the MI355X (gfx950) Mamba-1 selective scan (S6)
+ * forward pass and the single-token selective state update.
+ *
+ * What the calls compute (pages cited by title and section):
+ *   "Mamba 模型" (gaos6e.github.io), full-step flowchart nodes H to M and
+ *     their step notes: delta = softplus(delta_raw + bias); Abar = exp(delta A);
+ *     Bbar from (delta, A, B); h_t = Abar h_{t-1} + Bbar u_t;
+ *     y_t = C_t h_t + D u_t; output gated by z * sigmoid(z).
+ *   "Mamba模型：高效序列建模的新突破" (mhpn.cn) section 3.1 and
+ *   "Mamba 状态空间模型架构深度解析" (pnsm.cn) "状态空间模型（SSM）基础":
+ *     zero-order hold, Abar = exp(delta A), Bbar = (Abar - 1) A^-1 B, with A
+ *     diagonal ("Mamba-1：选择性状态空间"), so per state n:
+ *     Bbar_n = (exp(delta A_n) - 1) / A_n * B_n  (limit delta * B_n at A_n = 0).
+ *   "Mamba 与状态空间模型" (world.lapla.si, plate F56), "模型省略了什么": the
+ *     simplified rule Bbar = delta * B, selectable with MAMBA_FLAG_DELTA_B.
+ *   Same page, section 07: the scan is fused -- inputs are read once from
+ *     HBM, discretisation and the recurrence stay on chip, only y (and the
+ *     final state, when asked for) is written back.  The (B, D, L, N) state
+ *     is never materialised.
+ *   "Mamba 模型", "为什么 Mamba 推理更省": decoding updates a fixed-size state
+ *     one token at a time (mamba_state_update).
+ *
+ * Conventions shared by every call
+ *   - Every pointer argument is a DEVICE pointer owned by the caller, to dense
+ *     row-major data on the device that `stream` belongs to.  The library keeps
+ *     no reference to any pointer after the call returns.
+ *   - The library allocates nothing.  The scan's scratch memory is the
+ *     caller's `workspace` (size from mamba_scan_workspace_size).
+ *   - All argument checks run on the host before any HIP call; a failed check
+ *     returns a negative mamba_status_t and launches nothing.
+ *   - Work is enqueued on `stream` and runs asynchronously; MAMBA_OK means the
+ *     launches were accepted.  A fault inside a kernel surfaces at the
+ *     caller's next synchronisation with the stream.
+ *   - Outputs must not alias inputs (except `state`, which is updated in
+ *     place by design).  Calls that share an output or a workspace must not
+ *     run concurrently.
+ *   - No C++ exception crosses this interface.  The library holds no mutable
+ *     global state; concurrent calls on different streams with disjoint
+ *     buffers are safe.
+ *   - Supported sizes: 1 <= N <= 16; B, D, L >= 1; B*D*L < 2^46.
+ *   - Arithmetic is fp32 throughout (state, discretisation, accumulation);
+ *     bf16 inputs are widened exactly, outputs are rounded to nearest-even.
+ */
+#ifndef MAMBA_SCAN_H_
+#define MAMBA_SCAN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MAMBA_F32 = 0,   /* IEEE binary32 */
+  MAMBA_BF16 = 1   /* bfloat16, stored as 16-bit patterns */
+} mamba_dtype_t;
+
+typedef enum {
+  MAMBA_OK = 0,
+  MAMBA_ERR_NULL = -1,          /* a required pointer is NULL */
+  MAMBA_ERR_SHAPE = -2,         /* a size is <= 0 or the problem is too large */
+  MAMBA_ERR_DTYPE = -3,         /* unknown dtype */
+  MAMBA_ERR_ALIGN = -4,         /* a pointer is not 16-byte aligned */
+  MAMBA_ERR_UNSUPPORTED = -5,   /* N > 16, or an unknown flag bit */
+  MAMBA_ERR_WORKSPACE = -6,     /* workspace NULL or smaller than required */
+  MAMBA_ERR_HIP = -7            /* a HIP launch or runtime call failed */
+} mamba_status_t;
+
+/* Flag bits (the `flags` argument of both calls). */
+#define MAMBA_FLAG_DELTA_B 0x1u          /* Bbar = delta * B instead of zero-order hold */
+#define MAMBA_FLAG_ACCURATE_EXPM1 0x2u   /* force the cancellation-free (Abar - 1) path;
+                                            always on when in_dtype is MAMBA_F32 */
+
+/*
+ * Bytes of device workspace mamba_scan_fwd needs for a problem of this shape.
+ * Depends only on the shape (no device query, callable without a GPU).
+ * Returns 0 when the shape is scanned in one pass per channel (no scratch),
+ * and (size_t)-1 for an invalid shape.
+ */
+size_t mamba_scan_workspace_size(int64_t B, int64_t D, int64_t N, int64_t L);
+
+/*
+ * Selective scan forward over a whole sequence.
+ *
+ *   u, delta, z : (B, D, L) in_dtype.  `delta` is the raw step before the bias
+ *                 and softplus.  z may be NULL: then no gate is applied.
+ *   Bt, Ct      : (B, N, L) in_dtype, one B_t / C_t per batch row and token,
+ *                 shared by all D channels.
+ *   A           : (D, N) fp32, the diagonal state matrix of each channel.
+ *   Dskip       : (D) fp32 or NULL (treated as zeros).
+ *   delta_bias  : (D) fp32 or NULL (treated as zeros); added before softplus.
+ *   y           : (B, D, L) out_dtype, written.
+ *   final_state : (B, D, N) fp32, written iff return_final_state != 0
+ *                 (must then be non-NULL; ignored otherwise).
+ *   workspace   : scratch of at least mamba_scan_workspace_size(B, D, N, L)
+ *                 bytes (may be NULL when that size is 0); contents on entry
+ *                 are ignored, contents on exit are unspecified.
+ *   flags       : MAMBA_FLAG_* bits.
+ *
+ * The initial state is zero.  Alignment: u, delta, z, Bt, Ct, y must be
+ * 16-byte aligned; A, Dskip, delta_bias and final_state 4-byte aligned.
+ */
+int mamba_scan_fwd(const void* u, const void* delta, const void* z,
+                   const void* Bt, const void* Ct, const float* A,
+                   const float* Dskip, const float* delta_bias,
+                   void* y, float* final_state,
+                   int64_t B, int64_t D, int64_t N, int64_t L,
+                   mamba_dtype_t in_dtype, mamba_dtype_t out_dtype,
+                   int return_final_state, unsigned flags,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * One decoding step for every (b, d): the scan above with L = 1, starting
+ * from `state` instead of zero.
+ *
+ *   state       : (B, D, N) fp32, read and overwritten in place with h_t.
+ *   u, delta, z : (B, D) in_dtype (z may be NULL: no gate).
+ *   Bt, Ct      : (B, N) in_dtype.
+ *   A           : (D, N) fp32.  Dskip, delta_bias : (D) fp32 or NULL.
+ *   y           : (B, D) out_dtype, written.
+ *
+ * Alignment: state, A 16-byte aligned; the rest 4-byte (fp32) or 2-byte
+ * (bf16) aligned.  No workspace is used.
+ */
+int mamba_state_update(float* state, const void* u, const void* delta, const void* z,
+                       const void* Bt, const void* Ct, const float* A,
+                       const float* Dskip, const float* delta_bias, void* y,
+                       int64_t B, int64_t D, int64_t N,
+                       mamba_dtype_t in_dtype, mamba_dtype_t out_dtype,
+                       unsigned flags, hipStream_t stream);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char* mamba_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MAMBA_SCAN_H_ */

@@ -1,0 +1,12 @@
+"""MI355X (gfx950) Mamba-1 selective scan (S6) forward and selective state update.
+
+The computation runs in hand-written HIP kernels inside ``libmamba_scan.so``
+(C ABI: ``include/mamba_scan.h``).  This package is the thin Python side:
+``scan_fwd`` / ``state_update`` marshal torch tensors to that library, and
+``workloads`` draws the seeded synthetic inputs.
+"""
+from ._lib import (FLAG_ACCURATE_EXPM1, FLAG_DELTA_B, MambaError, lib, scan_fwd,  # noqa: F401
+                   state_update, status_string, workspace_size)
+
+__all__ = ["scan_fwd", "state_update", "workspace_size", "status_string", "lib", "MambaError",
+           "FLAG_DELTA_B", "FLAG_ACCURATE_EXPM1"]

@@ -1,0 +1,182 @@
+// abi.hip -- the C ABI declared in include/mamba_scan.h: argument checks,
+// the execution plan of a scan (single pass or chunked along L), and the
+// kernel launches.  Every check runs before any HIP call.
+#include <stdlib.h>
+
+#include "kernels.hpp"
+#include "mamba_scan.h"
+
+namespace {
+
+using mamba::Dt;
+
+constexpr int64_t kTile = 64;         // channels per scan workgroup
+constexpr int64_t kStage = 32;        // staging chunk of the scan kernel (steps)
+constexpr int64_t kMaxElems = int64_t(1) << 46;
+
+struct Plan {
+  int64_t tiles_d = 0;
+  int64_t n_chunks = 1;
+  int64_t chunk_len = 0;
+  size_t ws_bytes = 0;
+  size_t off_local = 0, off_start = 0, off_sum = 0;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool shape_ok(int64_t B, int64_t D, int64_t N, int64_t L) {
+  if (B < 1 || D < 1 || N < 1 || L < 1) return false;
+  if (B > kMaxElems / D) return false;
+  if (B * D > kMaxElems / L) return false;
+  return true;
+}
+
+// Test knob: MAMBA_SCAN_CHUNKS=K forces K chunks along L (K >= 1), so the
+// chunked path can be checked at small sizes.  Read on every call.
+int64_t forced_chunks() {
+  const char* s = getenv("MAMBA_SCAN_CHUNKS");
+  if (!s || !*s) return 0;
+  char* end = nullptr;
+  const long long v = strtoll(s, &end, 10);
+  return (end && *end == '\0' && v > 0) ? (int64_t)v : 0;
+}
+
+// Shape-only plan (no device query).  One pass per channel tile while there
+// are enough tiles to occupy the GPU; otherwise (few channels, long L) split L
+// so that about 1024 workgroups run, with chunks of at least 2048 steps.
+Plan make_plan(int64_t B, int64_t D, int64_t N, int64_t L) {
+  Plan p;
+  p.tiles_d = (D + kTile - 1) / kTile;
+  const int64_t tiles = B * p.tiles_d;
+  int64_t k = 1;
+  const int64_t forced = forced_chunks();
+  if (forced > 0) {
+    k = forced;
+  } else if (L >= 4096 && tiles < 512) {
+    k = (1024 + tiles - 1) / tiles;
+    if (k > L / 2048) k = L / 2048;
+    if (k > 64) k = 64;
+    if (k < 1) k = 1;
+  }
+  int64_t len = (L + k - 1) / k;
+  len = (len + kStage - 1) / kStage * kStage;
+  p.chunk_len = len;
+  p.n_chunks = (L + len - 1) / len;
+  if (p.n_chunks > 1) {
+    const size_t state = size_t(p.n_chunks) * size_t(B) * size_t(D) * size_t(N) * sizeof(float);
+    const size_t sums = size_t(p.n_chunks) * size_t(B) * size_t(D) * sizeof(float);
+    p.off_local = 0;
+    p.off_start = align256(state);
+    p.off_sum = p.off_start + align256(state);
+    p.ws_bytes = p.off_sum + align256(sums);
+  }
+  return p;
+}
+
+bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
+bool dtype_ok(int t) { return t == MAMBA_F32 || t == MAMBA_BF16; }
+constexpr unsigned kKnownFlags = MAMBA_FLAG_DELTA_B | MAMBA_FLAG_ACCURATE_EXPM1;
+
+}  // namespace
+
+extern "C" {
+
+size_t mamba_scan_workspace_size(int64_t B, int64_t D, int64_t N, int64_t L) {
+  if (!shape_ok(B, D, N, L) || N > 16) return (size_t)-1;
+  return make_plan(B, D, N, L).ws_bytes;
+}
+
+int mamba_scan_fwd(const void* u, const void* delta, const void* z, const void* Bt, const void* Ct,
+                   const float* A, const float* Dskip, const float* delta_bias, void* y,
+                   float* final_state, int64_t B, int64_t D, int64_t N, int64_t L,
+                   mamba_dtype_t in_dtype, mamba_dtype_t out_dtype, int return_final_state,
+                   unsigned flags, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return MAMBA_ERR_DTYPE;
+  if (flags & ~kKnownFlags) return MAMBA_ERR_UNSUPPORTED;
+  if (!shape_ok(B, D, N, L)) return MAMBA_ERR_SHAPE;
+  if (N > 16) return MAMBA_ERR_UNSUPPORTED;
+  if (!u || !delta || !Bt || !Ct || !A || !y) return MAMBA_ERR_NULL;
+  if (return_final_state && !final_state) return MAMBA_ERR_NULL;
+  for (const void* ptr : {u, delta, z, Bt, Ct, (const void*)y})
+    if (ptr && !aligned(ptr, 16)) return MAMBA_ERR_ALIGN;
+  for (const void* ptr : {(const void*)A, (const void*)Dskip, (const void*)delta_bias, (const void*)final_state})
+    if (ptr && !aligned(ptr, 4)) return MAMBA_ERR_ALIGN;
+
+  const Plan plan = make_plan(B, D, N, L);
+  if (plan.n_chunks * B * plan.tiles_d >= (int64_t(1) << 31)) return MAMBA_ERR_SHAPE;
+  if (plan.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < plan.ws_bytes) return MAMBA_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return MAMBA_ERR_ALIGN;
+  }
+
+  mamba::ScanParams p{};
+  p.u = u; p.delta = delta; p.z = z; p.Bt = Bt; p.Ct = Ct;
+  p.A = A; p.Dskip = Dskip; p.bias = delta_bias;
+  p.y = y; p.final_state = return_final_state ? final_state : nullptr;
+  p.B = B; p.D = D; p.N = N; p.L = L;
+  p.tiles_d = plan.tiles_d;
+  p.n_chunks = plan.n_chunks;
+  p.chunk_len = plan.chunk_len;
+  p.accurate = (in_dtype == MAMBA_F32) || (flags & MAMBA_FLAG_ACCURATE_EXPM1);
+  p.delta_b = (flags & MAMBA_FLAG_DELTA_B) ? 1 : 0;
+  p.vec = (L % 8 == 0) ? 1 : 0;
+  const Dt in = in_dtype == MAMBA_BF16 ? Dt::BF16 : Dt::F32;
+  const Dt out = out_dtype == MAMBA_BF16 ? Dt::BF16 : Dt::F32;
+
+  if (plan.n_chunks > 1) {
+    char* ws = static_cast<char*>(workspace);
+    p.h_local = reinterpret_cast<float*>(ws + plan.off_local);
+    p.h_start = reinterpret_cast<float*>(ws + plan.off_start);
+    p.s_sum = reinterpret_cast<float*>(ws + plan.off_sum);
+    if (mamba::launch_scan_summary(p, in, stream) != hipSuccess) return MAMBA_ERR_HIP;
+    if (mamba::launch_scan_carry(p, stream) != hipSuccess) return MAMBA_ERR_HIP;
+  }
+  if (mamba::launch_scan_full(p, in, out, stream) != hipSuccess) return MAMBA_ERR_HIP;
+  return MAMBA_OK;
+}
+
+int mamba_state_update(float* state, const void* u, const void* delta, const void* z,
+                       const void* Bt, const void* Ct, const float* A, const float* Dskip,
+                       const float* delta_bias, void* y, int64_t B, int64_t D, int64_t N,
+                       mamba_dtype_t in_dtype, mamba_dtype_t out_dtype, unsigned flags,
+                       hipStream_t stream) {
+  if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return MAMBA_ERR_DTYPE;
+  if (flags & ~kKnownFlags) return MAMBA_ERR_UNSUPPORTED;
+  if (!shape_ok(B, D, N, 1)) return MAMBA_ERR_SHAPE;
+  if (N > 16) return MAMBA_ERR_UNSUPPORTED;
+  if (!state || !u || !delta || !Bt || !Ct || !A || !y) return MAMBA_ERR_NULL;
+  if (!aligned(state, 16) || !aligned(A, 16)) return MAMBA_ERR_ALIGN;
+  const size_t ea = in_dtype == MAMBA_BF16 ? 2 : 4;
+  for (const void* ptr : {u, delta, z, Bt, Ct})
+    if (ptr && !aligned(ptr, ea)) return MAMBA_ERR_ALIGN;
+  if (!aligned(y, out_dtype == MAMBA_BF16 ? 2 : 4)) return MAMBA_ERR_ALIGN;
+  for (const void* ptr : {(const void*)Dskip, (const void*)delta_bias})
+    if (ptr && !aligned(ptr, 4)) return MAMBA_ERR_ALIGN;
+  if ((B * D * 4 + 255) / 256 >= (int64_t(1) << 31)) return MAMBA_ERR_SHAPE;
+
+  mamba::UpdateParams p{};
+  p.state = state; p.u = u; p.delta = delta; p.z = z; p.Bt = Bt; p.Ct = Ct;
+  p.A = A; p.Dskip = Dskip; p.bias = delta_bias; p.y = y;
+  p.B = B; p.D = D; p.N = N;
+  p.accurate = 1;
+  p.delta_b = (flags & MAMBA_FLAG_DELTA_B) ? 1 : 0;
+  const Dt in = in_dtype == MAMBA_BF16 ? Dt::BF16 : Dt::F32;
+  const Dt out = out_dtype == MAMBA_BF16 ? Dt::BF16 : Dt::F32;
+  return mamba::launch_state_update(p, in, out, stream) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
+}
+
+const char* mamba_status_string(int status) {
+  switch (status) {
+    case MAMBA_OK: return "ok";
+    case MAMBA_ERR_NULL: return "a required pointer is NULL";
+    case MAMBA_ERR_SHAPE: return "invalid or too large shape";
+    case MAMBA_ERR_DTYPE: return "unknown dtype";
+    case MAMBA_ERR_ALIGN: return "pointer is not sufficiently aligned";
+    case MAMBA_ERR_UNSUPPORTED: return "unsupported argument (N > 16 or unknown flag)";
+    case MAMBA_ERR_WORKSPACE: return "workspace missing or too small";
+    case MAMBA_ERR_HIP: return "HIP launch or runtime error";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,63 @@
+// kernels.hpp -- launch interface between the C ABI (abi.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mamba {
+
+enum class Dt : int { F32 = 0, BF16 = 1 };
+
+// Discretisation variants of the inner loop (chosen per wave at run time).
+enum LoopMode : int {
+  kZohFast = 0,      // (Abar - 1) / A as fma(Abar, 1/A, -1/A)
+  kZohAccurate = 1,  // (Abar - 1) from a series for small |delta A|
+  kDeltaB = 2        // simplified rule Bbar = delta * B
+};
+
+struct ScanParams {
+  const void* u;
+  const void* delta;
+  const void* z;        // may be null
+  const void* Bt;
+  const void* Ct;
+  const float* A;
+  const float* Dskip;   // may be null
+  const float* bias;    // may be null
+  void* y;
+  float* final_state;   // may be null
+  int64_t B, D, N, L;
+  int64_t tiles_d;      // ceil(D / 64)
+  int64_t n_chunks;     // L-chunks per channel tile (1 = whole sequence in one pass)
+  int64_t chunk_len;    // time steps per chunk, a multiple of the staging chunk
+  float* h_local;       // (n_chunks, B, D, N): chunk end states from a zero start
+  float* s_sum;         // (n_chunks, B, D): sum of delta over each chunk
+  float* h_start;       // (n_chunks, B, D, N): true start state of each chunk
+  int accurate;         // force the accurate (Abar - 1) loop
+  int delta_b;          // simplified discretisation
+  int vec;              // rows are 16-byte aligned multiples of 8 elements
+};
+
+struct UpdateParams {
+  float* state;
+  const void* u;
+  const void* delta;
+  const void* z;
+  const void* Bt;
+  const void* Ct;
+  const float* A;
+  const float* Dskip;
+  const float* bias;
+  void* y;
+  int64_t B, D, N;
+  int accurate;
+  int delta_b;
+};
+
+// Each returns hipSuccess or the launch error.
+hipError_t launch_scan_full(const ScanParams& p, Dt in, Dt out, hipStream_t s);
+hipError_t launch_scan_summary(const ScanParams& p, Dt in, hipStream_t s);
+hipError_t launch_scan_carry(const ScanParams& p, hipStream_t s);
+hipError_t launch_state_update(const UpdateParams& p, Dt in, Dt out, hipStream_t s);
+
+}  // namespace mamba

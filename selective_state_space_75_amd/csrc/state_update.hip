@@ -1,0 +1,113 @@
+// state_update.hip -- single-token selective state update for gfx950.
+//
+// One decoding step ("Mamba 模型", 为什么 Mamba 推理更省: the state is updated
+// in place one token at a time; "Mamba 与状态空间模型" section 03: the state
+// of a layer is channels x 16 numbers, independent of the sequence length):
+//   delta = softplus(delta_raw + bias_d)
+//   h_n  <- exp(delta A_dn) h_n + (exp(delta A_dn) - 1)/A_dn B_n u     (ZOH)
+//   y     = (sum_n C_n h_n + D_d u) * silu(z)
+//
+// The step is a stream over the fp32 state (B, D, N): every state number is
+// read once and written once, so the kernel is bound by HBM bandwidth and the
+// arithmetic per element is free.  Mapping: four lanes per channel, each lane
+// owning four consecutive states (one 16-byte load and store of state and of
+// A); the quad reduces the readout with two lane exchanges, and its first lane
+// applies the skip term and the gate and stores y.
+#include "device_math.hpp"
+#include "kernels.hpp"
+
+namespace mamba {
+namespace {
+
+template <bool kBF16>
+__device__ __forceinline__ float ld(const void* base, int64_t i) {
+  if constexpr (kBF16) return bf16_to_f32(static_cast<const uint16_t*>(base)[i]);
+  else return static_cast<const float*>(base)[i];
+}
+
+template <bool kInBF16, bool kOutBF16, bool kVec>
+__global__ __launch_bounds__(256) void state_update_kernel(UpdateParams p) {
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t ch = g >> 2;                 // flattened (b, d)
+  const int q = (int)(g & 3);                // quad lane: states 4q .. 4q+3
+  const int64_t N = p.N, D = p.D;
+  const bool ok = ch < p.B * D;
+  const int64_t b = ok ? ch / D : 0;
+  const int64_t d = ok ? ch - b * D : 0;
+
+  float acc = 0.0f, uu = 0.0f;
+  if (ok) {
+    uu = ld<kInBF16>(p.u, ch);
+    const float bias = p.bias ? p.bias[d] : 0.0f;
+    const float delta = softplus(ld<kInBF16>(p.delta, ch) + bias);
+    float hs[4], av[4];
+    float* srow = p.state + ch * N;
+    const float* arow = p.A + d * N;
+    if constexpr (kVec) {
+      const float4 s4 = *reinterpret_cast<const float4*>(srow + 4 * q);
+      const float4 a4 = *reinterpret_cast<const float4*>(arow + 4 * q);
+      hs[0] = s4.x; hs[1] = s4.y; hs[2] = s4.z; hs[3] = s4.w;
+      av[0] = a4.x; av[1] = a4.y; av[2] = a4.z; av[3] = a4.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t n = 4 * q + i;
+        hs[i] = n < N ? srow[n] : 0.0f;
+        av[i] = n < N ? arow[n] : -1.0f;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t n = 4 * q + i;
+      if (!kVec && n >= N) continue;
+      const float bn = ld<kInBF16>(p.Bt, b * N + n);
+      const float cn = ld<kInBF16>(p.Ct, b * N + n);
+      float a = av[i];
+      if (__builtin_fabsf(a) < 0x1p-40f) a = (a > 0.0f) ? 0x1p-40f : -0x1p-40f;
+      const float x = delta * (a * kLog2e);
+      const float e = hw_exp2(x);
+      // Bandwidth-bound: always the cancellation-free (Abar - 1) / A.
+      const float k = p.delta_b ? delta : expm1_from_exp2(x, e) / a;
+      hs[i] = __builtin_fmaf(e, hs[i], k * (bn * uu));
+      acc = __builtin_fmaf(cn, hs[i], acc);
+    }
+    if constexpr (kVec) {
+      *reinterpret_cast<float4*>(srow + 4 * q) = make_float4(hs[0], hs[1], hs[2], hs[3]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t n = 4 * q + i;
+        if (n < N) srow[n] = hs[i];
+      }
+    }
+  }
+  // Sum the four partial readouts of the quad (all lanes take part).
+  acc += __shfl_xor(acc, 1, 4);
+  acc += __shfl_xor(acc, 2, 4);
+  if (ok && q == 0) {
+    float v = acc + (p.Dskip ? p.Dskip[d] : 0.0f) * uu;
+    if (p.z) v *= silu(ld<kInBF16>(p.z, ch));
+    if constexpr (kOutBF16) static_cast<uint16_t*>(p.y)[ch] = f32_to_bf16(v);
+    else static_cast<float*>(p.y)[ch] = v;
+  }
+}
+
+template <bool kInBF16, bool kOutBF16>
+hipError_t launch_t(const UpdateParams& p, hipStream_t s) {
+  const int64_t threads = p.B * p.D * 4;
+  const dim3 g((unsigned)((threads + 255) / 256)), blk(256);
+  if (p.N == 16)
+    hipLaunchKernelGGL((state_update_kernel<kInBF16, kOutBF16, true>), g, blk, 0, s, p);
+  else
+    hipLaunchKernelGGL((state_update_kernel<kInBF16, kOutBF16, false>), g, blk, 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_state_update(const UpdateParams& p, Dt in, Dt out, hipStream_t s) {
+  if (in == Dt::BF16) return out == Dt::BF16 ? launch_t<true, true>(p, s) : launch_t<true, false>(p, s);
+  return out == Dt::BF16 ? launch_t<false, true>(p, s) : launch_t<false, false>(p, s);
+}
+
+}  // namespace mamba

@@ -1,0 +1,104 @@
+"""Shared helpers of the GPU parity tests: upload seeded inputs, run the HIP
+path through the binding, run the oracle on the same values, compare."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+from selective_state_space_75_amd import workloads as W
+
+BF16_REL_L2 = 2e-3          # bf16-input / fp32-state workloads: relative L2 ...
+BF16_MAX_ABS_FRAC = 1e-2    # ... and max-abs <= 1e-2 * max|y|
+F32_REL_L2 = 1e-5           # fp32 workloads
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(a, dev):
+    """numpy float32 or bf16 bit patterns (uint16) -> torch tensor on `dev`."""
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+    return torch.from_numpy(a.astype(np.float32, copy=False)).to(dev)
+
+
+def from_dev(t) -> np.ndarray:
+    import torch
+    return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
+
+
+def f64(a) -> np.ndarray:
+    return W.as_f32(a).astype(np.float64)
+
+
+def rel_l2(got, ref) -> float:
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    return float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
+
+
+def max_abs_frac(got, ref) -> float:
+    ref = np.asarray(ref, dtype=np.float64)
+    return float(np.max(np.abs(np.asarray(got, dtype=np.float64) - ref)) / max(np.max(np.abs(ref)), 1e-300))
+
+
+def bf16_floor(ref) -> float:
+    """Relative L2 error of rounding the fp64 reference itself to bf16."""
+    r = W.as_f32(W.f32_to_bf16_bits(np.asarray(ref, dtype=np.float32))).astype(np.float64)
+    return rel_l2(r, ref)
+
+
+def assert_close(got, ref, bf16: bool, what: str):
+    e = rel_l2(got, ref)
+    if bf16:
+        m = max_abs_frac(got, ref)
+        log("  %s: rel_l2=%.3e (bf16 floor %.3e) max_abs/max|y|=%.3e" % (what, e, bf16_floor(ref), m))
+        assert e <= BF16_REL_L2, "%s rel L2 %.3e > %.1e" % (what, e, BF16_REL_L2)
+        assert m <= BF16_MAX_ABS_FRAC, "%s max-abs fraction %.3e > %.1e" % (what, m, BF16_MAX_ABS_FRAC)
+    else:
+        log("  %s: rel_l2=%.3e" % (what, e))
+        assert e <= F32_REL_L2, "%s rel L2 %.3e > %.1e" % (what, e, F32_REL_L2)
+
+
+def upload_scan(x: dict, dev) -> dict:
+    return {k: to_dev(x[k], dev) for k in ("u", "delta_raw", "z", "Bt", "Ct", "A", "Dskip", "delta_bias")}
+
+
+def gpu_scan(t: dict, **kw):
+    import selective_state_space_75_amd as m
+    return m.scan_fwd(t["u"], t["delta_raw"], t.get("z"), t["Bt"], t["Ct"], t["A"], t.get("Dskip"),
+                      t.get("delta_bias"), **kw)
+
+
+def oracle_scan(x: dict, channels=None, use_z=True, use_dskip=True, use_bias=True, discretization="zoh",
+                h0=None):
+    """Oracle on the same values; `channels` = list of (b, d) to compute only those rows.
+    Returns (y, final_state) with a leading axis over the requested channels when given."""
+    import oracle
+    if channels is None:
+        return oracle.scan(f64(x["u"]), f64(x["delta_raw"]), f64(x["z"]) if use_z else None,
+                           f64(x["Bt"]), f64(x["Ct"]), x["A"].astype(np.float64),
+                           x["Dskip"].astype(np.float64) if use_dskip else None,
+                           x["delta_bias"].astype(np.float64) if use_bias else None,
+                           h0=h0, discretization=discretization)
+    ys, hs = [], []
+    for b in sorted(set(b for b, _ in channels)):
+        ds = [d for bb, d in channels if bb == b]
+        sl = lambda a: f64(a[b:b + 1, ds, :])  # noqa: E731
+        y, hN = oracle.scan(sl(x["u"]), sl(x["delta_raw"]), sl(x["z"]) if use_z else None,
+                            f64(x["Bt"][b:b + 1]), f64(x["Ct"][b:b + 1]), x["A"][ds].astype(np.float64),
+                            x["Dskip"][ds].astype(np.float64) if use_dskip else None,
+                            x["delta_bias"][ds].astype(np.float64) if use_bias else None,
+                            discretization=discretization)
+        for i, d in enumerate(ds):
+            ys.append(((b, d), y[0, i]))
+            hs.append(((b, d), hN[0, i]))
+    order = {c: i for i, c in enumerate(channels)}
+    ys.sort(key=lambda p: order[p[0]])
+    hs.sort(key=lambda p: order[p[0]])
+    return np.stack([v for _, v in ys]), np.stack([v for _, v in hs])
