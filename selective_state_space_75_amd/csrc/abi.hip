@@ -3,6 +3,10 @@
 // kernel launches.  Every check runs before any HIP call.
 #include <stdlib.h>
 
+#include <atomic>
+#include <chrono>
+#include <mutex>
+
 #include "kernels.hpp"
 #include "mamba_scan.h"
 
@@ -13,13 +17,19 @@ using mamba::Dt;
 constexpr int64_t kTile = 64;         // channels per scan workgroup
 constexpr int64_t kStage = 32;        // staging chunk of the scan kernel (steps)
 constexpr int64_t kMaxElems = int64_t(1) << 46;
+constexpr int64_t kV2Step = 32;       // the v2 kernel needs L to be a multiple of this
+constexpr int64_t kGroupsPlan = 256;  // workgroups of the balanced split (one per CU on MI355X)
+constexpr size_t kHandOverBytes = 64 * 16 * sizeof(float);
 
 struct Plan {
   int64_t tiles_d = 0;
   int64_t n_chunks = 1;
   int64_t chunk_len = 0;
+  bool v2 = false;          // the 8-wave kernel (L multiple of 32)
+  bool balanced = false;    // equal (tile x time) ranges with state hand-over
   size_t ws_bytes = 0;
   size_t off_local = 0, off_start = 0, off_sum = 0;
+  size_t off_flag = 0, off_pub = 0;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -62,6 +72,8 @@ Plan make_plan(int64_t B, int64_t D, int64_t N, int64_t L) {
   len = (len + kStage - 1) / kStage * kStage;
   p.chunk_len = len;
   p.n_chunks = (L + len - 1) / len;
+  p.v2 = (L % kV2Step == 0) && (getenv("MAMBA_SCAN_V1") == nullptr);
+  p.balanced = p.v2 && p.n_chunks == 1 && tiles >= kGroupsPlan;
   if (p.n_chunks > 1) {
     const size_t state = size_t(p.n_chunks) * size_t(B) * size_t(D) * size_t(N) * sizeof(float);
     const size_t sums = size_t(p.n_chunks) * size_t(B) * size_t(D) * sizeof(float);
@@ -69,8 +81,53 @@ Plan make_plan(int64_t B, int64_t D, int64_t N, int64_t L) {
     p.off_start = align256(state);
     p.off_sum = p.off_start + align256(state);
     p.ws_bytes = p.off_sum + align256(sums);
+  } else if (p.balanced) {
+    p.off_flag = 0;
+    p.off_pub = align256(kGroupsPlan * sizeof(uint64_t));
+    p.ws_bytes = p.off_pub + kGroupsPlan * kHandOverBytes;
   }
   return p;
+}
+
+// Compute units of the current device, cached per device id.
+int64_t device_cus() {
+  static std::mutex mu;
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 0;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// Bound of the wait for a state hand-over between workgroups (iterations of
+// a short sleep, about 50 ms in total).  Test knob: MAMBA_SCAN_HANDOVER_SPIN=n
+// sets it, so that 0 forces every workgroup to recompute the state instead.
+uint32_t handover_spin_limit() {
+  const char* s = getenv("MAMBA_SCAN_HANDOVER_SPIN");
+  if (s && *s) {
+    char* end = nullptr;
+    const long long v = strtoll(s, &end, 10);
+    if (end && *end == '\0' && v >= 0 && v <= (1ll << 30)) return (uint32_t)v;
+  }
+  return 1u << 20;
+}
+
+// Numbers launches of the balanced kernel: a hand-over slot counts as
+// published only when its flag holds this launch's value, so stale flags
+// left in a reused workspace are never mistaken for fresh ones.
+uint64_t next_epoch() {
+  static std::atomic<uint64_t> counter{0};
+  static std::once_flag once;
+  std::call_once(once, [] {
+    const uint64_t t = (uint64_t)std::chrono::high_resolution_clock::now().time_since_epoch().count();
+    counter.store((t * 0x9E3779B97F4A7C15ull) | 1ull);
+  });
+  return counter.fetch_add(1);
 }
 
 bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
@@ -123,15 +180,31 @@ int mamba_scan_fwd(const void* u, const void* delta, const void* z, const void* 
   const Dt in = in_dtype == MAMBA_BF16 ? Dt::BF16 : Dt::F32;
   const Dt out = out_dtype == MAMBA_BF16 ? Dt::BF16 : Dt::F32;
 
+  mamba::V2Params q{};
+  q.spin_limit = handover_spin_limit();
+  if (plan.balanced) {
+    const int64_t cus = device_cus();
+    if (cus <= 0) return MAMBA_ERR_HIP;
+    q.balanced = 1;
+    q.groups = cus < kGroupsPlan ? cus : kGroupsPlan;
+    q.epoch = next_epoch();
+    char* ws = static_cast<char*>(workspace);
+    q.pub_flag = reinterpret_cast<uint64_t*>(ws + plan.off_flag);
+    q.pub_state = reinterpret_cast<float*>(ws + plan.off_pub);
+  }
   if (plan.n_chunks > 1) {
     char* ws = static_cast<char*>(workspace);
     p.h_local = reinterpret_cast<float*>(ws + plan.off_local);
     p.h_start = reinterpret_cast<float*>(ws + plan.off_start);
     p.s_sum = reinterpret_cast<float*>(ws + plan.off_sum);
-    if (mamba::launch_scan_summary(p, in, stream) != hipSuccess) return MAMBA_ERR_HIP;
+    const hipError_t e = plan.v2 ? mamba::launch_scan_v2(p, q, in, out, true, stream)
+                                 : mamba::launch_scan_summary(p, in, stream);
+    if (e != hipSuccess) return MAMBA_ERR_HIP;
     if (mamba::launch_scan_carry(p, stream) != hipSuccess) return MAMBA_ERR_HIP;
   }
-  if (mamba::launch_scan_full(p, in, out, stream) != hipSuccess) return MAMBA_ERR_HIP;
+  const hipError_t e = plan.v2 ? mamba::launch_scan_v2(p, q, in, out, false, stream)
+                               : mamba::launch_scan_full(p, in, out, stream);
+  if (e != hipSuccess) return MAMBA_ERR_HIP;
   return MAMBA_OK;
 }
 

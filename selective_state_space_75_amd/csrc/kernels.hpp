@@ -38,6 +38,16 @@ struct ScanParams {
   int vec;              // rows are 16-byte aligned multiples of 8 elements
 };
 
+// Extra parameters of the v2 scan kernel (scan_v2.hip).
+struct V2Params {
+  int balanced;          // 1: equal (tile x time) ranges per workgroup with state hand-over
+  int64_t groups;        // workgroups in balanced mode
+  uint64_t epoch;        // value that marks a hand-over slot as published by this launch
+  uint32_t spin_limit;   // bounded wait for a hand-over before recomputing it
+  float* pub_state;      // (groups, 64, 16) fp32 hand-over states
+  uint64_t* pub_flag;    // (groups) epoch flags
+};
+
 struct UpdateParams {
   float* state;
   const void* u;
@@ -58,6 +68,7 @@ struct UpdateParams {
 hipError_t launch_scan_full(const ScanParams& p, Dt in, Dt out, hipStream_t s);
 hipError_t launch_scan_summary(const ScanParams& p, Dt in, hipStream_t s);
 hipError_t launch_scan_carry(const ScanParams& p, hipStream_t s);
+hipError_t launch_scan_v2(const ScanParams& p, const V2Params& q, Dt in, Dt out, bool summary, hipStream_t s);
 hipError_t launch_state_update(const UpdateParams& p, Dt in, Dt out, hipStream_t s);
 
 }  // namespace mamba

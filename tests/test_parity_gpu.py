@@ -115,6 +115,16 @@ CASES = [
     (2, 96, 16, 160, "bf16", "f32", None, {"accurate": True}),
     (2, 64, 16, 128, "f32", "f32", None, {"zero_A": True}),
     (1, 64, 16, 3000, "bf16", "bf16", 5, {"zero_A": True}),
+    # sequence lengths that are multiples of 32 take the 8-wave kernel
+    (1, 64, 16, 3072, "bf16", "bf16", 5, {"zero_A": True}),
+    (2, 100, 16, 320, "bf16", "f32", 3, {}),
+    (2, 100, 16, 320, "f32", "f32", 3, {"delta_b": True}),
+    (3, 70, 7, 64, "bf16", "bf16", None, {"no_z": True}),
+    (1, 33, 16, 32, "f32", "f32", None, {"accurate": True}),
+    # at least 256 tiles: balanced split with state hand-over between workgroups
+    (2, 10240, 16, 128, "bf16", "bf16", None, {}),
+    (1, 16384 + 64 * 60, 16, 96, "f32", "f32", None, {"zero_A": True}),
+    (3, 6000, 9, 64, "bf16", "f32", None, {"delta_b": True}),
 ]
 
 
@@ -151,6 +161,37 @@ def test_ragged_and_options(case, dev, monkeypatch):
     e = rel_l2(from_dev(hN), hr)
     log("  final state rel_l2=%.3e" % e)
     assert e <= (2e-3 if dt == "bf16" else 1e-5)
+
+
+def test_handover_fallback_matches(dev, monkeypatch):
+    """With the hand-over wait forced to zero every split tile recomputes its
+    state at the cut instead of receiving it; the output must not change."""
+    import torch
+    import selective_state_space_75_amd as m
+    B, D, N, L = 2, 10240, 16, 160
+    assert m.workspace_size(B, D, N, L) > 0
+    x = W.custom_scan_inputs(B, D, N, L, "bf16", seed=31337)
+    t = upload_scan(x, dev)
+    y1, h1 = gpu_scan(t, return_final_state=True)
+    monkeypatch.setenv("MAMBA_SCAN_HANDOVER_SPIN", "0")
+    y2, h2 = gpu_scan(t, return_final_state=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(h1, h2)
+    yr, _ = oracle_scan(x)
+    assert_close(from_dev(y2), yr, True, "fallback y")
+
+
+def test_v1_kernel_on_aligned_shape(dev, monkeypatch):
+    """The general kernel (used for ragged L) on an L % 32 == 0 workload."""
+    import torch
+    monkeypatch.setenv("MAMBA_SCAN_V1", "1")
+    x = W.custom_scan_inputs(2, 192, 16, 512, "bf16", seed=555)
+    t = upload_scan(x, dev)
+    y, hN = gpu_scan(t, return_final_state=True)
+    torch.cuda.synchronize()
+    yr, hr = oracle_scan(x)
+    assert_close(from_dev(y), yr, True, "v1 y")
+    assert rel_l2(from_dev(hN), hr) <= 2e-3
 
 
 def test_theorem1_gate_on_gpu(dev):
