@@ -17,15 +17,16 @@ using mamba::Dt;
 constexpr int64_t kTile = 64;         // channels per scan workgroup
 constexpr int64_t kStage = 32;        // staging chunk of the scan kernel (steps)
 constexpr int64_t kMaxElems = int64_t(1) << 46;
-constexpr int64_t kV2Step = 32;       // the v2 kernel needs L to be a multiple of this
-constexpr int64_t kGroupsPlan = 256;  // workgroups of the balanced split (one per CU on MI355X)
-constexpr size_t kHandOverBytes = 64 * 16 * sizeof(float);
+constexpr int64_t kV4Step = 32;       // the wave-tile kernel needs L to be a multiple of this
+constexpr int64_t kV4Tile = 16;       // channels per wave in the wave-tile kernel
+constexpr int64_t kGroupsPlan = 1024; // waves of the balanced split (one per SIMD on MI355X)
+constexpr size_t kHandOverBytes = kV4Tile * 16 * sizeof(float);
 
 struct Plan {
   int64_t tiles_d = 0;
   int64_t n_chunks = 1;
   int64_t chunk_len = 0;
-  bool v2 = false;          // the 8-wave kernel (L multiple of 32)
+  bool v4 = false;          // the wave-tile kernel (L multiple of 32)
   bool balanced = false;    // equal (tile x time) ranges with state hand-over
   size_t ws_bytes = 0;
   size_t off_local = 0, off_start = 0, off_sum = 0;
@@ -57,13 +58,17 @@ int64_t forced_chunks() {
 Plan make_plan(int64_t B, int64_t D, int64_t N, int64_t L) {
   Plan p;
   p.tiles_d = (D + kTile - 1) / kTile;
-  const int64_t tiles = B * p.tiles_d;
+  p.v4 = (L % kV4Step == 0) && (getenv("MAMBA_SCAN_V1") == nullptr);
+  // Units of independent sequential work: 16-channel tiles (wave-tile
+  // kernel) or 64-channel tiles (general kernel).
+  const int64_t tiles = p.v4 ? B * ((D + kV4Tile - 1) / kV4Tile) : B * p.tiles_d;
+  const int64_t target = p.v4 ? kGroupsPlan : 1024;
   int64_t k = 1;
   const int64_t forced = forced_chunks();
   if (forced > 0) {
     k = forced;
-  } else if (L >= 4096 && tiles < 512) {
-    k = (1024 + tiles - 1) / tiles;
+  } else if (L >= 4096 && tiles < (p.v4 ? target : 512)) {
+    k = (target + tiles - 1) / tiles;
     if (k > L / 2048) k = L / 2048;
     if (k > 64) k = 64;
     if (k < 1) k = 1;
@@ -72,8 +77,7 @@ Plan make_plan(int64_t B, int64_t D, int64_t N, int64_t L) {
   len = (len + kStage - 1) / kStage * kStage;
   p.chunk_len = len;
   p.n_chunks = (L + len - 1) / len;
-  p.v2 = (L % kV2Step == 0) && (getenv("MAMBA_SCAN_V1") == nullptr);
-  p.balanced = p.v2 && p.n_chunks == 1 && tiles >= kGroupsPlan;
+  p.balanced = p.v4 && p.n_chunks == 1 && tiles >= kGroupsPlan && getenv("MAMBA_SCAN_NO_BALANCE") == nullptr;
   if (p.n_chunks > 1) {
     const size_t state = size_t(p.n_chunks) * size_t(B) * size_t(D) * size_t(N) * sizeof(float);
     const size_t sums = size_t(p.n_chunks) * size_t(B) * size_t(D) * sizeof(float);
@@ -186,7 +190,7 @@ int mamba_scan_fwd(const void* u, const void* delta, const void* z, const void* 
     const int64_t cus = device_cus();
     if (cus <= 0) return MAMBA_ERR_HIP;
     q.balanced = 1;
-    q.groups = cus < kGroupsPlan ? cus : kGroupsPlan;
+    q.groups = 4 * cus < kGroupsPlan ? 4 * cus : kGroupsPlan;   // one wave per SIMD
     q.epoch = next_epoch();
     char* ws = static_cast<char*>(workspace);
     q.pub_flag = reinterpret_cast<uint64_t*>(ws + plan.off_flag);
@@ -197,12 +201,12 @@ int mamba_scan_fwd(const void* u, const void* delta, const void* z, const void* 
     p.h_local = reinterpret_cast<float*>(ws + plan.off_local);
     p.h_start = reinterpret_cast<float*>(ws + plan.off_start);
     p.s_sum = reinterpret_cast<float*>(ws + plan.off_sum);
-    const hipError_t e = plan.v2 ? mamba::launch_scan_v2(p, q, in, out, true, stream)
+    const hipError_t e = plan.v4 ? mamba::launch_scan_v4(p, q, in, out, true, stream)
                                  : mamba::launch_scan_summary(p, in, stream);
     if (e != hipSuccess) return MAMBA_ERR_HIP;
     if (mamba::launch_scan_carry(p, stream) != hipSuccess) return MAMBA_ERR_HIP;
   }
-  const hipError_t e = plan.v2 ? mamba::launch_scan_v2(p, q, in, out, false, stream)
+  const hipError_t e = plan.v4 ? mamba::launch_scan_v4(p, q, in, out, false, stream)
                                : mamba::launch_scan_full(p, in, out, stream);
   if (e != hipSuccess) return MAMBA_ERR_HIP;
   return MAMBA_OK;

@@ -38,7 +38,7 @@ struct ScanParams {
   int vec;              // rows are 16-byte aligned multiples of 8 elements
 };
 
-// Extra parameters of the v2 scan kernel (scan_v2.hip).
+// Extra parameters of the wave-tile scan kernel (scan_v4.hip, L % 32 == 0).
 struct V2Params {
   int balanced;          // 1: equal (tile x time) ranges per workgroup with state hand-over
   int64_t groups;        // workgroups in balanced mode
@@ -68,7 +68,7 @@ struct UpdateParams {
 hipError_t launch_scan_full(const ScanParams& p, Dt in, Dt out, hipStream_t s);
 hipError_t launch_scan_summary(const ScanParams& p, Dt in, hipStream_t s);
 hipError_t launch_scan_carry(const ScanParams& p, hipStream_t s);
-hipError_t launch_scan_v2(const ScanParams& p, const V2Params& q, Dt in, Dt out, bool summary, hipStream_t s);
+hipError_t launch_scan_v4(const ScanParams& p, const V2Params& q, Dt in, Dt out, bool summary, hipStream_t s);
 hipError_t launch_state_update(const UpdateParams& p, Dt in, Dt out, hipStream_t s);
 
 }  // namespace mamba

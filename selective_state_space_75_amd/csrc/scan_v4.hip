@@ -1,0 +1,443 @@
+// scan_v4.hip -- main selective-scan kernel for gfx950 (L a multiple of 32,
+// 16-byte aligned rows).  Computes what scan_fwd.hip computes ("Mamba 模型",
+// full-step flowchart nodes H to M; ZOH per "Mamba模型：高效序列建模的新突破"
+// 3.1): softplus step, ZOH discretisation, recurrence, readout, skip, gate.
+//
+// Layout on the GPU -- one wave is a whole, independent unit of work:
+//  * a wave owns a tile of 16 channels of one batch row; four lanes (a quad)
+//    per channel, each lane holding 4 of the 16 states in VGPRs;
+//  * the readout sum over the 16 states is 4 in-lane FMAs plus two DPP adds
+//    across the quad;
+//  * the sequence is walked in 32-step chunks.  Each chunk's u, delta_raw, z
+//    and B_t, C_t are loaded with coalesced 16-byte loads one chunk ahead,
+//    then staged in the wave's own LDS region (delta = softplus(delta_raw +
+//    bias) once per element; u and delta channel-major, B_t and C_t
+//    step-major so that a lane reads its 4 states of B or C with one 16-byte
+//    LDS read);
+//  * lane g of a quad keeps the outputs of steps 8g..8g+7, adds D u, applies
+//    the gate and writes them with one 16-byte store;
+//  * workgroups are single waves, so no workgroup barrier is ever needed.
+// Balanced split: with at least as many tiles as waves, the (tile x 32-step
+// block) work is cut into equal contiguous ranges, one per wave.  A tile cut
+// between waves g and g+1 is scanned by g from t = 0 to the cut (done first,
+// its end state published to a slot marked with this launch's epoch) and by
+// g+1 from the cut to the end (done last, after reading the slot).  The wait
+// is bounded; if it runs out, g+1 recomputes the state at the cut itself, so
+// the kernel always finishes.
+// Per ZOH state update: 6 fp32 VALU + 1 v_exp_f32, plus per step 2 DPP adds
+// and 1 select per lane (for 4 updates).
+#include "device_math.hpp"
+#include "kernels.hpp"
+
+namespace mamba {
+namespace {
+
+constexpr int kTile = 16;     // channels per wave
+constexpr int kNS = 4;        // states per lane
+constexpr int kCT = 32;       // steps per chunk
+constexpr int kSlot = kTile * 16;   // floats per hand-over slot
+
+struct WaveLds {
+  float4 B4[kCT * 4];         // B_t, [step][state quad] (16-byte reads of 4 states)
+  float4 C4[kCT * 4];         // C_t, [step][state quad]
+  int flag;
+};
+
+template <bool kBF16> struct Raw8;   // 8 consecutive elements
+template <> struct Raw8<true> { uint4 w; };
+template <> struct Raw8<false> { float4 a, b; };
+
+template <bool kBF16>
+__device__ __forceinline__ Raw8<kBF16> load8(const void* base, int64_t off, bool ok) {
+  Raw8<kBF16> r;
+  if constexpr (kBF16) {
+    r.w = ok ? *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off) : make_uint4(0, 0, 0, 0);
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
+    r.a = ok ? p[0] : make_float4(0, 0, 0, 0);
+    r.b = ok ? p[1] : make_float4(0, 0, 0, 0);
+  }
+  return r;
+}
+
+template <bool kBF16>
+__device__ __forceinline__ float at8(const Raw8<kBF16>& r, int j) {
+  if constexpr (kBF16) {
+    const uint32_t w = (j < 2) ? r.w.x : (j < 4) ? r.w.y : (j < 6) ? r.w.z : r.w.w;
+    return (j & 1) ? bf16_hi(w) : bf16_lo(w);
+  } else {
+    const float4 v = (j < 4) ? r.a : r.b;
+    const int k = j & 3;
+    return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
+  }
+}
+
+// Value of lane q of this lane's quad (DPP quad_perm [q,q,q,q]); folded by
+// the compiler into the instruction that consumes it.
+template <int q>
+__device__ __forceinline__ float quad_bcast(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), q * 0x55, 0xF, 0xF, true));
+}
+
+// Sum over the four lanes of a quad (result in every lane): two adds whose
+// second operand comes from another lane of the quad through DPP.
+__device__ __forceinline__ float quad_sum(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));
+  return v;
+}
+
+struct Consts {
+  float a2[kNS];   // A * log2(e)
+  float ia[kNS];   // 1 / A
+  float bias, dskip;
+  int accurate;    // wave-uniform
+};
+
+__device__ __forceinline__ Consts load_consts(const ScanParams& p, int64_t d, bool d_ok, int g) {
+  Consts k;
+  bool tiny = false;
+#pragma unroll
+  for (int i = 0; i < kNS; ++i) {
+    const int n = 4 * g + i;
+    float a = (d_ok && n < p.N) ? p.A[d * p.N + n] : -1.0f;
+    // |A| < 2^-40 (including 0) becomes -2^-40 (sign kept): the ZOH coefficient
+    // is then delta to within delta * 2^-41 (resolved by the accurate loop).
+    if (__builtin_fabsf(a) < 0x1p-40f) { tiny = true; a = (a > 0.0f) ? 0x1p-40f : -0x1p-40f; }
+    k.a2[i] = a * kLog2e;
+    k.ia[i] = 1.0f / a;
+  }
+  k.bias = (d_ok && p.bias) ? p.bias[d] : 0.0f;
+  k.dskip = (d_ok && p.Dskip) ? p.Dskip[d] : 0.0f;
+  k.accurate = (p.accurate || __any(tiny)) ? 1 : 0;
+  return k;
+}
+
+template <int M> struct ModeTag { static constexpr int kValue = M; };
+
+// Calls f(ModeTag<i>{}) for i = I .. E-1 (compile-time step indices).
+template <int I, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < E) {
+    f(ModeTag<I>{});
+    static_for<I + 1, E>(f);
+  }
+}
+
+template <bool kBF16>
+struct ChunkRaw {
+  Raw8<kBF16> u, d, z;        // channel c, steps 8g .. 8g+7
+  Raw8<kBF16> bc0, bc1;       // B or C row n, steps 16h .. 16h+15
+};
+
+// One tile-segment scan.  Every lane of the wave must call it.
+template <bool kInBF16, bool kOutBF16, bool kReadout>
+struct Segment {
+  static __device__ __forceinline__ float run(const ScanParams& p, WaveLds& s, int64_t b, int64_t d0,
+                                              int64_t t_begin, int64_t t_end, float (&h)[kNS], const Consts& k,
+                                              int mode) {
+    const int lane = threadIdx.x & 63;
+    const int c = lane >> 2, g = lane & 3;
+    const int64_t D = p.D, N = p.N, L = p.L;
+    const int64_t d = d0 + c;
+    const bool c_ok = d < D;
+    const int64_t row = (b * D + (c_ok ? d : 0)) * L;
+    // B/C staging role: lanes 0..31 -> B, 32..63 -> C; state n, half h2
+    const int bc_arr = lane >> 5, bc_n = (lane >> 1) & 15, bc_h = lane & 1;
+    const bool bc_ok = bc_n < N && (kReadout || bc_arr == 0);
+    const void* bc_base = bc_arr ? p.Ct : p.Bt;
+    const int64_t bc_row = (b * N + (bc_n < N ? bc_n : 0)) * L;
+    const bool want_z = kReadout && p.z != nullptr;
+
+    auto fetch = [&](int64_t t0, ChunkRaw<kInBF16>& r) {
+      r.u = load8<kInBF16>(p.u, row + t0 + 8 * g, c_ok);
+      r.d = load8<kInBF16>(p.delta, row + t0 + 8 * g, c_ok);
+      if (want_z) r.z = load8<kInBF16>(p.z, row + t0 + 8 * g, c_ok);
+      r.bc0 = load8<kInBF16>(bc_base, bc_row + t0 + 16 * bc_h, bc_ok);
+      r.bc1 = load8<kInBF16>(bc_base, bc_row + t0 + 16 * bc_h + 8, bc_ok);
+    };
+    float dsum = 0.0f;
+    float dreg[8], ureg[8];     // delta and u of this lane's 8 steps (8g .. 8g+7) of the chunk
+    auto stage = [&](const ChunkRaw<kInBF16>& r) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float dv = c_ok ? softplus(at8<kInBF16>(r.d, j) + k.bias) : 0.0f;
+        if constexpr (!kReadout) dsum += dv;
+        dreg[j] = dv;
+        ureg[j] = at8<kInBF16>(r.u, j);
+      }
+      float* dst = reinterpret_cast<float*>(bc_arr ? s.C4 : s.B4);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        dst[(16 * bc_h + j) * 16 + bc_n] = at8<kInBF16>(r.bc0, j);
+        dst[(16 * bc_h + 8 + j) * 16 + bc_n] = at8<kInBF16>(r.bc1, j);
+      }
+    };
+
+    const int64_t nck = (t_end - t_begin) / kCT;
+    if (nck <= 0) return 0.0f;
+    ChunkRaw<kInBF16> cur, nxt;
+    fetch(t_begin, cur);
+    for (int64_t ck = 0; ck < nck; ++ck) {
+      const int64_t t0 = t_begin + ck * kCT;
+      __syncthreads();            // previous chunk's LDS reads are done (single wave: cheap)
+      stage(cur);
+      if (ck + 1 < nck) fetch(t0 + kCT, nxt);
+      __syncthreads();            // staged values visible to the whole wave
+      // Software pipeline over the 32 steps of the chunk: the B/C operands of
+      // step t+2 are read from LDS, the state-independent part of step t+1
+      // (Abar and the input term) is computed, step t updates h and forms
+      // its 4-state readout, and the quad sum of step t-1 is finished.  delta
+      // and u of step t live in lane t/8 of the quad (register t%8) and reach
+      // the other lanes through DPP operands.
+      float yk[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) yk[j] = 0.0f;
+      auto steps = [&](auto mode_tag) {
+        constexpr int M = decltype(mode_tag)::kValue;
+        float4 Bv[kCT], Cv[kCT];
+        float ev[2][kNS], inv[2][kNS];
+        float accp = 0.0f;
+        auto load = [&](int t) {
+          Bv[t] = s.B4[t * 4 + g];
+          if constexpr (kReadout) Cv[t] = s.C4[t * 4 + g];
+        };
+        auto pre = [&](auto tc) {   // state-independent part of step t
+          constexpr int t = decltype(tc)::kValue;
+          const float dt = quad_bcast<t / 8>(dreg[t % 8]);
+          const float ut = quad_bcast<t / 8>(ureg[t % 8]);
+          const float bn[4] = {Bv[t].x, Bv[t].y, Bv[t].z, Bv[t].w};
+#pragma unroll
+          for (int i = 0; i < kNS; ++i) {
+            const float x = dt * k.a2[i];
+            const float e = hw_exp2(x);
+            float in;
+            if constexpr (M == kDeltaB) {
+              in = (dt * ut) * bn[i];
+            } else {
+              const float kc = (M == kZohFast) ? __builtin_fmaf(e, k.ia[i], -k.ia[i])
+                                               : expm1_from_exp2(x, e) * k.ia[i];
+              in = kc * (ut * bn[i]);
+            }
+            ev[t & 1][i] = e;
+            inv[t & 1][i] = in;
+          }
+        };
+        auto finish = [&](auto tc, float a) {   // quad sum of step t, kept by lane t/8
+          constexpr int t = decltype(tc)::kValue;
+          const float y = quad_sum(a);
+          if (g == t / 8) yk[t % 8] = y;
+        };
+        load(0);
+        load(1);
+        pre(ModeTag<0>{});
+        static_for<0, kCT>([&](auto tc) {
+          constexpr int t = decltype(tc)::kValue;
+          if constexpr (t + 2 < kCT) load(t + 2);
+          if constexpr (t + 1 < kCT) pre(ModeTag<t + 1>{});
+          float acc = 0.0f;
+#pragma unroll
+          for (int i = 0; i < kNS; ++i) {
+            h[i] = __builtin_fmaf(ev[t & 1][i], h[i], inv[t & 1][i]);
+            if constexpr (kReadout) {
+              const float cn = (i == 0) ? Cv[t].x : (i == 1) ? Cv[t].y : (i == 2) ? Cv[t].z : Cv[t].w;
+              acc = (i == 0) ? cn * h[i] : __builtin_fmaf(cn, h[i], acc);
+            }
+          }
+          if constexpr (kReadout) {
+            if constexpr (t > 0) finish(ModeTag<t - 1>{}, accp);
+            accp = acc;
+          }
+        });
+        if constexpr (kReadout) finish(ModeTag<kCT - 1>{}, accp);
+      };
+      if (mode == kZohFast) steps(ModeTag<kZohFast>{});
+      else if (mode == kZohAccurate) steps(ModeTag<kZohAccurate>{});
+      else steps(ModeTag<kDeltaB>{});
+
+      if constexpr (kReadout) {
+        float o[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          float v = __builtin_fmaf(k.dskip, at8<kInBF16>(cur.u, j), yk[j]);
+          if (want_z) v *= silu(at8<kInBF16>(cur.z, j));
+          o[j] = v;
+        }
+        if (c_ok) {
+          const int64_t at = row + t0 + 8 * g;
+          if constexpr (kOutBF16) {
+            *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.y) + at) =
+                make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                           pack_bf16x2(o[6], o[7]));
+          } else {
+            float4* q = reinterpret_cast<float4*>(static_cast<float*>(p.y) + at);
+            q[0] = make_float4(o[0], o[1], o[2], o[3]);
+            q[1] = make_float4(o[4], o[5], o[6], o[7]);
+          }
+        }
+      }
+      if (ck + 1 < nck) cur = nxt;
+    }
+    if constexpr (!kReadout) dsum = quad_sum(dsum);
+    return dsum;
+  }
+};
+
+// ------------------------------------------------------------------ state hand-over between waves
+__device__ __forceinline__ void publish(const V2Params& q, int64_t slot, const float (&h)[kNS]) {
+  const int lane = threadIdx.x & 63;
+  const int c = lane >> 2, g = lane & 3;
+  float* dst = q.pub_state + slot * kSlot;
+#pragma unroll
+  for (int i = 0; i < kNS; ++i)
+    __hip_atomic_store(dst + c * 16 + 4 * g + i, h[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __threadfence();
+  __syncthreads();
+  if (lane == 0) __hip_atomic_store(q.pub_flag + slot, q.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ bool receive(const V2Params& q, WaveLds& s, int64_t slot, float (&h)[kNS]) {
+  const int lane = threadIdx.x & 63;
+  const int c = lane >> 2, g = lane & 3;
+  if (lane == 0) {
+    int ok = 0;
+    for (uint32_t it = 0; it < q.spin_limit; ++it) {
+      if (__hip_atomic_load(q.pub_flag + slot, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == q.epoch) { ok = 1; break; }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    s.flag = ok;
+  }
+  __syncthreads();
+  const bool ok = s.flag != 0;
+  __syncthreads();
+  if (ok) {
+    __threadfence();
+    const float* src = q.pub_state + slot * kSlot;
+#pragma unroll
+    for (int i = 0; i < kNS; ++i)
+      h[i] = __hip_atomic_load(src + c * 16 + 4 * g + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  return ok;
+}
+
+struct Range {
+  int64_t nb, first, last, lo_off, hi_off, ft_begin;
+  int has_head, has_tail, count;
+};
+
+__device__ __forceinline__ Range balanced_range(const ScanParams& p, const V2Params& q, int64_t tiles) {
+  Range w;
+  const int64_t gi = blockIdx.x;
+  w.nb = p.L / kCT;
+  const int64_t U = tiles * w.nb;
+  const int64_t lo = gi * U / q.groups, hi = (gi + 1) * U / q.groups;
+  w.first = lo / w.nb;
+  w.last = (hi - 1) / w.nb;
+  w.lo_off = lo % w.nb;
+  w.hi_off = hi % w.nb;
+  w.has_head = (w.hi_off != 0 && !(w.first == w.last && w.lo_off != 0)) ? 1 : 0;
+  w.has_tail = (w.lo_off != 0) ? 1 : 0;
+  w.ft_begin = (w.lo_off == 0) ? w.first : w.first + 1;
+  const int64_t ft_end = (w.hi_off == 0) ? w.last + 1 : w.last;
+  w.count = w.has_head + (int)(ft_end > w.ft_begin ? ft_end - w.ft_begin : 0) + w.has_tail;
+  return w;
+}
+
+enum SegKind : int { kPlain = 0, kHead = 1, kWhole = 2, kTail = 3 };
+
+template <bool kInBF16, bool kOutBF16, bool kSummary>
+__global__ __launch_bounds__(64) void scan_v4_kernel(ScanParams p, V2Params q) {
+  __shared__ WaveLds s;
+  const int lane = threadIdx.x & 63;
+  const int c = lane >> 2, g = lane & 3;
+  const int64_t D = p.D, N = p.N, L = p.L;
+  const int64_t tiles_d = (D + kTile - 1) / kTile;
+  const int64_t tiles = p.B * tiles_d;
+  using Full = Segment<kInBF16, kOutBF16, true>;
+  using StateOnly = Segment<kInBF16, kOutBF16, false>;
+
+  Range w{};
+  int nseg = 1;
+  if (q.balanced) {
+    w = balanced_range(p, q, tiles);
+    nseg = w.count;
+  }
+  for (int si = 0; si < nseg; ++si) {
+    int kind;
+    int64_t tile, chunk = 0, t_begin, t_end;
+    if (!q.balanced) {
+      kind = kPlain;
+      chunk = (int64_t)blockIdx.x / tiles;
+      tile = (int64_t)blockIdx.x - chunk * tiles;
+      t_begin = chunk * p.chunk_len;
+      t_end = (t_begin + p.chunk_len < L) ? t_begin + p.chunk_len : L;
+    } else if (w.has_head && si == 0) {
+      kind = kHead; tile = w.last; t_begin = 0; t_end = w.hi_off * kCT;
+    } else if (w.has_tail && si == nseg - 1) {
+      kind = kTail; tile = w.first; t_begin = w.lo_off * kCT;
+      t_end = (w.first == w.last && w.hi_off != 0) ? w.hi_off * kCT : L;
+    } else {
+      kind = kWhole; tile = w.ft_begin + (si - w.has_head); t_begin = 0; t_end = L;
+    }
+    const int64_t b = tile / tiles_d;
+    const int64_t d0 = (tile - b * tiles_d) * kTile;
+    const int64_t d = d0 + c;
+    const bool d_ok = d < D;
+    const Consts k = load_consts(p, d, d_ok, g);
+    const int mode = p.delta_b ? kDeltaB : (k.accurate ? kZohAccurate : kZohFast);
+
+    float h[kNS];
+#pragma unroll
+    for (int i = 0; i < kNS; ++i) {
+      h[i] = 0.0f;
+      if (!kSummary && kind == kPlain && p.h_start != nullptr && chunk > 0 && d_ok && 4 * g + i < N)
+        h[i] = p.h_start[((chunk * p.B + b) * D + d) * N + 4 * g + i];
+    }
+    if (!kSummary && kind == kTail) {
+      if (!receive(q, s, (int64_t)blockIdx.x - 1, h)) {
+#pragma unroll
+        for (int i = 0; i < kNS; ++i) h[i] = 0.0f;
+        StateOnly::run(p, s, b, d0, 0, t_begin, h, k, mode);
+      }
+    }
+    if constexpr (kSummary) {
+      const float ds = StateOnly::run(p, s, b, d0, t_begin, t_end, h, k, mode);
+#pragma unroll
+      for (int i = 0; i < kNS; ++i)
+        if (d_ok && 4 * g + i < N) p.h_local[((chunk * p.B + b) * D + d) * N + 4 * g + i] = h[i];
+      if (g == 0 && d_ok) p.s_sum[(chunk * p.B + b) * D + d] = ds;
+    } else {
+      Full::run(p, s, b, d0, t_begin, t_end, h, k, mode);
+      if (kind == kHead || (kind == kTail && t_end != L)) {
+        publish(q, (int64_t)blockIdx.x, h);
+      } else if (t_end == L && p.final_state != nullptr && d_ok &&
+                 (kind != kPlain || chunk == p.n_chunks - 1)) {
+#pragma unroll
+        for (int i = 0; i < kNS; ++i)
+          if (4 * g + i < N) p.final_state[(b * D + d) * N + 4 * g + i] = h[i];
+      }
+    }
+  }
+}
+
+template <bool kInBF16, bool kOutBF16, bool kSummary>
+hipError_t launch_t(const ScanParams& p, const V2Params& q, hipStream_t st) {
+  const int64_t tiles = p.B * ((p.D + kTile - 1) / kTile);
+  int64_t grid;
+  if (q.balanced) grid = q.groups;
+  else grid = (kSummary ? p.n_chunks - 1 : p.n_chunks) * tiles;
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL((scan_v4_kernel<kInBF16, kOutBF16, kSummary>), dim3((unsigned)grid), dim3(64), 0, st, p, q);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_scan_v4(const ScanParams& p, const V2Params& q, Dt in, Dt out, bool summary, hipStream_t s) {
+  if (summary) return in == Dt::BF16 ? launch_t<true, false, true>(p, q, s) : launch_t<false, false, true>(p, q, s);
+  if (in == Dt::BF16)
+    return out == Dt::BF16 ? launch_t<true, true, false>(p, q, s) : launch_t<true, false, false>(p, q, s);
+  return out == Dt::BF16 ? launch_t<false, true, false>(p, q, s) : launch_t<false, false, false>(p, q, s);
+}
+
+}  // namespace mamba

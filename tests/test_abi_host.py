@@ -46,12 +46,16 @@ def test_workspace_size_plan():
     ws = _lib.workspace_size
     assert ws(1, 16, 16, 256) == 0
     assert ws(8, 1536, 16, 2048) == 0
-    # >= 256 tiles of 64 channels: balanced split, 256 hand-over slots
-    # (an 8-byte flag each, then 64 x 16 fp32 states each)
-    assert ws(4, 5120, 16, 2048) == 256 * 8 + 256 * 64 * 16 * 4
+    # >= 1024 tiles of 16 channels: balanced split over 1024 waves, one
+    # hand-over slot per wave (an 8-byte flag each, then 16 x 16 fp32 states each)
+    assert ws(4, 5120, 16, 2048) == 1024 * 8 + 1024 * 16 * 16 * 4
     assert ws(4, 5120, 16, 2040) == 0      # L % 32 != 0: general kernel, no hand-over
     n = ws(1, 4096, 16, 131072)
-    # 16 chunks: h_local and h_start (K, B, D, N) fp32 + sum of delta (K, B, D) fp32
+    # 256 tiles of 16 channels -> 4 chunks: h_local and h_start (K, B, D, N)
+    # fp32 + sum of delta (K, B, D) fp32
+    assert n == 2 * 4 * 4096 * 16 * 4 + 4 * 4096 * 4
+    # the general kernel (L % 32 != 0) plans with 64-channel tiles: 16 chunks
+    n = ws(1, 4096, 16, 131072 - 8)
     assert n == 2 * 16 * 4096 * 16 * 4 + 16 * 4096 * 4
     assert _lib.lib().mamba_scan_workspace_size(0, 1, 1, 1) == ctypes.c_size_t(-1).value
     assert _lib.lib().mamba_scan_workspace_size(1, 1, 17, 1) == ctypes.c_size_t(-1).value
