@@ -35,9 +35,12 @@
  *   - Outputs must not alias inputs (except `state`, which is updated in
  *     place by design).  Calls that share an output or a workspace must not
  *     run concurrently.
- *   - No C++ exception crosses this interface.  The library holds no mutable
- *     global state; concurrent calls on different streams with disjoint
- *     buffers are safe.
+ *   - No C++ exception crosses this interface.  The only process-wide state
+ *     is a per-device cache of the compute-unit count (read once) and an
+ *     atomic launch counter that tags the scan's hand-over slots in the
+ *     workspace, so a workspace is reused without being cleared.  Concurrent
+ *     calls on different streams with disjoint buffers (workspaces included)
+ *     are safe.
  *   - Supported sizes: 1 <= N <= 16; B, D, L >= 1; B*D*L < 2^46.
  *   - Arithmetic is fp32 throughout (state, discretisation, accumulation);
  *     bf16 inputs are widened exactly, outputs are rounded to nearest-even.
@@ -98,7 +101,9 @@ size_t mamba_scan_workspace_size(int64_t B, int64_t D, int64_t N, int64_t L);
  *                 (must then be non-NULL; ignored otherwise).
  *   workspace   : scratch of at least mamba_scan_workspace_size(B, D, N, L)
  *                 bytes (may be NULL when that size is 0); contents on entry
- *                 are ignored, contents on exit are unspecified.
+ *                 are ignored (hand-over slots are tagged with a per-launch
+ *                 64-bit value, so stale contents are never mistaken for
+ *                 this launch's), contents on exit are unspecified.
  *   flags       : MAMBA_FLAG_* bits.
  *
  * The initial state is zero.  Alignment: u, delta, z, Bt, Ct, y must be

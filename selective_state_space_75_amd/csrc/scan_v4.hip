@@ -38,9 +38,8 @@ constexpr int kCT = 32;       // steps per chunk
 constexpr int kSlot = kTile * 16;   // floats per hand-over slot
 
 struct WaveLds {
-  float4 B4[kCT * 4];         // B_t, [step][state quad] (16-byte reads of 4 states)
-  float4 C4[kCT * 4];         // C_t, [step][state quad]
-  int flag;
+  float4 B4[2][kCT * 4];      // B_t, [buffer][step][state quad] (16-byte reads of 4 states)
+  float4 C4[2][kCT * 4];      // C_t, same layout
 };
 
 template <bool kBF16> struct Raw8;   // 8 consecutive elements
@@ -131,6 +130,19 @@ struct ChunkRaw {
 };
 
 // One tile-segment scan.  Every lane of the wave must call it.
+//
+// Software pipeline over 32-step chunks, all within one wave (so no
+// barriers; the wave's LDS accesses are processed in order).  While the 32
+// steps of chunk k run, the wave also
+//   * has the global loads of chunk k+2 in flight,
+//   * evaluates softplus for chunk k+1 and stages its B_t/C_t in the other
+//     LDS buffer,
+//   * finishes chunk k-1's outputs (skip term, gate) -- stored after the steps,
+// so that independent work fills the latency of the recurrence.  Inside the
+// chunk, B/C of step t+2 are read, the state-independent part of step t+1 is
+// computed, step t updates h, and the quad sum of step t-1 is completed.
+// Prefetch addresses past the segment are clamped to its last chunk, so the
+// step loop has no branches.
 template <bool kInBF16, bool kOutBF16, bool kReadout>
 struct Segment {
   static __device__ __forceinline__ float run(const ScanParams& p, WaveLds& s, int64_t b, int64_t d0,
@@ -142,70 +154,82 @@ struct Segment {
     const int64_t d = d0 + c;
     const bool c_ok = d < D;
     const int64_t row = (b * D + (c_ok ? d : 0)) * L;
-    // B/C staging role: lanes 0..31 -> B, 32..63 -> C; state n, half h2
+    // B/C staging role: lanes 0..31 -> B, 32..63 -> C; state bc_n, steps 16*bc_h .. +15
     const int bc_arr = lane >> 5, bc_n = (lane >> 1) & 15, bc_h = lane & 1;
     const bool bc_ok = bc_n < N && (kReadout || bc_arr == 0);
     const void* bc_base = bc_arr ? p.Ct : p.Bt;
     const int64_t bc_row = (b * N + (bc_n < N ? bc_n : 0)) * L;
     const bool want_z = kReadout && p.z != nullptr;
 
+    const int64_t nck = (t_end - t_begin) / kCT;
+    if (nck <= 0) return 0.0f;
+    const int64_t t_last = t_end - kCT;
+
     auto fetch = [&](int64_t t0, ChunkRaw<kInBF16>& r) {
+      t0 = t0 < t_last ? t0 : t_last;     // clamp: stays inside the segment
       r.u = load8<kInBF16>(p.u, row + t0 + 8 * g, c_ok);
       r.d = load8<kInBF16>(p.delta, row + t0 + 8 * g, c_ok);
       if (want_z) r.z = load8<kInBF16>(p.z, row + t0 + 8 * g, c_ok);
       r.bc0 = load8<kInBF16>(bc_base, bc_row + t0 + 16 * bc_h, bc_ok);
       r.bc1 = load8<kInBF16>(bc_base, bc_row + t0 + 16 * bc_h + 8, bc_ok);
     };
-    float dsum = 0.0f;
-    float dreg[8], ureg[8];     // delta and u of this lane's 8 steps (8g .. 8g+7) of the chunk
-    auto stage = [&](const ChunkRaw<kInBF16>& r) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float dv = c_ok ? softplus(at8<kInBF16>(r.d, j) + k.bias) : 0.0f;
-        if constexpr (!kReadout) dsum += dv;
-        dreg[j] = dv;
-        ureg[j] = at8<kInBF16>(r.u, j);
-      }
-      float* dst = reinterpret_cast<float*>(bc_arr ? s.C4 : s.B4);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        dst[(16 * bc_h + j) * 16 + bc_n] = at8<kInBF16>(r.bc0, j);
-        dst[(16 * bc_h + 8 + j) * 16 + bc_n] = at8<kInBF16>(r.bc1, j);
-      }
+    auto stage_bc = [&](const ChunkRaw<kInBF16>& r, int buf, int j) {   // values j and 8+j of this lane's 16
+      float* dst = reinterpret_cast<float*>(bc_arr ? s.C4[buf] : s.B4[buf]);
+      dst[(16 * bc_h + j) * 16 + bc_n] = at8<kInBF16>(r.bc0, j);
+      dst[(16 * bc_h + 8 + j) * 16 + bc_n] = at8<kInBF16>(r.bc1, j);
+    };
+    // Branch-free (a branch would split the step loop's basic block): the
+    // softplus is always evaluated and then discarded for channels past D.
+    auto delta_of = [&](const ChunkRaw<kInBF16>& r, int j) {
+      const float sp = softplus(at8<kInBF16>(r.d, j) + k.bias);
+      return c_ok ? sp : 0.0f;
+    };
+    auto gate_of = [&](const Raw8<kInBF16>& z, int j) {
+      const float gz = silu(at8<kInBF16>(z, j));
+      return want_z ? gz : 1.0f;
     };
 
-    const int64_t nck = (t_end - t_begin) / kCT;
-    if (nck <= 0) return 0.0f;
-    ChunkRaw<kInBF16> cur, nxt;
-    fetch(t_begin, cur);
-    for (int64_t ck = 0; ck < nck; ++ck) {
-      const int64_t t0 = t_begin + ck * kCT;
-      __syncthreads();            // previous chunk's LDS reads are done (single wave: cheap)
-      stage(cur);
-      if (ck + 1 < nck) fetch(t0 + kCT, nxt);
-      __syncthreads();            // staged values visible to the whole wave
-      // Software pipeline over the 32 steps of the chunk: the B/C operands of
-      // step t+2 are read from LDS, the state-independent part of step t+1
-      // (Abar and the input term) is computed, step t updates h and forms
-      // its 4-state readout, and the quad sum of step t-1 is finished.  delta
-      // and u of step t live in lane t/8 of the quad (register t%8) and reach
-      // the other lanes through DPP operands.
-      float yk[8];
+    float dsum = 0.0f;
+    ChunkRaw<kInBF16> rc, r1, r2;     // raw inputs of chunks ck, ck+1, ck+2
+    float dcur[8], ucur[8];           // delta and u of chunk ck, steps 8g .. 8g+7 of this lane
+    float yo[8];                      // readout sums of chunk ck-1 (this lane's steps)
+    Raw8<kInBF16> uo, zo;             // u and z of chunk ck-1
+    fetch(t_begin, rc);
+    fetch(t_begin + kCT, r1);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) yk[j] = 0.0f;
-      auto steps = [&](auto mode_tag) {
-        constexpr int M = decltype(mode_tag)::kValue;
+    for (int j = 0; j < 8; ++j) {
+      dcur[j] = delta_of(rc, j);
+      ucur[j] = at8<kInBF16>(rc.u, j);
+      stage_bc(rc, 0, j);
+      yo[j] = 0.0f;
+    }
+    uo = rc.u;
+    zo = rc.z;
+
+    auto pipeline = [&](auto mode_tag) {
+      constexpr int M = decltype(mode_tag)::kValue;
+      for (int64_t ck = 0; ck < nck; ++ck) {
+        const int64_t t0 = t_begin + ck * kCT;
+        const int buf = (int)(ck & 1);
+        fetch(t0 + 2 * kCT, r2);
+        if constexpr (!kReadout) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) dsum += dcur[j];
+        }
+        float dnext[8], unext[8], o[8], yk[8];
         float4 Bv[kCT], Cv[kCT];
         float ev[2][kNS], inv[2][kNS];
         float accp = 0.0f;
+        const float4* B4 = s.B4[buf];
+        const float4* C4 = s.C4[buf];
         auto load = [&](int t) {
-          Bv[t] = s.B4[t * 4 + g];
-          if constexpr (kReadout) Cv[t] = s.C4[t * 4 + g];
+          Bv[t] = B4[t * 4 + g];
+          if constexpr (kReadout) Cv[t] = C4[t * 4 + g];
         };
         auto pre = [&](auto tc) {   // state-independent part of step t
           constexpr int t = decltype(tc)::kValue;
-          const float dt = quad_bcast<t / 8>(dreg[t % 8]);
-          const float ut = quad_bcast<t / 8>(ureg[t % 8]);
+          const float dt = quad_bcast<t / 8>(dcur[t % 8]);
+          const float ut = quad_bcast<t / 8>(ucur[t % 8]);
           const float bn[4] = {Bv[t].x, Bv[t].y, Bv[t].z, Bv[t].w};
 #pragma unroll
           for (int i = 0; i < kNS; ++i) {
@@ -226,13 +250,27 @@ struct Segment {
         auto finish = [&](auto tc, float a) {   // quad sum of step t, kept by lane t/8
           constexpr int t = decltype(tc)::kValue;
           const float y = quad_sum(a);
-          if (g == t / 8) yk[t % 8] = y;
+          yk[t % 8] = (g == t / 8) ? y : yk[t % 8];
         };
+#pragma unroll
+        for (int j = 0; j < 8; ++j) yk[j] = 0.0f;
         load(0);
         load(1);
         pre(ModeTag<0>{});
         static_for<0, kCT>([&](auto tc) {
           constexpr int t = decltype(tc)::kValue;
+          // independent work of the neighbouring chunks, one item every 4 steps
+          if constexpr (t % 4 == 0) {
+            constexpr int j = t / 4;
+            dnext[j] = delta_of(r1, j);
+            unext[j] = at8<kInBF16>(r1.u, j);
+            stage_bc(r1, buf ^ 1, j);
+          }
+          if constexpr (kReadout && t % 4 == 2) {
+            constexpr int j = t / 4;
+            o[j] = __builtin_fmaf(k.dskip, at8<kInBF16>(uo, j), yo[j]) * gate_of(zo, j);
+          }
+          // the recurrence
           if constexpr (t + 2 < kCT) load(t + 2);
           if constexpr (t + 1 < kCT) pre(ModeTag<t + 1>{});
           float acc = 0.0f;
@@ -249,75 +287,106 @@ struct Segment {
             accp = acc;
           }
         });
-        if constexpr (kReadout) finish(ModeTag<kCT - 1>{}, accp);
-      };
-      if (mode == kZohFast) steps(ModeTag<kZohFast>{});
-      else if (mode == kZohAccurate) steps(ModeTag<kZohAccurate>{});
-      else steps(ModeTag<kDeltaB>{});
-
-      if constexpr (kReadout) {
-        float o[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          float v = __builtin_fmaf(k.dskip, at8<kInBF16>(cur.u, j), yk[j]);
-          if (want_z) v *= silu(at8<kInBF16>(cur.z, j));
-          o[j] = v;
-        }
-        if (c_ok) {
-          const int64_t at = row + t0 + 8 * g;
-          if constexpr (kOutBF16) {
-            *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.y) + at) =
-                make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
-                           pack_bf16x2(o[6], o[7]));
-          } else {
-            float4* q = reinterpret_cast<float4*>(static_cast<float*>(p.y) + at);
-            q[0] = make_float4(o[0], o[1], o[2], o[3]);
-            q[1] = make_float4(o[4], o[5], o[6], o[7]);
+        if constexpr (kReadout) {
+          finish(ModeTag<kCT - 1>{}, accp);
+          // outputs of chunk ck-1
+          if (ck > 0 && c_ok) {
+            const int64_t at = row + t0 - kCT + 8 * g;
+            if constexpr (kOutBF16) {
+              *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.y) + at) =
+                  make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                             pack_bf16x2(o[6], o[7]));
+            } else {
+              float4* q = reinterpret_cast<float4*>(static_cast<float*>(p.y) + at);
+              q[0] = make_float4(o[0], o[1], o[2], o[3]);
+              q[1] = make_float4(o[4], o[5], o[6], o[7]);
+            }
           }
+#pragma unroll
+          for (int j = 0; j < 8; ++j) yo[j] = yk[j];
+          uo = rc.u;
+          zo = rc.z;
+        }
+        // rotate the pipeline
+#pragma unroll
+        for (int j = 0; j < 8; ++j) { dcur[j] = dnext[j]; ucur[j] = unext[j]; }
+        rc = r1;
+        r1 = r2;
+      }
+    };
+    if (mode == kZohFast) pipeline(ModeTag<kZohFast>{});
+    else if (mode == kZohAccurate) pipeline(ModeTag<kZohAccurate>{});
+    else pipeline(ModeTag<kDeltaB>{});
+
+    if constexpr (kReadout) {
+      // outputs of the last chunk
+      float o[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o[j] = __builtin_fmaf(k.dskip, at8<kInBF16>(uo, j), yo[j]) * gate_of(zo, j);
+      if (c_ok) {
+        const int64_t at = row + t_end - kCT + 8 * g;
+        if constexpr (kOutBF16) {
+          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.y) + at) =
+              make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                         pack_bf16x2(o[6], o[7]));
+        } else {
+          float4* q = reinterpret_cast<float4*>(static_cast<float*>(p.y) + at);
+          q[0] = make_float4(o[0], o[1], o[2], o[3]);
+          q[1] = make_float4(o[4], o[5], o[6], o[7]);
         }
       }
-      if (ck + 1 < nck) cur = nxt;
     }
     if constexpr (!kReadout) dsum = quad_sum(dsum);
+    __syncthreads();   // the next segment restages the LDS buffers
     return dsum;
   }
 };
 
 // ------------------------------------------------------------------ state hand-over between waves
+// The slot (16 channels x 16 states) and its flag are written and read only
+// with system-scope atomic accesses, which gfx950 performs with cache-bypass
+// bits (write-through on store, miss on load), so they are coherent across
+// the XCDs' separate L2 caches without any cache-wide writeback/invalidate.
+// The producer waits for its slot stores to complete (vmcnt(0)) before it
+// stores the flag; the consumer reads the slot only after it has seen the
+// flag.  The slot holds this launch's epoch only once its data is in memory.
+__device__ __forceinline__ void vmem_wait_all() {
+  // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maximum)
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
 __device__ __forceinline__ void publish(const V2Params& q, int64_t slot, const float (&h)[kNS]) {
   const int lane = threadIdx.x & 63;
   const int c = lane >> 2, g = lane & 3;
   float* dst = q.pub_state + slot * kSlot;
 #pragma unroll
   for (int i = 0; i < kNS; ++i)
-    __hip_atomic_store(dst + c * 16 + 4 * g + i, h[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __threadfence();
-  __syncthreads();
-  if (lane == 0) __hip_atomic_store(q.pub_flag + slot, q.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(dst + c * 16 + 4 * g + i, h[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  vmem_wait_all();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  if (lane == 0) __hip_atomic_store(q.pub_flag + slot, q.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
-__device__ __forceinline__ bool receive(const V2Params& q, WaveLds& s, int64_t slot, float (&h)[kNS]) {
+__device__ __forceinline__ bool receive(const V2Params& q, int64_t slot, float (&h)[kNS]) {
   const int lane = threadIdx.x & 63;
   const int c = lane >> 2, g = lane & 3;
+  int ok = 0;
   if (lane == 0) {
-    int ok = 0;
     for (uint32_t it = 0; it < q.spin_limit; ++it) {
-      if (__hip_atomic_load(q.pub_flag + slot, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == q.epoch) { ok = 1; break; }
+      if (__hip_atomic_load(q.pub_flag + slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) == q.epoch) { ok = 1; break; }
       __builtin_amdgcn_s_sleep(2);
     }
-    s.flag = ok;
   }
-  __syncthreads();
-  const bool ok = s.flag != 0;
-  __syncthreads();
+  ok = __builtin_amdgcn_readfirstlane(ok);   // the workgroup is this one wave
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
   if (ok) {
-    __threadfence();
     const float* src = q.pub_state + slot * kSlot;
 #pragma unroll
     for (int i = 0; i < kNS; ++i)
-      h[i] = __hip_atomic_load(src + c * 16 + 4 * g + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      h[i] = __hip_atomic_load(src + c * 16 + 4 * g + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   }
-  return ok;
+  return ok != 0;
 }
 
 struct Range {
@@ -346,7 +415,7 @@ __device__ __forceinline__ Range balanced_range(const ScanParams& p, const V2Par
 enum SegKind : int { kPlain = 0, kHead = 1, kWhole = 2, kTail = 3 };
 
 template <bool kInBF16, bool kOutBF16, bool kSummary>
-__global__ __launch_bounds__(64) void scan_v4_kernel(ScanParams p, V2Params q) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void scan_v4_kernel(ScanParams p, V2Params q) {
   __shared__ WaveLds s;
   const int lane = threadIdx.x & 63;
   const int c = lane >> 2, g = lane & 3;
@@ -394,7 +463,7 @@ __global__ __launch_bounds__(64) void scan_v4_kernel(ScanParams p, V2Params q) {
         h[i] = p.h_start[((chunk * p.B + b) * D + d) * N + 4 * g + i];
     }
     if (!kSummary && kind == kTail) {
-      if (!receive(q, s, (int64_t)blockIdx.x - 1, h)) {
+      if (!receive(q, (int64_t)blockIdx.x - 1, h)) {
 #pragma unroll
         for (int i = 0; i < kNS; ++i) h[i] = 0.0f;
         StateOnly::run(p, s, b, d0, 0, t_begin, h, k, mode);
