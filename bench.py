@@ -5,8 +5,8 @@
 Default workload: the Mamba-2.8B-shaped layer scan, B=4 D=5120 N=16 L=2048,
 bf16 inputs/outputs, fp32 state and arithmetic, final state returned.  A
 step is one call of mamba_scan_fwd over one batch (inputs resident in HBM;
-two input sets alternate so the 256 MB last-level cache cannot hold a step's
-inputs from the previous step).  Prints one JSON line.
+three input sets rotate so the 256 MB last-level cache cannot hold a step's
+inputs from an earlier step).  Prints one JSON line.
 
 Other workloads: --workload long_b1 (B=1 D=4096 L=131072, chunked along L),
 mamba130m_layer, tiny_fp32, decode48 (48 layers x 128 steps of
@@ -38,7 +38,12 @@ VALU_PEAK_TOPS = CUS * SIMDS_PER_CU * LANES_PER_SIMD * CLOCK_GHZ / 1e3
 # B*u, *coef, e*h + input, C*h accumulate): 6 VALU + 1 transcendental; the
 # transcendental occupies the VALU issue slot it is issued in.
 OPS_PER_UPDATE = 7
-MEASURED_TRANS_SLOTS = None     # filled from the rate probe, see DESIGN
+# Counter-derived HBM traffic of the scan kernel (rocprofv3 FETCH_SIZE and
+# WRITE_SIZE, scaled by the same counters on a plain copy of known size); used
+# only while the kernel sources still hash to the recorded value.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_mamba2.8b_layer_traffic.txt")
+SCAN_SOURCES = ["selective_state_space_75_amd/csrc/scan_v4.hip", "selective_state_space_75_amd/csrc/kernels.hpp",
+                "selective_state_space_75_amd/csrc/device_math.hpp", "selective_state_space_75_amd/csrc/abi.hip"]
 
 
 def log(msg):
@@ -61,34 +66,46 @@ def cpu_threads():
 
 # ----------------------------------------------------------------------------- CPU oracle baseline
 def cpu_baseline_scan(cfg, x, seconds: float):
-    """Time the fp64 oracle (as it stands) on whole channels of the same workload."""
+    """Time the fp64 oracle (as it stands) on the whole workload, repeated
+    until about `seconds` of wall time; report the median run."""
     import oracle
     from selective_state_space_75_amd import workloads as W
     nth = cpu_threads()
     f64 = lambda a: W.as_f32(a).astype(np.float64)  # noqa: E731
-
-    def run(nch):
-        b = 0
-        ds = list(range(nch))
-        args = (f64(x["u"][b:b + 1, ds]), f64(x["delta_raw"][b:b + 1, ds]), f64(x["z"][b:b + 1, ds]),
-                f64(x["Bt"][b:b + 1]), f64(x["Ct"][b:b + 1]), x["A"][ds].astype(np.float64),
-                x["Dskip"][ds].astype(np.float64), x["delta_bias"][ds].astype(np.float64))
+    args = (f64(x["u"]), f64(x["delta_raw"]), f64(x["z"]), f64(x["Bt"]), f64(x["Ct"]),
+            x["A"].astype(np.float64), x["Dskip"].astype(np.float64), x["delta_bias"].astype(np.float64))
+    times = []
+    t_all = time.perf_counter()
+    while not times or (time.perf_counter() - t_all < seconds and len(times) < 200):
         t0 = time.perf_counter()
         oracle.scan(*args, nthreads=nth)
-        return time.perf_counter() - t0
-
-    probe = min(cfg.D, 4 * nth)
-    t_probe = run(probe)
-    nch = int(min(cfg.D, max(probe, probe * seconds / max(t_probe, 1e-6))))
-    nch = max(nth, (nch // nth) * nth) if nch >= nth else nch
-    t = run(nch) if nch != probe else t_probe
-    frac = nch / float(cfg.B * cfg.D)
-    gbs = cfg.algorithmic_bytes() * frac / t / 1e9
+        times.append(time.perf_counter() - t0)
+    t = float(np.median(times))
+    gbs = cfg.algorithmic_bytes() / t / 1e9
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": nth, "kind": "oracle",
-            "sample": "%d of %d channels (batch row 0, full L=%d, N=%d), fp64 C oracle, %.1f s wall; "
-                      "GB/s = the workload's algorithmic bytes x sampled fraction / time"
-                      % (nch, cfg.B * cfg.D, cfg.L, cfg.N, t),
-            "elems_per_s": round(cfg.elements * frac / t, 1)}
+            "sample": "whole workload (B=%d D=%d N=%d L=%d, final state), fp64 C oracle, %d runs in %.1f s, "
+                      "median %.3f s per run; GB/s = the workload's algorithmic bytes / run time"
+                      % (cfg.B, cfg.D, cfg.N, cfg.L, len(times), time.perf_counter() - t_all, t),
+            "elems_per_s": round(cfg.elements / t, 1)}
+
+
+def recorded_traffic():
+    """(bytes per launch, note) from the committed counter summary, or (None,
+    reason) when it is missing or the kernel sources changed since."""
+    import hashlib
+    if not os.path.exists(TRAFFIC_FILE):
+        return None, "no counter summary"
+    kv = {}
+    for line in open(TRAFFIC_FILE, encoding="utf-8"):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for f in SCAN_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if kv.get("source_sha256") != h.hexdigest():
+        return None, "kernel changed since the counters were taken"
+    return int(kv["hbm_bytes_per_launch"]), kv.get("summary", "")
 
 
 # ----------------------------------------------------------------------------- scan benchmark
@@ -125,6 +142,7 @@ def bench_scan(args, dev):
         step(i)
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # the launch stream is torch's current stream, so these events bracket the kernel itself
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -140,6 +158,8 @@ def bench_scan(args, dev):
     gbs = nbytes / (ms_step * 1e-3) / 1e9
     ops = cfg.updates * OPS_PER_UPDATE
     achieved_tops = ops / (kern_ms * 1e-3) / 1e12
+    traffic, traffic_note = recorded_traffic() if cfg.name == "mamba2.8b_layer" else (None, "not measured")
+    p10, p50, p90 = (float(v) for v in np.percentile(per_launch_ms, [10, 50, 90]))
     line = {
         "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
@@ -150,10 +170,15 @@ def bench_scan(args, dev):
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "elems_per_s": round(cfg.elements / (ms_step * 1e-3), 1),
         "kernel_ms_mean": round(kern_ms, 5), "kernel_ms_min": round(float(np.min(per_launch_ms)), 5),
+        "kernel_ms_p10_p50_p90": [round(p10, 5), round(p50, 5), round(p90, 5)],
+        "input_sets": len(sets),
         "algorithmic_bytes": nbytes,
         "roofline": {"bound": "alu", "achieved": round(achieved_tops, 3), "peak": round(VALU_PEAK_TOPS, 2),
-                     "unit": "TOP/s", "frac": round(achieved_tops / VALU_PEAK_TOPS, 4), "traffic": None,
+                     "unit": "TOP/s", "frac": round(achieved_tops / VALU_PEAK_TOPS, 4), "traffic": traffic,
+                     "traffic_note": traffic_note,
                      "ops_per_update": OPS_PER_UPDATE, "updates_per_launch": cfg.updates,
+                     "op": "fp32 VALU lane-operations (6 per state update + 1 exp2); peak = 256 CUs x 64 "
+                           "lanes x 2.4 GHz, non-packed",
                      "hbm_achieved_gbs_kernel": round(nbytes / (kern_ms * 1e-3) / 1e9, 2)},
     }
     return line, cfg, x
@@ -194,7 +219,7 @@ def bench_decode(args, dev):
     for i in range(args.warmup):
         graphs[i % pool].replay()
     torch.cuda.synchronize()
-    steps = cfg.steps
+    steps = args.decode_steps
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -241,12 +266,13 @@ def copy_calibration(args, dev):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mamba2.8b_layer")
-    ap.add_argument("--sets", type=int, default=2, help="distinct input sets cycled over steps")
+    ap.add_argument("--sets", type=int, default=3, help="distinct input sets cycled over steps")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-steps", type=int, default=128, help="decode48: timed steps (the workload has 128)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--copy-mb", type=int, default=1024)
     args = ap.parse_args()

@@ -76,7 +76,8 @@ typedef enum {
 /* Flag bits (the `flags` argument of both calls). */
 #define MAMBA_FLAG_DELTA_B 0x1u          /* Bbar = delta * B instead of zero-order hold */
 #define MAMBA_FLAG_ACCURATE_EXPM1 0x2u   /* force the cancellation-free (Abar - 1) path;
-                                            always on when in_dtype is MAMBA_F32 */
+                                            always on in mamba_state_update and, in
+                                            mamba_scan_fwd, when in_dtype is MAMBA_F32 */
 
 /*
  * Bytes of device workspace mamba_scan_fwd needs for a problem of this shape.

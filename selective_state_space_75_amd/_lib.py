@@ -163,7 +163,7 @@ def scan_fwd(u, delta, z, Bt, Ct, A, Dskip=None, delta_bias=None, *, return_fina
 
 
 def state_update(state, u, delta, z, Bt, Ct, A, Dskip=None, delta_bias=None, *, out_dtype=None,
-                 delta_b=False, y=None, stream=None):
+                 delta_b=False, accurate_expm1=False, y=None, stream=None):
     """One decoding step; `state` (B, D, N) fp32 is updated in place.  Returns y (B, D)."""
     torch = _torch()
     if state.dim() != 3:
@@ -190,7 +190,8 @@ def state_update(state, u, delta, z, Bt, Ct, A, Dskip=None, delta_bias=None, *, 
     st = lib().mamba_state_update(
         _ptr(state), _ptr(u), _ptr(delta), _ptr(z), _ptr(Bt), _ptr(Ct), _ptr(A), _ptr(Dskip),
         _ptr(delta_bias), _ptr(y), B, D, N, _dtype_code(u), _dtype_code(y),
-        FLAG_DELTA_B if delta_b else 0, _stream(dev, stream))
+        (FLAG_DELTA_B if delta_b else 0) | (FLAG_ACCURATE_EXPM1 if accurate_expm1 else 0),
+        _stream(dev, stream))
     if st != 0:
         raise MambaError(st, "mamba_state_update")
     return y

@@ -235,7 +235,8 @@ int mamba_state_update(float* state, const void* u, const void* delta, const voi
   p.state = state; p.u = u; p.delta = delta; p.z = z; p.Bt = Bt; p.Ct = Ct;
   p.A = A; p.Dskip = Dskip; p.bias = delta_bias; p.y = y;
   p.B = B; p.D = D; p.N = N;
-  p.accurate = 1;
+  p.inv_d = 1.0 / (double)D;
+  p.accurate = 1;   // the step is bound by state traffic: always the cancellation-free form
   p.delta_b = (flags & MAMBA_FLAG_DELTA_B) ? 1 : 0;
   const Dt in = in_dtype == MAMBA_BF16 ? Dt::BF16 : Dt::F32;
   const Dt out = out_dtype == MAMBA_BF16 ? Dt::BF16 : Dt::F32;

@@ -60,6 +60,7 @@ struct UpdateParams {
   const float* bias;
   void* y;
   int64_t B, D, N;
+  double inv_d;    // 1.0 / D
   int accurate;
   int delta_b;
 };

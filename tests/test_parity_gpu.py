@@ -100,6 +100,74 @@ def test_decode48_layers_0_and_47(dev):
         assert e <= 1e-5
 
 
+# ----------------------------------------------------------------------------- decode options
+DECODE_CASES = [
+    # B, D, N, dtype, out, opts
+    (3, 100, 16, "bf16", "bf16", {}),                      # ragged B*D: last workgroup partly idle
+    (2, 70, 16, "f32", "f32", {}),
+    (2, 64, 16, "bf16", "f32", {"delta_b": True}),
+    (2, 64, 16, "bf16", "bf16", {"zero_A": True}),
+    (2, 64, 16, "bf16", "bf16", {"accurate": True}),
+    (2, 50, 7, "bf16", "bf16", {}),                        # N != 16: general kernel
+    (2, 64, 16, "bf16", "bf16", {"misaligned_bc": True}),  # B_t / C_t not 8-byte aligned: general kernel
+    (1, 33, 16, "f32", "f32", {"no_z": True, "no_dskip": True, "no_bias": True}),
+    (1, 1, 1, "f32", "f32", {}),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=lambda c: "B%dD%dN%d_%s_%s_%s" % (
+    c[0], c[1], c[2], c[3], c[4], "-".join(sorted(c[5])) or "plain"))
+def test_decode_options(case, dev):
+    """Three consecutive decoding steps against the oracle, state carried."""
+    import torch
+    import oracle
+    import selective_state_space_75_amd as m
+    B, D, N, dt, odt, opts = case
+    log("[decode] %s" % (case,))
+    steps = 3
+    x = W.custom_scan_inputs(B, D, N, steps, dt, seed=9100 + B * 17 + D * 3 + N)
+    A = x["A"].copy()
+    if opts.get("zero_A"):
+        A[::3, 1] = 0.0
+        A[1::5, 4] = 1e-45
+    rng = np.random.default_rng(9200 + D)
+    st0 = (0.1 * rng.standard_normal((B, D, N))).astype(np.float32)
+    state = to_dev(st0, dev).contiguous()
+    ref_state = st0.astype(np.float64)
+    A_d = to_dev(A, dev)
+    Ds = None if opts.get("no_dskip") else to_dev(x["Dskip"], dev)
+    bias = None if opts.get("no_bias") else to_dev(x["delta_bias"], dev)
+    out_dtype = torch.float32 if odt == "f32" else torch.bfloat16
+    ys_g, ys_r = [], []
+    for i in range(steps):
+        step = {k: np.ascontiguousarray(x[k][..., i]) for k in ("u", "delta_raw", "z", "Bt", "Ct")}
+        td = {k: to_dev(v, dev) for k, v in step.items()}
+        if opts.get("misaligned_bc"):
+            for k in ("Bt", "Ct"):
+                buf = torch.empty(B * N + 1, dtype=td[k].dtype, device=dev)
+                v = buf[1:].view(B, N)
+                v.copy_(td[k])
+                td[k] = v
+        z = None if opts.get("no_z") else td["z"]
+        y = m.state_update(state, td["u"], td["delta_raw"], z, td["Bt"], td["Ct"], A_d, Ds, bias,
+                           out_dtype=out_dtype, delta_b=opts.get("delta_b", False),
+                           accurate_expm1=opts.get("accurate", False))
+        ys_g.append(from_dev(y))
+        yr, ref_state = oracle.state_update(
+            ref_state, f64(step["u"]), f64(step["delta_raw"]), None if opts.get("no_z") else f64(step["z"]),
+            f64(step["Bt"]), f64(step["Ct"]), A.astype(np.float64),
+            None if opts.get("no_dskip") else x["Dskip"].astype(np.float64),
+            None if opts.get("no_bias") else x["delta_bias"].astype(np.float64),
+            discretization="delta_b" if opts.get("delta_b") else "zoh")
+        ys_r.append(yr)
+    torch.cuda.synchronize()
+    bf16 = dt == "bf16" or odt == "bf16"
+    assert_close(np.stack(ys_g), np.stack(ys_r), bf16, "decode y")
+    e = rel_l2(from_dev(state), ref_state)
+    log("  decode state rel_l2=%.3e" % e)
+    assert e <= 1e-5
+
+
 # ----------------------------------------------------------------------------- ragged shapes and options
 CASES = [
     # B, D, N, L, dtype, out, chunks, opts
