@@ -44,6 +44,9 @@ OPS_PER_UPDATE = 7
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_mamba2.8b_layer_traffic.txt")
 SCAN_SOURCES = ["selective_state_space_75_amd/csrc/scan_v4.hip", "selective_state_space_75_amd/csrc/kernels.hpp",
                 "selective_state_space_75_amd/csrc/device_math.hpp", "selective_state_space_75_amd/csrc/abi.hip"]
+DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "state_update_decode48_traffic.txt")
+DECODE_SOURCES = ["selective_state_space_75_amd/csrc/state_update.hip", "selective_state_space_75_amd/csrc/kernels.hpp",
+                  "selective_state_space_75_amd/csrc/device_math.hpp", "selective_state_space_75_amd/csrc/abi.hip"]
 
 
 def log(msg):
@@ -89,19 +92,19 @@ def cpu_baseline_scan(cfg, x, seconds: float):
             "elems_per_s": round(cfg.elements / t, 1)}
 
 
-def recorded_traffic():
+def recorded_traffic(path=TRAFFIC_FILE, sources=SCAN_SOURCES):
     """(bytes per launch, note) from the committed counter summary, or (None,
     reason) when it is missing or the kernel sources changed since."""
     import hashlib
-    if not os.path.exists(TRAFFIC_FILE):
+    if not os.path.exists(path):
         return None, "no counter summary"
     kv = {}
-    for line in open(TRAFFIC_FILE, encoding="utf-8"):
+    for line in open(path, encoding="utf-8"):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
     h = hashlib.sha256()
-    for f in SCAN_SOURCES:
+    for f in sources:
         h.update(open(os.path.join(ROOT, f), "rb").read())
     if kv.get("source_sha256") != h.hexdigest():
         return None, "kernel changed since the counters were taken"
@@ -234,6 +237,7 @@ def bench_decode(args, dev):
     total = per_ls * cfg.layers * steps
     gbs = total / (wall) / 1e9
     kern_us = gpu_ms * 1e3 / (cfg.layers * steps)
+    traffic, traffic_note = recorded_traffic(DECODE_TRAFFIC_FILE, DECODE_SOURCES)
     line = {
         "metric": "decode state-update HBM GB/s, 48 layers x 128 steps (B=128, D=4096, N=16)",
         "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": args.warmup,
@@ -246,7 +250,8 @@ def bench_decode(args, dev):
         "layer_step_us_mean": round(kern_us, 3),
         "roofline": {"bound": "hbm", "achieved": round(per_ls / (kern_us * 1e-6) / 1e9, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(per_ls / (kern_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                     "traffic": None, "bytes_per_layer_step": per_ls},
+                     "traffic": traffic, "traffic_note": traffic_note, "bytes_per_layer_step": per_ls,
+                     "launch_time": "graph replay time / launches (inter-kernel gaps included)"},
     }
     return line
 
