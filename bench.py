@@ -92,10 +92,23 @@ def cpu_baseline_scan(cfg, x, seconds: float):
             "elems_per_s": round(cfg.elements / t, 1)}
 
 
+def source_digest(files):
+    """sha256 over the sources with comments and whitespace removed, so that
+    only a change of the code itself invalidates a recorded measurement."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for f in files:
+        src = open(os.path.join(ROOT, f), encoding="utf-8").read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", "", src)
+        h.update(re.sub(r"\s+", "", src).encode())
+    return h.hexdigest()
+
+
 def recorded_traffic(path=TRAFFIC_FILE, sources=SCAN_SOURCES):
     """(bytes per launch, note) from the committed counter summary, or (None,
     reason) when it is missing or the kernel sources changed since."""
-    import hashlib
     if not os.path.exists(path):
         return None, "no counter summary"
     kv = {}
@@ -103,10 +116,7 @@ def recorded_traffic(path=TRAFFIC_FILE, sources=SCAN_SOURCES):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    h = hashlib.sha256()
-    for f in sources:
-        h.update(open(os.path.join(ROOT, f), "rb").read())
-    if kv.get("source_sha256") != h.hexdigest():
+    if kv.get("source_sha256") != source_digest(sources):
         return None, "kernel changed since the counters were taken"
     return int(kv["hbm_bytes_per_launch"]), kv.get("summary", "")
 

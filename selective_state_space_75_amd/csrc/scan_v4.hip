@@ -8,12 +8,14 @@
 //    per channel, each lane holding 4 of the 16 states in VGPRs;
 //  * the readout sum over the 16 states is 4 in-lane FMAs plus two DPP adds
 //    across the quad;
-//  * the sequence is walked in 32-step chunks.  Each chunk's u, delta_raw, z
-//    and B_t, C_t are loaded with coalesced 16-byte loads one chunk ahead,
-//    then staged in the wave's own LDS region (delta = softplus(delta_raw +
-//    bias) once per element; u and delta channel-major, B_t and C_t
-//    step-major so that a lane reads its 4 states of B or C with one 16-byte
-//    LDS read);
+//  * the sequence is walked in 32-step chunks.  A lane loads u, delta_raw, z
+//    of its channel for 8 consecutive steps (8g .. 8g+7) with one 16-byte
+//    load each, two chunks ahead; delta = softplus(delta_raw + bias) is
+//    evaluated once per element, and u and delta stay in VGPRs: step t reads
+//    them from lane t/8 of the quad through a DPP broadcast folded into the
+//    consuming instruction.  B_t and C_t of a chunk are staged step-major in
+//    the wave's own double-buffered LDS region, so a lane reads its 4 states
+//    of B or C with one 16-byte LDS read;
 //  * lane g of a quad keeps the outputs of steps 8g..8g+7, adds D u, applies
 //    the gate and writes them with one 16-byte store;
 //  * workgroups are single waves, so no workgroup barrier is ever needed.
