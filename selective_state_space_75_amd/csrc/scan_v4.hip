@@ -39,9 +39,12 @@ constexpr int kNS = 4;        // states per lane
 constexpr int kCT = 32;       // steps per chunk
 constexpr int kSlot = kTile * 16;   // floats per hand-over slot
 
+constexpr int kPRow = 36;     // floats per lane row of the readout transpose (32 + padding)
+
 struct WaveLds {
   float4 B4[2][kCT * 4];      // B_t, [buffer][step][state quad] (16-byte reads of 4 states)
   float4 C4[2][kCT * 4];      // C_t, same layout
+  float P[64 * kPRow];        // per-lane partial readouts of one chunk, [lane][step]
 };
 
 template <bool kBF16> struct Raw8;   // 8 consecutive elements
@@ -137,15 +140,25 @@ struct ChunkRaw {
 // barriers; the wave's LDS accesses are processed in order).  While the 32
 // steps of chunk k run, the wave also
 //   * has the global loads of chunk k+2 in flight,
-//   * evaluates softplus for chunk k+1 and stages its B_t/C_t in the other
-//     LDS buffer,
-//   * finishes chunk k-1's outputs (skip term, gate) -- stored after the steps,
+//   * unpacks chunk k+1 (softplus of delta, u, the gate of z) and stages its
+//     B_t/C_t in the other LDS buffer,
+//   * finishes chunk k-1's outputs (sum of the quad's partial readouts, skip
+//     term, gate) -- stored after the steps,
 // so that independent work fills the latency of the recurrence.  Inside the
 // chunk, B/C of step t+2 are read, the state-independent part of step t+1 is
-// computed, step t updates h, and the quad sum of step t-1 is completed.
-// Prefetch addresses past the segment are clamped to its last chunk, so the
-// step loop has no branches.
-template <bool kInBF16, bool kOutBF16, bool kReadout>
+// computed and step t updates h and forms this lane's partial readout
+// (4 states).  After the steps the 32 partials go through LDS to the lane
+// that owns each step's output (lane g owns steps 8g .. 8g+7), and the first
+// step of chunk k+1 is prepared.
+//
+// Every per-chunk buffer alternates between two copies, selected by the
+// chunk's parity, and the chunk loop is unrolled twice, so nothing is copied
+// between chunks.  Prefetch addresses past the segment are clamped to its
+// last chunk, so the step loop has no branches.
+//
+// kN16: N == 16.  Then every B/C lane holds a real state and all loads are
+// unconditional; otherwise lanes of absent states load zeros.
+template <bool kInBF16, bool kOutBF16, bool kReadout, bool kN16>
 struct Segment {
   static __device__ __forceinline__ float run(const ScanParams& p, WaveLds& s, int64_t b, int64_t d0,
                                               int64_t t_begin, int64_t t_end, float (&h)[kNS], const Consts& k,
@@ -155,10 +168,12 @@ struct Segment {
     const int64_t D = p.D, N = p.N, L = p.L;
     const int64_t d = d0 + c;
     const bool c_ok = d < D;
+    // Channels past D read channel 0 (always in bounds); their delta is forced
+    // to 0 below, so their state stays 0, and their outputs are not stored.
     const int64_t row = (b * D + (c_ok ? d : 0)) * L;
     // B/C staging role: lanes 0..31 -> B, 32..63 -> C; state bc_n, steps 16*bc_h .. +15
     const int bc_arr = lane >> 5, bc_n = (lane >> 1) & 15, bc_h = lane & 1;
-    const bool bc_ok = bc_n < N && (kReadout || bc_arr == 0);
+    const bool bc_ok = kN16 || (bc_n < N && (kReadout || bc_arr == 0));
     const void* bc_base = bc_arr ? p.Ct : p.Bt;
     const int64_t bc_row = (b * N + (bc_n < N ? bc_n : 0)) * L;
     const bool want_z = kReadout && p.z != nullptr;
@@ -169,9 +184,9 @@ struct Segment {
 
     auto fetch = [&](int64_t t0, ChunkRaw<kInBF16>& r) {
       t0 = t0 < t_last ? t0 : t_last;     // clamp: stays inside the segment
-      r.u = load8<kInBF16>(p.u, row + t0 + 8 * g, c_ok);
-      r.d = load8<kInBF16>(p.delta, row + t0 + 8 * g, c_ok);
-      if (want_z) r.z = load8<kInBF16>(p.z, row + t0 + 8 * g, c_ok);
+      r.u = load8<kInBF16>(p.u, row + t0 + 8 * g, true);
+      r.d = load8<kInBF16>(p.delta, row + t0 + 8 * g, true);
+      if (want_z) r.z = load8<kInBF16>(p.z, row + t0 + 8 * g, true);
       r.bc0 = load8<kInBF16>(bc_base, bc_row + t0 + 16 * bc_h, bc_ok);
       r.bc1 = load8<kInBF16>(bc_base, bc_row + t0 + 16 * bc_h + 8, bc_ok);
     };
@@ -190,91 +205,110 @@ struct Segment {
       const float gz = silu(at8<kInBF16>(z, j));
       return want_z ? gz : 1.0f;
     };
+    auto store_out = [&](int64_t t0, const float (&o)[8]) {
+      const int64_t at = row + t0 + 8 * g;
+      if constexpr (kOutBF16) {
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.y) + at) =
+            make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                       pack_bf16x2(o[6], o[7]));
+      } else {
+        float4* q4 = reinterpret_cast<float4*>(static_cast<float*>(p.y) + at);
+        q4[0] = make_float4(o[0], o[1], o[2], o[3]);
+        q4[1] = make_float4(o[4], o[5], o[6], o[7]);
+      }
+    };
 
     float dsum = 0.0f;
-    ChunkRaw<kInBF16> rc, r1, r2;     // raw inputs of chunks ck, ck+1, ck+2
-    float dcur[8], ucur[8];           // delta and u of chunk ck, steps 8g .. 8g+7 of this lane
-    float yo[8];                      // readout sums of chunk ck-1 (this lane's steps)
-    Raw8<kInBF16> uo, zo;             // u and z of chunk ck-1
-    fetch(t_begin, rc);
-    fetch(t_begin + kCT, r1);
+    ChunkRaw<kInBF16> raw[2];          // raw inputs, chunk parity
+    float dv[2][8], uv[2][8], gv[2][8];  // delta, u, gate of this lane's steps 8g..8g+7, chunk parity
+    float q[32];                       // partial readouts of the previous chunk, q[8*g' + j]:
+                                       // lane g' of the quad, step 8g + j
+
+    fetch(t_begin, raw[0]);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      dcur[j] = delta_of(rc, j);
-      ucur[j] = at8<kInBF16>(rc.u, j);
-      stage_bc(rc, 0, j);
-      yo[j] = 0.0f;
+      dv[0][j] = delta_of(raw[0], j);
+      uv[0][j] = at8<kInBF16>(raw[0].u, j);
+      if constexpr (kReadout) gv[0][j] = gate_of(raw[0].z, j);
+      stage_bc(raw[0], 0, j);
     }
-    uo = rc.u;
-    zo = rc.z;
+    fetch(t_begin + kCT, raw[1]);
+#pragma unroll
+    for (int j = 0; j < 32; ++j) q[j] = 0.0f;
 
     auto pipeline = [&](auto mode_tag) {
       constexpr int M = decltype(mode_tag)::kValue;
-      for (int64_t ck = 0; ck < nck; ++ck) {
+      // state-independent part of a step: Abar and Bbar u for this lane's 4 states
+      auto pre = [&](float dt, float ut, const float4& B, float (&e)[kNS], float (&in)[kNS]) {
+        const float bn[4] = {B.x, B.y, B.z, B.w};
+#pragma unroll
+        for (int i = 0; i < kNS; ++i) {
+          const float x = dt * k.a2[i];
+          e[i] = hw_exp2(x);
+          if constexpr (M == kDeltaB) {
+            in[i] = (dt * ut) * bn[i];
+          } else {
+            const float kc = (M == kZohFast) ? __builtin_fmaf(e[i], k.ia[i], -k.ia[i])
+                                             : expm1_from_exp2(x, e[i]) * k.ia[i];
+            in[i] = kc * (ut * bn[i]);
+          }
+        }
+      };
+      float4 Bn0, Bn1, Cn0, Cn1;      // B/C of steps 0 and 1 of the coming chunk
+      float evn[kNS], invn[kNS];      // its step 0, prepared
+      auto prepare_next = [&](int buf, auto pc) {
+        constexpr int Pn = decltype(pc)::kValue;
+        Bn0 = s.B4[buf][0 * 4 + g];
+        Bn1 = s.B4[buf][1 * 4 + g];
+        if constexpr (kReadout) {
+          Cn0 = s.C4[buf][0 * 4 + g];
+          Cn1 = s.C4[buf][1 * 4 + g];
+        }
+        pre(quad_bcast<0>(dv[Pn][0]), quad_bcast<0>(uv[Pn][0]), Bn0, evn, invn);
+      };
+      prepare_next(0, ModeTag<0>{});
+
+      auto chunk = [&](auto ptag, int64_t ck) {
+        constexpr int P = decltype(ptag)::kValue;
+        constexpr int Q = P ^ 1;
         const int64_t t0 = t_begin + ck * kCT;
-        const int buf = (int)(ck & 1);
-        fetch(t0 + 2 * kCT, r2);
+        fetch(t0 + 2 * kCT, raw[P]);            // chunk ck+2 has the parity of ck
         if constexpr (!kReadout) {
 #pragma unroll
-          for (int j = 0; j < 8; ++j) dsum += dcur[j];
+          for (int j = 0; j < 8; ++j) dsum += dv[P][j];
         }
-        float dnext[8], unext[8], o[8], yk[8];
         float4 Bv[kCT], Cv[kCT];
         float ev[2][kNS], inv[2][kNS];
-        float accp = 0.0f;
-        const float4* B4 = s.B4[buf];
-        const float4* C4 = s.C4[buf];
-        auto load = [&](int t) {
-          Bv[t] = B4[t * 4 + g];
-          if constexpr (kReadout) Cv[t] = C4[t * 4 + g];
-        };
-        auto pre = [&](auto tc) {   // state-independent part of step t
-          constexpr int t = decltype(tc)::kValue;
-          const float dt = quad_bcast<t / 8>(dcur[t % 8]);
-          const float ut = quad_bcast<t / 8>(ucur[t % 8]);
-          const float bn[4] = {Bv[t].x, Bv[t].y, Bv[t].z, Bv[t].w};
+        float pt[4], o[8];
+        float4* row_w = reinterpret_cast<float4*>(&s.P[lane * kPRow]);
+        const float4* B4 = s.B4[P];
+        const float4* C4 = s.C4[P];
+        Bv[0] = Bn0; Bv[1] = Bn1;
+        if constexpr (kReadout) { Cv[0] = Cn0; Cv[1] = Cn1; }
 #pragma unroll
-          for (int i = 0; i < kNS; ++i) {
-            const float x = dt * k.a2[i];
-            const float e = hw_exp2(x);
-            float in;
-            if constexpr (M == kDeltaB) {
-              in = (dt * ut) * bn[i];
-            } else {
-              const float kc = (M == kZohFast) ? __builtin_fmaf(e, k.ia[i], -k.ia[i])
-                                               : expm1_from_exp2(x, e) * k.ia[i];
-              in = kc * (ut * bn[i]);
-            }
-            ev[t & 1][i] = e;
-            inv[t & 1][i] = in;
-          }
-        };
-        auto finish = [&](auto tc, float a) {   // quad sum of step t, kept by lane t/8
-          constexpr int t = decltype(tc)::kValue;
-          const float y = quad_sum(a);
-          yk[t % 8] = (g == t / 8) ? y : yk[t % 8];
-        };
-#pragma unroll
-        for (int j = 0; j < 8; ++j) yk[j] = 0.0f;
-        load(0);
-        load(1);
-        pre(ModeTag<0>{});
+        for (int i = 0; i < kNS; ++i) { ev[0][i] = evn[i]; inv[0][i] = invn[i]; }
         static_for<0, kCT>([&](auto tc) {
           constexpr int t = decltype(tc)::kValue;
-          // independent work of the neighbouring chunks, one item every 4 steps
-          if constexpr (t % 4 == 0) {
-            constexpr int j = t / 4;
-            dnext[j] = delta_of(r1, j);
-            unext[j] = at8<kInBF16>(r1.u, j);
-            stage_bc(r1, buf ^ 1, j);
+          constexpr int j = t / 4;
+          // independent work of the neighbouring chunks, two items every 4 steps
+          if constexpr (kReadout && t % 4 == 1) {   // output j of chunk ck-1 (parity Q)
+            const float y = (q[j] + q[8 + j]) + (q[16 + j] + q[24 + j]);
+            o[j] = __builtin_fmaf(k.dskip, uv[Q][j], y) * gv[Q][j];
           }
-          if constexpr (kReadout && t % 4 == 2) {
-            constexpr int j = t / 4;
-            o[j] = __builtin_fmaf(k.dskip, at8<kInBF16>(uo, j), yo[j]) * gate_of(zo, j);
+          if constexpr (t % 4 == 3) {               // unpack chunk ck+1 (parity Q) after that use
+            dv[Q][j] = delta_of(raw[Q], j);
+            uv[Q][j] = at8<kInBF16>(raw[Q].u, j);
+            if constexpr (kReadout) gv[Q][j] = gate_of(raw[Q].z, j);
+            stage_bc(raw[Q], Q, j);
           }
           // the recurrence
-          if constexpr (t + 2 < kCT) load(t + 2);
-          if constexpr (t + 1 < kCT) pre(ModeTag<t + 1>{});
+          if constexpr (t + 2 < kCT) {
+            Bv[t + 2] = B4[(t + 2) * 4 + g];
+            if constexpr (kReadout) Cv[t + 2] = C4[(t + 2) * 4 + g];
+          }
+          if constexpr (t + 1 < kCT)
+            pre(quad_bcast<(t + 1) / 8>(dv[P][(t + 1) % 8]), quad_bcast<(t + 1) / 8>(uv[P][(t + 1) % 8]),
+                Bv[t + 1], ev[(t + 1) & 1], inv[(t + 1) & 1]);
           float acc = 0.0f;
 #pragma unroll
           for (int i = 0; i < kNS; ++i) {
@@ -285,59 +319,46 @@ struct Segment {
             }
           }
           if constexpr (kReadout) {
-            if constexpr (t > 0) finish(ModeTag<t - 1>{}, accp);
-            accp = acc;
+            pt[t % 4] = acc;
+            if constexpr (t % 4 == 3) row_w[t / 4] = make_float4(pt[0], pt[1], pt[2], pt[3]);
           }
         });
+        prepare_next(Q, ModeTag<Q>{});
         if constexpr (kReadout) {
-          finish(ModeTag<kCT - 1>{}, accp);
-          // outputs of chunk ck-1
-          if (ck > 0 && c_ok) {
-            const int64_t at = row + t0 - kCT + 8 * g;
-            if constexpr (kOutBF16) {
-              *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.y) + at) =
-                  make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
-                             pack_bf16x2(o[6], o[7]));
-            } else {
-              float4* q = reinterpret_cast<float4*>(static_cast<float*>(p.y) + at);
-              q[0] = make_float4(o[0], o[1], o[2], o[3]);
-              q[1] = make_float4(o[4], o[5], o[6], o[7]);
-            }
+          if (ck > 0 && c_ok) store_out(t0 - kCT, o);
+          // partial readouts (written every 4 steps) to the lanes that own the steps
+#pragma unroll
+          for (int gs = 0; gs < 4; ++gs) {
+            const float4* row_r = reinterpret_cast<const float4*>(&s.P[(4 * c + gs) * kPRow + 8 * g]);
+            const float4 lo = row_r[0], hi = row_r[1];
+            q[8 * gs + 0] = lo.x; q[8 * gs + 1] = lo.y; q[8 * gs + 2] = lo.z; q[8 * gs + 3] = lo.w;
+            q[8 * gs + 4] = hi.x; q[8 * gs + 5] = hi.y; q[8 * gs + 6] = hi.z; q[8 * gs + 7] = hi.w;
           }
-#pragma unroll
-          for (int j = 0; j < 8; ++j) yo[j] = yk[j];
-          uo = rc.u;
-          zo = rc.z;
         }
-        // rotate the pipeline
+      };
+      auto finish_last = [&](auto ptag) {   // outputs of the segment's last chunk
+        constexpr int P = decltype(ptag)::kValue;
+        if constexpr (kReadout) {
+          float o[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) { dcur[j] = dnext[j]; ucur[j] = unext[j]; }
-        rc = r1;
-        r1 = r2;
+          for (int j = 0; j < 8; ++j) {
+            const float y = (q[j] + q[8 + j]) + (q[16 + j] + q[24 + j]);
+            o[j] = __builtin_fmaf(k.dskip, uv[P][j], y) * gv[P][j];
+          }
+          if (c_ok) store_out(t_end - kCT, o);
+        }
+      };
+      for (int64_t ck = 0;; ck += 2) {
+        chunk(ModeTag<0>{}, ck);
+        if (ck + 1 >= nck) { finish_last(ModeTag<0>{}); break; }
+        chunk(ModeTag<1>{}, ck + 1);
+        if (ck + 2 >= nck) { finish_last(ModeTag<1>{}); break; }
       }
     };
     if (mode == kZohFast) pipeline(ModeTag<kZohFast>{});
     else if (mode == kZohAccurate) pipeline(ModeTag<kZohAccurate>{});
     else pipeline(ModeTag<kDeltaB>{});
 
-    if constexpr (kReadout) {
-      // outputs of the last chunk
-      float o[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) o[j] = __builtin_fmaf(k.dskip, at8<kInBF16>(uo, j), yo[j]) * gate_of(zo, j);
-      if (c_ok) {
-        const int64_t at = row + t_end - kCT + 8 * g;
-        if constexpr (kOutBF16) {
-          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.y) + at) =
-              make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
-                         pack_bf16x2(o[6], o[7]));
-        } else {
-          float4* q = reinterpret_cast<float4*>(static_cast<float*>(p.y) + at);
-          q[0] = make_float4(o[0], o[1], o[2], o[3]);
-          q[1] = make_float4(o[4], o[5], o[6], o[7]);
-        }
-      }
-    }
     if constexpr (!kReadout) dsum = quad_sum(dsum);
     __syncthreads();   // the next segment restages the LDS buffers
     return dsum;
@@ -416,7 +437,7 @@ __device__ __forceinline__ Range balanced_range(const ScanParams& p, const V2Par
 
 enum SegKind : int { kPlain = 0, kHead = 1, kWhole = 2, kTail = 3 };
 
-template <bool kInBF16, bool kOutBF16, bool kSummary>
+template <bool kInBF16, bool kOutBF16, bool kSummary, bool kN16>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void scan_v4_kernel(ScanParams p, V2Params q) {
   __shared__ WaveLds s;
   const int lane = threadIdx.x & 63;
@@ -424,8 +445,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   const int64_t D = p.D, N = p.N, L = p.L;
   const int64_t tiles_d = (D + kTile - 1) / kTile;
   const int64_t tiles = p.B * tiles_d;
-  using Full = Segment<kInBF16, kOutBF16, true>;
-  using StateOnly = Segment<kInBF16, kOutBF16, false>;
+  using Full = Segment<kInBF16, kOutBF16, true, kN16>;
+  using StateOnly = Segment<kInBF16, kOutBF16, false, kN16>;
 
   Range w{};
   int nseg = 1;
@@ -493,12 +514,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 
 template <bool kInBF16, bool kOutBF16, bool kSummary>
 hipError_t launch_t(const ScanParams& p, const V2Params& q, hipStream_t st) {
+  auto kern = p.N == 16 ? scan_v4_kernel<kInBF16, kOutBF16, kSummary, true>
+                        : scan_v4_kernel<kInBF16, kOutBF16, kSummary, false>;
   const int64_t tiles = p.B * ((p.D + kTile - 1) / kTile);
   int64_t grid;
   if (q.balanced) grid = q.groups;
   else grid = (kSummary ? p.n_chunks - 1 : p.n_chunks) * tiles;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((scan_v4_kernel<kInBF16, kOutBF16, kSummary>), dim3((unsigned)grid), dim3(64), 0, st, p, q);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64), 0, st, p, q);
   return hipGetLastError();
 }
 
