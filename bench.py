@@ -42,7 +42,8 @@ OPS_PER_UPDATE = 7
 # WRITE_SIZE, scaled by the same counters on a plain copy of known size); used
 # only while the kernel sources still hash to the recorded value.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_mamba2.8b_layer_traffic.txt")
-SCAN_SOURCES = ["selective_state_space_75_amd/csrc/scan_v4.hip", "selective_state_space_75_amd/csrc/kernels.hpp",
+SCAN_SOURCES = ["selective_state_space_75_amd/csrc/scan_v4.hpp", "selective_state_space_75_amd/csrc/scan_v4_bf16.hip",
+                "selective_state_space_75_amd/csrc/scan_v4_f32.hip", "selective_state_space_75_amd/csrc/kernels.hpp",
                 "selective_state_space_75_amd/csrc/device_math.hpp", "selective_state_space_75_amd/csrc/abi.hip"]
 DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "state_update_decode48_traffic.txt")
 DECODE_SOURCES = ["selective_state_space_75_amd/csrc/state_update.hip", "selective_state_space_75_amd/csrc/kernels.hpp",

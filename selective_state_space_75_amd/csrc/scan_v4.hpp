@@ -1,13 +1,15 @@
-// scan_v4.hip -- main selective-scan kernel for gfx950 (L a multiple of 32,
-// 16-byte aligned rows).  Computes what scan_fwd.hip computes ("Mamba 模型",
+// scan_v4.hpp -- main selective-scan kernel for gfx950 (L a multiple of 32,
+// 16-byte aligned rows).  Included by scan_v4_bf16.hip and scan_v4_f32.hip,
+// which instantiate it for one input dtype each (they compile in parallel).  Computes what scan_fwd.hip computes ("Mamba 模型",
 // full-step flowchart nodes H to M; ZOH per "Mamba模型：高效序列建模的新突破"
 // 3.1): softplus step, ZOH discretisation, recurrence, readout, skip, gate.
 //
 // Layout on the GPU -- one wave is a whole, independent unit of work:
 //  * a wave owns a tile of 16 channels of one batch row; four lanes (a quad)
 //    per channel, each lane holding 4 of the 16 states in VGPRs;
-//  * the readout sum over the 16 states is 4 in-lane FMAs plus two DPP adds
-//    across the quad;
+//  * the readout sum over the 16 states is 4 in-lane FMAs per step; the
+//    quad's partial sums go through LDS once per chunk to the lane that owns
+//    the step (3 adds per output);
 //  * the sequence is walked in 32-step chunks.  A lane loads u, delta_raw, z
 //    of its channel for 8 consecutive steps (8g .. 8g+7) with one 16-byte
 //    load each, two chunks ahead; delta = softplus(delta_raw + bias) is
@@ -26,8 +28,10 @@
 // g+1 from the cut to the end (done last, after reading the slot).  The wait
 // is bounded; if it runs out, g+1 recomputes the state at the cut itself, so
 // the kernel always finishes.
-// Per ZOH state update: 6 fp32 VALU + 1 v_exp_f32, plus per step 2 DPP adds
-// and 1 select per lane (for 4 updates).
+// Per ZOH state update: 6 fp32 VALU + 1 v_exp_f32; per 32-step chunk and lane
+// 64 LDS reads of B/C, 16 staging writes, 8 + 8 readout-transpose accesses.
+#pragma once
+
 #include "device_math.hpp"
 #include "kernels.hpp"
 
@@ -111,7 +115,9 @@ __device__ __forceinline__ Consts load_consts(const ScanParams& p, int64_t d, bo
     k.a2[i] = a * kLog2e;
     k.ia[i] = 1.0f / a;
   }
-  k.bias = (d_ok && p.bias) ? p.bias[d] : 0.0f;
+  // -inf for channels past D: their delta is then exactly 0 (softplus(-inf)),
+  // so their state stays 0 whatever they read.
+  k.bias = !d_ok ? -__builtin_inff() : (p.bias ? p.bias[d] : 0.0f);
   k.dskip = (d_ok && p.Dskip) ? p.Dskip[d] : 0.0f;
   k.accurate = (p.accurate || __any(tiny)) ? 1 : 0;
   return k;
@@ -168,8 +174,8 @@ struct Segment {
     const int64_t D = p.D, N = p.N, L = p.L;
     const int64_t d = d0 + c;
     const bool c_ok = d < D;
-    // Channels past D read channel 0 (always in bounds); their delta is forced
-    // to 0 below, so their state stays 0, and their outputs are not stored.
+    // Channels past D read channel 0 (always in bounds); their delta is 0 (bias
+    // -inf), so their state stays 0, and their outputs are not stored.
     const int64_t row = (b * D + (c_ok ? d : 0)) * L;
     // B/C staging role: lanes 0..31 -> B, 32..63 -> C; state bc_n, steps 16*bc_h .. +15
     const int bc_arr = lane >> 5, bc_n = (lane >> 1) & 15, bc_h = lane & 1;
@@ -195,11 +201,10 @@ struct Segment {
       dst[(16 * bc_h + j) * 16 + bc_n] = at8<kInBF16>(r.bc0, j);
       dst[(16 * bc_h + 8 + j) * 16 + bc_n] = at8<kInBF16>(r.bc1, j);
     };
-    // Branch-free (a branch would split the step loop's basic block): the
-    // softplus is always evaluated and then discarded for channels past D.
+    // Channels past D carry bias = -inf, so delta = softplus(-inf) = 0 there
+    // without a per-element select.
     auto delta_of = [&](const ChunkRaw<kInBF16>& r, int j) {
-      const float sp = softplus(at8<kInBF16>(r.d, j) + k.bias);
-      return c_ok ? sp : 0.0f;
+      return softplus(at8<kInBF16>(r.d, j) + k.bias);
     };
     auto gate_of = [&](const Raw8<kInBF16>& z, int j) {
       const float gz = silu(at8<kInBF16>(z, j));
@@ -256,17 +261,20 @@ struct Segment {
       };
       float4 Bn0, Bn1, Cn0, Cn1;      // B/C of steps 0 and 1 of the coming chunk
       float evn[kNS], invn[kNS];      // its step 0, prepared
-      auto prepare_next = [&](int buf, auto pc) {
-        constexpr int Pn = decltype(pc)::kValue;
+      auto read_next = [&](int buf) {
         Bn0 = s.B4[buf][0 * 4 + g];
         Bn1 = s.B4[buf][1 * 4 + g];
         if constexpr (kReadout) {
           Cn0 = s.C4[buf][0 * 4 + g];
           Cn1 = s.C4[buf][1 * 4 + g];
         }
+      };
+      auto pre_next = [&](auto pc) {
+        constexpr int Pn = decltype(pc)::kValue;
         pre(quad_bcast<0>(dv[Pn][0]), quad_bcast<0>(uv[Pn][0]), Bn0, evn, invn);
       };
-      prepare_next(0, ModeTag<0>{});
+      read_next(0);
+      pre_next(ModeTag<0>{});
 
       auto chunk = [&](auto ptag, int64_t ck) {
         constexpr int P = decltype(ptag)::kValue;
@@ -290,6 +298,10 @@ struct Segment {
         static_for<0, kCT>([&](auto tc) {
           constexpr int t = decltype(tc)::kValue;
           constexpr int j = t / 4;
+          // Keep the software pipeline as written: without this fence the
+          // scheduler sinks the B/C reads of step t+2 next to their use and
+          // every step then waits for LDS.
+          __builtin_amdgcn_sched_barrier(0);
           // independent work of the neighbouring chunks, two items every 4 steps
           if constexpr (kReadout && t % 4 == 1) {   // output j of chunk ck-1 (parity Q)
             const float y = (q[j] + q[8 + j]) + (q[16 + j] + q[24 + j]);
@@ -322,8 +334,10 @@ struct Segment {
             pt[t % 4] = acc;
             if constexpr (t % 4 == 3) row_w[t / 4] = make_float4(pt[0], pt[1], pt[2], pt[3]);
           }
+          // step 0 of chunk ck+1 (its B/C were staged at steps 3 and 7)
+          if constexpr (t == kCT - 4) read_next(Q);
+          if constexpr (t == kCT - 2) pre_next(ModeTag<Q>{});
         });
-        prepare_next(Q, ModeTag<Q>{});
         if constexpr (kReadout) {
           if (ck > 0 && c_ok) store_out(t0 - kCT, o);
           // partial readouts (written every 4 steps) to the lanes that own the steps
@@ -527,11 +541,8 @@ hipError_t launch_t(const ScanParams& p, const V2Params& q, hipStream_t st) {
 
 }  // namespace
 
-hipError_t launch_scan_v4(const ScanParams& p, const V2Params& q, Dt in, Dt out, bool summary, hipStream_t s) {
-  if (summary) return in == Dt::BF16 ? launch_t<true, false, true>(p, q, s) : launch_t<false, false, true>(p, q, s);
-  if (in == Dt::BF16)
-    return out == Dt::BF16 ? launch_t<true, true, false>(p, q, s) : launch_t<true, false, false>(p, q, s);
-  return out == Dt::BF16 ? launch_t<false, true, false>(p, q, s) : launch_t<false, false, false>(p, q, s);
-}
+// Launches of one input dtype (defined in scan_v4_bf16.hip / scan_v4_f32.hip).
+hipError_t launch_scan_v4_bf16in(const ScanParams& p, const V2Params& q, Dt out, bool summary, hipStream_t s);
+hipError_t launch_scan_v4_f32in(const ScanParams& p, const V2Params& q, Dt out, bool summary, hipStream_t s);
 
 }  // namespace mamba
