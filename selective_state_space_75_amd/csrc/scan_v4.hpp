@@ -149,7 +149,7 @@ struct ChunkRaw {
 //   * unpacks chunk k+1 (softplus of delta, u, the gate of z) and stages its
 //     B_t/C_t in the other LDS buffer,
 //   * finishes chunk k-1's outputs (sum of the quad's partial readouts, skip
-//     term, gate) -- stored after the steps,
+//     term, gate) in its first half and stores them at step 16,
 // so that independent work fills the latency of the recurrence.  Inside the
 // chunk, B/C of step t+2 are read, the state-independent part of step t+1 is
 // computed and step t updates h and forms this lane's partial readout
@@ -183,6 +183,10 @@ struct Segment {
     const void* bc_base = bc_arr ? p.Ct : p.Bt;
     const int64_t bc_row = (b * N + (bc_n < N ? bc_n : 0)) * L;
     const bool want_z = kReadout && p.z != nullptr;
+    // z is always loaded (from u when there is no gate, then discarded): a
+    // conditional load would leave the compiler unsure how many loads are in
+    // flight, and its waits would then cover the newest prefetch as well.
+    const void* z_src = p.z ? p.z : p.u;
 
     const int64_t nck = (t_end - t_begin) / kCT;
     if (nck <= 0) return 0.0f;
@@ -192,7 +196,7 @@ struct Segment {
       t0 = t0 < t_last ? t0 : t_last;     // clamp: stays inside the segment
       r.u = load8<kInBF16>(p.u, row + t0 + 8 * g, true);
       r.d = load8<kInBF16>(p.delta, row + t0 + 8 * g, true);
-      if (want_z) r.z = load8<kInBF16>(p.z, row + t0 + 8 * g, true);
+      if constexpr (kReadout) r.z = load8<kInBF16>(z_src, row + t0 + 8 * g, true);
       r.bc0 = load8<kInBF16>(bc_base, bc_row + t0 + 16 * bc_h, bc_ok);
       r.bc1 = load8<kInBF16>(bc_base, bc_row + t0 + 16 * bc_h + 8, bc_ok);
     };
@@ -240,6 +244,8 @@ struct Segment {
     fetch(t_begin + kCT, raw[1]);
 #pragma unroll
     for (int j = 0; j < 32; ++j) q[j] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) { uv[1][j] = 0.0f; gv[1][j] = 0.0f; }   // read (unused) by chunk 0
 
     auto pipeline = [&](auto mode_tag) {
       constexpr int M = decltype(mode_tag)::kValue;
@@ -303,11 +309,19 @@ struct Segment {
           // every step then waits for LDS.
           __builtin_amdgcn_sched_barrier(0);
           // independent work of the neighbouring chunks, two items every 4 steps
-          if constexpr (kReadout && t % 4 == 1) {   // output j of chunk ck-1 (parity Q)
-            const float y = (q[j] + q[8 + j]) + (q[16 + j] + q[24 + j]);
-            o[j] = __builtin_fmaf(k.dskip, uv[Q][j], y) * gv[Q][j];
+          if constexpr (kReadout && t % 2 == 1 && t < 16) {   // output t/2 of chunk ck-1 (parity Q)
+            constexpr int jo = t / 2;
+            const float y = (q[jo] + q[8 + jo]) + (q[16 + jo] + q[24 + jo]);
+            o[jo] = __builtin_fmaf(k.dskip, uv[Q][jo], y) * gv[Q][jo];
           }
-          if constexpr (t % 4 == 3) {               // unpack chunk ck+1 (parity Q) after that use
+          // Outputs of chunk ck-1 leave at mid-chunk, long before the next
+          // chunk waits on its loads (stores count in the same counter).  Chunk
+          // 0 has none yet: it writes its own first chunk, which the real
+          // outputs overwrite later (same lane, same address, program order).
+          if constexpr (kReadout && t == 16) {
+            if (c_ok) store_out(ck > 0 ? t0 - kCT : t0, o);
+          }
+          if constexpr (t % 4 == 3) {               // unpack chunk ck+1 (parity Q) after output j
             dv[Q][j] = delta_of(raw[Q], j);
             uv[Q][j] = at8<kInBF16>(raw[Q].u, j);
             if constexpr (kReadout) gv[Q][j] = gate_of(raw[Q].z, j);
@@ -339,7 +353,6 @@ struct Segment {
           if constexpr (t == kCT - 2) pre_next(ModeTag<Q>{});
         });
         if constexpr (kReadout) {
-          if (ck > 0 && c_ok) store_out(t0 - kCT, o);
           // partial readouts (written every 4 steps) to the lanes that own the steps
 #pragma unroll
           for (int gs = 0; gs < 4; ++gs) {
