@@ -146,12 +146,12 @@ struct ChunkRaw {
 // barriers; the wave's LDS accesses are processed in order).  While the 32
 // steps of chunk k run, the wave also
 //   * has the global loads of chunk k+2 in flight,
-//   * unpacks chunk k+1 (softplus of delta, u, the gate of z) and stages its
-//     B_t/C_t in the other LDS buffer,
+//   * unpacks chunk k+1 (softplus of delta, u, the gate of z) in its second
+//     half and stages its B_t/C_t in the other LDS buffer,
 //   * finishes chunk k-1's outputs (sum of the quad's partial readouts, skip
 //     term, gate) in its first half and stores them at step 16,
 // so that independent work fills the latency of the recurrence.  Inside the
-// chunk, B/C of step t+2 are read, the state-independent part of step t+1 is
+// chunk, B/C of step t+3 are read, the state-independent part of step t+1 is
 // computed and step t updates h and forms this lane's partial readout
 // (4 states).  After the steps the 32 partials go through LDS to the lane
 // that owns each step's output (lane g owns steps 8g .. 8g+7), and the first
@@ -265,14 +265,16 @@ struct Segment {
           }
         }
       };
-      float4 Bn0, Bn1, Cn0, Cn1;      // B/C of steps 0 and 1 of the coming chunk
+      float4 Bn0, Bn1, Bn2, Cn0, Cn1, Cn2;   // B/C of steps 0..2 of the coming chunk
       float evn[kNS], invn[kNS];      // its step 0, prepared
       auto read_next = [&](int buf) {
         Bn0 = s.B4[buf][0 * 4 + g];
         Bn1 = s.B4[buf][1 * 4 + g];
+        Bn2 = s.B4[buf][2 * 4 + g];
         if constexpr (kReadout) {
           Cn0 = s.C4[buf][0 * 4 + g];
           Cn1 = s.C4[buf][1 * 4 + g];
+          Cn2 = s.C4[buf][2 * 4 + g];
         }
       };
       auto pre_next = [&](auto pc) {
@@ -297,15 +299,15 @@ struct Segment {
         float4* row_w = reinterpret_cast<float4*>(&s.P[lane * kPRow]);
         const float4* B4 = s.B4[P];
         const float4* C4 = s.C4[P];
-        Bv[0] = Bn0; Bv[1] = Bn1;
-        if constexpr (kReadout) { Cv[0] = Cn0; Cv[1] = Cn1; }
+        Bv[0] = Bn0; Bv[1] = Bn1; Bv[2] = Bn2;
+        if constexpr (kReadout) { Cv[0] = Cn0; Cv[1] = Cn1; Cv[2] = Cn2; }
 #pragma unroll
         for (int i = 0; i < kNS; ++i) { ev[0][i] = evn[i]; inv[0][i] = invn[i]; }
         static_for<0, kCT>([&](auto tc) {
           constexpr int t = decltype(tc)::kValue;
           constexpr int j = t / 4;
           // Keep the software pipeline as written: without this fence the
-          // scheduler sinks the B/C reads of step t+2 next to their use and
+          // scheduler sinks the B/C reads of step t+3 next to their use and
           // every step then waits for LDS.
           __builtin_amdgcn_sched_barrier(0);
           // independent work of the neighbouring chunks, two items every 4 steps
@@ -321,16 +323,20 @@ struct Segment {
           if constexpr (kReadout && t == 16) {
             if (c_ok) store_out(ck > 0 ? t0 - kCT : t0, o);
           }
-          if constexpr (t % 4 == 3) {               // unpack chunk ck+1 (parity Q) after output j
-            dv[Q][j] = delta_of(raw[Q], j);
-            uv[Q][j] = at8<kInBF16>(raw[Q].u, j);
-            if constexpr (kReadout) gv[Q][j] = gate_of(raw[Q].z, j);
-            stage_bc(raw[Q], Q, j);
+          // Unpack chunk ck+1 (parity Q) in the second half: its loads were
+          // issued at the start of chunk ck-1, so they have 1.5 chunks to land,
+          // and output t/2 of chunk ck-1 has already used uv[Q], gv[Q].
+          if constexpr (t >= 17 && t % 2 == 1) {
+            constexpr int ju = (t - 17) / 2;
+            dv[Q][ju] = delta_of(raw[Q], ju);
+            uv[Q][ju] = at8<kInBF16>(raw[Q].u, ju);
+            if constexpr (kReadout) gv[Q][ju] = gate_of(raw[Q].z, ju);
+            stage_bc(raw[Q], Q, ju);
           }
           // the recurrence
-          if constexpr (t + 2 < kCT) {
-            Bv[t + 2] = B4[(t + 2) * 4 + g];
-            if constexpr (kReadout) Cv[t + 2] = C4[(t + 2) * 4 + g];
+          if constexpr (t + 3 < kCT) {
+            Bv[t + 3] = B4[(t + 3) * 4 + g];
+            if constexpr (kReadout) Cv[t + 3] = C4[(t + 3) * 4 + g];
           }
           if constexpr (t + 1 < kCT)
             pre(quad_bcast<(t + 1) / 8>(dv[P][(t + 1) % 8]), quad_bcast<(t + 1) / 8>(uv[P][(t + 1) % 8]),
@@ -348,8 +354,8 @@ struct Segment {
             pt[t % 4] = acc;
             if constexpr (t % 4 == 3) row_w[t / 4] = make_float4(pt[0], pt[1], pt[2], pt[3]);
           }
-          // step 0 of chunk ck+1 (its B/C were staged at steps 3 and 7)
-          if constexpr (t == kCT - 4) read_next(Q);
+          // step 0 of chunk ck+1 (B/C of its steps 0..2 were staged at steps 17..21)
+          if constexpr (t == kCT - 5) read_next(Q);
           if constexpr (t == kCT - 2) pre_next(ModeTag<Q>{});
         });
         if constexpr (kReadout) {
