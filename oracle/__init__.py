@@ -10,7 +10,7 @@ first up-converted to float64, which is exact for the bf16 and fp32 values
 the GPU sees.
 
 Pages followed (titles and sections; each step is cited in ``oracle.c``):
-  "Mamba 模型" (gaos6e.github.io) -- the full-step flowchart, nodes H to M;
+  "Mamba 模型" (gaos6e.github.io) -- the full-step flowchart, nodes E, F and H to M;
   "Mamba 与状态空间模型" (world.lapla.si, plate F56) -- sections 03, 06, 07;
   "Mamba 状态空间模型架构深度解析" (pnsm.cn) -- ZOH, diagonal A;
   "Mamba模型：高效序列建模的新突破" (mhpn.cn) -- section 3.1, ZOH B-bar.
@@ -57,6 +57,10 @@ def _load():
             lib.oracle_scan.restype = ctypes.c_int
             lib.oracle_state_update.argtypes = [i64, i64, i64, dp] + [dp] * 8 + [ctypes.c_int, dp, ctypes.c_int]
             lib.oracle_state_update.restype = ctypes.c_int
+            lib.oracle_conv1d.argtypes = [i64, i64, i64, i64, dp, dp, dp, dp, ctypes.c_int, dp, dp]
+            lib.oracle_conv1d.restype = ctypes.c_int
+            lib.oracle_conv1d_update.argtypes = [i64, i64, i64, dp, dp, dp, dp, ctypes.c_int, dp]
+            lib.oracle_conv1d_update.restype = ctypes.c_int
             lib.oracle_softplus.argtypes = [ctypes.c_double]
             lib.oracle_softplus.restype = ctypes.c_double
             _lib = lib
@@ -143,4 +147,43 @@ def state_update(state, u, delta_raw, z, Bt, Ct, A, Dskip=None, delta_bias=None,
                                      nthreads or default_threads())
     if rc != 0:
         raise RuntimeError("oracle_state_update failed with %d" % rc)
+    return y, st
+
+
+def conv1d(x, w, bias=None, state0=None, activation: bool = True):
+    """Causal depthwise convolution (+ SiLU) over (B, D, L); w is (D, K), tap i
+    multiplies x[t - i].  Returns (y (B,D,L), final_state (B,D,K)), float64."""
+    x = _f64(x)
+    if x.ndim != 3:
+        raise ValueError("x must be (B, D, L)")
+    B, D, L = x.shape
+    w = _f64(w)
+    if w.ndim != 2 or w.shape[0] != D:
+        raise ValueError("w must be (D, K)")
+    K = w.shape[1]
+    bias = _f64(bias, (D,))
+    state0 = _f64(state0, (B, D, K))
+    y = np.empty((B, D, L), dtype=np.float64)
+    fs = np.empty((B, D, K), dtype=np.float64)
+    rc = _load().oracle_conv1d(B, D, L, K, _ptr(x), _ptr(w), _ptr(bias), _ptr(state0), int(activation),
+                               _ptr(y), _ptr(fs))
+    if rc != 0:
+        raise RuntimeError("oracle_conv1d failed with %d" % rc)
+    return y, fs
+
+
+def conv1d_update(state, x, w, bias=None, activation: bool = True):
+    """One decoding step of the convolution.  state (B,D,K) (oldest first), x (B,D).
+    Returns (y (B,D), new_state (B,D,K)) as float64; the input is not modified."""
+    st = np.array(state, dtype=np.float64, copy=True, order="C")
+    if st.ndim != 3:
+        raise ValueError("state must be (B, D, K)")
+    B, D, K = st.shape
+    x = _f64(x, (B, D))
+    w = _f64(w, (D, K))
+    bias = _f64(bias, (D,))
+    y = np.empty((B, D), dtype=np.float64)
+    rc = _load().oracle_conv1d_update(B, D, K, _ptr(st), _ptr(x), _ptr(w), _ptr(bias), int(activation), _ptr(y))
+    if rc != 0:
+        raise RuntimeError("oracle_conv1d_update failed with %d" % rc)
     return y, st

@@ -176,3 +176,73 @@ int oracle_state_update(int64_t B, int64_t D, int64_t N, double* state,
   return oracle_scan(B, D, N, 1, u, delta_raw, z, Bt, Ct, A, Dskip, bias,
                      state, mode, y, state, nthreads);
 }
+
+/* ---------------------------------------------------------------------------
+ * Causal depthwise convolution along the sequence, then SiLU -- the step that
+ * produces the scan input u from the in_proj branch.
+ *
+ *   [P1] "Mamba 模型", flowchart node E (Causal Depthwise Conv1D):
+ *          Uc_t = sum_i W_conv_i * U_(t-i)  -- one filter per channel, only the
+ *          current and earlier positions;
+ *        node F (SiLU):  Xc_t = Uc_t * sigmoid(Uc_t).
+ *   [P3] "Mamba 与状态空间模型", section 03: besides its 16 state numbers each
+ *        channel keeps a short convolution's 4 most recent inputs -- the conv
+ *        state carried from token to token when decoding.
+ *
+ * Readings (listed in the design notes): tap i = 0 multiplies the current
+ * input; positions before the sequence read `state0` (the K inputs before
+ * t = 0, oldest first) or zero when state0 is NULL; an optional per-channel
+ * bias is added before the activation (NULL: none, as in the node formula);
+ * activation 1 = SiLU (the flowchart), 0 = none (used by the pins).
+ *
+ * Layout: x, y (B, D, L); w (D, K) with w[d*K + i] the tap of x[t - i];
+ * bias (D); state0, final_state (B, D, K) with [k] the input at time
+ * L - K + k (final_state) or k - K (state0).
+ */
+int oracle_conv1d(int64_t B, int64_t D, int64_t L, int64_t K, const double* x, const double* w,
+                  const double* bias, const double* state0, int activation, double* y,
+                  double* final_state) {
+  if (B < 0 || D < 0 || L < 0 || K < 1 || !w) return -2;
+  if ((B * D * L > 0) && (!x || !y)) return -1;
+  for (int64_t ch = 0; ch < B * D; ++ch) {
+    const int64_t d = ch % D;
+    const double* xr = x ? x + ch * L : NULL;
+    const double* s0 = state0 ? state0 + ch * K : NULL;
+    const double* wd = w + d * K;
+    /* input at time s (s may be negative: before the sequence) */
+#define ORACLE_CONV_IN(s) ((s) >= 0 ? xr[(s)] : (s0 ? s0[K + (s)] : 0.0))
+    for (int64_t t = 0; t < L; ++t) {
+      double acc = bias ? bias[d] : 0.0;
+      for (int64_t i = 0; i < K; ++i) {
+        const int64_t s = t - i;
+        if (s < -K) break;
+        acc += wd[i] * ORACLE_CONV_IN(s);
+      }
+      y[ch * L + t] = activation ? silu(acc) : acc;
+    }
+    if (final_state) {
+      for (int64_t k = 0; k < K; ++k) {
+        const int64_t s = L - K + k;
+        final_state[ch * K + k] = (s >= -K) ? ORACLE_CONV_IN(s) : 0.0;
+      }
+    }
+#undef ORACLE_CONV_IN
+  }
+  return 0;
+}
+
+/* One decoding step of the convolution: the computation above with L = 1,
+ * starting from `state` (the K most recent inputs, oldest first), which is
+ * replaced in place by the K most recent inputs including x ([P3] section 03).
+ * x, y: (B, D). */
+int oracle_conv1d_update(int64_t B, int64_t D, int64_t K, double* state, const double* x,
+                         const double* w, const double* bias, int activation, double* y) {
+  if (!state || K < 1) return -1;
+  double* next = (double*)malloc(sizeof(double) * (size_t)(B * D * K > 0 ? B * D * K : 1));
+  if (!next) return -3;
+  const int rc = oracle_conv1d(B, D, 1, K, x, w, bias, state, activation, y, next);
+  if (rc == 0)
+    for (int64_t i = 0; i < B * D * K; ++i) state[i] = next[i];
+  free(next);
+  return rc;
+}

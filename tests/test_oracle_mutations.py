@@ -31,6 +31,11 @@ MUTATIONS = {
     "ignores_initial_state": ("h[n] = j->h0 ? j->h0[ch * N + n] : 0.0;", "h[n] = 0.0;"),
     "sigmoid_not_silu": ("return z / (1.0 + exp(-z));", "return 1.0 / (1.0 + exp(-z));"),
     "abar_wrong_sign": ("const double abar = exp(delta * a);", "const double abar = exp(-delta * a);"),
+    "conv_taps_reversed": ("acc += wd[i] * ORACLE_CONV_IN(s);", "acc += wd[K - 1 - i] * ORACLE_CONV_IN(s);"),
+    "conv_reads_future": ("const int64_t s = t - i;", "const int64_t s = (t + i < L) ? t + i : t;"),
+    "conv_drops_bias": ("double acc = bias ? bias[d] : 0.0;", "double acc = 0.0;"),
+    "conv_state_off_by_one": ("(s0 ? s0[K + (s)] : 0.0)", "(s0 ? s0[K - 1 + (s) + ((s) == -K)] : 0.0)"),
+    "conv_final_state_shifted": ("const int64_t s = L - K + k;", "const int64_t s = L - K + k - 1;"),
 }
 
 

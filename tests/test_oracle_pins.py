@@ -336,3 +336,102 @@ def test_page_state_size_arithmetic():
     from selective_state_space_75_amd import workloads as W
     cfg = W.DECODE_CONFIGS["decode48"]
     assert cfg.N == v["mamba_state_per_channel"]
+
+
+# ----------------------------------------------------------------------------- causal depthwise conv1d + SiLU
+# "Mamba 模型", flowchart nodes E (Uc_t = sum_i W_i U_(t-i)) and F (SiLU);
+# "Mamba 与状态空间模型" section 03 (the conv keeps the 4 most recent inputs).
+def _conv_problem(rng, B, D, L, K):
+    return rng.standard_normal((B, D, L)), rng.uniform(-0.5, 0.5, size=(D, K)), rng.uniform(-0.5, 0.5, size=D)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_conv_matches_library_convolution(seed):
+    """Pre-activation output = numpy's full 1-D convolution of each channel with
+    its taps, truncated to the first L outputs (causal), plus the bias."""
+    rng = np.random.default_rng(300 + seed)
+    for K in (1, 2, 3, 4):
+        x, w, b = _conv_problem(rng, 2, 3, 37, K)
+        y, _ = oracle.conv1d(x, w, b, activation=False)
+        ref = np.stack([np.stack([np.convolve(x[i, d], w[d])[:37] + b[d] for d in range(3)]) for i in range(2)])
+        assert rel(y, ref) < 1e-14
+
+
+def test_conv_impulse_response_is_the_taps():
+    rng = np.random.default_rng(310)
+    B, D, L, K, t0 = 1, 4, 20, 4, 6
+    w = rng.uniform(-0.5, 0.5, size=(D, K))
+    x = np.zeros((B, D, L))
+    x[:, :, t0] = 1.0
+    y, _ = oracle.conv1d(x, w, activation=False)
+    for d in range(D):
+        expect = np.zeros(L)
+        expect[t0:t0 + K] = w[d]
+        assert np.array_equal(y[0, d], expect)
+
+
+def test_conv_is_causal():
+    rng = np.random.default_rng(320)
+    x, w, b = _conv_problem(rng, 2, 3, 40, 4)
+    y1, _ = oracle.conv1d(x, w, b)
+    x2 = x.copy()
+    x2[:, :, 25:] += rng.standard_normal((2, 3, 15))
+    y2, _ = oracle.conv1d(x2, w, b)
+    assert np.array_equal(y1[:, :, :25], y2[:, :, :25])
+    assert not np.array_equal(y1[:, :, 25:], y2[:, :, 25:])
+
+
+def test_conv_silu_closed_forms():
+    """With one unit tap and no bias the output is SiLU of the input:
+    silu(0) = 0, silu(x) - silu(-x) = x, silu(ln 3) = (3/4) ln 3, silu -> x."""
+    xs = np.array([0.0, math.log(3.0), -math.log(3.0), 1.5, -1.5, 40.0, -40.0])
+    y, _ = oracle.conv1d(xs.reshape(1, 1, -1), np.ones((1, 1)))
+    y = y[0, 0]
+    assert y[0] == 0.0
+    assert abs(y[1] - 0.75 * math.log(3.0)) < 1e-15
+    assert abs((y[3] - y[4]) - 1.5) < 1e-15 and abs((y[1] - y[2]) - math.log(3.0)) < 1e-15
+    assert abs(y[5] - 40.0) < 1e-15 and abs(y[6]) < 1e-15
+    # against an independent sigmoid (tanh form)
+    r = np.random.default_rng(330).standard_normal(64) * 4
+    y, _ = oracle.conv1d(r.reshape(1, 1, -1), np.ones((1, 1)))
+    assert rel(y[0, 0], np_silu(r)) < 1e-15
+
+
+def test_conv_state_holds_the_last_inputs():
+    rng = np.random.default_rng(340)
+    x, w, b = _conv_problem(rng, 2, 3, 9, 4)
+    _, fs = oracle.conv1d(x, w, b)
+    assert np.array_equal(fs, x[:, :, -4:])
+    _, fs = oracle.conv1d(x[:, :, :2], w, b)          # shorter than the filter: zeros first
+    assert np.array_equal(fs[:, :, :2], np.zeros((2, 3, 2))) and np.array_equal(fs[:, :, 2:], x[:, :, :2])
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_conv_split_equivalence(seed):
+    """conv over L = conv over the first L1, then the rest from the carried
+    state, then token-by-token updates for the tail."""
+    rng = np.random.default_rng(350 + seed)
+    x, w, b = _conv_problem(rng, 2, 5, 30, 4)
+    y, fs = oracle.conv1d(x, w, b)
+    ya, sa = oracle.conv1d(x[:, :, :17], w, b)
+    yb, sb = oracle.conv1d(x[:, :, 17:24], w, b, state0=sa)
+    ys = [ya, yb]
+    st = sb
+    for t in range(24, 30):
+        yt, st = oracle.conv1d_update(st, x[:, :, t], w, b)
+        ys.append(yt[:, :, None])
+    assert rel(np.concatenate(ys, axis=2), y) < 1e-15
+    assert np.array_equal(st, fs)
+
+
+def test_conv_one_tap_is_elementwise_and_linear_in_taps():
+    rng = np.random.default_rng(360)
+    x = rng.standard_normal((1, 3, 12))
+    w1 = rng.uniform(-0.5, 0.5, size=(3, 4))
+    w2 = rng.uniform(-0.5, 0.5, size=(3, 4))
+    ya, _ = oracle.conv1d(x, w1, activation=False)
+    yb, _ = oracle.conv1d(x, w2, activation=False)
+    yc, _ = oracle.conv1d(x, w1 + 2.0 * w2, activation=False)
+    assert rel(yc, ya + 2.0 * yb) < 1e-14
+    y1, _ = oracle.conv1d(x, np.full((3, 1), 2.0), np.full(3, 0.25), activation=False)
+    assert np.array_equal(y1, 2.0 * x + 0.25)
