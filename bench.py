@@ -10,7 +10,9 @@ inputs from an earlier step).  Prints one JSON line.
 
 Other workloads: --workload long_b1 (B=1 D=4096 L=131072, chunked along L),
 mamba130m_layer, tiny_fp32, decode48 (48 layers x 128 steps of
-mamba_state_update at B=128 D=4096, the 48-layer step replayed as a graph).
+mamba_state_update at B=128 D=4096, the 48-layer step replayed as a graph),
+conv_2.8b_layer (causal conv1d + SiLU at B=4 D=5120 L=2048 K=4) and
+conv_decode48 (48 layers x 128 steps of the one-token conv update).
 
 --copy-calibration runs only a plain device copy of known size (used to
 scale rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes).
@@ -46,6 +48,9 @@ SCAN_SOURCES = ["selective_state_space_75_amd/csrc/scan_v4.hpp", "selective_stat
                 "selective_state_space_75_amd/csrc/scan_v4_f32.hip", "selective_state_space_75_amd/csrc/kernels.hpp",
                 "selective_state_space_75_amd/csrc/device_math.hpp", "selective_state_space_75_amd/csrc/abi.hip"]
 DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "state_update_decode48_traffic.txt")
+CONV_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "conv1d_2.8b_layer_traffic.txt")
+CONV_SOURCES = ["selective_state_space_75_amd/csrc/conv1d.hip", "selective_state_space_75_amd/csrc/kernels.hpp",
+                "selective_state_space_75_amd/csrc/device_math.hpp", "selective_state_space_75_amd/csrc/abi.hip"]
 DECODE_SOURCES = ["selective_state_space_75_amd/csrc/state_update.hip", "selective_state_space_75_amd/csrc/kernels.hpp",
                   "selective_state_space_75_amd/csrc/device_math.hpp", "selective_state_space_75_amd/csrc/abi.hip"]
 
@@ -267,6 +272,112 @@ def bench_decode(args, dev):
     return line
 
 
+def bench_conv(args, dev):
+    """Causal conv1d + SiLU over the 2.8B-layer shape; HBM-bound."""
+    import torch
+    import selective_state_space_75_amd as m
+    from selective_state_space_75_amd import workloads as W
+    cfg = W.CONV_CONFIGS[args.workload]
+    log("conv workload %s: B=%d D=%d L=%d K=%d %s" % (cfg.name, cfg.B, cfg.D, cfg.L, cfg.K, cfg.dtype))
+    sets = []
+    for k in range(args.sets):
+        xs = W.conv_inputs(cfg.B, cfg.D, cfg.L, cfg.K, cfg.dtype, cfg.seed + 100 * k)
+        sets.append({n: to_dev(v, dev) for n, v in xs.items()})
+    odt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    ys = [torch.empty((cfg.B, cfg.D, cfg.L), dtype=odt, device=dev) for _ in sets]
+    fss = [torch.empty((cfg.B, cfg.D, cfg.K), dtype=torch.float32, device=dev) for _ in sets]
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        t = sets[i % len(sets)]
+        m.conv1d_fwd(t["x"], t["w"], t["bias"], return_final_state=True, y=ys[i % len(sets)],
+                     final_state=fss[i % len(sets)], stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [a.elapsed_time(b) for a, b in ev]
+    kern_ms = float(np.mean(per))
+    ms_step = wall * 1e3 / args.steps
+    nbytes = cfg.algorithmic_bytes()
+    ach = nbytes / (kern_ms * 1e-3) / 1e9
+    traffic, note = recorded_traffic(CONV_TRAFFIC_FILE, CONV_SOURCES)
+    return {
+        "metric": "causal conv1d + SiLU HBM GB/s (% of MI355X peak) at Mamba-2.8B layer shape",
+        "value": round(nbytes / (ms_step * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "io_dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": cfg.name, "B": cfg.B, "D": cfg.D, "L": cfg.L, "K": cfg.K, "input_sets": len(sets)},
+        "elems_per_s": round(cfg.elements / (ms_step * 1e-3), 1),
+        "kernel_ms_mean": round(kern_ms, 5),
+        "kernel_ms_p10_p50_p90": [round(float(v), 5) for v in np.percentile(per, [10, 50, 90])],
+        "roofline": {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic, "traffic_note": note,
+                     "algorithmic_bytes": nbytes},
+    }
+
+
+def bench_conv_decode(args, dev):
+    """48 layers x 128 steps of the one-token conv update (B=128 D=4096 K=4),
+    step-major, the 48-layer step replayed as a graph."""
+    import torch
+    import selective_state_space_75_amd as m
+    from selective_state_space_75_amd import workloads as W
+    cfg = W.CONV_UPDATE_CONFIGS[args.workload]
+    log("conv decode: %d layers x %d steps, B=%d D=%d K=%d" % (cfg.layers, cfg.steps, cfg.B, cfg.D, cfg.K))
+    pool = 4
+    layers = []
+    for l in range(cfg.layers):
+        w, bias, st0 = W.conv_update_layer(cfg, l)
+        layers.append({"w": to_dev(w, dev), "bias": to_dev(bias, dev), "state": to_dev(st0, dev),
+                       "x": [to_dev(W.conv_update_step(cfg, l, s), dev) for s in range(pool)],
+                       "y": torch.empty((cfg.B, cfg.D), dtype=torch.bfloat16, device=dev)})
+    stream = torch.cuda.Stream(dev)
+    graphs = []
+    torch.cuda.synchronize()
+    for s in range(pool):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for L_ in layers:
+                m.conv1d_update(L_["state"], L_["x"][s], L_["w"], L_["bias"], y=L_["y"], stream=stream)
+        graphs.append(g)
+    for i in range(args.warmup):
+        graphs[i % pool].replay()
+    torch.cuda.synchronize()
+    steps = args.decode_steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(torch.cuda.current_stream(dev))
+    for s in range(steps):
+        graphs[s % pool].replay()
+    e1.record(torch.cuda.current_stream(dev))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_ls = cfg.bytes_per_layer_step()
+    kern_us = e0.elapsed_time(e1) * 1e3 / (cfg.layers * steps)
+    ach = per_ls / (kern_us * 1e-6) / 1e9
+    return {
+        "metric": "conv1d one-token update HBM GB/s, 48 layers x 128 steps (B=128, D=4096, K=4)",
+        "value": round(per_ls * cfg.layers * steps / wall / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps,
+        "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / steps, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "io_dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.name, "layers": cfg.layers, "steps": steps, "B": cfg.B, "D": cfg.D, "K": cfg.K,
+                   "order": "step-major, 48-layer step replayed as a HIP graph"},
+        "layer_step_us_mean": round(kern_us, 3),
+        "roofline": {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "bytes_per_layer_step": per_ls,
+                     "launch_time": "graph replay time / launches (inter-kernel gaps included)"},
+    }
+
+
 def copy_calibration(args, dev):
     import torch
     n = args.copy_mb * (1 << 20) // 4
@@ -304,8 +415,13 @@ def main():
     if args.copy_calibration:
         copy_calibration(args, dev)
         return
+    from selective_state_space_75_amd import workloads as W
     if args.workload == "decode48":
         line = bench_decode(args, dev)
+    elif args.workload in W.CONV_CONFIGS:
+        line = bench_conv(args, dev)
+    elif args.workload in W.CONV_UPDATE_CONFIGS:
+        line = bench_conv_decode(args, dev)
     else:
         line, cfg, x = bench_scan(args, dev)
         if not args.no_cpu_baseline:

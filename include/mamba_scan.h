@@ -1,6 +1,8 @@
 /*
  * mamba_scan.h -- C ABI of the MI355X (gfx950) Mamba-1 selective scan (S6)
- * forward pass and the single-token selective state update.
+ * forward pass and the single-token selective state update, plus the causal
+ * depthwise conv1d + SiLU that produces the scan input and its one-token
+ * update (declared last).
  *
  * What the calls compute (pages cited by title and section):
  *   "Mamba 模型" (gaos6e.github.io), full-step flowchart nodes H to M and
@@ -138,6 +140,51 @@ int mamba_state_update(float* state, const void* u, const void* delta, const voi
                        int64_t B, int64_t D, int64_t N,
                        mamba_dtype_t in_dtype, mamba_dtype_t out_dtype,
                        unsigned flags, hipStream_t stream);
+
+/*
+ * Causal depthwise convolution along the sequence, then SiLU: the step that
+ * produces the scan input u.
+ *   "Mamba 模型", full-step flowchart node E: Uc_t = sum_i W_i U_(t-i), one
+ *     filter per channel over the current and earlier positions only; node F:
+ *     u_t = Uc_t * sigmoid(Uc_t).
+ *   "Mamba 与状态空间模型", section 03: each channel also keeps its short
+ *     convolution's most recent inputs (4 for Mamba) between tokens.
+ *
+ *   x           : (B, D, L) in_dtype.
+ *   weight      : (D, K) fp32; weight[d*K + i] multiplies x[b, d, t - i]
+ *                 (i = 0 is the current position).
+ *   bias        : (D) fp32 or NULL (no bias); added before SiLU.
+ *   y           : (B, D, L) out_dtype, written: silu of the convolution.
+ *   final_state : (B, D, K) fp32, written iff return_final_state != 0: the K
+ *                 most recent inputs x[b, d, L-K .. L-1], oldest first (zero
+ *                 where L - K + k < 0) -- the state mamba_conv1d_update
+ *                 continues from.  Ignored (may be NULL) otherwise.
+ *
+ * Positions before t = 0 read zero.  1 <= K <= 4 (MAMBA_ERR_UNSUPPORTED
+ * above).  Alignment: x, y to their element size (16 bytes, with L % 8 == 0,
+ * selects the vectorised kernel); weight, bias, final_state 4-byte.
+ */
+int mamba_conv1d_fwd(const void* x, const float* weight, const float* bias, void* y, float* final_state,
+                     int64_t B, int64_t D, int64_t L, int64_t K,
+                     mamba_dtype_t in_dtype, mamba_dtype_t out_dtype, int return_final_state,
+                     hipStream_t stream);
+
+/*
+ * One decoding step of the convolution for every (b, d).
+ *
+ *   state  : (B, D, K) fp32, read and overwritten in place: on entry the K
+ *            most recent inputs (oldest first), on return the K most recent
+ *            including x.
+ *   x      : (B, D) in_dtype, the new input.
+ *   weight : (D, K) fp32, as in mamba_conv1d_fwd.  bias : (D) fp32 or NULL.
+ *   y      : (B, D) out_dtype, written: silu(sum_i weight[d*K+i] * x_(t-i) + bias).
+ *
+ * 1 <= K <= 4.  Alignment: state, weight, bias 4-byte (state 16-byte with
+ * K = 4 selects vector accesses); x, y to their element size.  No workspace.
+ */
+int mamba_conv1d_update(float* state, const void* x, const float* weight, const float* bias, void* y,
+                        int64_t B, int64_t D, int64_t K, mamba_dtype_t in_dtype, mamba_dtype_t out_dtype,
+                        hipStream_t stream);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char* mamba_status_string(int status);

@@ -1,12 +1,14 @@
-"""MI355X (gfx950) Mamba-1 selective scan (S6) forward and selective state update.
+"""MI355X (gfx950) Mamba-1 selective scan (S6) forward and selective state update,
+with the causal conv1d + SiLU that produces the scan input.
 
 The computation runs in hand-written HIP kernels inside ``libmamba_scan.so``
 (C ABI: ``include/mamba_scan.h``).  This package is the thin Python side:
-``scan_fwd`` / ``state_update`` marshal torch tensors to that library, and
-``workloads`` draws the seeded synthetic inputs.
+``scan_fwd`` / ``state_update`` / ``conv1d_fwd`` / ``conv1d_update`` marshal
+torch tensors to that library, and ``workloads`` draws the seeded synthetic
+inputs.
 """
-from ._lib import (FLAG_ACCURATE_EXPM1, FLAG_DELTA_B, MambaError, lib, scan_fwd,  # noqa: F401
-                   state_update, status_string, workspace_size)
+from ._lib import (FLAG_ACCURATE_EXPM1, FLAG_DELTA_B, MambaError, conv1d_fwd, conv1d_update,  # noqa: F401
+                   lib, scan_fwd, state_update, status_string, workspace_size)
 
-__all__ = ["scan_fwd", "state_update", "workspace_size", "status_string", "lib", "MambaError",
-           "FLAG_DELTA_B", "FLAG_ACCURATE_EXPM1"]
+__all__ = ["scan_fwd", "state_update", "conv1d_fwd", "conv1d_update", "workspace_size", "status_string", "lib",
+           "MambaError", "FLAG_DELTA_B", "FLAG_ACCURATE_EXPM1"]

@@ -51,6 +51,10 @@ def lib() -> ctypes.CDLL:
             L.mamba_scan_fwd.restype = c_int
             L.mamba_state_update.argtypes = [vp] * 10 + [i64] * 3 + [c_int, c_int, u32, vp]
             L.mamba_state_update.restype = c_int
+            L.mamba_conv1d_fwd.argtypes = [vp] * 5 + [i64] * 4 + [c_int, c_int, c_int, vp]
+            L.mamba_conv1d_fwd.restype = c_int
+            L.mamba_conv1d_update.argtypes = [vp] * 5 + [i64] * 3 + [c_int, c_int, vp]
+            L.mamba_conv1d_update.restype = c_int
             L.mamba_status_string.argtypes = [c_int]
             L.mamba_status_string.restype = ctypes.c_char_p
             _lib = L
@@ -194,4 +198,66 @@ def state_update(state, u, delta, z, Bt, Ct, A, Dskip=None, delta_bias=None, *, 
         _stream(dev, stream))
     if st != 0:
         raise MambaError(st, "mamba_state_update")
+    return y
+
+
+def conv1d_fwd(x, weight, bias=None, *, return_final_state=False, out_dtype=None, y=None, final_state=None,
+               stream=None):
+    """Causal depthwise conv1d + SiLU.  x: (B, D, L); weight: (D, K) fp32 with
+    weight[d, i] multiplying x[..., t - i]; bias: (D) fp32 or None.
+
+    Returns y (B, D, L), or (y, final_state (B, D, K) fp32) when return_final_state.
+    """
+    torch = _torch()
+    if x.dim() != 3 or weight.dim() != 2:
+        raise ValueError("x must be (B, D, L) and weight (D, K)")
+    B, D, L = x.shape
+    K = weight.shape[1]
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU device")
+    _dtype_code(x)
+    _check(x, "x", (B, D, L), x.dtype, dev)
+    _check(weight, "weight", (D, K), torch.float32, dev)
+    _check(bias, "bias", (D,), torch.float32, dev)
+    out_dt = x.dtype if out_dtype is None else out_dtype
+    if y is None:
+        y = torch.empty((B, D, L), dtype=out_dt, device=dev)
+    _check(y, "y", (B, D, L), out_dt, dev)
+    if return_final_state:
+        if final_state is None:
+            final_state = torch.empty((B, D, K), dtype=torch.float32, device=dev)
+        _check(final_state, "final_state", (B, D, K), torch.float32, dev)
+    st = lib().mamba_conv1d_fwd(_ptr(x), _ptr(weight), _ptr(bias), _ptr(y),
+                                _ptr(final_state if return_final_state else None), B, D, L, K,
+                                _dtype_code(x), _dtype_code(y), 1 if return_final_state else 0,
+                                _stream(dev, stream))
+    if st != 0:
+        raise MambaError(st, "mamba_conv1d_fwd")
+    return (y, final_state) if return_final_state else y
+
+
+def conv1d_update(state, x, weight, bias=None, *, out_dtype=None, y=None, stream=None):
+    """One decoding step of the convolution; `state` (B, D, K) fp32 (the K most
+    recent inputs, oldest first) is updated in place.  x: (B, D).  Returns y (B, D)."""
+    torch = _torch()
+    if state.dim() != 3:
+        raise ValueError("state must be (B, D, K)")
+    B, D, K = state.shape
+    dev = state.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU device")
+    _dtype_code(x)
+    _check(state, "state", (B, D, K), torch.float32, dev)
+    _check(x, "x", (B, D), x.dtype, dev)
+    _check(weight, "weight", (D, K), torch.float32, dev)
+    _check(bias, "bias", (D,), torch.float32, dev)
+    out_dt = x.dtype if out_dtype is None else out_dtype
+    if y is None:
+        y = torch.empty((B, D), dtype=out_dt, device=dev)
+    _check(y, "y", (B, D), out_dt, dev)
+    st = lib().mamba_conv1d_update(_ptr(state), _ptr(x), _ptr(weight), _ptr(bias), _ptr(y), B, D, K,
+                                   _dtype_code(x), _dtype_code(y), _stream(dev, stream))
+    if st != 0:
+        raise MambaError(st, "mamba_conv1d_update")
     return y

@@ -243,6 +243,50 @@ int mamba_state_update(float* state, const void* u, const void* delta, const voi
   return mamba::launch_state_update(p, in, out, stream) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
 }
 
+int mamba_conv1d_fwd(const void* x, const float* weight, const float* bias, void* y, float* final_state,
+                     int64_t B, int64_t D, int64_t L, int64_t K, mamba_dtype_t in_dtype,
+                     mamba_dtype_t out_dtype, int return_final_state, hipStream_t stream) {
+  if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return MAMBA_ERR_DTYPE;
+  if (!shape_ok(B, D, 1, L) || K < 1) return MAMBA_ERR_SHAPE;
+  if (K > 4) return MAMBA_ERR_UNSUPPORTED;
+  if (!x || !weight || !y || (return_final_state && !final_state)) return MAMBA_ERR_NULL;
+  const size_t ei = in_dtype == MAMBA_BF16 ? 2 : 4, eo = out_dtype == MAMBA_BF16 ? 2 : 4;
+  if (!aligned(x, ei) || !aligned(y, eo)) return MAMBA_ERR_ALIGN;
+  if (!aligned(weight, 4) || (bias && !aligned(bias, 4)) || (return_final_state && !aligned(final_state, 4)))
+    return MAMBA_ERR_ALIGN;
+  const bool vec = (L % 8 == 0) && aligned(x, 16) && aligned(y, 16);
+  const int64_t threads = vec ? B * D * (L / 8) : B * D * L;
+  if ((threads + 255) / 256 >= (int64_t(1) << 31)) return MAMBA_ERR_SHAPE;
+
+  mamba::ConvParams p{};
+  p.x = x; p.w = weight; p.bias = bias; p.y = y;
+  p.final_state = return_final_state ? final_state : nullptr;
+  p.rows = B * D; p.D = D; p.L = L; p.K = K;
+  const Dt in = in_dtype == MAMBA_BF16 ? Dt::BF16 : Dt::F32;
+  const Dt out = out_dtype == MAMBA_BF16 ? Dt::BF16 : Dt::F32;
+  return mamba::launch_conv1d_fwd(p, in, out, vec, stream) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
+}
+
+int mamba_conv1d_update(float* state, const void* x, const float* weight, const float* bias, void* y,
+                        int64_t B, int64_t D, int64_t K, mamba_dtype_t in_dtype, mamba_dtype_t out_dtype,
+                        hipStream_t stream) {
+  if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return MAMBA_ERR_DTYPE;
+  if (!shape_ok(B, D, 1, 1) || K < 1) return MAMBA_ERR_SHAPE;
+  if (K > 4) return MAMBA_ERR_UNSUPPORTED;
+  if (!state || !x || !weight || !y) return MAMBA_ERR_NULL;
+  const size_t ei = in_dtype == MAMBA_BF16 ? 2 : 4, eo = out_dtype == MAMBA_BF16 ? 2 : 4;
+  if (!aligned(state, 4) || !aligned(x, ei) || !aligned(y, eo) || !aligned(weight, 4) || (bias && !aligned(bias, 4)))
+    return MAMBA_ERR_ALIGN;
+  if ((B * D + 255) / 256 >= (int64_t(1) << 31)) return MAMBA_ERR_SHAPE;
+
+  mamba::ConvParams p{};
+  p.state = state; p.x = x; p.w = weight; p.bias = bias; p.y = y;
+  p.rows = B * D; p.D = D; p.L = 1; p.K = K;
+  const Dt in = in_dtype == MAMBA_BF16 ? Dt::BF16 : Dt::F32;
+  const Dt out = out_dtype == MAMBA_BF16 ? Dt::BF16 : Dt::F32;
+  return mamba::launch_conv1d_update(p, in, out, stream) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
+}
+
 const char* mamba_status_string(int status) {
   switch (status) {
     case MAMBA_OK: return "ok";

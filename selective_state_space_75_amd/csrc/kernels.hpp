@@ -65,11 +65,24 @@ struct UpdateParams {
   int delta_b;
 };
 
+// Causal depthwise conv1d (+ SiLU) and its one-token update.
+struct ConvParams {
+  const void* x;          // (rows, L) or (rows) for the update
+  const float* w;         // (D, K)
+  const float* bias;      // (D) or null
+  void* y;                // like x
+  float* final_state;     // (rows, K) or null (forward)
+  float* state;           // (rows, K) in/out (update)
+  int64_t rows, D, L, K;  // rows = B * D
+};
+
 // Each returns hipSuccess or the launch error.
 hipError_t launch_scan_full(const ScanParams& p, Dt in, Dt out, hipStream_t s);
 hipError_t launch_scan_summary(const ScanParams& p, Dt in, hipStream_t s);
 hipError_t launch_scan_carry(const ScanParams& p, hipStream_t s);
 hipError_t launch_scan_v4(const ScanParams& p, const V2Params& q, Dt in, Dt out, bool summary, hipStream_t s);
 hipError_t launch_state_update(const UpdateParams& p, Dt in, Dt out, hipStream_t s);
+hipError_t launch_conv1d_fwd(const ConvParams& p, Dt in, Dt out, bool vec, hipStream_t s);
+hipError_t launch_conv1d_update(const ConvParams& p, Dt in, Dt out, hipStream_t s);
 
 }  // namespace mamba

@@ -35,6 +35,7 @@ BLOCK = 1 << 22
 
 # Array ids used in the seed tree (kept fixed: changing them changes every input).
 _ID_PARAMS, _ID_DELTA, _ID_U, _ID_Z, _ID_B, _ID_C, _ID_STATE = range(7)
+_ID_CONV_X, _ID_CONV_PARAMS, _ID_CONV_STATE = range(7, 10)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -203,3 +204,81 @@ def decode_step_inputs(cfg: DecodeConfig, layer: int, step: int) -> dict:
         "Bt": f32_to_bf16_bits(_normal_f32(s + [_ID_B], cfg.B * cfg.N)).reshape(bn),
         "Ct": f32_to_bf16_bits(_normal_f32(s + [_ID_C], cfg.B * cfg.N)).reshape(bn),
     }
+
+
+# ----------------------------------------------------------------------------- causal conv1d + SiLU
+@dataclasses.dataclass(frozen=True)
+class ConvConfig:
+    """Causal depthwise conv1d + SiLU over x (B, D, L) with K taps per channel."""
+    name: str
+    B: int
+    D: int
+    L: int
+    K: int
+    dtype: str          # dtype of x and y
+    seed: int
+
+    @property
+    def elements(self) -> int:
+        return self.B * self.D * self.L
+
+    def algorithmic_bytes(self) -> int:
+        """x read once, y written once, taps and bias read once, final state written."""
+        e = 2 if self.dtype == "bf16" else 4
+        return self.elements * 2 * e + self.D * (self.K + 1) * 4 + self.B * self.D * self.K * 4
+
+
+@dataclasses.dataclass(frozen=True)
+class ConvUpdateConfig:
+    """One-token conv updates: `layers` layers x `steps` steps at (B, D, K)."""
+    name: str
+    B: int
+    D: int
+    K: int
+    layers: int
+    steps: int
+    seed: int
+
+    def bytes_per_layer_step(self) -> int:
+        """state read + written (fp32), x read and y written (bf16), taps and bias."""
+        rows = self.B * self.D
+        return rows * self.K * 4 * 2 + rows * 2 * 2 + self.D * (self.K + 1) * 4
+
+
+# The scan's 2.8B layer shape (the conv feeds u to it); the decode shape of the
+# 48-layer state update.  Taps and bias ~ U(-1/2, 1/2) (the usual uniform
+# initialisation bound 1/sqrt(fan-in) for K = 4 taps), x ~ N(0, 1).
+CONV_CONFIGS = {
+    "conv_2.8b_layer": ConvConfig("conv_2.8b_layer", 4, 5120, 2048, 4, "bf16", 1005),
+}
+CONV_UPDATE_CONFIGS = {
+    "conv_decode48": ConvUpdateConfig("conv_decode48", 128, 4096, 4, 48, 128, 1006),
+}
+
+
+def _conv_params(seed_path, D: int, K: int):
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(list(seed_path) + [_ID_CONV_PARAMS])))
+    w = g.uniform(-0.5, 0.5, size=(D, K)).astype(np.float32)
+    bias = g.uniform(-0.5, 0.5, size=D).astype(np.float32)
+    return w, bias
+
+
+def conv_inputs(B: int, D: int, L: int, K: int, dtype: str, seed: int) -> dict:
+    """x (B, D, L) in `dtype` (bf16 as uint16 bit patterns), w (D, K) and bias (D) fp32."""
+    x = _normal_f32([seed, _ID_CONV_X], B * D * L).reshape(B, D, L)
+    w, bias = _conv_params([seed], D, K)
+    return {"x": _store(x, dtype), "w": w, "bias": bias}
+
+
+def conv_update_layer(cfg: ConvUpdateConfig, layer: int):
+    """(w, bias, state0) of one layer; state0 ~ N(0, 1) fp32 rounded through bf16
+    (the state holds past inputs, which are bf16 values)."""
+    w, bias = _conv_params([cfg.seed, layer], cfg.D, cfg.K)
+    st = _normal_f32([cfg.seed, layer, _ID_CONV_STATE], cfg.B * cfg.D * cfg.K).reshape(cfg.B, cfg.D, cfg.K)
+    return w, bias, as_f32(f32_to_bf16_bits(st))
+
+
+def conv_update_step(cfg: ConvUpdateConfig, layer: int, step: int) -> np.ndarray:
+    """x (B, D) bf16 bit patterns of one layer at one step."""
+    x = _normal_f32([cfg.seed, layer, step, _ID_CONV_X], cfg.B * cfg.D).reshape(cfg.B, cfg.D)
+    return f32_to_bf16_bits(x)

@@ -23,13 +23,13 @@ F32, BF16 = 0, 1
 def declared_functions():
     src = open(HEADER, encoding="utf-8").read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(mamba_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(mamba_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_header_symbols_are_exported():
     names = declared_functions()
-    assert names == ["mamba_scan_fwd", "mamba_scan_workspace_size", "mamba_state_update",
-                     "mamba_status_string"]
+    assert names == ["mamba_conv1d_fwd", "mamba_conv1d_update", "mamba_scan_fwd", "mamba_scan_workspace_size",
+                     "mamba_state_update", "mamba_status_string"]
     L = _lib.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -136,3 +136,46 @@ def test_python_binding_rejects_before_calling():
     x = torch.zeros(1, 2, 8)
     with pytest.raises(ValueError):
         m.scan_fwd(x, x, x, torch.zeros(1, 3, 8), torch.zeros(1, 3, 8), torch.zeros(2, 3))
+
+
+def conv(**kw):
+    a = dict(x=P, w=P, bias=P, y=P, fs=P, B=2, D=64, L=64, K=4, ind=BF16, outd=BF16, rfs=1)
+    a.update(kw)
+    vp = lambda v: ctypes.c_void_p(v) if v is not None else None  # noqa: E731
+    return _lib.lib().mamba_conv1d_fwd(vp(a["x"]), vp(a["w"]), vp(a["bias"]), vp(a["y"]), vp(a["fs"]),
+                                       a["B"], a["D"], a["L"], a["K"], a["ind"], a["outd"], a["rfs"], None)
+
+
+def conv_update(**kw):
+    a = dict(st=P, x=P, w=P, bias=P, y=P, B=2, D=64, K=4, ind=BF16, outd=BF16)
+    a.update(kw)
+    vp = lambda v: ctypes.c_void_p(v) if v is not None else None  # noqa: E731
+    return _lib.lib().mamba_conv1d_update(vp(a["st"]), vp(a["x"]), vp(a["w"]), vp(a["bias"]), vp(a["y"]),
+                                          a["B"], a["D"], a["K"], a["ind"], a["outd"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ind=5), DTYPE), (dict(outd=9), DTYPE),
+    (dict(B=0), SHAPE), (dict(L=-1), SHAPE), (dict(K=0), SHAPE), (dict(K=5), UNSUP),
+    (dict(B=1 << 20, D=1 << 20, L=1 << 20), SHAPE),
+    (dict(x=None), NULL), (dict(w=None), NULL), (dict(y=None), NULL), (dict(fs=None), NULL),
+    (dict(x=P + 1), ALIGN), (dict(ind=F32, x=P + 2), ALIGN), (dict(outd=F32, y=P + 2), ALIGN),
+    (dict(w=P + 2), ALIGN), (dict(bias=P + 1), ALIGN), (dict(fs=P + 2), ALIGN),
+])
+def test_conv_rejects_bad_arguments(kw, code):
+    assert conv(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ind=3), DTYPE), (dict(B=0), SHAPE), (dict(K=0), SHAPE), (dict(K=7), UNSUP),
+    (dict(st=None), NULL), (dict(x=None), NULL), (dict(w=None), NULL), (dict(y=None), NULL),
+    (dict(st=P + 2), ALIGN), (dict(x=P + 1), ALIGN), (dict(w=P + 1), ALIGN),
+])
+def test_conv_update_rejects_bad_arguments(kw, code):
+    assert conv_update(**kw) == code
+
+
+def test_conv_optional_pointers():
+    # bias may be NULL and final_state is ignored when not requested: with every
+    # other argument valid the call only fails at the size check we force here
+    assert conv(bias=None, fs=None, rfs=0, K=9) == UNSUP
