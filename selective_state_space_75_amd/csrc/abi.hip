@@ -255,8 +255,7 @@ int mamba_conv1d_fwd(const void* x, const float* weight, const float* bias, void
   if (!aligned(weight, 4) || (bias && !aligned(bias, 4)) || (return_final_state && !aligned(final_state, 4)))
     return MAMBA_ERR_ALIGN;
   const bool vec = (L % 8 == 0) && aligned(x, 16) && aligned(y, 16);
-  const int64_t threads = vec ? B * D * (L / 8) : B * D * L;
-  if ((threads + 255) / 256 >= (int64_t(1) << 31)) return MAMBA_ERR_SHAPE;
+  if ((B * D * L + 255) / 256 >= (int64_t(1) << 31)) return MAMBA_ERR_SHAPE;   // grid of the element kernel
 
   mamba::ConvParams p{};
   p.x = x; p.w = weight; p.bias = bias; p.y = y;
