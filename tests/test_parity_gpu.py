@@ -193,6 +193,9 @@ CASES = [
     (2, 10240, 16, 128, "bf16", "bf16", None, {}),
     (1, 16384 + 64 * 60, 16, 96, "f32", "f32", None, {"zero_A": True}),
     (3, 6000, 9, 64, "bf16", "f32", None, {"delta_b": True}),
+    # fewer tiles than waves: one pass per tile, ragged last tile
+    (4, 2040, 16, 64, "bf16", "bf16", None, {}),
+    (8, 1024, 16, 256, "f32", "f32", None, {}),
 ]
 
 
