@@ -57,6 +57,9 @@ def _load():
             lib.oracle_scan.restype = ctypes.c_int
             lib.oracle_state_update.argtypes = [i64, i64, i64, dp] + [dp] * 8 + [ctypes.c_int, dp, ctypes.c_int]
             lib.oracle_state_update.restype = ctypes.c_int
+            lib.oracle_scan_bwd.argtypes = [i64, i64, i64, i64] + [dp] * 8 + [ctypes.c_int] + [dp] * 9 + \
+                [ctypes.c_int]
+            lib.oracle_scan_bwd.restype = ctypes.c_int
             lib.oracle_conv1d.argtypes = [i64, i64, i64, i64, dp, dp, dp, dp, ctypes.c_int, dp, dp]
             lib.oracle_conv1d.restype = ctypes.c_int
             lib.oracle_conv1d_update.argtypes = [i64, i64, i64, dp, dp, dp, dp, ctypes.c_int, dp]
@@ -187,3 +190,39 @@ def conv1d_update(state, x, w, bias=None, activation: bool = True):
     if rc != 0:
         raise RuntimeError("oracle_conv1d_update failed with %d" % rc)
     return y, st
+
+
+def scan_bwd(u, delta_raw, z, Bt, Ct, A, Dskip, delta_bias, dy, discretization: str = "zoh",
+             nthreads: int | None = None):
+    """Gradients of the scan for output gradient dy (B, D, L).
+
+    Returns a dict of float64 arrays: du, ddelta_raw, dz (B, D, L; dz None when
+    z is None), dBt, dCt (B, N, L), dA (D, N), dDskip (D), ddelta_bias (D).
+    Dskip / delta_bias of None mean zeros (their gradients are still returned).
+    """
+    u = _f64(u)
+    if u.ndim != 3:
+        raise ValueError("u must be (B, D, L)")
+    B, D, L = u.shape
+    Bt = _f64(Bt)
+    N = Bt.shape[1]
+    delta_raw = _f64(delta_raw, (B, D, L))
+    z = _f64(z, (B, D, L))
+    Bt = _f64(Bt, (B, N, L))
+    Ct = _f64(Ct, (B, N, L))
+    A = _f64(A, (D, N))
+    Dskip = _f64(Dskip, (D,))
+    delta_bias = _f64(delta_bias, (D,))
+    dy = _f64(dy, (B, D, L))
+    out = {"du": np.empty((B, D, L)), "ddelta_raw": np.empty((B, D, L)),
+           "dz": np.empty((B, D, L)) if z is not None else None,
+           "dBt": np.empty((B, N, L)), "dCt": np.empty((B, N, L)), "dA": np.empty((D, N)),
+           "dDskip": np.empty(D), "ddelta_bias": np.empty(D)}
+    rc = _load().oracle_scan_bwd(B, D, N, L, _ptr(u), _ptr(delta_raw), _ptr(z), _ptr(Bt), _ptr(Ct), _ptr(A),
+                                 _ptr(Dskip), _ptr(delta_bias), DISCRETIZATIONS[discretization], _ptr(dy),
+                                 _ptr(out["du"]), _ptr(out["ddelta_raw"]), _ptr(out["dz"]), _ptr(out["dBt"]),
+                                 _ptr(out["dCt"]), _ptr(out["dA"]), _ptr(out["dDskip"]), _ptr(out["ddelta_bias"]),
+                                 nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError("oracle_scan_bwd failed with %d" % rc)
+    return out

@@ -246,3 +246,193 @@ int oracle_conv1d_update(int64_t B, int64_t D, int64_t K, double* state, const d
   free(next);
   return rc;
 }
+
+/* ---------------------------------------------------------------------------
+ * Backward pass of the scan: gradients of all inputs for a given dy.
+ *
+ *   [P2] "Mamba论文研读笔记" 3.2.3 C (recomputation) and [P3] section 07: the
+ *   backward pass works from the same inputs and recomputes the states h_t
+ *   instead of reading stored ones.  Here, per channel, the forward recurrence
+ *   is rerun in fp64 (keeping its L x N states in a private buffer) and then
+ *   walked in reverse, applying the chain rule to each forward step:
+ *
+ *     yc_t = sum_n C_tn h_tn + D u_t;   y_t = yc_t * silu(z_t)   (or yc_t)
+ *     h_tn = Abar_tn h_(t-1)n + coef_tn B_tn u_t,
+ *     Abar = exp(delta a), coef = (Abar - 1)/a (ZOH) or delta,
+ *     delta_t = softplus(delta_raw_t + bias).
+ *
+ *   Adjoint of the state: g_tn = dyc_t C_tn + Abar_(t+1)n g_(t+1)n.
+ *   d coef / d delta = Abar (ZOH), 1 (delta*B);
+ *   d coef / d a     = delta^2 phi(delta a), phi(x) = (x e^x - e^x + 1) / x^2
+ *                      (ZOH; series near 0, where it tends to 1/2), 0 (delta*B);
+ *   d softplus / dx  = sigmoid(x);  d silu / dz = s (1 + z (1 - s)), s = sigmoid(z).
+ *
+ * Outputs: du, ddelta_raw, dz (B, D, L) per channel; dBt, dCt (B, N, L)
+ * summed over the D channels of a batch row; dA (D, N), dDskip (D) and
+ * ddelta_bias (D) summed over batch rows and time.  dz is written only when
+ * z is given.  Threads split the channels; each keeps private sums that are
+ * added in thread order at the end, so results do not depend on timing.
+ * ------------------------------------------------------------------------- */
+static double sigmoid(double x) {
+  if (x >= 0.0) return 1.0 / (1.0 + exp(-x));
+  const double e = exp(x);
+  return e / (1.0 + e);
+}
+
+/* (x e^x - e^x + 1) / x^2 */
+static double phi_coef(double x) {
+  if (fabs(x) < 0.5) {
+    /* sum_{k>=0} (k+1) x^k / (k+2)! */
+    double term = 0.5, sum = 0.0;       /* k = 0: 1 / 2! */
+    for (int k = 0; k < 40; ++k) {
+      sum += term;
+      term *= x * (double)(k + 2) / ((double)(k + 1) * (double)(k + 3));
+    }
+    return sum;
+  }
+  return (x * exp(x) - expm1(x)) / (x * x);
+}
+
+typedef struct {
+  int64_t B, D, N, L;
+  const double *u, *delta_raw, *z, *Bt, *Ct, *A, *Dskip, *bias, *dy;
+  int mode;
+  double *du, *ddr, *dz;
+  double *dBt, *dCt, *dA, *dD, *dbias;   /* this thread's private sums */
+  int64_t ch_begin, ch_end;
+} bjob_t;
+
+static void bwd_one_channel(const bjob_t* j, int64_t ch, double* H, double* dl) {
+  const int64_t b = ch / j->D, d = ch % j->D;
+  const int64_t N = j->N, L = j->L;
+  const double* u = j->u + ch * L;
+  const double* dr = j->delta_raw + ch * L;
+  const double* z = j->z ? j->z + ch * L : NULL;
+  const double* Bb = j->Bt + b * N * L;
+  const double* Cb = j->Ct + b * N * L;
+  const double* Ad = j->A + d * N;
+  const double Dd = j->Dskip ? j->Dskip[d] : 0.0;
+  const double bias = j->bias ? j->bias[d] : 0.0;
+  const double* dy = j->dy + ch * L;
+
+  /* forward, keeping H[(l+1)*N + n] = h_ln and H[n] = h_(-1)n = 0 */
+  for (int64_t n = 0; n < N; ++n) H[n] = 0.0;
+  for (int64_t l = 0; l < L; ++l) {
+    dl[l] = oracle_softplus(dr[l] + bias);
+    for (int64_t n = 0; n < N; ++n) {
+      const double a = Ad[n];
+      H[(l + 1) * N + n] = exp(dl[l] * a) * H[l * N + n] + bbar_coef(dl[l], a, j->mode) * Bb[n * L + l] * u[l];
+    }
+  }
+  /* reverse */
+  double g[16], anext[16];
+  for (int64_t n = 0; n < N; ++n) { g[n] = 0.0; anext[n] = 0.0; }
+  for (int64_t l = L - 1; l >= 0; --l) {
+    const double x = u[l], delta = dl[l];
+    double dyc = dy[l];
+    if (z) {
+      double yc = Dd * x;
+      for (int64_t n = 0; n < N; ++n) yc += Cb[n * L + l] * H[(l + 1) * N + n];
+      const double s = sigmoid(z[l]);
+      j->dz[ch * L + l] = dy[l] * yc * s * (1.0 + z[l] * (1.0 - s));
+      dyc = dy[l] * silu(z[l]);
+    }
+    double dux = dyc * Dd, ddelta = 0.0;
+    j->dD[d] += dyc * x;
+    for (int64_t n = 0; n < N; ++n) {
+      const double a = Ad[n];
+      const double abar = exp(delta * a);
+      const double coef = bbar_coef(delta, a, j->mode);
+      const double gn = dyc * Cb[n * L + l] + anext[n] * g[n];
+      const double dabar = gn * H[l * N + n];              /* d / d Abar_ln */
+      const double dcoef = gn * Bb[n * L + l] * x;         /* d / d coef_ln */
+      j->dCt[b * N * L + n * L + l] += dyc * H[(l + 1) * N + n];
+      j->dBt[b * N * L + n * L + l] += gn * coef * x;
+      dux += gn * coef * Bb[n * L + l];
+      if (j->mode == ORACLE_DELTA_B) {
+        ddelta += dabar * a * abar + dcoef;
+        j->dA[d * N + n] += dabar * delta * abar;
+      } else {
+        ddelta += dabar * a * abar + dcoef * abar;
+        j->dA[d * N + n] += dabar * delta * abar + dcoef * delta * delta * phi_coef(delta * a);
+      }
+      g[n] = gn;
+      anext[n] = abar;
+    }
+    j->du[ch * L + l] = dux;
+    const double dr_l = ddelta * sigmoid(dr[l] + bias);
+    j->ddr[ch * L + l] = dr_l;
+    j->dbias[d] += dr_l;
+  }
+}
+
+static void* run_bjob(void* arg) {
+  const bjob_t* j = (const bjob_t*)arg;
+  const int64_t N = j->N, L = j->L;
+  double* H = (double*)malloc(sizeof(double) * (size_t)((L + 1) * N + 1));
+  double* dl = (double*)malloc(sizeof(double) * (size_t)(L + 1));
+  if (!H || !dl) { free(H); free(dl); return (void*)1; }
+  for (int64_t ch = j->ch_begin; ch < j->ch_end; ++ch) bwd_one_channel(j, ch, H, dl);
+  free(H);
+  free(dl);
+  return NULL;
+}
+
+/* Returns 0 on success, -1 on bad arguments, -2 on allocation/thread failure. */
+int oracle_scan_bwd(int64_t B, int64_t D, int64_t N, int64_t L,
+                    const double* u, const double* delta_raw, const double* z,
+                    const double* Bt, const double* Ct, const double* A,
+                    const double* Dskip, const double* bias, int mode, const double* dy,
+                    double* du, double* ddelta_raw, double* dz, double* dBt, double* dCt,
+                    double* dA, double* dDskip, double* dbias, int nthreads) {
+  if (B < 0 || D < 0 || N < 1 || N > 16 || L < 0) return -1;
+  if (!u || !delta_raw || !Bt || !Ct || !A || !dy || !du || !ddelta_raw || !dBt || !dCt || !dA ||
+      !dDskip || !dbias || (z && !dz))
+    return -1;
+  const int64_t C = B * D;
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > C) nthreads = C > 0 ? (int)C : 1;
+  const size_t nbc = (size_t)(B * N * L), nda = (size_t)(D * N), nd = (size_t)D;
+  const size_t per = 2 * nbc + nda + 2 * nd;
+  double* priv = (double*)calloc((size_t)nthreads * per + 1, sizeof(double));
+  bjob_t* jobs = (bjob_t*)calloc((size_t)nthreads, sizeof(bjob_t));
+  pthread_t* tids = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+  if (!priv || !jobs || !tids) { free(priv); free(jobs); free(tids); return -2; }
+  int rc = 0;
+  for (int t = 0; t < nthreads; ++t) {
+    bjob_t* j = &jobs[t];
+    j->B = B; j->D = D; j->N = N; j->L = L;
+    j->u = u; j->delta_raw = delta_raw; j->z = z; j->Bt = Bt; j->Ct = Ct; j->A = A;
+    j->Dskip = Dskip; j->bias = bias; j->dy = dy; j->mode = mode;
+    j->du = du; j->ddr = ddelta_raw; j->dz = dz;
+    double* p = priv + (size_t)t * per;
+    j->dBt = p; j->dCt = p + nbc; j->dA = p + 2 * nbc; j->dD = p + 2 * nbc + nda; j->dbias = p + 2 * nbc + nda + nd;
+    j->ch_begin = C * t / nthreads;
+    j->ch_end = C * (t + 1) / nthreads;
+  }
+  int started = 0;
+  for (int t = 0; t < nthreads; ++t) {
+    if (pthread_create(&tids[t], NULL, run_bjob, &jobs[t]) != 0) { rc = -2; break; }
+    ++started;
+  }
+  for (int t = 0; t < started; ++t) {
+    void* ret = NULL;
+    pthread_join(tids[t], &ret);
+    if (ret) rc = -2;
+  }
+  if (rc == 0) {
+    for (size_t i = 0; i < nbc; ++i) { dBt[i] = 0.0; dCt[i] = 0.0; }
+    for (size_t i = 0; i < nda; ++i) dA[i] = 0.0;
+    for (size_t i = 0; i < nd; ++i) { dDskip[i] = 0.0; dbias[i] = 0.0; }
+    for (int t = 0; t < nthreads; ++t) {   /* fixed order: deterministic for a given thread count */
+      const bjob_t* j = &jobs[t];
+      for (size_t i = 0; i < nbc; ++i) { dBt[i] += j->dBt[i]; dCt[i] += j->dCt[i]; }
+      for (size_t i = 0; i < nda; ++i) dA[i] += j->dA[i];
+      for (size_t i = 0; i < nd; ++i) { dDskip[i] += j->dD[i]; dbias[i] += j->dbias[i]; }
+    }
+  }
+  free(priv);
+  free(jobs);
+  free(tids);
+  return rc;
+}

@@ -36,6 +36,17 @@ MUTATIONS = {
     "conv_drops_bias": ("double acc = bias ? bias[d] : 0.0;", "double acc = 0.0;"),
     "conv_state_off_by_one": ("(s0 ? s0[K + (s)] : 0.0)", "(s0 ? s0[K - 1 + (s) + ((s) == -K)] : 0.0)"),
     "conv_final_state_shifted": ("const int64_t s = L - K + k;", "const int64_t s = L - K + k - 1;"),
+    "bwd_drops_state_carry": ("const double gn = dyc * Cb[n * L + l] + anext[n] * g[n];",
+                              "const double gn = dyc * Cb[n * L + l];"),
+    "bwd_dcoef_ddelta_wrong": ("ddelta += dabar * a * abar + dcoef * abar;", "ddelta += dabar * a * abar + dcoef;"),
+    "bwd_dA_misses_coef_term": ("j->dA[d * N + n] += dabar * delta * abar + dcoef * delta * delta * phi_coef(delta * a);",
+                                "j->dA[d * N + n] += dabar * delta * abar;"),
+    "bwd_softplus_grad_dropped": ("const double dr_l = ddelta * sigmoid(dr[l] + bias);", "const double dr_l = ddelta;"),
+    "bwd_dB_misses_coef": ("j->dBt[b * N * L + n * L + l] += gn * coef * x;", "j->dBt[b * N * L + n * L + l] += gn * x;"),
+    "bwd_dC_uses_previous_state": ("j->dCt[b * N * L + n * L + l] += dyc * H[(l + 1) * N + n];",
+                                   "j->dCt[b * N * L + n * L + l] += dyc * H[l * N + n];"),
+    "bwd_dsilu_incomplete": ("s * (1.0 + z[l] * (1.0 - s))", "s"),
+    "bwd_phi_series_wrong": ("double term = 0.5, sum = 0.0;", "double term = 1.0, sum = 0.0;"),
 }
 
 

@@ -435,3 +435,86 @@ def test_conv_one_tap_is_elementwise_and_linear_in_taps():
     assert rel(yc, ya + 2.0 * yb) < 1e-14
     y1, _ = oracle.conv1d(x, np.full((3, 1), 2.0), np.full(3, 0.25), activation=False)
     assert np.array_equal(y1, 2.0 * x + 0.25)
+
+
+# ----------------------------------------------------------------------------- backward pass
+# "Mamba论文研读笔记" 3.2.3 C: the backward pass recomputes the states.  The
+# gradients are pinned by central finite differences of the (pinned) forward
+# oracle: for J = sum(w * y), dJ/dx must equal the backward pass at dy = w.
+def _bwd_problem(rng, B=2, D=3, N=4, L=13, a_kind="random"):
+    u, dr, z, Bt, Ct, A, Dskip, bias = rand_problem(rng, B, D, N, L, a_kind)
+    return dict(u=u, delta_raw=dr, z=z, Bt=Bt, Ct=Ct, A=A, Dskip=Dskip, delta_bias=bias)
+
+
+def _fd_check(args, disc, use_z, rng, n_probe=6):
+    w = rng.standard_normal(args["u"].shape)
+    a = dict(args)
+    if not use_z:
+        a["z"] = None
+
+    def J(aa):
+        y, _ = oracle.scan(aa["u"], aa["delta_raw"], aa["z"], aa["Bt"], aa["Ct"], aa["A"], aa["Dskip"],
+                           aa["delta_bias"], discretization=disc)
+        return float(np.sum(w * y))
+
+    g = oracle.scan_bwd(a["u"], a["delta_raw"], a["z"], a["Bt"], a["Ct"], a["A"], a["Dskip"], a["delta_bias"], w,
+                        discretization=disc)
+    names = {"u": "du", "delta_raw": "ddelta_raw", "Bt": "dBt", "Ct": "dCt", "A": "dA", "Dskip": "dDskip",
+             "delta_bias": "ddelta_bias"}
+    if use_z:
+        names["z"] = "dz"
+    worst = 0.0
+    for name, gname in names.items():
+        arr = a[name]
+        for _ in range(n_probe):
+            idx = tuple(int(rng.integers(0, s)) for s in arr.shape)
+            eps = 1e-6 * max(1.0, abs(arr[idx]))
+            ap = dict(a); ap[name] = arr.copy(); ap[name][idx] += eps
+            am = dict(a); am[name] = arr.copy(); am[name][idx] -= eps
+            fd = (J(ap) - J(am)) / (2 * eps)
+            an = g[gname][idx]
+            err = abs(fd - an) / max(1e-2, abs(fd), abs(an))   # FD roundoff is ~1e-9 absolute
+            worst = max(worst, err)
+            assert err < 1e-6, (name, idx, fd, an)
+    return worst
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_bwd_matches_finite_differences_zoh(seed):
+    rng = np.random.default_rng(400 + seed)
+    _fd_check(_bwd_problem(rng), "zoh", True, rng)
+    _fd_check(_bwd_problem(rng, a_kind="s4d"), "zoh", False, rng)
+
+
+def test_bwd_matches_finite_differences_delta_b():
+    rng = np.random.default_rng(410)
+    _fd_check(_bwd_problem(rng), "delta_b", True, rng)
+
+
+def test_bwd_zero_and_tiny_A():
+    """A = 0 and |A delta| small exercise the limit and the series branch of
+    d coef / d A."""
+    rng = np.random.default_rng(420)
+    p = _bwd_problem(rng, N=3)
+    p["A"][:, 0] = 0.0
+    p["A"][:, 1] = -1e-4
+    _fd_check(p, "zoh", True, rng, n_probe=8)
+
+
+def test_bwd_gate_factor_and_linearity_in_dy():
+    """Gradients are linear in dy; with z = None they equal the gated ones at
+    dy * silu(z) for the inputs that do not see z."""
+    rng = np.random.default_rng(430)
+    p = _bwd_problem(rng)
+    w1 = rng.standard_normal(p["u"].shape)
+    w2 = rng.standard_normal(p["u"].shape)
+    args = (p["u"], p["delta_raw"], p["z"], p["Bt"], p["Ct"], p["A"], p["Dskip"], p["delta_bias"])
+    g1 = oracle.scan_bwd(*args, w1)
+    g2 = oracle.scan_bwd(*args, w2)
+    g12 = oracle.scan_bwd(*args, w1 + 3.0 * w2)
+    for k in ("du", "dBt", "dA", "ddelta_bias", "dz"):
+        assert rel(g12[k], g1[k] + 3.0 * g2[k]) < 1e-12
+    nz = (p["u"], p["delta_raw"], None, p["Bt"], p["Ct"], p["A"], p["Dskip"], p["delta_bias"])
+    gn = oracle.scan_bwd(*nz, w1 * np_silu(p["z"]))
+    for k in ("du", "ddelta_raw", "dBt", "dCt", "dA", "dDskip", "ddelta_bias"):
+        assert rel(gn[k], g1[k]) < 1e-12
