@@ -1,8 +1,8 @@
 /*
  * mamba_scan.h -- C ABI of the MI355X (gfx950) Mamba-1 selective scan (S6)
- * forward pass and the single-token selective state update, plus the causal
- * depthwise conv1d + SiLU that produces the scan input and its one-token
- * update (declared last).
+ * forward pass and the single-token selective state update, the backward pass
+ * of the scan, and the causal depthwise conv1d + SiLU that produces the scan
+ * input with its one-token update (the last two groups declared last).
  *
  * What the calls compute (pages cited by title and section):
  *   "Mamba 模型" (gaos6e.github.io), full-step flowchart nodes H to M and
@@ -140,6 +140,44 @@ int mamba_state_update(float* state, const void* u, const void* delta, const voi
                        int64_t B, int64_t D, int64_t N,
                        mamba_dtype_t in_dtype, mamba_dtype_t out_dtype,
                        unsigned flags, hipStream_t stream);
+
+/*
+ * Bytes of device workspace mamba_scan_bwd needs (shape only; callable
+ * without a GPU), (size_t)-1 for an invalid shape.
+ */
+size_t mamba_scan_bwd_workspace_size(int64_t B, int64_t D, int64_t N, int64_t L);
+
+/*
+ * Backward pass of mamba_scan_fwd (initial state zero): the gradients of all
+ * inputs for an output gradient dy.  The states are recomputed from the inputs
+ * rather than read back ("Mamba论文研读笔记" 3.2.3 C, recomputation;
+ * "Mamba 与状态空间模型" section 07).
+ *
+ *   u, delta, z, Bt, Ct, A, Dskip, delta_bias : as for mamba_scan_fwd
+ *                 (in_dtype; z, Dskip, delta_bias may be NULL).
+ *   dy          : (B, D, L) grad_dtype, gradient of y.
+ *   du, ddelta  : (B, D, L) grad_dtype, written; ddelta is the gradient of
+ *                 the raw delta (before bias and softplus).
+ *   dz          : (B, D, L) grad_dtype, written; required iff z is given.
+ *   dBt, dCt    : (B, N, L) fp32, written (summed over the D channels).
+ *   dA          : (D, N) fp32; dDskip, ddelta_bias : (D) fp32, written
+ *                 (summed over batch rows and time), also when Dskip or
+ *                 delta_bias is NULL.
+ *   flags       : MAMBA_FLAG_DELTA_B selects the simplified rule, as in the
+ *                 forward pass; the cancellation-free (Abar - 1)/A is always used.
+ *   workspace   : at least mamba_scan_bwd_workspace_size bytes, 256-byte
+ *                 aligned; contents on entry ignored.
+ *
+ * Alignment: the dtype inputs and gradients to their element size; fp32
+ * arrays 4-byte.  All outputs are overwritten (not accumulated into); the
+ * result is deterministic (fixed-order reductions).  1 <= N <= 16.
+ */
+int mamba_scan_bwd(const void* u, const void* delta, const void* z, const void* Bt, const void* Ct,
+                   const float* A, const float* Dskip, const float* delta_bias, const void* dy,
+                   void* du, void* ddelta, void* dz, float* dBt, float* dCt, float* dA, float* dDskip,
+                   float* ddelta_bias, int64_t B, int64_t D, int64_t N, int64_t L,
+                   mamba_dtype_t in_dtype, mamba_dtype_t grad_dtype, unsigned flags,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Causal depthwise convolution along the sequence, then SiLU: the step that

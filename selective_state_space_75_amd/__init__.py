@@ -8,7 +8,8 @@ torch tensors to that library, and ``workloads`` draws the seeded synthetic
 inputs.
 """
 from ._lib import (FLAG_ACCURATE_EXPM1, FLAG_DELTA_B, MambaError, conv1d_fwd, conv1d_update,  # noqa: F401
-                   lib, scan_fwd, state_update, status_string, workspace_size)
+                   lib, scan_bwd, scan_bwd_workspace_size, scan_fwd, state_update, status_string,
+                   workspace_size)
 
-__all__ = ["scan_fwd", "state_update", "conv1d_fwd", "conv1d_update", "workspace_size", "status_string", "lib",
+__all__ = ["scan_fwd", "scan_bwd", "scan_bwd_workspace_size", "state_update", "conv1d_fwd", "conv1d_update", "workspace_size", "status_string", "lib",
            "MambaError", "FLAG_DELTA_B", "FLAG_ACCURATE_EXPM1"]

@@ -51,6 +51,10 @@ def lib() -> ctypes.CDLL:
             L.mamba_scan_fwd.restype = c_int
             L.mamba_state_update.argtypes = [vp] * 10 + [i64] * 3 + [c_int, c_int, u32, vp]
             L.mamba_state_update.restype = c_int
+            L.mamba_scan_bwd_workspace_size.argtypes = [i64, i64, i64, i64]
+            L.mamba_scan_bwd_workspace_size.restype = ctypes.c_size_t
+            L.mamba_scan_bwd.argtypes = [vp] * 17 + [i64] * 4 + [c_int, c_int, u32, vp, ctypes.c_size_t, vp]
+            L.mamba_scan_bwd.restype = c_int
             L.mamba_conv1d_fwd.argtypes = [vp] * 5 + [i64] * 4 + [c_int, c_int, c_int, vp]
             L.mamba_conv1d_fwd.restype = c_int
             L.mamba_conv1d_update.argtypes = [vp] * 5 + [i64] * 3 + [c_int, c_int, vp]
@@ -261,3 +265,56 @@ def conv1d_update(state, x, weight, bias=None, *, out_dtype=None, y=None, stream
     if st != 0:
         raise MambaError(st, "mamba_conv1d_update")
     return y
+
+
+def scan_bwd_workspace_size(B: int, D: int, N: int, L: int) -> int:
+    n = lib().mamba_scan_bwd_workspace_size(B, D, N, L)
+    if n == ctypes.c_size_t(-1).value:
+        raise MambaError(-2, "mamba_scan_bwd_workspace_size")
+    return n
+
+
+def scan_bwd(u, delta, z, Bt, Ct, A, Dskip, delta_bias, dy, *, grad_dtype=None, delta_b=False, workspace=None,
+             stream=None):
+    """Gradients of scan_fwd (zero initial state) for output gradient dy (B, D, L).
+
+    Returns a dict: du, ddelta, dz (B, D, L) in grad_dtype (dz None when z is
+    None); dBt, dCt (B, N, L), dA (D, N), dDskip (D), ddelta_bias (D) fp32.
+    """
+    torch = _torch()
+    if u.dim() != 3 or Bt.dim() != 3:
+        raise ValueError("u must be (B, D, L) and Bt (B, N, L)")
+    B, D, L = u.shape
+    N = Bt.shape[1]
+    dev = u.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU device")
+    in_dt = u.dtype
+    _dtype_code(u)
+    for t, n, shp in ((u, "u", (B, D, L)), (delta, "delta", (B, D, L)), (z, "z", (B, D, L)),
+                      (Bt, "Bt", (B, N, L)), (Ct, "Ct", (B, N, L))):
+        _check(t, n, shp, in_dt, dev)
+    _check(A, "A", (D, N), torch.float32, dev)
+    _check(Dskip, "Dskip", (D,), torch.float32, dev)
+    _check(delta_bias, "delta_bias", (D,), torch.float32, dev)
+    gdt = dy.dtype if grad_dtype is None else grad_dtype
+    _check(dy, "dy", (B, D, L), gdt, dev)
+    out = {"du": torch.empty((B, D, L), dtype=gdt, device=dev), "ddelta": torch.empty((B, D, L), dtype=gdt, device=dev),
+           "dz": torch.empty((B, D, L), dtype=gdt, device=dev) if z is not None else None,
+           "dBt": torch.empty((B, N, L), dtype=torch.float32, device=dev),
+           "dCt": torch.empty((B, N, L), dtype=torch.float32, device=dev),
+           "dA": torch.empty((D, N), dtype=torch.float32, device=dev),
+           "dDskip": torch.empty((D,), dtype=torch.float32, device=dev),
+           "ddelta_bias": torch.empty((D,), dtype=torch.float32, device=dev)}
+    wsb = scan_bwd_workspace_size(B, D, N, L)
+    if workspace is None:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    st = lib().mamba_scan_bwd(
+        _ptr(u), _ptr(delta), _ptr(z), _ptr(Bt), _ptr(Ct), _ptr(A), _ptr(Dskip), _ptr(delta_bias), _ptr(dy),
+        _ptr(out["du"]), _ptr(out["ddelta"]), _ptr(out["dz"]), _ptr(out["dBt"]), _ptr(out["dCt"]), _ptr(out["dA"]),
+        _ptr(out["dDskip"]), _ptr(out["ddelta_bias"]), B, D, N, L, _dtype_code(u), _dtype_code(dy),
+        FLAG_DELTA_B if delta_b else 0, _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(dev, stream))
+    if st != 0:
+        raise MambaError(st, "mamba_scan_bwd")
+    return out

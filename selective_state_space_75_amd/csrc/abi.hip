@@ -140,6 +140,26 @@ constexpr unsigned kKnownFlags = MAMBA_FLAG_DELTA_B | MAMBA_FLAG_ACCURATE_EXPM1;
 
 }  // namespace
 
+struct BwdPlan {
+  int64_t tiles_d = 0, nck = 0;
+  size_t off_ckpt = 0, off_pb = 0, off_pc = 0, off_pa = 0, off_pd = 0, off_pbias = 0, bytes = 0;
+};
+
+BwdPlan make_bwd_plan(int64_t B, int64_t D, int64_t L) {
+  BwdPlan q;
+  q.tiles_d = (D + 15) / 16;
+  q.nck = (L + 31) / 32;
+  size_t o = 0;
+  q.off_ckpt = o; o += align256(size_t(B) * size_t(D) * size_t(q.nck) * 16 * sizeof(float));
+  q.off_pb = o; o += align256(size_t(B) * size_t(q.tiles_d) * 16 * size_t(L) * sizeof(float));
+  q.off_pc = o; o += align256(size_t(B) * size_t(q.tiles_d) * 16 * size_t(L) * sizeof(float));
+  q.off_pa = o; o += align256(size_t(B) * size_t(D) * 16 * sizeof(float));
+  q.off_pd = o; o += align256(size_t(B) * size_t(D) * sizeof(float));
+  q.off_pbias = o; o += align256(size_t(B) * size_t(D) * sizeof(float));
+  q.bytes = o;
+  return q;
+}
+
 extern "C" {
 
 size_t mamba_scan_workspace_size(int64_t B, int64_t D, int64_t N, int64_t L) {
@@ -241,6 +261,57 @@ int mamba_state_update(float* state, const void* u, const void* delta, const voi
   const Dt in = in_dtype == MAMBA_BF16 ? Dt::BF16 : Dt::F32;
   const Dt out = out_dtype == MAMBA_BF16 ? Dt::BF16 : Dt::F32;
   return mamba::launch_state_update(p, in, out, stream) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
+}
+
+size_t mamba_scan_bwd_workspace_size(int64_t B, int64_t D, int64_t N, int64_t L) {
+  if (!shape_ok(B, D, N, L) || N > 16) return (size_t)-1;
+  return make_bwd_plan(B, D, L).bytes;
+}
+
+int mamba_scan_bwd(const void* u, const void* delta, const void* z, const void* Bt, const void* Ct,
+                   const float* A, const float* Dskip, const float* delta_bias, const void* dy,
+                   void* du, void* ddelta, void* dz, float* dBt, float* dCt, float* dA, float* dDskip,
+                   float* ddelta_bias, int64_t B, int64_t D, int64_t N, int64_t L,
+                   mamba_dtype_t in_dtype, mamba_dtype_t grad_dtype, unsigned flags,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!dtype_ok(in_dtype) || !dtype_ok(grad_dtype)) return MAMBA_ERR_DTYPE;
+  if (flags & ~kKnownFlags) return MAMBA_ERR_UNSUPPORTED;
+  if (!shape_ok(B, D, N, L)) return MAMBA_ERR_SHAPE;
+  if (N > 16) return MAMBA_ERR_UNSUPPORTED;
+  if (!u || !delta || !Bt || !Ct || !A || !dy || !du || !ddelta || !dBt || !dCt || !dA || !dDskip ||
+      !ddelta_bias || (z && !dz))
+    return MAMBA_ERR_NULL;
+  const size_t ei = in_dtype == MAMBA_BF16 ? 2 : 4, eg = grad_dtype == MAMBA_BF16 ? 2 : 4;
+  for (const void* ptr : {u, delta, z, Bt, Ct})
+    if (ptr && !aligned(ptr, ei)) return MAMBA_ERR_ALIGN;
+  for (const void* ptr : {dy, (const void*)du, (const void*)ddelta, (const void*)dz})
+    if (ptr && !aligned(ptr, eg)) return MAMBA_ERR_ALIGN;
+  for (const void* ptr : {(const void*)A, (const void*)Dskip, (const void*)delta_bias, (const void*)dBt,
+                          (const void*)dCt, (const void*)dA, (const void*)dDskip, (const void*)ddelta_bias})
+    if (ptr && !aligned(ptr, 4)) return MAMBA_ERR_ALIGN;
+  const BwdPlan plan = make_bwd_plan(B, D, L);
+  if (B * plan.tiles_d >= (int64_t(1) << 31) || (B * N * L + 255) / 256 >= (int64_t(1) << 31))
+    return MAMBA_ERR_SHAPE;
+  if (!workspace || workspace_bytes < plan.bytes) return MAMBA_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return MAMBA_ERR_ALIGN;
+
+  mamba::BwdParams p{};
+  p.u = u; p.delta = delta; p.z = z; p.Bt = Bt; p.Ct = Ct; p.dy = dy;
+  p.A = A; p.Dskip = Dskip; p.bias = delta_bias;
+  p.du = du; p.ddelta = ddelta; p.dz = z ? dz : nullptr;
+  p.dBt = dBt; p.dCt = dCt; p.dA = dA; p.dDskip = dDskip; p.dbias = ddelta_bias;
+  char* ws = static_cast<char*>(workspace);
+  p.ckpt = reinterpret_cast<float*>(ws + plan.off_ckpt);
+  p.part_dB = reinterpret_cast<float*>(ws + plan.off_pb);
+  p.part_dC = reinterpret_cast<float*>(ws + plan.off_pc);
+  p.part_dA = reinterpret_cast<float*>(ws + plan.off_pa);
+  p.part_dD = reinterpret_cast<float*>(ws + plan.off_pd);
+  p.part_dbias = reinterpret_cast<float*>(ws + plan.off_pbias);
+  p.B = B; p.D = D; p.N = N; p.L = L; p.tiles_d = plan.tiles_d; p.nck = plan.nck;
+  p.delta_b = (flags & MAMBA_FLAG_DELTA_B) ? 1 : 0;
+  const Dt in = in_dtype == MAMBA_BF16 ? Dt::BF16 : Dt::F32;
+  const Dt gd = grad_dtype == MAMBA_BF16 ? Dt::BF16 : Dt::F32;
+  return mamba::launch_scan_bwd(p, in, gd, stream) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
 }
 
 int mamba_conv1d_fwd(const void* x, const float* weight, const float* bias, void* y, float* final_state,

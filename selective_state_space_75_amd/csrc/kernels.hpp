@@ -76,12 +76,26 @@ struct ConvParams {
   int64_t rows, D, L, K;  // rows = B * D
 };
 
+// Backward pass of the scan.
+struct BwdParams {
+  const void *u, *delta, *z, *Bt, *Ct, *dy;
+  const float *A, *Dskip, *bias;
+  void *du, *ddelta, *dz;                       // grad dtype, (B, D, L)
+  float *dBt, *dCt, *dA, *dDskip, *dbias;       // fp32 results
+  float *ckpt;                                  // (B, D, nck, 16) chunk-start states
+  float *part_dB, *part_dC;                     // (B, tiles_d, 16, L) per-tile sums over channels
+  float *part_dA, *part_dD, *part_dbias;        // (B, D, 16), (B, D), (B, D) per-batch-row sums
+  int64_t B, D, N, L, tiles_d, nck;
+  int delta_b;
+};
+
 // Each returns hipSuccess or the launch error.
 hipError_t launch_scan_full(const ScanParams& p, Dt in, Dt out, hipStream_t s);
 hipError_t launch_scan_summary(const ScanParams& p, Dt in, hipStream_t s);
 hipError_t launch_scan_carry(const ScanParams& p, hipStream_t s);
 hipError_t launch_scan_v4(const ScanParams& p, const V2Params& q, Dt in, Dt out, bool summary, hipStream_t s);
 hipError_t launch_state_update(const UpdateParams& p, Dt in, Dt out, hipStream_t s);
+hipError_t launch_scan_bwd(const BwdParams& p, Dt in, Dt grad, hipStream_t s);
 hipError_t launch_conv1d_fwd(const ConvParams& p, Dt in, Dt out, bool vec, hipStream_t s);
 hipError_t launch_conv1d_update(const ConvParams& p, Dt in, Dt out, hipStream_t s);
 

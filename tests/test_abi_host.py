@@ -28,8 +28,8 @@ def declared_functions():
 
 def test_header_symbols_are_exported():
     names = declared_functions()
-    assert names == ["mamba_conv1d_fwd", "mamba_conv1d_update", "mamba_scan_fwd", "mamba_scan_workspace_size",
-                     "mamba_state_update", "mamba_status_string"]
+    assert names == ["mamba_conv1d_fwd", "mamba_conv1d_update", "mamba_scan_bwd", "mamba_scan_bwd_workspace_size",
+                     "mamba_scan_fwd", "mamba_scan_workspace_size", "mamba_state_update", "mamba_status_string"]
     L = _lib.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -179,3 +179,36 @@ def test_conv_optional_pointers():
     # bias may be NULL and final_state is ignored when not requested: with every
     # other argument valid the call only fails at the size check we force here
     assert conv(bias=None, fs=None, rfs=0, K=9) == UNSUP
+
+
+def test_bwd_workspace_size():
+    ws = _lib.scan_bwd_workspace_size
+    a = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    B, D, N, L = 2, 70, 5, 100
+    tiles, nck = 5, 4
+    assert ws(B, D, N, L) == (a(B * D * nck * 16 * 4) + 2 * a(B * tiles * 16 * L * 4) + a(B * D * 16 * 4)
+                              + 2 * a(B * D * 4))
+    assert _lib.lib().mamba_scan_bwd_workspace_size(1, 1, 17, 1) == ctypes.c_size_t(-1).value
+
+
+def bwd(**kw):
+    a = dict(u=P, delta=P, z=P, Bt=P, Ct=P, A=P, Dskip=P, bias=P, dy=P, du=P, ddelta=P, dz=P, dBt=P, dCt=P,
+             dA=P, dD=P, dbias=P, B=2, D=64, N=16, L=64, ind=BF16, gd=F32, flags=0, ws=P, wsb=1 << 40)
+    a.update(kw)
+    vp = lambda v: ctypes.c_void_p(v) if v is not None else None  # noqa: E731
+    return _lib.lib().mamba_scan_bwd(*[vp(a[k]) for k in ("u", "delta", "z", "Bt", "Ct", "A", "Dskip", "bias", "dy",
+                                                         "du", "ddelta", "dz", "dBt", "dCt", "dA", "dD", "dbias")],
+                                     a["B"], a["D"], a["N"], a["L"], a["ind"], a["gd"], a["flags"], vp(a["ws"]),
+                                     a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ind=4), DTYPE), (dict(gd=-2), DTYPE), (dict(flags=0x40), UNSUP),
+    (dict(B=0), SHAPE), (dict(N=17), UNSUP),
+    (dict(u=None), NULL), (dict(dy=None), NULL), (dict(dBt=None), NULL), (dict(dA=None), NULL),
+    (dict(dz=None), NULL), (dict(dbias=None), NULL),
+    (dict(u=P + 1), ALIGN), (dict(dy=P + 2), ALIGN), (dict(dA=P + 2), ALIGN),
+    (dict(ws=None), WS), (dict(wsb=1024), WS), (dict(ws=P + 16), ALIGN),
+])
+def test_bwd_rejects_bad_arguments(kw, code):
+    assert bwd(**kw) == code
