@@ -12,7 +12,8 @@ Other workloads: --workload long_b1 (B=1 D=4096 L=131072, chunked along L),
 mamba130m_layer, tiny_fp32, decode48 (48 layers x 128 steps of
 mamba_state_update at B=128 D=4096, the 48-layer step replayed as a graph),
 conv_2.8b_layer (causal conv1d + SiLU at B=4 D=5120 L=2048 K=4) and
-conv_decode48 (48 layers x 128 steps of the one-token conv update).
+conv_decode48 (48 layers x 128 steps of the one-token conv update) and
+bwd_2.8b_layer (the scan's backward pass at the 2.8B-layer shape).
 
 --copy-calibration runs only a plain device copy of known size (used to
 scale rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes).
@@ -378,6 +379,68 @@ def bench_conv_decode(args, dev):
     }
 
 
+# fp32 lane-operations of one state update in the backward pass, counted as the
+# method needs them once: the forward step (6 + exp) and the reverse step (the
+# state adjoint, the four input coefficients' partials, dB/dC/du/ddelta/dA
+# accumulations and exp of the step again: 22).
+OPS_PER_UPDATE_BWD = 29
+
+
+def bench_bwd(args, dev):
+    """Backward pass at the 2.8B-layer shape: bf16 inputs, dy and input gradients."""
+    import torch
+    import selective_state_space_75_amd as m
+    from selective_state_space_75_amd import workloads as W
+    cfg = W.SCAN_CONFIGS["mamba2.8b_layer"]
+    log("bwd workload: B=%d D=%d N=%d L=%d" % (cfg.B, cfg.D, cfg.N, cfg.L))
+    sets = []
+    for k in range(2):
+        xs = W.scan_inputs(W.ScanConfig(cfg.name, cfg.B, cfg.D, cfg.N, cfg.L, cfg.dtype, cfg.seed + 100 * k,
+                                        cfg.dskip, cfg.final_state))
+        t = {k2: to_dev(xs[k2], dev) for k2 in ("u", "delta_raw", "z", "Bt", "Ct", "A", "Dskip", "delta_bias")}
+        t["dy"] = torch.randn((cfg.B, cfg.D, cfg.L), device=dev).to(torch.bfloat16)
+        sets.append(t)
+    ws = torch.empty(m.scan_bwd_workspace_size(cfg.B, cfg.D, cfg.N, cfg.L), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        t = sets[i % len(sets)]
+        m.scan_bwd(t["u"], t["delta_raw"], t["z"], t["Bt"], t["Ct"], t["A"], t["Dskip"], t["delta_bias"], t["dy"],
+                   workspace=ws, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    steps = min(args.steps, 20)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [a.elapsed_time(b) for a, b in ev]
+    call_ms = float(np.mean(per))
+    e = cfg.elements
+    bc = cfg.B * cfg.N * cfg.L
+    nbytes = e * 2 * 4 + bc * 2 * 2 + e * 2 * 3 + bc * 4 * 2 + cfg.D * (cfg.N + 3) * 4 * 2
+    ops = cfg.updates * OPS_PER_UPDATE_BWD
+    ach = ops / (call_ms * 1e-3) / 1e12
+    return {
+        "metric": "scan backward: algorithmic GB/s and fp32 lane-op rate at Mamba-2.8B layer shape",
+        "value": round(nbytes / (wall / steps) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps,
+        "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / steps, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "io_dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "bwd_2.8b_layer", "B": cfg.B, "D": cfg.D, "N": cfg.N, "L": cfg.L,
+                   "grads": "du, ddelta, dz bf16; dB, dC, dA, dD, dbias fp32"},
+        "call_ms_mean": round(call_ms, 5), "algorithmic_bytes": nbytes,
+        "roofline": {"bound": "alu", "achieved": round(ach, 3), "peak": round(VALU_PEAK_TOPS, 2), "unit": "TOP/s",
+                     "frac": round(ach / VALU_PEAK_TOPS, 4), "traffic": None, "ops_per_update": OPS_PER_UPDATE_BWD,
+                     "launch_time": "whole call: recompute kernel + two reduce kernels"},
+    }
+
+
 def copy_calibration(args, dev):
     import torch
     n = args.copy_mb * (1 << 20) // 4
@@ -418,6 +481,8 @@ def main():
     from selective_state_space_75_amd import workloads as W
     if args.workload == "decode48":
         line = bench_decode(args, dev)
+    elif args.workload == "bwd_2.8b_layer":
+        line = bench_bwd(args, dev)
     elif args.workload in W.CONV_CONFIGS:
         line = bench_conv(args, dev)
     elif args.workload in W.CONV_UPDATE_CONFIGS:

@@ -148,7 +148,7 @@ struct BwdPlan {
 BwdPlan make_bwd_plan(int64_t B, int64_t D, int64_t L) {
   BwdPlan q;
   q.tiles_d = (D + 15) / 16;
-  q.nck = (L + 31) / 32;
+  q.nck = (L + mamba::kBwdChunk - 1) / mamba::kBwdChunk;
   size_t o = 0;
   q.off_ckpt = o; o += align256(size_t(B) * size_t(D) * size_t(q.nck) * 16 * sizeof(float));
   q.off_pb = o; o += align256(size_t(B) * size_t(q.tiles_d) * 16 * size_t(L) * sizeof(float));
@@ -309,6 +309,9 @@ int mamba_scan_bwd(const void* u, const void* delta, const void* z, const void* 
   p.part_dbias = reinterpret_cast<float*>(ws + plan.off_pbias);
   p.B = B; p.D = D; p.N = N; p.L = L; p.tiles_d = plan.tiles_d; p.nck = plan.nck;
   p.delta_b = (flags & MAMBA_FLAG_DELTA_B) ? 1 : 0;
+  p.vec = L % 4 == 0;
+  for (const void* ptr : {u, delta, z, Bt, Ct, dy, (const void*)du, (const void*)ddelta, (const void*)dz})
+    if (ptr && !aligned(ptr, 16)) p.vec = 0;
   const Dt in = in_dtype == MAMBA_BF16 ? Dt::BF16 : Dt::F32;
   const Dt gd = grad_dtype == MAMBA_BF16 ? Dt::BF16 : Dt::F32;
   return mamba::launch_scan_bwd(p, in, gd, stream) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;

@@ -77,6 +77,9 @@ struct ConvParams {
 };
 
 // Backward pass of the scan.
+// Steps per recomputed chunk of the backward pass: one stored start state each.
+constexpr int kBwdChunk = 16;
+
 struct BwdParams {
   const void *u, *delta, *z, *Bt, *Ct, *dy;
   const float *A, *Dskip, *bias;
@@ -87,6 +90,7 @@ struct BwdParams {
   float *part_dA, *part_dD, *part_dbias;        // (B, D, 16), (B, D), (B, D) per-batch-row sums
   int64_t B, D, N, L, tiles_d, nck;
   int delta_b;
+  int vec;      // L % 4 == 0 and every (B, D, L) / (B, N, L) array 16-byte aligned
 };
 
 // Each returns hipSuccess or the launch error.

@@ -9,8 +9,8 @@
 // Per channel and state (lane layout of the forward kernel: one wave owns 16
 // channels of one batch row, four lanes per channel, four states per lane):
 //   pass 1: run the recurrence forward and store h at the start of every
-//           32-step chunk (workspace, fp32);
-//   pass 2: for each chunk from the last: rerun its 32 steps from the stored
+//           16-step chunk (workspace, fp32);
+//   pass 2: for each chunk from the last: rerun its 16 steps from the stored
 //           start state, keeping h_t in the wave's LDS, then walk them in
 //           reverse with the state adjoint g_t = dyc_t C_t + Abar_(t+1) g_(t+1):
 //             dyc  = dy * silu(z)            dz = dy * yc * s (1 + z (1 - s))
@@ -20,30 +20,22 @@
 //             dA  += dAbar delta Abar + dcoef delta^2 phi(delta a)   (ZOH)
 //             ddelta_raw = ddelta * sigmoid(delta_raw + bias)
 //           with phi(x) = (x e^x - e^x + 1) / x^2 (a series near 0).
-// dB_t and dC_t are shared by the D channels of a batch row: each wave sums
-// its 16 channels (two DPP row rotations, then LDS atomics across the four
-// rows) into a per-tile partial; a second kernel adds the partials of all
-// tiles in a fixed order, and the per-batch-row partials of dA, dD and the
-// bias gradient likewise, so results are deterministic.
+// Each chunk's inputs are loaded with vector loads one chunk ahead and
+// staged in LDS; the per-element terms (softplus, its derivative, the gate)
+// are evaluated once there, not once per lane of a channel.
+// dB_t and dC_t are shared by the D channels of a batch row: each step, the
+// wave sums its 16 channels' contributions with cross-lane swaps (permlane32,
+// permlane16, two DPP row rotations) into one per-tile partial per state; a
+// second kernel adds the partials of all tiles in a fixed order, and the
+// per-batch-row partials of dA, dD and the bias gradient likewise, so results
+// are deterministic.
 #include "device_math.hpp"
 #include "kernels.hpp"
 
 namespace mamba {
 namespace {
 
-constexpr int kBC = 32;   // steps per recomputed chunk
-
-template <bool kBF16>
-__device__ __forceinline__ float ldv(const void* base, int64_t i) {
-  if constexpr (kBF16) return bf16_to_f32(static_cast<const uint16_t*>(base)[i]);
-  else return static_cast<const float*>(base)[i];
-}
-
-template <bool kBF16>
-__device__ __forceinline__ void stv(void* base, int64_t i, float v) {
-  if constexpr (kBF16) static_cast<uint16_t*>(base)[i] = f32_to_bf16(v);
-  else static_cast<float*>(base)[i] = v;
-}
+constexpr int kBC = kBwdChunk;
 
 // Sum over the four lanes of a quad (DPP quad permutations).
 __device__ __forceinline__ float quad_sum4(float v) {
@@ -52,58 +44,128 @@ __device__ __forceinline__ float quad_sum4(float v) {
   return v;
 }
 
-// Sum over the four lanes of a 16-lane row that share lane & 3 (row rotations
-// by 4 and 8): every lane of the row ends with the sum for its own lane & 3.
-__device__ __forceinline__ float row_sum_same_g(float v) {
-  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
-  return v;
-}
-
-// (x e^x - e^x + 1) / x^2 given e = e^x: the Taylor series
-// sum_k (k+1) x^k / (k+2)! for |x| < 1/2 (next term below 2^-31 there),
-// the closed form otherwise.
-__device__ __forceinline__ float phi_coef(float x, float e) {
-  if (__builtin_fabsf(x) < 0.5f) {
-    float p = 1.0f / 403200.0f;
-    p = __builtin_fmaf(x, p, 1.0f / 45360.0f);
-    p = __builtin_fmaf(x, p, 1.0f / 5760.0f);
-    p = __builtin_fmaf(x, p, 1.0f / 840.0f);
-    p = __builtin_fmaf(x, p, 1.0f / 144.0f);
-    p = __builtin_fmaf(x, p, 1.0f / 30.0f);
-    p = __builtin_fmaf(x, p, 1.0f / 8.0f);
-    p = __builtin_fmaf(x, p, 1.0f / 3.0f);
-    return __builtin_fmaf(x, p, 0.5f);
-  }
-  return (x * e - (e - 1.0f)) / (x * x);
-}
-
 __device__ __forceinline__ float sigmoidf(float x) { return hw_rcp(1.0f + hw_exp2(-x * kLog2e)); }
 
-template <bool kInBF16, bool kGradBF16>
+// Four consecutive elements of one row as loaded from global memory; they
+// are widened only where they are consumed, so the loads stay in flight
+// across the chunk being computed.
+template <bool kBF16> struct Raw4;
+template <> struct Raw4<true> {
+  uint2 w;
+  __device__ __forceinline__ float get(int j) const {
+    const uint32_t x = j < 2 ? w.x : w.y;
+    return (j & 1) ? bf16_hi(x) : bf16_lo(x);
+  }
+};
+template <> struct Raw4<false> {
+  float4 f;
+  __device__ __forceinline__ float get(int j) const { return j == 0 ? f.x : j == 1 ? f.y : j == 2 ? f.z : f.w; }
+};
+
+// Elements off .. off + 3 of `base`: one vector load when `vec` (the caller
+// guarantees alignment and bounds), else element loads with zeros from index
+// `valid` on (and everywhere when !ok).
+template <bool kBF16>
+__device__ __forceinline__ void ld_raw4(Raw4<kBF16>& r, const void* base, int64_t off, bool vec, bool ok, int valid) {
+  if constexpr (kBF16) {
+    const uint16_t* q = static_cast<const uint16_t*>(base) + off;
+    if (vec) {
+      r.w = ok ? *reinterpret_cast<const uint2*>(q) : make_uint2(0u, 0u);
+    } else {
+      uint32_t h[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) h[j] = (ok && j < valid) ? (uint32_t)q[j] : 0u;
+      r.w = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+    }
+  } else {
+    const float* q = static_cast<const float*>(base) + off;
+    if (vec) {
+      r.f = ok ? *reinterpret_cast<const float4*>(q) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    } else {
+      float h[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) h[j] = (ok && j < valid) ? q[j] : 0.0f;
+      r.f = make_float4(h[0], h[1], h[2], h[3]);
+    }
+  }
+}
+
+// Stores v[0..3] at off .. off + 3 (vector store when `vec`, else the first
+// `valid` elements).
+template <bool kBF16>
+__device__ __forceinline__ void st4(void* base, int64_t off, bool vec, int valid, const float (&v)[4]) {
+  if constexpr (kBF16) {
+    uint16_t* q = static_cast<uint16_t*>(base) + off;
+    if (vec) {
+      *reinterpret_cast<uint2*>(q) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (j < valid) q[j] = f32_to_bf16(v[j]);
+    }
+  } else {
+    float* q = static_cast<float*>(base) + off;
+    if (vec) {
+      *reinterpret_cast<float4*>(q) = make_float4(v[0], v[1], v[2], v[3]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (j < valid) q[j] = v[j];
+    }
+  }
+}
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, false));
+}
+
+// x + y summed across the two wave halves: lanes 0-31 get the sum of x over
+// lanes l and l + 32, lanes 32-63 the sum of y over lanes l - 32 and l.
+__device__ __forceinline__ float swap32_sum(float x, float y) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, y),
+                                                  false, false);
+  const unsigned r0 = r[0], r1 = r[1];   // elements as scalars: bit-casting a subscript reads element 0
+  return __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
+}
+// The same across the two rows of each 32-lane half: even rows get the sum of
+// x over the row pair, odd rows the sum of y.
+__device__ __forceinline__ float swap16_sum(float x, float y) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, y),
+                                                  false, false);
+  const unsigned r0 = r[0], r1 = r[1];   // elements as scalars: bit-casting a subscript reads element 0
+  return __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
+}
+
+// Inputs of one chunk for the wave's 16 channels, staged in LDS.  The walk
+// over a step overwrites that step's entries with its results.
+struct BwdStage {
+  float4 V[kBC][16];   // [step][channel] {u, delta, dyc, kz}; after the walk {du, ddelta/sigmoid', dz, -}
+  float B[kBC][16];    // [step][state] B_t; after the walk the tile's dB_t partial
+  float C[kBC][16];    // [step][state] C_t; after the walk the tile's dC_t partial
+};
+
+template <bool kInBF16, bool kGradBF16, bool kDeltaB>
 __global__ __launch_bounds__(64) void scan_bwd_kernel(BwdParams p) {
-  __shared__ float4 Hs[kBC][64];      // h_t of the chunk being walked, per lane
-  __shared__ float AccB[kBC][16];     // dB_t partial of this tile, [step][state]
-  __shared__ float AccC[kBC][16];
+  __shared__ float4 Hs[kBC + 1][64];   // chunk start state, then h_t after each step, per lane
+  __shared__ BwdStage S[2];
   const int lane = threadIdx.x;
   const int c = lane >> 2, g = lane & 3;
   const int64_t b = (int64_t)blockIdx.x / p.tiles_d;
   const int64_t td = (int64_t)blockIdx.x - b * p.tiles_d;
-  const int64_t N = p.N, L = p.L, D = p.D;
+  const int64_t N = p.N, L = p.L, D = p.D, nck = p.nck;
   const int64_t d = td * 16 + c;
   const bool c_ok = d < D;
   const int64_t dd = c_ok ? d : 0;          // channels past D read channel 0 and contribute nothing
-  const float cmask = c_ok ? 1.0f : 0.0f;
   const int64_t row = (b * D + dd) * L;
-  const int64_t brow = b * N * L;
+  const bool has_z = p.z != nullptr;
+  const bool vecp = p.vec != 0;
 
   float a[4], a2[4], ia[4];
-  bool n_ok[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int64_t n = 4 * g + i;
-    n_ok[i] = n < N;
-    float an = n_ok[i] ? p.A[dd * N + n] : -1.0f;
+    float an = n < N ? p.A[dd * N + n] : -1.0f;
     // |A| < 2^-40 (including 0) as +-2^-40: the coefficient is then delta to
     // within delta * 2^-41, and its derivative in A is delta^2 / 2
     if (__builtin_fabsf(an) < 0x1p-40f) an = (an > 0.0f) ? 0x1p-40f : -0x1p-40f;
@@ -113,140 +175,262 @@ __global__ __launch_bounds__(64) void scan_bwd_kernel(BwdParams p) {
   }
   const float bias = p.bias ? p.bias[dd] : 0.0f;
   const float Dd = p.Dskip ? p.Dskip[dd] : 0.0f;
-  auto bc = [&](const void* base, int i, int64_t t) -> float {
-    return n_ok[i] ? ldv<kInBF16>(base, brow + (4 * g + i) * L + t) : 0.0f;
+  // B/C role of a lane when staging and writing out: state sn, steps 4 sq ..
+  const int sn = lane >> 2, sq = lane & 3;
+  const bool sn_ok = sn < N;
+  const int64_t brow = (b * N + (sn_ok ? sn : 0)) * L;
+  // lane's slot for the reduced dB/dC value of a step: type (lane bit 5),
+  // state 4 g + 2 (lane bit 4) + (lane bit 3)
+  const int red_state = 4 * g + 2 * ((lane >> 4) & 1) + ((lane >> 3) & 1);
+  const bool red_c = lane >= 32;
+  const bool bit3 = (lane >> 3) & 1, bit2 = (lane >> 2) & 1;
+
+  struct RawF { Raw4<kInBF16> u, r, bt; };
+  struct RawB { Raw4<kInBF16> u, r, bt, ct, z; Raw4<kGradBF16> dy; };
+
+  auto chunk_len = [&](int64_t ck) -> int {
+    const int64_t rem = L - ck * kBC;
+    return rem < kBC ? (int)rem : kBC;
   };
-  // one forward step of this lane's 4 states
-  auto step = [&](int64_t t, float (&h)[4]) {
-    const float u = ldv<kInBF16>(p.u, row + t);
-    const float delta = softplus(ldv<kInBF16>(p.delta, row + t) + bias);
+
+  // ---- pass 1: forward recurrence, chunk start states to the workspace ----
+  auto fetch1 = [&](int64_t ck, RawF& r) {
+    const int64_t t0 = ck * kBC;
+    const bool vec = vecp && t0 + kBC <= L;
+    ld_raw4<kInBF16>(r.u, p.u, row + t0 + 4 * g, vec, true, (int)(L - t0 - 4 * g));
+    ld_raw4<kInBF16>(r.r, p.delta, row + t0 + 4 * g, vec, true, (int)(L - t0 - 4 * g));
+    ld_raw4<kInBF16>(r.bt, p.Bt, brow + t0 + 4 * sq, vec, sn_ok, (int)(L - t0 - 4 * sq));
+  };
+  auto stage1 = [&](const RawF& r, BwdStage& st) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      *reinterpret_cast<float2*>(&st.V[4 * g + j][c]) = make_float2(r.u.get(j), softplus(r.r.get(j) + bias));
+      st.B[4 * sq + j][sn] = r.bt.get(j);
+    }
+  };
+  auto fstep = [&](const BwdStage& st, int tl, float (&h)[4]) {
+    const float2 v = *reinterpret_cast<const float2*>(&st.V[tl][c]);
+    const float4 Bq = *reinterpret_cast<const float4*>(&st.B[tl][4 * g]);
+    const float bv[4] = {Bq.x, Bq.y, Bq.z, Bq.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float x = v.y * a2[i];
+      const float e = hw_exp2(x);
+      const float coef = kDeltaB ? v.y : expm1_from_exp2(x, e) * ia[i];
+      h[i] = __builtin_fmaf(e, h[i], coef * (bv[i] * v.x));
+    }
+  };
+
+  float h[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  {
+    RawF r;
+    fetch1(0, r);
+    stage1(r, S[0]);
+    __syncthreads();
+    for (int64_t ck = 0; ck < nck; ++ck) {
+      const BwdStage& st = S[ck & 1];
+      const bool more = ck + 1 < nck;
+      if (more) fetch1(ck + 1, r);
+      if (c_ok)
+        *reinterpret_cast<float4*>(p.ckpt + ((b * D + d) * nck + ck) * 16 + 4 * g) =
+            make_float4(h[0], h[1], h[2], h[3]);
+      const int len = chunk_len(ck);
+      if (len == kBC) {
+#pragma unroll
+        for (int tl = 0; tl < kBC; ++tl) fstep(st, tl, h);
+      } else {
+        for (int tl = 0; tl < len; ++tl) fstep(st, tl, h);
+      }
+      if (more) stage1(r, S[(ck + 1) & 1]);
+      __syncthreads();
+    }
+  }
+
+  // ---- pass 2: chunks in reverse: recompute h, then walk back with the adjoint ----
+  auto fetch2 = [&](int64_t ck, RawB& r, float4& hs) {
+    const int64_t t0 = ck * kBC;
+    const bool vec = vecp && t0 + kBC <= L;
+    const int vc = (int)(L - t0 - 4 * g), vs = (int)(L - t0 - 4 * sq);
+    ld_raw4<kInBF16>(r.u, p.u, row + t0 + 4 * g, vec, true, vc);
+    ld_raw4<kInBF16>(r.r, p.delta, row + t0 + 4 * g, vec, true, vc);
+    ld_raw4<kInBF16>(r.z, has_z ? p.z : p.u, row + t0 + 4 * g, vec, true, vc);
+    ld_raw4<kGradBF16>(r.dy, p.dy, row + t0 + 4 * g, vec, true, vc);
+    ld_raw4<kInBF16>(r.bt, p.Bt, brow + t0 + 4 * sq, vec, sn_ok, vs);
+    ld_raw4<kInBF16>(r.ct, p.Ct, brow + t0 + 4 * sq, vec, sn_ok, vs);
+    hs = c_ok ? *reinterpret_cast<const float4*>(p.ckpt + ((b * D + d) * nck + ck) * 16 + 4 * g)
+              : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  };
+  // per element, once: delta, the softplus derivative (kept in sg for the
+  // write-out), the gated output gradient dyc = dy silu(z) and the factor of
+  // dz = dy yc s (1 + z (1 - s)), s = sigmoid(z); the D gradient sum
+  float accD = 0.0f;
+  auto stage2 = [&](const RawB& r, BwdStage& st, float (&sg)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float x = r.r.get(j) + bias;
+      const float uu = r.u.get(j);
+      const float dy = r.dy.get(j);
+      float dyc = dy, kz = 0.0f;
+      if (has_z) {
+        const float zv = r.z.get(j);
+        const float s = sigmoidf(zv);
+        dyc = dy * (zv * s);
+        kz = dy * s * __builtin_fmaf(zv, 1.0f - s, 1.0f);
+      }
+      if (!c_ok) { dyc = 0.0f; kz = 0.0f; }
+      st.V[4 * g + j][c] = make_float4(uu, softplus(x), dyc, kz);
+      sg[j] = sigmoidf(x);
+      accD = __builtin_fmaf(dyc, uu, accD);
+      st.B[4 * sq + j][sn] = r.bt.get(j);
+      st.C[4 * sq + j][sn] = r.ct.get(j);
+    }
+  };
+
+  float gs[4] = {0.0f, 0.0f, 0.0f, 0.0f}, anext[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float dAacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float accBias = 0.0f;
+  float sg_cur[4], sg_next[4];
+  float4 hs_cur, hs_next;
+  RawB r;
+  fetch2(nck - 1, r, hs_next);
+  stage2(r, S[0], sg_next);
+  __syncthreads();
+
+  // one reverse step; ht = h_t in, h_(t-1) out
+  auto rstep = [&](BwdStage& st, int tl, float (&ht)[4]) {
+    const float4 v = st.V[tl][c];
+    const float4 Bq = *reinterpret_cast<const float4*>(&st.B[tl][4 * g]);
+    const float4 Cq = *reinterpret_cast<const float4*>(&st.C[tl][4 * g]);
+    const float4 hp4 = Hs[tl][lane];
+    const float u = v.x, delta = v.y, dyc = v.z, kz = v.w;
+    const float Bv[4] = {Bq.x, Bq.y, Bq.z, Bq.w}, Cv[4] = {Cq.x, Cq.y, Cq.z, Cq.w};
+    const float hp[4] = {hp4.x, hp4.y, hp4.z, hp4.w};
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s = __builtin_fmaf(Cv[i], ht[i], s);
+    const float dz = kz * __builtin_fmaf(Dd, u, quad_sum4(s));
+    const float d2 = delta * delta;
+    float sdu = 0.0f, sdd = 0.0f, dBv[4], dCv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float x = delta * a2[i];
       const float e = hw_exp2(x);
-      const float coef = p.delta_b ? delta : expm1_from_exp2(x, e) * ia[i];
-      h[i] = __builtin_fmaf(e, h[i], coef * (bc(p.Bt, i, t) * u));
+      const float coef = kDeltaB ? delta : expm1_from_exp2(x, e) * ia[i];
+      const float gn = __builtin_fmaf(dyc, Cv[i], anext[i] * gs[i]);
+      const float dabar = gn * hp[i];
+      const float gc = gn * coef;
+      dBv[i] = gc * u;
+      dCv[i] = dyc * ht[i];
+      sdu = __builtin_fmaf(gc, Bv[i], sdu);
+      const float dcoef = gn * (Bv[i] * u);
+      const float de = dabar * e;
+      if constexpr (kDeltaB) {
+        sdd = __builtin_fmaf(de, a[i], sdd + dcoef);
+        dAacc[i] = __builtin_fmaf(de, delta, dAacc[i]);
+      } else {
+        sdd = __builtin_fmaf(__builtin_fmaf(dabar, a[i], dcoef), e, sdd);
+        // d coef / dA = delta^2 phi(delta A), phi(y) = (y e^y - e^y + 1) / y^2:
+        // its series to y^5 for |y| < 1/4 (next term y^6 / 5760, below 2^-24
+        // of phi there), else (y e^y - e^y + 1) / A^2
+        const float y = delta * a[i];
+        float ps = __builtin_fmaf(y, 1.0f / 840.0f, 1.0f / 144.0f);
+        ps = __builtin_fmaf(y, ps, 1.0f / 30.0f);
+        ps = __builtin_fmaf(y, ps, 1.0f / 8.0f);
+        ps = __builtin_fmaf(y, ps, 1.0f / 3.0f);
+        ps = __builtin_fmaf(y, ps, 0.5f);
+        const float closed = __builtin_fmaf(y, e, 1.0f - e) * (ia[i] * ia[i]);
+        const float q = (__builtin_fabsf(y) < 0.25f) ? d2 * ps : closed;
+        dAacc[i] = __builtin_fmaf(dcoef, q, __builtin_fmaf(de, delta, dAacc[i]));
+      }
+      gs[i] = gn;
+      anext[i] = e;
+      ht[i] = hp[i];
     }
+    const float du = __builtin_fmaf(dyc, Dd, quad_sum4(sdu));
+    const float dpre = quad_sum4(sdd);
+    // results of this step over its inputs: lane g writes component g
+    reinterpret_cast<float*>(&st.V[tl][c])[g] = g == 0 ? du : (g == 1 ? dpre : dz);
+    // dB_t, dC_t over the wave's 16 channels (lane bits 2..5)
+    float w0 = swap32_sum(dBv[0], dCv[0]);
+    float w1 = swap32_sum(dBv[1], dCv[1]);
+    float w2 = swap32_sum(dBv[2], dCv[2]);
+    float w3 = swap32_sum(dBv[3], dCv[3]);
+    const float q0 = swap16_sum(w0, w2);
+    const float q1 = swap16_sum(w1, w3);
+    const float keep = bit3 ? q1 : q0, send = bit3 ? q0 : q1;
+    const float rr = keep + dpp_mov<0x128>(send);           // row_ror:8 pairs lane bit 3
+    // partner lane ^ 4: row_ror:4 reads lane i - 4, row_ror:12 lane i + 4
+    // (both evaluated with the whole wave active, then selected)
+    const float from_m4 = dpp_mov<0x124>(rr), from_p4 = dpp_mov<0x12C>(rr);
+    const float fin = rr + (bit2 ? from_m4 : from_p4);
+    (red_c ? st.C[tl] : st.B[tl])[red_state] = fin;
   };
 
-  // pass 1: chunk-start states
-  float h[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int64_t ck = 0; ck < p.nck; ++ck) {
-    if (c_ok)
-      *reinterpret_cast<float4*>(p.ckpt + ((b * D + d) * p.nck + ck) * 16 + 4 * g) = make_float4(h[0], h[1], h[2], h[3]);
+  for (int64_t ck = nck - 1, it = 0; ck >= 0; --ck, ++it) {
+    BwdStage& st = S[it & 1];
+    const bool more = ck > 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sg_cur[j] = sg_next[j];
+    hs_cur = hs_next;
+    if (more) fetch2(ck - 1, r, hs_next);
     const int64_t t0 = ck * kBC;
-    const int len = (int)((L - t0) < kBC ? (L - t0) : kBC);
-    for (int tl = 0; tl < len; ++tl) step(t0 + tl, h);
-  }
-
-  // pass 2: reverse
-  float gs[4] = {0.0f, 0.0f, 0.0f, 0.0f}, anext[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  float dAacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  float accD = 0.0f, accBias = 0.0f;
-  for (int64_t ck = p.nck - 1; ck >= 0; --ck) {
-    const int64_t t0 = ck * kBC;
-    const int len = (int)((L - t0) < kBC ? (L - t0) : kBC);
-    float hs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (c_ok) {
-      const float4 v = *reinterpret_cast<const float4*>(p.ckpt + ((b * D + d) * p.nck + ck) * 16 + 4 * g);
-      hs[0] = v.x; hs[1] = v.y; hs[2] = v.z; hs[3] = v.w;
-    }
-    float hh[4] = {hs[0], hs[1], hs[2], hs[3]};
-    for (int tl = 0; tl < len; ++tl) {
-      step(t0 + tl, hh);
-      Hs[tl][lane] = make_float4(hh[0], hh[1], hh[2], hh[3]);
-    }
-    for (int k = lane; k < kBC * 16; k += 64) {
-      (&AccB[0][0])[k] = 0.0f;
-      (&AccC[0][0])[k] = 0.0f;
+    const int len = chunk_len(ck);
+    float hh[4] = {hs_cur.x, hs_cur.y, hs_cur.z, hs_cur.w};
+    Hs[0][lane] = hs_cur;
+    if (len == kBC) {
+#pragma unroll
+      for (int tl = 0; tl < kBC; ++tl) {
+        fstep(st, tl, hh);
+        Hs[tl + 1][lane] = make_float4(hh[0], hh[1], hh[2], hh[3]);
+      }
+#pragma unroll 2
+      for (int tl = kBC - 1; tl >= 0; --tl) rstep(st, tl, hh);
+    } else {
+      for (int tl = 0; tl < len; ++tl) {
+        fstep(st, tl, hh);
+        Hs[tl + 1][lane] = make_float4(hh[0], hh[1], hh[2], hh[3]);
+      }
+      for (int tl = len - 1; tl >= 0; --tl) rstep(st, tl, hh);
     }
     __syncthreads();
-    for (int tl = len - 1; tl >= 0; --tl) {
-      const int64_t t = t0 + tl;
-      const float u = ldv<kInBF16>(p.u, row + t);
-      const float xr = ldv<kInBF16>(p.delta, row + t) + bias;
-      const float delta = softplus(xr);
-      const float sg = sigmoidf(xr);
-      const float dy = ldv<kGradBF16>(p.dy, row + t);
-      const float4 ht4 = Hs[tl][lane];
-      const float ht[4] = {ht4.x, ht4.y, ht4.z, ht4.w};
-      float hp[4];
-      if (tl > 0) {
-        const float4 v = Hs[tl - 1][lane];
-        hp[0] = v.x; hp[1] = v.y; hp[2] = v.z; hp[3] = v.w;
-      } else {
-        hp[0] = hs[0]; hp[1] = hs[1]; hp[2] = hs[2]; hp[3] = hs[3];
+    // write out: lane (c, g) owns steps 4 g .. 4 g + 3 of channel c
+    {
+      const bool vec = vecp && len == kBC;
+      const int valid = len - 4 * g;
+      float du[4], dr[4], dz[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float4 o = st.V[4 * g + j][c];
+        du[j] = o.x;
+        dr[j] = o.y * sg_cur[j];
+        dz[j] = o.z;
+        if (j < valid) accBias += dr[j];
       }
-      float Bv[4], Cv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) { Bv[i] = bc(p.Bt, i, t); Cv[i] = bc(p.Ct, i, t); }
-      float dyc = dy, dzv = 0.0f;
-      if (p.z) {
-        float s = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s = __builtin_fmaf(Cv[i], ht[i], s);
-        const float yc = quad_sum4(s) + Dd * u;
-        const float zv = ldv<kInBF16>(p.z, row + t);
-        const float sz = sigmoidf(zv);
-        dzv = dy * yc * sz * __builtin_fmaf(zv, 1.0f - sz, 1.0f);
-        dyc = dy * (zv * sz);
+      if (c_ok) {
+        st4<kGradBF16>(p.du, row + t0 + 4 * g, vec, valid, du);
+        st4<kGradBF16>(p.ddelta, row + t0 + 4 * g, vec, valid, dr);
+        if (has_z) st4<kGradBF16>(p.dz, row + t0 + 4 * g, vec, valid, dz);
       }
-      float sdu = 0.0f, sdd = 0.0f, dBp[4], dCp[4];
+      if (sn_ok) {
+        float vb[4], vcc[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float x = delta * a2[i];
-        const float e = hw_exp2(x);
-        const float coef = p.delta_b ? delta : expm1_from_exp2(x, e) * ia[i];
-        const float gn = __builtin_fmaf(dyc, Cv[i], anext[i] * gs[i]);
-        const float dabar = gn * hp[i];
-        const float dcoef = gn * Bv[i] * u;
-        dBp[i] = gn * coef * u * cmask;
-        dCp[i] = dyc * ht[i] * cmask;
-        sdu = __builtin_fmaf(gn * coef, Bv[i], sdu);
-        const float xa = delta * a[i];
-        if (p.delta_b) {
-          sdd += dabar * a[i] * e + dcoef;
-          dAacc[i] += dabar * delta * e;
-        } else {
-          sdd += (dabar * a[i] + dcoef) * e;
-          dAacc[i] += dabar * delta * e + dcoef * delta * delta * phi_coef(xa, e);
+        for (int j = 0; j < 4; ++j) {
+          vb[j] = st.B[4 * sq + j][sn];
+          vcc[j] = st.C[4 * sq + j][sn];
         }
-        gs[i] = gn;
-        anext[i] = e;
-      }
-      const float du = __builtin_fmaf(dyc, Dd, quad_sum4(sdu));
-      const float dr = quad_sum4(sdd) * sg;
-      accBias += dr;
-      accD = __builtin_fmaf(dyc, u, accD);
-      if (c_ok && g == 0) {
-        stv<kGradBF16>(p.du, row + t, du);
-        stv<kGradBF16>(p.ddelta, row + t, dr);
-        if (p.z) stv<kGradBF16>(p.dz, row + t, dzv);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float vb = row_sum_same_g(dBp[i]);
-        const float vc = row_sum_same_g(dCp[i]);
-        if ((c & 3) == 0) {
-          atomicAdd(&AccB[tl][4 * g + i], vb);
-          atomicAdd(&AccC[tl][4 * g + i], vc);
-        }
+        const int64_t o = ((b * p.tiles_d + td) * 16 + sn) * L + t0 + 4 * sq;
+        st4<false>(p.part_dB, o, vec, len - 4 * sq, vb);
+        st4<false>(p.part_dC, o, vec, len - 4 * sq, vcc);
       }
     }
-    __syncthreads();
-    for (int k = lane; k < kBC * 16; k += 64) {
-      const int tl = k >> 4, n = k & 15;
-      if (tl < len && n < N) {
-        const int64_t o = ((b * p.tiles_d + td) * 16 + n) * L + t0 + tl;
-        p.part_dB[o] = AccB[tl][n];
-        p.part_dC[o] = AccC[tl][n];
-      }
-    }
+    if (more) stage2(r, S[(it + 1) & 1], sg_next);
     __syncthreads();
   }
+  accD = quad_sum4(accD);
+  accBias = quad_sum4(accBias);
   if (c_ok) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) p.part_dA[(b * D + d) * 16 + 4 * g + i] = dAacc[i];
+    *reinterpret_cast<float4*>(p.part_dA + (b * D + d) * 16 + 4 * g) =
+        make_float4(dAacc[0], dAacc[1], dAacc[2], dAacc[3]);
     if (g == 0) {
       p.part_dD[b * D + d] = accD;
       p.part_dbias[b * D + d] = accBias;
@@ -295,7 +479,10 @@ __global__ __launch_bounds__(256) void bwd_reduce_params_kernel(BwdParams p) {
 
 template <bool kInBF16, bool kGradBF16>
 hipError_t bwd_t(const BwdParams& p, hipStream_t s) {
-  hipLaunchKernelGGL((scan_bwd_kernel<kInBF16, kGradBF16>), dim3((unsigned)(p.B * p.tiles_d)), dim3(64), 0, s, p);
+  if (p.delta_b)
+    hipLaunchKernelGGL((scan_bwd_kernel<kInBF16, kGradBF16, true>), dim3((unsigned)(p.B * p.tiles_d)), dim3(64), 0, s, p);
+  else
+    hipLaunchKernelGGL((scan_bwd_kernel<kInBF16, kGradBF16, false>), dim3((unsigned)(p.B * p.tiles_d)), dim3(64), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t nbc = p.B * p.N * p.L;

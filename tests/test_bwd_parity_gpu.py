@@ -68,6 +68,8 @@ CASES = [
     (2, 32, 16, 64, "f32", "f32", {"zero_A": True}),
     (1, 17, 16, 1, "f32", "f32", {}),
     (1, 1, 1, 33, "f32", "f32", {}),
+    (2, 40, 16, 44, "bf16", "bf16", {"delta_b": True}),   # vector loads, ragged last chunk
+    (1, 16, 16, 48, "f32", "bf16", {}),
 ]
 
 
