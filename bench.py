@@ -437,7 +437,7 @@ def bench_bwd(args, dev):
         "call_ms_mean": round(call_ms, 5), "algorithmic_bytes": nbytes,
         "roofline": {"bound": "alu", "achieved": round(ach, 3), "peak": round(VALU_PEAK_TOPS, 2), "unit": "TOP/s",
                      "frac": round(ach / VALU_PEAK_TOPS, 4), "traffic": None, "ops_per_update": OPS_PER_UPDATE_BWD,
-                     "launch_time": "whole call: recompute kernel + two reduce kernels"},
+                     "launch_time": "whole call: segment summary, carry, segment recompute and two reduce kernels"},
     }
 
 

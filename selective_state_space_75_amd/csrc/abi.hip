@@ -141,21 +141,42 @@ constexpr unsigned kKnownFlags = MAMBA_FLAG_DELTA_B | MAMBA_FLAG_ACCURATE_EXPM1;
 }  // namespace
 
 struct BwdPlan {
-  int64_t tiles_d = 0, nck = 0;
-  size_t off_ckpt = 0, off_pb = 0, off_pc = 0, off_pa = 0, off_pd = 0, off_pbias = 0, bytes = 0;
+  int64_t tiles_d = 0, nck = 0, S = 0, seg_len = 0;
+  size_t off_ckh = 0, off_ckd = 0, off_sp = 0, off_sh = 0, off_sH = 0, off_hin = 0, off_gin = 0;
+  size_t off_pb = 0, off_pc = 0, off_pa = 0, off_pd = 0, off_pbias = 0, bytes = 0;
 };
 
+// Segments: enough (batch row, channel tile, segment) tasks to give every
+// SIMD of the chip several (at least 8192 in all), segments of at least 64
+// steps, lengths a multiple of 16.
 BwdPlan make_bwd_plan(int64_t B, int64_t D, int64_t L) {
   BwdPlan q;
+  constexpr int64_t kC = mamba::kBwdChunk;
   q.tiles_d = (D + 15) / 16;
-  q.nck = (L + mamba::kBwdChunk - 1) / mamba::kBwdChunk;
+  q.nck = (L + kC - 1) / kC;
+  const int64_t rows = B * q.tiles_d;
+  int64_t S = (8192 + rows - 1) / rows;
+  const int64_t smax = (L + 63) / 64;
+  if (S > smax) S = smax;
+  if (S < 1) S = 1;
+  int64_t len = (L + S - 1) / S;
+  len = (len + 15) / 16 * 16;
+  q.seg_len = len;
+  q.S = (L + len - 1) / len;
+  const size_t bd = size_t(B) * size_t(D), bsd = bd * size_t(q.S);
   size_t o = 0;
-  q.off_ckpt = o; o += align256(size_t(B) * size_t(D) * size_t(q.nck) * 16 * sizeof(float));
+  q.off_ckh = o; o += align256(bd * size_t(q.nck) * 16 * sizeof(float));
+  q.off_ckd = o; o += align256(bd * size_t(q.nck) * sizeof(float));
+  q.off_sp = o; o += align256(bsd * 16 * sizeof(float));
+  q.off_sh = o; o += align256(bsd * 16 * sizeof(float));
+  q.off_sH = o; o += align256(bsd * 16 * sizeof(float));
+  q.off_hin = o; o += align256(bsd * 16 * sizeof(float));
+  q.off_gin = o; o += align256(bsd * 16 * sizeof(float));
   q.off_pb = o; o += align256(size_t(B) * size_t(q.tiles_d) * 16 * size_t(L) * sizeof(float));
   q.off_pc = o; o += align256(size_t(B) * size_t(q.tiles_d) * 16 * size_t(L) * sizeof(float));
-  q.off_pa = o; o += align256(size_t(B) * size_t(D) * 16 * sizeof(float));
-  q.off_pd = o; o += align256(size_t(B) * size_t(D) * sizeof(float));
-  q.off_pbias = o; o += align256(size_t(B) * size_t(D) * sizeof(float));
+  q.off_pa = o; o += align256(bsd * 16 * sizeof(float));
+  q.off_pd = o; o += align256(bsd * sizeof(float));
+  q.off_pbias = o; o += align256(bsd * sizeof(float));
   q.bytes = o;
   return q;
 }
@@ -290,7 +311,8 @@ int mamba_scan_bwd(const void* u, const void* delta, const void* z, const void* 
                           (const void*)dCt, (const void*)dA, (const void*)dDskip, (const void*)ddelta_bias})
     if (ptr && !aligned(ptr, 4)) return MAMBA_ERR_ALIGN;
   const BwdPlan plan = make_bwd_plan(B, D, L);
-  if (B * plan.tiles_d >= (int64_t(1) << 31) || (B * N * L + 255) / 256 >= (int64_t(1) << 31))
+  if (B * plan.tiles_d * plan.S >= (int64_t(1) << 31) || (B * N * L + 255) / 256 >= (int64_t(1) << 31) ||
+      (B * D * 16 + 255) / 256 >= (int64_t(1) << 31))
     return MAMBA_ERR_SHAPE;
   if (!workspace || workspace_bytes < plan.bytes) return MAMBA_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return MAMBA_ERR_ALIGN;
@@ -301,17 +323,25 @@ int mamba_scan_bwd(const void* u, const void* delta, const void* z, const void* 
   p.du = du; p.ddelta = ddelta; p.dz = z ? dz : nullptr;
   p.dBt = dBt; p.dCt = dCt; p.dA = dA; p.dDskip = dDskip; p.dbias = ddelta_bias;
   char* ws = static_cast<char*>(workspace);
-  p.ckpt = reinterpret_cast<float*>(ws + plan.off_ckpt);
-  p.part_dB = reinterpret_cast<float*>(ws + plan.off_pb);
-  p.part_dC = reinterpret_cast<float*>(ws + plan.off_pc);
-  p.part_dA = reinterpret_cast<float*>(ws + plan.off_pa);
-  p.part_dD = reinterpret_cast<float*>(ws + plan.off_pd);
-  p.part_dbias = reinterpret_cast<float*>(ws + plan.off_pbias);
+  auto at = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+  p.ckpt_h = at(plan.off_ckh);
+  p.ckpt_cd = at(plan.off_ckd);
+  p.seg_P = at(plan.off_sp);
+  p.seg_h = at(plan.off_sh);
+  p.seg_H = at(plan.off_sH);
+  p.h_in = at(plan.off_hin);
+  p.g_in = at(plan.off_gin);
+  p.part_dB = at(plan.off_pb);
+  p.part_dC = at(plan.off_pc);
+  p.part_dA = at(plan.off_pa);
+  p.part_dD = at(plan.off_pd);
+  p.part_dbias = at(plan.off_pbias);
   p.B = B; p.D = D; p.N = N; p.L = L; p.tiles_d = plan.tiles_d; p.nck = plan.nck;
+  p.S = plan.S; p.seg_len = plan.seg_len;
   p.delta_b = (flags & MAMBA_FLAG_DELTA_B) ? 1 : 0;
-  p.vec = L % 4 == 0;
+  p.vec = L % 2 == 0;
   for (const void* ptr : {u, delta, z, Bt, Ct, dy, (const void*)du, (const void*)ddelta, (const void*)dz})
-    if (ptr && !aligned(ptr, 16)) p.vec = 0;
+    if (ptr && !aligned(ptr, 8)) p.vec = 0;
   const Dt in = in_dtype == MAMBA_BF16 ? Dt::BF16 : Dt::F32;
   const Dt gd = grad_dtype == MAMBA_BF16 ? Dt::BF16 : Dt::F32;
   return mamba::launch_scan_bwd(p, in, gd, stream) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;

@@ -77,20 +77,25 @@ struct ConvParams {
 };
 
 // Backward pass of the scan.
-// Steps per recomputed chunk of the backward pass: one stored start state each.
-constexpr int kBwdChunk = 16;
+// Backward pass: L is cut into segments of seg_len steps (a multiple of
+// kBwdChunk); each segment is cut into chunks of kBwdChunk steps, the unit
+// that is recomputed on chip.
+constexpr int kBwdChunk = 8;
 
 struct BwdParams {
   const void *u, *delta, *z, *Bt, *Ct, *dy;
   const float *A, *Dskip, *bias;
   void *du, *ddelta, *dz;                       // grad dtype, (B, D, L)
   float *dBt, *dCt, *dA, *dDskip, *dbias;       // fp32 results
-  float *ckpt;                                  // (B, D, nck, 16) chunk-start states
+  float *ckpt_h;                                // (B, D, nck, 16) chunk-start states from a zero segment start
+  float *ckpt_cd;                               // (B, D, nck) sum of delta from the segment start to the chunk
+  float *seg_P, *seg_h, *seg_H;                 // (B, S, D, 16) segment summaries
+  float *h_in, *g_in;                           // (B, S, D, 16) state entering / adjoint leaving each segment
   float *part_dB, *part_dC;                     // (B, tiles_d, 16, L) per-tile sums over channels
-  float *part_dA, *part_dD, *part_dbias;        // (B, D, 16), (B, D), (B, D) per-batch-row sums
-  int64_t B, D, N, L, tiles_d, nck;
+  float *part_dA, *part_dD, *part_dbias;        // (B, S, D, 16), (B, S, D), (B, S, D) per-segment sums
+  int64_t B, D, N, L, tiles_d, nck, S, seg_len;
   int delta_b;
-  int vec;      // L % 4 == 0 and every (B, D, L) / (B, N, L) array 16-byte aligned
+  int vec;      // L even and every (B, D, L) / (B, N, L) array 8-byte aligned
 };
 
 // Each returns hipSuccess or the launch error.

@@ -35,7 +35,7 @@
 namespace mamba {
 namespace {
 
-constexpr int kBC = kBwdChunk;
+constexpr int kT = kBwdChunk;
 
 // Sum over the four lanes of a quad (DPP quad permutations).
 __device__ __forceinline__ float quad_sum4(float v) {
@@ -45,75 +45,6 @@ __device__ __forceinline__ float quad_sum4(float v) {
 }
 
 __device__ __forceinline__ float sigmoidf(float x) { return hw_rcp(1.0f + hw_exp2(-x * kLog2e)); }
-
-// Four consecutive elements of one row as loaded from global memory; they
-// are widened only where they are consumed, so the loads stay in flight
-// across the chunk being computed.
-template <bool kBF16> struct Raw4;
-template <> struct Raw4<true> {
-  uint2 w;
-  __device__ __forceinline__ float get(int j) const {
-    const uint32_t x = j < 2 ? w.x : w.y;
-    return (j & 1) ? bf16_hi(x) : bf16_lo(x);
-  }
-};
-template <> struct Raw4<false> {
-  float4 f;
-  __device__ __forceinline__ float get(int j) const { return j == 0 ? f.x : j == 1 ? f.y : j == 2 ? f.z : f.w; }
-};
-
-// Elements off .. off + 3 of `base`: one vector load when `vec` (the caller
-// guarantees alignment and bounds), else element loads with zeros from index
-// `valid` on (and everywhere when !ok).
-template <bool kBF16>
-__device__ __forceinline__ void ld_raw4(Raw4<kBF16>& r, const void* base, int64_t off, bool vec, bool ok, int valid) {
-  if constexpr (kBF16) {
-    const uint16_t* q = static_cast<const uint16_t*>(base) + off;
-    if (vec) {
-      r.w = ok ? *reinterpret_cast<const uint2*>(q) : make_uint2(0u, 0u);
-    } else {
-      uint32_t h[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) h[j] = (ok && j < valid) ? (uint32_t)q[j] : 0u;
-      r.w = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-    }
-  } else {
-    const float* q = static_cast<const float*>(base) + off;
-    if (vec) {
-      r.f = ok ? *reinterpret_cast<const float4*>(q) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    } else {
-      float h[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) h[j] = (ok && j < valid) ? q[j] : 0.0f;
-      r.f = make_float4(h[0], h[1], h[2], h[3]);
-    }
-  }
-}
-
-// Stores v[0..3] at off .. off + 3 (vector store when `vec`, else the first
-// `valid` elements).
-template <bool kBF16>
-__device__ __forceinline__ void st4(void* base, int64_t off, bool vec, int valid, const float (&v)[4]) {
-  if constexpr (kBF16) {
-    uint16_t* q = static_cast<uint16_t*>(base) + off;
-    if (vec) {
-      *reinterpret_cast<uint2*>(q) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (j < valid) q[j] = f32_to_bf16(v[j]);
-    }
-  } else {
-    float* q = static_cast<float*>(base) + off;
-    if (vec) {
-      *reinterpret_cast<float4*>(q) = make_float4(v[0], v[1], v[2], v[3]);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (j < valid) q[j] = v[j];
-    }
-  }
-}
 
 template <int kCtrl>
 __device__ __forceinline__ float dpp_mov(float v) {
@@ -133,307 +64,457 @@ __device__ __forceinline__ float swap32_sum(float x, float y) {
 __device__ __forceinline__ float swap16_sum(float x, float y) {
   const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, y),
                                                   false, false);
-  const unsigned r0 = r[0], r1 = r[1];   // elements as scalars: bit-casting a subscript reads element 0
+  const unsigned r0 = r[0], r1 = r[1];
   return __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
 }
 
-// Inputs of one chunk for the wave's 16 channels, staged in LDS.  The walk
-// over a step overwrites that step's entries with its results.
-struct BwdStage {
-  float4 V[kBC][16];   // [step][channel] {u, delta, dyc, kz}; after the walk {du, ddelta/sigmoid', dz, -}
-  float B[kBC][16];    // [step][state] B_t; after the walk the tile's dB_t partial
-  float C[kBC][16];    // [step][state] C_t; after the walk the tile's dC_t partial
+// Two consecutive elements of one row as loaded from global memory; they are
+// widened only where they are consumed, so the loads stay in flight across
+// the chunk being computed.
+template <bool kBF16> struct Raw2;
+template <> struct Raw2<true> {
+  uint32_t w;
+  __device__ __forceinline__ float get(int j) const { return j ? bf16_hi(w) : bf16_lo(w); }
+};
+template <> struct Raw2<false> {
+  float2 f;
+  __device__ __forceinline__ float get(int j) const { return j ? f.y : f.x; }
 };
 
-template <bool kInBF16, bool kGradBF16, bool kDeltaB>
-__global__ __launch_bounds__(64) void scan_bwd_kernel(BwdParams p) {
-  __shared__ float4 Hs[kBC + 1][64];   // chunk start state, then h_t after each step, per lane
-  __shared__ BwdStage S[2];
-  const int lane = threadIdx.x;
-  const int c = lane >> 2, g = lane & 3;
-  const int64_t b = (int64_t)blockIdx.x / p.tiles_d;
-  const int64_t td = (int64_t)blockIdx.x - b * p.tiles_d;
-  const int64_t N = p.N, L = p.L, D = p.D, nck = p.nck;
-  const int64_t d = td * 16 + c;
-  const bool c_ok = d < D;
-  const int64_t dd = c_ok ? d : 0;          // channels past D read channel 0 and contribute nothing
-  const int64_t row = (b * D + dd) * L;
-  const bool has_z = p.z != nullptr;
-  const bool vecp = p.vec != 0;
-
-  float a[4], a2[4], ia[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t n = 4 * g + i;
-    float an = n < N ? p.A[dd * N + n] : -1.0f;
-    // |A| < 2^-40 (including 0) as +-2^-40: the coefficient is then delta to
-    // within delta * 2^-41, and its derivative in A is delta^2 / 2
-    if (__builtin_fabsf(an) < 0x1p-40f) an = (an > 0.0f) ? 0x1p-40f : -0x1p-40f;
-    a[i] = an;
-    a2[i] = an * kLog2e;
-    ia[i] = 1.0f / an;
-  }
-  const float bias = p.bias ? p.bias[dd] : 0.0f;
-  const float Dd = p.Dskip ? p.Dskip[dd] : 0.0f;
-  // B/C role of a lane when staging and writing out: state sn, steps 4 sq ..
-  const int sn = lane >> 2, sq = lane & 3;
-  const bool sn_ok = sn < N;
-  const int64_t brow = (b * N + (sn_ok ? sn : 0)) * L;
-  // lane's slot for the reduced dB/dC value of a step: type (lane bit 5),
-  // state 4 g + 2 (lane bit 4) + (lane bit 3)
-  const int red_state = 4 * g + 2 * ((lane >> 4) & 1) + ((lane >> 3) & 1);
-  const bool red_c = lane >= 32;
-  const bool bit3 = (lane >> 3) & 1, bit2 = (lane >> 2) & 1;
-
-  struct RawF { Raw4<kInBF16> u, r, bt; };
-  struct RawB { Raw4<kInBF16> u, r, bt, ct, z; Raw4<kGradBF16> dy; };
-
-  auto chunk_len = [&](int64_t ck) -> int {
-    const int64_t rem = L - ck * kBC;
-    return rem < kBC ? (int)rem : kBC;
-  };
-
-  // ---- pass 1: forward recurrence, chunk start states to the workspace ----
-  auto fetch1 = [&](int64_t ck, RawF& r) {
-    const int64_t t0 = ck * kBC;
-    const bool vec = vecp && t0 + kBC <= L;
-    ld_raw4<kInBF16>(r.u, p.u, row + t0 + 4 * g, vec, true, (int)(L - t0 - 4 * g));
-    ld_raw4<kInBF16>(r.r, p.delta, row + t0 + 4 * g, vec, true, (int)(L - t0 - 4 * g));
-    ld_raw4<kInBF16>(r.bt, p.Bt, brow + t0 + 4 * sq, vec, sn_ok, (int)(L - t0 - 4 * sq));
-  };
-  auto stage1 = [&](const RawF& r, BwdStage& st) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      *reinterpret_cast<float2*>(&st.V[4 * g + j][c]) = make_float2(r.u.get(j), softplus(r.r.get(j) + bias));
-      st.B[4 * sq + j][sn] = r.bt.get(j);
+// Elements off, off + 1 of `base`: one load when `vec` (the caller guarantees
+// alignment and bounds), else element loads with zeros from index `valid` on
+// (and everywhere when !ok).
+template <bool kBF16>
+__device__ __forceinline__ void ld_raw2(Raw2<kBF16>& r, const void* base, int64_t off, bool vec, bool ok, int valid) {
+  if constexpr (kBF16) {
+    const uint16_t* q = static_cast<const uint16_t*>(base) + off;
+    if (vec) {
+      r.w = ok ? *reinterpret_cast<const uint32_t*>(q) : 0u;
+    } else {
+      const uint32_t lo = (ok && valid > 0) ? (uint32_t)q[0] : 0u;
+      const uint32_t hi = (ok && valid > 1) ? (uint32_t)q[1] : 0u;
+      r.w = lo | (hi << 16);
     }
+  } else {
+    const float* q = static_cast<const float*>(base) + off;
+    if (vec) {
+      r.f = ok ? *reinterpret_cast<const float2*>(q) : make_float2(0.0f, 0.0f);
+    } else {
+      r.f = make_float2((ok && valid > 0) ? q[0] : 0.0f, (ok && valid > 1) ? q[1] : 0.0f);
+    }
+  }
+}
+
+// Stores v0, v1 at off, off + 1 (one store when `vec`, else the first `valid`).
+template <bool kBF16>
+__device__ __forceinline__ void st2(void* base, int64_t off, bool vec, int valid, float v0, float v1) {
+  if constexpr (kBF16) {
+    uint16_t* q = static_cast<uint16_t*>(base) + off;
+    if (vec) {
+      *reinterpret_cast<uint32_t*>(q) = pack_bf16x2(v0, v1);
+    } else {
+      if (valid > 0) q[0] = f32_to_bf16(v0);
+      if (valid > 1) q[1] = f32_to_bf16(v1);
+    }
+  } else {
+    float* q = static_cast<float*>(base) + off;
+    if (vec) {
+      *reinterpret_cast<float2*>(q) = make_float2(v0, v1);
+    } else {
+      if (valid > 0) q[0] = v0;
+      if (valid > 1) q[1] = v1;
+    }
+  }
+}
+
+// Inputs of one chunk for the wave's 16 channels, staged in LDS.  The reverse
+// walk over a step overwrites that step's entries with its results.
+struct Stage {
+  float4 V[kT][16];   // [step][channel] {u, delta, dyc, kz}; after the walk {du, ddelta/sigmoid', dz, -}
+  float B[kT][16];    // [step][state] B_t; after the walk the tile's dB_t partial
+  float C[kT][16];    // [step][state] C_t; after the walk the tile's dC_t partial
+};
+
+// One wave's task: 16 channels of one batch row over one segment of L.
+// Lane roles: (c, g) = (lane / 4, lane % 4) is channel c, states 4 g .. 4 g + 3
+// in the recurrence, and steps 2 g, 2 g + 1 of channel c when loading and
+// storing per-channel rows; (sn, sq) = (lane / 4, lane % 4) is state sn,
+// steps 2 sq, 2 sq + 1 when loading B_t / C_t and storing their gradients.
+template <bool kInBF16, bool kGradBF16>
+struct Wave {
+  const BwdParams& p;
+  int lane, c, g;
+  int64_t b, s, td, d, dd, row, brow, t_begin, t_end;
+  bool c_ok, sn_ok, has_z, vecp;
+  float bias, Dd;
+  float a[4], a2[4], ia[4];
+
+  struct Raw {
+    Raw2<kInBF16> u, r, z, bt, ct;
+    Raw2<kGradBF16> dy;
   };
-  auto fstep = [&](const BwdStage& st, int tl, float (&h)[4]) {
-    const float2 v = *reinterpret_cast<const float2*>(&st.V[tl][c]);
-    const float4 Bq = *reinterpret_cast<const float4*>(&st.B[tl][4 * g]);
-    const float bv[4] = {Bq.x, Bq.y, Bq.z, Bq.w};
+
+  __device__ explicit Wave(const BwdParams& pp) : p(pp) {
+    lane = threadIdx.x;
+    c = lane >> 2;
+    g = lane & 3;
+    const int64_t w = blockIdx.x;
+    td = w % p.tiles_d;
+    const int64_t rest = w / p.tiles_d;
+    s = rest % p.S;
+    b = rest / p.S;
+    d = td * 16 + c;
+    c_ok = d < p.D;
+    dd = c_ok ? d : 0;          // channels past D read channel 0 and contribute nothing
+    row = (b * p.D + dd) * p.L;
+    sn_ok = c < p.N;            // state role: sn == c
+    brow = (b * p.N + (sn_ok ? c : 0)) * p.L;
+    t_begin = s * p.seg_len;
+    t_end = t_begin + p.seg_len < p.L ? t_begin + p.seg_len : p.L;
+    has_z = p.z != nullptr;
+    vecp = p.vec != 0;
+    bias = p.bias ? p.bias[dd] : 0.0f;
+    Dd = p.Dskip ? p.Dskip[dd] : 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float x = v.y * a2[i];
-      const float e = hw_exp2(x);
-      const float coef = kDeltaB ? v.y : expm1_from_exp2(x, e) * ia[i];
-      h[i] = __builtin_fmaf(e, h[i], coef * (bv[i] * v.x));
+      const int64_t n = 4 * g + i;
+      float an = n < p.N ? p.A[dd * p.N + n] : -1.0f;
+      // |A| < 2^-40 (including 0) as +-2^-40: the coefficient is then delta to
+      // within delta * 2^-41, and its derivative in A is delta^2 / 2
+      if (__builtin_fabsf(an) < 0x1p-40f) an = (an > 0.0f) ? 0x1p-40f : -0x1p-40f;
+      a[i] = an;
+      a2[i] = an * kLog2e;
+      ia[i] = 1.0f / an;
     }
-  };
+  }
 
-  float h[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  {
-    RawF r;
-    fetch1(0, r);
-    stage1(r, S[0]);
-    __syncthreads();
-    for (int64_t ck = 0; ck < nck; ++ck) {
-      const BwdStage& st = S[ck & 1];
-      const bool more = ck + 1 < nck;
-      if (more) fetch1(ck + 1, r);
-      if (c_ok)
-        *reinterpret_cast<float4*>(p.ckpt + ((b * D + d) * nck + ck) * 16 + 4 * g) =
-            make_float4(h[0], h[1], h[2], h[3]);
-      const int len = chunk_len(ck);
-      if (len == kBC) {
+  __device__ int chunk_len(int64_t ck) const {
+    const int64_t rem = t_end - ck * kT;
+    return rem < kT ? (int)rem : kT;
+  }
+  __device__ int64_t first_chunk() const { return t_begin / kT; }
+  __device__ int64_t last_chunk() const { return (t_end + kT - 1) / kT - 1; }
+  __device__ int64_t seg_index() const { return (b * p.S + s) * p.D + d; }
+
+  // global loads of chunk ck (the z / dy / C_t loads only when `adjoint`)
+  __device__ void fetch(int64_t ck, Raw& x, bool adjoint) const {
+    const int64_t t0 = ck * kT;
+    const bool vec = vecp && t0 + kT <= t_end;
+    const int vc = (int)(t_end - t0 - 2 * g);
+    ld_raw2<kInBF16>(x.u, p.u, row + t0 + 2 * g, vec, true, vc);
+    ld_raw2<kInBF16>(x.r, p.delta, row + t0 + 2 * g, vec, true, vc);
+    ld_raw2<kInBF16>(x.bt, p.Bt, brow + t0 + 2 * g, vec, sn_ok, vc);
+    if (adjoint) {
+      ld_raw2<kInBF16>(x.ct, p.Ct, brow + t0 + 2 * g, vec, sn_ok, vc);
+      ld_raw2<kInBF16>(x.z, has_z ? p.z : p.u, row + t0 + 2 * g, vec, true, vc);
+      ld_raw2<kGradBF16>(x.dy, p.dy, row + t0 + 2 * g, vec, true, vc);
+    }
+  }
+
+  // per element, once: delta, the gated output gradient dyc = dy silu(z),
+  // the factor kz of dz = kz yc (kz = dy s (1 + z (1 - s)), s = sigmoid(z)),
+  // and (for the write-out) the softplus derivative sigmoid(delta_raw + bias)
+  __device__ void stage(const Raw& x, Stage& st, bool adjoint, float (&sg)[2], float& accD) const {
 #pragma unroll
-        for (int tl = 0; tl < kBC; ++tl) fstep(st, tl, h);
-      } else {
-        for (int tl = 0; tl < len; ++tl) fstep(st, tl, h);
+    for (int j = 0; j < 2; ++j) {
+      const float xr = x.r.get(j) + bias;
+      const float uu = x.u.get(j);
+      float dyc = 0.0f, kz = 0.0f;
+      if (adjoint) {
+        const float dy = x.dy.get(j);
+        dyc = dy;
+        if (has_z) {
+          const float zv = x.z.get(j);
+          const float sz = sigmoidf(zv);
+          dyc = dy * (zv * sz);
+          kz = dy * sz * __builtin_fmaf(zv, 1.0f - sz, 1.0f);
+        }
+        if (!c_ok) { dyc = 0.0f; kz = 0.0f; }
+        sg[j] = sigmoidf(xr);
+        accD = __builtin_fmaf(dyc, uu, accD);
+        st.C[2 * g + j][c] = x.ct.get(j);
       }
-      if (more) stage1(r, S[(ck + 1) & 1]);
+      st.V[2 * g + j][c] = make_float4(uu, softplus(xr), dyc, kz);
+      st.B[2 * g + j][c] = x.bt.get(j);
+    }
+  }
+};
+
+// Segment pass 1: per segment, the recurrence from a zero start.  Stores
+// the chunk-start states and the running sum of delta at every chunk start,
+// and per segment the end state h, the product P of Abar over the segment,
+// and H = sum_t (prod_(r <= t) Abar_r) dyc_t C_t, which carry the state into
+// the next segment and the adjoint into the previous one.
+template <bool kInBF16, bool kGradBF16, bool kDeltaB>
+__global__ __launch_bounds__(64) void bwd_summary_kernel(BwdParams p) {
+  __shared__ Stage st[2];
+  using W = Wave<kInBF16, kGradBF16>;
+  const W w(p);
+  float h[4] = {0.0f, 0.0f, 0.0f, 0.0f}, R[4] = {1.0f, 1.0f, 1.0f, 1.0f}, H[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float cum = 0.0f, sg[2], accD = 0.0f;
+  const int64_t ck0 = w.first_chunk(), ck1 = w.last_chunk();
+  typename W::Raw x;
+  w.fetch(ck0, x, true);
+  w.stage(x, st[0], true, sg, accD);
+  __syncthreads();
+  for (int64_t ck = ck0; ck <= ck1; ++ck) {
+    const Stage& cs = st[(ck - ck0) & 1];
+    const bool more = ck < ck1;
+    if (more) w.fetch(ck + 1, x, true);
+    if (w.c_ok) {
+      *reinterpret_cast<float4*>(p.ckpt_h + ((w.b * p.D + w.d) * p.nck + ck) * 16 + 4 * w.g) =
+          make_float4(h[0], h[1], h[2], h[3]);
+      if (w.g == 0) p.ckpt_cd[(w.b * p.D + w.d) * p.nck + ck] = cum;
+    }
+    const int len = w.chunk_len(ck);
+#pragma unroll
+    for (int tl = 0; tl < kT; ++tl) {
+      if (tl < len) {
+        const float4 v = cs.V[tl][w.c];
+        const float4 Bq = *reinterpret_cast<const float4*>(&cs.B[tl][4 * w.g]);
+        const float4 Cq = *reinterpret_cast<const float4*>(&cs.C[tl][4 * w.g]);
+        const float bv[4] = {Bq.x, Bq.y, Bq.z, Bq.w}, cv[4] = {Cq.x, Cq.y, Cq.z, Cq.w};
+        cum += v.y;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float xx = v.y * w.a2[i];
+          const float e = hw_exp2(xx);
+          const float coef = kDeltaB ? v.y : expm1_from_exp2(xx, e) * w.ia[i];
+          h[i] = __builtin_fmaf(e, h[i], coef * (bv[i] * v.x));
+          R[i] *= e;
+          H[i] = __builtin_fmaf(R[i], v.z * cv[i], H[i]);
+        }
+      }
+    }
+    if (more) {
+      __syncthreads();
+      w.stage(x, st[(ck + 1 - ck0) & 1], true, sg, accD);
       __syncthreads();
     }
   }
+  if (w.c_ok) {
+    const int64_t o = w.seg_index() * 16 + 4 * w.g;
+    *reinterpret_cast<float4*>(p.seg_h + o) = make_float4(h[0], h[1], h[2], h[3]);
+    *reinterpret_cast<float4*>(p.seg_P + o) = make_float4(R[0], R[1], R[2], R[3]);
+    *reinterpret_cast<float4*>(p.seg_H + o) = make_float4(H[0], H[1], H[2], H[3]);
+  }
+}
 
-  // ---- pass 2: chunks in reverse: recompute h, then walk back with the adjoint ----
-  auto fetch2 = [&](int64_t ck, RawB& r, float4& hs) {
-    const int64_t t0 = ck * kBC;
-    const bool vec = vecp && t0 + kBC <= L;
-    const int vc = (int)(L - t0 - 4 * g), vs = (int)(L - t0 - 4 * sq);
-    ld_raw4<kInBF16>(r.u, p.u, row + t0 + 4 * g, vec, true, vc);
-    ld_raw4<kInBF16>(r.r, p.delta, row + t0 + 4 * g, vec, true, vc);
-    ld_raw4<kInBF16>(r.z, has_z ? p.z : p.u, row + t0 + 4 * g, vec, true, vc);
-    ld_raw4<kGradBF16>(r.dy, p.dy, row + t0 + 4 * g, vec, true, vc);
-    ld_raw4<kInBF16>(r.bt, p.Bt, brow + t0 + 4 * sq, vec, sn_ok, vs);
-    ld_raw4<kInBF16>(r.ct, p.Ct, brow + t0 + 4 * sq, vec, sn_ok, vs);
-    hs = c_ok ? *reinterpret_cast<const float4*>(p.ckpt + ((b * D + d) * nck + ck) * 16 + 4 * g)
-              : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  };
-  // per element, once: delta, the softplus derivative (kept in sg for the
-  // write-out), the gated output gradient dyc = dy silu(z) and the factor of
-  // dz = dy yc s (1 + z (1 - s)), s = sigmoid(z); the D gradient sum
-  float accD = 0.0f;
-  auto stage2 = [&](const RawB& r, BwdStage& st, float (&sg)[4]) {
+// Segment carries, one thread per (batch row, channel, state): the state
+// entering segment s, h_in(s + 1) = P(s) h_in(s) + h(s), and the adjoint term
+// entering from segment s + 1, g_in(s - 1) = H(s) + P(s) g_in(s).
+__global__ __launch_bounds__(256) void bwd_carry_kernel(BwdParams p) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= p.B * p.D * 16) return;
+  const int64_t b = i / (p.D * 16), dn = i - b * p.D * 16;
+  float h = 0.0f;
+  for (int64_t s = 0; s < p.S; ++s) {
+    const int64_t o = (b * p.S + s) * p.D * 16 + dn;
+    p.h_in[o] = h;
+    h = __builtin_fmaf(p.seg_P[o], h, p.seg_h[o]);
+  }
+  float gc = 0.0f;
+  for (int64_t s = p.S - 1; s >= 0; --s) {
+    const int64_t o = (b * p.S + s) * p.D * 16 + dn;
+    p.g_in[o] = gc;
+    gc = __builtin_fmaf(p.seg_P[o], gc, p.seg_H[o]);
+  }
+}
+
+// Segment pass 2: chunks of the segment from the last: rebuild the chunk's
+// start state from the stored one and the segment's entering state, rerun
+// its steps keeping h_t and (Abar_t - 1) in registers, then walk them in
+// reverse with the adjoint.
+template <bool kInBF16, bool kGradBF16, bool kDeltaB>
+__global__ __launch_bounds__(64) void bwd_segment_kernel(BwdParams p) {
+  __shared__ Stage st[2];
+  using W = Wave<kInBF16, kGradBF16>;
+  const W w(p);
+  const int lane = w.lane, c = w.c, g = w.g;
+  const bool red_c = lane >= 32;
+  const bool bit3 = (lane >> 3) & 1, bit2 = (lane >> 2) & 1;
+  // lane's slot for the reduced dB/dC value of a step: type (lane bit 5),
+  // state 4 g + 2 (lane bit 4) + (lane bit 3)
+  const int red_state = 4 * g + 2 * ((lane >> 4) & 1) + ((lane >> 3) & 1);
+  float ia2[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float x = r.r.get(j) + bias;
-      const float uu = r.u.get(j);
-      const float dy = r.dy.get(j);
-      float dyc = dy, kz = 0.0f;
-      if (has_z) {
-        const float zv = r.z.get(j);
-        const float s = sigmoidf(zv);
-        dyc = dy * (zv * s);
-        kz = dy * s * __builtin_fmaf(zv, 1.0f - s, 1.0f);
-      }
-      if (!c_ok) { dyc = 0.0f; kz = 0.0f; }
-      st.V[4 * g + j][c] = make_float4(uu, softplus(x), dyc, kz);
-      sg[j] = sigmoidf(x);
-      accD = __builtin_fmaf(dyc, uu, accD);
-      st.B[4 * sq + j][sn] = r.bt.get(j);
-      st.C[4 * sq + j][sn] = r.ct.get(j);
+  for (int i = 0; i < 4; ++i) ia2[i] = w.ia[i] * w.ia[i];
+
+  float hin[4] = {0.0f, 0.0f, 0.0f, 0.0f}, gs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (w.c_ok) {
+    const int64_t o = w.seg_index() * 16 + 4 * g;
+    const float4 hv = *reinterpret_cast<const float4*>(p.h_in + o);
+    const float4 gv = *reinterpret_cast<const float4*>(p.g_in + o);
+    hin[0] = hv.x; hin[1] = hv.y; hin[2] = hv.z; hin[3] = hv.w;
+    gs[0] = gv.x; gs[1] = gv.y; gs[2] = gv.z; gs[3] = gv.w;
+  }
+  float anext[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+  float dAacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float accD = 0.0f, accBias = 0.0f;
+  float sg_cur[2], sg_next[2];
+  float4 hl_cur, hl_next;
+  float cd_cur, cd_next;
+  const int64_t ck0 = w.first_chunk(), ck1 = w.last_chunk();
+  auto fetch_ckpt = [&](int64_t ck, float4& hl, float& cd) {
+    if (w.c_ok) {
+      hl = *reinterpret_cast<const float4*>(p.ckpt_h + ((w.b * p.D + w.d) * p.nck + ck) * 16 + 4 * g);
+      cd = p.ckpt_cd[(w.b * p.D + w.d) * p.nck + ck];
+    } else {
+      hl = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      cd = 0.0f;
     }
   };
-
-  float gs[4] = {0.0f, 0.0f, 0.0f, 0.0f}, anext[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  float dAacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  float accBias = 0.0f;
-  float sg_cur[4], sg_next[4];
-  float4 hs_cur, hs_next;
-  RawB r;
-  fetch2(nck - 1, r, hs_next);
-  stage2(r, S[0], sg_next);
+  typename W::Raw x;
+  w.fetch(ck1, x, true);
+  fetch_ckpt(ck1, hl_next, cd_next);
+  w.stage(x, st[0], true, sg_next, accD);
   __syncthreads();
 
-  // one reverse step; ht = h_t in, h_(t-1) out
-  auto rstep = [&](BwdStage& st, int tl, float (&ht)[4]) {
-    const float4 v = st.V[tl][c];
-    const float4 Bq = *reinterpret_cast<const float4*>(&st.B[tl][4 * g]);
-    const float4 Cq = *reinterpret_cast<const float4*>(&st.C[tl][4 * g]);
-    const float4 hp4 = Hs[tl][lane];
-    const float u = v.x, delta = v.y, dyc = v.z, kz = v.w;
-    const float Bv[4] = {Bq.x, Bq.y, Bq.z, Bq.w}, Cv[4] = {Cq.x, Cq.y, Cq.z, Cq.w};
-    const float hp[4] = {hp4.x, hp4.y, hp4.z, hp4.w};
-    float s = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s = __builtin_fmaf(Cv[i], ht[i], s);
-    const float dz = kz * __builtin_fmaf(Dd, u, quad_sum4(s));
-    const float d2 = delta * delta;
-    float sdu = 0.0f, sdd = 0.0f, dBv[4], dCv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float x = delta * a2[i];
-      const float e = hw_exp2(x);
-      const float coef = kDeltaB ? delta : expm1_from_exp2(x, e) * ia[i];
-      const float gn = __builtin_fmaf(dyc, Cv[i], anext[i] * gs[i]);
-      const float dabar = gn * hp[i];
-      const float gc = gn * coef;
-      dBv[i] = gc * u;
-      dCv[i] = dyc * ht[i];
-      sdu = __builtin_fmaf(gc, Bv[i], sdu);
-      const float dcoef = gn * (Bv[i] * u);
-      const float de = dabar * e;
-      if constexpr (kDeltaB) {
-        sdd = __builtin_fmaf(de, a[i], sdd + dcoef);
-        dAacc[i] = __builtin_fmaf(de, delta, dAacc[i]);
-      } else {
-        sdd = __builtin_fmaf(__builtin_fmaf(dabar, a[i], dcoef), e, sdd);
-        // d coef / dA = delta^2 phi(delta A), phi(y) = (y e^y - e^y + 1) / y^2:
-        // its series to y^5 for |y| < 1/4 (next term y^6 / 5760, below 2^-24
-        // of phi there), else (y e^y - e^y + 1) / A^2
-        const float y = delta * a[i];
-        float ps = __builtin_fmaf(y, 1.0f / 840.0f, 1.0f / 144.0f);
-        ps = __builtin_fmaf(y, ps, 1.0f / 30.0f);
-        ps = __builtin_fmaf(y, ps, 1.0f / 8.0f);
-        ps = __builtin_fmaf(y, ps, 1.0f / 3.0f);
-        ps = __builtin_fmaf(y, ps, 0.5f);
-        const float closed = __builtin_fmaf(y, e, 1.0f - e) * (ia[i] * ia[i]);
-        const float q = (__builtin_fabsf(y) < 0.25f) ? d2 * ps : closed;
-        dAacc[i] = __builtin_fmaf(dcoef, q, __builtin_fmaf(de, delta, dAacc[i]));
-      }
-      gs[i] = gn;
-      anext[i] = e;
-      ht[i] = hp[i];
+  for (int64_t ck = ck1, it = 0; ck >= ck0; --ck, ++it) {
+    Stage& cs = st[it & 1];
+    const bool more = ck > ck0;
+    sg_cur[0] = sg_next[0];
+    sg_cur[1] = sg_next[1];
+    hl_cur = hl_next;
+    cd_cur = cd_next;
+    if (more) {
+      w.fetch(ck - 1, x, true);
+      fetch_ckpt(ck - 1, hl_next, cd_next);
     }
-    const float du = __builtin_fmaf(dyc, Dd, quad_sum4(sdu));
-    const float dpre = quad_sum4(sdd);
-    // results of this step over its inputs: lane g writes component g
-    reinterpret_cast<float*>(&st.V[tl][c])[g] = g == 0 ? du : (g == 1 ? dpre : dz);
-    // dB_t, dC_t over the wave's 16 channels (lane bits 2..5)
-    float w0 = swap32_sum(dBv[0], dCv[0]);
-    float w1 = swap32_sum(dBv[1], dCv[1]);
-    float w2 = swap32_sum(dBv[2], dCv[2]);
-    float w3 = swap32_sum(dBv[3], dCv[3]);
-    const float q0 = swap16_sum(w0, w2);
-    const float q1 = swap16_sum(w1, w3);
-    const float keep = bit3 ? q1 : q0, send = bit3 ? q0 : q1;
-    const float rr = keep + dpp_mov<0x128>(send);           // row_ror:8 pairs lane bit 3
-    // partner lane ^ 4: row_ror:4 reads lane i - 4, row_ror:12 lane i + 4
-    // (both evaluated with the whole wave active, then selected)
-    const float from_m4 = dpp_mov<0x124>(rr), from_p4 = dpp_mov<0x12C>(rr);
-    const float fin = rr + (bit2 ? from_m4 : from_p4);
-    (red_c ? st.C[tl] : st.B[tl])[red_state] = fin;
-  };
-
-  for (int64_t ck = nck - 1, it = 0; ck >= 0; --ck, ++it) {
-    BwdStage& st = S[it & 1];
-    const bool more = ck > 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) sg_cur[j] = sg_next[j];
-    hs_cur = hs_next;
-    if (more) fetch2(ck - 1, r, hs_next);
-    const int64_t t0 = ck * kBC;
-    const int len = chunk_len(ck);
-    float hh[4] = {hs_cur.x, hs_cur.y, hs_cur.z, hs_cur.w};
-    Hs[0][lane] = hs_cur;
-    if (len == kBC) {
-#pragma unroll
-      for (int tl = 0; tl < kBC; ++tl) {
-        fstep(st, tl, hh);
-        Hs[tl + 1][lane] = make_float4(hh[0], hh[1], hh[2], hh[3]);
-      }
-#pragma unroll 2
-      for (int tl = kBC - 1; tl >= 0; --tl) rstep(st, tl, hh);
-    } else {
-      for (int tl = 0; tl < len; ++tl) {
-        fstep(st, tl, hh);
-        Hs[tl + 1][lane] = make_float4(hh[0], hh[1], hh[2], hh[3]);
-      }
-      for (int tl = len - 1; tl >= 0; --tl) rstep(st, tl, hh);
-    }
-    __syncthreads();
-    // write out: lane (c, g) owns steps 4 g .. 4 g + 3 of channel c
+    const int64_t t0 = ck * kT;
+    const int len = w.chunk_len(ck);
+    // chunk start state: stored (zero segment start) + P(start .. chunk) h_in
+    float hist[kT + 1][4], ec[kT][4];
     {
-      const bool vec = vecp && len == kBC;
-      const int valid = len - 4 * g;
-      float du[4], dr[4], dz[4];
+      const float hl[4] = {hl_cur.x, hl_cur.y, hl_cur.z, hl_cur.w};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float4 o = st.V[4 * g + j][c];
-        du[j] = o.x;
-        dr[j] = o.y * sg_cur[j];
-        dz[j] = o.z;
-        if (j < valid) accBias += dr[j];
-      }
-      if (c_ok) {
-        st4<kGradBF16>(p.du, row + t0 + 4 * g, vec, valid, du);
-        st4<kGradBF16>(p.ddelta, row + t0 + 4 * g, vec, valid, dr);
-        if (has_z) st4<kGradBF16>(p.dz, row + t0 + 4 * g, vec, valid, dz);
-      }
-      if (sn_ok) {
-        float vb[4], vcc[4];
+      for (int i = 0; i < 4; ++i) hist[0][i] = __builtin_fmaf(hw_exp2(w.a2[i] * cd_cur), hin[i], hl[i]);
+    }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          vb[j] = st.B[4 * sq + j][sn];
-          vcc[j] = st.C[4 * sq + j][sn];
+    for (int tl = 0; tl < kT; ++tl) {
+      if (tl < len) {
+        const float2 v = *reinterpret_cast<const float2*>(&cs.V[tl][c]);
+        const float4 Bq = *reinterpret_cast<const float4*>(&cs.B[tl][4 * g]);
+        const float bv[4] = {Bq.x, Bq.y, Bq.z, Bq.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float xx = v.y * w.a2[i];
+          const float e = hw_exp2(xx);
+          float coef;
+          if constexpr (kDeltaB) {
+            ec[tl][i] = e;
+            coef = v.y;
+          } else {
+            const float E = expm1_from_exp2(xx, e);
+            ec[tl][i] = E;
+            coef = E * w.ia[i];
+          }
+          hist[tl + 1][i] = __builtin_fmaf(e, hist[tl][i], coef * (bv[i] * v.x));
         }
-        const int64_t o = ((b * p.tiles_d + td) * 16 + sn) * L + t0 + 4 * sq;
-        st4<false>(p.part_dB, o, vec, len - 4 * sq, vb);
-        st4<false>(p.part_dC, o, vec, len - 4 * sq, vcc);
       }
     }
-    if (more) stage2(r, S[(it + 1) & 1], sg_next);
+#pragma unroll
+    for (int tl = kT - 1; tl >= 0; --tl) {
+      if (tl < len) {
+        const float4 v = cs.V[tl][c];
+        const float4 Bq = *reinterpret_cast<const float4*>(&cs.B[tl][4 * g]);
+        const float4 Cq = *reinterpret_cast<const float4*>(&cs.C[tl][4 * g]);
+        const float u = v.x, delta = v.y, dyc = v.z, kz = v.w;
+        const float Bv[4] = {Bq.x, Bq.y, Bq.z, Bq.w}, Cv[4] = {Cq.x, Cq.y, Cq.z, Cq.w};
+        float s = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s = __builtin_fmaf(Cv[i], hist[tl + 1][i], s);
+        const float dz = kz * __builtin_fmaf(w.Dd, u, quad_sum4(s));
+        const float d2 = delta * delta;
+        float sdu = 0.0f, sdd = 0.0f, dBv[4], dCv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float e = kDeltaB ? ec[tl][i] : ec[tl][i] + 1.0f;
+          const float coef = kDeltaB ? delta : ec[tl][i] * w.ia[i];
+          const float gn = __builtin_fmaf(dyc, Cv[i], anext[i] * gs[i]);
+          const float dabar = gn * hist[tl][i];
+          const float gc = gn * coef;
+          dBv[i] = gc * u;
+          dCv[i] = dyc * hist[tl + 1][i];
+          sdu = __builtin_fmaf(gc, Bv[i], sdu);
+          const float dcoef = gn * (Bv[i] * u);
+          const float de = dabar * e;
+          if constexpr (kDeltaB) {
+            sdd = __builtin_fmaf(de, w.a[i], sdd + dcoef);
+            dAacc[i] = __builtin_fmaf(de, delta, dAacc[i]);
+          } else {
+            sdd = __builtin_fmaf(__builtin_fmaf(dabar, w.a[i], dcoef), e, sdd);
+            // d coef / dA = delta^2 phi(delta A), phi(y) = (y e^y - e^y + 1) / y^2:
+            // its series to y^5 for |y| < 1/4 (next term y^6 / 5760, below 2^-24
+            // of phi there), else (y e^y - e^y + 1) / A^2
+            const float y = delta * w.a[i];
+            float ps = __builtin_fmaf(y, 1.0f / 840.0f, 1.0f / 144.0f);
+            ps = __builtin_fmaf(y, ps, 1.0f / 30.0f);
+            ps = __builtin_fmaf(y, ps, 1.0f / 8.0f);
+            ps = __builtin_fmaf(y, ps, 1.0f / 3.0f);
+            ps = __builtin_fmaf(y, ps, 0.5f);
+            const float closed = __builtin_fmaf(y, e, -ec[tl][i]) * ia2[i];
+            const float q = (__builtin_fabsf(y) < 0.25f) ? d2 * ps : closed;
+            dAacc[i] = __builtin_fmaf(dcoef, q, __builtin_fmaf(de, delta, dAacc[i]));
+          }
+          gs[i] = gn;
+          anext[i] = e;
+        }
+        const float du = __builtin_fmaf(dyc, w.Dd, quad_sum4(sdu));
+        const float dpre = quad_sum4(sdd);
+        // results of this step over its inputs: lane g writes component g
+        reinterpret_cast<float*>(&cs.V[tl][c])[g] = g == 0 ? du : (g == 1 ? dpre : dz);
+        // dB_t, dC_t over the wave's 16 channels (lane bits 2..5)
+        const float w0 = swap32_sum(dBv[0], dCv[0]);
+        const float w1 = swap32_sum(dBv[1], dCv[1]);
+        const float w2 = swap32_sum(dBv[2], dCv[2]);
+        const float w3 = swap32_sum(dBv[3], dCv[3]);
+        const float q0 = swap16_sum(w0, w2);
+        const float q1 = swap16_sum(w1, w3);
+        const float keep = bit3 ? q1 : q0, send = bit3 ? q0 : q1;
+        const float rr = keep + dpp_mov<0x128>(send);           // row_ror:8 pairs lane bit 3
+        // partner lane ^ 4: row_ror:4 reads lane i - 4, row_ror:12 lane i + 4
+        // (both evaluated with the whole wave active, then selected)
+        const float from_m4 = dpp_mov<0x124>(rr), from_p4 = dpp_mov<0x12C>(rr);
+        const float fin = rr + (bit2 ? from_m4 : from_p4);
+        (red_c ? cs.C[tl] : cs.B[tl])[red_state] = fin;
+      }
+    }
     __syncthreads();
+    // write out: lane (c, g) owns steps 2 g, 2 g + 1 of channel c; as (sn, sq)
+    // steps 2 sq, 2 sq + 1 of state sn == c
+    {
+      const bool vec = w.vecp && len == kT;
+      const int valid = len - 2 * g;
+      const float4 o0 = cs.V[2 * g][c], o1 = cs.V[2 * g + 1][c];
+      const float dr0 = o0.y * sg_cur[0], dr1 = o1.y * sg_cur[1];
+      if (valid > 0) accBias += dr0;
+      if (valid > 1) accBias += dr1;
+      if (w.c_ok) {
+        st2<kGradBF16>(p.du, w.row + t0 + 2 * g, vec, valid, o0.x, o1.x);
+        st2<kGradBF16>(p.ddelta, w.row + t0 + 2 * g, vec, valid, dr0, dr1);
+        if (w.has_z) st2<kGradBF16>(p.dz, w.row + t0 + 2 * g, vec, valid, o0.z, o1.z);
+      }
+      if (w.sn_ok) {
+        const int64_t o = ((w.b * p.tiles_d + w.td) * 16 + c) * p.L + t0 + 2 * g;
+        st2<false>(p.part_dB, o, vec, valid, cs.B[2 * g][c], cs.B[2 * g + 1][c]);
+        st2<false>(p.part_dC, o, vec, valid, cs.C[2 * g][c], cs.C[2 * g + 1][c]);
+      }
+    }
+    if (more) {
+      __syncthreads();
+      w.stage(x, st[(it + 1) & 1], true, sg_next, accD);
+      __syncthreads();
+    }
   }
   accD = quad_sum4(accD);
   accBias = quad_sum4(accBias);
-  if (c_ok) {
-    *reinterpret_cast<float4*>(p.part_dA + (b * D + d) * 16 + 4 * g) =
-        make_float4(dAacc[0], dAacc[1], dAacc[2], dAacc[3]);
+  if (w.c_ok) {
+    const int64_t o = w.seg_index();
+    *reinterpret_cast<float4*>(p.part_dA + o * 16 + 4 * g) = make_float4(dAacc[0], dAacc[1], dAacc[2], dAacc[3]);
     if (g == 0) {
-      p.part_dD[b * D + d] = accD;
-      p.part_dbias[b * D + d] = accBias;
+      p.part_dD[o] = accD;
+      p.part_dbias[o] = accBias;
     }
   }
 }
@@ -446,44 +527,53 @@ __global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(BwdParams p) {
   const int64_t b = i / (p.N * p.L);
   const int64_t rem = i - b * p.N * p.L;
   const int64_t n = rem / p.L, t = rem - n * p.L;
+  const float* pb = p.part_dB + (b * p.tiles_d * 16 + n) * p.L + t;
+  const float* pc = p.part_dC + (b * p.tiles_d * 16 + n) * p.L + t;
+  const int64_t stride = 16 * p.L;
   float sb = 0.0f, sc = 0.0f;
+#pragma unroll 8
   for (int64_t td = 0; td < p.tiles_d; ++td) {
-    const int64_t o = ((b * p.tiles_d + td) * 16 + n) * p.L + t;
-    sb += p.part_dB[o];
-    sc += p.part_dC[o];
+    sb += pb[td * stride];
+    sc += pc[td * stride];
   }
   p.dBt[i] = sb;
   p.dCt[i] = sc;
 }
 
-// dA, dD, bias gradient: sum of the per-batch-row partials, in row order.
+// dA, dD, bias gradient: sum of the per-segment partials, batch rows outer,
+// segments inner.
 __global__ __launch_bounds__(256) void bwd_reduce_params_kernel(BwdParams p) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= p.D * 16) return;
   const int64_t d = i >> 4, n = i & 15;
+  const int64_t rows = p.B * p.S;
   if (n < p.N) {
     float s = 0.0f;
-    for (int64_t b = 0; b < p.B; ++b) s += p.part_dA[(b * p.D + d) * 16 + n];
+    for (int64_t r = 0; r < rows; ++r) s += p.part_dA[(r * p.D + d) * 16 + n];
     p.dA[d * p.N + n] = s;
   }
   if (n == 0) {
     float sd = 0.0f, sb = 0.0f;
-    for (int64_t b = 0; b < p.B; ++b) {
-      sd += p.part_dD[b * p.D + d];
-      sb += p.part_dbias[b * p.D + d];
+    for (int64_t r = 0; r < rows; ++r) {
+      sd += p.part_dD[r * p.D + d];
+      sb += p.part_dbias[r * p.D + d];
     }
     p.dDskip[d] = sd;
     p.dbias[d] = sb;
   }
 }
 
-template <bool kInBF16, bool kGradBF16>
+template <bool kInBF16, bool kGradBF16, bool kDeltaB>
 hipError_t bwd_t(const BwdParams& p, hipStream_t s) {
-  if (p.delta_b)
-    hipLaunchKernelGGL((scan_bwd_kernel<kInBF16, kGradBF16, true>), dim3((unsigned)(p.B * p.tiles_d)), dim3(64), 0, s, p);
-  else
-    hipLaunchKernelGGL((scan_bwd_kernel<kInBF16, kGradBF16, false>), dim3((unsigned)(p.B * p.tiles_d)), dim3(64), 0, s, p);
+  const dim3 tasks((unsigned)(p.B * p.tiles_d * p.S));
+  hipLaunchKernelGGL((bwd_summary_kernel<kInBF16, kGradBF16, kDeltaB>), tasks, dim3(64), 0, s, p);
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_carry_kernel, dim3((unsigned)((p.B * p.D * 16 + 255) / 256)), dim3(256), 0, s, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_segment_kernel<kInBF16, kGradBF16, kDeltaB>), tasks, dim3(64), 0, s, p);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t nbc = p.B * p.N * p.L;
   hipLaunchKernelGGL(bwd_reduce_bc_kernel, dim3((unsigned)((nbc + 255) / 256)), dim3(256), 0, s, p);
@@ -493,11 +583,16 @@ hipError_t bwd_t(const BwdParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <bool kInBF16, bool kGradBF16>
+hipError_t bwd_d(const BwdParams& p, hipStream_t s) {
+  return p.delta_b ? bwd_t<kInBF16, kGradBF16, true>(p, s) : bwd_t<kInBF16, kGradBF16, false>(p, s);
+}
+
 }  // namespace
 
 hipError_t launch_scan_bwd(const BwdParams& p, Dt in, Dt grad, hipStream_t s) {
-  if (in == Dt::BF16) return grad == Dt::BF16 ? bwd_t<true, true>(p, s) : bwd_t<true, false>(p, s);
-  return grad == Dt::BF16 ? bwd_t<false, true>(p, s) : bwd_t<false, false>(p, s);
+  if (in == Dt::BF16) return grad == Dt::BF16 ? bwd_d<true, true>(p, s) : bwd_d<true, false>(p, s);
+  return grad == Dt::BF16 ? bwd_d<false, true>(p, s) : bwd_d<false, false>(p, s);
 }
 
 }  // namespace mamba

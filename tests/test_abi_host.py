@@ -185,9 +185,13 @@ def test_bwd_workspace_size():
     ws = _lib.scan_bwd_workspace_size
     a = lambda x: (x + 255) // 256 * 256  # noqa: E731
     B, D, N, L = 2, 70, 5, 100
-    tiles, nck = 5, 7   # 16-step chunks
-    assert ws(B, D, N, L) == (a(B * D * nck * 16 * 4) + 2 * a(B * tiles * 16 * L * 4) + a(B * D * 16 * 4)
-                              + 2 * a(B * D * 4))
+    # 5 channel tiles; 8-step chunks -> 13; segments: 10 (row, tile) pairs
+    # want 820 segments, at most ceil(100 / 64) = 2 -> 50 steps, rounded up to
+    # 64 -> 2 segments
+    tiles, nck, S = 5, 13, 2
+    bd, bsd = B * D, B * D * S
+    assert ws(B, D, N, L) == (a(bd * nck * 16 * 4) + a(bd * nck * 4) + 5 * a(bsd * 16 * 4)
+                              + 2 * a(B * tiles * 16 * L * 4) + a(bsd * 16 * 4) + 2 * a(bsd * 4))
     assert _lib.lib().mamba_scan_bwd_workspace_size(1, 1, 17, 1) == ctypes.c_size_t(-1).value
 
 

@@ -70,6 +70,8 @@ CASES = [
     (1, 1, 1, 33, "f32", "f32", {}),
     (2, 40, 16, 44, "bf16", "bf16", {"delta_b": True}),   # vector loads, ragged last chunk
     (1, 16, 16, 48, "f32", "bf16", {}),
+    (1, 16, 16, 1000, "f32", "f32", {}),                # 16 segments of L, the last one ragged
+    (1, 8, 7, 777, "bf16", "f32", {}),                  # 13 segments, odd L, a one-step last chunk
 ]
 
 
