@@ -398,7 +398,8 @@ def bench_bwd(args, dev):
         xs = W.scan_inputs(W.ScanConfig(cfg.name, cfg.B, cfg.D, cfg.N, cfg.L, cfg.dtype, cfg.seed + 100 * k,
                                         cfg.dskip, cfg.final_state))
         t = {k2: to_dev(xs[k2], dev) for k2 in ("u", "delta_raw", "z", "Bt", "Ct", "A", "Dskip", "delta_bias")}
-        t["dy"] = torch.randn((cfg.B, cfg.D, cfg.L), device=dev).to(torch.bfloat16)
+        dy = W._normal_f32([cfg.seed + 100 * k, 77], cfg.B * cfg.D * cfg.L).reshape(cfg.B, cfg.D, cfg.L)
+        t["dy"] = torch.from_numpy(dy).to(dev).to(torch.bfloat16)
         sets.append(t)
     ws = torch.empty(m.scan_bwd_workspace_size(cfg.B, cfg.D, cfg.N, cfg.L), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)

@@ -143,7 +143,10 @@ int mamba_state_update(float* state, const void* u, const void* delta, const voi
 
 /*
  * Bytes of device workspace mamba_scan_bwd needs (shape only; callable
- * without a GPU), (size_t)-1 for an invalid shape.
+ * without a GPU), (size_t)-1 for an invalid shape.  It holds fp32 chunk-start
+ * states (one per 8 steps), the segment summaries and carries, and per-tile
+ * partial sums of dB_t / dC_t: about 18 bytes per (B, D, L) element for
+ * D = 5120, N = 16.
  */
 size_t mamba_scan_bwd_workspace_size(int64_t B, int64_t D, int64_t N, int64_t L);
 
