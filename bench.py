@@ -12,8 +12,10 @@ Other workloads: --workload long_b1 (B=1 D=4096 L=131072, chunked along L),
 mamba130m_layer, tiny_fp32, decode48 (48 layers x 128 steps of
 mamba_state_update at B=128 D=4096, the 48-layer step replayed as a graph),
 conv_2.8b_layer (causal conv1d + SiLU at B=4 D=5120 L=2048 K=4) and
-conv_decode48 (48 layers x 128 steps of the one-token conv update) and
-bwd_2.8b_layer (the scan's backward pass at the 2.8B-layer shape).
+conv_decode48 (48 layers x 128 steps of the one-token conv update),
+bwd_2.8b_layer (the scan's backward pass at the 2.8B-layer shape) and
+ssd_2.7b_layer (the Mamba-2 layer forward: B=4, 80 heads x 64 channels,
+N=128, L=2048, on the matrix cores).
 
 --copy-calibration runs only a plain device copy of known size (used to
 scale rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes).
@@ -442,6 +444,80 @@ def bench_bwd(args, dev):
     }
 
 
+# MI355X dense bf16 matrix peak (AMD published, without sparsity).
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+SSD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ssd_2.7b_layer_traffic.txt")
+SSD_SOURCES = ["selective_state_space_75_amd/csrc/ssd.hip", "selective_state_space_75_amd/csrc/kernels.hpp",
+               "selective_state_space_75_amd/csrc/device_math.hpp", "selective_state_space_75_amd/csrc/abi.hip"]
+
+
+def ssd_mfma_flops(cfg) -> int:
+    """Matrix-core flops one launch issues (the split operands counted twice):
+    per 64-channel block and 32-step chunk, C B^T on 3 of 4 16x16 tiles (K = N),
+    G x (K = 32, two parts), C H (K = N, two parts) and B^T (w o x) (K = 32,
+    two parts)."""
+    q, pb = 32, 64
+    per_chunk = 2 * (3 * 16 * 16 * cfg.N + 2 * q * pb * q + 2 * q * pb * cfg.N + 2 * cfg.N * pb * q)
+    chunks = (cfg.L + q - 1) // q
+    return per_chunk * chunks * cfg.B * cfg.H * (cfg.P // pb)
+
+
+def bench_ssd(args, dev):
+    """Mamba-2 (SSD) layer forward: B=4, 80 heads x 64 channels, N=128, L=2048."""
+    import torch
+    import selective_state_space_75_amd as m
+    from selective_state_space_75_amd import workloads as W
+    cfg = W.SSD_CONFIGS[args.workload]
+    log("ssd workload %s: B=%d H=%d P=%d N=%d L=%d" % (cfg.name, cfg.B, cfg.H, cfg.P, cfg.N, cfg.L))
+    sets = []
+    for k in range(args.sets):
+        xs = W.ssd_inputs(cfg.B, cfg.H, cfg.P, cfg.N, cfg.L, cfg.seed + 100 * k, cfg.gate)
+        sets.append({n: (None if v is None else to_dev(v, dev)) for n, v in xs.items() if n != "dt"})
+    ys = [torch.empty((cfg.B, cfg.D, cfg.L), dtype=torch.bfloat16, device=dev) for _ in sets]
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        t = sets[i % len(sets)]
+        m.ssd_fwd(t["x"], t["delta_raw"], t["z"], t["Bt"], t["Ct"], t["A"], t["Dskip"], t["delta_bias"], P=cfg.P,
+                  y=ys[i % len(sets)], stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [a.elapsed_time(b) for a, b in ev]
+    kern_ms = float(np.mean(per))
+    ms_step = wall * 1e3 / args.steps
+    nbytes = cfg.algorithmic_bytes()
+    ach = nbytes / (kern_ms * 1e-3) / 1e9
+    flops = ssd_mfma_flops(cfg)
+    traffic, note = recorded_traffic(SSD_TRAFFIC_FILE, SSD_SOURCES)
+    return {
+        "metric": "Mamba-2 SSD layer HBM GB/s (% of MI355X peak) at a 2.7B-shaped layer",
+        "value": round(nbytes / (ms_step * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.name, "B": cfg.B, "H": cfg.H, "P": cfg.P, "N": cfg.N, "L": cfg.L,
+                   "gate": cfg.gate, "input_sets": len(sets)},
+        "elems_per_s": round(cfg.elements / (ms_step * 1e-3), 1),
+        "kernel_ms_mean": round(kern_ms, 5),
+        "kernel_ms_p10_p50_p90": [round(float(v), 5) for v in np.percentile(per, [10, 50, 90])],
+        "roofline": {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic, "traffic_note": note,
+                     "algorithmic_bytes": nbytes},
+        "mfma": {"flops_per_launch": flops, "achieved_tflops": round(flops / (kern_ms * 1e-3) / 1e12, 1),
+                 "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+                 "frac": round(flops / (kern_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
+    }
+
+
 def copy_calibration(args, dev):
     import torch
     n = args.copy_mb * (1 << 20) // 4
@@ -488,6 +564,8 @@ def main():
         line = bench_conv(args, dev)
     elif args.workload in W.CONV_UPDATE_CONFIGS:
         line = bench_conv_decode(args, dev)
+    elif args.workload in W.SSD_CONFIGS:
+        line = bench_ssd(args, dev)
     else:
         line, cfg, x = bench_scan(args, dev)
         if not args.no_cpu_baseline:

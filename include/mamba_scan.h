@@ -227,6 +227,37 @@ int mamba_conv1d_update(float* state, const void* x, const float* weight, const 
                         int64_t B, int64_t D, int64_t K, mamba_dtype_t in_dtype, mamba_dtype_t out_dtype,
                         hipStream_t stream);
 
+/*
+ * Mamba-2 layer forward (state space duality), one scalar A per head.
+ *   "Mamba 与状态空间模型" section 09 and "Mamba 状态空间模型架构深度解析"
+ *   (Mamba-2): with A a scalar times the identity, a layer multiplies the
+ *   sequence by a lower-triangular matrix, entry (t, s) = C_t . B_s times the
+ *   decay between steps s and t times B-bar's coefficient; it is computed in
+ *   chunks, with matrix products inside a chunk and the state passed between
+ *   chunks.  Per head h of P channels (channel d = h P + p):
+ *     delta_t = softplus(delta_raw[b,h,t] + delta_bias[h]),
+ *     h_t = exp(delta_t A[h]) h_(t-1) + coef_t B_t x_t  (state N per channel,
+ *     coef = (exp(delta A) - 1)/A, or delta with MAMBA_FLAG_DELTA_B),
+ *     y_t = (C_t . h_t + Dskip[d] x_t) * silu(z_t)  (no gate when z is NULL).
+ *
+ *   x, z        : (B, H*P, L) bf16; z may be NULL.
+ *   delta       : (B, H, L) bf16, raw step sizes, one per head.
+ *   Bt, Ct      : (B, N, L) bf16, shared by all heads.
+ *   A           : (H) fp32.  Dskip : (H*P) fp32 or NULL.  delta_bias : (H) fp32 or NULL.
+ *   y           : (B, H*P, L) out_dtype (bf16 or fp32), written.
+ *   final_state : (B, H*P, N) fp32, written iff return_final_state.
+ *
+ * in_dtype must be MAMBA_BF16 (MAMBA_ERR_UNSUPPORTED otherwise); N must be 64
+ * or 128 and P a multiple of 64 (MAMBA_ERR_UNSUPPORTED).  Alignment: bf16
+ * arrays 2-byte, fp32 arrays 4-byte (16-byte pointers and L % 8 == 0 select
+ * vector accesses).  No workspace; the initial state is zero.
+ */
+int mamba_ssd_fwd(const void* x, const void* delta, const void* z, const void* Bt, const void* Ct,
+                  const float* A, const float* Dskip, const float* delta_bias, void* y, float* final_state,
+                  int64_t B, int64_t H, int64_t P, int64_t N, int64_t L,
+                  mamba_dtype_t in_dtype, mamba_dtype_t out_dtype, int return_final_state,
+                  unsigned flags, hipStream_t stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char* mamba_status_string(int status);
 

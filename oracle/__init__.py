@@ -153,6 +153,36 @@ def state_update(state, u, delta_raw, z, Bt, Ct, A, Dskip=None, delta_bias=None,
     return y, st
 
 
+def ssd_scan(x, delta_raw, z, Bt, Ct, A_head, Dskip=None, delta_bias=None, P: int = 64,
+             discretization: str = "zoh", nthreads: int | None = None):
+    """Mamba-2 layer (SSD) over x (B, H*P, L) with one scalar A per head.
+
+    "Mamba 与状态空间模型" section 09 and "Mamba 状态空间模型架构深度解析"
+    (Mamba-2): A is a scalar times the identity, so the layer is the same
+    selective recurrence with A[d, n] = A_head[h] for every state n of every
+    channel d of head h; the step size is shared by the head's P channels,
+    which is what lets one lower-triangular matrix act on all of them.
+
+    delta_raw (B, H, L), delta_bias (H) are per head; x, z (B, H*P, L);
+    Bt, Ct (B, N, L); Dskip (H*P).  Returns (y (B, H*P, L), final_state
+    (B, H*P, N)) as float64, by expanding the heads into the pinned scan.
+    """
+    x = _f64(x)
+    if x.ndim != 3:
+        raise ValueError("x must be (B, H*P, L)")
+    B, D, L = x.shape
+    if P < 1 or D % P:
+        raise ValueError("H*P must be a multiple of P")
+    H = D // P
+    delta_raw = _f64(delta_raw, (B, H, L))
+    A_head = _f64(A_head, (H,))
+    N = _f64(Bt).shape[1]
+    A = np.repeat(A_head, P)[:, None] * np.ones((1, N))
+    dr = np.repeat(delta_raw, P, axis=1)
+    bias = None if delta_bias is None else np.repeat(_f64(delta_bias, (H,)), P)
+    return scan(x, dr, z, Bt, Ct, A, Dskip, bias, discretization=discretization, nthreads=nthreads)
+
+
 def conv1d(x, w, bias=None, state0=None, activation: bool = True):
     """Causal depthwise convolution (+ SiLU) over (B, D, L); w is (D, K), tap i
     multiplies x[t - i].  Returns (y (B,D,L), final_state (B,D,K)), float64."""

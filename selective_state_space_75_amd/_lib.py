@@ -59,6 +59,8 @@ def lib() -> ctypes.CDLL:
             L.mamba_conv1d_fwd.restype = c_int
             L.mamba_conv1d_update.argtypes = [vp] * 5 + [i64] * 3 + [c_int, c_int, vp]
             L.mamba_conv1d_update.restype = c_int
+            L.mamba_ssd_fwd.argtypes = [vp] * 10 + [i64] * 5 + [c_int, c_int, c_int, u32, vp]
+            L.mamba_ssd_fwd.restype = c_int
             L.mamba_status_string.argtypes = [c_int]
             L.mamba_status_string.restype = ctypes.c_char_p
             _lib = L
@@ -167,6 +169,52 @@ def scan_fwd(u, delta, z, Bt, Ct, A, Dskip=None, delta_bias=None, *, return_fina
         _stream(dev, stream))
     if st != 0:
         raise MambaError(st, "mamba_scan_fwd")
+    return (y, final_state) if return_final_state else y
+
+
+def ssd_fwd(x, delta, z, Bt, Ct, A, Dskip=None, delta_bias=None, *, P=64, return_final_state=False,
+            out_dtype=None, delta_b=False, y=None, final_state=None, stream=None):
+    """Mamba-2 (SSD) layer forward.  x, z: (B, H*P, L) bf16; delta: (B, H, L) bf16;
+    Bt, Ct: (B, N, L) bf16; A, delta_bias: (H) fp32; Dskip: (H*P) fp32.
+
+    Returns y (B, H*P, L), or (y, final_state (B, H*P, N) fp32) when return_final_state.
+    """
+    torch = _torch()
+    if x.dim() != 3 or Bt.dim() != 3 or delta.dim() != 3:
+        raise ValueError("x must be (B, H*P, L), delta (B, H, L) and Bt (B, N, L)")
+    B, D, L = x.shape
+    H = delta.shape[1]
+    N = Bt.shape[1]
+    if H * P != D:
+        raise ValueError("x has %d channels, delta %d heads of P = %d" % (D, H, P))
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU device")
+    in_dt = x.dtype
+    _dtype_code(x)
+    _check(x, "x", (B, D, L), in_dt, dev)
+    _check(delta, "delta", (B, H, L), in_dt, dev)
+    _check(z, "z", (B, D, L), in_dt, dev)
+    _check(Bt, "Bt", (B, N, L), in_dt, dev)
+    _check(Ct, "Ct", (B, N, L), in_dt, dev)
+    _check(A, "A", (H,), torch.float32, dev)
+    _check(Dskip, "Dskip", (D,), torch.float32, dev)
+    _check(delta_bias, "delta_bias", (H,), torch.float32, dev)
+    out_dt = in_dt if out_dtype is None else out_dtype
+    if y is None:
+        y = torch.empty((B, D, L), dtype=out_dt, device=dev)
+    _check(y, "y", (B, D, L), out_dt, dev)
+    if return_final_state:
+        if final_state is None:
+            final_state = torch.empty((B, D, N), dtype=torch.float32, device=dev)
+        _check(final_state, "final_state", (B, D, N), torch.float32, dev)
+    st = lib().mamba_ssd_fwd(
+        _ptr(x), _ptr(delta), _ptr(z), _ptr(Bt), _ptr(Ct), _ptr(A), _ptr(Dskip), _ptr(delta_bias),
+        _ptr(y), _ptr(final_state if return_final_state else None), B, H, P, N, L,
+        _dtype_code(x), _dtype_code(y), 1 if return_final_state else 0, FLAG_DELTA_B if delta_b else 0,
+        _stream(dev, stream))
+    if st != 0:
+        raise MambaError(st, "mamba_ssd_fwd")
     return (y, final_state) if return_final_state else y
 
 

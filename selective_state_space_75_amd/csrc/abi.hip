@@ -347,6 +347,36 @@ int mamba_scan_bwd(const void* u, const void* delta, const void* z, const void* 
   return mamba::launch_scan_bwd(p, in, gd, stream) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
 }
 
+int mamba_ssd_fwd(const void* x, const void* delta, const void* z, const void* Bt, const void* Ct,
+                  const float* A, const float* Dskip, const float* delta_bias, void* y, float* final_state,
+                  int64_t B, int64_t H, int64_t P, int64_t N, int64_t L,
+                  mamba_dtype_t in_dtype, mamba_dtype_t out_dtype, int return_final_state,
+                  unsigned flags, hipStream_t stream) {
+  if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return MAMBA_ERR_DTYPE;
+  if (flags & ~MAMBA_FLAG_DELTA_B) return MAMBA_ERR_UNSUPPORTED;
+  if (H < 1 || P < 1 || H > kMaxElems / P || !shape_ok(B, H * P, N, L)) return MAMBA_ERR_SHAPE;
+  if (in_dtype != MAMBA_BF16 || (N != 64 && N != 128) || P % 64 != 0) return MAMBA_ERR_UNSUPPORTED;
+  if (!x || !delta || !Bt || !Ct || !A || !y || (return_final_state && !final_state)) return MAMBA_ERR_NULL;
+  for (const void* ptr : {x, delta, z, Bt, Ct})
+    if (ptr && !aligned(ptr, 2)) return MAMBA_ERR_ALIGN;
+  if (!aligned(y, out_dtype == MAMBA_BF16 ? 2 : 4)) return MAMBA_ERR_ALIGN;
+  for (const void* ptr : {(const void*)A, (const void*)Dskip, (const void*)delta_bias,
+                          (const void*)(return_final_state ? final_state : nullptr)})
+    if (ptr && !aligned(ptr, 4)) return MAMBA_ERR_ALIGN;
+  if (B * H * (P / 64) >= (int64_t(1) << 31)) return MAMBA_ERR_SHAPE;
+  mamba::SsdParams p{};
+  p.x = x; p.delta = delta; p.z = z; p.Bt = Bt; p.Ct = Ct;
+  p.A = A; p.Dskip = Dskip; p.bias = delta_bias;
+  p.y = y; p.final_state = return_final_state ? final_state : nullptr;
+  p.B = B; p.H = H; p.P = P; p.N = N; p.L = L;
+  p.delta_b = (flags & MAMBA_FLAG_DELTA_B) ? 1 : 0;
+  p.vec = L % 8 == 0;
+  for (const void* ptr : {x, delta, z, Bt, Ct, (const void*)y})
+    if (ptr && !aligned(ptr, 16)) p.vec = 0;
+  const Dt out = out_dtype == MAMBA_BF16 ? Dt::BF16 : Dt::F32;
+  return mamba::launch_ssd(p, out, stream) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
+}
+
 int mamba_conv1d_fwd(const void* x, const float* weight, const float* bias, void* y, float* final_state,
                      int64_t B, int64_t D, int64_t L, int64_t K, mamba_dtype_t in_dtype,
                      mamba_dtype_t out_dtype, int return_final_state, hipStream_t stream) {

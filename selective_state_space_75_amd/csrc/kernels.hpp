@@ -98,6 +98,17 @@ struct BwdParams {
   int vec;      // L even and every (B, D, L) / (B, N, L) array 8-byte aligned
 };
 
+// Mamba-2 (SSD) layer forward: H heads of P channels, one scalar A per head.
+struct SsdParams {
+  const void *x, *delta, *z, *Bt, *Ct;          // bf16: x, z (B, H P, L); delta (B, H, L); Bt, Ct (B, N, L)
+  const float *A, *Dskip, *bias;                // (H), (H P), (H)
+  void* y;                                      // (B, H P, L) out dtype
+  float* final_state;                           // (B, H P, N) or null
+  int64_t B, H, P, N, L;
+  int delta_b;
+  int vec;      // L % 8 == 0 and every pointer 16-byte aligned
+};
+
 // Each returns hipSuccess or the launch error.
 hipError_t launch_scan_full(const ScanParams& p, Dt in, Dt out, hipStream_t s);
 hipError_t launch_scan_summary(const ScanParams& p, Dt in, hipStream_t s);
@@ -107,5 +118,6 @@ hipError_t launch_state_update(const UpdateParams& p, Dt in, Dt out, hipStream_t
 hipError_t launch_scan_bwd(const BwdParams& p, Dt in, Dt grad, hipStream_t s);
 hipError_t launch_conv1d_fwd(const ConvParams& p, Dt in, Dt out, bool vec, hipStream_t s);
 hipError_t launch_conv1d_update(const ConvParams& p, Dt in, Dt out, hipStream_t s);
+hipError_t launch_ssd(const SsdParams& p, Dt out, hipStream_t s);
 
 }  // namespace mamba

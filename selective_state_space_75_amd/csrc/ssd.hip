@@ -1,0 +1,364 @@
+// ssd.hip -- Mamba-2 layer (state space duality) forward for gfx950, with the
+// products inside each chunk on the matrix cores.
+//
+// What it computes ("Mamba 与状态空间模型" section 09; "Mamba 状态空间模型架构深度解析",
+// Mamba-2): A is a scalar times the identity, one A_h and one step size per
+// head of P channels.  With delta_t = softplus(delta_raw_t + bias_h),
+// coef_t = (exp(delta_t A_h) - 1) / A_h (or delta_t under the simplified rule)
+// and cum_t = A_h sum_(r <= t) delta_r, each channel's output is
+//   y_t = sum_(s <= t) (C_t . B_s) exp(cum_t - cum_s) coef_s x_s + D x_t,
+// times silu(z_t) when z is given: the lower-triangular matrix of section 09,
+// C like a query, B like a key, x like the values, no softmax.
+//
+// Chunked as section 09 describes (matrix products inside a chunk, only the
+// state passed between chunks).  For a chunk of Q = 32 steps from t0, with the
+// entering state H (N x P) and cum counted from t0:
+//   S = C B^T (Q x Q);  G = S o exp(cum_t - cum_s) coef_s [s <= t]
+//   y = G x + exp(cum_t) (C H) + D x
+//   H <- exp(cum_last) H + B^T (w o x),  w_s = exp(cum_last - cum_s) coef_s
+// Every product is v_mfma_f32_16x16x32_bf16.  x, B and C are bf16 inputs and
+// exact operands; the fp32 intermediates G, w o x and H are each split into a
+// bf16 high part and a bf16 remainder that are multiplied separately, which
+// keeps about 16 significant bits per operand; all sums are fp32.
+//
+// One workgroup (4 waves) per (batch row, head, 64-channel block).  Wave w owns
+// channels 16 w .. 16 w + 15 of the block and their whole N x 16 state, held in
+// MFMA accumulators across chunks; the accumulator layout is exactly the B
+// operand layout of the C H product, so the state never goes through LDS.
+#include "device_math.hpp"
+#include "kernels.hpp"
+
+namespace mamba {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kQ = 32;     // steps per chunk
+constexpr int kP = 64;     // channels per workgroup
+constexpr int kPad = 8;    // bf16 of padding per LDS row (16 bytes): conflict-free operand reads
+
+template <int kN>
+struct SsdLds {
+  uint16_t Cc[kQ][kN + kPad];     // C_t   [step][state]
+  uint16_t Bc[kQ][kN + kPad];     // B_t   [step][state]
+  uint16_t BcT[kN][kQ + kPad];    // B_t   [state][step]
+  uint16_t X[kP][kQ + kPad];      // x     [channel][step]
+  uint16_t Xh[kP][kQ + kPad];     // w o x [channel][step], high part
+  uint16_t Xl[kP][kQ + kPad];     //                        remainder
+  uint16_t Gh[kQ][kQ + kPad];     // G     [t][s], high part
+  uint16_t Gl[kQ][kQ + kPad];     //               remainder
+  float cum[kQ];                  // A sum_(t0 <= r <= t) delta_r
+  float coef[kQ];
+  float ecum[kQ];                 // exp(cum_t)
+  float wl[kQ];                   // exp(cum_last - cum_s) coef_s
+  float elast;                    // exp(cum_last)
+};
+
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// 8 consecutive bf16 from LDS (16-byte aligned)
+__device__ __forceinline__ bf16x8 lds8(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+}
+// 4 + 4 bf16 from two 8-byte aligned LDS addresses
+__device__ __forceinline__ bf16x8 lds4x2(const uint16_t* p, const uint16_t* q) {
+  const uint2 a = *reinterpret_cast<const uint2*>(p), b = *reinterpret_cast<const uint2*>(q);
+  return __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
+}
+
+// fp32 -> bf16 high part and bf16 remainder (both round-to-nearest-even)
+__device__ __forceinline__ void split_bf16(float v, uint16_t& hi, uint16_t& lo) {
+  hi = f32_to_bf16(v);
+  lo = f32_to_bf16(v - bf16_to_f32(hi));
+}
+
+// Four consecutive bf16 of a row: one 8-byte load when `vec`, else element
+// loads with zeros from index `valid` on.
+__device__ __forceinline__ uint2 ld_row4(const uint16_t* row, int64_t t, bool vec, int64_t valid) {
+  if (vec) return *reinterpret_cast<const uint2*>(row + t);
+  uint32_t h[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) h[j] = (j < valid) ? (uint32_t)row[t + j] : 0u;
+  return make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+}
+
+template <int kN, bool kOutBF16, bool kDeltaB>
+__global__ __launch_bounds__(256) void ssd_chunk_kernel(SsdParams p) {
+  __shared__ SsdLds<kN> S;
+  constexpr int kNT = kN / 16;     // 16-row tiles of the state
+  constexpr int kNK = kN / 32;     // 32-wide K blocks over the states
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, l = tid & 63;
+  const int g = l >> 4, r = l & 15;
+  const int64_t pblocks = p.P / kP;
+  const int64_t wg = blockIdx.x;
+  const int64_t b = wg / (p.H * pblocks);
+  const int64_t rest = wg - b * p.H * pblocks;
+  const int64_t h = rest / pblocks;
+  const int64_t d0 = h * p.P + (rest - h * pblocks) * kP;   // first channel of the block
+  const int64_t L = p.L, D = p.H * p.P, N = p.N;
+  const float a = p.A[h];
+  const float a2 = a * kLog2e;
+  const float ia = 1.0f / a;
+  const float bias = p.bias ? p.bias[h] : 0.0f;
+  const bool vecp = p.vec != 0;
+
+  // staging roles: (nq, tb4) = 4 states x 4 steps of B_t / C_t; (px, tb8) = 8 steps of one channel of x
+  const int nq = tid >> 3, tb4 = tid & 7;
+  const int px = tid >> 2, tb8 = tid & 3;
+  // output role: channel 16 w + r, steps 16 tm + 4 g .. + 3 (tm = 0, 1)
+  const int pc = 16 * w + r;
+  const float Dp = p.Dskip ? p.Dskip[d0 + pc] : 0.0f;
+  const uint16_t* xrow = static_cast<const uint16_t*>(p.x) + (b * D + d0 + px) * L;
+  const uint16_t* zrow = p.z ? static_cast<const uint16_t*>(p.z) + (b * D + d0 + pc) * L : nullptr;
+  const uint16_t* dtrow = static_cast<const uint16_t*>(p.delta) + (b * p.H + h) * L;
+  const uint16_t* Brow = static_cast<const uint16_t*>(p.Bt) + b * N * L;
+  const uint16_t* Crow = static_cast<const uint16_t*>(p.Ct) + b * N * L;
+
+  // the upper off-diagonal 16 x 16 block of G is zero in every chunk
+  for (int i = tid; i < 16 * 16; i += 256) {
+    S.Gh[i >> 4][16 + (i & 15)] = 0;
+    S.Gl[i >> 4][16 + (i & 15)] = 0;
+  }
+
+  struct Raw {
+    uint2 c[4], bb[4];   // states 4 nq + j, steps 4 tb4 .. + 3
+    uint4 x;             // channel px, steps 8 tb8 .. + 7
+    uint2 z[2];          // channel pc, steps 16 tm + 4 g .. + 3
+    uint32_t dt;         // step l of the chunk (wave 3, lanes < 32)
+  };
+  auto fetch = [&](int64_t t0, Raw& R) {
+    const int64_t valid = L - t0;
+    const bool vec = vecp && valid >= kQ;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t n = 4 * nq + j;
+      const bool ok = n < N;
+      const int64_t off = (ok ? n : 0) * L + t0;
+      R.c[j] = ok ? ld_row4(Crow + off, 4 * tb4, vec, valid - 4 * tb4) : make_uint2(0u, 0u);
+      R.bb[j] = ok ? ld_row4(Brow + off, 4 * tb4, vec, valid - 4 * tb4) : make_uint2(0u, 0u);
+    }
+    if (vec) {
+      R.x = *reinterpret_cast<const uint4*>(xrow + t0 + 8 * tb8);
+    } else {
+      const uint2 lo = ld_row4(xrow + t0, 8 * tb8, false, valid - 8 * tb8);
+      const uint2 hi = ld_row4(xrow + t0, 8 * tb8 + 4, false, valid - 8 * tb8 - 4);
+      R.x = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    }
+#pragma unroll
+    for (int tm = 0; tm < 2; ++tm)
+      R.z[tm] = zrow ? ld_row4(zrow + t0, 16 * tm + 4 * g, vec, valid - 16 * tm - 4 * g) : make_uint2(0u, 0u);
+    R.dt = (w == 3 && l < valid && l < kQ) ? (uint32_t)dtrow[t0 + l] : 0u;
+  };
+  auto stage = [&](const Raw& R) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = 4 * nq + j;
+      if (n < kN) {
+        *reinterpret_cast<uint2*>(&S.BcT[n][4 * tb4]) = R.bb[j];
+      }
+    }
+    // transpose 4 states x 4 steps into [step][state]
+    const uint32_t c16[4][2] = {{R.c[0].x, R.c[0].y}, {R.c[1].x, R.c[1].y}, {R.c[2].x, R.c[2].y}, {R.c[3].x, R.c[3].y}};
+    const uint32_t b16[4][2] = {{R.bb[0].x, R.bb[0].y}, {R.bb[1].x, R.bb[1].y}, {R.bb[2].x, R.bb[2].y},
+                                {R.bb[3].x, R.bb[3].y}};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      auto el = [&](const uint32_t (&m)[4][2], int j) -> uint32_t {
+        const uint32_t word = m[j][s >> 1];
+        return (s & 1) ? (word >> 16) : (word & 0xffffu);
+      };
+      const uint2 cv = make_uint2(el(c16, 0) | (el(c16, 1) << 16), el(c16, 2) | (el(c16, 3) << 16));
+      const uint2 bv = make_uint2(el(b16, 0) | (el(b16, 1) << 16), el(b16, 2) | (el(b16, 3) << 16));
+      if (4 * nq < kN) {
+        *reinterpret_cast<uint2*>(&S.Cc[4 * tb4 + s][4 * nq]) = cv;
+        *reinterpret_cast<uint2*>(&S.Bc[4 * tb4 + s][4 * nq]) = bv;
+      }
+    }
+    *reinterpret_cast<uint4*>(&S.X[px][8 * tb8]) = R.x;
+  };
+
+  f32x4 Hs[kNT];
+#pragma unroll
+  for (int i = 0; i < kNT; ++i) Hs[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int64_t nchunks = (L + kQ - 1) / kQ;
+  Raw cur, nxt;
+  fetch(0, cur);
+  for (int64_t c = 0; c < nchunks; ++c) {
+    const int64_t t0 = c * kQ;
+    const int64_t valid = L - t0;
+    __syncthreads();                       // the previous chunk's LDS reads are done
+    stage(cur);
+    const uint2 zc[2] = {cur.z[0], cur.z[1]};
+    const uint32_t dtc = cur.dt;
+    __syncthreads();
+    if (c + 1 < nchunks) fetch(t0 + kQ, nxt);
+
+    // ---- S = C B^T on the three lower 16 x 16 tiles (waves 0..2); the step
+    // sizes, decays and coefficients of the chunk (wave 3)
+    f32x4 St = {0.0f, 0.0f, 0.0f, 0.0f};
+    const int tm1 = (w == 0) ? 0 : 1, tn1 = (w == 2) ? 1 : 0;
+    if (w < 3) {
+#pragma unroll
+      for (int kb = 0; kb < kNK; ++kb)
+        St = mfma(lds8(&S.Cc[16 * tm1 + r][32 * kb + 8 * g]), lds8(&S.Bc[16 * tn1 + r][32 * kb + 8 * g]), St);
+    } else {
+      float dl = 0.0f, cf = 0.0f;
+      if (l < valid && l < kQ) {
+        dl = softplus(bf16_to_f32((uint16_t)dtc) + bias);
+        cf = kDeltaB ? dl : expm1_from_exp2(dl * a2, hw_exp2(dl * a2)) * ia;
+      }
+      float v = dl * a;
+#pragma unroll
+      for (int off = 1; off < kQ; off <<= 1) {
+        const float o = __shfl_up(v, off, 64);
+        if (l >= off) v += o;
+      }
+      const float last = __shfl(v, kQ - 1, 64);
+      if (l < kQ) {
+        S.cum[l] = v;
+        S.coef[l] = cf;
+        S.ecum[l] = hw_exp2(v * kLog2e);
+        S.wl[l] = hw_exp2((last - v) * kLog2e) * cf;
+      }
+      if (l == 0) S.elast = hw_exp2(last * kLog2e);
+    }
+    __syncthreads();
+
+    // ---- G from S (waves 0..2); w o x for the wave's own channels; H split
+    if (w < 3) {
+      const int s = 16 * tn1 + r;
+      const float cs = S.cum[s], fs = S.coef[s];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * tm1 + 4 * g + e;
+        const float gv = (s <= t) ? St[e] * hw_exp2((S.cum[t] - cs) * kLog2e) * fs : 0.0f;
+        split_bf16(gv, S.Gh[t][s], S.Gl[t][s]);
+      }
+    }
+    {
+      const uint32_t xw[4] = {cur.x.x, cur.x.y, cur.x.z, cur.x.w};
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint16_t h0, l0, h1, l1;
+        split_bf16(bf16_lo(xw[j]) * S.wl[8 * tb8 + 2 * j], h0, l0);
+        split_bf16(bf16_hi(xw[j]) * S.wl[8 * tb8 + 2 * j + 1], h1, l1);
+        hw[j] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        lw[j] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+      }
+      *reinterpret_cast<uint4*>(&S.Xh[px][8 * tb8]) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      *reinterpret_cast<uint4*>(&S.Xl[px][8 * tb8]) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+    }
+    // the entering state as B operands of C H: K block kb holds states
+    // 32 kb + 4 g + e (tile 2 kb) and 32 kb + 16 + 4 g + e (tile 2 kb + 1)
+    bf16x8 Hh[kNK], Hl[kNK];
+#pragma unroll
+    for (int kb = 0; kb < kNK; ++kb) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = (e < 4) ? Hs[2 * kb][e] : Hs[2 * kb + 1][e - 4];
+        uint16_t hi, lo;
+        split_bf16(v, hi, lo);
+        Hh[kb][e] = __builtin_bit_cast(__bf16, hi);
+        Hl[kb][e] = __builtin_bit_cast(__bf16, lo);
+      }
+    }
+    __syncthreads();
+
+    // ---- y = G x + exp(cum_t) C H + D x for the wave's 16 channels
+    f32x4 Yd[2], Yo[2];
+#pragma unroll
+    for (int tm = 0; tm < 2; ++tm) {
+      const bf16x8 xb = lds8(&S.X[pc][8 * g]);
+      Yd[tm] = mfma(lds8(&S.Gh[16 * tm + r][8 * g]), xb, f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+      Yd[tm] = mfma(lds8(&S.Gl[16 * tm + r][8 * g]), xb, Yd[tm]);
+      Yo[tm] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kb = 0; kb < kNK; ++kb) {
+        const bf16x8 ca = lds4x2(&S.Cc[16 * tm + r][32 * kb + 4 * g], &S.Cc[16 * tm + r][32 * kb + 16 + 4 * g]);
+        Yo[tm] = mfma(ca, Hh[kb], Yo[tm]);
+        Yo[tm] = mfma(ca, Hl[kb], Yo[tm]);
+      }
+    }
+    // ---- H <- exp(cum_last) H + B^T (w o x)
+    {
+      const float el = S.elast;
+      const bf16x8 xh = lds8(&S.Xh[pc][8 * g]), xl = lds8(&S.Xl[pc][8 * g]);
+#pragma unroll
+      for (int tn = 0; tn < kNT; ++tn) {
+        Hs[tn] *= el;
+        const bf16x8 bt = lds8(&S.BcT[16 * tn + r][8 * g]);
+        Hs[tn] = mfma(bt, xh, Hs[tn]);
+        Hs[tn] = mfma(bt, xl, Hs[tn]);
+      }
+    }
+    // ---- gate and store: lane holds steps 16 tm + 4 g + e of channel pc
+#pragma unroll
+    for (int tm = 0; tm < 2; ++tm) {
+      const int tb = 16 * tm + 4 * g;
+      const uint2 xv = *reinterpret_cast<const uint2*>(&S.X[pc][tb]);
+      const float xs[4] = {bf16_lo(xv.x), bf16_hi(xv.x), bf16_lo(xv.y), bf16_hi(xv.y)};
+      const float zs[4] = {bf16_lo(zc[tm].x), bf16_hi(zc[tm].x), bf16_lo(zc[tm].y), bf16_hi(zc[tm].y)};
+      float yv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float v = __builtin_fmaf(S.ecum[tb + e], Yo[tm][e], Yd[tm][e]);
+        v = __builtin_fmaf(Dp, xs[e], v);
+        if (zrow) v *= silu(zs[e]);
+        yv[e] = v;
+      }
+      const int64_t o = (b * D + d0 + pc) * L + t0 + tb;
+      const int64_t nv = valid - tb;
+      if (kOutBF16) {
+        uint16_t* yp = static_cast<uint16_t*>(p.y) + o;
+        if (vecp && nv >= 4) {
+          *reinterpret_cast<uint2*>(yp) = make_uint2(pack_bf16x2(yv[0], yv[1]), pack_bf16x2(yv[2], yv[3]));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (e < nv) yp[e] = f32_to_bf16(yv[e]);
+        }
+      } else {
+        float* yp = static_cast<float*>(p.y) + o;
+        if (vecp && nv >= 4) {
+          *reinterpret_cast<float4*>(yp) = make_float4(yv[0], yv[1], yv[2], yv[3]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (e < nv) yp[e] = yv[e];
+        }
+      }
+    }
+    if (c + 1 < nchunks) cur = nxt;
+  }
+  if (p.final_state) {
+    float* fs = p.final_state + (b * D + d0 + pc) * N;
+#pragma unroll
+    for (int tn = 0; tn < kNT; ++tn)
+      *reinterpret_cast<float4*>(fs + 16 * tn + 4 * g) = make_float4(Hs[tn][0], Hs[tn][1], Hs[tn][2], Hs[tn][3]);
+  }
+}
+
+template <int kN, bool kOutBF16>
+hipError_t ssd_t(const SsdParams& p, hipStream_t s) {
+  const dim3 grid((unsigned)(p.B * p.H * (p.P / kP)));
+  if (p.delta_b)
+    hipLaunchKernelGGL((ssd_chunk_kernel<kN, kOutBF16, true>), grid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((ssd_chunk_kernel<kN, kOutBF16, false>), grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_ssd(const SsdParams& p, Dt out, hipStream_t s) {
+  if (p.N == 128) return out == Dt::BF16 ? ssd_t<128, true>(p, s) : ssd_t<128, false>(p, s);
+  return out == Dt::BF16 ? ssd_t<64, true>(p, s) : ssd_t<64, false>(p, s);
+}
+
+}  // namespace mamba

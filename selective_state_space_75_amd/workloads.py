@@ -36,6 +36,7 @@ BLOCK = 1 << 22
 # Array ids used in the seed tree (kept fixed: changing them changes every input).
 _ID_PARAMS, _ID_DELTA, _ID_U, _ID_Z, _ID_B, _ID_C, _ID_STATE = range(7)
 _ID_CONV_X, _ID_CONV_PARAMS, _ID_CONV_STATE = range(7, 10)
+_ID_SSD_PARAMS, _ID_SSD_X, _ID_SSD_DT, _ID_SSD_Z, _ID_SSD_B, _ID_SSD_C = range(10, 16)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -282,3 +283,63 @@ def conv_update_step(cfg: ConvUpdateConfig, layer: int, step: int) -> np.ndarray
     """x (B, D) bf16 bit patterns of one layer at one step."""
     x = _normal_f32([cfg.seed, layer, step, _ID_CONV_X], cfg.B * cfg.D).reshape(cfg.B, cfg.D)
     return f32_to_bf16_bits(x)
+
+
+# ----------------------------------------------------------------------------- Mamba-2 (SSD)
+@dataclasses.dataclass(frozen=True)
+class SsdConfig:
+    """Mamba-2 layer: H heads of P channels (D = H P), one scalar A and one step
+    size per head, N states per channel shared B_t / C_t ("Mamba 与状态空间模型"
+    section 09: N = 128 in the released models)."""
+    name: str
+    B: int
+    H: int
+    P: int
+    N: int
+    L: int
+    seed: int
+    gate: bool
+
+    @property
+    def D(self) -> int:
+        return self.H * self.P
+
+    @property
+    def elements(self) -> int:
+        return self.B * self.D * self.L
+
+    def algorithmic_bytes(self, out_bytes: int = 2) -> int:
+        """x (and z) read, y written, delta (B, H, L) and B_t / C_t read, all bf16;
+        A, delta bias per head and D per channel read."""
+        per = 2 * (2 if self.gate else 1) + out_bytes
+        return (self.elements * per + self.B * self.H * self.L * 2 + 2 * self.B * self.N * self.L * 2
+                + self.H * 2 * 4 + self.D * 4)
+
+
+# The 2.8B-layer channel count (D = 5,120) cut into 80 heads of 64 channels,
+# N = 128, batch 4, 2,048 tokens, gated.
+SSD_CONFIGS = {
+    "ssd_2.7b_layer": SsdConfig("ssd_2.7b_layer", 4, 80, 64, 128, 2048, 1007, True),
+}
+
+
+def ssd_inputs(B: int, H: int, P: int, N: int, L: int, seed: int, gate: bool = True) -> dict:
+    """x, z (B, H P, L), delta_raw (B, H, L), B_t, C_t (B, N, L) ~ N(0, 1) as bf16 bit
+    patterns; per head dt ~ log-uniform[1e-3, 1e-1] with delta_bias = log(expm1(dt))
+    and A = -U[1, 16]; Dskip (H P) ~ N(0, 1); all fp32."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, _ID_SSD_PARAMS])))
+    dt = np.exp(g.uniform(np.log(1e-3), np.log(1e-1), size=H))
+    delta_bias = np.log(np.expm1(dt)).astype(np.float32)
+    A = (-g.uniform(1.0, 16.0, size=H)).astype(np.float32)
+    Dskip = g.standard_normal(H * P).astype(np.float32)
+    D = H * P
+    big, bc = (B, D, L), (B, N, L)
+    out = {
+        "A": A, "Dskip": Dskip, "delta_bias": delta_bias, "dt": dt,
+        "x": f32_to_bf16_bits(_normal_f32([seed, _ID_SSD_X], B * D * L)).reshape(big),
+        "delta_raw": f32_to_bf16_bits(_normal_f32([seed, _ID_SSD_DT], B * H * L)).reshape(B, H, L),
+        "Bt": f32_to_bf16_bits(_normal_f32([seed, _ID_SSD_B], B * N * L)).reshape(bc),
+        "Ct": f32_to_bf16_bits(_normal_f32([seed, _ID_SSD_C], B * N * L)).reshape(bc),
+        "z": f32_to_bf16_bits(_normal_f32([seed, _ID_SSD_Z], B * D * L)).reshape(big) if gate else None,
+    }
+    return out

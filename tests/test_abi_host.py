@@ -29,7 +29,8 @@ def declared_functions():
 def test_header_symbols_are_exported():
     names = declared_functions()
     assert names == ["mamba_conv1d_fwd", "mamba_conv1d_update", "mamba_scan_bwd", "mamba_scan_bwd_workspace_size",
-                     "mamba_scan_fwd", "mamba_scan_workspace_size", "mamba_state_update", "mamba_status_string"]
+                     "mamba_scan_fwd", "mamba_scan_workspace_size", "mamba_ssd_fwd", "mamba_state_update",
+                     "mamba_status_string"]
     L = _lib.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -216,3 +217,27 @@ def bwd(**kw):
 ])
 def test_bwd_rejects_bad_arguments(kw, code):
     assert bwd(**kw) == code
+
+
+def ssd(**kw):
+    a = dict(x=P, delta=P, z=P, Bt=P, Ct=P, A=P, Dskip=P, bias=P, y=P, fs=P, B=2, H=4, Pd=64, N=128, L=64,
+             ind=BF16, outd=BF16, rfs=1, flags=0)
+    a.update(kw)
+    vp = lambda v: ctypes.c_void_p(v) if v is not None else None  # noqa: E731
+    return _lib.lib().mamba_ssd_fwd(vp(a["x"]), vp(a["delta"]), vp(a["z"]), vp(a["Bt"]), vp(a["Ct"]), vp(a["A"]),
+                                    vp(a["Dskip"]), vp(a["bias"]), vp(a["y"]), vp(a["fs"]), a["B"], a["H"], a["Pd"],
+                                    a["N"], a["L"], a["ind"], a["outd"], a["rfs"], a["flags"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ind=4), DTYPE), (dict(outd=3), DTYPE), (dict(flags=0x2), UNSUP), (dict(flags=0x10), UNSUP),
+    (dict(B=0), SHAPE), (dict(H=0), SHAPE), (dict(Pd=0), SHAPE), (dict(L=0), SHAPE), (dict(N=0), SHAPE),
+    (dict(B=1 << 20, H=1 << 20, L=1 << 20), SHAPE),
+    (dict(ind=F32), UNSUP), (dict(N=16), UNSUP), (dict(N=96), UNSUP), (dict(Pd=32), UNSUP), (dict(Pd=96), UNSUP),
+    (dict(x=None), NULL), (dict(delta=None), NULL), (dict(Bt=None), NULL), (dict(Ct=None), NULL),
+    (dict(A=None), NULL), (dict(y=None), NULL), (dict(fs=None), NULL),
+    (dict(x=P + 1), ALIGN), (dict(Ct=P + 1), ALIGN), (dict(outd=F32, y=P + 2), ALIGN), (dict(A=P + 2), ALIGN),
+    (dict(fs=P + 2), ALIGN), (dict(Dskip=P + 1), ALIGN),
+])
+def test_ssd_rejects_bad_arguments(kw, code):
+    assert ssd(**kw) == code

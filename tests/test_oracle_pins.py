@@ -518,3 +518,67 @@ def test_bwd_gate_factor_and_linearity_in_dy():
     gn = oracle.scan_bwd(*nz, w1 * np_silu(p["z"]))
     for k in ("du", "ddelta_raw", "dBt", "dCt", "dA", "dDskip", "ddelta_bias"):
         assert rel(gn[k], g1[k]) < 1e-12
+
+
+# ----------------------------------------------------------------------------- Mamba-2 (SSD)
+# "Mamba 与状态空间模型" section 09: with A a scalar times the identity, the
+# layer is multiplication by a lower-triangular matrix whose (i, j) entry is
+# C at step i times B at step j times all the decay between the two steps; the
+# input plays the part of the values.  Written out here by brute force, per
+# head, from that description alone.
+def _ssd_matrix_form(x, dr, z, Bt, Ct, Ah, Dskip, bias, P, disc):
+    B, D, L = x.shape
+    H = D // P
+    y = np.zeros((B, D, L))
+    for b in range(B):
+        for h in range(H):
+            dl = np.array([np_softplus(dr[b, h, t] + bias[h]) for t in range(L)])
+            a = Ah[h]
+            coef = dl if disc == "delta_b" else np.expm1(dl * a) / a
+            M = np.zeros((L, L))
+            for i in range(L):
+                for j in range(i + 1):
+                    decay = np.exp(a * np.sum(dl[j + 1:i + 1]))
+                    M[i, j] = np.dot(Ct[b, :, i], Bt[b, :, j]) * decay * coef[j]
+            for p in range(P):
+                d = h * P + p
+                yc = M @ x[b, d] + Dskip[d] * x[b, d]
+                y[b, d] = yc * np_silu(z[b, d]) if z is not None else yc
+    return y
+
+
+@pytest.mark.parametrize("disc,gate", [("zoh", True), ("zoh", False), ("delta_b", True)])
+def test_ssd_equals_lower_triangular_matrix_form(disc, gate):
+    rng = np.random.default_rng(600)
+    B, H, P, N, L = 2, 3, 2, 5, 11
+    x = rng.standard_normal((B, H * P, L))
+    dr = rng.standard_normal((B, H, L))
+    z = rng.standard_normal((B, H * P, L)) if gate else None
+    Bt = rng.standard_normal((B, N, L))
+    Ct = rng.standard_normal((B, N, L))
+    Ah = -rng.uniform(0.5, 4.0, H)
+    Dskip = rng.standard_normal(H * P)
+    bias = rng.standard_normal(H)
+    y, _ = oracle.ssd_scan(x, dr, z, Bt, Ct, Ah, Dskip, bias, P=P, discretization=disc)
+    ref = _ssd_matrix_form(x, dr, z, Bt, Ct, Ah, Dskip, bias, P, disc)
+    assert rel(y, ref) < 1e-12
+
+
+def test_ssd_final_state_is_decayed_sum():
+    """The state after L steps is sum_j (decay j -> L-1) coef_j B_j x_j, the
+    last row of the same matrix before C is applied."""
+    rng = np.random.default_rng(610)
+    B, H, P, N, L = 1, 2, 3, 4, 9
+    x = rng.standard_normal((B, H * P, L))
+    dr = rng.standard_normal((B, H, L))
+    Bt = rng.standard_normal((B, N, L))
+    Ct = rng.standard_normal((B, N, L))
+    Ah = -rng.uniform(0.5, 4.0, H)
+    _, st = oracle.ssd_scan(x, dr, None, Bt, Ct, Ah, None, None, P=P)
+    for h in range(H):
+        dl = np.array([np_softplus(v) for v in dr[0, h]])
+        coef = np.expm1(dl * Ah[h]) / Ah[h]
+        for p in range(P):
+            d = h * P + p
+            ref = sum(np.exp(Ah[h] * np.sum(dl[j + 1:])) * coef[j] * Bt[0, :, j] * x[0, d, j] for j in range(L))
+            assert np.allclose(st[0, d], ref, rtol=1e-12, atol=1e-14)
