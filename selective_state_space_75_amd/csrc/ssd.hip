@@ -48,11 +48,13 @@ struct SsdLds {
   uint16_t Xl[kP][kQ + kPad];     //                        remainder
   uint16_t Gh[kQ][kQ + kPad];     // G     [t][s], high part
   uint16_t Gl[kQ][kQ + kPad];     //               remainder
-  float cum[kQ];                  // A sum_(t0 <= r <= t) delta_r
-  float coef[kQ];
-  float ecum[kQ];                 // exp(cum_t)
-  float wl[kQ];                   // exp(cum_last - cum_s) coef_s
-  float elast;                    // exp(cum_last)
+  // per step of a chunk, double-buffered by chunk parity (the next chunk's
+  // values are computed while the current one runs)
+  float cum[2][kQ];               // A sum_(t0 <= r <= t) delta_r
+  float coef[2][kQ];
+  float ecum[2][kQ];              // exp(cum_t)
+  float wl[2][kQ];                // exp(cum_last - cum_s) coef_s
+  float elast[2];                 // exp(cum_last)
 };
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -128,7 +130,7 @@ __global__ __launch_bounds__(256) void ssd_chunk_kernel(SsdParams p) {
     uint2 c[4], bb[4];   // states 4 nq + j, steps 4 tb4 .. + 3
     uint4 x;             // channel px, steps 8 tb8 .. + 7
     uint2 z[2];          // channel pc, steps 16 tm + 4 g .. + 3
-    uint32_t dt;         // step l of the chunk (wave 3, lanes < 32)
+    uint32_t dt;         // step l of the chunk after this one (wave 3, lanes < 32)
   };
   auto fetch = [&](int64_t t0, Raw& R) {
     const int64_t valid = L - t0;
@@ -151,7 +153,32 @@ __global__ __launch_bounds__(256) void ssd_chunk_kernel(SsdParams p) {
 #pragma unroll
     for (int tm = 0; tm < 2; ++tm)
       R.z[tm] = zrow ? ld_row4(zrow + t0, 16 * tm + 4 * g, vec, valid - 16 * tm - 4 * g) : make_uint2(0u, 0u);
-    R.dt = (w == 3 && l < valid && l < kQ) ? (uint32_t)dtrow[t0 + l] : 0u;
+    const int64_t vnext = valid - kQ;
+    R.dt = (w == 3 && l < vnext && l < kQ) ? (uint32_t)dtrow[t0 + kQ + l] : 0u;
+  };
+  // step sizes, decays and coefficients of the chunk at t0 from its raw delta
+  // (wave 3 only; lane l = step l)
+  auto chunk_params = [&](int64_t t0, uint32_t dtw, int buf) {
+    const int64_t valid = L - t0;
+    float dl = 0.0f, cf = 0.0f;
+    if (l < valid && l < kQ) {
+      dl = softplus(bf16_to_f32((uint16_t)dtw) + bias);
+      cf = kDeltaB ? dl : expm1_from_exp2(dl * a2, hw_exp2(dl * a2)) * ia;
+    }
+    float v = dl * a;
+#pragma unroll
+    for (int off = 1; off < kQ; off <<= 1) {
+      const float o = __shfl_up(v, off, 64);
+      if (l >= off) v += o;
+    }
+    const float last = __shfl(v, kQ - 1, 64);
+    if (l < kQ) {
+      S.cum[buf][l] = v;
+      S.coef[buf][l] = cf;
+      S.ecum[buf][l] = hw_exp2(v * kLog2e);
+      S.wl[buf][l] = hw_exp2((last - v) * kLog2e) * cf;
+    }
+    if (l == 0) S.elast[buf] = hw_exp2(last * kLog2e);
   };
   auto stage = [&](const Raw& R) {
 #pragma unroll
@@ -188,57 +215,36 @@ __global__ __launch_bounds__(256) void ssd_chunk_kernel(SsdParams p) {
   const int64_t nchunks = (L + kQ - 1) / kQ;
   Raw cur, nxt;
   fetch(0, cur);
+  if (w == 3) chunk_params(0, (l < L && l < kQ) ? (uint32_t)dtrow[l] : 0u, 0);
   for (int64_t c = 0; c < nchunks; ++c) {
     const int64_t t0 = c * kQ;
     const int64_t valid = L - t0;
+    const int cb = (int)(c & 1);
     __syncthreads();                       // the previous chunk's LDS reads are done
     stage(cur);
     const uint2 zc[2] = {cur.z[0], cur.z[1]};
-    const uint32_t dtc = cur.dt;
+    const uint32_t dtn = cur.dt;
     __syncthreads();
     if (c + 1 < nchunks) fetch(t0 + kQ, nxt);
 
-    // ---- S = C B^T on the three lower 16 x 16 tiles (waves 0..2); the step
-    // sizes, decays and coefficients of the chunk (wave 3)
-    f32x4 St = {0.0f, 0.0f, 0.0f, 0.0f};
+    // ---- S = C B^T on the three lower 16 x 16 tiles and G from it (waves
+    // 0..2); the next chunk's step sizes, decays and coefficients (wave 3)
     const int tm1 = (w == 0) ? 0 : 1, tn1 = (w == 2) ? 1 : 0;
     if (w < 3) {
+      f32x4 St = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int kb = 0; kb < kNK; ++kb)
         St = mfma(lds8(&S.Cc[16 * tm1 + r][32 * kb + 8 * g]), lds8(&S.Bc[16 * tn1 + r][32 * kb + 8 * g]), St);
-    } else {
-      float dl = 0.0f, cf = 0.0f;
-      if (l < valid && l < kQ) {
-        dl = softplus(bf16_to_f32((uint16_t)dtc) + bias);
-        cf = kDeltaB ? dl : expm1_from_exp2(dl * a2, hw_exp2(dl * a2)) * ia;
-      }
-      float v = dl * a;
-#pragma unroll
-      for (int off = 1; off < kQ; off <<= 1) {
-        const float o = __shfl_up(v, off, 64);
-        if (l >= off) v += o;
-      }
-      const float last = __shfl(v, kQ - 1, 64);
-      if (l < kQ) {
-        S.cum[l] = v;
-        S.coef[l] = cf;
-        S.ecum[l] = hw_exp2(v * kLog2e);
-        S.wl[l] = hw_exp2((last - v) * kLog2e) * cf;
-      }
-      if (l == 0) S.elast = hw_exp2(last * kLog2e);
-    }
-    __syncthreads();
-
-    // ---- G from S (waves 0..2); w o x for the wave's own channels; H split
-    if (w < 3) {
       const int s = 16 * tn1 + r;
-      const float cs = S.cum[s], fs = S.coef[s];
+      const float cs = S.cum[cb][s], fs = S.coef[cb][s];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = 16 * tm1 + 4 * g + e;
-        const float gv = (s <= t) ? St[e] * hw_exp2((S.cum[t] - cs) * kLog2e) * fs : 0.0f;
+        const float gv = (s <= t) ? St[e] * hw_exp2((S.cum[cb][t] - cs) * kLog2e) * fs : 0.0f;
         split_bf16(gv, S.Gh[t][s], S.Gl[t][s]);
       }
+    } else if (c + 1 < nchunks) {
+      chunk_params(t0 + kQ, dtn, cb ^ 1);
     }
     {
       const uint32_t xw[4] = {cur.x.x, cur.x.y, cur.x.z, cur.x.w};
@@ -246,8 +252,8 @@ __global__ __launch_bounds__(256) void ssd_chunk_kernel(SsdParams p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         uint16_t h0, l0, h1, l1;
-        split_bf16(bf16_lo(xw[j]) * S.wl[8 * tb8 + 2 * j], h0, l0);
-        split_bf16(bf16_hi(xw[j]) * S.wl[8 * tb8 + 2 * j + 1], h1, l1);
+        split_bf16(bf16_lo(xw[j]) * S.wl[cb][8 * tb8 + 2 * j], h0, l0);
+        split_bf16(bf16_hi(xw[j]) * S.wl[cb][8 * tb8 + 2 * j + 1], h1, l1);
         hw[j] = (uint32_t)h0 | ((uint32_t)h1 << 16);
         lw[j] = (uint32_t)l0 | ((uint32_t)l1 << 16);
       }
@@ -287,7 +293,7 @@ __global__ __launch_bounds__(256) void ssd_chunk_kernel(SsdParams p) {
     }
     // ---- H <- exp(cum_last) H + B^T (w o x)
     {
-      const float el = S.elast;
+      const float el = S.elast[cb];
       const bf16x8 xh = lds8(&S.Xh[pc][8 * g]), xl = lds8(&S.Xl[pc][8 * g]);
 #pragma unroll
       for (int tn = 0; tn < kNT; ++tn) {
@@ -307,7 +313,7 @@ __global__ __launch_bounds__(256) void ssd_chunk_kernel(SsdParams p) {
       float yv[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float v = __builtin_fmaf(S.ecum[tb + e], Yo[tm][e], Yd[tm][e]);
+        float v = __builtin_fmaf(S.ecum[cb][tb + e], Yo[tm][e], Yd[tm][e]);
         v = __builtin_fmaf(Dp, xs[e], v);
         if (zrow) v *= silu(zs[e]);
         yv[e] = v;
