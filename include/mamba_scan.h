@@ -247,16 +247,27 @@ int mamba_conv1d_update(float* state, const void* x, const float* weight, const 
  *   y           : (B, H*P, L) out_dtype (bf16 or fp32), written.
  *   final_state : (B, H*P, N) fp32, written iff return_final_state.
  *
+ *   workspace   : at least mamba_ssd_workspace_size bytes (may be NULL when
+ *                 that is 0), 256-byte aligned; contents on entry ignored.
+ *
  * in_dtype must be MAMBA_BF16 (MAMBA_ERR_UNSUPPORTED otherwise); N must be 64
  * or 128 and P a multiple of 64 (MAMBA_ERR_UNSUPPORTED).  Alignment: bf16
  * arrays 2-byte, fp32 arrays 4-byte (16-byte pointers and L % 8 == 0 select
- * vector accesses).  No workspace; the initial state is zero.
+ * vector accesses).  The initial state is zero.
  */
 int mamba_ssd_fwd(const void* x, const void* delta, const void* z, const void* Bt, const void* Ct,
                   const float* A, const float* Dskip, const float* delta_bias, void* y, float* final_state,
                   int64_t B, int64_t H, int64_t P, int64_t N, int64_t L,
                   mamba_dtype_t in_dtype, mamba_dtype_t out_dtype, int return_final_state,
-                  unsigned flags, hipStream_t stream);
+                  unsigned flags, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Bytes of device workspace mamba_ssd_fwd needs (shape only; callable without
+ * a GPU): L is cut into segments that run in parallel, and the workspace
+ * holds each segment's fp32 end state (N per channel) and decay.  0 when one
+ * segment suffices; (size_t)-1 for an invalid or unsupported shape.
+ */
+size_t mamba_ssd_workspace_size(int64_t B, int64_t H, int64_t P, int64_t N, int64_t L);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char* mamba_status_string(int status);

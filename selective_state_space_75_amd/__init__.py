@@ -9,9 +9,10 @@ The computation runs in hand-written HIP kernels inside ``libmamba_scan.so``
 ``workloads`` draws the seeded synthetic inputs.
 """
 from ._lib import (FLAG_ACCURATE_EXPM1, FLAG_DELTA_B, MambaError, conv1d_fwd, conv1d_update,  # noqa: F401
-                   lib, scan_bwd, scan_bwd_workspace_size, scan_fwd, ssd_fwd, state_update, status_string,
+                   lib, scan_bwd, scan_bwd_workspace_size, scan_fwd, ssd_fwd, ssd_workspace_size, state_update,
+                   status_string,
                    workspace_size)
 
 __all__ = ["scan_fwd", "scan_bwd", "scan_bwd_workspace_size", "state_update", "conv1d_fwd", "conv1d_update",
-           "ssd_fwd", "workspace_size", "status_string", "lib", "MambaError", "FLAG_DELTA_B",
+           "ssd_fwd", "ssd_workspace_size", "workspace_size", "status_string", "lib", "MambaError", "FLAG_DELTA_B",
            "FLAG_ACCURATE_EXPM1"]

@@ -59,8 +59,10 @@ def lib() -> ctypes.CDLL:
             L.mamba_conv1d_fwd.restype = c_int
             L.mamba_conv1d_update.argtypes = [vp] * 5 + [i64] * 3 + [c_int, c_int, vp]
             L.mamba_conv1d_update.restype = c_int
-            L.mamba_ssd_fwd.argtypes = [vp] * 10 + [i64] * 5 + [c_int, c_int, c_int, u32, vp]
+            L.mamba_ssd_fwd.argtypes = [vp] * 10 + [i64] * 5 + [c_int, c_int, c_int, u32, vp, ctypes.c_size_t, vp]
             L.mamba_ssd_fwd.restype = c_int
+            L.mamba_ssd_workspace_size.argtypes = [i64] * 5
+            L.mamba_ssd_workspace_size.restype = ctypes.c_size_t
             L.mamba_status_string.argtypes = [c_int]
             L.mamba_status_string.restype = ctypes.c_char_p
             _lib = L
@@ -172,8 +174,15 @@ def scan_fwd(u, delta, z, Bt, Ct, A, Dskip=None, delta_bias=None, *, return_fina
     return (y, final_state) if return_final_state else y
 
 
+def ssd_workspace_size(B: int, H: int, P: int, N: int, L: int) -> int:
+    n = lib().mamba_ssd_workspace_size(B, H, P, N, L)
+    if n == ctypes.c_size_t(-1).value:
+        raise MambaError(-5, "mamba_ssd_workspace_size")
+    return n
+
+
 def ssd_fwd(x, delta, z, Bt, Ct, A, Dskip=None, delta_bias=None, *, P=64, return_final_state=False,
-            out_dtype=None, delta_b=False, y=None, final_state=None, stream=None):
+            out_dtype=None, delta_b=False, y=None, final_state=None, workspace=None, stream=None):
     """Mamba-2 (SSD) layer forward.  x, z: (B, H*P, L) bf16; delta: (B, H, L) bf16;
     Bt, Ct: (B, N, L) bf16; A, delta_bias: (H) fp32; Dskip: (H*P) fp32.
 
@@ -208,10 +217,14 @@ def ssd_fwd(x, delta, z, Bt, Ct, A, Dskip=None, delta_bias=None, *, P=64, return
         if final_state is None:
             final_state = torch.empty((B, D, N), dtype=torch.float32, device=dev)
         _check(final_state, "final_state", (B, D, N), torch.float32, dev)
+    ws_bytes = ssd_workspace_size(B, H, P, N, L) if (N in (64, 128) and P % 64 == 0) else 0
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     st = lib().mamba_ssd_fwd(
         _ptr(x), _ptr(delta), _ptr(z), _ptr(Bt), _ptr(Ct), _ptr(A), _ptr(Dskip), _ptr(delta_bias),
         _ptr(y), _ptr(final_state if return_final_state else None), B, H, P, N, L,
         _dtype_code(x), _dtype_code(y), 1 if return_final_state else 0, FLAG_DELTA_B if delta_b else 0,
+        _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
         _stream(dev, stream))
     if st != 0:
         raise MambaError(st, "mamba_ssd_fwd")

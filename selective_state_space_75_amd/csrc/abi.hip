@@ -347,11 +347,63 @@ int mamba_scan_bwd(const void* u, const void* delta, const void* z, const void* 
   return mamba::launch_scan_bwd(p, in, gd, stream) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
 }
 
+}  // extern "C"
+
+namespace {
+
+struct SsdPlan {
+  int64_t S = 1, seg_len = 0;
+  size_t off_h = 0, off_P = 0, bytes = 0;
+};
+
+// Segments of L: only when the (batch row, head, 64-channel block) workgroups
+// are too few to give every CU one (fewer than 256): the extra state-only pass
+// and carry cost more than the added parallelism saves beyond that (measured
+// at B=4, 80 heads: 1 segment 278 us, 2: 336, 4: 302, 8: 322).  Segments of at
+// least 256 steps, lengths a multiple of 32 (the chunk).
+// Test knob: MAMBA_SSD_SEGMENTS=S asks for S segments (still at most one per
+// 32-step chunk).  Read on every call, by the size query and the launch alike.
+SsdPlan make_ssd_plan(int64_t B, int64_t H, int64_t P, int64_t N, int64_t L) {
+  SsdPlan q;
+  const int64_t wgs = B * H * (P / 64);
+  int64_t S = (256 + wgs - 1) / wgs;
+  const int64_t smax = (L + 255) / 256;
+  if (S > smax) S = smax;
+  if (const char* e = getenv("MAMBA_SSD_SEGMENTS")) {
+    char* end = nullptr;
+    const long long v = strtoll(e, &end, 10);
+    if (end && *end == '\0' && v > 0) S = (v < (L + 31) / 32) ? (int64_t)v : (L + 31) / 32;
+  }
+  if (S < 1) S = 1;
+  int64_t len = (L + S - 1) / S;
+  len = (len + 31) / 32 * 32;
+  q.seg_len = len;
+  q.S = (L + len - 1) / len;
+  if (q.S > 1) {
+    const size_t slots = size_t(q.S) * size_t(wgs);   // wgs counts the batch rows
+    size_t o = 0;
+    q.off_h = o; o += align256(slots * 64 * size_t(N) * sizeof(float));
+    q.off_P = o; o += align256(slots * sizeof(float));
+    q.bytes = o;
+  }
+  return q;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mamba_ssd_workspace_size(int64_t B, int64_t H, int64_t P, int64_t N, int64_t L) {
+  if (H < 1 || P < 1 || H > kMaxElems / P || !shape_ok(B, H * P, N, L)) return (size_t)-1;
+  if ((N != 64 && N != 128) || P % 64 != 0) return (size_t)-1;
+  return make_ssd_plan(B, H, P, N, L).bytes;
+}
+
 int mamba_ssd_fwd(const void* x, const void* delta, const void* z, const void* Bt, const void* Ct,
                   const float* A, const float* Dskip, const float* delta_bias, void* y, float* final_state,
                   int64_t B, int64_t H, int64_t P, int64_t N, int64_t L,
                   mamba_dtype_t in_dtype, mamba_dtype_t out_dtype, int return_final_state,
-                  unsigned flags, hipStream_t stream) {
+                  unsigned flags, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return MAMBA_ERR_DTYPE;
   if (flags & ~MAMBA_FLAG_DELTA_B) return MAMBA_ERR_UNSUPPORTED;
   if (H < 1 || P < 1 || H > kMaxElems / P || !shape_ok(B, H * P, N, L)) return MAMBA_ERR_SHAPE;
@@ -363,8 +415,16 @@ int mamba_ssd_fwd(const void* x, const void* delta, const void* z, const void* B
   for (const void* ptr : {(const void*)A, (const void*)Dskip, (const void*)delta_bias,
                           (const void*)(return_final_state ? final_state : nullptr)})
     if (ptr && !aligned(ptr, 4)) return MAMBA_ERR_ALIGN;
-  if (B * H * (P / 64) >= (int64_t(1) << 31)) return MAMBA_ERR_SHAPE;
+  const SsdPlan plan = make_ssd_plan(B, H, P, N, L);
+  if (B * plan.S * H * (P / 64) >= (int64_t(1) << 31)) return MAMBA_ERR_SHAPE;
+  if (plan.bytes && (!workspace || workspace_bytes < plan.bytes)) return MAMBA_ERR_WORKSPACE;
+  if (plan.bytes && !aligned(workspace, 256)) return MAMBA_ERR_ALIGN;
   mamba::SsdParams p{};
+  p.S = plan.S; p.seg_len = plan.seg_len;
+  if (plan.bytes) {
+    p.ws_h = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.off_h);
+    p.ws_P = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.off_P);
+  }
   p.x = x; p.delta = delta; p.z = z; p.Bt = Bt; p.Ct = Ct;
   p.A = A; p.Dskip = Dskip; p.bias = delta_bias;
   p.y = y; p.final_state = return_final_state ? final_state : nullptr;

@@ -104,7 +104,10 @@ struct SsdParams {
   const float *A, *Dskip, *bias;                // (H), (H P), (H)
   void* y;                                      // (B, H P, L) out dtype
   float* final_state;                           // (B, H P, N) or null
+  float* ws_h;                                  // per (b, segment, h, 64-channel block): [64][N] states (S > 1)
+  float* ws_P;                                  // per segment slot: decay over the segment (S > 1)
   int64_t B, H, P, N, L;
+  int64_t S, seg_len;                           // segments of L (multiple of 32 steps)
   int delta_b;
   int vec;      // L % 8 == 0 and every pointer 16-byte aligned
 };

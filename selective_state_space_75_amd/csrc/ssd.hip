@@ -21,10 +21,19 @@
 // bf16 high part and a bf16 remainder that are multiplied separately, which
 // keeps about 16 significant bits per operand; all sums are fp32.
 //
-// One workgroup (4 waves) per (batch row, head, 64-channel block).  Wave w owns
-// channels 16 w .. 16 w + 15 of the block and their whole N x 16 state, held in
-// MFMA accumulators across chunks; the accumulator layout is exactly the B
-// operand layout of the C H product, so the state never goes through LDS.
+// One workgroup (4 waves) per (batch row, segment of L, head, 64-channel
+// block).  Wave w owns channels 16 w .. 16 w + 15 of the block and their whole
+// N x 16 state, held in MFMA accumulators across chunks; the accumulator
+// layout is exactly the B operand layout of the C H product, so the state
+// never goes through LDS.
+//
+// L is cut into segments so that there are enough workgroups to hide latency
+// (a head alone is a chain of dependent chunks).  A first launch runs only the
+// state update over each segment from a zero state and keeps its end state
+// and total decay; a carry kernel chains them into each segment's entering
+// state (the associative combination of "Mamba论文研读笔记" 3.2.3 B over
+// segment aggregates); the full launch then runs every segment from its
+// entering state.
 #include "device_math.hpp"
 #include "kernels.hpp"
 
@@ -87,7 +96,9 @@ __device__ __forceinline__ uint2 ld_row4(const uint16_t* row, int64_t t, bool ve
   return make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
 }
 
-template <int kN, bool kOutBF16, bool kDeltaB>
+// kSummary: the state update only (no C_t, z or output), from a zero state;
+// the segment's end state and total decay go to the workspace.
+template <int kN, bool kOutBF16, bool kDeltaB, bool kSummary>
 __global__ __launch_bounds__(256) void ssd_chunk_kernel(SsdParams p) {
   __shared__ SsdLds<kN> S;
   constexpr int kNT = kN / 16;     // 16-row tiles of the state
@@ -96,11 +107,14 @@ __global__ __launch_bounds__(256) void ssd_chunk_kernel(SsdParams p) {
   const int w = tid >> 6, l = tid & 63;
   const int g = l >> 4, r = l & 15;
   const int64_t pblocks = p.P / kP;
-  const int64_t wg = blockIdx.x;
-  const int64_t b = wg / (p.H * pblocks);
-  const int64_t rest = wg - b * p.H * pblocks;
-  const int64_t h = rest / pblocks;
-  const int64_t d0 = h * p.P + (rest - h * pblocks) * kP;   // first channel of the block
+  const int64_t wg = blockIdx.x;                             // ((b S + seg) H + h) pblocks + pb
+  const int64_t pb = wg % pblocks;
+  const int64_t h = (wg / pblocks) % p.H;
+  const int64_t bs = wg / (pblocks * p.H);
+  const int64_t seg = bs % p.S, b = bs / p.S;
+  const int64_t d0 = h * p.P + pb * kP;                      // first channel of the block
+  const int64_t t_begin = seg * p.seg_len;
+  const int64_t t_end = t_begin + p.seg_len < p.L ? t_begin + p.seg_len : p.L;
   const int64_t L = p.L, D = p.H * p.P, N = p.N;
   const float a = p.A[h];
   const float a2 = a * kLog2e;
@@ -140,7 +154,7 @@ __global__ __launch_bounds__(256) void ssd_chunk_kernel(SsdParams p) {
       const int64_t n = 4 * nq + j;
       const bool ok = n < N;
       const int64_t off = (ok ? n : 0) * L + t0;
-      R.c[j] = ok ? ld_row4(Crow + off, 4 * tb4, vec, valid - 4 * tb4) : make_uint2(0u, 0u);
+      R.c[j] = (!kSummary && ok) ? ld_row4(Crow + off, 4 * tb4, vec, valid - 4 * tb4) : make_uint2(0u, 0u);
       R.bb[j] = ok ? ld_row4(Brow + off, 4 * tb4, vec, valid - 4 * tb4) : make_uint2(0u, 0u);
     }
     if (vec) {
@@ -152,12 +166,14 @@ __global__ __launch_bounds__(256) void ssd_chunk_kernel(SsdParams p) {
     }
 #pragma unroll
     for (int tm = 0; tm < 2; ++tm)
-      R.z[tm] = zrow ? ld_row4(zrow + t0, 16 * tm + 4 * g, vec, valid - 16 * tm - 4 * g) : make_uint2(0u, 0u);
+      R.z[tm] = (!kSummary && zrow) ? ld_row4(zrow + t0, 16 * tm + 4 * g, vec, valid - 16 * tm - 4 * g)
+                                    : make_uint2(0u, 0u);
     const int64_t vnext = valid - kQ;
     R.dt = (w == 3 && l < vnext && l < kQ) ? (uint32_t)dtrow[t0 + kQ + l] : 0u;
   };
   // step sizes, decays and coefficients of the chunk at t0 from its raw delta
   // (wave 3 only; lane l = step l)
+  float seg_log = 0.0f;   // A sum of delta over the segment so far (wave 3)
   auto chunk_params = [&](int64_t t0, uint32_t dtw, int buf) {
     const int64_t valid = L - t0;
     float dl = 0.0f, cf = 0.0f;
@@ -172,6 +188,7 @@ __global__ __launch_bounds__(256) void ssd_chunk_kernel(SsdParams p) {
       if (l >= off) v += o;
     }
     const float last = __shfl(v, kQ - 1, 64);
+    seg_log += last;
     if (l < kQ) {
       S.cum[buf][l] = v;
       S.coef[buf][l] = cf;
@@ -200,7 +217,7 @@ __global__ __launch_bounds__(256) void ssd_chunk_kernel(SsdParams p) {
       };
       const uint2 cv = make_uint2(el(c16, 0) | (el(c16, 1) << 16), el(c16, 2) | (el(c16, 3) << 16));
       const uint2 bv = make_uint2(el(b16, 0) | (el(b16, 1) << 16), el(b16, 2) | (el(b16, 3) << 16));
-      if (4 * nq < kN) {
+      if (!kSummary && 4 * nq < kN) {
         *reinterpret_cast<uint2*>(&S.Cc[4 * tb4 + s][4 * nq]) = cv;
         *reinterpret_cast<uint2*>(&S.Bc[4 * tb4 + s][4 * nq]) = bv;
       }
@@ -208,15 +225,26 @@ __global__ __launch_bounds__(256) void ssd_chunk_kernel(SsdParams p) {
     *reinterpret_cast<uint4*>(&S.X[px][8 * tb8]) = R.x;
   };
 
+  // the segment's state slot in the workspace: [channel][state] fp32
+  const int64_t slot = wg;
   f32x4 Hs[kNT];
+  if (!kSummary && seg > 0) {
+    const float* hin = p.ws_h + (slot * kP + pc) * N;
 #pragma unroll
-  for (int i = 0; i < kNT; ++i) Hs[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int tn = 0; tn < kNT; ++tn) {
+      const float4 v = *reinterpret_cast<const float4*>(hin + 16 * tn + 4 * g);
+      Hs[tn] = f32x4{v.x, v.y, v.z, v.w};
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kNT; ++i) Hs[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
 
-  const int64_t nchunks = (L + kQ - 1) / kQ;
+  const int64_t ck0 = t_begin / kQ, nchunks = (t_end + kQ - 1) / kQ;
   Raw cur, nxt;
-  fetch(0, cur);
-  if (w == 3) chunk_params(0, (l < L && l < kQ) ? (uint32_t)dtrow[l] : 0u, 0);
-  for (int64_t c = 0; c < nchunks; ++c) {
+  fetch(t_begin, cur);
+  if (w == 3) chunk_params(t_begin, (l < L - t_begin && l < kQ) ? (uint32_t)dtrow[t_begin + l] : 0u, (int)(ck0 & 1));
+  for (int64_t c = ck0; c < nchunks; ++c) {
     const int64_t t0 = c * kQ;
     const int64_t valid = L - t0;
     const int cb = (int)(c & 1);
@@ -230,7 +258,7 @@ __global__ __launch_bounds__(256) void ssd_chunk_kernel(SsdParams p) {
     // ---- S = C B^T on the three lower 16 x 16 tiles and G from it (waves
     // 0..2); the next chunk's step sizes, decays and coefficients (wave 3)
     const int tm1 = (w == 0) ? 0 : 1, tn1 = (w == 2) ? 1 : 0;
-    if (w < 3) {
+    if (!kSummary && w < 3) {
       f32x4 St = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int kb = 0; kb < kNK; ++kb)
@@ -243,7 +271,7 @@ __global__ __launch_bounds__(256) void ssd_chunk_kernel(SsdParams p) {
         const float gv = (s <= t) ? St[e] * hw_exp2((S.cum[cb][t] - cs) * kLog2e) * fs : 0.0f;
         split_bf16(gv, S.Gh[t][s], S.Gl[t][s]);
       }
-    } else if (c + 1 < nchunks) {
+    } else if (w == 3 && c + 1 < nchunks) {
       chunk_params(t0 + kQ, dtn, cb ^ 1);
     }
     {
@@ -264,7 +292,7 @@ __global__ __launch_bounds__(256) void ssd_chunk_kernel(SsdParams p) {
     // 32 kb + 4 g + e (tile 2 kb) and 32 kb + 16 + 4 g + e (tile 2 kb + 1)
     bf16x8 Hh[kNK], Hl[kNK];
 #pragma unroll
-    for (int kb = 0; kb < kNK; ++kb) {
+    for (int kb = 0; kb < (kSummary ? 0 : kNK); ++kb) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float v = (e < 4) ? Hs[2 * kb][e] : Hs[2 * kb + 1][e - 4];
@@ -279,7 +307,7 @@ __global__ __launch_bounds__(256) void ssd_chunk_kernel(SsdParams p) {
     // ---- y = G x + exp(cum_t) C H + D x for the wave's 16 channels
     f32x4 Yd[2], Yo[2];
 #pragma unroll
-    for (int tm = 0; tm < 2; ++tm) {
+    for (int tm = 0; tm < (kSummary ? 0 : 2); ++tm) {
       const bf16x8 xb = lds8(&S.X[pc][8 * g]);
       Yd[tm] = mfma(lds8(&S.Gh[16 * tm + r][8 * g]), xb, f32x4{0.0f, 0.0f, 0.0f, 0.0f});
       Yd[tm] = mfma(lds8(&S.Gl[16 * tm + r][8 * g]), xb, Yd[tm]);
@@ -305,7 +333,7 @@ __global__ __launch_bounds__(256) void ssd_chunk_kernel(SsdParams p) {
     }
     // ---- gate and store: lane holds steps 16 tm + 4 g + e of channel pc
 #pragma unroll
-    for (int tm = 0; tm < 2; ++tm) {
+    for (int tm = 0; tm < (kSummary ? 0 : 2); ++tm) {
       const int tb = 16 * tm + 4 * g;
       const uint2 xv = *reinterpret_cast<const uint2*>(&S.X[pc][tb]);
       const float xs[4] = {bf16_lo(xv.x), bf16_hi(xv.x), bf16_lo(xv.y), bf16_hi(xv.y)};
@@ -342,7 +370,13 @@ __global__ __launch_bounds__(256) void ssd_chunk_kernel(SsdParams p) {
     }
     if (c + 1 < nchunks) cur = nxt;
   }
-  if (p.final_state) {
+  if constexpr (kSummary) {
+    float* ho = p.ws_h + (slot * kP + pc) * N;
+#pragma unroll
+    for (int tn = 0; tn < kNT; ++tn)
+      *reinterpret_cast<float4*>(ho + 16 * tn + 4 * g) = make_float4(Hs[tn][0], Hs[tn][1], Hs[tn][2], Hs[tn][3]);
+    if (w == 3 && l == 0) p.ws_P[slot] = hw_exp2(seg_log * kLog2e);
+  } else if (p.final_state && seg == p.S - 1) {
     float* fs = p.final_state + (b * D + d0 + pc) * N;
 #pragma unroll
     for (int tn = 0; tn < kNT; ++tn)
@@ -350,14 +384,44 @@ __global__ __launch_bounds__(256) void ssd_chunk_kernel(SsdParams p) {
   }
 }
 
+// Segment carries, one thread per (batch row, head, channel block, channel,
+// state): the state entering segment s + 1 is P(s) h_in(s) + h_end(s), written
+// over the segment's slot in order.
+__global__ __launch_bounds__(256) void ssd_carry_kernel(SsdParams p) {
+  const int64_t per = p.H * (p.P / kP) * kP * p.N;          // elements per (batch row, segment)
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= p.B * per) return;
+  const int64_t b = i / per, e = i - b * per;                 // e = (h pblocks + pb) kP N + c N + n
+  const int64_t blk = e / (kP * p.N);
+  float hin = 0.0f;
+  for (int64_t s = 0; s < p.S; ++s) {
+    const int64_t slot = (b * p.S + s) * (per / (kP * p.N)) + blk;
+    float* q = p.ws_h + slot * kP * p.N + (e - blk * kP * p.N);
+    const float v = *q;
+    *q = hin;
+    hin = __builtin_fmaf(p.ws_P[slot], hin, v);
+  }
+}
+
+template <int kN, bool kOutBF16, bool kDeltaB>
+hipError_t ssd_d(const SsdParams& p, hipStream_t s) {
+  const dim3 grid((unsigned)(p.B * p.S * p.H * (p.P / kP)));
+  if (p.S > 1) {
+    hipLaunchKernelGGL((ssd_chunk_kernel<kN, kOutBF16, kDeltaB, true>), grid, dim3(256), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t n = p.B * p.H * p.P * p.N;
+    hipLaunchKernelGGL(ssd_carry_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((ssd_chunk_kernel<kN, kOutBF16, kDeltaB, false>), grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
 template <int kN, bool kOutBF16>
 hipError_t ssd_t(const SsdParams& p, hipStream_t s) {
-  const dim3 grid((unsigned)(p.B * p.H * (p.P / kP)));
-  if (p.delta_b)
-    hipLaunchKernelGGL((ssd_chunk_kernel<kN, kOutBF16, true>), grid, dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL((ssd_chunk_kernel<kN, kOutBF16, false>), grid, dim3(256), 0, s, p);
-  return hipGetLastError();
+  return p.delta_b ? ssd_d<kN, kOutBF16, true>(p, s) : ssd_d<kN, kOutBF16, false>(p, s);
 }
 
 }  // namespace

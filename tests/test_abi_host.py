@@ -29,8 +29,8 @@ def declared_functions():
 def test_header_symbols_are_exported():
     names = declared_functions()
     assert names == ["mamba_conv1d_fwd", "mamba_conv1d_update", "mamba_scan_bwd", "mamba_scan_bwd_workspace_size",
-                     "mamba_scan_fwd", "mamba_scan_workspace_size", "mamba_ssd_fwd", "mamba_state_update",
-                     "mamba_status_string"]
+                     "mamba_scan_fwd", "mamba_scan_workspace_size", "mamba_ssd_fwd", "mamba_ssd_workspace_size",
+                     "mamba_state_update", "mamba_status_string"]
     L = _lib.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -221,12 +221,13 @@ def test_bwd_rejects_bad_arguments(kw, code):
 
 def ssd(**kw):
     a = dict(x=P, delta=P, z=P, Bt=P, Ct=P, A=P, Dskip=P, bias=P, y=P, fs=P, B=2, H=4, Pd=64, N=128, L=64,
-             ind=BF16, outd=BF16, rfs=1, flags=0)
+             ind=BF16, outd=BF16, rfs=1, flags=0, ws=None, wsb=0)
     a.update(kw)
     vp = lambda v: ctypes.c_void_p(v) if v is not None else None  # noqa: E731
     return _lib.lib().mamba_ssd_fwd(vp(a["x"]), vp(a["delta"]), vp(a["z"]), vp(a["Bt"]), vp(a["Ct"]), vp(a["A"]),
                                     vp(a["Dskip"]), vp(a["bias"]), vp(a["y"]), vp(a["fs"]), a["B"], a["H"], a["Pd"],
-                                    a["N"], a["L"], a["ind"], a["outd"], a["rfs"], a["flags"], None)
+                                    a["N"], a["L"], a["ind"], a["outd"], a["rfs"], a["flags"], vp(a["ws"]), a["wsb"],
+                                    None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -238,6 +239,23 @@ def ssd(**kw):
     (dict(A=None), NULL), (dict(y=None), NULL), (dict(fs=None), NULL),
     (dict(x=P + 1), ALIGN), (dict(Ct=P + 1), ALIGN), (dict(outd=F32, y=P + 2), ALIGN), (dict(A=P + 2), ALIGN),
     (dict(fs=P + 2), ALIGN), (dict(Dskip=P + 1), ALIGN),
+    # long enough to be cut into segments: a workspace is needed
+    (dict(B=1, H=2, L=4096), WS), (dict(B=1, H=2, L=4096, ws=P, wsb=64), WS),
+    (dict(B=1, H=2, L=4096, ws=P + 16, wsb=1 << 40), ALIGN),
 ])
 def test_ssd_rejects_bad_arguments(kw, code):
     assert ssd(**kw) == code
+
+
+def test_ssd_workspace_size():
+    ws = _lib.ssd_workspace_size
+    a = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    assert ws(1, 2, 64, 128, 200) == 0                    # one segment (L < 2 x 256)
+    # B=4, 80 heads of one 64-channel block: 320 workgroups, one segment
+    assert ws(4, 80, 64, 128, 2048) == 0
+    # B=1, 8 heads: 8 workgroups want 32 segments of 2048 steps
+    slots = 32 * 8
+    assert ws(1, 8, 64, 128, 65536) == a(slots * 64 * 128 * 4) + a(slots * 4)
+    # 1 x 2 blocks want 128 segments; at most ceil(1000 / 256) = 4 -> 250 -> 256 steps -> 4
+    assert ws(1, 2, 64, 64, 1000) == a(1 * 4 * 2 * 64 * 64 * 4) + a(1 * 4 * 2 * 4)
+    assert _lib.lib().mamba_ssd_workspace_size(1, 2, 64, 16, 100) == ctypes.c_size_t(-1).value

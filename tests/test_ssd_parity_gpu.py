@@ -66,6 +66,9 @@ CASES = [
     (1, 1, 64, 128, 1, {"f32_out": True}),
     (2, 2, 64, 64, 64, {"no_z": True, "no_dskip": True, "no_bias": True, "f32_out": True}),
     (1, 2, 64, 128, 40, {"no_final": True}),
+    (1, 2, 64, 128, 1000, {"f32_out": True}),                  # 4 segments of L, ragged last chunk
+    (1, 1, 64, 64, 777, {"f32_out": True, "delta_b": True}),   # 4 segments, odd L: element loads
+    (2, 1, 128, 128, 600, {}),                                 # 3 segments, two channel blocks
 ]
 
 
