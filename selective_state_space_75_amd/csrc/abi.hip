@@ -148,7 +148,7 @@ struct BwdPlan {
 
 // Segments: enough (batch row, channel tile, segment) tasks to give every
 // SIMD of the chip several (at least 8192 in all), segments of at least 64
-// steps, lengths a multiple of 16.
+// steps, lengths a multiple of 32.
 BwdPlan make_bwd_plan(int64_t B, int64_t D, int64_t L) {
   BwdPlan q;
   constexpr int64_t kC = mamba::kBwdChunk;
@@ -160,7 +160,7 @@ BwdPlan make_bwd_plan(int64_t B, int64_t D, int64_t L) {
   if (S > smax) S = smax;
   if (S < 1) S = 1;
   int64_t len = (L + S - 1) / S;
-  len = (len + 15) / 16 * 16;
+  len = (len + 31) / 32 * 32;     // whole 32-step staging blocks
   q.seg_len = len;
   q.S = (L + len - 1) / len;
   const size_t bd = size_t(B) * size_t(D), bsd = bd * size_t(q.S);
@@ -339,9 +339,9 @@ int mamba_scan_bwd(const void* u, const void* delta, const void* z, const void* 
   p.B = B; p.D = D; p.N = N; p.L = L; p.tiles_d = plan.tiles_d; p.nck = plan.nck;
   p.S = plan.S; p.seg_len = plan.seg_len;
   p.delta_b = (flags & MAMBA_FLAG_DELTA_B) ? 1 : 0;
-  p.vec = L % 2 == 0;
+  p.vec = L % 8 == 0;
   for (const void* ptr : {u, delta, z, Bt, Ct, dy, (const void*)du, (const void*)ddelta, (const void*)dz})
-    if (ptr && !aligned(ptr, 8)) p.vec = 0;
+    if (ptr && !aligned(ptr, 16)) p.vec = 0;
   const Dt in = in_dtype == MAMBA_BF16 ? Dt::BF16 : Dt::F32;
   const Dt gd = grad_dtype == MAMBA_BF16 ? Dt::BF16 : Dt::F32;
   return mamba::launch_scan_bwd(p, in, gd, stream) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;

@@ -95,7 +95,7 @@ struct BwdParams {
   float *part_dA, *part_dD, *part_dbias;        // (B, S, D, 16), (B, S, D), (B, S, D) per-segment sums
   int64_t B, D, N, L, tiles_d, nck, S, seg_len;
   int delta_b;
-  int vec;      // L even and every (B, D, L) / (B, N, L) array 8-byte aligned
+  int vec;      // L % 8 == 0 and every (B, D, L) / (B, N, L) array 16-byte aligned
 };
 
 // Mamba-2 (SSD) layer forward: H heads of P channels, one scalar A per head.

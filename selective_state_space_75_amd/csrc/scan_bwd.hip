@@ -35,7 +35,8 @@
 namespace mamba {
 namespace {
 
-constexpr int kT = kBwdChunk;
+constexpr int kT = kBwdChunk;      // steps recomputed at a time
+constexpr int kBlk = 4 * kT;       // steps staged at a time
 
 // Sum over the four lanes of a quad (DPP quad permutations).
 __device__ __forceinline__ float quad_sum4(float v) {
@@ -68,78 +69,97 @@ __device__ __forceinline__ float swap16_sum(float x, float y) {
   return __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
 }
 
-// Two consecutive elements of one row as loaded from global memory; they are
-// widened only where they are consumed, so the loads stay in flight across
-// the chunk being computed.
-template <bool kBF16> struct Raw2;
-template <> struct Raw2<true> {
-  uint32_t w;
-  __device__ __forceinline__ float get(int j) const { return j ? bf16_hi(w) : bf16_lo(w); }
+// Eight consecutive elements of one row as loaded from global memory (16
+// bytes of bf16, 32 of fp32); they are widened only where they are consumed,
+// so the loads stay in flight across the block being computed.
+template <bool kBF16> struct Raw8;
+template <> struct Raw8<true> {
+  uint4 w;
+  __device__ __forceinline__ float get(int j) const {
+    const uint32_t x = j < 2 ? w.x : j < 4 ? w.y : j < 6 ? w.z : w.w;
+    return (j & 1) ? bf16_hi(x) : bf16_lo(x);
+  }
 };
-template <> struct Raw2<false> {
-  float2 f;
-  __device__ __forceinline__ float get(int j) const { return j ? f.y : f.x; }
+template <> struct Raw8<false> {
+  float4 f0, f1;
+  __device__ __forceinline__ float get(int j) const {
+    const float4& f = j < 4 ? f0 : f1;
+    const int k = j & 3;
+    return k == 0 ? f.x : k == 1 ? f.y : k == 2 ? f.z : f.w;
+  }
 };
 
-// Elements off, off + 1 of `base`: one load when `vec` (the caller guarantees
-// alignment and bounds), else element loads with zeros from index `valid` on
-// (and everywhere when !ok).
+// Elements off .. off + 7 of `base`: vector loads when `vec` (the caller
+// guarantees alignment and bounds), else element loads with zeros from index
+// `valid` on (and everywhere when !ok).
 template <bool kBF16>
-__device__ __forceinline__ void ld_raw2(Raw2<kBF16>& r, const void* base, int64_t off, bool vec, bool ok, int valid) {
+__device__ __forceinline__ void ld_raw8(Raw8<kBF16>& r, const void* base, int64_t off, bool vec, bool ok, int valid) {
   if constexpr (kBF16) {
     const uint16_t* q = static_cast<const uint16_t*>(base) + off;
     if (vec) {
-      r.w = ok ? *reinterpret_cast<const uint32_t*>(q) : 0u;
+      r.w = ok ? *reinterpret_cast<const uint4*>(q) : make_uint4(0u, 0u, 0u, 0u);
     } else {
-      const uint32_t lo = (ok && valid > 0) ? (uint32_t)q[0] : 0u;
-      const uint32_t hi = (ok && valid > 1) ? (uint32_t)q[1] : 0u;
-      r.w = lo | (hi << 16);
+      uint32_t h[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) h[j] = (ok && j < valid) ? (uint32_t)q[j] : 0u;
+      r.w = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
     }
   } else {
     const float* q = static_cast<const float*>(base) + off;
     if (vec) {
-      r.f = ok ? *reinterpret_cast<const float2*>(q) : make_float2(0.0f, 0.0f);
+      r.f0 = ok ? *reinterpret_cast<const float4*>(q) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      r.f1 = ok ? *reinterpret_cast<const float4*>(q + 4) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     } else {
-      r.f = make_float2((ok && valid > 0) ? q[0] : 0.0f, (ok && valid > 1) ? q[1] : 0.0f);
+      float h[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) h[j] = (ok && j < valid) ? q[j] : 0.0f;
+      r.f0 = make_float4(h[0], h[1], h[2], h[3]);
+      r.f1 = make_float4(h[4], h[5], h[6], h[7]);
     }
   }
 }
 
-// Stores v0, v1 at off, off + 1 (one store when `vec`, else the first `valid`).
+// Stores v[0..7] at off .. off + 7 (vector stores when `vec`, else the first `valid`).
 template <bool kBF16>
-__device__ __forceinline__ void st2(void* base, int64_t off, bool vec, int valid, float v0, float v1) {
+__device__ __forceinline__ void st8(void* base, int64_t off, bool vec, int valid, const float (&v)[8]) {
   if constexpr (kBF16) {
     uint16_t* q = static_cast<uint16_t*>(base) + off;
     if (vec) {
-      *reinterpret_cast<uint32_t*>(q) = pack_bf16x2(v0, v1);
+      *reinterpret_cast<uint4*>(q) = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                                pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
     } else {
-      if (valid > 0) q[0] = f32_to_bf16(v0);
-      if (valid > 1) q[1] = f32_to_bf16(v1);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (j < valid) q[j] = f32_to_bf16(v[j]);
     }
   } else {
     float* q = static_cast<float*>(base) + off;
     if (vec) {
-      *reinterpret_cast<float2*>(q) = make_float2(v0, v1);
+      *reinterpret_cast<float4*>(q) = make_float4(v[0], v[1], v[2], v[3]);
+      *reinterpret_cast<float4*>(q + 4) = make_float4(v[4], v[5], v[6], v[7]);
     } else {
-      if (valid > 0) q[0] = v0;
-      if (valid > 1) q[1] = v1;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (j < valid) q[j] = v[j];
     }
   }
 }
 
-// Inputs of one chunk for the wave's 16 channels, staged in LDS.  The reverse
-// walk over a step overwrites that step's entries with its results.
+// Inputs of one block of kBlk steps for the wave's 16 channels, staged in
+// LDS.  The reverse walk over a step overwrites that step's entries with its
+// results, which are then stored for the whole block at once.
 struct Stage {
-  float4 V[kT][16];   // [step][channel] {u, delta, dyc, kz}; after the walk {du, ddelta/sigmoid', dz, -}
-  float B[kT][16];    // [step][state] B_t; after the walk the tile's dB_t partial
-  float C[kT][16];    // [step][state] C_t; after the walk the tile's dC_t partial
+  float4 V[kBlk][16];   // [step][channel] {u, delta, dyc, kz}; after the walk {du, ddelta/sigmoid', dz, -}
+  float B[kBlk][16];    // [step][state] B_t; after the walk the tile's dB_t partial
+  float C[kBlk][16];    // [step][state] C_t; after the walk the tile's dC_t partial
 };
 
 // One wave's task: 16 channels of one batch row over one segment of L.
 // Lane roles: (c, g) = (lane / 4, lane % 4) is channel c, states 4 g .. 4 g + 3
-// in the recurrence, and steps 2 g, 2 g + 1 of channel c when loading and
-// storing per-channel rows; (sn, sq) = (lane / 4, lane % 4) is state sn,
-// steps 2 sq, 2 sq + 1 when loading B_t / C_t and storing their gradients.
+// in the recurrence; and steps 8 g .. 8 g + 7 of a block when loading and
+// storing the rows of channel c and of state c (B_t, C_t and their gradients).
+// Each row of a block is thus read and written as 4 lanes x 8 contiguous
+// elements, whole cache lines at a time.
 template <bool kInBF16, bool kGradBF16>
 struct Wave {
   const BwdParams& p;
@@ -150,8 +170,8 @@ struct Wave {
   float a[4], a2[4], ia[4];
 
   struct Raw {
-    Raw2<kInBF16> u, r, z, bt, ct;
-    Raw2<kGradBF16> dy;
+    Raw8<kInBF16> u, r, z, bt, ct;
+    Raw8<kGradBF16> dy;
   };
 
   __device__ explicit Wave(const BwdParams& pp) : p(pp) {
@@ -167,7 +187,7 @@ struct Wave {
     c_ok = d < p.D;
     dd = c_ok ? d : 0;          // channels past D read channel 0 and contribute nothing
     row = (b * p.D + dd) * p.L;
-    sn_ok = c < p.N;            // state role: sn == c
+    sn_ok = c < p.N;            // state role: state c
     brow = (b * p.N + (sn_ok ? c : 0)) * p.L;
     t_begin = s * p.seg_len;
     t_end = t_begin + p.seg_len < p.L ? t_begin + p.seg_len : p.L;
@@ -188,35 +208,29 @@ struct Wave {
     }
   }
 
-  __device__ int chunk_len(int64_t ck) const {
-    const int64_t rem = t_end - ck * kT;
-    return rem < kT ? (int)rem : kT;
-  }
-  __device__ int64_t first_chunk() const { return t_begin / kT; }
-  __device__ int64_t last_chunk() const { return (t_end + kT - 1) / kT - 1; }
-  __device__ int64_t seg_index() const { return (b * p.S + s) * p.D + d; }
+  __device__ int64_t nblocks() const { return (t_end - t_begin + kBlk - 1) / kBlk; }
+  __device__ int64_t ckpt_index(int64_t t) const { return (b * p.D + d) * p.nck + t / kT; }
 
-  // global loads of chunk ck (the z / dy / C_t loads only when `adjoint`)
-  __device__ void fetch(int64_t ck, Raw& x, bool adjoint) const {
-    const int64_t t0 = ck * kT;
-    const bool vec = vecp && t0 + kT <= t_end;
-    const int vc = (int)(t_end - t0 - 2 * g);
-    ld_raw2<kInBF16>(x.u, p.u, row + t0 + 2 * g, vec, true, vc);
-    ld_raw2<kInBF16>(x.r, p.delta, row + t0 + 2 * g, vec, true, vc);
-    ld_raw2<kInBF16>(x.bt, p.Bt, brow + t0 + 2 * g, vec, sn_ok, vc);
+  // global loads of the block at t0 (z / dy / C_t only when `adjoint`)
+  __device__ void fetch(int64_t t0, Raw& x, bool adjoint) const {
+    const bool vec = vecp && t0 + kBlk <= t_end;
+    const int vc = (int)(t_end - t0 - 8 * g);
+    ld_raw8<kInBF16>(x.u, p.u, row + t0 + 8 * g, vec, true, vc);
+    ld_raw8<kInBF16>(x.r, p.delta, row + t0 + 8 * g, vec, true, vc);
+    ld_raw8<kInBF16>(x.bt, p.Bt, brow + t0 + 8 * g, vec, sn_ok, vc);
     if (adjoint) {
-      ld_raw2<kInBF16>(x.ct, p.Ct, brow + t0 + 2 * g, vec, sn_ok, vc);
-      ld_raw2<kInBF16>(x.z, has_z ? p.z : p.u, row + t0 + 2 * g, vec, true, vc);
-      ld_raw2<kGradBF16>(x.dy, p.dy, row + t0 + 2 * g, vec, true, vc);
+      ld_raw8<kInBF16>(x.ct, p.Ct, brow + t0 + 8 * g, vec, sn_ok, vc);
+      ld_raw8<kInBF16>(x.z, has_z ? p.z : p.u, row + t0 + 8 * g, vec, true, vc);
+      ld_raw8<kGradBF16>(x.dy, p.dy, row + t0 + 8 * g, vec, true, vc);
     }
   }
 
   // per element, once: delta, the gated output gradient dyc = dy silu(z),
   // the factor kz of dz = kz yc (kz = dy s (1 + z (1 - s)), s = sigmoid(z)),
   // and (for the write-out) the softplus derivative sigmoid(delta_raw + bias)
-  __device__ void stage(const Raw& x, Stage& st, bool adjoint, float (&sg)[2], float& accD) const {
+  __device__ void stage(const Raw& x, Stage& st, bool adjoint, float (&sg)[8], float& accD) const {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < 8; ++j) {
       const float xr = x.r.get(j) + bias;
       const float uu = x.u.get(j);
       float dyc = 0.0f, kz = 0.0f;
@@ -232,10 +246,10 @@ struct Wave {
         if (!c_ok) { dyc = 0.0f; kz = 0.0f; }
         sg[j] = sigmoidf(xr);
         accD = __builtin_fmaf(dyc, uu, accD);
-        st.C[2 * g + j][c] = x.ct.get(j);
+        st.C[8 * g + j][c] = x.ct.get(j);
       }
-      st.V[2 * g + j][c] = make_float4(uu, softplus(xr), dyc, kz);
-      st.B[2 * g + j][c] = x.bt.get(j);
+      st.V[8 * g + j][c] = make_float4(uu, softplus(xr), dyc, kz);
+      st.B[8 * g + j][c] = x.bt.get(j);
     }
   }
 };
@@ -247,53 +261,70 @@ struct Wave {
 // the next segment and the adjoint into the previous one.
 template <bool kInBF16, bool kGradBF16, bool kDeltaB>
 __global__ __launch_bounds__(64) void bwd_summary_kernel(BwdParams p) {
-  __shared__ Stage st[2];
+  __shared__ Stage st;
   using W = Wave<kInBF16, kGradBF16>;
   const W w(p);
   float h[4] = {0.0f, 0.0f, 0.0f, 0.0f}, R[4] = {1.0f, 1.0f, 1.0f, 1.0f}, H[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  float cum = 0.0f, sg[2], accD = 0.0f;
-  const int64_t ck0 = w.first_chunk(), ck1 = w.last_chunk();
+  float cum = 0.0f, sg[8], accD = 0.0f;
+  const int64_t nb = w.nblocks();
   typename W::Raw x;
-  w.fetch(ck0, x, true);
-  w.stage(x, st[0], true, sg, accD);
+  w.fetch(w.t_begin, x, true);
+  w.stage(x, st, true, sg, accD);
   __syncthreads();
-  for (int64_t ck = ck0; ck <= ck1; ++ck) {
-    const Stage& cs = st[(ck - ck0) & 1];
-    const bool more = ck < ck1;
-    if (more) w.fetch(ck + 1, x, true);
-    if (w.c_ok) {
-      *reinterpret_cast<float4*>(p.ckpt_h + ((w.b * p.D + w.d) * p.nck + ck) * 16 + 4 * w.g) =
-          make_float4(h[0], h[1], h[2], h[3]);
-      if (w.g == 0) p.ckpt_cd[(w.b * p.D + w.d) * p.nck + ck] = cum;
+  for (int64_t ib = 0; ib < nb; ++ib) {
+    const int64_t t0 = w.t_begin + ib * kBlk;
+    const bool more = ib + 1 < nb;
+    if (more) w.fetch(t0 + kBlk, x, true);
+    float4 ckh[4];
+    float ckc[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int64_t tk = t0 + k * kT;
+      ckh[k] = make_float4(h[0], h[1], h[2], h[3]);
+      ckc[k] = cum;
+      if (tk < w.t_end) {
+        const int len = (w.t_end - tk) < kT ? (int)(w.t_end - tk) : kT;
+#pragma unroll
+        for (int tl = 0; tl < kT; ++tl) {
+          if (tl < len) {
+            const int ts = k * kT + tl;
+            const float4 v = st.V[ts][w.c];
+            const float4 Bq = *reinterpret_cast<const float4*>(&st.B[ts][4 * w.g]);
+            const float4 Cq = *reinterpret_cast<const float4*>(&st.C[ts][4 * w.g]);
+            const float bv[4] = {Bq.x, Bq.y, Bq.z, Bq.w}, cv[4] = {Cq.x, Cq.y, Cq.z, Cq.w};
+            cum += v.y;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float xx = v.y * w.a2[i];
+              const float e = hw_exp2(xx);
+              const float coef = kDeltaB ? v.y : expm1_from_exp2(xx, e) * w.ia[i];
+              h[i] = __builtin_fmaf(e, h[i], coef * (bv[i] * v.x));
+              R[i] *= e;
+              H[i] = __builtin_fmaf(R[i], v.z * cv[i], H[i]);
+            }
+          }
+        }
+      }
     }
-    const int len = w.chunk_len(ck);
+    // the block's chunk-start states: 4 x 64 contiguous bytes per channel
+    if (w.c_ok) {
 #pragma unroll
-    for (int tl = 0; tl < kT; ++tl) {
-      if (tl < len) {
-        const float4 v = cs.V[tl][w.c];
-        const float4 Bq = *reinterpret_cast<const float4*>(&cs.B[tl][4 * w.g]);
-        const float4 Cq = *reinterpret_cast<const float4*>(&cs.C[tl][4 * w.g]);
-        const float bv[4] = {Bq.x, Bq.y, Bq.z, Bq.w}, cv[4] = {Cq.x, Cq.y, Cq.z, Cq.w};
-        cum += v.y;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float xx = v.y * w.a2[i];
-          const float e = hw_exp2(xx);
-          const float coef = kDeltaB ? v.y : expm1_from_exp2(xx, e) * w.ia[i];
-          h[i] = __builtin_fmaf(e, h[i], coef * (bv[i] * v.x));
-          R[i] *= e;
-          H[i] = __builtin_fmaf(R[i], v.z * cv[i], H[i]);
+      for (int k = 0; k < 4; ++k) {
+        const int64_t tk = t0 + k * kT;
+        if (tk < w.t_end) {
+          *reinterpret_cast<float4*>(p.ckpt_h + w.ckpt_index(tk) * 16 + 4 * w.g) = ckh[k];
+          if (w.g == k) p.ckpt_cd[w.ckpt_index(tk)] = ckc[k];
         }
       }
     }
     if (more) {
       __syncthreads();
-      w.stage(x, st[(ck + 1 - ck0) & 1], true, sg, accD);
+      w.stage(x, st, true, sg, accD);
       __syncthreads();
     }
   }
   if (w.c_ok) {
-    const int64_t o = w.seg_index() * 16 + 4 * w.g;
+    const int64_t o = ((w.b * p.S + w.s) * p.D + w.d) * 16 + 4 * w.g;
     *reinterpret_cast<float4*>(p.seg_h + o) = make_float4(h[0], h[1], h[2], h[3]);
     *reinterpret_cast<float4*>(p.seg_P + o) = make_float4(R[0], R[1], R[2], R[3]);
     *reinterpret_cast<float4*>(p.seg_H + o) = make_float4(H[0], H[1], H[2], H[3]);
@@ -321,13 +352,13 @@ __global__ __launch_bounds__(256) void bwd_carry_kernel(BwdParams p) {
   }
 }
 
-// Segment pass 2: chunks of the segment from the last: rebuild the chunk's
-// start state from the stored one and the segment's entering state, rerun
-// its steps keeping h_t and (Abar_t - 1) in registers, then walk them in
-// reverse with the adjoint.
+// Segment pass 2: blocks of the segment from the last, and the chunks of a
+// block from the last: rebuild the chunk's start state from the stored one
+// and the segment's entering state, rerun its steps keeping h_t and
+// (Abar_t - 1) in registers, then walk them in reverse with the adjoint.
 template <bool kInBF16, bool kGradBF16, bool kDeltaB>
 __global__ __launch_bounds__(64) void bwd_segment_kernel(BwdParams p) {
-  __shared__ Stage st[2];
+  __shared__ Stage st;
   using W = Wave<kInBF16, kGradBF16>;
   const W w(p);
   const int lane = w.lane, c = w.c, g = w.g;
@@ -342,7 +373,7 @@ __global__ __launch_bounds__(64) void bwd_segment_kernel(BwdParams p) {
 
   float hin[4] = {0.0f, 0.0f, 0.0f, 0.0f}, gs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   if (w.c_ok) {
-    const int64_t o = w.seg_index() * 16 + 4 * g;
+    const int64_t o = ((w.b * p.S + w.s) * p.D + w.d) * 16 + 4 * g;
     const float4 hv = *reinterpret_cast<const float4*>(p.h_in + o);
     const float4 gv = *reinterpret_cast<const float4*>(p.g_in + o);
     hin[0] = hv.x; hin[1] = hv.y; hin[2] = hv.z; hin[3] = hv.w;
@@ -351,166 +382,192 @@ __global__ __launch_bounds__(64) void bwd_segment_kernel(BwdParams p) {
   float anext[4] = {1.0f, 1.0f, 1.0f, 1.0f};
   float dAacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   float accD = 0.0f, accBias = 0.0f;
-  float sg_cur[2], sg_next[2];
-  float4 hl_cur, hl_next;
-  float cd_cur, cd_next;
-  const int64_t ck0 = w.first_chunk(), ck1 = w.last_chunk();
-  auto fetch_ckpt = [&](int64_t ck, float4& hl, float& cd) {
-    if (w.c_ok) {
-      hl = *reinterpret_cast<const float4*>(p.ckpt_h + ((w.b * p.D + w.d) * p.nck + ck) * 16 + 4 * g);
-      cd = p.ckpt_cd[(w.b * p.D + w.d) * p.nck + ck];
-    } else {
-      hl = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-      cd = 0.0f;
+  float sg_cur[8], sg_next[8];
+  float4 ckh_cur[4], ckh_next[4];
+  float ckc_cur[4], ckc_next[4];
+  const int64_t nb = w.nblocks();
+  // the chunk-start states of the block at t0 (4 x 64 contiguous bytes per channel)
+  auto fetch_ckpt = [&](int64_t t0, float4 (&ckh)[4], float (&ckc)[4]) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int64_t tk = t0 + k * kT;
+      const bool ok = w.c_ok && tk < w.t_end;
+      ckh[k] = ok ? *reinterpret_cast<const float4*>(p.ckpt_h + w.ckpt_index(tk) * 16 + 4 * g)
+                  : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      ckc[k] = ok ? p.ckpt_cd[w.ckpt_index(tk)] : 0.0f;
     }
   };
   typename W::Raw x;
-  w.fetch(ck1, x, true);
-  fetch_ckpt(ck1, hl_next, cd_next);
-  w.stage(x, st[0], true, sg_next, accD);
+  {
+    const int64_t tl0 = w.t_begin + (nb - 1) * kBlk;
+    w.fetch(tl0, x, true);
+    fetch_ckpt(tl0, ckh_next, ckc_next);
+    w.stage(x, st, true, sg_next, accD);
+  }
   __syncthreads();
 
-  for (int64_t ck = ck1, it = 0; ck >= ck0; --ck, ++it) {
-    Stage& cs = st[it & 1];
-    const bool more = ck > ck0;
-    sg_cur[0] = sg_next[0];
-    sg_cur[1] = sg_next[1];
-    hl_cur = hl_next;
-    cd_cur = cd_next;
+  for (int64_t ib = nb - 1; ib >= 0; --ib) {
+    const int64_t t0 = w.t_begin + ib * kBlk;
+    const bool more = ib > 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sg_cur[j] = sg_next[j];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      ckh_cur[k] = ckh_next[k];
+      ckc_cur[k] = ckc_next[k];
+    }
     if (more) {
-      w.fetch(ck - 1, x, true);
-      fetch_ckpt(ck - 1, hl_next, cd_next);
+      w.fetch(t0 - kBlk, x, true);
+      fetch_ckpt(t0 - kBlk, ckh_next, ckc_next);
     }
-    const int64_t t0 = ck * kT;
-    const int len = w.chunk_len(ck);
-    // chunk start state: stored (zero segment start) + P(start .. chunk) h_in
-    float hist[kT + 1][4], ec[kT][4];
-    {
-      const float hl[4] = {hl_cur.x, hl_cur.y, hl_cur.z, hl_cur.w};
+    const int blen = (w.t_end - t0) < kBlk ? (int)(w.t_end - t0) : kBlk;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) hist[0][i] = __builtin_fmaf(hw_exp2(w.a2[i] * cd_cur), hin[i], hl[i]);
-    }
+    for (int k = 3; k >= 0; --k) {
+      if (k * kT < blen) {
+        const int len = (blen - k * kT) < kT ? blen - k * kT : kT;
+        // chunk start state: stored (zero segment start) + P(start .. chunk) h_in
+        float hist[kT + 1][4], ec[kT][4];
+        {
+          const float hl[4] = {ckh_cur[k].x, ckh_cur[k].y, ckh_cur[k].z, ckh_cur[k].w};
 #pragma unroll
-    for (int tl = 0; tl < kT; ++tl) {
-      if (tl < len) {
-        const float2 v = *reinterpret_cast<const float2*>(&cs.V[tl][c]);
-        const float4 Bq = *reinterpret_cast<const float4*>(&cs.B[tl][4 * g]);
-        const float bv[4] = {Bq.x, Bq.y, Bq.z, Bq.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float xx = v.y * w.a2[i];
-          const float e = hw_exp2(xx);
-          float coef;
-          if constexpr (kDeltaB) {
-            ec[tl][i] = e;
-            coef = v.y;
-          } else {
-            const float E = expm1_from_exp2(xx, e);
-            ec[tl][i] = E;
-            coef = E * w.ia[i];
-          }
-          hist[tl + 1][i] = __builtin_fmaf(e, hist[tl][i], coef * (bv[i] * v.x));
+          for (int i = 0; i < 4; ++i) hist[0][i] = __builtin_fmaf(hw_exp2(w.a2[i] * ckc_cur[k]), hin[i], hl[i]);
         }
-      }
-    }
 #pragma unroll
-    for (int tl = kT - 1; tl >= 0; --tl) {
-      if (tl < len) {
-        const float4 v = cs.V[tl][c];
-        const float4 Bq = *reinterpret_cast<const float4*>(&cs.B[tl][4 * g]);
-        const float4 Cq = *reinterpret_cast<const float4*>(&cs.C[tl][4 * g]);
-        const float u = v.x, delta = v.y, dyc = v.z, kz = v.w;
-        const float Bv[4] = {Bq.x, Bq.y, Bq.z, Bq.w}, Cv[4] = {Cq.x, Cq.y, Cq.z, Cq.w};
-        float s = 0.0f;
+        for (int tl = 0; tl < kT; ++tl) {
+          if (tl < len) {
+            const int ts = k * kT + tl;
+            const float2 v = *reinterpret_cast<const float2*>(&st.V[ts][c]);
+            const float4 Bq = *reinterpret_cast<const float4*>(&st.B[ts][4 * g]);
+            const float bv[4] = {Bq.x, Bq.y, Bq.z, Bq.w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s = __builtin_fmaf(Cv[i], hist[tl + 1][i], s);
-        const float dz = kz * __builtin_fmaf(w.Dd, u, quad_sum4(s));
-        const float d2 = delta * delta;
-        float sdu = 0.0f, sdd = 0.0f, dBv[4], dCv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float e = kDeltaB ? ec[tl][i] : ec[tl][i] + 1.0f;
-          const float coef = kDeltaB ? delta : ec[tl][i] * w.ia[i];
-          const float gn = __builtin_fmaf(dyc, Cv[i], anext[i] * gs[i]);
-          const float dabar = gn * hist[tl][i];
-          const float gc = gn * coef;
-          dBv[i] = gc * u;
-          dCv[i] = dyc * hist[tl + 1][i];
-          sdu = __builtin_fmaf(gc, Bv[i], sdu);
-          const float dcoef = gn * (Bv[i] * u);
-          const float de = dabar * e;
-          if constexpr (kDeltaB) {
-            sdd = __builtin_fmaf(de, w.a[i], sdd + dcoef);
-            dAacc[i] = __builtin_fmaf(de, delta, dAacc[i]);
-          } else {
-            sdd = __builtin_fmaf(__builtin_fmaf(dabar, w.a[i], dcoef), e, sdd);
-            // d coef / dA = delta^2 phi(delta A), phi(y) = (y e^y - e^y + 1) / y^2:
-            // its series to y^5 for |y| < 1/4 (next term y^6 / 5760, below 2^-24
-            // of phi there), else (y e^y - e^y + 1) / A^2
-            const float y = delta * w.a[i];
-            float ps = __builtin_fmaf(y, 1.0f / 840.0f, 1.0f / 144.0f);
-            ps = __builtin_fmaf(y, ps, 1.0f / 30.0f);
-            ps = __builtin_fmaf(y, ps, 1.0f / 8.0f);
-            ps = __builtin_fmaf(y, ps, 1.0f / 3.0f);
-            ps = __builtin_fmaf(y, ps, 0.5f);
-            const float closed = __builtin_fmaf(y, e, -ec[tl][i]) * ia2[i];
-            const float q = (__builtin_fabsf(y) < 0.25f) ? d2 * ps : closed;
-            dAacc[i] = __builtin_fmaf(dcoef, q, __builtin_fmaf(de, delta, dAacc[i]));
+            for (int i = 0; i < 4; ++i) {
+              const float xx = v.y * w.a2[i];
+              const float e = hw_exp2(xx);
+              float coef;
+              if constexpr (kDeltaB) {
+                ec[tl][i] = e;
+                coef = v.y;
+              } else {
+                const float E = expm1_from_exp2(xx, e);
+                ec[tl][i] = E;
+                coef = E * w.ia[i];
+              }
+              hist[tl + 1][i] = __builtin_fmaf(e, hist[tl][i], coef * (bv[i] * v.x));
+            }
           }
-          gs[i] = gn;
-          anext[i] = e;
         }
-        const float du = __builtin_fmaf(dyc, w.Dd, quad_sum4(sdu));
-        const float dpre = quad_sum4(sdd);
-        // results of this step over its inputs: lane g writes component g
-        reinterpret_cast<float*>(&cs.V[tl][c])[g] = g == 0 ? du : (g == 1 ? dpre : dz);
-        // dB_t, dC_t over the wave's 16 channels (lane bits 2..5)
-        const float w0 = swap32_sum(dBv[0], dCv[0]);
-        const float w1 = swap32_sum(dBv[1], dCv[1]);
-        const float w2 = swap32_sum(dBv[2], dCv[2]);
-        const float w3 = swap32_sum(dBv[3], dCv[3]);
-        const float q0 = swap16_sum(w0, w2);
-        const float q1 = swap16_sum(w1, w3);
-        const float keep = bit3 ? q1 : q0, send = bit3 ? q0 : q1;
-        const float rr = keep + dpp_mov<0x128>(send);           // row_ror:8 pairs lane bit 3
-        // partner lane ^ 4: row_ror:4 reads lane i - 4, row_ror:12 lane i + 4
-        // (both evaluated with the whole wave active, then selected)
-        const float from_m4 = dpp_mov<0x124>(rr), from_p4 = dpp_mov<0x12C>(rr);
-        const float fin = rr + (bit2 ? from_m4 : from_p4);
-        (red_c ? cs.C[tl] : cs.B[tl])[red_state] = fin;
+#pragma unroll
+        for (int tl = kT - 1; tl >= 0; --tl) {
+          if (tl < len) {
+            const int ts = k * kT + tl;
+            const float4 v = st.V[ts][c];
+            const float4 Bq = *reinterpret_cast<const float4*>(&st.B[ts][4 * g]);
+            const float4 Cq = *reinterpret_cast<const float4*>(&st.C[ts][4 * g]);
+            const float u = v.x, delta = v.y, dyc = v.z, kz = v.w;
+            const float Bv[4] = {Bq.x, Bq.y, Bq.z, Bq.w}, Cv[4] = {Cq.x, Cq.y, Cq.z, Cq.w};
+            float sy = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sy = __builtin_fmaf(Cv[i], hist[tl + 1][i], sy);
+            const float dz = kz * __builtin_fmaf(w.Dd, u, quad_sum4(sy));
+            const float d2 = delta * delta;
+            float sdu = 0.0f, sdd = 0.0f, dBv[4], dCv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float e = kDeltaB ? ec[tl][i] : ec[tl][i] + 1.0f;
+              const float coef = kDeltaB ? delta : ec[tl][i] * w.ia[i];
+              const float gn = __builtin_fmaf(dyc, Cv[i], anext[i] * gs[i]);
+              const float dabar = gn * hist[tl][i];
+              const float gc = gn * coef;
+              dBv[i] = gc * u;
+              dCv[i] = dyc * hist[tl + 1][i];
+              sdu = __builtin_fmaf(gc, Bv[i], sdu);
+              const float dcoef = gn * (Bv[i] * u);
+              const float de = dabar * e;
+              if constexpr (kDeltaB) {
+                sdd = __builtin_fmaf(de, w.a[i], sdd + dcoef);
+                dAacc[i] = __builtin_fmaf(de, delta, dAacc[i]);
+              } else {
+                sdd = __builtin_fmaf(__builtin_fmaf(dabar, w.a[i], dcoef), e, sdd);
+                // d coef / dA = delta^2 phi(delta A), phi(y) = (y e^y - e^y + 1) / y^2:
+                // its series to y^5 for |y| < 1/4 (next term y^6 / 5760, below 2^-24
+                // of phi there), else (y e^y - e^y + 1) / A^2
+                const float y = delta * w.a[i];
+                float ps = __builtin_fmaf(y, 1.0f / 840.0f, 1.0f / 144.0f);
+                ps = __builtin_fmaf(y, ps, 1.0f / 30.0f);
+                ps = __builtin_fmaf(y, ps, 1.0f / 8.0f);
+                ps = __builtin_fmaf(y, ps, 1.0f / 3.0f);
+                ps = __builtin_fmaf(y, ps, 0.5f);
+                const float closed = __builtin_fmaf(y, e, -ec[tl][i]) * ia2[i];
+                const float q = (__builtin_fabsf(y) < 0.25f) ? d2 * ps : closed;
+                dAacc[i] = __builtin_fmaf(dcoef, q, __builtin_fmaf(de, delta, dAacc[i]));
+              }
+              gs[i] = gn;
+              anext[i] = e;
+            }
+            const float du = __builtin_fmaf(dyc, w.Dd, quad_sum4(sdu));
+            const float dpre = quad_sum4(sdd);
+            // results of this step over its inputs: lane g writes component g
+            reinterpret_cast<float*>(&st.V[ts][c])[g] = g == 0 ? du : (g == 1 ? dpre : dz);
+            // dB_t, dC_t over the wave's 16 channels (lane bits 2..5)
+            const float w0 = swap32_sum(dBv[0], dCv[0]);
+            const float w1 = swap32_sum(dBv[1], dCv[1]);
+            const float w2 = swap32_sum(dBv[2], dCv[2]);
+            const float w3 = swap32_sum(dBv[3], dCv[3]);
+            const float q0 = swap16_sum(w0, w2);
+            const float q1 = swap16_sum(w1, w3);
+            const float keep = bit3 ? q1 : q0, send = bit3 ? q0 : q1;
+            const float rr = keep + dpp_mov<0x128>(send);           // row_ror:8 pairs lane bit 3
+            // partner lane ^ 4: row_ror:4 reads lane i - 4, row_ror:12 lane i + 4
+            // (both evaluated with the whole wave active, then selected)
+            const float from_m4 = dpp_mov<0x124>(rr), from_p4 = dpp_mov<0x12C>(rr);
+            const float fin = rr + (bit2 ? from_m4 : from_p4);
+            (red_c ? st.C[ts] : st.B[ts])[red_state] = fin;
+          }
+        }
       }
     }
     __syncthreads();
-    // write out: lane (c, g) owns steps 2 g, 2 g + 1 of channel c; as (sn, sq)
-    // steps 2 sq, 2 sq + 1 of state sn == c
+    // write out the block: lane (c, g) owns steps 8 g .. 8 g + 7 of channel c
+    // and of state c
     {
-      const bool vec = w.vecp && len == kT;
-      const int valid = len - 2 * g;
-      const float4 o0 = cs.V[2 * g][c], o1 = cs.V[2 * g + 1][c];
-      const float dr0 = o0.y * sg_cur[0], dr1 = o1.y * sg_cur[1];
-      if (valid > 0) accBias += dr0;
-      if (valid > 1) accBias += dr1;
+      const bool vec = w.vecp && blen == kBlk;
+      const int valid = blen - 8 * g;
+      float du[8], dr[8], dz[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float4 o = st.V[8 * g + j][c];
+        du[j] = o.x;
+        dr[j] = o.y * sg_cur[j];
+        dz[j] = o.z;
+        if (j < valid) accBias += dr[j];
+      }
       if (w.c_ok) {
-        st2<kGradBF16>(p.du, w.row + t0 + 2 * g, vec, valid, o0.x, o1.x);
-        st2<kGradBF16>(p.ddelta, w.row + t0 + 2 * g, vec, valid, dr0, dr1);
-        if (w.has_z) st2<kGradBF16>(p.dz, w.row + t0 + 2 * g, vec, valid, o0.z, o1.z);
+        st8<kGradBF16>(p.du, w.row + t0 + 8 * g, vec, valid, du);
+        st8<kGradBF16>(p.ddelta, w.row + t0 + 8 * g, vec, valid, dr);
+        if (w.has_z) st8<kGradBF16>(p.dz, w.row + t0 + 8 * g, vec, valid, dz);
       }
       if (w.sn_ok) {
-        const int64_t o = ((w.b * p.tiles_d + w.td) * 16 + c) * p.L + t0 + 2 * g;
-        st2<false>(p.part_dB, o, vec, valid, cs.B[2 * g][c], cs.B[2 * g + 1][c]);
-        st2<false>(p.part_dC, o, vec, valid, cs.C[2 * g][c], cs.C[2 * g + 1][c]);
+        float vb[8], vcc[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          vb[j] = st.B[8 * g + j][c];
+          vcc[j] = st.C[8 * g + j][c];
+        }
+        const int64_t o = ((w.b * p.tiles_d + w.td) * 16 + c) * p.L + t0 + 8 * g;
+        st8<false>(p.part_dB, o, vec, valid, vb);
+        st8<false>(p.part_dC, o, vec, valid, vcc);
       }
     }
     if (more) {
       __syncthreads();
-      w.stage(x, st[(it + 1) & 1], true, sg_next, accD);
+      w.stage(x, st, true, sg_next, accD);
       __syncthreads();
     }
   }
   accD = quad_sum4(accD);
   accBias = quad_sum4(accBias);
   if (w.c_ok) {
-    const int64_t o = w.seg_index();
+    const int64_t o = (w.b * p.S + w.s) * p.D + w.d;
     *reinterpret_cast<float4*>(p.part_dA + o * 16 + 4 * g) = make_float4(dAacc[0], dAacc[1], dAacc[2], dAacc[3]);
     if (g == 0) {
       p.part_dD[o] = accD;
