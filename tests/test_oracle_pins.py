@@ -582,3 +582,38 @@ def test_ssd_final_state_is_decayed_sum():
             d = h * P + p
             ref = sum(np.exp(Ah[h] * np.sum(dl[j + 1:])) * coef[j] * Bt[0, :, j] * x[0, d, j] for j in range(L))
             assert np.allclose(st[0, d], ref, rtol=1e-12, atol=1e-14)
+
+
+def test_ssd_pin_catches_expansion_mistakes():
+    """Planted mistakes in the head expansion of the SSD oracle must fail the
+    matrix-form pin: heads tiled instead of repeated over their channels, one
+    head's bias used for all, and A varying with the state instead of the head."""
+    rng = np.random.default_rng(620)
+    B, H, P, N, L = 1, 3, 2, 4, 9
+    x = rng.standard_normal((B, H * P, L))
+    dr = rng.standard_normal((B, H, L))
+    z = rng.standard_normal((B, H * P, L))
+    Bt = rng.standard_normal((B, N, L))
+    Ct = rng.standard_normal((B, N, L))
+    Ah = -rng.uniform(0.5, 4.0, H)
+    Dskip = rng.standard_normal(H * P)
+    bias = rng.standard_normal(H)
+    ref = _ssd_matrix_form(x, dr, z, Bt, Ct, Ah, Dskip, bias, P, "zoh")
+
+    def planted(kind):
+        A = np.repeat(Ah, P)[:, None] * np.ones((1, N))
+        drx = np.repeat(dr, P, axis=1)
+        bx = np.repeat(bias, P)
+        if kind == "tile":
+            drx = np.tile(dr, (1, P, 1))
+        elif kind == "bias0":
+            bx = np.full(H * P, bias[0])
+        elif kind == "A_per_state":
+            A = np.repeat(Ah, P)[:, None] * (1.0 + np.arange(N))[None, :]
+        y, _ = oracle.scan(x, drx, z, Bt, Ct, A, Dskip, bx)
+        return y
+
+    y_ok, _ = oracle.ssd_scan(x, dr, z, Bt, Ct, Ah, Dskip, bias, P=P)
+    assert rel(y_ok, ref) < 1e-12
+    for kind in ("tile", "bias0", "A_per_state"):
+        assert rel(planted(kind), ref) > 1e-3, kind
