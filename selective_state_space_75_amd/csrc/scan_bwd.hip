@@ -606,11 +606,13 @@ __global__ __launch_bounds__(256) void bwd_reduce_params_kernel(BwdParams p) {
   const int64_t rows = p.B * p.S;
   if (n < p.N) {
     float s = 0.0f;
+#pragma unroll 8
     for (int64_t r = 0; r < rows; ++r) s += p.part_dA[(r * p.D + d) * 16 + n];
     p.dA[d * p.N + n] = s;
   }
   if (n == 0) {
     float sd = 0.0f, sb = 0.0f;
+#pragma unroll 8
     for (int64_t r = 0; r < rows; ++r) {
       sd += p.part_dD[r * p.D + d];
       sb += p.part_dbias[r * p.D + d];

@@ -305,7 +305,6 @@ struct Segment {
         for (int i = 0; i < kNS; ++i) { ev[0][i] = evn[i]; inv[0][i] = invn[i]; }
         static_for<0, kCT>([&](auto tc) {
           constexpr int t = decltype(tc)::kValue;
-          constexpr int j = t / 4;
           // Keep the software pipeline as written: without this fence the
           // scheduler sinks the B/C reads of step t+3 next to their use and
           // every step then waits for LDS.
