@@ -52,9 +52,24 @@ int64_t forced_chunks() {
   return (end && *end == '\0' && v > 0) ? (int64_t)v : 0;
 }
 
+// Relative time of the wave-tile kernel over k chunks of L, in units of one
+// wave's full pass over L, for G = kGroupsPlan waves (one per SIMD): the
+// state-only summary pass over the first k - 1 chunks (no readout, gate or
+// output: about 3/4 of the full pass per step) and the full pass, which is
+// balanced over the G waves once there are at least G (chunk, tile) pairs.
+double v4_chunk_cost(int64_t tiles, int64_t k) {
+  const int64_t G = kGroupsPlan;
+  auto rounds = [&](int64_t waves) { return double((waves + G - 1) / G); };
+  const double full = k * tiles >= G ? double(tiles) / double(G) : rounds(k * tiles) / double(k);
+  const double summary = k > 1 ? 0.75 * rounds((k - 1) * tiles) / double(k) : 0.0;
+  return full + summary;
+}
+
 // Shape-only plan (no device query).  One pass per channel tile while there
 // are enough tiles to occupy the GPU; otherwise (few channels, long L) split L
-// so that about 1024 workgroups run, with chunks of at least 2048 steps.
+// into chunks of at least 2048 steps: for the wave-tile kernel the number of
+// chunks that minimises v4_chunk_cost, for the general kernel about 1024
+// workgroups.
 Plan make_plan(int64_t B, int64_t D, int64_t N, int64_t L) {
   Plan p;
   p.tiles_d = (D + kTile - 1) / kTile;
@@ -62,13 +77,19 @@ Plan make_plan(int64_t B, int64_t D, int64_t N, int64_t L) {
   // Units of independent sequential work: 16-channel tiles (wave-tile
   // kernel) or 64-channel tiles (general kernel).
   const int64_t tiles = p.v4 ? B * ((D + kV4Tile - 1) / kV4Tile) : B * p.tiles_d;
-  const int64_t target = p.v4 ? kGroupsPlan : 1024;
   int64_t k = 1;
   const int64_t forced = forced_chunks();
   if (forced > 0) {
     k = forced;
-  } else if (L >= 4096 && tiles < (p.v4 ? target : 512)) {
-    k = (target + tiles - 1) / tiles;
+  } else if (p.v4 && L >= 4096 && tiles < kGroupsPlan) {
+    const int64_t kmax = L / 2048 < 64 ? L / 2048 : 64;
+    double best = v4_chunk_cost(tiles, 1);
+    for (int64_t c = 2; c <= kmax; ++c) {
+      const double cost = v4_chunk_cost(tiles, c);
+      if (cost < best) { best = cost; k = c; }
+    }
+  } else if (!p.v4 && L >= 4096 && tiles < 512) {
+    k = (1024 + tiles - 1) / tiles;
     if (k > L / 2048) k = L / 2048;
     if (k > 64) k = 64;
     if (k < 1) k = 1;
@@ -77,19 +98,22 @@ Plan make_plan(int64_t B, int64_t D, int64_t N, int64_t L) {
   len = (len + kStage - 1) / kStage * kStage;
   p.chunk_len = len;
   p.n_chunks = (L + len - 1) / len;
-  p.balanced = p.v4 && p.n_chunks == 1 && tiles >= kGroupsPlan && getenv("MAMBA_SCAN_NO_BALANCE") == nullptr;
+  p.balanced = p.v4 && p.n_chunks * tiles >= kGroupsPlan && getenv("MAMBA_SCAN_NO_BALANCE") == nullptr;
+  size_t o = 0;
   if (p.n_chunks > 1) {
     const size_t state = size_t(p.n_chunks) * size_t(B) * size_t(D) * size_t(N) * sizeof(float);
     const size_t sums = size_t(p.n_chunks) * size_t(B) * size_t(D) * sizeof(float);
     p.off_local = 0;
     p.off_start = align256(state);
     p.off_sum = p.off_start + align256(state);
-    p.ws_bytes = p.off_sum + align256(sums);
-  } else if (p.balanced) {
-    p.off_flag = 0;
-    p.off_pub = align256(kGroupsPlan * sizeof(uint64_t));
-    p.ws_bytes = p.off_pub + kGroupsPlan * kHandOverBytes;
+    o = p.off_sum + align256(sums);
   }
+  if (p.balanced) {
+    p.off_flag = o;
+    p.off_pub = o + align256(kGroupsPlan * sizeof(uint64_t));
+    o = p.off_pub + kGroupsPlan * kHandOverBytes;
+  }
+  p.ws_bytes = o;
   return p;
 }
 
@@ -242,7 +266,9 @@ int mamba_scan_fwd(const void* u, const void* delta, const void* z, const void* 
     p.h_local = reinterpret_cast<float*>(ws + plan.off_local);
     p.h_start = reinterpret_cast<float*>(ws + plan.off_start);
     p.s_sum = reinterpret_cast<float*>(ws + plan.off_sum);
-    const hipError_t e = plan.v4 ? mamba::launch_scan_v4(p, q, in, out, true, stream)
+    mamba::V2Params qs = q;   // the summary pass runs one workgroup per (chunk, tile)
+    qs.balanced = 0;
+    const hipError_t e = plan.v4 ? mamba::launch_scan_v4(p, qs, in, out, true, stream)
                                  : mamba::launch_scan_summary(p, in, stream);
     if (e != hipSuccess) return MAMBA_ERR_HIP;
     if (mamba::launch_scan_carry(p, stream) != hipSuccess) return MAMBA_ERR_HIP;

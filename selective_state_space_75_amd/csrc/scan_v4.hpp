@@ -444,21 +444,47 @@ __device__ __forceinline__ bool receive(const V2Params& q, int64_t slot, float (
   return ok != 0;
 }
 
+// The full pass of a scan is a set of "virtual tiles": one per (chunk of L,
+// channel tile), chunk-major.  Every chunk but the last has nbf staging
+// blocks of kCT steps, the last has nbl (a single chunk: nbf = nbl = L/kCT).
+// The balanced split flattens (virtual tile, block) and gives every workgroup
+// an equal range of it.
+struct VtGeom {
+  int64_t tiles, nbf, nbl, split;   // split: virtual tiles before the last chunk
+};
+
+__device__ __forceinline__ VtGeom vt_geom(const ScanParams& p, int64_t tiles) {
+  VtGeom v;
+  v.tiles = tiles;
+  v.nbf = p.chunk_len / kCT;
+  v.nbl = (p.L - (p.n_chunks - 1) * p.chunk_len) / kCT;
+  v.split = (p.n_chunks - 1) * tiles;
+  return v;
+}
+__device__ __forceinline__ int64_t vt_pos(const VtGeom& v, int64_t vt) {
+  return vt < v.split ? vt * v.nbf : v.split * v.nbf + (vt - v.split) * v.nbl;
+}
+__device__ __forceinline__ int64_t vt_len(const VtGeom& v, int64_t vt) { return vt < v.split ? v.nbf : v.nbl; }
+__device__ __forceinline__ int64_t vt_at(const VtGeom& v, int64_t x) {   // virtual tile holding block x
+  const int64_t xs = v.split * v.nbf;
+  return x < xs ? x / v.nbf : v.split + (x - xs) / v.nbl;
+}
+
 struct Range {
-  int64_t nb, first, last, lo_off, hi_off, ft_begin;
+  int64_t first, last, lo_off, hi_off, ft_begin;   // virtual tiles; offsets in blocks
   int has_head, has_tail, count;
 };
 
-__device__ __forceinline__ Range balanced_range(const ScanParams& p, const V2Params& q, int64_t tiles) {
+__device__ __forceinline__ Range balanced_range(const VtGeom& v, const V2Params& q) {
   Range w;
   const int64_t gi = blockIdx.x;
-  w.nb = p.L / kCT;
-  const int64_t U = tiles * w.nb;
+  const int64_t U = v.split * v.nbf + v.tiles * v.nbl;
   const int64_t lo = gi * U / q.groups, hi = (gi + 1) * U / q.groups;
-  w.first = lo / w.nb;
-  w.last = (hi - 1) / w.nb;
-  w.lo_off = lo % w.nb;
-  w.hi_off = hi % w.nb;
+  w.first = vt_at(v, lo);
+  w.last = vt_at(v, hi - 1);
+  w.lo_off = lo - vt_pos(v, w.first);
+  const int64_t hi_rel = hi - vt_pos(v, w.last);          // in [1, length of last]
+  w.hi_off = hi_rel == vt_len(v, w.last) ? 0 : hi_rel;
   w.has_head = (w.hi_off != 0 && !(w.first == w.last && w.lo_off != 0)) ? 1 : 0;
   w.has_tail = (w.lo_off != 0) ? 1 : 0;
   w.ft_begin = (w.lo_off == 0) ? w.first : w.first + 1;
@@ -481,27 +507,43 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   using StateOnly = Segment<kInBF16, kOutBF16, false, kN16>;
 
   Range w{};
+  VtGeom v{};
   int nseg = 1;
   if (q.balanced) {
-    w = balanced_range(p, q, tiles);
+    v = vt_geom(p, tiles);
+    w = balanced_range(v, q);
     nseg = w.count;
   }
   for (int si = 0; si < nseg; ++si) {
+    // The segment [t_begin, t_end) lies in chunk `chunk`, which spans
+    // [c_begin, c_end); a segment that starts at c_begin takes the chunk's
+    // start state (zero for chunk 0), any other one the state handed over.
     int kind;
-    int64_t tile, chunk = 0, t_begin, t_end;
+    int64_t tile, chunk, t_begin, t_end, c_begin, c_end;
     if (!q.balanced) {
       kind = kPlain;
       chunk = (int64_t)blockIdx.x / tiles;
       tile = (int64_t)blockIdx.x - chunk * tiles;
-      t_begin = chunk * p.chunk_len;
-      t_end = (t_begin + p.chunk_len < L) ? t_begin + p.chunk_len : L;
-    } else if (w.has_head && si == 0) {
-      kind = kHead; tile = w.last; t_begin = 0; t_end = w.hi_off * kCT;
-    } else if (w.has_tail && si == nseg - 1) {
-      kind = kTail; tile = w.first; t_begin = w.lo_off * kCT;
-      t_end = (w.first == w.last && w.hi_off != 0) ? w.hi_off * kCT : L;
+      c_begin = chunk * p.chunk_len;
+      c_end = (c_begin + p.chunk_len < L) ? c_begin + p.chunk_len : L;
+      t_begin = c_begin;
+      t_end = c_end;
     } else {
-      kind = kWhole; tile = w.ft_begin + (si - w.has_head); t_begin = 0; t_end = L;
+      int64_t vt, b_lo, b_hi;
+      if (w.has_head && si == 0) {
+        kind = kHead; vt = w.last; b_lo = 0; b_hi = w.hi_off;
+      } else if (w.has_tail && si == nseg - 1) {
+        kind = kTail; vt = w.first; b_lo = w.lo_off;
+        b_hi = (w.first == w.last && w.hi_off != 0) ? w.hi_off : vt_len(v, vt);
+      } else {
+        kind = kWhole; vt = w.ft_begin + (si - w.has_head); b_lo = 0; b_hi = vt_len(v, vt);
+      }
+      chunk = vt / tiles;
+      tile = vt - chunk * tiles;
+      c_begin = chunk * p.chunk_len;
+      c_end = c_begin + vt_len(v, vt) * kCT;
+      t_begin = c_begin + b_lo * kCT;
+      t_end = c_begin + b_hi * kCT;
     }
     const int64_t b = tile / tiles_d;
     const int64_t d0 = (tile - b * tiles_d) * kTile;
@@ -514,14 +556,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 #pragma unroll
     for (int i = 0; i < kNS; ++i) {
       h[i] = 0.0f;
-      if (!kSummary && kind == kPlain && p.h_start != nullptr && chunk > 0 && d_ok && 4 * g + i < N)
+      if (!kSummary && p.h_start != nullptr && chunk > 0 && d_ok && 4 * g + i < N)
         h[i] = p.h_start[((chunk * p.B + b) * D + d) * N + 4 * g + i];
     }
     if (!kSummary && kind == kTail) {
       if (!receive(q, (int64_t)blockIdx.x - 1, h)) {
+        // recompute the state at t_begin from the chunk's start state
 #pragma unroll
-        for (int i = 0; i < kNS; ++i) h[i] = 0.0f;
-        StateOnly::run(p, s, b, d0, 0, t_begin, h, k, mode);
+        for (int i = 0; i < kNS; ++i)
+          if (p.h_start == nullptr || chunk == 0) h[i] = 0.0f;
+        StateOnly::run(p, s, b, d0, c_begin, t_begin, h, k, mode);
       }
     }
     if constexpr (kSummary) {
@@ -532,10 +576,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
       if (g == 0 && d_ok) p.s_sum[(chunk * p.B + b) * D + d] = ds;
     } else {
       Full::run(p, s, b, d0, t_begin, t_end, h, k, mode);
-      if (kind == kHead || (kind == kTail && t_end != L)) {
+      if (kind == kHead || (kind == kTail && t_end != c_end)) {
         publish(q, (int64_t)blockIdx.x, h);
-      } else if (t_end == L && p.final_state != nullptr && d_ok &&
-                 (kind != kPlain || chunk == p.n_chunks - 1)) {
+      } else if (t_end == L && p.final_state != nullptr && d_ok) {
 #pragma unroll
         for (int i = 0; i < kNS; ++i)
           if (4 * g + i < N) p.final_state[(b * D + d) * N + 4 * g + i] = h[i];

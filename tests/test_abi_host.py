@@ -52,9 +52,15 @@ def test_workspace_size_plan():
     assert ws(4, 5120, 16, 2048) == 1024 * 8 + 1024 * 16 * 16 * 4
     assert ws(4, 5120, 16, 2040) == 0      # L % 32 != 0: general kernel, no hand-over
     n = ws(1, 4096, 16, 131072)
-    # 256 tiles of 16 channels -> 4 chunks: h_local and h_start (K, B, D, N)
-    # fp32 + sum of delta (K, B, D) fp32
-    assert n == 2 * 4 * 4096 * 16 * 4 + 4 * 4096 * 4
+    # 256 tiles of 16 channels -> 5 chunks (a summary pass of 4 x 256 waves,
+    # a full pass of 5 x 256 (chunk, tile) pairs balanced over 1024 waves):
+    # h_local and h_start (K, B, D, N) fp32, sum of delta (K, B, D) fp32, then
+    # the hand-over flags and slots
+    assert n == 2 * 5 * 4096 * 16 * 4 + 5 * 4096 * 4 + 1024 * 8 + 1024 * 16 * 16 * 4
+    # 512 tiles -> 3 chunks; 64 tiles -> 17 chunks; 768 tiles: one pass
+    assert ws(2, 4096, 16, 65536) == 2 * 3 * 2 * 4096 * 16 * 4 + 3 * 2 * 4096 * 4 + 1024 * 8 + 1024 * 16 * 16 * 4
+    assert ws(1, 1024, 16, 65536) == 2 * 17 * 1024 * 16 * 4 + 17 * 1024 * 4 + 1024 * 8 + 1024 * 16 * 16 * 4
+    assert ws(8, 1536, 16, 65536) == 0
     # the general kernel (L % 32 != 0) plans with 64-channel tiles: 16 chunks
     n = ws(1, 4096, 16, 131072 - 8)
     assert n == 2 * 16 * 4096 * 16 * 4 + 16 * 4096 * 4
@@ -63,6 +69,10 @@ def test_workspace_size_plan():
 
 
 def test_forced_chunks_knob(monkeypatch):
+    # 5 forced chunks x 256 tiles: summary workspace plus the hand-over area
+    monkeypatch.setenv("MAMBA_SCAN_CHUNKS", "5")
+    assert _lib.workspace_size(1, 4096, 16, 320) == 2 * 5 * 4096 * 16 * 4 + 5 * 4096 * 4 + 1024 * 8 + \
+        1024 * 16 * 16 * 4
     monkeypatch.setenv("MAMBA_SCAN_CHUNKS", "3")
     # L = 100 -> chunk_len rounds 34 up to 64 -> 2 chunks
     assert _lib.workspace_size(2, 70, 5, 100) == 2 * (((2 * 2 * 70 * 5 * 4) + 255) // 256 * 256) + \

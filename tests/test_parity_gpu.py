@@ -193,6 +193,11 @@ CASES = [
     (2, 10240, 16, 128, "bf16", "bf16", None, {}),
     (1, 16384 + 64 * 60, 16, 96, "f32", "f32", None, {"zero_A": True}),
     (3, 6000, 9, 64, "bf16", "f32", None, {"delta_b": True}),
+    # at least 1024 (chunk, tile) pairs: summary pass, carry, and a full pass
+    # balanced over (chunk, tile) pairs with state hand-over inside a chunk
+    (1, 4096, 16, 320, "bf16", "bf16", 5, {}),
+    (1, 4096, 16, 352, "f32", "f32", 5, {}),               # last chunk shorter (3, 3, 3, 2 blocks)
+    (2, 2040, 16, 256, "bf16", "f32", 4, {"delta_b": True}),
     # fewer tiles than waves: one pass per tile, ragged last tile
     (4, 2040, 16, 64, "bf16", "bf16", None, {}),
     (8, 1024, 16, 256, "f32", "f32", None, {}),
@@ -234,12 +239,17 @@ def test_ragged_and_options(case, dev, monkeypatch):
     assert e <= (2e-3 if dt == "bf16" else 1e-5)
 
 
-def test_handover_fallback_matches(dev, monkeypatch):
+@pytest.mark.parametrize("shape", [(2, 10240, 16, 160, None), (1, 4096, 16, 352, 5)],
+                         ids=["tiles", "chunk_tiles"])
+def test_handover_fallback_matches(shape, dev, monkeypatch):
     """With the hand-over wait forced to zero every split tile recomputes its
-    state at the cut instead of receiving it; the output must not change."""
+    state at the cut (from the start of its chunk) instead of receiving it;
+    the output must not change."""
     import torch
     import selective_state_space_75_amd as m
-    B, D, N, L = 2, 10240, 16, 160
+    B, D, N, L, chunks = shape
+    if chunks is not None:
+        monkeypatch.setenv("MAMBA_SCAN_CHUNKS", str(chunks))
     assert m.workspace_size(B, D, N, L) > 0
     x = W.custom_scan_inputs(B, D, N, L, "bf16", seed=31337)
     t = upload_scan(x, dev)
