@@ -79,7 +79,10 @@ typedef enum {
 #define MAMBA_FLAG_DELTA_B 0x1u          /* Bbar = delta * B instead of zero-order hold */
 #define MAMBA_FLAG_ACCURATE_EXPM1 0x2u   /* force the cancellation-free (Abar - 1) path;
                                             always on in mamba_state_update and, in
-                                            mamba_scan_fwd, when in_dtype is MAMBA_F32 */
+                                            mamba_scan_fwd and mamba_scan_bwd, when
+                                            in_dtype is MAMBA_F32 or for the channels
+                                            of a 16-channel tile (64 for L % 32 != 0)
+                                            with some |A| < 1/16 */
 
 /*
  * Bytes of device workspace mamba_scan_fwd needs for a problem of this shape.
@@ -166,8 +169,10 @@ size_t mamba_scan_bwd_workspace_size(int64_t B, int64_t D, int64_t N, int64_t L)
  *   dA          : (D, N) fp32; dDskip, ddelta_bias : (D) fp32, written
  *                 (summed over batch rows and time), also when Dskip or
  *                 delta_bias is NULL.
- *   flags       : MAMBA_FLAG_DELTA_B selects the simplified rule, as in the
- *                 forward pass; the cancellation-free (Abar - 1)/A is always used.
+ *   flags       : MAMBA_FLAG_DELTA_B selects the simplified rule, and
+ *                 MAMBA_FLAG_ACCURATE_EXPM1 the cancellation-free (Abar - 1)/A
+ *                 for bf16 inputs, as in the forward pass (fp32 inputs, and a
+ *                 16-channel tile holding a |A| < 1/16, always take it).
  *   workspace   : at least mamba_scan_bwd_workspace_size bytes, 256-byte
  *                 aligned; contents on entry ignored.
  *

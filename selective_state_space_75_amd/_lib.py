@@ -335,8 +335,8 @@ def scan_bwd_workspace_size(B: int, D: int, N: int, L: int) -> int:
     return n
 
 
-def scan_bwd(u, delta, z, Bt, Ct, A, Dskip, delta_bias, dy, *, grad_dtype=None, delta_b=False, workspace=None,
-             stream=None):
+def scan_bwd(u, delta, z, Bt, Ct, A, Dskip, delta_bias, dy, *, grad_dtype=None, delta_b=False,
+             accurate_expm1=False, workspace=None, stream=None):
     """Gradients of scan_fwd (zero initial state) for output gradient dy (B, D, L).
 
     Returns a dict: du, ddelta, dz (B, D, L) in grad_dtype (dz None when z is
@@ -374,7 +374,8 @@ def scan_bwd(u, delta, z, Bt, Ct, A, Dskip, delta_bias, dy, *, grad_dtype=None, 
         _ptr(u), _ptr(delta), _ptr(z), _ptr(Bt), _ptr(Ct), _ptr(A), _ptr(Dskip), _ptr(delta_bias), _ptr(dy),
         _ptr(out["du"]), _ptr(out["ddelta"]), _ptr(out["dz"]), _ptr(out["dBt"]), _ptr(out["dCt"]), _ptr(out["dA"]),
         _ptr(out["dDskip"]), _ptr(out["ddelta_bias"]), B, D, N, L, _dtype_code(u), _dtype_code(dy),
-        FLAG_DELTA_B if delta_b else 0, _ptr(workspace), workspace.numel() * workspace.element_size(),
+        (FLAG_DELTA_B if delta_b else 0) | (FLAG_ACCURATE_EXPM1 if accurate_expm1 else 0),
+        _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(dev, stream))
     if st != 0:
         raise MambaError(st, "mamba_scan_bwd")

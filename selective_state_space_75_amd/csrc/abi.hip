@@ -365,6 +365,7 @@ int mamba_scan_bwd(const void* u, const void* delta, const void* z, const void* 
   p.B = B; p.D = D; p.N = N; p.L = L; p.tiles_d = plan.tiles_d; p.nck = plan.nck;
   p.S = plan.S; p.seg_len = plan.seg_len;
   p.delta_b = (flags & MAMBA_FLAG_DELTA_B) ? 1 : 0;
+  p.accurate = (flags & MAMBA_FLAG_ACCURATE_EXPM1) ? 1 : 0;
   p.vec = L % 8 == 0;
   for (const void* ptr : {u, delta, z, Bt, Ct, dy, (const void*)du, (const void*)ddelta, (const void*)dz})
     if (ptr && !aligned(ptr, 16)) p.vec = 0;

@@ -15,6 +15,13 @@ enum LoopMode : int {
   kDeltaB = 2        // simplified rule Bbar = delta * B
 };
 
+// kZohFast rounds Abar before subtracting 1, so B-bar carries a relative
+// error of about 1.2e-7 / (delta |A|): 1e-5 at |A| = 1, delta = 0.01, but all
+// of it once delta |A| nears 2^-24.  A wave takes kZohAccurate instead when
+// one of its |A| is below this bound (the error is then below 5e-4 for
+// delta >= 1e-3).
+constexpr float kFastZohMinAbsA = 0x1p-4f;
+
 struct ScanParams {
   const void* u;
   const void* delta;
@@ -95,6 +102,7 @@ struct BwdParams {
   float *part_dA, *part_dD, *part_dbias;        // (B, S, D, 16), (B, S, D), (B, S, D) per-segment sums
   int64_t B, D, N, L, tiles_d, nck, S, seg_len;
   int delta_b;
+  int accurate; // cancellation-free (Abar - 1)/A for bf16 inputs too
   int vec;      // L % 8 == 0 and every (B, D, L) / (B, N, L) array 16-byte aligned
 };
 

@@ -20,6 +20,9 @@
 //             dA  += dAbar delta Abar + dcoef delta^2 phi(delta a)   (ZOH)
 //             ddelta_raw = ddelta * sigmoid(delta_raw + bias)
 //           with phi(x) = (x e^x - e^x + 1) / x^2 (a series near 0).
+// The ZOH coefficient follows the forward pass: (Abar - 1)/A from a
+// cancellation-free series for fp32 inputs (or when asked), else as
+// fma(Abar, 1/A, -1/A) from Abar itself.
 // Each chunk's inputs are loaded with vector loads one chunk ahead and
 // staged in LDS; the per-element terms (softplus, its derivative, the gate)
 // are evaluated once there, not once per lane of a channel.
@@ -165,7 +168,7 @@ struct Wave {
   const BwdParams& p;
   int lane, c, g;
   int64_t b, s, td, d, dd, row, brow, t_begin, t_end;
-  bool c_ok, sn_ok, has_z, vecp;
+  bool c_ok, sn_ok, has_z, vecp, small_a;
   float bias, Dd;
   float a[4], a2[4], ia[4];
 
@@ -195,12 +198,14 @@ struct Wave {
     vecp = p.vec != 0;
     bias = p.bias ? p.bias[dd] : 0.0f;
     Dd = p.Dskip ? p.Dskip[dd] : 0.0f;
+    small_a = false;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int64_t n = 4 * g + i;
       float an = n < p.N ? p.A[dd * p.N + n] : -1.0f;
       // |A| < 2^-40 (including 0) as +-2^-40: the coefficient is then delta to
       // within delta * 2^-41, and its derivative in A is delta^2 / 2
+      if (__builtin_fabsf(an) < kFastZohMinAbsA) small_a = true;
       if (__builtin_fabsf(an) < 0x1p-40f) an = (an > 0.0f) ? 0x1p-40f : -0x1p-40f;
       a[i] = an;
       a2[i] = an * kLog2e;
@@ -259,11 +264,9 @@ struct Wave {
 // and per segment the end state h, the product P of Abar over the segment,
 // and H = sum_t (prod_(r <= t) Abar_r) dyc_t C_t, which carry the state into
 // the next segment and the adjoint into the previous one.
-template <bool kInBF16, bool kGradBF16, bool kDeltaB>
-__global__ __launch_bounds__(64) void bwd_summary_kernel(BwdParams p) {
-  __shared__ Stage st;
+template <bool kInBF16, bool kGradBF16, int M>
+__device__ __forceinline__ void summary_body(const BwdParams& p, const Wave<kInBF16, kGradBF16>& w, Stage& st) {
   using W = Wave<kInBF16, kGradBF16>;
-  const W w(p);
   float h[4] = {0.0f, 0.0f, 0.0f, 0.0f}, R[4] = {1.0f, 1.0f, 1.0f, 1.0f}, H[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   float cum = 0.0f, sg[8], accD = 0.0f;
   const int64_t nb = w.nblocks();
@@ -297,7 +300,9 @@ __global__ __launch_bounds__(64) void bwd_summary_kernel(BwdParams p) {
             for (int i = 0; i < 4; ++i) {
               const float xx = v.y * w.a2[i];
               const float e = hw_exp2(xx);
-              const float coef = kDeltaB ? v.y : expm1_from_exp2(xx, e) * w.ia[i];
+              const float coef = M == kDeltaB ? v.y
+                                 : M == kZohFast ? __builtin_fmaf(e, w.ia[i], -w.ia[i])
+                                                 : expm1_from_exp2(xx, e) * w.ia[i];
               h[i] = __builtin_fmaf(e, h[i], coef * (bv[i] * v.x));
               R[i] *= e;
               H[i] = __builtin_fmaf(R[i], v.z * cv[i], H[i]);
@@ -331,6 +336,16 @@ __global__ __launch_bounds__(64) void bwd_summary_kernel(BwdParams p) {
   }
 }
 
+// M = kZohFast falls back to the cancellation-free quotient for a wave with
+// an |A| below kFastZohMinAbsA, as the forward pass does.
+template <bool kInBF16, bool kGradBF16, int M>
+__global__ __launch_bounds__(64) void bwd_summary_kernel(BwdParams p) {
+  __shared__ Stage st;
+  const Wave<kInBF16, kGradBF16> w(p);
+  if (M == kZohFast && __any(w.small_a)) summary_body<kInBF16, kGradBF16, kZohAccurate>(p, w, st);
+  else summary_body<kInBF16, kGradBF16, M>(p, w, st);
+}
+
 // Segment carries, one thread per (batch row, channel, state): the state
 // entering segment s, h_in(s + 1) = P(s) h_in(s) + h(s), and the adjoint term
 // entering from segment s + 1, g_in(s - 1) = H(s) + P(s) g_in(s).
@@ -356,11 +371,9 @@ __global__ __launch_bounds__(256) void bwd_carry_kernel(BwdParams p) {
 // block from the last: rebuild the chunk's start state from the stored one
 // and the segment's entering state, rerun its steps keeping h_t and
 // (Abar_t - 1) in registers, then walk them in reverse with the adjoint.
-template <bool kInBF16, bool kGradBF16, bool kDeltaB>
-__global__ __launch_bounds__(64) void bwd_segment_kernel(BwdParams p) {
-  __shared__ Stage st;
+template <bool kInBF16, bool kGradBF16, int M>
+__device__ __forceinline__ void segment_body(const BwdParams& p, const Wave<kInBF16, kGradBF16>& w, Stage& st) {
   using W = Wave<kInBF16, kGradBF16>;
-  const W w(p);
   const int lane = w.lane, c = w.c, g = w.g;
   const bool red_c = lane >= 32;
   const bool bit3 = (lane >> 3) & 1, bit2 = (lane >> 2) & 1;
@@ -426,7 +439,8 @@ __global__ __launch_bounds__(64) void bwd_segment_kernel(BwdParams p) {
       if (k * kT < blen) {
         const int len = (blen - k * kT) < kT ? blen - k * kT : kT;
         // chunk start state: stored (zero segment start) + P(start .. chunk) h_in
-        float hist[kT + 1][4], ec[kT][4];
+        // er: Abar - 1 (cancellation-free quotient) or Abar (the other rules)
+        float hist[kT + 1][4], er[kT][4];
         {
           const float hl[4] = {ckh_cur[k].x, ckh_cur[k].y, ckh_cur[k].z, ckh_cur[k].w};
 #pragma unroll
@@ -444,12 +458,15 @@ __global__ __launch_bounds__(64) void bwd_segment_kernel(BwdParams p) {
               const float xx = v.y * w.a2[i];
               const float e = hw_exp2(xx);
               float coef;
-              if constexpr (kDeltaB) {
-                ec[tl][i] = e;
+              if constexpr (M == kDeltaB) {
+                er[tl][i] = e;
                 coef = v.y;
+              } else if constexpr (M == kZohFast) {
+                er[tl][i] = e;
+                coef = __builtin_fmaf(e, w.ia[i], -w.ia[i]);
               } else {
                 const float E = expm1_from_exp2(xx, e);
-                ec[tl][i] = E;
+                er[tl][i] = E;
                 coef = E * w.ia[i];
               }
               hist[tl + 1][i] = __builtin_fmaf(e, hist[tl][i], coef * (bv[i] * v.x));
@@ -473,8 +490,9 @@ __global__ __launch_bounds__(64) void bwd_segment_kernel(BwdParams p) {
             float sdu = 0.0f, sdd = 0.0f, dBv[4], dCv[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const float e = kDeltaB ? ec[tl][i] : ec[tl][i] + 1.0f;
-              const float coef = kDeltaB ? delta : ec[tl][i] * w.ia[i];
+              const float e = M == kZohAccurate ? er[tl][i] + 1.0f : er[tl][i];
+              const float coef = M == kDeltaB ? delta
+                                 : M == kZohFast ? __builtin_fmaf(e, w.ia[i], -w.ia[i]) : er[tl][i] * w.ia[i];
               const float gn = __builtin_fmaf(dyc, Cv[i], anext[i] * gs[i]);
               const float dabar = gn * hist[tl][i];
               const float gc = gn * coef;
@@ -483,7 +501,7 @@ __global__ __launch_bounds__(64) void bwd_segment_kernel(BwdParams p) {
               sdu = __builtin_fmaf(gc, Bv[i], sdu);
               const float dcoef = gn * (Bv[i] * u);
               const float de = dabar * e;
-              if constexpr (kDeltaB) {
+              if constexpr (M == kDeltaB) {
                 sdd = __builtin_fmaf(de, w.a[i], sdd + dcoef);
                 dAacc[i] = __builtin_fmaf(de, delta, dAacc[i]);
               } else {
@@ -497,7 +515,8 @@ __global__ __launch_bounds__(64) void bwd_segment_kernel(BwdParams p) {
                 ps = __builtin_fmaf(y, ps, 1.0f / 8.0f);
                 ps = __builtin_fmaf(y, ps, 1.0f / 3.0f);
                 ps = __builtin_fmaf(y, ps, 0.5f);
-                const float closed = __builtin_fmaf(y, e, -ec[tl][i]) * ia2[i];
+                const float em1 = M == kZohFast ? 1.0f - e : -er[tl][i];   // -(Abar - 1)
+                const float closed = __builtin_fmaf(y, e, em1) * ia2[i];
                 const float q = (__builtin_fabsf(y) < 0.25f) ? d2 * ps : closed;
                 dAacc[i] = __builtin_fmaf(dcoef, q, __builtin_fmaf(de, delta, dAacc[i]));
               }
@@ -576,6 +595,14 @@ __global__ __launch_bounds__(64) void bwd_segment_kernel(BwdParams p) {
   }
 }
 
+template <bool kInBF16, bool kGradBF16, int M>
+__global__ __launch_bounds__(64) void bwd_segment_kernel(BwdParams p) {
+  __shared__ Stage st;
+  const Wave<kInBF16, kGradBF16> w(p);
+  if (M == kZohFast && __any(w.small_a)) segment_body<kInBF16, kGradBF16, kZohAccurate>(p, w, st);
+  else segment_body<kInBF16, kGradBF16, M>(p, w, st);
+}
+
 // dB_t, dC_t: sum of the per-tile partials, in tile order.
 __global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(BwdParams p) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -622,16 +649,16 @@ __global__ __launch_bounds__(256) void bwd_reduce_params_kernel(BwdParams p) {
   }
 }
 
-template <bool kInBF16, bool kGradBF16, bool kDeltaB>
+template <bool kInBF16, bool kGradBF16, int M>
 hipError_t bwd_t(const BwdParams& p, hipStream_t s) {
   const dim3 tasks((unsigned)(p.B * p.tiles_d * p.S));
-  hipLaunchKernelGGL((bwd_summary_kernel<kInBF16, kGradBF16, kDeltaB>), tasks, dim3(64), 0, s, p);
+  hipLaunchKernelGGL((bwd_summary_kernel<kInBF16, kGradBF16, M>), tasks, dim3(64), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_carry_kernel, dim3((unsigned)((p.B * p.D * 16 + 255) / 256)), dim3(256), 0, s, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_segment_kernel<kInBF16, kGradBF16, kDeltaB>), tasks, dim3(64), 0, s, p);
+  hipLaunchKernelGGL((bwd_segment_kernel<kInBF16, kGradBF16, M>), tasks, dim3(64), 0, s, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t nbc = p.B * p.N * p.L;
@@ -642,9 +669,15 @@ hipError_t bwd_t(const BwdParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// The forward's rules: bf16 inputs take (Abar - 1)/A from Abar unless the
+// accurate quotient is asked for; fp32 inputs always take it.
 template <bool kInBF16, bool kGradBF16>
 hipError_t bwd_d(const BwdParams& p, hipStream_t s) {
-  return p.delta_b ? bwd_t<kInBF16, kGradBF16, true>(p, s) : bwd_t<kInBF16, kGradBF16, false>(p, s);
+  if (p.delta_b) return bwd_t<kInBF16, kGradBF16, kDeltaB>(p, s);
+  if constexpr (kInBF16) {
+    if (!p.accurate) return bwd_t<kInBF16, kGradBF16, kZohFast>(p, s);
+  }
+  return bwd_t<kInBF16, kGradBF16, kZohAccurate>(p, s);
 }
 
 }  // namespace

@@ -190,16 +190,17 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanParams p) {
   const bool d_ok = d < D;
   const int n0 = wave * kNSW;
   float h[kNSW], a2[kNSW], ia[kNSW];
-  bool tiny = false;
+  bool small_a = false;
 #pragma unroll
   for (int i = 0; i < kNSW; ++i) {
     const int n = n0 + i;
     const bool ok = d_ok && n < N;
     float a = ok ? p.A[d * N + n] : -1.0f;
+    if (__builtin_fabsf(a) < kFastZohMinAbsA) small_a = true;
     // |A| below 2^-40 (including 0) is replaced by -2^-40 (sign kept): the
     // coefficient (e^{delta A} - 1)/A then equals delta to within delta*2^-41,
     // which the accurate loop resolves; 1/A stays finite.
-    if (__builtin_fabsf(a) < 0x1p-40f) { tiny = true; a = (a > 0.0f) ? 0x1p-40f : -0x1p-40f; }
+    if (__builtin_fabsf(a) < 0x1p-40f) a = (a > 0.0f) ? 0x1p-40f : -0x1p-40f;
     a2[i] = a * kLog2e;
     ia[i] = 1.0f / a;
     h[i] = 0.0f;
@@ -207,7 +208,7 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanParams p) {
       if (p.h_start != nullptr && chunk > 0 && ok) h[i] = p.h_start[((chunk * p.B + b) * D + d) * N + n];
     }
   }
-  const int mode = p.delta_b ? kDeltaB : ((p.accurate || __any(tiny)) ? kZohAccurate : kZohFast);
+  const int mode = p.delta_b ? kDeltaB : ((p.accurate || __any(small_a)) ? kZohAccurate : kZohFast);
 
   // ---- staging role: thread = (channel c, 8-step piece pc); B/C: (state sn, 2 steps)
   const int c = tid >> 2, pc = tid & 3;

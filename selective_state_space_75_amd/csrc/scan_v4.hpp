@@ -104,14 +104,15 @@ struct Consts {
 
 __device__ __forceinline__ Consts load_consts(const ScanParams& p, int64_t d, bool d_ok, int g) {
   Consts k;
-  bool tiny = false;
+  bool small_a = false;
 #pragma unroll
   for (int i = 0; i < kNS; ++i) {
     const int n = 4 * g + i;
     float a = (d_ok && n < p.N) ? p.A[d * p.N + n] : -1.0f;
+    if (__builtin_fabsf(a) < kFastZohMinAbsA) small_a = true;
     // |A| < 2^-40 (including 0) becomes -2^-40 (sign kept): the ZOH coefficient
     // is then delta to within delta * 2^-41 (resolved by the accurate loop).
-    if (__builtin_fabsf(a) < 0x1p-40f) { tiny = true; a = (a > 0.0f) ? 0x1p-40f : -0x1p-40f; }
+    if (__builtin_fabsf(a) < 0x1p-40f) a = (a > 0.0f) ? 0x1p-40f : -0x1p-40f;
     k.a2[i] = a * kLog2e;
     k.ia[i] = 1.0f / a;
   }
@@ -119,7 +120,7 @@ __device__ __forceinline__ Consts load_consts(const ScanParams& p, int64_t d, bo
   // so their state stays 0 whatever they read.
   k.bias = !d_ok ? -__builtin_inff() : (p.bias ? p.bias[d] : 0.0f);
   k.dskip = (d_ok && p.Dskip) ? p.Dskip[d] : 0.0f;
-  k.accurate = (p.accurate || __any(tiny)) ? 1 : 0;
+  k.accurate = (p.accurate || __any(small_a)) ? 1 : 0;
   return k;
 }
 

@@ -3,9 +3,11 @@
 forward oracle pin.
 
 Bars: gradients computed in fp32 and returned in fp32 must match to relative
-L2 <= 1e-5 (measured worst: 9.4e-7, dA at the 2.8B-layer shape, a sum over
-4 x 2048 steps; the bar leaves a factor 10); gradients rounded to bf16 to
-relative L2 <= 2e-3 and max-abs <= 1e-2 max|g|.
+L2 <= 1e-5, with bf16 inputs on either ZOH quotient as well (measured worst:
+9.9e-7 with the fast quotient, 5.6e-7 with the cancellation-free one, at the
+2.8B-layer shape, where dA is a sum over 4 x 2048 steps; the bar leaves a
+factor 10); gradients rounded to bf16 to relative L2 <= 2e-3 and max-abs
+<= 1e-2 max|g|.
 """
 import numpy as np
 import pytest
@@ -31,7 +33,7 @@ def _run(x, dev, dy, grad_dtype, opts):
         t["delta_bias"] = None
     dyd = to_dev(dy, dev) if grad_dtype == "f32" else to_dev(W.f32_to_bf16_bits(dy), dev)
     g = m.scan_bwd(t["u"], t["delta_raw"], t["z"], t["Bt"], t["Ct"], t["A"], t["Dskip"], t["delta_bias"], dyd,
-                   delta_b=opts.get("delta_b", False))
+                   delta_b=opts.get("delta_b", False), accurate_expm1=opts.get("accurate", False))
     torch.cuda.synchronize()
     dy64 = dy.astype(np.float64) if grad_dtype == "f32" else f64(W.f32_to_bf16_bits(dy))
     r = oracle.scan_bwd(f64(x["u"]), f64(x["delta_raw"]), None if opts.get("no_z") else f64(x["z"]),
@@ -72,6 +74,9 @@ CASES = [
     (1, 16, 16, 48, "f32", "bf16", {}),
     (1, 16, 16, 1000, "f32", "f32", {}),                # 16 segments of L, the last one ragged
     (1, 8, 7, 777, "bf16", "f32", {}),                  # 13 segments, odd L, a one-step last chunk
+    (3, 33, 5, 41, "bf16", "f32", {"accurate": True}),
+    (2, 48, 16, 96, "bf16", "f32", {"small_A": True}),   # tile 0 on the accurate quotient, tiles 1-2 fast
+    (2, 48, 16, 96, "bf16", "f32", {"small_A": True, "accurate": True}),
 ]
 
 
@@ -86,18 +91,24 @@ def test_bwd_cases(case, dev):
         A[::3, 1] = 0.0
         A[1::4, 5] = -1e-6
         x["A"] = A
+    if opts.get("small_A"):
+        A = x["A"].copy()
+        A[:16, :] *= np.float32(1e-5)
+        x["A"] = A
     dy = np.random.default_rng(9400 + L).standard_normal((B, D, L)).astype(np.float32)
     _run(x, dev, dy, gd, opts)
 
 
-def test_bwd_2p8b_layer_shape(dev):
+@pytest.mark.parametrize("accurate", [False, True], ids=["fast_zoh", "accurate_zoh"])
+def test_bwd_2p8b_layer_shape(accurate, dev):
     """The 2.8B-layer workload (B=4 D=5120 N=16 L=2048, bf16 inputs), fp32
-    gradients, every output compared."""
+    gradients, every output compared, on the default (fast) ZOH quotient and
+    with the cancellation-free one forced."""
     cfg = W.SCAN_CONFIGS["mamba2.8b_layer"]
-    log("[bwd] %s" % cfg.name)
+    log("[bwd] %s accurate=%s" % (cfg.name, accurate))
     x = W.scan_inputs(cfg)
     dy = W._normal_f32([cfg.seed, 77], cfg.B * cfg.D * cfg.L).reshape(cfg.B, cfg.D, cfg.L)
-    _run(x, dev, dy, "f32", {})
+    _run(x, dev, dy, "f32", {"accurate": accurate})
 
 
 def test_bwd_is_deterministic(dev):

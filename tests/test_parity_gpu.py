@@ -198,6 +198,11 @@ CASES = [
     (1, 4096, 16, 320, "bf16", "bf16", 5, {}),
     (1, 4096, 16, 352, "f32", "f32", 5, {}),               # last chunk shorter (3, 3, 3, 2 blocks)
     (2, 2040, 16, 256, "bf16", "f32", 4, {"delta_b": True}),
+    # |A| below 1/16 in the first 16 channels only: those waves (and, for
+    # L % 32 != 0, the first 64-channel tile) take the cancellation-free
+    # quotient, the others the fast one
+    (2, 48, 16, 128, "bf16", "bf16", None, {"small_A": True}),
+    (2, 80, 16, 100, "bf16", "f32", None, {"small_A": True}),
     # fewer tiles than waves: one pass per tile, ragged last tile
     (4, 2040, 16, 64, "bf16", "bf16", None, {}),
     (8, 1024, 16, 256, "f32", "f32", None, {}),
@@ -217,6 +222,11 @@ def test_ragged_and_options(case, dev, monkeypatch):
         A = x["A"].copy()
         A[::3, 1] = 0.0
         A[1::5, 4] = 1e-45
+        x["A"] = A
+    if opts.get("small_A"):
+        A = x["A"].copy()
+        A[:16, :] *= np.float32(1e-5)
+        A[3, 2] = np.float32(-0.05)
         x["A"] = A
     t = upload_scan(x, dev)
     if opts.get("no_z"):
