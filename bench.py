@@ -452,10 +452,12 @@ SSD_SOURCES = ["selective_state_space_75_amd/csrc/ssd.hip", "selective_state_spa
 
 
 def ssd_mfma_flops(cfg) -> int:
-    """Matrix-core flops one launch issues (the split operands counted twice):
-    per 64-channel block and 32-step chunk, C B^T on 3 of 4 16x16 tiles (K = N),
-    G x (K = 32, two parts), C H (K = N, two parts) and B^T (w o x) (K = 32,
-    two parts)."""
+    """Matrix-core flops of the chunked algorithm (the split operands counted
+    twice): per 64-channel block and 32-step chunk, C B^T on 3 of 4 16x16 tiles
+    (K = N), G x (K = 32, two parts), C H (K = N, two parts) and B^T (w o x)
+    (K = 32, two parts).  The segment-state launch, which repeats B^T (w o x)
+    over all segments but the last when L is cut into segments, is not
+    counted."""
     q, pb = 32, 64
     per_chunk = 2 * (3 * 16 * 16 * cfg.N + 2 * q * pb * q + 2 * q * pb * cfg.N + 2 * cfg.N * pb * q)
     chunks = (cfg.L + q - 1) // q

@@ -383,17 +383,18 @@ struct SsdPlan {
   size_t off_h = 0, off_P = 0, bytes = 0;
 };
 
-// Segments of L: only when the (batch row, head, 64-channel block) workgroups
-// are too few to give every CU one (fewer than 256): the extra state-only pass
-// and carry cost more than the added parallelism saves beyond that (measured
-// at B=4, 80 heads: 1 segment 278 us, 2: 336, 4: 302, 8: 322).  Segments of at
-// least 256 steps, lengths a multiple of 32 (the chunk).
+// Segments of L when the (batch row, head, 64-channel block) workgroups are
+// fewer than 512: about 1024 workgroups in all, segments of at least 256
+// steps, lengths a multiple of 32 (the chunk).  Measured at B=4, 80 heads, L =
+// 2048 (chunk launch + segment-state launch): 1 segment 281 us; 2: 248 + 43;
+// 3: 210 + 45; 4: 209 + 46; 6: 221 + 56; 8: 221 + 56.  With 512 or more
+// workgroups the state launch costs about what the added parallelism saves.
 // Test knob: MAMBA_SSD_SEGMENTS=S asks for S segments (still at most one per
 // 32-step chunk).  Read on every call, by the size query and the launch alike.
 SsdPlan make_ssd_plan(int64_t B, int64_t H, int64_t P, int64_t N, int64_t L) {
   SsdPlan q;
   const int64_t wgs = B * H * (P / 64);
-  int64_t S = (256 + wgs - 1) / wgs;
+  int64_t S = wgs < 512 ? (1024 + wgs - 1) / wgs : 1;
   const int64_t smax = (L + 255) / 256;
   if (S > smax) S = smax;
   if (const char* e = getenv("MAMBA_SSD_SEGMENTS")) {

@@ -28,12 +28,12 @@
 // never goes through LDS.
 //
 // L is cut into segments so that there are enough workgroups to hide latency
-// (a head alone is a chain of dependent chunks).  A first launch runs only the
-// state update over each segment from a zero state and keeps its end state
-// and total decay; a carry kernel chains them into each segment's entering
-// state (the associative combination of "Mamba论文研读笔记" 3.2.3 B over
-// segment aggregates); the full launch then runs every segment from its
-// entering state.
+// (a head alone is a chain of dependent chunks).  A first launch computes the
+// end state of every segment but the last from a zero state at its start (one
+// weighted product over the segment's steps) and the segment's total decay;
+// the full launch then runs every segment from its entering state, which it
+// chains from those of the segments before it (the associative combination
+// of "Mamba论文研读笔记" 3.2.3 B over segment aggregates).
 #include "device_math.hpp"
 #include "kernels.hpp"
 
@@ -96,9 +96,7 @@ __device__ __forceinline__ uint2 ld_row4(const uint16_t* row, int64_t t, bool ve
   return make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
 }
 
-// kSummary: the state update only (no C_t, z or output), from a zero state;
-// the segment's end state and total decay go to the workspace.
-template <int kN, bool kOutBF16, bool kDeltaB, bool kSummary>
+template <int kN, bool kOutBF16, bool kDeltaB>
 __global__ __launch_bounds__(256) void ssd_chunk_kernel(SsdParams p) {
   __shared__ SsdLds<kN> S;
   constexpr int kNT = kN / 16;     // 16-row tiles of the state
@@ -154,7 +152,7 @@ __global__ __launch_bounds__(256) void ssd_chunk_kernel(SsdParams p) {
       const int64_t n = 4 * nq + j;
       const bool ok = n < N;
       const int64_t off = (ok ? n : 0) * L + t0;
-      R.c[j] = (!kSummary && ok) ? ld_row4(Crow + off, 4 * tb4, vec, valid - 4 * tb4) : make_uint2(0u, 0u);
+      R.c[j] = ok ? ld_row4(Crow + off, 4 * tb4, vec, valid - 4 * tb4) : make_uint2(0u, 0u);
       R.bb[j] = ok ? ld_row4(Brow + off, 4 * tb4, vec, valid - 4 * tb4) : make_uint2(0u, 0u);
     }
     if (vec) {
@@ -166,14 +164,13 @@ __global__ __launch_bounds__(256) void ssd_chunk_kernel(SsdParams p) {
     }
 #pragma unroll
     for (int tm = 0; tm < 2; ++tm)
-      R.z[tm] = (!kSummary && zrow) ? ld_row4(zrow + t0, 16 * tm + 4 * g, vec, valid - 16 * tm - 4 * g)
+      R.z[tm] = zrow ? ld_row4(zrow + t0, 16 * tm + 4 * g, vec, valid - 16 * tm - 4 * g)
                                     : make_uint2(0u, 0u);
     const int64_t vnext = valid - kQ;
     R.dt = (w == 3 && l < vnext && l < kQ) ? (uint32_t)dtrow[t0 + kQ + l] : 0u;
   };
   // step sizes, decays and coefficients of the chunk at t0 from its raw delta
   // (wave 3 only; lane l = step l)
-  float seg_log = 0.0f;   // A sum of delta over the segment so far (wave 3)
   auto chunk_params = [&](int64_t t0, uint32_t dtw, int buf) {
     const int64_t valid = L - t0;
     float dl = 0.0f, cf = 0.0f;
@@ -188,7 +185,6 @@ __global__ __launch_bounds__(256) void ssd_chunk_kernel(SsdParams p) {
       if (l >= off) v += o;
     }
     const float last = __shfl(v, kQ - 1, 64);
-    seg_log += last;
     if (l < kQ) {
       S.cum[buf][l] = v;
       S.coef[buf][l] = cf;
@@ -217,7 +213,7 @@ __global__ __launch_bounds__(256) void ssd_chunk_kernel(SsdParams p) {
       };
       const uint2 cv = make_uint2(el(c16, 0) | (el(c16, 1) << 16), el(c16, 2) | (el(c16, 3) << 16));
       const uint2 bv = make_uint2(el(b16, 0) | (el(b16, 1) << 16), el(b16, 2) | (el(b16, 3) << 16));
-      if (!kSummary && 4 * nq < kN) {
+      if (4 * nq < kN) {
         *reinterpret_cast<uint2*>(&S.Cc[4 * tb4 + s][4 * nq]) = cv;
         *reinterpret_cast<uint2*>(&S.Bc[4 * tb4 + s][4 * nq]) = bv;
       }
@@ -225,19 +221,23 @@ __global__ __launch_bounds__(256) void ssd_chunk_kernel(SsdParams p) {
     *reinterpret_cast<uint4*>(&S.X[px][8 * tb8]) = R.x;
   };
 
-  // the segment's state slot in the workspace: [channel][state] fp32
-  const int64_t slot = wg;
+  // the entering state: the earlier segments' end states (from zero) and
+  // decays chained in order, h_in(j + 1) = P(j) h_in(j) + h_end(j) -- the
+  // associative combination over segment aggregates.  Slots are
+  // ((b S + j) H + h) pblocks + pb, [channel][state] fp32.
   f32x4 Hs[kNT];
-  if (!kSummary && seg > 0) {
-    const float* hin = p.ws_h + (slot * kP + pc) * N;
+#pragma unroll
+  for (int i = 0; i < kNT; ++i) Hs[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int64_t j = 0; j < seg; ++j) {
+    const int64_t sj = ((b * p.S + j) * p.H + h) * pblocks + pb;
+    const float Pj = p.ws_P[sj];
+    const float* hl = p.ws_h + (sj * kP + pc) * N;
 #pragma unroll
     for (int tn = 0; tn < kNT; ++tn) {
-      const float4 v = *reinterpret_cast<const float4*>(hin + 16 * tn + 4 * g);
-      Hs[tn] = f32x4{v.x, v.y, v.z, v.w};
+      const float4 v = *reinterpret_cast<const float4*>(hl + 16 * tn + 4 * g);
+      Hs[tn] = f32x4{__builtin_fmaf(Pj, Hs[tn][0], v.x), __builtin_fmaf(Pj, Hs[tn][1], v.y),
+                     __builtin_fmaf(Pj, Hs[tn][2], v.z), __builtin_fmaf(Pj, Hs[tn][3], v.w)};
     }
-  } else {
-#pragma unroll
-    for (int i = 0; i < kNT; ++i) Hs[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   }
 
   const int64_t ck0 = t_begin / kQ, nchunks = (t_end + kQ - 1) / kQ;
@@ -258,7 +258,7 @@ __global__ __launch_bounds__(256) void ssd_chunk_kernel(SsdParams p) {
     // ---- S = C B^T on the three lower 16 x 16 tiles and G from it (waves
     // 0..2); the next chunk's step sizes, decays and coefficients (wave 3)
     const int tm1 = (w == 0) ? 0 : 1, tn1 = (w == 2) ? 1 : 0;
-    if (!kSummary && w < 3) {
+    if (w < 3) {
       f32x4 St = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int kb = 0; kb < kNK; ++kb)
@@ -292,7 +292,7 @@ __global__ __launch_bounds__(256) void ssd_chunk_kernel(SsdParams p) {
     // 32 kb + 4 g + e (tile 2 kb) and 32 kb + 16 + 4 g + e (tile 2 kb + 1)
     bf16x8 Hh[kNK], Hl[kNK];
 #pragma unroll
-    for (int kb = 0; kb < (kSummary ? 0 : kNK); ++kb) {
+    for (int kb = 0; kb < kNK; ++kb) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float v = (e < 4) ? Hs[2 * kb][e] : Hs[2 * kb + 1][e - 4];
@@ -307,7 +307,7 @@ __global__ __launch_bounds__(256) void ssd_chunk_kernel(SsdParams p) {
     // ---- y = G x + exp(cum_t) C H + D x for the wave's 16 channels
     f32x4 Yd[2], Yo[2];
 #pragma unroll
-    for (int tm = 0; tm < (kSummary ? 0 : 2); ++tm) {
+    for (int tm = 0; tm < 2; ++tm) {
       const bf16x8 xb = lds8(&S.X[pc][8 * g]);
       Yd[tm] = mfma(lds8(&S.Gh[16 * tm + r][8 * g]), xb, f32x4{0.0f, 0.0f, 0.0f, 0.0f});
       Yd[tm] = mfma(lds8(&S.Gl[16 * tm + r][8 * g]), xb, Yd[tm]);
@@ -333,7 +333,7 @@ __global__ __launch_bounds__(256) void ssd_chunk_kernel(SsdParams p) {
     }
     // ---- gate and store: lane holds steps 16 tm + 4 g + e of channel pc
 #pragma unroll
-    for (int tm = 0; tm < (kSummary ? 0 : 2); ++tm) {
+    for (int tm = 0; tm < 2; ++tm) {
       const int tb = 16 * tm + 4 * g;
       const uint2 xv = *reinterpret_cast<const uint2*>(&S.X[pc][tb]);
       const float xs[4] = {bf16_lo(xv.x), bf16_hi(xv.x), bf16_lo(xv.y), bf16_hi(xv.y)};
@@ -370,13 +370,7 @@ __global__ __launch_bounds__(256) void ssd_chunk_kernel(SsdParams p) {
     }
     if (c + 1 < nchunks) cur = nxt;
   }
-  if constexpr (kSummary) {
-    float* ho = p.ws_h + (slot * kP + pc) * N;
-#pragma unroll
-    for (int tn = 0; tn < kNT; ++tn)
-      *reinterpret_cast<float4*>(ho + 16 * tn + 4 * g) = make_float4(Hs[tn][0], Hs[tn][1], Hs[tn][2], Hs[tn][3]);
-    if (w == 3 && l == 0) p.ws_P[slot] = hw_exp2(seg_log * kLog2e);
-  } else if (p.final_state && seg == p.S - 1) {
+  if (p.final_state && seg == p.S - 1) {
     float* fs = p.final_state + (b * D + d0 + pc) * N;
 #pragma unroll
     for (int tn = 0; tn < kNT; ++tn)
@@ -384,38 +378,200 @@ __global__ __launch_bounds__(256) void ssd_chunk_kernel(SsdParams p) {
   }
 }
 
-// Segment carries, one thread per (batch row, head, channel block, channel,
-// state): the state entering segment s + 1 is P(s) h_in(s) + h_end(s), written
-// over the segment's slot in order.
-__global__ __launch_bounds__(256) void ssd_carry_kernel(SsdParams p) {
-  const int64_t per = p.H * (p.P / kP) * kP * p.N;          // elements per (batch row, segment)
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= p.B * per) return;
-  const int64_t b = i / per, e = i - b * per;                 // e = (h pblocks + pb) kP N + c N + n
-  const int64_t blk = e / (kP * p.N);
-  float hin = 0.0f;
-  for (int64_t s = 0; s < p.S; ++s) {
-    const int64_t slot = (b * p.S + s) * (per / (kP * p.N)) + blk;
-    float* q = p.ws_h + slot * kP * p.N + (e - blk * kP * p.N);
-    const float v = *q;
-    *q = hin;
-    hin = __builtin_fmaf(p.ws_P[slot], hin, v);
+// End state of every segment but the last, from a zero state at its start,
+// and the segment's decay exp(A sum delta), for the carry:
+//   H = sum_s exp(A sum_(s < r <= end) delta_r) coef_s x_s B_s^T.
+// Each step's weight folds in its decay to the segment end, so the segment
+// is one weighted product over its steps: no chunk products, no rescaling of
+// the state.  Per 32-step block the workgroup stages B_t ([state][step], as
+// read) and the weighted x split into two bf16 parts in LDS, double-buffered
+// with one barrier per block, with the global loads two blocks ahead; wave w
+// then accumulates channels 16 w .. 16 w + 15 exactly as the chunk kernel
+// holds its state.  The weights of up to kPiece steps at a time are computed
+// from the segment end backwards: suffix sums of delta stay small, and
+// exact, where the decay is near 1.
+constexpr int kPiece = 512;
+
+template <int V> struct IntTag { static constexpr int kValue = V; };
+// f(IntTag<i>{}) for i = I .. E-1, unrolled
+template <int I, int E, typename F>
+__device__ __forceinline__ void unroll_for(F&& f) {
+  if constexpr (I < E) {
+    f(IntTag<I>{});
+    unroll_for<I + 1, E>(f);
   }
+}
+
+template <int kN>
+struct StateLds {
+  uint16_t BT[2][kN][kQ + kPad];   // B_t [state][step]
+  uint16_t Xh[2][kP][kQ + kPad];   // w o x [channel][step], high part
+  uint16_t Xl[2][kP][kQ + kPad];   //                        remainder
+  float Wt[kPiece];                // w of the piece's steps
+  float wave_sum[2][4];
+};
+
+template <int kN, bool kDeltaB, bool kVec>
+__global__ __launch_bounds__(256) void ssd_state_kernel(SsdParams p) {
+  __shared__ StateLds<kN> S;
+  constexpr int kNT = kN / 16;
+  constexpr int kBR = kN / 64;                               // B rows per staging thread
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, l = tid & 63;
+  const int g = l >> 4, r = l & 15;
+  const int lr = tid >> 2, lq = tid & 3;                     // staging: row lr (+ 64 i), steps 8 lq .. + 7
+  const int64_t pblocks = p.P / kP;
+  const int64_t segs = p.S - 1;                              // the last segment needs no end state
+  const int64_t wg = blockIdx.x;                             // ((b segs + seg) H + h) pblocks + pb
+  const int64_t pb = wg % pblocks;
+  const int64_t h = (wg / pblocks) % p.H;
+  const int64_t bs = wg / (pblocks * p.H);
+  const int64_t seg = bs % segs, b = bs / segs;
+  const int64_t slot = ((b * p.S + seg) * p.H + h) * pblocks + pb;
+  const int64_t t_begin = seg * p.seg_len;                   // whole segment: t_begin + seg_len < L
+  const int64_t L = p.L, D = p.H * p.P, N = p.N;
+  const float a = p.A[h];
+  const float a2 = a * kLog2e;
+  const float ia = 1.0f / a;
+  const float bias = p.bias ? p.bias[h] : 0.0f;
+  const int pc = 16 * w + r;
+  const uint16_t* xrow = static_cast<const uint16_t*>(p.x) + (b * D + h * p.P + pb * kP + lr) * L;
+  const uint16_t* dtrow = static_cast<const uint16_t*>(p.delta) + (b * p.H + h) * L;
+  const uint16_t* Bbase = static_cast<const uint16_t*>(p.Bt) + b * N * L;
+
+  f32x4 Hs[kNT];
+#pragma unroll
+  for (int i = 0; i < kNT; ++i) Hs[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // 8 consecutive bf16 of a row at t (one 16-byte load when the rows allow it)
+  auto ld8 = [&](const uint16_t* row, int64_t t) -> uint4 {
+    if constexpr (kVec) return *reinterpret_cast<const uint4*>(row + t);
+    uint32_t e[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = row[t + j];
+    return make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16));
+  };
+  struct Raw {
+    uint4 x;
+    uint4 bt[kBR];
+  };
+  auto fetch = [&](int64_t t, Raw& o) {
+    o.x = ld8(xrow, t + 8 * lq);
+#pragma unroll
+    for (int i = 0; i < kBR; ++i) o.bt[i] = ld8(Bbase + (lr + 64 * i) * L, t + 8 * lq);
+  };
+
+  float after = 0.0f;   // sum of delta over the segment's steps after the current piece
+  const int64_t npieces = (p.seg_len + kPiece - 1) / kPiece;
+  for (int64_t pi = npieces - 1; pi >= 0; --pi) {
+    const int64_t p0 = t_begin + pi * kPiece;
+    const int plen = (int)((p.seg_len - pi * kPiece) < kPiece ? (p.seg_len - pi * kPiece) : kPiece);
+    // weights of steps 2 tid and 2 tid + 1 of the piece
+    const int s0 = 2 * tid;
+    float dl[2] = {0.0f, 0.0f}, cf[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if (s0 + j < plen) {
+        dl[j] = softplus(bf16_to_f32(dtrow[p0 + s0 + j]) + bias);
+        cf[j] = kDeltaB ? dl[j] : expm1_from_exp2(dl[j] * a2, hw_exp2(dl[j] * a2)) * ia;
+      }
+    }
+    const float own = dl[0] + dl[1];
+    float v = own;                                      // sum over this lane and the lanes above it
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float o = __shfl_down(v, off, 64);
+      if (l + off < 64) v += o;
+    }
+    const int par = (int)(pi & 1);
+    if (l == 0) S.wave_sum[par][w] = v;
+    __syncthreads();                                    // also: the previous piece's blocks are consumed
+    float later_waves = 0.0f;
+#pragma unroll
+    for (int j = 1; j < 4; ++j)
+      if (w + j < 4) later_waves += S.wave_sum[par][w + j];
+    const float beyond = (v - own) + later_waves + after;   // delta after step s0 + 1
+    if (s0 < plen) S.Wt[s0] = hw_exp2(a2 * (beyond + dl[1])) * cf[0];
+    if (s0 + 1 < plen) S.Wt[s0 + 1] = hw_exp2(a2 * beyond) * cf[1];
+    after += (S.wave_sum[par][0] + S.wave_sum[par][1]) + (S.wave_sum[par][2] + S.wave_sum[par][3]);
+    __syncthreads();
+
+    // the piece's 32-step blocks: global loads two blocks ahead in three
+    // rotating register sets (none is copied: a copy would wait for the loads
+    // in flight), issued unconditionally with addresses past the piece
+    // clamped to its last block (a conditional load would leave the compiler
+    // unsure how many loads are in flight, and its waits would then cover the
+    // newest ones as well)
+    const int nblk = plen / 32;
+    auto block = [&](const Raw& o, int k) {
+      const int buf = k & 1;
+      const float4 w0 = *reinterpret_cast<const float4*>(&S.Wt[32 * k + 8 * lq]);
+      const float4 w1 = *reinterpret_cast<const float4*>(&S.Wt[32 * k + 8 * lq + 4]);
+      const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+      const uint32_t xw[4] = {o.x.x, o.x.y, o.x.z, o.x.w};
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint16_t h0, l0, h1, l1;
+        split_bf16(bf16_lo(xw[i]) * wv[2 * i], h0, l0);
+        split_bf16(bf16_hi(xw[i]) * wv[2 * i + 1], h1, l1);
+        hw[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        lw[i] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+      }
+      *reinterpret_cast<uint4*>(&S.Xh[buf][lr][8 * lq]) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      *reinterpret_cast<uint4*>(&S.Xl[buf][lr][8 * lq]) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+#pragma unroll
+      for (int i = 0; i < kBR; ++i) *reinterpret_cast<uint4*>(&S.BT[buf][lr + 64 * i][8 * lq]) = o.bt[i];
+      // the other buffer's readers finished before they reached this barrier
+      __syncthreads();
+      const bf16x8 xh = lds8(&S.Xh[buf][pc][8 * g]), xl = lds8(&S.Xl[buf][pc][8 * g]);
+#pragma unroll
+      for (int tn = 0; tn < kNT; ++tn) {
+        const bf16x8 bt = lds8(&S.BT[buf][16 * tn + r][8 * g]);
+        Hs[tn] = mfma(bt, xh, Hs[tn]);
+        Hs[tn] = mfma(bt, xl, Hs[tn]);
+      }
+    };
+    auto blk_t = [&](int k) { return p0 + 32 * (k < nblk ? k : nblk - 1); };
+    constexpr int kAhead = 2, kSets = 3;
+    Raw o[kSets];
+    unroll_for<0, kAhead>([&](auto jc) { fetch(blk_t(decltype(jc)::kValue), o[decltype(jc)::kValue]); });
+    const int ngroups = nblk / kSets;
+    for (int gi = 0; gi < ngroups; ++gi) {
+      unroll_for<0, kSets>([&](auto jc) {
+        constexpr int j = decltype(jc)::kValue;
+        const int k = gi * kSets + j;
+        fetch(blk_t(k + kAhead), o[(j + kAhead) % kSets]);
+        block(o[j], k);
+      });
+    }
+    // the last nblk % kSets blocks are already loaded, in o[0] ..
+    const int rem = nblk - ngroups * kSets;
+    unroll_for<0, kSets - 1>([&](auto jc) {
+      constexpr int j = decltype(jc)::kValue;
+      if (j < rem) block(o[j], ngroups * kSets + j);
+    });
+  }
+  float* ho = p.ws_h + (slot * kP + pc) * N;
+#pragma unroll
+  for (int tn = 0; tn < kNT; ++tn)
+    *reinterpret_cast<float4*>(ho + 16 * tn + 4 * g) = make_float4(Hs[tn][0], Hs[tn][1], Hs[tn][2], Hs[tn][3]);
+  if (tid == 0) p.ws_P[slot] = hw_exp2(a2 * after);
 }
 
 template <int kN, bool kOutBF16, bool kDeltaB>
 hipError_t ssd_d(const SsdParams& p, hipStream_t s) {
   const dim3 grid((unsigned)(p.B * p.S * p.H * (p.P / kP)));
   if (p.S > 1) {
-    hipLaunchKernelGGL((ssd_chunk_kernel<kN, kOutBF16, kDeltaB, true>), grid, dim3(256), 0, s, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int64_t n = p.B * p.H * p.P * p.N;
-    hipLaunchKernelGGL(ssd_carry_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p);
-    e = hipGetLastError();
+    const dim3 sgrid((unsigned)(p.B * (p.S - 1) * p.H * (p.P / kP)));
+    if (p.vec)
+      hipLaunchKernelGGL((ssd_state_kernel<kN, kDeltaB, true>), sgrid, dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL((ssd_state_kernel<kN, kDeltaB, false>), sgrid, dim3(256), 0, s, p);
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((ssd_chunk_kernel<kN, kOutBF16, kDeltaB, false>), grid, dim3(256), 0, s, p);
+  hipLaunchKernelGGL((ssd_chunk_kernel<kN, kOutBF16, kDeltaB>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

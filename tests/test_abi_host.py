@@ -261,10 +261,14 @@ def test_ssd_workspace_size():
     ws = _lib.ssd_workspace_size
     a = lambda x: (x + 255) // 256 * 256  # noqa: E731
     assert ws(1, 2, 64, 128, 200) == 0                    # one segment (L < 2 x 256)
-    # B=4, 80 heads of one 64-channel block: 320 workgroups, one segment
-    assert ws(4, 80, 64, 128, 2048) == 0
-    # B=1, 8 heads: 8 workgroups want 32 segments of 2048 steps
-    slots = 32 * 8
+    # B=4, 80 heads of one 64-channel block: 320 workgroups want 4 segments
+    # (about 1024 workgroups) of 512 steps: one state slot per workgroup
+    slots = 4 * 320
+    assert ws(4, 80, 64, 128, 2048) == a(slots * 64 * 128 * 4) + a(slots * 4)
+    # 512 workgroups or more: one segment
+    assert ws(8, 64, 64, 128, 2048) == 0
+    # B=1, 8 heads: 8 workgroups want 128 segments of 512 steps
+    slots = 128 * 8
     assert ws(1, 8, 64, 128, 65536) == a(slots * 64 * 128 * 4) + a(slots * 4)
     # 1 x 2 blocks want 128 segments; at most ceil(1000 / 256) = 4 -> 250 -> 256 steps -> 4
     assert ws(1, 2, 64, 64, 1000) == a(1 * 4 * 2 * 64 * 64 * 4) + a(1 * 4 * 2 * 4)

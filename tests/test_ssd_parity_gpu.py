@@ -84,6 +84,18 @@ def test_ssd_cases(case, dev):
          final=not opts.get("no_final"))
 
 
+@pytest.mark.parametrize("segments, L", [(2, 1600), (3, 1000), (5, 2080)])
+def test_ssd_forced_segments(segments, L, dev, monkeypatch):
+    """Segments of L forced: segment end states from the weighted product over
+    each segment's steps (weights staged 512 steps at a time: 800-step
+    segments take two pieces), the carry, and the full pass per segment."""
+    import torch
+    monkeypatch.setenv("MAMBA_SSD_SEGMENTS", str(segments))
+    log("[ssd] forced %d segments, L=%d" % (segments, L))
+    x = W.ssd_inputs(1, 2, 64, 128, L, seed=7200 + L)
+    _run(x, dev, 64, out_dtype=torch.float32)
+
+
 def test_ssd_2p7b_layer_shape(dev):
     """The bench workload (B=4, 80 heads of 64 channels, N=128, L=2048, gated),
     every output and the final state compared."""
