@@ -84,16 +84,19 @@ def test_ssd_cases(case, dev):
          final=not opts.get("no_final"))
 
 
-@pytest.mark.parametrize("segments, L", [(2, 1600), (3, 1000), (5, 2080)])
-def test_ssd_forced_segments(segments, L, dev, monkeypatch):
+@pytest.mark.parametrize("segments, L, N, delta_b", [(2, 1600, 128, False), (3, 1000, 128, False),
+                                                      (5, 2080, 128, False), (3, 1600, 64, True),
+                                                      (2, 1601, 64, False)])
+def test_ssd_forced_segments(segments, L, N, delta_b, dev, monkeypatch):
     """Segments of L forced: segment end states from the weighted product over
     each segment's steps (weights staged 512 steps at a time: 800-step
-    segments take two pieces), the carry, and the full pass per segment."""
+    segments take two pieces; odd L takes element loads), then the chunk pass
+    per segment from the entering state chained from them."""
     import torch
     monkeypatch.setenv("MAMBA_SSD_SEGMENTS", str(segments))
-    log("[ssd] forced %d segments, L=%d" % (segments, L))
-    x = W.ssd_inputs(1, 2, 64, 128, L, seed=7200 + L)
-    _run(x, dev, 64, out_dtype=torch.float32)
+    log("[ssd] forced %d segments, L=%d N=%d delta_b=%s" % (segments, L, N, delta_b))
+    x = W.ssd_inputs(1, 2, 64, N, L, seed=7200 + L + N)
+    _run(x, dev, 64, out_dtype=torch.float32, delta_b=delta_b)
 
 
 def test_ssd_2p7b_layer_shape(dev):
