@@ -32,6 +32,8 @@
 // second kernel adds the partials of all tiles in a fixed order, and the
 // per-batch-row partials of dA, dD and the bias gradient likewise, so results
 // are deterministic.
+#include <type_traits>
+
 #include "device_math.hpp"
 #include "kernels.hpp"
 
@@ -280,37 +282,43 @@ __device__ __forceinline__ void summary_body(const BwdParams& p, const Wave<kInB
     if (more) w.fetch(t0 + kBlk, x, true);
     float4 ckh[4];
     float ckc[4];
+    // whole blocks take a copy of the steps with every count known at compile time
+    auto steps = [&](auto whole) {
+      constexpr bool kWhole = decltype(whole)::value;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int64_t tk = t0 + k * kT;
-      ckh[k] = make_float4(h[0], h[1], h[2], h[3]);
-      ckc[k] = cum;
-      if (tk < w.t_end) {
-        const int len = (w.t_end - tk) < kT ? (int)(w.t_end - tk) : kT;
+      for (int k = 0; k < 4; ++k) {
+        const int64_t tk = t0 + k * kT;
+        ckh[k] = make_float4(h[0], h[1], h[2], h[3]);
+        ckc[k] = cum;
+        if (kWhole || tk < w.t_end) {
+          const int len = kWhole ? kT : ((w.t_end - tk) < kT ? (int)(w.t_end - tk) : kT);
 #pragma unroll
-        for (int tl = 0; tl < kT; ++tl) {
-          if (tl < len) {
-            const int ts = k * kT + tl;
-            const float4 v = st.V[ts][w.c];
-            const float4 Bq = *reinterpret_cast<const float4*>(&st.B[ts][4 * w.g]);
-            const float4 Cq = *reinterpret_cast<const float4*>(&st.C[ts][4 * w.g]);
-            const float bv[4] = {Bq.x, Bq.y, Bq.z, Bq.w}, cv[4] = {Cq.x, Cq.y, Cq.z, Cq.w};
-            cum += v.y;
+          for (int tl = 0; tl < kT; ++tl) {
+            if (tl < len) {
+              const int ts = k * kT + tl;
+              const float4 v = st.V[ts][w.c];
+              const float4 Bq = *reinterpret_cast<const float4*>(&st.B[ts][4 * w.g]);
+              const float4 Cq = *reinterpret_cast<const float4*>(&st.C[ts][4 * w.g]);
+              const float bv[4] = {Bq.x, Bq.y, Bq.z, Bq.w}, cv[4] = {Cq.x, Cq.y, Cq.z, Cq.w};
+              cum += v.y;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float xx = v.y * w.a2[i];
-              const float e = hw_exp2(xx);
-              const float coef = M == kDeltaB ? v.y
-                                 : M == kZohFast ? __builtin_fmaf(e, w.ia[i], -w.ia[i])
-                                                 : expm1_from_exp2(xx, e) * w.ia[i];
-              h[i] = __builtin_fmaf(e, h[i], coef * (bv[i] * v.x));
-              R[i] *= e;
-              H[i] = __builtin_fmaf(R[i], v.z * cv[i], H[i]);
+              for (int i = 0; i < 4; ++i) {
+                const float xx = v.y * w.a2[i];
+                const float e = hw_exp2(xx);
+                const float coef = M == kDeltaB ? v.y
+                                   : M == kZohFast ? __builtin_fmaf(e, w.ia[i], -w.ia[i])
+                                                   : expm1_from_exp2(xx, e) * w.ia[i];
+                h[i] = __builtin_fmaf(e, h[i], coef * (bv[i] * v.x));
+                R[i] *= e;
+                H[i] = __builtin_fmaf(R[i], v.z * cv[i], H[i]);
+              }
             }
           }
         }
       }
-    }
+    };
+    if (t0 + kBlk <= w.t_end) steps(std::true_type{});
+    else steps(std::false_type{});
     // the block's chunk-start states: 4 x 64 contiguous bytes per channel
     if (w.c_ok) {
 #pragma unroll
