@@ -194,6 +194,10 @@ def bench_scan(args, dev):
         "kernel_ms_mean": round(kern_ms, 5), "kernel_ms_min": round(float(np.min(per_launch_ms)), 5),
         "kernel_ms_p10_p50_p90": [round(p10, 5), round(p50, 5), round(p90, 5)],
         "input_sets": len(sets),
+        # the first input set's arrays (as generated, bf16 as bit patterns), to pin the workload
+        "inputs": {"numpy": np.__version__,
+                   "sha256": {k2: W.sha256(x[k2]) for k2 in ("u", "delta_raw", "z", "Bt", "Ct", "A", "Dskip",
+                                                            "delta_bias")}},
         "algorithmic_bytes": nbytes,
         "roofline": {"bound": "alu", "achieved": round(achieved_tops, 3), "peak": round(VALU_PEAK_TOPS, 2),
                      "unit": "TOP/s", "frac": round(achieved_tops / VALU_PEAK_TOPS, 4), "traffic": traffic,
