@@ -94,11 +94,20 @@ def cpu_baseline_scan(cfg, x, seconds: float):
         times.append(time.perf_counter() - t0)
     t = float(np.median(times))
     gbs = cfg.algorithmic_bytes() / t / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": nth, "kind": "oracle",
-            "sample": "whole workload (B=%d D=%d N=%d L=%d, final state), fp64 C oracle, %d runs in %.1f s, "
-                      "median %.3f s per run; GB/s = the workload's algorithmic bytes / run time"
-                      % (cfg.B, cfg.D, cfg.N, cfg.L, len(times), time.perf_counter() - t_all, t),
-            "elems_per_s": round(cfg.elements / t, 1)}
+    out = {"value": round(gbs, 4), "unit": "GB/s", "cores": nth, "kind": "oracle",
+           "sample": "whole workload (B=%d D=%d N=%d L=%d%s), fp64 C oracle, %d runs in %.1f s, "
+                     "median %.3f s per run; GB/s = the workload's algorithmic bytes / run time"
+                     % (cfg.B, cfg.D, cfg.N, cfg.L, ", final state" if cfg.final_state else "", len(times),
+                        time.perf_counter() - t_all, t),
+           "elems_per_s": round(cfg.elements / t, 1)}
+    if nth > 1:
+        # one run on a single thread, for the per-core rate
+        t0 = time.perf_counter()
+        oracle.scan(*args, nthreads=1)
+        t1 = time.perf_counter() - t0
+        out["single_thread"] = {"value": round(cfg.algorithmic_bytes() / t1 / 1e9, 4), "unit": "GB/s",
+                                "run_s": round(t1, 3), "elems_per_s": round(cfg.elements / t1, 1)}
+    return out
 
 
 def source_digest(files):
