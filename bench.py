@@ -43,6 +43,7 @@ VALU_PEAK_TOPS = CUS * SIMDS_PER_CU * LANES_PER_SIMD * CLOCK_GHZ / 1e3
 # B*u, *coef, e*h + input, C*h accumulate): 6 VALU + 1 transcendental; the
 # transcendental occupies the VALU issue slot it is issued in.
 OPS_PER_UPDATE = 7
+OPS_PER_UPDATE_DELTA_B = 5   # delta A', exp2, (delta u) B, the h fma, the readout fma
 # Counter-derived HBM traffic of the scan kernel (rocprofv3 FETCH_SIZE and
 # WRITE_SIZE, scaled by the same counters on a plain copy of known size); used
 # only while the kernel sources still hash to the recorded value.
@@ -167,7 +168,7 @@ def bench_scan(args, dev):
         t = sets[i % len(sets)]
         m.scan_fwd(t["u"], t["delta_raw"], t["z"], t["Bt"], t["Ct"], t["A"], t["Dskip"], t["delta_bias"],
                    return_final_state=cfg.final_state, y=ys[i % len(sets)], final_state=hs[i % len(sets)],
-                   workspace=ws if wsb else None, stream=stream)
+                   workspace=ws if wsb else None, stream=stream, delta_b=args.delta_b)
 
     for i in range(args.warmup):
         step(i)
@@ -187,9 +188,11 @@ def bench_scan(args, dev):
     kern_ms = float(np.mean(per_launch_ms))
     nbytes = cfg.algorithmic_bytes()
     gbs = nbytes / (ms_step * 1e-3) / 1e9
-    ops = cfg.updates * OPS_PER_UPDATE
+    opu = OPS_PER_UPDATE_DELTA_B if args.delta_b else OPS_PER_UPDATE
+    ops = cfg.updates * opu
     achieved_tops = ops / (kern_ms * 1e-3) / 1e12
-    traffic, traffic_note = recorded_traffic() if cfg.name == "mamba2.8b_layer" else (None, "not measured")
+    traffic, traffic_note = (recorded_traffic() if cfg.name == "mamba2.8b_layer" and not args.delta_b
+                             else (None, "not measured"))
     p10, p50, p90 = (float(v) for v in np.percentile(per_launch_ms, [10, 50, 90]))
     line = {
         "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -197,7 +200,7 @@ def bench_scan(args, dev):
         "vs_baseline": None, "dtype": "f32", "io_dtype": cfg.dtype, "data": "synthetic",
         "config": {"workload": cfg.name, "B": cfg.B, "D": cfg.D, "N": cfg.N, "L": cfg.L,
                    "final_state": cfg.final_state, "global_batch": cfg.B, "seq_len": cfg.L,
-                   "parallelism": "none (1 GPU)"},
+                   "discretization": "delta_b" if args.delta_b else "zoh", "parallelism": "none (1 GPU)"},
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "elems_per_s": round(cfg.elements / (ms_step * 1e-3), 1),
         "kernel_ms_mean": round(kern_ms, 5), "kernel_ms_min": round(float(np.min(per_launch_ms)), 5),
@@ -211,9 +214,9 @@ def bench_scan(args, dev):
         "roofline": {"bound": "alu", "achieved": round(achieved_tops, 3), "peak": round(VALU_PEAK_TOPS, 2),
                      "unit": "TOP/s", "frac": round(achieved_tops / VALU_PEAK_TOPS, 4), "traffic": traffic,
                      "traffic_note": traffic_note,
-                     "ops_per_update": OPS_PER_UPDATE, "updates_per_launch": cfg.updates,
-                     "op": "fp32 VALU lane-operations (6 per state update + 1 exp2); peak = 256 CUs x 64 "
-                           "lanes x 2.4 GHz, non-packed",
+                     "ops_per_update": opu, "updates_per_launch": cfg.updates,
+                     "op": "fp32 VALU lane-operations (%d per state update + 1 exp2); peak = 256 CUs x 64 "
+                           "lanes x 2.4 GHz, non-packed" % (opu - 1),
                      "hbm_achieved_gbs_kernel": round(nbytes / (kern_ms * 1e-3) / 1e9, 2)},
     }
     return line, cfg, x
@@ -557,6 +560,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=128, help="decode48: timed steps (the workload has 128)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--copy-mb", type=int, default=1024)
+    ap.add_argument("--delta-b", action="store_true",
+                    help="scan workloads: the simplified rule B-bar = delta B instead of zero-order hold")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -583,7 +588,7 @@ def main():
         line = bench_ssd(args, dev)
     else:
         line, cfg, x = bench_scan(args, dev)
-        if not args.no_cpu_baseline:
+        if not args.no_cpu_baseline and not args.delta_b:
             log("cpu baseline (oracle) ...")
             line["cpu_baseline"] = cpu_baseline_scan(cfg, x, args.cpu_seconds)
     print(json.dumps(line), flush=True)
