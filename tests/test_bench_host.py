@@ -1,0 +1,68 @@
+"""Host-side checks of bench.py (no GPU): the one-GPU guard, the digest that
+ties a committed counter summary to the kernel sources, and the accounting
+of algorithmic bytes and work."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from selective_state_space_75_amd import workloads as W  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_source_digest_ignores_comments_and_spacing(tmp_path, monkeypatch):
+    a = tmp_path / "a.hip"
+    b = tmp_path / "b.hip"
+    a.write_text("int f(int x) { return x + 1; }  // one\n/* block\n comment */\n")
+    b.write_text("int  f(int x)\n{\n  return x + 1;   // other words\n}\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.source_digest(["a.hip"]) == bench.source_digest(["b.hip"])
+    b.write_text("int f(int x) { return x + 2; }\n")
+    assert bench.source_digest(["a.hip"]) != bench.source_digest(["b.hip"])
+
+
+def test_recorded_traffic_needs_matching_sources(tmp_path, monkeypatch):
+    src = tmp_path / "k.hip"
+    src.write_text("__global__ void k() {}\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    summary = tmp_path / "traffic.txt"
+    summary.write_text("# counters\nhbm_bytes_per_launch: 1234\nsource_sha256: %s\nsummary: s\n"
+                       % bench.source_digest(["k.hip"]))
+    assert bench.recorded_traffic(str(summary), ["k.hip"]) == (1234, "s")
+    src.write_text("__global__ void k() { int a = 0; }\n")
+    value, note = bench.recorded_traffic(str(summary), ["k.hip"])
+    assert value is None and "changed" in note
+    assert bench.recorded_traffic(str(tmp_path / "missing.txt"), ["k.hip"])[0] is None
+
+
+@pytest.mark.parametrize("name", sorted(W.SCAN_CONFIGS))
+def test_scan_algorithmic_bytes(name):
+    """u, delta, z read and y written per element (2 or 4 bytes each), B_t and
+    C_t per batch row, A, D and the bias per channel, and the final state."""
+    cfg = W.SCAN_CONFIGS[name]
+    e = 2 if cfg.dtype == "bf16" else 4
+    want = (cfg.B * cfg.D * cfg.L * 4 * e + 2 * cfg.B * cfg.N * cfg.L * e + cfg.D * cfg.N * 4 + 2 * cfg.D * 4
+            + (cfg.B * cfg.D * cfg.N * 4 if cfg.final_state else 0))
+    assert cfg.algorithmic_bytes() == want
+    assert cfg.updates == cfg.B * cfg.D * cfg.L * cfg.N
+
+
+def test_ssd_mfma_flops_per_chunk():
+    """Per 64-channel block and 32-step chunk: C B^T on 3 tiles of 16 x 16 with
+    K = N, and the three split products (two parts each)."""
+    cfg = W.SSD_CONFIGS["ssd_2.7b_layer"]
+    q, pb, n = 32, 64, cfg.N
+    per_chunk = 2 * (3 * 256 * n + 2 * q * pb * q + 2 * q * pb * n + 2 * n * pb * q)
+    assert bench.ssd_mfma_flops(cfg) == per_chunk * (cfg.L // q) * cfg.B * cfg.H * (cfg.P // pb)
