@@ -19,9 +19,12 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_constants.txt")
 
 
 def rel(a, b):
+    """Relative L2 distance; nan when either side holds inf or nan (which then
+    fails every bar, as a planted mistake that overflows should)."""
     a = np.asarray(a, dtype=np.float64)
     b = np.asarray(b, dtype=np.float64)
-    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+    with np.errstate(invalid="ignore", over="ignore"):
+        return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
 
 
 def np_softplus(x):
