@@ -198,6 +198,8 @@ CASES = [
     (1, 4096, 16, 320, "bf16", "bf16", 5, {}),
     (1, 4096, 16, 352, "f32", "f32", 5, {}),               # last chunk shorter (3, 3, 3, 2 blocks)
     (2, 2040, 16, 256, "bf16", "f32", 4, {"delta_b": True}),
+    (1, 4096, 7, 320, "f32", "f32", 5, {}),                 # N < 16 (states padded per lane quad)
+    (1, 4096, 16, 320, "bf16", "f32", 5, {"small_A": True}),   # one wave on the cancellation-free quotient
     # |A| below 1/16 in the first 16 channels only: those waves (and, for
     # L % 32 != 0, the first 64-channel tile) take the cancellation-free
     # quotient, the others the fast one
