@@ -172,7 +172,10 @@ struct BwdPlan {
 
 // Segments: enough (batch row, channel tile, segment) tasks to give every
 // SIMD of the chip several (at least 8192 in all), segments of at least 64
-// steps, lengths a multiple of 32.
+// steps, lengths a multiple of 32.  Where a count up to twice that minimum
+// cuts L into equal whole 32-step blocks it is taken instead, so that no
+// short last segment leaves the final round of waves half empty (2.8B
+// layer: 8 segments of 256 steps rather than 6 of 320 and one of 128).
 BwdPlan make_bwd_plan(int64_t B, int64_t D, int64_t L) {
   BwdPlan q;
   constexpr int64_t kC = mamba::kBwdChunk;
@@ -183,6 +186,10 @@ BwdPlan make_bwd_plan(int64_t B, int64_t D, int64_t L) {
   const int64_t smax = (L + 63) / 64;
   if (S > smax) S = smax;
   if (S < 1) S = 1;
+  if (L % 32 == 0) {
+    for (int64_t c = S; c <= 2 * S && c <= smax; ++c)
+      if ((L / 32) % c == 0) { S = c; break; }
+  }
   int64_t len = (L + S - 1) / S;
   len = (len + 31) / 32 * 32;     // whole 32-step staging blocks
   q.seg_len = len;
