@@ -81,7 +81,8 @@ typedef enum {
                                             always on in mamba_state_update and, in
                                             mamba_scan_fwd and mamba_scan_bwd, when
                                             in_dtype is MAMBA_F32 or for the channels
-                                            of a 16-channel tile (64 for L % 32 != 0)
+                                            of a 16-channel tile (64 for L % 8 != 0
+                                            or L < 32)
                                             with some |A| < 1/16 */
 
 /*

@@ -17,7 +17,7 @@ using mamba::Dt;
 constexpr int64_t kTile = 64;         // channels per scan workgroup
 constexpr int64_t kStage = 32;        // staging chunk of the scan kernel (steps)
 constexpr int64_t kMaxElems = int64_t(1) << 46;
-constexpr int64_t kV4Step = 32;       // the wave-tile kernel needs L to be a multiple of this
+constexpr int64_t kV4Step = 32;       // the wave-tile kernel's chunk: L at least this, and a multiple of 8
 constexpr int64_t kV4Tile = 16;       // channels per wave in the wave-tile kernel
 constexpr int64_t kGroupsPlan = 1024; // waves of the balanced split (one per SIMD on MI355X)
 constexpr size_t kHandOverBytes = kV4Tile * 16 * sizeof(float);
@@ -26,7 +26,7 @@ struct Plan {
   int64_t tiles_d = 0;
   int64_t n_chunks = 1;
   int64_t chunk_len = 0;
-  bool v4 = false;          // the wave-tile kernel (L multiple of 32)
+  bool v4 = false;          // the wave-tile kernel (L a multiple of 8, L >= 32)
   bool balanced = false;    // equal (tile x time) ranges with state hand-over
   size_t ws_bytes = 0;
   size_t off_local = 0, off_start = 0, off_sum = 0;
@@ -73,7 +73,7 @@ double v4_chunk_cost(int64_t tiles, int64_t k) {
 Plan make_plan(int64_t B, int64_t D, int64_t N, int64_t L) {
   Plan p;
   p.tiles_d = (D + kTile - 1) / kTile;
-  p.v4 = (L % kV4Step == 0) && (getenv("MAMBA_SCAN_V1") == nullptr);
+  p.v4 = (L % 8 == 0) && L >= kV4Step && (getenv("MAMBA_SCAN_V1") == nullptr);
   // Units of independent sequential work: 16-channel tiles (wave-tile
   // kernel) or 64-channel tiles (general kernel).
   const int64_t tiles = p.v4 ? B * ((D + kV4Tile - 1) / kV4Tile) : B * p.tiles_d;

@@ -45,7 +45,7 @@ struct ScanParams {
   int vec;              // rows are 16-byte aligned multiples of 8 elements
 };
 
-// Extra parameters of the wave-tile scan kernel (scan_v4.hpp, L % 32 == 0).
+// Extra parameters of the wave-tile scan kernel (scan_v4.hpp, L % 8 == 0, L >= 32).
 struct V2Params {
   int balanced;          // 1: equal (tile x time) ranges per workgroup with state hand-over
   int64_t groups;        // workgroups in balanced mode

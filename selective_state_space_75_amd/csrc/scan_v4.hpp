@@ -1,5 +1,5 @@
-// scan_v4.hpp -- main selective-scan kernel for gfx950 (L a multiple of 32,
-// 16-byte aligned rows).  Included by scan_v4_bf16.hip and scan_v4_f32.hip,
+// scan_v4.hpp -- main selective-scan kernel for gfx950 (L a multiple of 8, at
+// least 32; 16-byte aligned rows).  Included by scan_v4_bf16.hip and scan_v4_f32.hip,
 // which instantiate it for one input dtype each (they compile in parallel).  Computes what scan_fwd.hip computes ("Mamba 模型",
 // full-step flowchart nodes H to M; ZOH per "Mamba模型：高效序列建模的新突破"
 // 3.1): softplus step, ZOH discretisation, recurrence, readout, skip, gate.
@@ -165,7 +165,9 @@ struct ChunkRaw {
 //
 // kN16: N == 16.  Then every B/C lane holds a real state and all loads are
 // unconditional; otherwise lanes of absent states load zeros.
-template <bool kInBF16, bool kOutBF16, bool kReadout, bool kN16>
+// kRagged: the segment's length may not be a multiple of kCT (see below);
+// a separate instance, so that aligned lengths run the plain loop.
+template <bool kInBF16, bool kOutBF16, bool kReadout, bool kN16, bool kRagged = false>
 struct Segment {
   static __device__ __forceinline__ float run(const ScanParams& p, WaveLds& s, int64_t b, int64_t d0,
                                               int64_t t_begin, int64_t t_end, float (&h)[kNS], const Consts& k,
@@ -189,9 +191,19 @@ struct Segment {
     // flight, and its waits would then cover the newest prefetch as well.
     const void* z_src = p.z ? p.z : p.u;
 
-    const int64_t nck = (t_end - t_begin) / kCT;
+    // A segment whose length is not a multiple of kCT (the sequence's end,
+    // L % kCT != 0, L % 8 == 0) ends with a chunk shifted back to [t_end - kCT,
+    // t_end): its first `skip` steps were already scanned, so they run with
+    // delta = 0 (bias -inf: Abar = 1 and Bbar = 0 exactly, h unchanged) and
+    // their outputs are not stored.  skip is a multiple of 8, so each lane's
+    // 8 steps are either all repeated or all new.
+    const int64_t nck = kRagged ? (t_end - t_begin + kCT - 1) / kCT : (t_end - t_begin) / kCT;
     if (nck <= 0) return 0.0f;
     const int64_t t_last = t_end - kCT;
+    const int skip = kRagged ? (int)(nck * kCT - (t_end - t_begin)) : 0;
+    const bool new_steps = 8 * g >= skip;     // this lane's steps of the last chunk are not repeats
+    const bool out_last = kRagged ? (c_ok && new_steps) : c_ok;
+    const float bias_last = (kRagged && !new_steps) ? -__builtin_inff() : k.bias;
 
     auto fetch = [&](int64_t t0, ChunkRaw<kInBF16>& r) {
       t0 = t0 < t_last ? t0 : t_last;     // clamp: stays inside the segment
@@ -207,9 +219,10 @@ struct Segment {
       dst[(16 * bc_h + 8 + j) * 16 + bc_n] = at8<kInBF16>(r.bc1, j);
     };
     // Channels past D carry bias = -inf, so delta = softplus(-inf) = 0 there
-    // without a per-element select.
-    auto delta_of = [&](const ChunkRaw<kInBF16>& r, int j) {
-      return softplus(at8<kInBF16>(r.d, j) + k.bias);
+    // without a per-element select; so do the repeated steps of a shifted
+    // last chunk (bias_last).
+    auto delta_of = [&](const ChunkRaw<kInBF16>& r, int j, float bias) {
+      return softplus(at8<kInBF16>(r.d, j) + bias);
     };
     auto gate_of = [&](const Raw8<kInBF16>& z, int j) {
       const float gz = silu(at8<kInBF16>(z, j));
@@ -235,9 +248,10 @@ struct Segment {
                                        // lane g' of the quad, step 8g + j
 
     fetch(t_begin, raw[0]);
+    const float bias0 = (kRagged && nck == 1) ? bias_last : k.bias;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      dv[0][j] = delta_of(raw[0], j);
+      dv[0][j] = delta_of(raw[0], j, bias0);
       uv[0][j] = at8<kInBF16>(raw[0].u, j);
       if constexpr (kReadout) gv[0][j] = gate_of(raw[0].z, j);
       stage_bc(raw[0], 0, j);
@@ -290,6 +304,7 @@ struct Segment {
         constexpr int Q = P ^ 1;
         const int64_t t0 = t_begin + ck * kCT;
         fetch(t0 + 2 * kCT, raw[P]);            // chunk ck+2 has the parity of ck
+        const float bias_n = (kRagged && ck + 2 == nck) ? bias_last : k.bias;   // for chunk ck+1
         if constexpr (!kReadout) {
 #pragma unroll
           for (int j = 0; j < 8; ++j) dsum += dv[P][j];
@@ -318,17 +333,22 @@ struct Segment {
           }
           // Outputs of chunk ck-1 leave at mid-chunk, long before the next
           // chunk waits on its loads (stores count in the same counter).  Chunk
-          // 0 has none yet: it writes its own first chunk, which the real
+          // 0 has none yet: it writes its own first chunk (where the last
+          // chunk's outputs go when it is the only one), which the real
           // outputs overwrite later (same lane, same address, program order).
           if constexpr (kReadout && t == 16) {
-            if (c_ok) store_out(ck > 0 ? t0 - kCT : t0, o);
+            if constexpr (kRagged) {
+              if (ck > 0 || nck > 1 ? c_ok : out_last) store_out(ck > 0 ? t0 - kCT : (nck > 1 ? t0 : t_last), o);
+            } else {
+              if (c_ok) store_out(ck > 0 ? t0 - kCT : t0, o);
+            }
           }
           // Unpack chunk ck+1 (parity Q) in the second half: its loads were
           // issued at the start of chunk ck-1, so they have 1.5 chunks to land,
           // and output t/2 of chunk ck-1 has already used uv[Q], gv[Q].
           if constexpr (t >= 17 && t % 2 == 1) {
             constexpr int ju = (t - 17) / 2;
-            dv[Q][ju] = delta_of(raw[Q], ju);
+            dv[Q][ju] = delta_of(raw[Q], ju, bias_n);
             uv[Q][ju] = at8<kInBF16>(raw[Q].u, ju);
             if constexpr (kReadout) gv[Q][ju] = gate_of(raw[Q].z, ju);
             stage_bc(raw[Q], Q, ju);
@@ -378,7 +398,7 @@ struct Segment {
             const float y = (q[j] + q[8 + j]) + (q[16 + j] + q[24 + j]);
             o[j] = __builtin_fmaf(k.dskip, uv[P][j], y) * gv[P][j];
           }
-          if (c_ok) store_out(t_end - kCT, o);
+          if (out_last) store_out(t_last, o);
         }
       };
       for (int64_t ck = 0;; ck += 2) {
@@ -458,7 +478,7 @@ __device__ __forceinline__ VtGeom vt_geom(const ScanParams& p, int64_t tiles) {
   VtGeom v;
   v.tiles = tiles;
   v.nbf = p.chunk_len / kCT;
-  v.nbl = (p.L - (p.n_chunks - 1) * p.chunk_len) / kCT;
+  v.nbl = (p.L - (p.n_chunks - 1) * p.chunk_len + kCT - 1) / kCT;   // the last block may be short
   v.split = (p.n_chunks - 1) * tiles;
   return v;
 }
@@ -496,7 +516,8 @@ __device__ __forceinline__ Range balanced_range(const VtGeom& v, const V2Params&
 
 enum SegKind : int { kPlain = 0, kHead = 1, kWhole = 2, kTail = 3 };
 
-template <bool kInBF16, bool kOutBF16, bool kSummary, bool kN16>
+// kRagged: L % kCT != 0 (full pass only; every summary chunk is whole).
+template <bool kInBF16, bool kOutBF16, bool kSummary, bool kN16, bool kRagged>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void scan_v4_kernel(ScanParams p, V2Params q) {
   __shared__ WaveLds s;
   const int lane = threadIdx.x & 63;
@@ -504,7 +525,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   const int64_t D = p.D, N = p.N, L = p.L;
   const int64_t tiles_d = (D + kTile - 1) / kTile;
   const int64_t tiles = p.B * tiles_d;
-  using Full = Segment<kInBF16, kOutBF16, true, kN16>;
+  using Full = Segment<kInBF16, kOutBF16, true, kN16, kRagged>;
   using StateOnly = Segment<kInBF16, kOutBF16, false, kN16>;
 
   Range w{};
@@ -543,8 +564,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
       tile = vt - chunk * tiles;
       c_begin = chunk * p.chunk_len;
       c_end = c_begin + vt_len(v, vt) * kCT;
+      c_end = c_end < L ? c_end : L;
       t_begin = c_begin + b_lo * kCT;
       t_end = c_begin + b_hi * kCT;
+      t_end = t_end < L ? t_end : L;
     }
     const int64_t b = tile / tiles_d;
     const int64_t d0 = (tile - b * tiles_d) * kTile;
@@ -590,8 +613,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 
 template <bool kInBF16, bool kOutBF16, bool kSummary>
 hipError_t launch_t(const ScanParams& p, const V2Params& q, hipStream_t st) {
-  auto kern = p.N == 16 ? scan_v4_kernel<kInBF16, kOutBF16, kSummary, true>
-                        : scan_v4_kernel<kInBF16, kOutBF16, kSummary, false>;
+  constexpr bool kR = !kSummary;   // a ragged instance for the full pass only
+  const bool ragged = kR && p.L % kCT != 0;
+  auto kern = p.N == 16 ? (ragged ? scan_v4_kernel<kInBF16, kOutBF16, kSummary, true, kR>
+                                  : scan_v4_kernel<kInBF16, kOutBF16, kSummary, true, false>)
+                        : (ragged ? scan_v4_kernel<kInBF16, kOutBF16, kSummary, false, kR>
+                                  : scan_v4_kernel<kInBF16, kOutBF16, kSummary, false, false>);
   const int64_t tiles = p.B * ((p.D + kTile - 1) / kTile);
   int64_t grid;
   if (q.balanced) grid = q.groups;

@@ -50,7 +50,9 @@ def test_workspace_size_plan():
     # >= 1024 tiles of 16 channels: balanced split over 1024 waves, one
     # hand-over slot per wave (an 8-byte flag each, then 16 x 16 fp32 states each)
     assert ws(4, 5120, 16, 2048) == 1024 * 8 + 1024 * 16 * 16 * 4
-    assert ws(4, 5120, 16, 2040) == 0      # L % 32 != 0: general kernel, no hand-over
+    # L % 32 != 0 but L % 8 == 0: the same kernel, its last chunk shifted back
+    assert ws(4, 5120, 16, 2040) == 1024 * 8 + 1024 * 16 * 16 * 4
+    assert ws(4, 5120, 16, 2044) == 0      # L % 8 != 0: general kernel, no hand-over
     n = ws(1, 4096, 16, 131072)
     # 256 tiles of 16 channels -> 5 chunks (a summary pass of 4 x 256 waves,
     # a full pass of 5 x 256 (chunk, tile) pairs balanced over 1024 waves):
@@ -61,9 +63,10 @@ def test_workspace_size_plan():
     assert ws(2, 4096, 16, 65536) == 2 * 3 * 2 * 4096 * 16 * 4 + 3 * 2 * 4096 * 4 + 1024 * 8 + 1024 * 16 * 16 * 4
     assert ws(1, 1024, 16, 65536) == 2 * 17 * 1024 * 16 * 4 + 17 * 1024 * 4 + 1024 * 8 + 1024 * 16 * 16 * 4
     assert ws(8, 1536, 16, 65536) == 0
-    # the general kernel (L % 32 != 0) plans with 64-channel tiles: 16 chunks
-    n = ws(1, 4096, 16, 131072 - 8)
-    assert n == 2 * 16 * 4096 * 16 * 4 + 16 * 4096 * 4
+    # a ragged last chunk (L % 32 == 24) plans like L = 131072: 5 chunks
+    assert ws(1, 4096, 16, 131072 - 8) == n
+    # the general kernel (L % 8 != 0) plans with 64-channel tiles: 16 chunks
+    assert ws(1, 4096, 16, 131072 - 4) == 2 * 16 * 4096 * 16 * 4 + 16 * 4096 * 4
     assert _lib.lib().mamba_scan_workspace_size(0, 1, 1, 1) == ctypes.c_size_t(-1).value
     assert _lib.lib().mamba_scan_workspace_size(1, 1, 17, 1) == ctypes.c_size_t(-1).value
 

@@ -183,7 +183,7 @@ CASES = [
     (2, 96, 16, 160, "bf16", "f32", None, {"accurate": True}),
     (2, 64, 16, 128, "f32", "f32", None, {"zero_A": True}),
     (1, 64, 16, 3000, "bf16", "bf16", 5, {"zero_A": True}),
-    # sequence lengths that are multiples of 32 take the 8-wave kernel
+    # L a multiple of 32
     (1, 64, 16, 3072, "bf16", "bf16", 5, {"zero_A": True}),
     (2, 100, 16, 320, "bf16", "f32", 3, {}),
     (2, 100, 16, 320, "f32", "f32", 3, {"delta_b": True}),
@@ -201,13 +201,24 @@ CASES = [
     (1, 4096, 7, 320, "f32", "f32", 5, {}),                 # N < 16 (states padded per lane quad)
     (1, 4096, 16, 320, "bf16", "f32", 5, {"small_A": True}),   # one wave on the cancellation-free quotient
     # |A| below 1/16 in the first 16 channels only: those waves (and, for
-    # L % 32 != 0, the first 64-channel tile) take the cancellation-free
+    # L % 8 != 0, the first 64-channel tile) take the cancellation-free
     # quotient, the others the fast one
     (2, 48, 16, 128, "bf16", "bf16", None, {"small_A": True}),
     (2, 80, 16, 100, "bf16", "f32", None, {"small_A": True}),
     # fewer tiles than waves: one pass per tile, ragged last tile
     (4, 2040, 16, 64, "bf16", "bf16", None, {}),
     (8, 1024, 16, 256, "f32", "f32", None, {}),
+    # L % 8 == 0 but L % 32 != 0: the wave-tile kernel with its last chunk
+    # shifted back to end at L (8, 16 or 24 repeated steps)
+    (2, 100, 16, 40, "bf16", "bf16", None, {}),
+    (1, 33, 16, 48, "f32", "f32", None, {"no_z": True}),
+    (2, 64, 16, 56, "bf16", "f32", None, {"delta_b": True}),
+    (2, 70, 16, 1000, "f32", "f32", None, {"accurate": True}),
+    (1, 64, 16, 200, "bf16", "bf16", 3, {"small_A": True}),
+    (2, 10240, 16, 168, "bf16", "bf16", None, {}),          # balanced, the tail block 8 steps
+    (1, 16384 + 64 * 60, 16, 104, "f32", "f32", None, {}),
+    (1, 4096, 16, 328, "bf16", "f32", 5, {}),              # chunked, balanced, ragged last chunk
+    (1, 4096, 16, 344, "f32", "f32", 5, {"delta_b": True}),
 ]
 
 
@@ -251,8 +262,9 @@ def test_ragged_and_options(case, dev, monkeypatch):
     assert e <= (2e-3 if dt == "bf16" else 1e-5)
 
 
-@pytest.mark.parametrize("shape", [(2, 10240, 16, 160, None), (1, 4096, 16, 352, 5)],
-                         ids=["tiles", "chunk_tiles"])
+@pytest.mark.parametrize("shape", [(2, 10240, 16, 160, None), (1, 4096, 16, 352, 5), (2, 10240, 16, 168, None),
+                                   (1, 4096, 16, 328, 5)],
+                         ids=["tiles", "chunk_tiles", "tiles_ragged_L", "chunk_tiles_ragged_L"])
 def test_handover_fallback_matches(shape, dev, monkeypatch):
     """With the hand-over wait forced to zero every split tile recomputes its
     state at the cut (from the start of its chunk) instead of receiving it;
