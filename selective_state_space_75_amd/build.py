@@ -30,6 +30,10 @@ def sources():
 
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wall"]
+# Per-file additions.  ssd.hip: MFMA accumulators in ordinary VGPRs, so the
+# state the SSD kernels update with both MFMA and VALU instructions is not
+# copied between AGPRs and VGPRs every chunk.
+FILE_FLAGS = {"ssd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 NOISE = "is not a recognized feature for this target"
 
 
@@ -48,7 +52,8 @@ def build(verbose: bool = False) -> str:
         jobs = []
         for src in sources():
             obj = os.path.join(tmpdir, os.path.basename(src) + ".o")
-            jobs.append(([HIPCC] + FLAGS + incs + ["-c", "-o", obj, src], obj))
+            extra = FILE_FLAGS.get(os.path.basename(src), [])
+            jobs.append(([HIPCC] + FLAGS + extra + incs + ["-c", "-o", obj, src], obj))
         workers = max(1, min(len(jobs), os.cpu_count() or 1, 16))
         with concurrent.futures.ThreadPoolExecutor(workers) as ex:
             futs = []

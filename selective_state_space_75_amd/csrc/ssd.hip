@@ -144,8 +144,34 @@ __global__ __launch_bounds__(256) void ssd_chunk_kernel(SsdParams p) {
     uint2 z[2];          // channel pc, steps 16 tm + 4 g .. + 3
     uint32_t dt;         // step l of the chunk after this one (wave 3, lanes < 32)
   };
+  // A chunk that lies wholly inside the rows (and rows that allow 8- and
+  // 16-byte loads) is fetched without per-load conditions: a uniform base per
+  // array and chunk plus this lane's fixed 32-bit byte offset, which the
+  // compiler turns into scalar-base loads.  The offsets need L < 2^24.
+  const bool off32 = L < (int64_t(1) << 24);
+  const uint32_t voff_bc = (uint32_t)((4 * nq) * L + 4 * tb4) * 2u;
+  const uint32_t voff_x = (uint32_t)(px * L + 8 * tb8) * 2u;
+  const uint32_t voff_z = (uint32_t)(pc * L + 4 * g) * 2u;
+  const uint16_t* xblk = static_cast<const uint16_t*>(p.x) + (b * D + d0) * L;
+  const uint16_t* zblk = p.z ? static_cast<const uint16_t*>(p.z) + (b * D + d0) * L : nullptr;
+  auto at_off = [](const uint16_t* base, uint32_t off) { return reinterpret_cast<const char*>(base) + off; };
   auto fetch = [&](int64_t t0, Raw& R) {
     const int64_t valid = L - t0;
+    if (vecp && off32 && valid >= kQ) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (kN == 128 || 4 * nq < kN) {   // rows past kN are not staged
+          R.c[j] = *reinterpret_cast<const uint2*>(at_off(Crow + j * L + t0, voff_bc));
+          R.bb[j] = *reinterpret_cast<const uint2*>(at_off(Brow + j * L + t0, voff_bc));
+        }
+      }
+      R.x = *reinterpret_cast<const uint4*>(at_off(xblk + t0, voff_x));
+#pragma unroll
+      for (int tm = 0; tm < 2; ++tm)
+        R.z[tm] = zblk ? *reinterpret_cast<const uint2*>(at_off(zblk + t0 + 16 * tm, voff_z)) : make_uint2(0u, 0u);
+      R.dt = (w == 3 && l < valid - kQ && l < kQ) ? (uint32_t)dtrow[t0 + kQ + l] : 0u;
+      return;
+    }
     const bool vec = vecp && valid >= kQ;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -241,7 +267,9 @@ __global__ __launch_bounds__(256) void ssd_chunk_kernel(SsdParams p) {
   }
 
   const int64_t ck0 = t_begin / kQ, nchunks = (t_end + kQ - 1) / kQ;
-  Raw cur, nxt;
+  // One register set: once staged (and past the barrier that follows), it
+  // receives the next chunk's loads, so nothing is copied between chunks.
+  Raw cur;
   fetch(t_begin, cur);
   if (w == 3) chunk_params(t_begin, (l < L - t_begin && l < kQ) ? (uint32_t)dtrow[t_begin + l] : 0u, (int)(ck0 & 1));
   for (int64_t c = ck0; c < nchunks; ++c) {
@@ -250,10 +278,11 @@ __global__ __launch_bounds__(256) void ssd_chunk_kernel(SsdParams p) {
     const int cb = (int)(c & 1);
     __syncthreads();                       // the previous chunk's LDS reads are done
     stage(cur);
-    const uint2 zc[2] = {cur.z[0], cur.z[1]};
+    const uint2 zc[2] = {cur.z[0], cur.z[1]};   // cur receives the next chunk below
+    const uint4 xc = cur.x;
     const uint32_t dtn = cur.dt;
     __syncthreads();
-    if (c + 1 < nchunks) fetch(t0 + kQ, nxt);
+    if (c + 1 < nchunks) fetch(t0 + kQ, cur);
 
     // ---- S = C B^T on the three lower 16 x 16 tiles and G from it (waves
     // 0..2); the next chunk's step sizes, decays and coefficients (wave 3)
@@ -275,7 +304,7 @@ __global__ __launch_bounds__(256) void ssd_chunk_kernel(SsdParams p) {
       chunk_params(t0 + kQ, dtn, cb ^ 1);
     }
     {
-      const uint32_t xw[4] = {cur.x.x, cur.x.y, cur.x.z, cur.x.w};
+      const uint32_t xw[4] = {xc.x, xc.y, xc.z, xc.w};
       uint32_t hw[4], lw[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -368,7 +397,6 @@ __global__ __launch_bounds__(256) void ssd_chunk_kernel(SsdParams p) {
         }
       }
     }
-    if (c + 1 < nchunks) cur = nxt;
   }
   if (p.final_state && seg == p.S - 1) {
     float* fs = p.final_state + (b * D + d0 + pc) * N;
