@@ -146,6 +146,9 @@ def bench_scan(args, dev):
     import selective_state_space_75_amd as m
     from selective_state_space_75_amd import workloads as W
     cfg = W.SCAN_CONFIGS[args.workload]
+    if args.seq_len:   # same batch, channels, states, dtype and seed at another length
+        cfg = W.ScanConfig("%s_L%d" % (cfg.name, args.seq_len), cfg.B, cfg.D, cfg.N, args.seq_len, cfg.dtype,
+                           cfg.seed, cfg.dskip, cfg.final_state)
     log("workload %s: B=%d D=%d N=%d L=%d %s" % (cfg.name, cfg.B, cfg.D, cfg.N, cfg.L, cfg.dtype))
     x = W.scan_inputs(cfg)
     sets = []
@@ -560,6 +563,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=128, help="decode48: timed steps (the workload has 128)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--copy-mb", type=int, default=1024)
+    ap.add_argument("--seq-len", type=int, default=0,
+                    help="scan workloads: another sequence length L (same B, D, N, dtype, seed)")
     ap.add_argument("--delta-b", action="store_true",
                     help="scan workloads: the simplified rule B-bar = delta B instead of zero-order hold")
     args = ap.parse_args()
