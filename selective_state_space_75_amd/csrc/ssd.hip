@@ -97,7 +97,7 @@ __device__ __forceinline__ uint2 ld_row4(const uint16_t* row, int64_t t, bool ve
 }
 
 template <int kN, bool kOutBF16, bool kDeltaB>
-__global__ __launch_bounds__(256) void ssd_chunk_kernel(SsdParams p) {
+__global__ __launch_bounds__(256, 3) void ssd_chunk_kernel(SsdParams p) {
   __shared__ SsdLds<kN> S;
   constexpr int kNT = kN / 16;     // 16-row tiles of the state
   constexpr int kNK = kN / 32;     // 32-wide K blocks over the states
@@ -145,30 +145,39 @@ __global__ __launch_bounds__(256) void ssd_chunk_kernel(SsdParams p) {
     uint32_t dt;         // step l of the chunk after this one (wave 3, lanes < 32)
   };
   // A chunk that lies wholly inside the rows (and rows that allow 8- and
-  // 16-byte loads) is fetched without per-load conditions: a uniform base per
-  // array and chunk plus this lane's fixed 32-bit byte offset, which the
-  // compiler turns into scalar-base loads.  The offsets need L < 2^24.
+  // 16-byte loads) is fetched without per-load conditions, as buffer loads:
+  // a descriptor per array (the batch row's B_t / C_t, the block's x / z
+  // rows), this lane's fixed 32-bit byte offset, and a uniform offset per
+  // row and chunk.  Byte ranges must fit 32 bits: L < 2^24.
   const bool off32 = L < (int64_t(1) << 24);
+  constexpr int kRawWord3 = 0x00020000;   // 32-bit data format, as raw buffer loads need
   const uint32_t voff_bc = (uint32_t)((4 * nq) * L + 4 * tb4) * 2u;
   const uint32_t voff_x = (uint32_t)(px * L + 8 * tb8) * 2u;
   const uint32_t voff_z = (uint32_t)(pc * L + 4 * g) * 2u;
-  const uint16_t* xblk = static_cast<const uint16_t*>(p.x) + (b * D + d0) * L;
-  const uint16_t* zblk = p.z ? static_cast<const uint16_t*>(p.z) + (b * D + d0) * L : nullptr;
-  auto at_off = [](const uint16_t* base, uint32_t off) { return reinterpret_cast<const char*>(base) + off; };
+  const int bc_bytes = (int)(uint32_t)(off32 ? N * L * 2 : 0);
+  const int blk_bytes = (int)(uint32_t)(off32 ? kP * L * 2 : 0);
+  const __amdgpu_buffer_rsrc_t rsC = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Crow), 0, bc_bytes, kRawWord3);
+  const __amdgpu_buffer_rsrc_t rsB = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Brow), 0, bc_bytes, kRawWord3);
+  const __amdgpu_buffer_rsrc_t rsX = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(static_cast<const uint16_t*>(p.x) + (b * D + d0) * L), 0, blk_bytes, kRawWord3);
+  const __amdgpu_buffer_rsrc_t rsZ = __builtin_amdgcn_make_buffer_rsrc(
+      p.z ? const_cast<uint16_t*>(static_cast<const uint16_t*>(p.z) + (b * D + d0) * L) : nullptr, 0, blk_bytes, kRawWord3);
   auto fetch = [&](int64_t t0, Raw& R) {
     const int64_t valid = L - t0;
     if (vecp && off32 && valid >= kQ) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         if (kN == 128 || 4 * nq < kN) {   // rows past kN are not staged
-          R.c[j] = *reinterpret_cast<const uint2*>(at_off(Crow + j * L + t0, voff_bc));
-          R.bb[j] = *reinterpret_cast<const uint2*>(at_off(Brow + j * L + t0, voff_bc));
+          const int so = (int)((j * L + t0) * 2);
+          R.c[j] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rsC, voff_bc, so, 0));
+          R.bb[j] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rsB, voff_bc, so, 0));
         }
       }
-      R.x = *reinterpret_cast<const uint4*>(at_off(xblk + t0, voff_x));
+      R.x = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsX, voff_x, (int)(t0 * 2), 0));
 #pragma unroll
       for (int tm = 0; tm < 2; ++tm)
-        R.z[tm] = zblk ? *reinterpret_cast<const uint2*>(at_off(zblk + t0 + 16 * tm, voff_z)) : make_uint2(0u, 0u);
+        R.z[tm] = p.z ? __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rsZ, voff_z, (int)((t0 + 16 * tm) * 2), 0))
+                      : make_uint2(0u, 0u);
       R.dt = (w == 3 && l < valid - kQ && l < kQ) ? (uint32_t)dtrow[t0 + kQ + l] : 0u;
       return;
     }
@@ -317,20 +326,6 @@ __global__ __launch_bounds__(256) void ssd_chunk_kernel(SsdParams p) {
       *reinterpret_cast<uint4*>(&S.Xh[px][8 * tb8]) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
       *reinterpret_cast<uint4*>(&S.Xl[px][8 * tb8]) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
     }
-    // the entering state as B operands of C H: K block kb holds states
-    // 32 kb + 4 g + e (tile 2 kb) and 32 kb + 16 + 4 g + e (tile 2 kb + 1)
-    bf16x8 Hh[kNK], Hl[kNK];
-#pragma unroll
-    for (int kb = 0; kb < kNK; ++kb) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float v = (e < 4) ? Hs[2 * kb][e] : Hs[2 * kb + 1][e - 4];
-        uint16_t hi, lo;
-        split_bf16(v, hi, lo);
-        Hh[kb][e] = __builtin_bit_cast(__bf16, hi);
-        Hl[kb][e] = __builtin_bit_cast(__bf16, lo);
-      }
-    }
     __syncthreads();
 
     // ---- y = G x + exp(cum_t) C H + D x for the wave's 16 channels
@@ -341,11 +336,26 @@ __global__ __launch_bounds__(256) void ssd_chunk_kernel(SsdParams p) {
       Yd[tm] = mfma(lds8(&S.Gh[16 * tm + r][8 * g]), xb, f32x4{0.0f, 0.0f, 0.0f, 0.0f});
       Yd[tm] = mfma(lds8(&S.Gl[16 * tm + r][8 * g]), xb, Yd[tm]);
       Yo[tm] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    // the entering state as B operands of C H, one K block at a time (its
+    // split overlaps the products of the block before): K block kb holds
+    // states 32 kb + 4 g + e (tile 2 kb) and 32 kb + 16 + 4 g + e (tile 2 kb + 1)
 #pragma unroll
-      for (int kb = 0; kb < kNK; ++kb) {
+    for (int kb = 0; kb < kNK; ++kb) {
+      bf16x8 hh, hl;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = (e < 4) ? Hs[2 * kb][e] : Hs[2 * kb + 1][e - 4];
+        uint16_t hi, lo;
+        split_bf16(v, hi, lo);
+        hh[e] = __builtin_bit_cast(__bf16, hi);
+        hl[e] = __builtin_bit_cast(__bf16, lo);
+      }
+#pragma unroll
+      for (int tm = 0; tm < 2; ++tm) {
         const bf16x8 ca = lds4x2(&S.Cc[16 * tm + r][32 * kb + 4 * g], &S.Cc[16 * tm + r][32 * kb + 16 + 4 * g]);
-        Yo[tm] = mfma(ca, Hh[kb], Yo[tm]);
-        Yo[tm] = mfma(ca, Hl[kb], Yo[tm]);
+        Yo[tm] = mfma(ca, hh, Yo[tm]);
+        Yo[tm] = mfma(ca, hl, Yo[tm]);
       }
     }
     // ---- H <- exp(cum_last) H + B^T (w o x)
