@@ -141,14 +141,22 @@ def recorded_traffic(path=TRAFFIC_FILE, sources=SCAN_SOURCES):
 
 
 # ----------------------------------------------------------------------------- scan benchmark
+def scan_config(workload, seq_len=0):
+    """The scan workload's configuration; seq_len > 0 keeps its batch,
+    channels, states, dtype and seed at another sequence length."""
+    from selective_state_space_75_amd import workloads as W
+    cfg = W.SCAN_CONFIGS[workload]
+    if seq_len:
+        cfg = W.ScanConfig("%s_L%d" % (cfg.name, seq_len), cfg.B, cfg.D, cfg.N, seq_len, cfg.dtype,
+                           cfg.seed, cfg.dskip, cfg.final_state)
+    return cfg
+
+
 def bench_scan(args, dev):
     import torch
     import selective_state_space_75_amd as m
     from selective_state_space_75_amd import workloads as W
-    cfg = W.SCAN_CONFIGS[args.workload]
-    if args.seq_len:   # same batch, channels, states, dtype and seed at another length
-        cfg = W.ScanConfig("%s_L%d" % (cfg.name, args.seq_len), cfg.B, cfg.D, cfg.N, args.seq_len, cfg.dtype,
-                           cfg.seed, cfg.dskip, cfg.final_state)
+    cfg = scan_config(args.workload, args.seq_len)
     log("workload %s: B=%d D=%d N=%d L=%d %s" % (cfg.name, cfg.B, cfg.D, cfg.N, cfg.L, cfg.dtype))
     x = W.scan_inputs(cfg)
     sets = []

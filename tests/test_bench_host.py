@@ -66,3 +66,15 @@ def test_ssd_mfma_flops_per_chunk():
     q, pb, n = 32, 64, cfg.N
     per_chunk = 2 * (3 * 256 * n + 2 * q * pb * q + 2 * q * pb * n + 2 * n * pb * q)
     assert bench.ssd_mfma_flops(cfg) == per_chunk * (cfg.L // q) * cfg.B * cfg.H * (cfg.P // pb)
+
+
+def test_scan_config_seq_len_override():
+    """--seq-len keeps the workload's batch, channels, states, dtype and seed
+    and changes only L (and the name, so no recorded traffic applies)."""
+    base = bench.scan_config("mamba2.8b_layer")
+    assert base is W.SCAN_CONFIGS["mamba2.8b_layer"]
+    cfg = bench.scan_config("mamba2.8b_layer", 2040)
+    assert (cfg.B, cfg.D, cfg.N, cfg.dtype, cfg.seed, cfg.final_state) == \
+        (base.B, base.D, base.N, base.dtype, base.seed, base.final_state)
+    assert cfg.L == 2040 and cfg.name != base.name
+    assert cfg.updates == base.updates // 2048 * 2040
