@@ -440,17 +440,22 @@ __device__ __forceinline__ void unroll_for(F&& f) {
   }
 }
 
+// Rows of 32 bf16 with no padding; the 16-byte block q of row n is stored at
+// block q ^ swz(n), so that 16 lanes reading block q of rows n .. n + 15 (an
+// MFMA operand) or writing 4 blocks of 4 rows touch every LDS bank once.
+__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
+
 template <int kN>
 struct StateLds {
-  uint16_t BT[2][kN][kQ + kPad];   // B_t [state][step]
-  uint16_t Xh[2][kP][kQ + kPad];   // w o x [channel][step], high part
-  uint16_t Xl[2][kP][kQ + kPad];   //                        remainder
+  uint16_t BT[2][kN][kQ];          // B_t [state][step], swizzled blocks
+  uint16_t Xh[2][kP][kQ];          // w o x [channel][step], high part, swizzled blocks
+  uint16_t Xl[2][kP][kQ];          //                        remainder
   float Wt[kPiece];                // w of the piece's steps
   float wave_sum[2][4];
 };
 
 template <int kN, bool kDeltaB, bool kVec>
-__global__ __launch_bounds__(256) void ssd_state_kernel(SsdParams p) {
+__global__ __launch_bounds__(256, 4) void ssd_state_kernel(SsdParams p) {
   __shared__ StateLds<kN> S;
   constexpr int kNT = kN / 16;
   constexpr int kBR = kN / 64;                               // B rows per staging thread
@@ -556,16 +561,18 @@ __global__ __launch_bounds__(256) void ssd_state_kernel(SsdParams p) {
         hw[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
         lw[i] = (uint32_t)l0 | ((uint32_t)l1 << 16);
       }
-      *reinterpret_cast<uint4*>(&S.Xh[buf][lr][8 * lq]) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-      *reinterpret_cast<uint4*>(&S.Xl[buf][lr][8 * lq]) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+      const int wq = 8 * (lq ^ swz(lr));                 // rows lr + 64 i share the swizzle
+      *reinterpret_cast<uint4*>(&S.Xh[buf][lr][wq]) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      *reinterpret_cast<uint4*>(&S.Xl[buf][lr][wq]) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
 #pragma unroll
-      for (int i = 0; i < kBR; ++i) *reinterpret_cast<uint4*>(&S.BT[buf][lr + 64 * i][8 * lq]) = o.bt[i];
+      for (int i = 0; i < kBR; ++i) *reinterpret_cast<uint4*>(&S.BT[buf][lr + 64 * i][wq]) = o.bt[i];
       // the other buffer's readers finished before they reached this barrier
       __syncthreads();
-      const bf16x8 xh = lds8(&S.Xh[buf][pc][8 * g]), xl = lds8(&S.Xl[buf][pc][8 * g]);
+      const int rq = 8 * (g ^ swz(r));                   // rows pc and 16 tn + r have r's swizzle
+      const bf16x8 xh = lds8(&S.Xh[buf][pc][rq]), xl = lds8(&S.Xl[buf][pc][rq]);
 #pragma unroll
       for (int tn = 0; tn < kNT; ++tn) {
-        const bf16x8 bt = lds8(&S.BT[buf][16 * tn + r][8 * g]);
+        const bf16x8 bt = lds8(&S.BT[buf][16 * tn + r][rq]);
         Hs[tn] = mfma(bt, xh, Hs[tn]);
         Hs[tn] = mfma(bt, xl, Hs[tn]);
       }
