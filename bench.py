@@ -78,37 +78,95 @@ def cpu_threads():
 
 
 # ----------------------------------------------------------------------------- CPU oracle baseline
-def cpu_baseline_scan(cfg, x, seconds: float):
-    """Time the fp64 oracle (as it stands) on the whole workload, repeated
-    until about `seconds` of wall time; report the median run."""
+def cpu_baseline_scan(cfg, x, seconds: float, channels: int = 0, single_channels: int = 0):
+    """Time the fp64 oracle (as it stands) on a bounded sample of the workload,
+    repeated until about `seconds` of wall time; report the median run.
+
+    channels > 0 samples the first `channels` channels of batch row 0 (whole
+    sequence) instead of the whole workload; single_channels, likewise, the
+    sample of the one-thread run.  Rates are per unit of work (bytes and
+    elements scale with the sampled channels), so they compare with the
+    whole-workload GPU rate."""
     import oracle
     from selective_state_space_75_amd import workloads as W
     nth = cpu_threads()
     f64 = lambda a: W.as_f32(a).astype(np.float64)  # noqa: E731
-    args = (f64(x["u"]), f64(x["delta_raw"]), f64(x["z"]), f64(x["Bt"]), f64(x["Ct"]),
-            x["A"].astype(np.float64), x["Dskip"].astype(np.float64), x["delta_bias"].astype(np.float64))
+    total_ch = cfg.B * cfg.D
+
+    def args_for(nch):
+        if nch <= 0 or nch >= total_ch:
+            return (f64(x["u"]), f64(x["delta_raw"]), f64(x["z"]), f64(x["Bt"]), f64(x["Ct"]),
+                    x["A"].astype(np.float64), x["Dskip"].astype(np.float64),
+                    x["delta_bias"].astype(np.float64)), 1.0, "whole workload"
+        nch = min(nch, cfg.D)
+        sl = lambda a: f64(a[0:1, 0:nch, :])  # noqa: E731
+        return ((sl(x["u"]), sl(x["delta_raw"]), sl(x["z"]), f64(x["Bt"][0:1]), f64(x["Ct"][0:1]),
+                 x["A"][0:nch].astype(np.float64), x["Dskip"][0:nch].astype(np.float64),
+                 x["delta_bias"][0:nch].astype(np.float64)), nch / total_ch,
+                "channels 0..%d of batch row 0 (%.4g of the workload), whole sequence" % (nch - 1, nch / total_ch))
+
+    args, frac, what = args_for(channels)
     times = []
     t_all = time.perf_counter()
-    while not times or (time.perf_counter() - t_all < seconds and len(times) < 200):
+    while len(times) < 3 or (time.perf_counter() - t_all < seconds and len(times) < 200):
         t0 = time.perf_counter()
         oracle.scan(*args, nthreads=nth)
         times.append(time.perf_counter() - t0)
     t = float(np.median(times))
-    gbs = cfg.algorithmic_bytes() / t / 1e9
-    out = {"value": round(gbs, 4), "unit": "GB/s", "cores": nth, "kind": "oracle",
-           "sample": "whole workload (B=%d D=%d N=%d L=%d%s), fp64 C oracle, %d runs in %.1f s, "
-                     "median %.3f s per run; GB/s = the workload's algorithmic bytes / run time"
-                     % (cfg.B, cfg.D, cfg.N, cfg.L, ", final state" if cfg.final_state else "", len(times),
+    nbytes = cfg.algorithmic_bytes() * frac
+    out = {"value": round(nbytes / t / 1e9, 4), "unit": "GB/s", "cores": nth, "kind": "oracle",
+           "sample": "%s (B=%d D=%d N=%d L=%d%s), fp64 C oracle, %d runs in %.1f s, median %.3f s per run; "
+                     "GB/s = the sample's share of the workload's algorithmic bytes / run time"
+                     % (what, cfg.B, cfg.D, cfg.N, cfg.L, ", final state" if cfg.final_state else "", len(times),
                         time.perf_counter() - t_all, t),
-           "elems_per_s": round(cfg.elements / t, 1)}
+           "elems_per_s": round(cfg.elements * frac / t, 1),
+           "updates_per_s": round(cfg.updates * frac / t, 1)}
+    del args
     if nth > 1:
         # one run on a single thread, for the per-core rate
+        args1, frac1, what1 = args_for(single_channels if single_channels else channels)
         t0 = time.perf_counter()
-        oracle.scan(*args, nthreads=1)
+        oracle.scan(*args1, nthreads=1)
         t1 = time.perf_counter() - t0
-        out["single_thread"] = {"value": round(cfg.algorithmic_bytes() / t1 / 1e9, 4), "unit": "GB/s",
-                                "run_s": round(t1, 3), "elems_per_s": round(cfg.elements / t1, 1)}
+        out["single_thread"] = {"value": round(cfg.algorithmic_bytes() * frac1 / t1 / 1e9, 4), "unit": "GB/s",
+                                "run_s": round(t1, 3), "sample": what1,
+                                "elems_per_s": round(cfg.elements * frac1 / t1, 1),
+                                "updates_per_s": round(cfg.updates * frac1 / t1, 1)}
     return out
+
+
+def cpu_baseline_decode(cfg, layers=(0, 47), steps: int = 128):
+    """The fp64 oracle's decode step on layers {0, 47} x `steps` steps (step-major
+    within the sample), extrapolated to all layers: the sample is 2 of the 48
+    layers, so the whole workload takes 24 times as long."""
+    import oracle
+    from selective_state_space_75_amd import workloads as W
+    nth = cpu_threads()
+    f64 = lambda a: W.as_f32(a).astype(np.float64)  # noqa: E731
+    prm, states = {}, {}
+    for l in layers:
+        A, Dskip, bias, st0 = W.decode_layer_params(cfg, l)
+        prm[l] = (A.astype(np.float64), Dskip.astype(np.float64), bias.astype(np.float64))
+        states[l] = st0.astype(np.float64)
+    t_run = 0.0
+    for s in range(steps):
+        for l in layers:
+            si = W.decode_step_inputs(cfg, l, s)
+            ins = (f64(si["u"]), f64(si["delta_raw"]), f64(si["z"]), f64(si["Bt"]), f64(si["Ct"]))
+            t0 = time.perf_counter()
+            _, states[l] = oracle.state_update(states[l], *ins, *prm[l], nthreads=nth)
+            t_run += time.perf_counter() - t0
+    scale = cfg.layers / len(layers)
+    per_ls = cfg.bytes_per_layer_step()
+    total_s = t_run * scale
+    return {"value": round(per_ls * len(layers) * steps / t_run / 1e9, 4), "unit": "GB/s", "cores": nth,
+            "kind": "oracle",
+            "sample": "layers %s x %d steps of the decode workload (B=%d D=%d N=%d), fp64 C oracle, %.1f s; "
+                      "extrapolated x%g to all %d layers" % (list(layers), steps, cfg.B, cfg.D, cfg.N, t_run, scale,
+                                                            cfg.layers),
+            "extrapolated": True, "extrapolated_total_s": round(total_s, 2),
+            "tokens_per_s": round(cfg.B * steps / total_s, 2),
+            "layer_step_ms": round(t_run * 1e3 / (len(layers) * steps), 3)}
 
 
 def source_digest(files):
@@ -559,12 +617,68 @@ def copy_calibration(args, dev):
                       "launches": args.steps}), flush=True)
 
 
+def sub_args(args, **kw):
+    """A copy of the command-line options for one of the nested workloads."""
+    a = argparse.Namespace(**vars(args))
+    a.seq_len = 0
+    a.delta_b = False
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def headline(args, dev):
+    """The default run: the 2.8B-layer scan line, with the other workloads of
+    the path nested under "workloads" (each with its own roofline and CPU
+    oracle baseline): the 48-layer decode step, the 130M layer and the
+    batch-1 long sequence."""
+    import torch
+    from selective_state_space_75_amd import workloads as W
+    line, cfg, x = bench_scan(sub_args(args, workload="mamba2.8b_layer"), dev)
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle), mamba2.8b_layer ...")
+        line["cpu_baseline"] = cpu_baseline_scan(cfg, x, args.cpu_seconds)
+    del x
+    if args.headline_only:
+        return line
+    nested = {}
+    torch.cuda.empty_cache()
+    dec = bench_decode(sub_args(args, warmup=min(args.warmup, 4)), dev)
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle), decode48 layers {0, 47} ...")
+        dec["cpu_baseline"] = cpu_baseline_decode(W.DECODE_CONFIGS["decode48"])
+    nested["decode48"] = dec
+    torch.cuda.empty_cache()
+    # (workload, timed steps, input sets, oracle sample channels, one-thread sample channels)
+    for name, steps, sets, ch, ch1 in (("mamba130m_layer", min(args.steps, 50), 3, 0, 0),
+                                       ("long_b1", min(args.steps, 10), 1, 512, 64)):
+        ln, c, xx = bench_scan(sub_args(args, workload=name, steps=steps, sets=sets,
+                                        warmup=min(args.warmup, 3)), dev)
+        if not args.no_cpu_baseline:
+            log("cpu baseline (oracle), %s ..." % name)
+            ln["cpu_baseline"] = cpu_baseline_scan(c, xx, min(args.cpu_seconds, 6.0), channels=ch,
+                                                   single_channels=ch1)
+        del xx
+        for k in ("metric", "n_gpus", "higher_is_better", "scaling", "data", "inputs"):
+            ln.pop(k, None)
+        nested[name] = ln
+        torch.cuda.empty_cache()
+    for k in ("metric", "n_gpus", "higher_is_better", "scaling", "data"):
+        nested["decode48"].pop(k, None)
+    line["workloads"] = nested
+    return line
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="mamba2.8b_layer")
+    ap.add_argument("--workload", default=None,
+                    help="one workload only (default: the 2.8B-layer line with the decode, 130M-layer and "
+                         "batch-1 long workloads nested)")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="default run without the nested workloads")
     ap.add_argument("--sets", type=int, default=3, help="distinct input sets cycled over steps")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -589,8 +703,12 @@ def main():
         copy_calibration(args, dev)
         return
     from selective_state_space_75_amd import workloads as W
-    if args.workload == "decode48":
+    if args.workload is None:
+        line = headline(args, dev)
+    elif args.workload == "decode48":
         line = bench_decode(args, dev)
+        if not args.no_cpu_baseline:
+            line["cpu_baseline"] = cpu_baseline_decode(W.DECODE_CONFIGS["decode48"])
     elif args.workload == "bwd_2.8b_layer":
         line = bench_bwd(args, dev)
     elif args.workload in W.CONV_CONFIGS:
@@ -603,7 +721,9 @@ def main():
         line, cfg, x = bench_scan(args, dev)
         if not args.no_cpu_baseline and not args.delta_b:
             log("cpu baseline (oracle) ...")
-            line["cpu_baseline"] = cpu_baseline_scan(cfg, x, args.cpu_seconds)
+            big = cfg.updates > 2e9
+            line["cpu_baseline"] = cpu_baseline_scan(cfg, x, args.cpu_seconds, channels=512 if big else 0,
+                                                     single_channels=64 if big else 0)
     print(json.dumps(line), flush=True)
 
 

@@ -38,11 +38,16 @@
  *     place by design).  Calls that share an output or a workspace must not
  *     run concurrently.
  *   - No C++ exception crosses this interface.  The only process-wide state
- *     is a per-device cache of the compute-unit count (read once) and an
- *     atomic launch counter that tags the scan's hand-over slots in the
- *     workspace, so a workspace is reused without being cleared.  Concurrent
- *     calls on different streams with disjoint buffers (workspaces included)
- *     are safe.
+ *     is a per-device cache of the compute-unit count (read once), an atomic
+ *     launch counter that tags the scan's hand-over slots in the workspace,
+ *     so a workspace is reused without being cleared, and the test knobs of
+ *     mamba_set_test_knobs.  Concurrent calls on different streams with
+ *     disjoint buffers (workspaces included) are safe.
+ *   - Graph capture: every call may be recorded into a HIP graph.  A scan
+ *     recorded while its stream is capturing clears its hand-over flags with
+ *     a small kernel of its own before the scan kernel, so every replay starts
+ *     from cleared flags (a replay cannot take a new launch tag from the
+ *     host).
  *   - Supported sizes: 1 <= N <= 16; B, D, L >= 1; B*D*L < 2^46.
  *   - Arithmetic is fp32 throughout (state, discretisation, accumulation);
  *     bf16 inputs are widened exactly, outputs are rounded to nearest-even.
@@ -274,6 +279,41 @@ int mamba_ssd_fwd(const void* x, const void* delta, const void* z, const void* B
  * segment suffices; (size_t)-1 for an invalid or unsupported shape.
  */
 size_t mamba_ssd_workspace_size(int64_t B, int64_t H, int64_t P, int64_t N, int64_t L);
+
+/*
+ * Test and diagnostic knobs.  They change how a call is carried out, never
+ * what it computes (every setting gives the same result up to floating-point
+ * summation order, and the hand-over settings bit for bit).  Process-wide:
+ * every later call uses them, so a workspace size queried before a change
+ * does not fit a launch after it.  Not for production use.
+ *
+ *   scan_chunks           > 0: mamba_scan_fwd cuts L into this many chunks
+ *                         (summary pass, carry, full pass) whatever the shape;
+ *                         0: the planner decides.
+ *   scan_general_kernel   != 0: mamba_scan_fwd always uses the general
+ *                         64-channel kernel (normally only for L % 8 != 0 or
+ *                         L < 32).
+ *   scan_no_balance       != 0: no balanced split with state hand-over.
+ *   handover_spin         >= 0: bound of a workgroup's wait for the state handed
+ *                         over by the previous one, in polls (0: every split
+ *                         tile recomputes its state instead of waiting);
+ *                         < 0: the default, max(8192, 256 polls per 32-step
+ *                         block of a workgroup's share).
+ *   ssd_segments          > 0: mamba_ssd_fwd cuts L into this many segments
+ *                         (at most one per 32 steps); 0: the planner decides.
+ *
+ * mamba_set_test_knobs(NULL) restores the defaults {0, 0, 0, -1, 0}.
+ * Returns MAMBA_ERR_SHAPE for a negative chunk or segment count.
+ */
+typedef struct {
+  int64_t scan_chunks;
+  int32_t scan_general_kernel;
+  int32_t scan_no_balance;
+  int64_t handover_spin;
+  int64_t ssd_segments;
+} mamba_test_knobs_t;
+
+int mamba_set_test_knobs(const mamba_test_knobs_t* knobs);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char* mamba_status_string(int status);

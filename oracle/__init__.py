@@ -26,7 +26,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# ORACLE_LIB points the wrapper at another build of oracle.c (the sanitizer
+# test's instrumented copy); it is then loaded as it is, never rebuilt.
+_LIB = os.environ.get("ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lock = threading.Lock()
 _lib = None
 
@@ -48,7 +50,8 @@ def _load():
     global _lib
     with _lock:
         if _lib is None:
-            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            if not os.environ.get("ORACLE_LIB") and (not os.path.exists(_LIB) or
+                                                      os.path.getmtime(_LIB) < os.path.getmtime(_SRC)):
                 build(force=True)
             lib = ctypes.CDLL(_LIB)
             dp = ctypes.POINTER(ctypes.c_double)

@@ -28,6 +28,13 @@ _lock = threading.Lock()
 _lib = None
 
 
+class TestKnobs(ctypes.Structure):
+    """mamba_test_knobs_t of include/mamba_scan.h."""
+    _fields_ = [("scan_chunks", ctypes.c_int64), ("scan_general_kernel", ctypes.c_int32),
+                ("scan_no_balance", ctypes.c_int32), ("handover_spin", ctypes.c_int64),
+                ("ssd_segments", ctypes.c_int64)]
+
+
 class MambaError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
@@ -63,6 +70,8 @@ def lib() -> ctypes.CDLL:
             L.mamba_ssd_fwd.restype = c_int
             L.mamba_ssd_workspace_size.argtypes = [i64] * 5
             L.mamba_ssd_workspace_size.restype = ctypes.c_size_t
+            L.mamba_set_test_knobs.argtypes = [ctypes.POINTER(TestKnobs)]
+            L.mamba_set_test_knobs.restype = c_int
             L.mamba_status_string.argtypes = [c_int]
             L.mamba_status_string.restype = ctypes.c_char_p
             _lib = L
@@ -74,6 +83,33 @@ def status_string(status: int) -> str:
         return lib().mamba_status_string(int(status)).decode()
     except Exception:
         return "?"
+
+
+def set_test_knobs(scan_chunks: int = 0, scan_general_kernel: bool = False, scan_no_balance: bool = False,
+                   handover_spin: int = -1, ssd_segments: int = 0) -> None:
+    """Process-wide test knobs of the library (mamba_set_test_knobs); no
+    arguments restores the defaults."""
+    k = TestKnobs(scan_chunks, int(scan_general_kernel), int(scan_no_balance), handover_spin, ssd_segments)
+    st = lib().mamba_set_test_knobs(ctypes.byref(k))
+    if st != 0:
+        raise MambaError(st, "mamba_set_test_knobs")
+
+
+class test_knobs:  # noqa: N801 (used as a context manager)
+    """``with test_knobs(scan_chunks=5): ...`` sets the knobs for the block and
+    restores the defaults after it."""
+    __test__ = False   # not a pytest test class
+
+    def __init__(self, **kw):
+        self.kw = kw
+
+    def __enter__(self):
+        set_test_knobs(**self.kw)
+        return self
+
+    def __exit__(self, *exc):
+        set_test_knobs()
+        return False
 
 
 def workspace_size(B: int, D: int, N: int, L: int) -> int:

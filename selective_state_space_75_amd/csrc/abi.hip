@@ -1,8 +1,6 @@
 // abi.hip -- the C ABI declared in include/mamba_scan.h: argument checks,
 // the execution plan of a scan (single pass or chunked along L), and the
 // kernel launches.  Every check runs before any HIP call.
-#include <stdlib.h>
-
 #include <atomic>
 #include <chrono>
 #include <mutex>
@@ -42,14 +40,15 @@ bool shape_ok(int64_t B, int64_t D, int64_t N, int64_t L) {
   return true;
 }
 
-// Test knob: MAMBA_SCAN_CHUNKS=K forces K chunks along L (K >= 1), so the
-// chunked path can be checked at small sizes.  Read on every call.
-int64_t forced_chunks() {
-  const char* s = getenv("MAMBA_SCAN_CHUNKS");
-  if (!s || !*s) return 0;
-  char* end = nullptr;
-  const long long v = strtoll(s, &end, 10);
-  return (end && *end == '\0' && v > 0) ? (int64_t)v : 0;
+// Test knobs (mamba_set_test_knobs): process-wide, copied once per call so
+// that a call sees one consistent set.  Zero-initialised fields and a negative
+// hand-over bound are the defaults.
+std::mutex g_knob_mu;
+mamba_test_knobs_t g_knobs = {0, 0, 0, -1, 0};
+
+mamba_test_knobs_t knobs() {
+  std::lock_guard<std::mutex> lock(g_knob_mu);
+  return g_knobs;
 }
 
 // Relative time of the wave-tile kernel over k chunks of L, in units of one
@@ -70,17 +69,16 @@ double v4_chunk_cost(int64_t tiles, int64_t k) {
 // into chunks of at least 2048 steps: for the wave-tile kernel the number of
 // chunks that minimises v4_chunk_cost, for the general kernel about 1024
 // workgroups.
-Plan make_plan(int64_t B, int64_t D, int64_t N, int64_t L) {
+Plan make_plan(int64_t B, int64_t D, int64_t N, int64_t L, const mamba_test_knobs_t& kn) {
   Plan p;
   p.tiles_d = (D + kTile - 1) / kTile;
-  p.v4 = (L % 8 == 0) && L >= kV4Step && (getenv("MAMBA_SCAN_V1") == nullptr);
+  p.v4 = (L % 8 == 0) && L >= kV4Step && !kn.scan_general_kernel;
   // Units of independent sequential work: 16-channel tiles (wave-tile
   // kernel) or 64-channel tiles (general kernel).
   const int64_t tiles = p.v4 ? B * ((D + kV4Tile - 1) / kV4Tile) : B * p.tiles_d;
   int64_t k = 1;
-  const int64_t forced = forced_chunks();
-  if (forced > 0) {
-    k = forced;
+  if (kn.scan_chunks > 0) {
+    k = kn.scan_chunks;
   } else if (p.v4 && L >= 4096 && tiles < kGroupsPlan) {
     const int64_t kmax = L / 2048 < 64 ? L / 2048 : 64;
     double best = v4_chunk_cost(tiles, 1);
@@ -98,7 +96,7 @@ Plan make_plan(int64_t B, int64_t D, int64_t N, int64_t L) {
   len = (len + kStage - 1) / kStage * kStage;
   p.chunk_len = len;
   p.n_chunks = (L + len - 1) / len;
-  p.balanced = p.v4 && p.n_chunks * tiles >= kGroupsPlan && getenv("MAMBA_SCAN_NO_BALANCE") == nullptr;
+  p.balanced = p.v4 && p.n_chunks * tiles >= kGroupsPlan && !kn.scan_no_balance;
   size_t o = 0;
   if (p.n_chunks > 1) {
     const size_t state = size_t(p.n_chunks) * size_t(B) * size_t(D) * size_t(N) * sizeof(float);
@@ -132,22 +130,27 @@ int64_t device_cus() {
   return cached[dev];
 }
 
-// Bound of the wait for a state hand-over between workgroups (iterations of
-// a short sleep, about 50 ms in total).  Test knob: MAMBA_SCAN_HANDOVER_SPIN=n
-// sets it, so that 0 forces every workgroup to recompute the state instead.
-uint32_t handover_spin_limit() {
-  const char* s = getenv("MAMBA_SCAN_HANDOVER_SPIN");
-  if (s && *s) {
-    char* end = nullptr;
-    const long long v = strtoll(s, &end, 10);
-    if (end && *end == '\0' && v >= 0 && v <= (1ll << 30)) return (uint32_t)v;
-  }
-  return 1u << 20;
+// Bound of the wait for a state hand-over between workgroups, in polls of a
+// short sleep (each at least ~60 ns): 256 polls per 32-step block of a
+// workgroup's share, at least 8192.  A share's blocks take well under 256
+// polls each to scan, so the bound is several times the launch's own
+// duration; when it runs out (the publishing workgroup is not resident), the
+// waiting one recomputes the state instead.  The test knob sets it directly
+// (0 forces every recompute).
+uint32_t handover_spin_limit(int64_t blocks_per_group, const mamba_test_knobs_t& kn) {
+  if (kn.handover_spin >= 0) return kn.handover_spin < (1ll << 30) ? (uint32_t)kn.handover_spin : (1u << 30);
+  const int64_t v = 256 * blocks_per_group;
+  return v < 8192 ? 8192u : (v > (1ll << 24) ? (1u << 24) : (uint32_t)v);
 }
 
 // Numbers launches of the balanced kernel: a hand-over slot counts as
 // published only when its flag holds this launch's value, so stale flags
-// left in a reused workspace are never mistaken for fresh ones.
+// left in a reused workspace are never mistaken for fresh ones.  These values
+// always have the top bit set; a launch recorded into a graph uses the fixed
+// value kCaptureEpoch instead (a replay cannot take a new value from the
+// host), after a small kernel clears the flags on every replay.
+constexpr uint64_t kCaptureEpoch = 1;
+
 uint64_t next_epoch() {
   static std::atomic<uint64_t> counter{0};
   static std::once_flag once;
@@ -155,7 +158,7 @@ uint64_t next_epoch() {
     const uint64_t t = (uint64_t)std::chrono::high_resolution_clock::now().time_since_epoch().count();
     counter.store((t * 0x9E3779B97F4A7C15ull) | 1ull);
   });
-  return counter.fetch_add(1);
+  return counter.fetch_add(1) | (1ull << 63);
 }
 
 bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
@@ -212,18 +215,13 @@ BwdPlan make_bwd_plan(int64_t B, int64_t D, int64_t L) {
   return q;
 }
 
-extern "C" {
+namespace {
 
-size_t mamba_scan_workspace_size(int64_t B, int64_t D, int64_t N, int64_t L) {
-  if (!shape_ok(B, D, N, L) || N > 16) return (size_t)-1;
-  return make_plan(B, D, N, L).ws_bytes;
-}
-
-int mamba_scan_fwd(const void* u, const void* delta, const void* z, const void* Bt, const void* Ct,
-                   const float* A, const float* Dskip, const float* delta_bias, void* y,
-                   float* final_state, int64_t B, int64_t D, int64_t N, int64_t L,
-                   mamba_dtype_t in_dtype, mamba_dtype_t out_dtype, int return_final_state,
-                   unsigned flags, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+// Argument checks of mamba_scan_fwd; no HIP call.
+int check_scan_args(const void* u, const void* delta, const void* z, const void* Bt, const void* Ct,
+                    const float* A, const float* Dskip, const float* delta_bias, const void* y,
+                    const float* final_state, int64_t B, int64_t D, int64_t N, int64_t L,
+                    mamba_dtype_t in_dtype, mamba_dtype_t out_dtype, int return_final_state, unsigned flags) {
   if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return MAMBA_ERR_DTYPE;
   if (flags & ~kKnownFlags) return MAMBA_ERR_UNSUPPORTED;
   if (!shape_ok(B, D, N, L)) return MAMBA_ERR_SHAPE;
@@ -235,13 +233,16 @@ int mamba_scan_fwd(const void* u, const void* delta, const void* z, const void* 
   for (const void* ptr : {(const void*)A, (const void*)Dskip, (const void*)delta_bias, (const void*)final_state})
     if (ptr && !aligned(ptr, 4)) return MAMBA_ERR_ALIGN;
 
-  const Plan plan = make_plan(B, D, N, L);
-  if (plan.n_chunks * B * plan.tiles_d >= (int64_t(1) << 31)) return MAMBA_ERR_SHAPE;
-  if (plan.ws_bytes > 0) {
-    if (!workspace || workspace_bytes < plan.ws_bytes) return MAMBA_ERR_WORKSPACE;
-    if (!aligned(workspace, 16)) return MAMBA_ERR_ALIGN;
-  }
+  return MAMBA_OK;
+}
 
+// The launches of a checked scan whose workspace holds at least plan.ws_bytes.
+int scan_fwd_run(const void* u, const void* delta, const void* z, const void* Bt, const void* Ct,
+                 const float* A, const float* Dskip, const float* delta_bias, void* y,
+                 float* final_state, int64_t B, int64_t D, int64_t N, int64_t L,
+                 mamba_dtype_t in_dtype, mamba_dtype_t out_dtype, int return_final_state,
+                 unsigned flags, const Plan& plan, const mamba_test_knobs_t& kn, void* workspace,
+                 hipStream_t stream) {
   mamba::ScanParams p{};
   p.u = u; p.delta = delta; p.z = z; p.Bt = Bt; p.Ct = Ct;
   p.A = A; p.Dskip = Dskip; p.bias = delta_bias;
@@ -257,16 +258,26 @@ int mamba_scan_fwd(const void* u, const void* delta, const void* z, const void* 
   const Dt out = out_dtype == MAMBA_BF16 ? Dt::BF16 : Dt::F32;
 
   mamba::V2Params q{};
-  q.spin_limit = handover_spin_limit();
   if (plan.balanced) {
     const int64_t cus = device_cus();
     if (cus <= 0) return MAMBA_ERR_HIP;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return MAMBA_ERR_HIP;
     q.balanced = 1;
     q.groups = 4 * cus < kGroupsPlan ? 4 * cus : kGroupsPlan;   // one wave per SIMD
-    q.epoch = next_epoch();
+    const int64_t tiles = B * ((D + kV4Tile - 1) / kV4Tile);
+    const int64_t blocks = (plan.n_chunks - 1) * tiles * (plan.chunk_len / kV4Step) +
+                           tiles * ((L - (plan.n_chunks - 1) * plan.chunk_len + kV4Step - 1) / kV4Step);
+    q.spin_limit = handover_spin_limit((blocks + q.groups - 1) / q.groups, kn);
     char* ws = static_cast<char*>(workspace);
     q.pub_flag = reinterpret_cast<uint64_t*>(ws + plan.off_flag);
     q.pub_state = reinterpret_cast<float*>(ws + plan.off_pub);
+    if (cs == hipStreamCaptureStatusNone) {
+      q.epoch = next_epoch();
+    } else {
+      q.epoch = kCaptureEpoch;
+      if (mamba::launch_clear_u64(q.pub_flag, q.groups, stream) != hipSuccess) return MAMBA_ERR_HIP;
+    }
   }
   if (plan.n_chunks > 1) {
     char* ws = static_cast<char*>(workspace);
@@ -284,6 +295,46 @@ int mamba_scan_fwd(const void* u, const void* delta, const void* z, const void* 
                                : mamba::launch_scan_full(p, in, out, stream);
   if (e != hipSuccess) return MAMBA_ERR_HIP;
   return MAMBA_OK;
+}
+
+
+}  // namespace
+
+extern "C" {
+
+size_t mamba_scan_workspace_size(int64_t B, int64_t D, int64_t N, int64_t L) {
+  if (!shape_ok(B, D, N, L) || N > 16) return (size_t)-1;
+  return make_plan(B, D, N, L, knobs()).ws_bytes;
+}
+
+int mamba_set_test_knobs(const mamba_test_knobs_t* k) {
+  mamba_test_knobs_t v = {0, 0, 0, -1, 0};
+  if (k) {
+    if (k->scan_chunks < 0 || k->ssd_segments < 0) return MAMBA_ERR_SHAPE;
+    v = *k;
+  }
+  std::lock_guard<std::mutex> lock(g_knob_mu);
+  g_knobs = v;
+  return MAMBA_OK;
+}
+
+int mamba_scan_fwd(const void* u, const void* delta, const void* z, const void* Bt, const void* Ct,
+                   const float* A, const float* Dskip, const float* delta_bias, void* y,
+                   float* final_state, int64_t B, int64_t D, int64_t N, int64_t L,
+                   mamba_dtype_t in_dtype, mamba_dtype_t out_dtype, int return_final_state,
+                   unsigned flags, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const int st = check_scan_args(u, delta, z, Bt, Ct, A, Dskip, delta_bias, y, final_state, B, D, N, L, in_dtype,
+                                 out_dtype, return_final_state, flags);
+  if (st != MAMBA_OK) return st;
+  const mamba_test_knobs_t kn = knobs();
+  const Plan plan = make_plan(B, D, N, L, kn);
+  if (plan.n_chunks * B * plan.tiles_d >= (int64_t(1) << 31)) return MAMBA_ERR_SHAPE;
+  if (plan.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < plan.ws_bytes) return MAMBA_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return MAMBA_ERR_ALIGN;
+  }
+  return scan_fwd_run(u, delta, z, Bt, Ct, A, Dskip, delta_bias, y, final_state, B, D, N, L, in_dtype, out_dtype,
+                      return_final_state, flags, plan, kn, workspace, stream);
 }
 
 int mamba_state_update(float* state, const void* u, const void* delta, const void* z,
@@ -396,19 +447,15 @@ struct SsdPlan {
 // 2048 (chunk launch + segment-state launch): 1 segment 281 us; 2: 248 + 43;
 // 3: 210 + 45; 4: 209 + 46; 6: 221 + 56; 8: 221 + 56.  With 512 or more
 // workgroups the state launch costs about what the added parallelism saves.
-// Test knob: MAMBA_SSD_SEGMENTS=S asks for S segments (still at most one per
-// 32-step chunk).  Read on every call, by the size query and the launch alike.
-SsdPlan make_ssd_plan(int64_t B, int64_t H, int64_t P, int64_t N, int64_t L) {
+// Test knob ssd_segments = S asks for S segments (still at most one per
+// 32-step chunk), for the size query and the launch alike.
+SsdPlan make_ssd_plan(int64_t B, int64_t H, int64_t P, int64_t N, int64_t L, const mamba_test_knobs_t& kn) {
   SsdPlan q;
   const int64_t wgs = B * H * (P / 64);
   int64_t S = wgs < 512 ? (1024 + wgs - 1) / wgs : 1;
   const int64_t smax = (L + 255) / 256;
   if (S > smax) S = smax;
-  if (const char* e = getenv("MAMBA_SSD_SEGMENTS")) {
-    char* end = nullptr;
-    const long long v = strtoll(e, &end, 10);
-    if (end && *end == '\0' && v > 0) S = (v < (L + 31) / 32) ? (int64_t)v : (L + 31) / 32;
-  }
+  if (kn.ssd_segments > 0) S = (kn.ssd_segments < (L + 31) / 32) ? kn.ssd_segments : (L + 31) / 32;
   if (S < 1) S = 1;
   int64_t len = (L + S - 1) / S;
   len = (len + 31) / 32 * 32;
@@ -431,7 +478,7 @@ extern "C" {
 size_t mamba_ssd_workspace_size(int64_t B, int64_t H, int64_t P, int64_t N, int64_t L) {
   if (H < 1 || P < 1 || H > kMaxElems / P || !shape_ok(B, H * P, N, L)) return (size_t)-1;
   if ((N != 64 && N != 128) || P % 64 != 0) return (size_t)-1;
-  return make_ssd_plan(B, H, P, N, L).bytes;
+  return make_ssd_plan(B, H, P, N, L, knobs()).bytes;
 }
 
 int mamba_ssd_fwd(const void* x, const void* delta, const void* z, const void* Bt, const void* Ct,
@@ -450,7 +497,7 @@ int mamba_ssd_fwd(const void* x, const void* delta, const void* z, const void* B
   for (const void* ptr : {(const void*)A, (const void*)Dskip, (const void*)delta_bias,
                           (const void*)(return_final_state ? final_state : nullptr)})
     if (ptr && !aligned(ptr, 4)) return MAMBA_ERR_ALIGN;
-  const SsdPlan plan = make_ssd_plan(B, H, P, N, L);
+  const SsdPlan plan = make_ssd_plan(B, H, P, N, L, knobs());
   if (B * plan.S * H * (P / 64) >= (int64_t(1) << 31)) return MAMBA_ERR_SHAPE;
   if (plan.bytes && (!workspace || workspace_bytes < plan.bytes)) return MAMBA_ERR_WORKSPACE;
   if (plan.bytes && !aligned(workspace, 256)) return MAMBA_ERR_ALIGN;

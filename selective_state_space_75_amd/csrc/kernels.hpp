@@ -16,10 +16,12 @@ enum LoopMode : int {
 };
 
 // kZohFast rounds Abar before subtracting 1, so B-bar carries a relative
-// error of about 1.2e-7 / (delta |A|): 1e-5 at |A| = 1, delta = 0.01, but all
-// of it once delta |A| nears 2^-24.  A wave takes kZohAccurate instead when
-// one of its |A| is below this bound (the error is then below 5e-4 for
-// delta >= 1e-3).
+// error of about 1.2e-7 / (delta |A|): 1.2e-5 at |A| = 1, delta = 0.01, but
+// all of it once delta |A| nears 2^-24.  A wave takes kZohAccurate instead
+// when one of its |A| is below this bound.  At the bound the per-step error
+// is up to 1.9e-3 for delta = 1e-3; a state averages these independent
+// errors over about 1 / (delta |A|) steps, so the state and y carry about
+// 1.2e-7 / sqrt(delta |A|) = 1.5e-5 there.
 constexpr float kFastZohMinAbsA = 0x1p-4f;
 
 struct ScanParams {
@@ -124,6 +126,7 @@ struct SsdParams {
 hipError_t launch_scan_full(const ScanParams& p, Dt in, Dt out, hipStream_t s);
 hipError_t launch_scan_summary(const ScanParams& p, Dt in, hipStream_t s);
 hipError_t launch_scan_carry(const ScanParams& p, hipStream_t s);
+hipError_t launch_clear_u64(uint64_t* p, int64_t n, hipStream_t s);
 hipError_t launch_scan_v4(const ScanParams& p, const V2Params& q, Dt in, Dt out, bool summary, hipStream_t s);
 hipError_t launch_state_update(const UpdateParams& p, Dt in, Dt out, hipStream_t s);
 hipError_t launch_scan_bwd(const BwdParams& p, Dt in, Dt grad, hipStream_t s);

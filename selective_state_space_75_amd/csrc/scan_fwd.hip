@@ -346,6 +346,19 @@ hipError_t launch_scan_summary(const ScanParams& p, Dt in, hipStream_t s) {
   return in == Dt::BF16 ? launch_scan_t<true, false, true>(p, s) : launch_scan_t<false, false, true>(p, s);
 }
 
+// Sets n 64-bit words to zero with ordinary stores: the hand-over flags of a
+// scan recorded into a graph are cleared this way on every replay.
+__global__ __launch_bounds__(256) void clear_u64_kernel(uint64_t* p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+hipError_t launch_clear_u64(uint64_t* p, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(clear_u64_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_scan_carry(const ScanParams& p, hipStream_t s) {
   const int64_t total = p.B * p.D * p.N;
   const dim3 g((unsigned)((total + 255) / 256)), blk(256);

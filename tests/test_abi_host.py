@@ -29,8 +29,8 @@ def declared_functions():
 def test_header_symbols_are_exported():
     names = declared_functions()
     assert names == ["mamba_conv1d_fwd", "mamba_conv1d_update", "mamba_scan_bwd", "mamba_scan_bwd_workspace_size",
-                     "mamba_scan_fwd", "mamba_scan_workspace_size", "mamba_ssd_fwd", "mamba_ssd_workspace_size",
-                     "mamba_state_update", "mamba_status_string"]
+                     "mamba_scan_fwd", "mamba_scan_workspace_size", "mamba_set_test_knobs", "mamba_ssd_fwd",
+                     "mamba_ssd_workspace_size", "mamba_state_update", "mamba_status_string"]
     L = _lib.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -71,17 +71,33 @@ def test_workspace_size_plan():
     assert _lib.lib().mamba_scan_workspace_size(1, 1, 17, 1) == ctypes.c_size_t(-1).value
 
 
-def test_forced_chunks_knob(monkeypatch):
+def test_forced_chunks_knob():
     # 5 forced chunks x 256 tiles: summary workspace plus the hand-over area
-    monkeypatch.setenv("MAMBA_SCAN_CHUNKS", "5")
-    assert _lib.workspace_size(1, 4096, 16, 320) == 2 * 5 * 4096 * 16 * 4 + 5 * 4096 * 4 + 1024 * 8 + \
-        1024 * 16 * 16 * 4
-    monkeypatch.setenv("MAMBA_SCAN_CHUNKS", "3")
-    # L = 100 -> chunk_len rounds 34 up to 64 -> 2 chunks
-    assert _lib.workspace_size(2, 70, 5, 100) == 2 * (((2 * 2 * 70 * 5 * 4) + 255) // 256 * 256) + \
-        ((2 * 2 * 70 * 4 + 255) // 256 * 256)
-    monkeypatch.setenv("MAMBA_SCAN_CHUNKS", "1")
+    with _lib.test_knobs(scan_chunks=5):
+        assert _lib.workspace_size(1, 4096, 16, 320) == 2 * 5 * 4096 * 16 * 4 + 5 * 4096 * 4 + 1024 * 8 + \
+            1024 * 16 * 16 * 4
+    with _lib.test_knobs(scan_chunks=3):
+        # L = 100 -> chunk_len rounds 34 up to 64 -> 2 chunks
+        assert _lib.workspace_size(2, 70, 5, 100) == 2 * (((2 * 2 * 70 * 5 * 4) + 255) // 256 * 256) + \
+            ((2 * 2 * 70 * 4 + 255) // 256 * 256)
+    with _lib.test_knobs(scan_chunks=1):
+        assert _lib.workspace_size(2, 70, 5, 100) == 0
+    # back to the planner: one pass, no workspace
     assert _lib.workspace_size(2, 70, 5, 100) == 0
+    assert _lib.workspace_size(1, 4096, 16, 320) == 0
+
+
+def test_knob_defaults_and_errors():
+    import pytest as _pt
+    # the general kernel takes 64-channel tiles; no balance drops the hand-over area
+    with _lib.test_knobs(scan_no_balance=True):
+        assert _lib.workspace_size(4, 5120, 16, 2048) == 0
+    assert _lib.workspace_size(4, 5120, 16, 2048) == 1024 * 8 + 1024 * 16 * 16 * 4
+    with _pt.raises(_lib.MambaError):
+        _lib.set_test_knobs(scan_chunks=-1)
+    with _lib.test_knobs(ssd_segments=3):
+        assert _lib.ssd_workspace_size(4, 80, 64, 128, 2048) > 0
+    assert _lib.lib().mamba_set_test_knobs(None) == 0
 
 
 P = 0x10000  # fake 64 KiB-aligned device address, never dereferenced

@@ -78,3 +78,27 @@ def test_scan_config_seq_len_override():
         (base.B, base.D, base.N, base.dtype, base.seed, base.final_state)
     assert cfg.L == 2040 and cfg.name != base.name
     assert cfg.updates == base.updates // 2048 * 2040
+
+
+def test_cpu_baseline_scan_sample_scales_rates():
+    """A channel sample reports rates per unit of work: the sampled share of
+    the workload's bytes, elements and updates over the sample's run time."""
+    cfg = W.ScanConfig("t", 2, 64, 16, 64, "bf16", 5, "normal", True)
+    x = W.scan_inputs(cfg)
+    whole = bench.cpu_baseline_scan(cfg, x, 0.0)
+    part = bench.cpu_baseline_scan(cfg, x, 0.0, channels=16, single_channels=8)
+    for r in (whole, part):
+        assert r["kind"] == "oracle" and r["unit"] == "GB/s" and r["value"] > 0 and r["cores"] >= 1
+        assert r["updates_per_s"] == pytest.approx(r["elems_per_s"] * cfg.N, rel=1e-6)
+    assert "whole workload" in whole["sample"]
+    assert "channels 0..15 of batch row 0" in part["sample"]
+    if part["cores"] > 1:
+        assert "channels 0..7" in part["single_thread"]["sample"]
+
+
+def test_cpu_baseline_decode_extrapolates():
+    cfg = W.DecodeConfig("tiny_decode", 48, 4, 2, 64, 16, 77)
+    r = bench.cpu_baseline_decode(cfg, steps=2)
+    assert r["extrapolated"] is True and r["kind"] == "oracle"
+    assert "x24" in r["sample"]
+    assert r["extrapolated_total_s"] > 0 and r["tokens_per_s"] > 0

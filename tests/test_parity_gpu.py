@@ -224,12 +224,17 @@ CASES = [
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "B%dD%dN%dL%d_%s_%s_k%s_%s" % (
     c[0], c[1], c[2], c[3], c[4], c[5], c[6], "-".join(sorted(c[7])) or "plain"))
-def test_ragged_and_options(case, dev, monkeypatch):
-    import torch
+def test_ragged_and_options(case, dev):
+    import selective_state_space_75_amd as m
     B, D, N, L, dt, odt, chunks, opts = case
     log("[ragged] %s" % (case,))
-    if chunks is not None:
-        monkeypatch.setenv("MAMBA_SCAN_CHUNKS", str(chunks))
+    with m.test_knobs(scan_chunks=chunks or 0):
+        _ragged_case(case, dev)
+
+
+def _ragged_case(case, dev):
+    import torch
+    B, D, N, L, dt, odt, chunks, opts = case
     x = W.custom_scan_inputs(B, D, N, L, dt, seed=7000 + B * 131 + D * 7 + L)
     if opts.get("zero_A"):
         A = x["A"].copy()
@@ -265,34 +270,34 @@ def test_ragged_and_options(case, dev, monkeypatch):
 @pytest.mark.parametrize("shape", [(2, 10240, 16, 160, None), (1, 4096, 16, 352, 5), (2, 10240, 16, 168, None),
                                    (1, 4096, 16, 328, 5)],
                          ids=["tiles", "chunk_tiles", "tiles_ragged_L", "chunk_tiles_ragged_L"])
-def test_handover_fallback_matches(shape, dev, monkeypatch):
+def test_handover_fallback_matches(shape, dev):
     """With the hand-over wait forced to zero every split tile recomputes its
     state at the cut (from the start of its chunk) instead of receiving it;
     the output must not change."""
     import torch
     import selective_state_space_75_amd as m
     B, D, N, L, chunks = shape
-    if chunks is not None:
-        monkeypatch.setenv("MAMBA_SCAN_CHUNKS", str(chunks))
-    assert m.workspace_size(B, D, N, L) > 0
     x = W.custom_scan_inputs(B, D, N, L, "bf16", seed=31337)
     t = upload_scan(x, dev)
-    y1, h1 = gpu_scan(t, return_final_state=True)
-    monkeypatch.setenv("MAMBA_SCAN_HANDOVER_SPIN", "0")
-    y2, h2 = gpu_scan(t, return_final_state=True)
+    with m.test_knobs(scan_chunks=chunks or 0):
+        assert m.workspace_size(B, D, N, L) > 0
+        y1, h1 = gpu_scan(t, return_final_state=True)
+    with m.test_knobs(scan_chunks=chunks or 0, handover_spin=0):
+        y2, h2 = gpu_scan(t, return_final_state=True)
     torch.cuda.synchronize()
     assert torch.equal(y1, y2) and torch.equal(h1, h2)
     yr, _ = oracle_scan(x)
     assert_close(from_dev(y2), yr, True, "fallback y")
 
 
-def test_v1_kernel_on_aligned_shape(dev, monkeypatch):
+def test_v1_kernel_on_aligned_shape(dev):
     """The general kernel (used for ragged L) on an L % 32 == 0 workload."""
     import torch
-    monkeypatch.setenv("MAMBA_SCAN_V1", "1")
+    import selective_state_space_75_amd as m
     x = W.custom_scan_inputs(2, 192, 16, 512, "bf16", seed=555)
     t = upload_scan(x, dev)
-    y, hN = gpu_scan(t, return_final_state=True)
+    with m.test_knobs(scan_general_kernel=True):
+        y, hN = gpu_scan(t, return_final_state=True)
     torch.cuda.synchronize()
     yr, hr = oracle_scan(x)
     assert_close(from_dev(y), yr, True, "v1 y")
