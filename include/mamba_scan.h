@@ -131,6 +131,28 @@ int mamba_scan_fwd(const void* u, const void* delta, const void* z,
                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * mamba_scan_fwd without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Arguments, results and errors are those
+ * of mamba_scan_fwd.  The scratch memory the scan needs (hand-over slots of
+ * the balanced split, chunk carries of long sequences) comes from a buffer
+ * the library holds in device memory, one per GPU, 8 MiB, kept until the
+ * process ends; this call allocates nothing.  A shape whose plan needs more
+ * (mamba_scan_workspace_size above 8 MiB, e.g. very long sequences over many
+ * channels) returns MAMBA_ERR_WORKSPACE and launches nothing.  The buffer is
+ * shared by every call on that GPU: calls of this function that overlap in
+ * time on one GPU (different streams, or host threads) race and give wrong
+ * results; serialise them.  The stream must belong to the current device.
+ */
+int mamba_scan_fwd_noalloc(const void* u, const void* delta, const void* z,
+                           const void* Bt, const void* Ct, const float* A,
+                           const float* Dskip, const float* delta_bias,
+                           void* y, float* final_state,
+                           int64_t B, int64_t D, int64_t N, int64_t L,
+                           mamba_dtype_t in_dtype, mamba_dtype_t out_dtype,
+                           int return_final_state, unsigned flags, hipStream_t stream);
+
+/*
  * One decoding step for every (b, d): the scan above with L = 1, starting
  * from `state` instead of zero.
  *

@@ -56,6 +56,8 @@ def lib() -> ctypes.CDLL:
             L.mamba_scan_fwd.argtypes = ([vp] * 10 + [i64] * 4 + [c_int, c_int, c_int, u32, vp,
                                                                  ctypes.c_size_t, vp])
             L.mamba_scan_fwd.restype = c_int
+            L.mamba_scan_fwd_noalloc.argtypes = [vp] * 10 + [i64] * 4 + [c_int, c_int, c_int, u32, vp]
+            L.mamba_scan_fwd_noalloc.restype = c_int
             L.mamba_state_update.argtypes = [vp] * 10 + [i64] * 3 + [c_int, c_int, u32, vp]
             L.mamba_state_update.restype = c_int
             L.mamba_scan_bwd_workspace_size.argtypes = [i64, i64, i64, i64]
@@ -208,6 +210,34 @@ def scan_fwd(u, delta, z, Bt, Ct, A, Dskip=None, delta_bias=None, *, return_fina
     if st != 0:
         raise MambaError(st, "mamba_scan_fwd")
     return (y, final_state) if return_final_state else y
+
+
+def scan_fwd_noalloc(u, delta, z, Bt, Ct, A, Dskip=None, delta_bias=None, *, y, final_state=None,
+                     out_dtype=None, delta_b=False, accurate_expm1=False, stream=None):
+    """scan_fwd through mamba_scan_fwd_noalloc: the library's own per-GPU
+    scratch instead of a workspace, and caller-provided outputs (y, and
+    final_state when given), so nothing is allocated."""
+    B, D, L = u.shape
+    N = Bt.shape[1]
+    dev = u.device
+    in_dt = u.dtype
+    _dtype_code(u)
+    for t, name, shape, dt in ((u, "u", (B, D, L), in_dt), (delta, "delta", (B, D, L), in_dt),
+                               (z, "z", (B, D, L), in_dt), (Bt, "Bt", (B, N, L), in_dt),
+                               (Ct, "Ct", (B, N, L), in_dt), (A, "A", (D, N), _torch().float32),
+                               (Dskip, "Dskip", (D,), _torch().float32),
+                               (delta_bias, "delta_bias", (D,), _torch().float32)):
+        _check(t, name, shape, dt, dev)
+    _check(y, "y", (B, D, L), y.dtype if out_dtype is None else out_dtype, dev)
+    _check(final_state, "final_state", (B, D, N), _torch().float32, dev)
+    flags = (FLAG_DELTA_B if delta_b else 0) | (FLAG_ACCURATE_EXPM1 if accurate_expm1 else 0)
+    st = lib().mamba_scan_fwd_noalloc(
+        _ptr(u), _ptr(delta), _ptr(z), _ptr(Bt), _ptr(Ct), _ptr(A), _ptr(Dskip), _ptr(delta_bias),
+        _ptr(y), _ptr(final_state), B, D, N, L, _dtype_code(u), _dtype_code(y),
+        1 if final_state is not None else 0, flags, _stream(dev, stream))
+    if st != 0:
+        raise MambaError(st, "mamba_scan_fwd_noalloc")
+    return (y, final_state) if final_state is not None else y
 
 
 def ssd_workspace_size(B: int, H: int, P: int, N: int, L: int) -> int:

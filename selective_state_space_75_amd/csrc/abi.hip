@@ -217,7 +217,7 @@ BwdPlan make_bwd_plan(int64_t B, int64_t D, int64_t L) {
 
 namespace {
 
-// Argument checks of mamba_scan_fwd; no HIP call.
+// Argument checks shared by mamba_scan_fwd and mamba_scan_fwd_noalloc; no HIP call.
 int check_scan_args(const void* u, const void* delta, const void* z, const void* Bt, const void* Ct,
                     const float* A, const float* Dskip, const float* delta_bias, const void* y,
                     const float* final_state, int64_t B, int64_t D, int64_t N, int64_t L,
@@ -298,6 +298,29 @@ int scan_fwd_run(const void* u, const void* delta, const void* z, const void* Bt
 }
 
 
+// Scratch memory of mamba_scan_fwd_noalloc: the scan's hand-over slots and
+// chunk carries for callers that cannot allocate.  One copy per GPU, held
+// until the process ends; every call on a GPU shares it.
+constexpr size_t kNoAllocScratchBytes = size_t(8) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+// Device address of `scratch` on the current device, looked up once per
+// device (each GPU holds its own copy at its own address).  In host code the
+// array's name is only a handle for this lookup, never an address to pass on.
+void* scratch_ptr() {
+  static std::mutex mu;
+  static void* ptrs[64] = {nullptr};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    ptrs[dev] = ptr;
+  }
+  return ptrs[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -335,6 +358,27 @@ int mamba_scan_fwd(const void* u, const void* delta, const void* z, const void* 
   }
   return scan_fwd_run(u, delta, z, Bt, Ct, A, Dskip, delta_bias, y, final_state, B, D, N, L, in_dtype, out_dtype,
                       return_final_state, flags, plan, kn, workspace, stream);
+}
+
+int mamba_scan_fwd_noalloc(const void* u, const void* delta, const void* z, const void* Bt, const void* Ct,
+                           const float* A, const float* Dskip, const float* delta_bias, void* y,
+                           float* final_state, int64_t B, int64_t D, int64_t N, int64_t L,
+                           mamba_dtype_t in_dtype, mamba_dtype_t out_dtype, int return_final_state,
+                           unsigned flags, hipStream_t stream) {
+  const int st = check_scan_args(u, delta, z, Bt, Ct, A, Dskip, delta_bias, y, final_state, B, D, N, L, in_dtype,
+                                 out_dtype, return_final_state, flags);
+  if (st != MAMBA_OK) return st;
+  const mamba_test_knobs_t kn = knobs();
+  const Plan plan = make_plan(B, D, N, L, kn);
+  if (plan.n_chunks * B * plan.tiles_d >= (int64_t(1) << 31)) return MAMBA_ERR_SHAPE;
+  if (plan.ws_bytes > kNoAllocScratchBytes) return MAMBA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (plan.ws_bytes > 0) {
+    ws = scratch_ptr();
+    if (!ws) return MAMBA_ERR_HIP;
+  }
+  return scan_fwd_run(u, delta, z, Bt, Ct, A, Dskip, delta_bias, y, final_state, B, D, N, L, in_dtype, out_dtype,
+                      return_final_state, flags, plan, kn, ws, stream);
 }
 
 int mamba_state_update(float* state, const void* u, const void* delta, const void* z,

@@ -29,7 +29,8 @@ def declared_functions():
 def test_header_symbols_are_exported():
     names = declared_functions()
     assert names == ["mamba_conv1d_fwd", "mamba_conv1d_update", "mamba_scan_bwd", "mamba_scan_bwd_workspace_size",
-                     "mamba_scan_fwd", "mamba_scan_workspace_size", "mamba_set_test_knobs", "mamba_ssd_fwd",
+                     "mamba_scan_fwd", "mamba_scan_fwd_noalloc", "mamba_scan_workspace_size", "mamba_set_test_knobs",
+                     "mamba_ssd_fwd",
                      "mamba_ssd_workspace_size", "mamba_state_update", "mamba_status_string"]
     L = _lib.lib()
     for n in names:
@@ -292,3 +293,34 @@ def test_ssd_workspace_size():
     # 1 x 2 blocks want 128 segments; at most ceil(1000 / 256) = 4 -> 250 -> 256 steps -> 4
     assert ws(1, 2, 64, 64, 1000) == a(1 * 4 * 2 * 64 * 64 * 4) + a(1 * 4 * 2 * 4)
     assert _lib.lib().mamba_ssd_workspace_size(1, 2, 64, 16, 100) == ctypes.c_size_t(-1).value
+
+
+def test_noalloc_refuses_oversized_plan():
+    """mamba_scan_fwd_noalloc's scratch buffer holds 8 MiB.  The planner's own
+    plans stay far below it (the batch-1 long sequence needs 3.75 MiB); 64
+    forced chunks over 16384 channels need 134 MB of carries, so the call is
+    refused in its host checks, before any HIP call (the fake pointers are
+    never dereferenced)."""
+    from selective_state_space_75_amd import workloads as W
+    B, D, N, L = 1, 16384, 16, 1 << 16
+    with _lib.test_knobs(scan_chunks=64):
+        assert _lib.workspace_size(B, D, N, L) > (8 << 20)
+        st = scan_noalloc(B=B, D=D, N=N, L=L)
+    assert st == WS, "expected MAMBA_ERR_WORKSPACE, got %d" % st
+    cfg = W.SCAN_CONFIGS["long_b1"]
+    assert _lib.workspace_size(cfg.B, cfg.D, cfg.N, cfg.L) <= (8 << 20)
+    # argument checks come first, as in mamba_scan_fwd
+    assert scan_noalloc(N=17) == UNSUP
+    assert scan_noalloc(u=None) == NULL
+    assert scan_noalloc(u=P + 2) == ALIGN
+
+
+def scan_noalloc(**kw):
+    a = dict(u=P, delta=P, z=P, Bt=P, Ct=P, A=P, Dskip=P, bias=P, y=P, fs=P, B=2, D=64, N=16, L=64,
+             ind=BF16, outd=BF16, rfs=1, flags=0)
+    a.update(kw)
+    vp = lambda v: ctypes.c_void_p(v) if v is not None else None  # noqa: E731
+    return _lib.lib().mamba_scan_fwd_noalloc(vp(a["u"]), vp(a["delta"]), vp(a["z"]), vp(a["Bt"]), vp(a["Ct"]),
+                                             vp(a["A"]), vp(a["Dskip"]), vp(a["bias"]), vp(a["y"]), vp(a["fs"]),
+                                             a["B"], a["D"], a["N"], a["L"], a["ind"], a["outd"], a["rfs"],
+                                             a["flags"], None)
