@@ -210,6 +210,12 @@ def scan_config(workload, seq_len=0):
     return cfg
 
 
+def scan_kernel_name(cfg, args):
+    """The kernel the library runs for this workload (mamba_scan_kernel)."""
+    import selective_state_space_75_amd as m
+    return m.scan_kernel(cfg.B, cfg.D, cfg.N, cfg.L)
+
+
 def bench_scan(args, dev):
     import torch
     import selective_state_space_75_amd as m
@@ -269,7 +275,8 @@ def bench_scan(args, dev):
         "vs_baseline": None, "dtype": "f32", "io_dtype": cfg.dtype, "data": "synthetic",
         "config": {"workload": cfg.name, "B": cfg.B, "D": cfg.D, "N": cfg.N, "L": cfg.L,
                    "final_state": cfg.final_state, "global_batch": cfg.B, "seq_len": cfg.L,
-                   "discretization": "delta_b" if args.delta_b else "zoh", "parallelism": "none (1 GPU)"},
+                   "discretization": "delta_b" if args.delta_b else "zoh", "parallelism": "none (1 GPU)",
+                   "scan_kernel": scan_kernel_name(cfg, args)},
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "elems_per_s": round(cfg.elements / (ms_step * 1e-3), 1),
         "kernel_ms_mean": round(kern_ms, 5), "kernel_ms_min": round(float(np.min(per_launch_ms)), 5),
@@ -689,6 +696,8 @@ def main():
                     help="scan workloads: another sequence length L (same B, D, N, dtype, seed)")
     ap.add_argument("--delta-b", action="store_true",
                     help="scan workloads: the simplified rule B-bar = delta B instead of zero-order hold")
+    ap.add_argument("--scan-kernel", default="planner", choices=["planner", "wave_tile", "row", "general"],
+                    help="diagnostic: force a scan kernel through the library's test knob")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
@@ -703,6 +712,9 @@ def main():
         copy_calibration(args, dev)
         return
     from selective_state_space_75_amd import workloads as W
+    if args.scan_kernel != "planner":
+        import selective_state_space_75_amd as m
+        m.set_test_knobs(scan_kernel=args.scan_kernel)
     if args.workload is None:
         line = headline(args, dev)
     elif args.workload == "decode48":

@@ -99,6 +99,24 @@ typedef enum {
 size_t mamba_scan_workspace_size(int64_t B, int64_t D, int64_t N, int64_t L);
 
 /*
+ * The kernel mamba_scan_fwd runs for a problem of this shape (shape only, no
+ * device query; callable without a GPU), or a negative status for an invalid
+ * shape:
+ *   MAMBA_KERNEL_GENERAL    64 channels per 4-wave workgroup, L staged in
+ *                           32-step chunks through LDS (L % 8 != 0 or L < 32);
+ *   MAMBA_KERNEL_WAVE_TILE  16 channels per wave, 16 states per lane-quad,
+ *                           optionally chunked along L or balanced over the
+ *                           SIMDs with state hand-over (L % 8 == 0, L >= 32);
+ *   MAMBA_KERNEL_ROW        16 channels per 4-wave workgroup, one state per
+ *                           lane, one pass (L % 32 == 0), chosen when the
+ *                           wave tiles would leave SIMDs idle or need chunking.
+ */
+#define MAMBA_KERNEL_GENERAL 1
+#define MAMBA_KERNEL_WAVE_TILE 2
+#define MAMBA_KERNEL_ROW 3
+int mamba_scan_kernel(int64_t B, int64_t D, int64_t N, int64_t L);
+
+/*
  * Selective scan forward over a whole sequence.
  *
  *   u, delta, z : (B, D, L) in_dtype.  `delta` is the raw step before the bias
@@ -312,9 +330,13 @@ size_t mamba_ssd_workspace_size(int64_t B, int64_t H, int64_t P, int64_t N, int6
  *   scan_chunks           > 0: mamba_scan_fwd cuts L into this many chunks
  *                         (summary pass, carry, full pass) whatever the shape;
  *                         0: the planner decides.
- *   scan_general_kernel   != 0: mamba_scan_fwd always uses the general
- *                         64-channel kernel (normally only for L % 8 != 0 or
- *                         L < 32).
+ *   scan_kernel           which kernel mamba_scan_fwd runs: 0 the planner's
+ *                         choice; 1 the general 64-channel kernel (normally
+ *                         only for L % 8 != 0 or L < 32); 2 the wave-tile
+ *                         kernel with 16 states per lane (L % 8 == 0, L >= 32);
+ *                         3 the row kernel with one state per lane
+ *                         (L % 32 == 0).  A kernel that cannot take the shape
+ *                         gives way to the planner's choice.
  *   scan_no_balance       != 0: no balanced split with state hand-over.
  *   handover_spin         >= 0: bound of a workgroup's wait for the state handed
  *                         over by the previous one, in polls (0: every split
@@ -329,7 +351,7 @@ size_t mamba_ssd_workspace_size(int64_t B, int64_t H, int64_t P, int64_t N, int6
  */
 typedef struct {
   int64_t scan_chunks;
-  int32_t scan_general_kernel;
+  int32_t scan_kernel;
   int32_t scan_no_balance;
   int64_t handover_spin;
   int64_t ssd_segments;

@@ -9,9 +9,9 @@ The computation runs in hand-written HIP kernels inside ``libmamba_scan.so``
 ``workloads`` draws the seeded synthetic inputs.
 """
 from ._lib import (FLAG_ACCURATE_EXPM1, FLAG_DELTA_B, MambaError, conv1d_fwd, conv1d_update,  # noqa: F401
-                   lib, scan_bwd, scan_bwd_workspace_size, scan_fwd, scan_fwd_noalloc, set_test_knobs, ssd_fwd, ssd_workspace_size,
+                   lib, scan_bwd, scan_bwd_workspace_size, scan_fwd, scan_fwd_noalloc, scan_kernel, set_test_knobs, ssd_fwd, ssd_workspace_size,
                    state_update, status_string, test_knobs, workspace_size)
 
 __all__ = ["scan_fwd", "scan_bwd", "scan_bwd_workspace_size", "state_update", "conv1d_fwd", "conv1d_update",
            "ssd_fwd", "ssd_workspace_size", "workspace_size", "status_string", "lib", "MambaError", "FLAG_DELTA_B",
-           "FLAG_ACCURATE_EXPM1", "set_test_knobs", "test_knobs", "scan_fwd_noalloc"]
+           "FLAG_ACCURATE_EXPM1", "set_test_knobs", "test_knobs", "scan_fwd_noalloc", "scan_kernel"]

@@ -30,7 +30,7 @@ _lib = None
 
 class TestKnobs(ctypes.Structure):
     """mamba_test_knobs_t of include/mamba_scan.h."""
-    _fields_ = [("scan_chunks", ctypes.c_int64), ("scan_general_kernel", ctypes.c_int32),
+    _fields_ = [("scan_chunks", ctypes.c_int64), ("scan_kernel", ctypes.c_int32),
                 ("scan_no_balance", ctypes.c_int32), ("handover_spin", ctypes.c_int64),
                 ("ssd_segments", ctypes.c_int64)]
 
@@ -72,6 +72,8 @@ def lib() -> ctypes.CDLL:
             L.mamba_ssd_fwd.restype = c_int
             L.mamba_ssd_workspace_size.argtypes = [i64] * 5
             L.mamba_ssd_workspace_size.restype = ctypes.c_size_t
+            L.mamba_scan_kernel.argtypes = [i64, i64, i64, i64]
+            L.mamba_scan_kernel.restype = c_int
             L.mamba_set_test_knobs.argtypes = [ctypes.POINTER(TestKnobs)]
             L.mamba_set_test_knobs.restype = c_int
             L.mamba_status_string.argtypes = [c_int]
@@ -87,11 +89,15 @@ def status_string(status: int) -> str:
         return "?"
 
 
-def set_test_knobs(scan_chunks: int = 0, scan_general_kernel: bool = False, scan_no_balance: bool = False,
+SCAN_KERNELS = {"planner": 0, "general": 1, "wave_tile": 2, "row": 3}
+
+
+def set_test_knobs(scan_chunks: int = 0, scan_kernel: str = "planner", scan_no_balance: bool = False,
                    handover_spin: int = -1, ssd_segments: int = 0) -> None:
     """Process-wide test knobs of the library (mamba_set_test_knobs); no
-    arguments restores the defaults."""
-    k = TestKnobs(scan_chunks, int(scan_general_kernel), int(scan_no_balance), handover_spin, ssd_segments)
+    arguments restores the defaults.  scan_kernel: planner, general,
+    wave_tile or row."""
+    k = TestKnobs(scan_chunks, SCAN_KERNELS[scan_kernel], int(scan_no_balance), handover_spin, ssd_segments)
     st = lib().mamba_set_test_knobs(ctypes.byref(k))
     if st != 0:
         raise MambaError(st, "mamba_set_test_knobs")
@@ -112,6 +118,14 @@ class test_knobs:  # noqa: N801 (used as a context manager)
     def __exit__(self, *exc):
         set_test_knobs()
         return False
+
+
+def scan_kernel(B: int, D: int, N: int, L: int) -> str:
+    """Name of the kernel mamba_scan_fwd runs for this shape (mamba_scan_kernel)."""
+    k = lib().mamba_scan_kernel(B, D, N, L)
+    if k < 0:
+        raise MambaError(k, "mamba_scan_kernel")
+    return {1: "general", 2: "wave_tile", 3: "row"}[k]
 
 
 def workspace_size(B: int, D: int, N: int, L: int) -> int:

@@ -18,6 +18,8 @@ constexpr int64_t kMaxElems = int64_t(1) << 46;
 constexpr int64_t kV4Step = 32;       // the wave-tile kernel's chunk: L at least this, and a multiple of 8
 constexpr int64_t kV4Tile = 16;       // channels per wave in the wave-tile kernel
 constexpr int64_t kGroupsPlan = 1024; // waves of the balanced split (one per SIMD on MI355X)
+constexpr int64_t kRowStep = 32;      // the row kernel's chunk: L a multiple of this
+constexpr int64_t kCUsPlan = 256;     // compute units the plan assumes (MI355X)
 constexpr size_t kHandOverBytes = kV4Tile * 16 * sizeof(float);
 
 struct Plan {
@@ -25,6 +27,7 @@ struct Plan {
   int64_t n_chunks = 1;
   int64_t chunk_len = 0;
   bool v4 = false;          // the wave-tile kernel (L a multiple of 8, L >= 32)
+  bool row = false;         // the row kernel (one state per lane, L a multiple of 32)
   bool balanced = false;    // equal (tile x time) ranges with state hand-over
   size_t ws_bytes = 0;
   size_t off_local = 0, off_start = 0, off_sum = 0;
@@ -64,15 +67,45 @@ double v4_chunk_cost(int64_t tiles, int64_t k) {
   return full + summary;
 }
 
-// Shape-only plan (no device query).  One pass per channel tile while there
-// are enough tiles to occupy the GPU; otherwise (few channels, long L) split L
-// into chunks of at least 2048 steps: for the wave-tile kernel the number of
-// chunks that minimises v4_chunk_cost, for the general kernel about 1024
-// workgroups.
+// Relative time of the row kernel (one state per lane, a 16-channel tile per
+// 4-wave workgroup, up to three workgroups per CU) in the units of
+// v4_chunk_cost.  Measured per 2048 steps on MI355X: 68 us with one workgroup
+// per CU, 156 us with three, against 190 us for a wave-tile pass of one tile
+// per SIMD; in between about 24 + 44 k us for k workgroups per CU.
+double row_cost(int64_t wgs) {
+  const int64_t per_cu = (wgs + kCUsPlan - 1) / kCUsPlan;
+  const int64_t full = per_cu / 3, rem = per_cu % 3;
+  return (full * 156.0 + (rem ? 24.0 + 44.0 * rem : 0.0)) / 190.0;
+}
+
+// Shape-only plan (no device query).  The row kernel when L is a multiple of
+// 32 and its cost model beats the wave-tile kernel's (few 16-channel tiles:
+// the 130M layer, the batch-1 long sequence); else one pass per channel tile
+// while there are enough tiles to occupy the GPU; otherwise (few channels,
+// long L) split L into chunks of at least 2048 steps: for the wave-tile
+// kernel the number of chunks that minimises v4_chunk_cost, for the general
+// kernel about 1024 workgroups.
 Plan make_plan(int64_t B, int64_t D, int64_t N, int64_t L, const mamba_test_knobs_t& kn) {
   Plan p;
   p.tiles_d = (D + kTile - 1) / kTile;
-  p.v4 = (L % 8 == 0) && L >= kV4Step && !kn.scan_general_kernel;
+  p.v4 = (L % 8 == 0) && L >= kV4Step && kn.scan_kernel != 1;
+  const bool row_ok = L % kRowStep == 0 && kn.scan_kernel != 1 && kn.scan_kernel != 2 && kn.scan_chunks == 0;
+  if (row_ok) {
+    const int64_t tiles16 = B * ((D + kV4Tile - 1) / kV4Tile);
+    bool row = kn.scan_kernel == 3;
+    if (!row) {
+      double best = v4_chunk_cost(tiles16, 1);
+      const int64_t kmax = L >= 4096 && tiles16 < kGroupsPlan ? (L / 2048 < 64 ? L / 2048 : 64) : 1;
+      for (int64_t c = 2; c <= kmax; ++c) best = v4_chunk_cost(tiles16, c) < best ? v4_chunk_cost(tiles16, c) : best;
+      row = row_cost(tiles16) < best;
+    }
+    if (row) {
+      p.row = true;
+      p.v4 = false;
+      p.tiles_d = (D + kV4Tile - 1) / kV4Tile;
+      return p;   // one pass, no workspace
+    }
+  }
   // Units of independent sequential work: 16-channel tiles (wave-tile
   // kernel) or 64-channel tiles (general kernel).
   const int64_t tiles = p.v4 ? B * ((D + kV4Tile - 1) / kV4Tile) : B * p.tiles_d;
@@ -291,8 +324,9 @@ int scan_fwd_run(const void* u, const void* delta, const void* z, const void* Bt
     if (e != hipSuccess) return MAMBA_ERR_HIP;
     if (mamba::launch_scan_carry(p, stream) != hipSuccess) return MAMBA_ERR_HIP;
   }
-  const hipError_t e = plan.v4 ? mamba::launch_scan_v4(p, q, in, out, false, stream)
-                               : mamba::launch_scan_full(p, in, out, stream);
+  const hipError_t e = plan.row ? mamba::launch_scan_row(p, in, out, stream)
+                       : plan.v4 ? mamba::launch_scan_v4(p, q, in, out, false, stream)
+                                 : mamba::launch_scan_full(p, in, out, stream);
   if (e != hipSuccess) return MAMBA_ERR_HIP;
   return MAMBA_OK;
 }
@@ -328,6 +362,13 @@ extern "C" {
 size_t mamba_scan_workspace_size(int64_t B, int64_t D, int64_t N, int64_t L) {
   if (!shape_ok(B, D, N, L) || N > 16) return (size_t)-1;
   return make_plan(B, D, N, L, knobs()).ws_bytes;
+}
+
+int mamba_scan_kernel(int64_t B, int64_t D, int64_t N, int64_t L) {
+  if (!shape_ok(B, D, N, L)) return MAMBA_ERR_SHAPE;
+  if (N > 16) return MAMBA_ERR_UNSUPPORTED;
+  const Plan p = make_plan(B, D, N, L, knobs());
+  return p.row ? MAMBA_KERNEL_ROW : p.v4 ? MAMBA_KERNEL_WAVE_TILE : MAMBA_KERNEL_GENERAL;
 }
 
 int mamba_set_test_knobs(const mamba_test_knobs_t* k) {

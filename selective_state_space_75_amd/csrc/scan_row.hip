@@ -1,0 +1,341 @@
+// scan_row.hip -- selective-scan kernel with one state per lane (gfx950), for
+// shapes with few channel tiles: the batch-1 long sequence and other layers
+// whose 16-channel tiles do not fill the chip.  Same computation as
+// scan_v4.hpp ("Mamba 模型", full-step flowchart nodes H to M; ZOH per
+// "Mamba模型：高效序列建模的新突破" 3.1): softplus step, ZOH discretisation,
+// recurrence, readout, skip, gate.
+//
+// Layout -- a workgroup of 4 waves owns 16 channels of one batch row:
+//  * wave w holds channels 4w .. 4w+3, one per 16-lane DPP row; lane n of a
+//    row holds state n in a VGPR (N <= 16; lanes past N hold a zero state).
+//    A tile therefore occupies 4 SIMDs instead of one, so a sequence that
+//    would need chunking along L with 16 states per lane (summary pass, carry
+//    and a rescan) is scanned in a single pass;
+//  * the sequence is walked in 32-step chunks.  Lane j of a row loads
+//    elements 2j, 2j+1 of its channel's u, delta_raw and z (one 4-byte load
+//    each for bf16), evaluates softplus and the gate for them once, and later
+//    owns their two outputs.  Step t reads delta and u from lane t/2 of the
+//    row through a DPP row broadcast (row_newbcast) folded into the consuming
+//    multiply;
+//  * B_t and C_t of a chunk are staged once per workgroup in LDS as fp32,
+//    state-major with padded rows, double-buffered; a lane reads 4 steps of
+//    its state with one 16-byte read (the 4 rows of a wave read the same
+//    addresses).  One workgroup barrier per chunk guards the buffers;
+//  * the readout's per-state products C_t,n h_t,n go through LDS once per
+//    chunk: each lane writes its 32 products, then reads the 16 products of
+//    each of its 2 output steps and sums them (15 adds per output).
+// Per state update: 6 fp32 VALU + 1 v_exp_f32, as in the 4-states-per-lane
+// kernel, plus a quarter of a 16-byte LDS read each for B_t and C_t.
+#include "device_math.hpp"
+#include "kernels.hpp"
+
+namespace mamba {
+namespace {
+
+constexpr int kRCT = 32;          // steps per chunk
+constexpr int kBCRow = 36;        // floats per staged B/C row (32 + padding)
+constexpr int kPRowR = 36;        // floats per partial-readout row (32 + padding)
+constexpr int kPWave = 4 * 16 * kPRowR + 32;   // floats per wave of partial readouts (+32: row-block skew)
+
+struct alignas(16) RowLds {
+  float bc[2][2][16 * kBCRow];    // [buffer][B, C][state * kBCRow + step]
+  float part[4 * kPWave];         // [wave][row][state][step] partial readouts
+};
+
+// Value of lane k of this lane's 16-lane row (DPP row_newbcast); folded by
+// the compiler into the VOP2 instruction that consumes it.
+template <int k>
+__device__ __forceinline__ float row_bcast(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x150 + k, 0xF, 0xF, true));
+}
+
+template <bool kBF16> struct Raw2;                       // 2 consecutive elements
+template <> struct Raw2<true> { uint32_t w; };
+template <> struct Raw2<false> { float2 v; };
+
+template <bool kBF16>
+__device__ __forceinline__ Raw2<kBF16> load2(const void* base, int64_t off) {
+  Raw2<kBF16> r;
+  if constexpr (kBF16) r.w = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(base) + off);
+  else r.v = *reinterpret_cast<const float2*>(static_cast<const float*>(base) + off);
+  return r;
+}
+template <bool kBF16>
+__device__ __forceinline__ float at2(const Raw2<kBF16>& r, int j) {
+  if constexpr (kBF16) return j ? bf16_hi(r.w) : bf16_lo(r.w);
+  else return j ? r.v.y : r.v.x;
+}
+
+template <bool kBF16> struct Raw4;                       // 4 consecutive elements (B/C staging)
+template <> struct Raw4<true> { uint2 w; };
+template <> struct Raw4<false> { float4 v; };
+
+template <bool kBF16>
+__device__ __forceinline__ Raw4<kBF16> load4(const void* base, int64_t off, bool ok) {
+  Raw4<kBF16> r;
+  if constexpr (kBF16) {
+    r.w = ok ? *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + off) : make_uint2(0, 0);
+  } else {
+    r.v = ok ? *reinterpret_cast<const float4*>(static_cast<const float*>(base) + off) : make_float4(0, 0, 0, 0);
+  }
+  return r;
+}
+template <bool kBF16>
+__device__ __forceinline__ float4 widen4(const Raw4<kBF16>& r) {
+  if constexpr (kBF16) return make_float4(bf16_lo(r.w.x), bf16_hi(r.w.x), bf16_lo(r.w.y), bf16_hi(r.w.y));
+  else return r.v;
+}
+
+// s_waitcnt lgkmcnt(0) (vmcnt and expcnt left at their maximum): this wave's
+// LDS writes are complete, its global loads may still be in flight.
+__device__ __forceinline__ void lds_wait_all() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Workgroup barrier that waits only for LDS: the prefetched global loads stay
+// in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  lds_wait_all();
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+template <int M> struct Tag { static constexpr int kValue = M; };
+
+template <int I, int E, typename F>
+__device__ __forceinline__ void unroll(F&& f) {
+  if constexpr (I < E) {
+    f(Tag<I>{});
+    unroll<I + 1, E>(f);
+  }
+}
+
+template <bool kInBF16>
+struct RowRaw {
+  Raw2<kInBF16> u, d, z;     // this lane's 2 elements of its channel
+  Raw4<kInBF16> bc;          // 4 steps of one B or C row (staging role)
+};
+
+template <bool kInBF16, bool kOutBF16, int kMode>
+__device__ __forceinline__ void row_scan(const ScanParams& p, RowLds& s, int64_t b, int64_t d0) {
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63;
+  const int r = lane >> 4, n = lane & 15;
+  const int64_t D = p.D, N = p.N, L = p.L;
+  const int64_t d = d0 + 4 * w + r;
+  const bool c_ok = d < D;
+  const bool n_ok = n < N;
+  const int64_t row = (b * D + (c_ok ? d : 0)) * L;
+
+  // per-lane constants
+  float a = (c_ok && n_ok) ? p.A[(c_ok ? d : 0) * N + n] : -1.0f;
+  if (__builtin_fabsf(a) < 0x1p-40f) a = (a > 0.0f) ? 0x1p-40f : -0x1p-40f;
+  const float a2 = a * kLog2e, ia = 1.0f / a;
+  const float bias = !c_ok ? -__builtin_inff() : (p.bias ? p.bias[d] : 0.0f);
+  const float dskip = (c_ok && p.Dskip) ? p.Dskip[d] : 0.0f;
+  const bool want_z = p.z != nullptr;
+  const void* z_src = p.z ? p.z : p.u;
+
+  // B/C staging role: threads 0..127 stage B, 128..255 C; state sn, steps 4*sg .. 4*sg+3
+  const int s_arr = tid >> 7, sn = (tid >> 3) & 15, sg = tid & 7;
+  const bool s_ok = sn < N;
+  const void* s_base = s_arr ? p.Ct : p.Bt;
+  const int64_t s_row = (b * N + (s_ok ? sn : 0)) * L;
+
+  const int64_t nck = L / kRCT;
+  auto fetch = [&](int64_t ck, RowRaw<kInBF16>& raw) {
+    const int64_t c = ck < nck ? ck : nck - 1;     // clamp: prefetch past the end re-reads the last chunk
+    const int64_t t0 = c * kRCT;
+    raw.u = load2<kInBF16>(p.u, row + t0 + 2 * n);
+    raw.d = load2<kInBF16>(p.delta, row + t0 + 2 * n);
+    raw.z = load2<kInBF16>(z_src, row + t0 + 2 * n);
+    raw.bc = load4<kInBF16>(s_base, s_row + t0 + 4 * sg, s_ok);
+  };
+  auto stage = [&](const RowRaw<kInBF16>& raw, int buf) {
+    *reinterpret_cast<float4*>(&s.bc[buf][s_arr][sn * kBCRow + 4 * sg]) = widen4<kInBF16>(raw.bc);
+  };
+
+  float h = 0.0f;
+  RowRaw<kInBF16> raw[2];
+  float dv[2][2], uv[2][2], gv[2][2];   // [chunk parity][element]: delta, u, gate of this lane's 2 elements
+  float duv[2][2];                       // delta * u (the simplified rule's per-step factor)
+  float q[32];                           // partial readouts of the previous chunk: q[2 * n' + j]
+  auto prep = [&](const RowRaw<kInBF16>& rr, int par, int j) {
+    dv[par][j] = softplus(at2<kInBF16>(rr.d, j) + bias);
+    uv[par][j] = at2<kInBF16>(rr.u, j);
+    const float gz = silu(at2<kInBF16>(rr.z, j));
+    gv[par][j] = want_z ? gz : 1.0f;
+    if constexpr (kMode == kDeltaB) duv[par][j] = dv[par][j] * uv[par][j];
+  };
+  float* prow = &s.part[w * kPWave + r * (16 * kPRowR + 8) + n * kPRowR];   // this lane's product row
+  const float* pread = &s.part[w * kPWave + r * (16 * kPRowR + 8) + 2 * n]; // its outputs' column pair
+
+  fetch(0, raw[0]);
+  fetch(1, raw[1]);
+  stage(raw[0], 0);
+  prep(raw[0], 0, 0);
+  prep(raw[0], 0, 1);
+#pragma unroll
+  for (int i = 0; i < 32; ++i) q[i] = 0.0f;
+  uv[1][0] = uv[1][1] = gv[1][0] = gv[1][1] = 0.0f;
+  lds_barrier();
+
+  auto chunk = [&](auto ptag, int64_t ck) {
+    constexpr int P = decltype(ptag)::kValue;
+    constexpr int Q = P ^ 1;
+    const int64_t t0 = ck * kRCT;
+    fetch(ck + 2, raw[P]);          // chunk ck+2 has the parity of ck; raw[P] was consumed by chunk ck-1
+    const float* Bs = &s.bc[P][0][n * kBCRow];
+    const float* Cs = &s.bc[P][1][n * kBCRow];
+    float4 Bq[3], Cq[3];            // B, C of 4-step groups g, g+1, g+2 (rotating)
+    Bq[0] = *reinterpret_cast<const float4*>(Bs + 0);
+    Cq[0] = *reinterpret_cast<const float4*>(Cs + 0);
+    Bq[1] = *reinterpret_cast<const float4*>(Bs + 4);
+    Cq[1] = *reinterpret_cast<const float4*>(Cs + 4);
+    float e[2][4], in[2][4], o[2];  // [group parity][step of the group]: Abar and Bbar u, prepared a group ahead
+    // state-independent part of step t: Abar and Bbar u
+    auto pre = [&](auto tt, float& ee, float& ii) {
+      constexpr int t = decltype(tt)::kValue;
+      const float4& B4 = Bq[(t / 4) % 3];
+      const float bn = (t % 4 == 0) ? B4.x : (t % 4 == 1) ? B4.y : (t % 4 == 2) ? B4.z : B4.w;
+      const float x = row_bcast<t / 2>(dv[P][t % 2]) * a2;
+      ee = hw_exp2(x);
+      if constexpr (kMode == kDeltaB) {
+        ii = row_bcast<t / 2>(duv[P][t % 2]) * bn;
+      } else {
+        const float kc = (kMode == kZohFast) ? __builtin_fmaf(ee, ia, -ia) : expm1_from_exp2(x, ee) * ia;
+        ii = kc * (row_bcast<t / 2>(uv[P][t % 2]) * bn);
+      }
+    };
+    // the four steps of a group: four independent chains, so that their
+    // latencies overlap even with a single wave on the SIMD
+    auto pre_group = [&](auto gt) {
+      constexpr int G = decltype(gt)::kValue;
+      unroll<0, 4>([&](auto it) {
+        constexpr int i = decltype(it)::kValue;
+        pre(Tag<4 * G + i>{}, e[G & 1][i], in[G & 1][i]);
+      });
+    };
+    pre_group(Tag<0>{});
+    unroll<0, kRCT / 4>([&](auto gc) {
+      constexpr int G = decltype(gc)::kValue;
+      // Keep the pipeline as written: the scheduler would otherwise sink the
+      // LDS reads of later groups next to their use.
+      __builtin_amdgcn_sched_barrier(0);
+      // B/C of group G + 2, two groups ahead
+      if constexpr (G + 2 < kRCT / 4) {
+        Bq[(G + 2) % 3] = *reinterpret_cast<const float4*>(Bs + 4 * G + 8);
+        Cq[(G + 2) % 3] = *reinterpret_cast<const float4*>(Cs + 4 * G + 8);
+      }
+      // outputs of the previous chunk (parity Q) in the first half: output j
+      // over groups 2j, 2j+1, 8 of its 16 products per group
+      if constexpr (G < 4) {
+        constexpr int j = G / 2;            // output j: step 2n + j of chunk ck-1
+        constexpr int m0 = 8 * (G % 2);     // products of states m0 .. m0+7
+        const float s0 = (q[2 * m0 + j] + q[2 * (m0 + 1) + j]) + (q[2 * (m0 + 2) + j] + q[2 * (m0 + 3) + j]);
+        const float s1 = (q[2 * (m0 + 4) + j] + q[2 * (m0 + 5) + j]) + (q[2 * (m0 + 6) + j] + q[2 * (m0 + 7) + j]);
+        if constexpr (G % 2 == 0) o[j] = s0 + s1;
+        else o[j] = __builtin_fmaf(dskip, uv[Q][j], o[j] + (s0 + s1)) * gv[Q][j];
+      }
+      if constexpr (G == 4) {
+        if (c_ok && ck > 0) {
+          const int64_t at = row + t0 - kRCT + 2 * n;
+          if constexpr (kOutBF16) *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(p.y) + at) = pack_bf16x2(o[0], o[1]);
+          else *reinterpret_cast<float2*>(static_cast<float*>(p.y) + at) = make_float2(o[0], o[1]);
+        }
+      }
+      // unpack the next chunk (parity Q) in the second half, after its u and gate were used above
+      if constexpr (G == 4) prep(raw[Q], Q, 0);
+      if constexpr (G == 5) prep(raw[Q], Q, 1);
+      if constexpr (G == 6) stage(raw[Q], Q);
+      // the next group's state-independent part, then this group's recurrence and products
+      if constexpr (G + 1 < kRCT / 4) pre_group(Tag<G + 1>{});
+      const float4& C4 = Cq[G % 3];
+      float pt[4];
+      h = __builtin_fmaf(e[G & 1][0], h, in[G & 1][0]);
+      pt[0] = C4.x * h;
+      h = __builtin_fmaf(e[G & 1][1], h, in[G & 1][1]);
+      pt[1] = C4.y * h;
+      h = __builtin_fmaf(e[G & 1][2], h, in[G & 1][2]);
+      pt[2] = C4.z * h;
+      h = __builtin_fmaf(e[G & 1][3], h, in[G & 1][3]);
+      pt[3] = C4.w * h;
+      *reinterpret_cast<float4*>(prow + 4 * G) = make_float4(pt[0], pt[1], pt[2], pt[3]);
+    });
+    // all of this chunk's B/C reads and the next chunk's staging are done by
+    // every wave; this wave's products are in LDS (in order before the reads below)
+    lds_barrier();
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      const float2 v = *reinterpret_cast<const float2*>(pread + m * kPRowR);
+      q[2 * m] = v.x;
+      q[2 * m + 1] = v.y;
+    }
+  };
+  for (int64_t ck = 0;; ck += 2) {
+    chunk(Tag<0>{}, ck);
+    if (ck + 1 >= nck) {
+      // outputs of the last chunk (parity 0)
+      float o0 = 0.0f, o1 = 0.0f;
+#pragma unroll
+      for (int m = 0; m < 16; ++m) { o0 += q[2 * m]; o1 += q[2 * m + 1]; }
+      o0 = __builtin_fmaf(dskip, uv[0][0], o0) * gv[0][0];
+      o1 = __builtin_fmaf(dskip, uv[0][1], o1) * gv[0][1];
+      if (c_ok) {
+        const int64_t at = row + ck * kRCT + 2 * n;
+        if constexpr (kOutBF16) *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(p.y) + at) = pack_bf16x2(o0, o1);
+        else *reinterpret_cast<float2*>(static_cast<float*>(p.y) + at) = make_float2(o0, o1);
+      }
+      break;
+    }
+    chunk(Tag<1>{}, ck + 1);
+    if (ck + 2 >= nck) {
+      float o0 = 0.0f, o1 = 0.0f;
+#pragma unroll
+      for (int m = 0; m < 16; ++m) { o0 += q[2 * m]; o1 += q[2 * m + 1]; }
+      o0 = __builtin_fmaf(dskip, uv[1][0], o0) * gv[1][0];
+      o1 = __builtin_fmaf(dskip, uv[1][1], o1) * gv[1][1];
+      if (c_ok) {
+        const int64_t at = row + (ck + 1) * kRCT + 2 * n;
+        if constexpr (kOutBF16) *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(p.y) + at) = pack_bf16x2(o0, o1);
+        else *reinterpret_cast<float2*>(static_cast<float*>(p.y) + at) = make_float2(o0, o1);
+      }
+      break;
+    }
+  }
+  if (p.final_state != nullptr && c_ok && n_ok) p.final_state[(b * D + d) * N + n] = h;
+}
+
+template <bool kInBF16, bool kOutBF16>
+__global__ __launch_bounds__(256) void scan_row_kernel(ScanParams p) {
+  __shared__ RowLds s;
+  const int64_t tiles_d = (p.D + 15) / 16;
+  const int64_t b = (int64_t)blockIdx.x / tiles_d;
+  const int64_t d0 = ((int64_t)blockIdx.x - b * tiles_d) * 16;
+  // the discretisation loop, uniform over the workgroup: the cancellation-free
+  // quotient when asked for or when any |A| of the tile is small
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t d = d0 + 4 * w + (lane >> 4);
+  const int n = lane & 15;
+  const bool small_a = d < p.D && n < p.N && __builtin_fabsf(p.A[d * p.N + n]) < kFastZohMinAbsA;
+  const int any_small = __syncthreads_or(small_a ? 1 : 0);
+  if (p.delta_b) row_scan<kInBF16, kOutBF16, kDeltaB>(p, s, b, d0);
+  else if (p.accurate || any_small) row_scan<kInBF16, kOutBF16, kZohAccurate>(p, s, b, d0);
+  else row_scan<kInBF16, kOutBF16, kZohFast>(p, s, b, d0);
+}
+
+template <bool kInBF16, bool kOutBF16>
+hipError_t launch_row_t(const ScanParams& p, hipStream_t st) {
+  const int64_t grid = p.B * ((p.D + 15) / 16);
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL((scan_row_kernel<kInBF16, kOutBF16>), dim3((unsigned)grid), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_scan_row(const ScanParams& p, Dt in, Dt out, hipStream_t s) {
+  if (in == Dt::BF16) return out == Dt::BF16 ? launch_row_t<true, true>(p, s) : launch_row_t<true, false>(p, s);
+  return out == Dt::BF16 ? launch_row_t<false, true>(p, s) : launch_row_t<false, false>(p, s);
+}
+
+}  // namespace mamba

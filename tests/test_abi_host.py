@@ -29,7 +29,8 @@ def declared_functions():
 def test_header_symbols_are_exported():
     names = declared_functions()
     assert names == ["mamba_conv1d_fwd", "mamba_conv1d_update", "mamba_scan_bwd", "mamba_scan_bwd_workspace_size",
-                     "mamba_scan_fwd", "mamba_scan_fwd_noalloc", "mamba_scan_workspace_size", "mamba_set_test_knobs",
+                     "mamba_scan_fwd", "mamba_scan_fwd_noalloc", "mamba_scan_kernel", "mamba_scan_workspace_size",
+                     "mamba_set_test_knobs",
                      "mamba_ssd_fwd",
                      "mamba_ssd_workspace_size", "mamba_state_update", "mamba_status_string"]
     L = _lib.lib()
@@ -54,17 +55,24 @@ def test_workspace_size_plan():
     # L % 32 != 0 but L % 8 == 0: the same kernel, its last chunk shifted back
     assert ws(4, 5120, 16, 2040) == 1024 * 8 + 1024 * 16 * 16 * 4
     assert ws(4, 5120, 16, 2044) == 0      # L % 8 != 0: general kernel, no hand-over
-    n = ws(1, 4096, 16, 131072)
-    # 256 tiles of 16 channels -> 5 chunks (a summary pass of 4 x 256 waves,
-    # a full pass of 5 x 256 (chunk, tile) pairs balanced over 1024 waves):
-    # h_local and h_start (K, B, D, N) fp32, sum of delta (K, B, D) fp32, then
-    # the hand-over flags and slots
-    assert n == 2 * 5 * 4096 * 16 * 4 + 5 * 4096 * 4 + 1024 * 8 + 1024 * 16 * 16 * 4
-    # 512 tiles -> 3 chunks; 64 tiles -> 17 chunks; 768 tiles: one pass
-    assert ws(2, 4096, 16, 65536) == 2 * 3 * 2 * 4096 * 16 * 4 + 3 * 2 * 4096 * 4 + 1024 * 8 + 1024 * 16 * 16 * 4
+    # the batch-1 long sequence: the row kernel, one pass, no workspace
+    assert ws(1, 4096, 16, 131072) == 0
+    assert ws(2, 4096, 16, 65536) == 0      # 512 tiles: the row kernel too
+    with _lib.test_knobs(scan_kernel="wave_tile"):
+        n = ws(1, 4096, 16, 131072)
+        # 256 tiles of 16 channels -> 5 chunks (a summary pass of 4 x 256 waves,
+        # a full pass of 5 x 256 (chunk, tile) pairs balanced over 1024 waves):
+        # h_local and h_start (K, B, D, N) fp32, sum of delta (K, B, D) fp32, then
+        # the hand-over flags and slots
+        assert n == 2 * 5 * 4096 * 16 * 4 + 5 * 4096 * 4 + 1024 * 8 + 1024 * 16 * 16 * 4
+        # 512 tiles -> 3 chunks; 768 tiles: one pass
+        assert ws(2, 4096, 16, 65536) == 2 * 3 * 2 * 4096 * 16 * 4 + 3 * 2 * 4096 * 4 + 1024 * 8 + \
+            1024 * 16 * 16 * 4
+        assert ws(8, 1536, 16, 65536) == 0
+    # 64 tiles: few enough that chunking the wave-tile kernel (17 chunks) beats
+    # the row kernel's 64 workgroups on 256 CUs
     assert ws(1, 1024, 16, 65536) == 2 * 17 * 1024 * 16 * 4 + 17 * 1024 * 4 + 1024 * 8 + 1024 * 16 * 16 * 4
-    assert ws(8, 1536, 16, 65536) == 0
-    # a ragged last chunk (L % 32 == 24) plans like L = 131072: 5 chunks
+    # a ragged last chunk (L % 32 == 24) cannot take the row kernel: 5 chunks as above
     assert ws(1, 4096, 16, 131072 - 8) == n
     # the general kernel (L % 8 != 0) plans with 64-channel tiles: 16 chunks
     assert ws(1, 4096, 16, 131072 - 4) == 2 * 16 * 4096 * 16 * 4 + 16 * 4096 * 4
@@ -135,9 +143,9 @@ def update(**kw):
     (dict(A=None), NULL), (dict(y=None), NULL), (dict(fs=None), NULL),
     (dict(u=P + 2), ALIGN), (dict(z=P + 8), ALIGN), (dict(y=P + 4), ALIGN), (dict(Ct=P + 2), ALIGN),
     (dict(A=P + 2), ALIGN), (dict(fs=P + 1), ALIGN),
-    # batch-1 long sequence needs a workspace
-    (dict(B=1, D=4096, L=131072), WS),
-    (dict(B=1, D=4096, L=131072, ws=P, wsb=1024), WS),
+    # the 2.8B layer's balanced split needs a workspace (hand-over slots)
+    (dict(B=4, D=5120, L=2048), WS),
+    (dict(B=4, D=5120, L=2048, ws=P, wsb=1024), WS),
 ])
 def test_scan_rejects_bad_arguments(kw, code):
     assert scan(**kw) == code
@@ -147,7 +155,7 @@ def test_scan_optional_pointers_do_not_trigger_errors_early():
     # z, Dskip, bias may be NULL and final state is ignored when not requested;
     # with everything else valid but the workspace missing, the workspace error
     # is what comes back (so no launch happens).
-    st = scan(z=None, Dskip=None, bias=None, fs=None, rfs=0, B=1, D=4096, L=131072)
+    st = scan(z=None, Dskip=None, bias=None, fs=None, rfs=0, B=4, D=5120, L=2048)
     assert st == WS
 
 
@@ -324,3 +332,28 @@ def scan_noalloc(**kw):
                                              vp(a["A"]), vp(a["Dskip"]), vp(a["bias"]), vp(a["y"]), vp(a["fs"]),
                                              a["B"], a["D"], a["N"], a["L"], a["ind"], a["outd"], a["rfs"],
                                              a["flags"], None)
+
+
+def test_scan_kernel_choice():
+    """The planner's kernel per workload: the row kernel where 16-channel wave
+    tiles would leave SIMDs idle or need chunking (130M layer, batch-1 long
+    sequence), the wave-tile kernel's balanced split at the 2.8B layer and for
+    ragged lengths, chunking of the wave-tile kernel for very few tiles, the
+    general kernel for L % 8 != 0."""
+    k = _lib.scan_kernel
+    assert k(8, 1536, 16, 2048) == "row"
+    assert k(1, 4096, 16, 131072) == "row"
+    assert k(4, 5120, 16, 2048) == "wave_tile"
+    assert k(1, 4096, 16, 131072 - 8) == "wave_tile"
+    assert k(1, 1024, 16, 65536) == "wave_tile"
+    assert k(2, 100, 16, 100) == "general"
+    assert k(1, 16, 16, 16) == "general"
+    with _lib.test_knobs(scan_kernel="wave_tile"):
+        assert k(8, 1536, 16, 2048) == "wave_tile"
+    with _lib.test_knobs(scan_kernel="row"):
+        assert k(4, 5120, 16, 2048) == "row"
+        assert k(4, 5120, 16, 2040) == "wave_tile"    # the row kernel needs L % 32 == 0
+    with _lib.test_knobs(scan_kernel="general"):
+        assert k(4, 5120, 16, 2048) == "general"
+    assert _lib.lib().mamba_scan_kernel(1, 1, 17, 1) == UNSUP
+    assert _lib.lib().mamba_scan_kernel(0, 1, 1, 1) == SHAPE

@@ -22,26 +22,31 @@ from selective_state_space_75_amd import workloads as W
 pytestmark = pytest.mark.gpu
 
 
-def _full_compare(name, dev, out_dtypes):
-    """Runs the workload once per output dtype and compares every output and
-    the final state against the oracle, which runs once in channel blocks."""
+def _full_compare(name, dev, out_dtypes, kernels=("planner",)):
+    """Runs the workload once per output dtype (and kernel) and compares every
+    output and the final state against the oracle, which runs once in channel
+    blocks.  Keys of the result: the output dtype, or (kernel, dtype)."""
     import torch
+    import selective_state_space_75_amd as m
     cfg = W.SCAN_CONFIGS[name]
     log("[%s full] B=%d D=%d N=%d L=%d: drawing inputs" % (name, cfg.B, cfg.D, cfg.N, cfg.L))
     x = W.scan_inputs(cfg)
     t = upload_scan(x, dev)
     outs = {}
-    for odt in out_dtypes:
-        log("[%s full] GPU scan, %s output" % (name, odt))
-        outs[odt] = gpu_scan(t, return_final_state=True, out_dtype=odt)
+    for kern in kernels:
+        for odt in out_dtypes:
+            log("[%s full] GPU scan, %s kernel, %s output" % (name, kern, odt))
+            with m.test_knobs(scan_kernel=kern):
+                out = gpu_scan(t, return_final_state=True, out_dtype=odt)
+            outs[odt if len(kernels) == 1 else (kern, odt)] = out
     torch.cuda.synchronize()
     del t
-    errs = {odt: (BlockErr(), BlockErr()) for odt in out_dtypes}
+    errs = {key: (BlockErr(), BlockErr()) for key in outs}
     floor = BlockErr()
     nblk = 0
     for b, d0, d1, yr, hr in oracle_scan_blocks(x, block=256):
-        for odt, (ey, eh) in errs.items():
-            y, hN = outs[odt]
+        for key, (ey, eh) in errs.items():
+            y, hN = outs[key]
             ey.add(from_dev(y[b, d0:d1]), yr)
             eh.add(from_dev(hN[b, d0:d1]), hr)
         floor.add(W.as_f32(W.f32_to_bf16_bits(yr.astype(np.float32))), yr)
@@ -52,22 +57,26 @@ def _full_compare(name, dev, out_dtypes):
 
 
 def test_long_b1_all_channels(dev):
-    """Every output of the chunked long scan, bf16 and fp32 output."""
+    """Every output of the long scan, bf16 and fp32 output, on the planner's
+    kernel (one state per lane, one pass) and on the wave-tile kernel's
+    chunked path (summary, carry, balanced full pass)."""
     import torch
     import selective_state_space_75_amd as m
     cfg = W.SCAN_CONFIGS["long_b1"]
-    assert m.workspace_size(cfg.B, cfg.D, cfg.N, cfg.L) > 0, "long sequence should take the chunked path"
-    errs, floor = _full_compare("long_b1", dev, (torch.bfloat16, torch.float32))
-    ey, eh = errs[torch.bfloat16]
-    log("  long_b1 y bf16: rel_l2=%.3e (bf16 floor %.3e) max_abs/max|y|=%.3e; final state rel_l2=%.3e"
-        % (ey.rel_l2, floor.rel_l2, ey.max_abs_frac, eh.rel_l2))
-    assert ey.rel_l2 <= BF16_REL_L2 and ey.max_abs_frac <= BF16_MAX_ABS_FRAC
-    assert eh.rel_l2 <= F32_OUT_REL_L2
-    ey, eh = errs[torch.float32]
-    log("  long_b1 y fp32: rel_l2=%.3e max_abs/max|y|=%.3e; final state rel_l2=%.3e"
-        % (ey.rel_l2, ey.max_abs_frac, eh.rel_l2))
-    assert ey.rel_l2 <= F32_OUT_REL_L2
-    assert eh.rel_l2 <= F32_OUT_REL_L2
+    with m.test_knobs(scan_kernel="wave_tile"):
+        assert m.workspace_size(cfg.B, cfg.D, cfg.N, cfg.L) > 0, "the wave-tile kernel should chunk along L"
+    errs, floor = _full_compare("long_b1", dev, (torch.bfloat16, torch.float32), kernels=("planner", "wave_tile"))
+    for kern in ("planner", "wave_tile"):
+        ey, eh = errs[(kern, torch.bfloat16)]
+        log("  long_b1 %s y bf16: rel_l2=%.3e (bf16 floor %.3e) max_abs/max|y|=%.3e; final state rel_l2=%.3e"
+            % (kern, ey.rel_l2, floor.rel_l2, ey.max_abs_frac, eh.rel_l2))
+        assert ey.rel_l2 <= BF16_REL_L2 and ey.max_abs_frac <= BF16_MAX_ABS_FRAC
+        assert eh.rel_l2 <= F32_OUT_REL_L2
+        ey, eh = errs[(kern, torch.float32)]
+        log("  long_b1 %s y fp32: rel_l2=%.3e max_abs/max|y|=%.3e; final state rel_l2=%.3e"
+            % (kern, ey.rel_l2, ey.max_abs_frac, eh.rel_l2))
+        assert ey.rel_l2 <= F32_OUT_REL_L2
+        assert eh.rel_l2 <= F32_OUT_REL_L2
 
 
 @pytest.mark.parametrize("name", ["mamba2.8b_layer", "mamba130m_layer"])

@@ -64,11 +64,15 @@ def test_mamba28b_layer(dev):
 
 
 def test_long_b1_chunked(dev):
+    """The wave-tile kernel's chunked path (summary, carry, balanced full pass)
+    at the full long-sequence shape; sampled channels (every channel, on both
+    kernels, is in test_parity_full_gpu.py)."""
     import selective_state_space_75_amd as m
     cfg = W.SCAN_CONFIGS["long_b1"]
-    assert m.workspace_size(cfg.B, cfg.D, cfg.N, cfg.L) > 0, "long sequence should take the chunked path"
     chans = [(0, d) for d in (0, 1, 63, 64, 1000, 2047, 2048, 3071, 4032, 4095)]
-    _run_config("long_b1", dev, channels=chans, final_state=True)
+    with m.test_knobs(scan_kernel="wave_tile"):
+        assert m.workspace_size(cfg.B, cfg.D, cfg.N, cfg.L) > 0, "long sequence should take the chunked path"
+        _run_config("long_b1", dev, channels=chans, final_state=True)
 
 
 def test_decode48_layers_0_and_47(dev):
@@ -222,13 +226,16 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("kernel", ["planner", "wave_tile"])
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "B%dD%dN%dL%d_%s_%s_k%s_%s" % (
     c[0], c[1], c[2], c[3], c[4], c[5], c[6], "-".join(sorted(c[7])) or "plain"))
-def test_ragged_and_options(case, dev):
+def test_ragged_and_options(case, kernel, dev):
+    """Each case with the planner's kernel (the row kernel for small shapes
+    with L % 32 == 0) and with the wave-tile kernel forced."""
     import selective_state_space_75_amd as m
     B, D, N, L, dt, odt, chunks, opts = case
-    log("[ragged] %s" % (case,))
-    with m.test_knobs(scan_chunks=chunks or 0):
+    log("[ragged] %s %s" % (kernel, case))
+    with m.test_knobs(scan_chunks=chunks or 0, scan_kernel=kernel):
         _ragged_case(case, dev)
 
 
@@ -296,7 +303,7 @@ def test_v1_kernel_on_aligned_shape(dev):
     import selective_state_space_75_amd as m
     x = W.custom_scan_inputs(2, 192, 16, 512, "bf16", seed=555)
     t = upload_scan(x, dev)
-    with m.test_knobs(scan_general_kernel=True):
+    with m.test_knobs(scan_kernel="general"):
         y, hN = gpu_scan(t, return_final_state=True)
     torch.cuda.synchronize()
     yr, hr = oracle_scan(x)

@@ -20,21 +20,28 @@ NOALLOC_BYTES = 8 << 20
 
 
 def test_noalloc_matches_workspace_entry_point(dev):
-    import torch
     import selective_state_space_75_amd as m
+    # the wave-tile kernel (the planner would scan the first shape with the
+    # row kernel, which needs no scratch)
     for i, (B, D, N, L) in enumerate([(1, 4096, 16, 16384), (2, 10240, 16, 128)]):
-        wsb = m.workspace_size(B, D, N, L)
-        log("[noalloc] call %d: B=%d D=%d N=%d L=%d (scratch %d bytes)" % (i, B, D, N, L, wsb))
-        assert 0 < wsb <= NOALLOC_BYTES, "the shape should use the scratch buffer"
-        x = W.custom_scan_inputs(B, D, N, L, "bf16", seed=9700 + i)
-        t = upload_scan(x, dev)
-        y_ref, h_ref = m.scan_fwd(t["u"], t["delta_raw"], t["z"], t["Bt"], t["Ct"], t["A"], t["Dskip"],
-                                  t["delta_bias"], return_final_state=True)
-        y = torch.empty((B, D, L), dtype=torch.bfloat16, device=dev)
-        h = torch.empty((B, D, N), dtype=torch.float32, device=dev)
-        m.scan_fwd_noalloc(t["u"], t["delta_raw"], t["z"], t["Bt"], t["Ct"], t["A"], t["Dskip"],
-                           t["delta_bias"], y=y, final_state=h)
-        torch.cuda.synchronize()
-        assert torch.equal(y, y_ref) and torch.equal(h, h_ref), "call %d differs from mamba_scan_fwd" % i
-        yr, _ = oracle_scan(x)
-        assert_close(from_dev(y), yr, True, "noalloc call %d y" % i)
+        with m.test_knobs(scan_kernel="wave_tile"):
+            _call(m, i, B, D, N, L, dev)
+
+
+def _call(m, i, B, D, N, L, dev):
+    import torch
+    wsb = m.workspace_size(B, D, N, L)
+    log("[noalloc] call %d: B=%d D=%d N=%d L=%d (scratch %d bytes)" % (i, B, D, N, L, wsb))
+    assert 0 < wsb <= NOALLOC_BYTES, "the shape should use the scratch buffer"
+    x = W.custom_scan_inputs(B, D, N, L, "bf16", seed=9700 + i)
+    t = upload_scan(x, dev)
+    y_ref, h_ref = m.scan_fwd(t["u"], t["delta_raw"], t["z"], t["Bt"], t["Ct"], t["A"], t["Dskip"],
+                              t["delta_bias"], return_final_state=True)
+    y = torch.empty((B, D, L), dtype=torch.bfloat16, device=dev)
+    h = torch.empty((B, D, N), dtype=torch.float32, device=dev)
+    m.scan_fwd_noalloc(t["u"], t["delta_raw"], t["z"], t["Bt"], t["Ct"], t["A"], t["Dskip"],
+                       t["delta_bias"], y=y, final_state=h)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_ref) and torch.equal(h, h_ref), "call %d differs from mamba_scan_fwd" % i
+    yr, _ = oracle_scan(x)
+    assert_close(from_dev(y), yr, True, "noalloc call %d y" % i)
