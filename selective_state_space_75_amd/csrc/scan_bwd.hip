@@ -7,19 +7,28 @@
 // ("Mamba论文研读笔记" 3.2.3 C, recomputation; "Mamba 与状态空间模型" section 07).
 //
 // Per channel and state (lane layout of the forward kernel: one wave owns 16
-// channels of one batch row, four lanes per channel, four states per lane):
-//   pass 1: run the recurrence forward and store h at the start of every
-//           16-step chunk (workspace, fp32);
-//   pass 2: for each chunk from the last: rerun its 16 steps from the stored
-//           start state, keeping h_t in the wave's LDS, then walk them in
-//           reverse with the state adjoint g_t = dyc_t C_t + Abar_(t+1) g_(t+1):
+// channels of one batch row, four lanes per channel, four states per lane).
+// L is cut into segments (2.8B layer: 8 of 256 steps), each segment into
+// 8-step chunks, and five launches run:
+//   summary:  each segment's recurrence from a zero start; stores the state
+//             and the running sum of delta at every chunk start, and per
+//             segment the end state, the product of Abar and the adjoint term
+//             it passes to the previous segment;
+//   carry:    one thread per (batch row, channel, state) chains the segments:
+//             the state entering each segment and the adjoint leaving it;
+//   segment:  walks the segment's chunks from the last: rebuilds the chunk's
+//             start state (stored state + decayed entering state), reruns its
+//             8 steps keeping h_t in registers, then walks them in reverse
+//             with the state adjoint g_t = dyc_t C_t + Abar_(t+1) g_(t+1):
 //             dyc  = dy * silu(z)            dz = dy * yc * s (1 + z (1 - s))
 //             dAbar = g h_(t-1)              dcoef = g B u
 //             du   = dyc D + sum_n g coef B
 //             ddelta = sum_n (dAbar a Abar + dcoef dcoef/ddelta)
 //             dA  += dAbar delta Abar + dcoef delta^2 phi(delta a)   (ZOH)
 //             ddelta_raw = ddelta * sigmoid(delta_raw + bias)
-//           with phi(x) = (x e^x - e^x + 1) / x^2 (a series near 0).
+//             with phi(x) = (x e^x - e^x + 1) / x^2 (a series near 0);
+//   two reductions: the per-tile dB_t / dC_t partials and the per-segment
+//             dA, dD, bias-gradient partials, each in a fixed order.
 // The ZOH coefficient follows the forward pass: (Abar - 1)/A from a
 // cancellation-free series for fp32 inputs (or when asked), else as
 // fma(Abar, 1/A, -1/A) from Abar itself.  With the latter, dA also takes the

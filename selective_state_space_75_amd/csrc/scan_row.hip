@@ -218,9 +218,8 @@ __device__ __forceinline__ void row_scan(const ScanParams& p, RowLds& s, int64_t
     pre_group(Tag<0>{});
     unroll<0, kRCT / 4>([&](auto gc) {
       constexpr int G = decltype(gc)::kValue;
-      // Keep the pipeline as written: the scheduler would otherwise sink the
-      // LDS reads of later groups next to their use.
-      __builtin_amdgcn_sched_barrier(0);
+      // (no scheduling fence here: the compiler's own interleaving of the
+      // groups measured 2% faster at the batch-1 long sequence)
       // B/C of group G + 2, two groups ahead
       if constexpr (G + 2 < kRCT / 4) {
         Bq[(G + 2) % 3] = *reinterpret_cast<const float4*>(Bs + 4 * G + 8);
