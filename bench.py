@@ -51,6 +51,17 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_mamba2.8b_layer_traffic.txt"
 SCAN_SOURCES = ["selective_state_space_75_amd/csrc/scan_v4.hpp", "selective_state_space_75_amd/csrc/scan_v4_bf16.hip",
                 "selective_state_space_75_amd/csrc/scan_v4_f32.hip", "selective_state_space_75_amd/csrc/kernels.hpp",
                 "selective_state_space_75_amd/csrc/device_math.hpp", "selective_state_space_75_amd/csrc/abi.hip"]
+ROW_SOURCES = ["selective_state_space_75_amd/csrc/scan_row.hip", "selective_state_space_75_amd/csrc/kernels.hpp",
+               "selective_state_space_75_amd/csrc/device_math.hpp", "selective_state_space_75_amd/csrc/abi.hip"]
+# Counter summaries per scan workload (taken with the kernel the planner picks for it).
+SCAN_TRAFFIC = {
+    "mamba2.8b_layer": (TRAFFIC_FILE, SCAN_SOURCES),
+    "mamba130m_layer": (os.path.join(ROOT, "profiles", "scan_mamba130m_layer_traffic.txt"), ROW_SOURCES),
+    "long_b1": (os.path.join(ROOT, "profiles", "scan_long_b1_traffic.txt"), ROW_SOURCES),
+}
+# Shader clock measured on the 2.8B-layer scan (rocprofv3 GRBM counters over
+# the kernel's duration); the ALU peak is also given at this clock.
+CLOCK_FILE = os.path.join(ROOT, "profiles", "scan_mamba2.8b_layer_sq_counters.txt")
 DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "state_update_decode48_traffic.txt")
 CONV_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "conv1d_2.8b_layer_traffic.txt")
 CONV_SOURCES = ["selective_state_space_75_amd/csrc/conv1d.hip", "selective_state_space_75_amd/csrc/kernels.hpp",
@@ -183,6 +194,16 @@ def source_digest(files):
     return h.hexdigest()
 
 
+def measured_clock_ghz(path=CLOCK_FILE):
+    """Shader clock (GHz) recorded in the committed counter summary, or None."""
+    if not os.path.exists(path):
+        return None
+    for line in open(path, encoding="utf-8"):
+        if line.startswith("measured_clock_ghz:"):
+            return float(line.split(":", 1)[1])
+    return None
+
+
 def recorded_traffic(path=TRAFFIC_FILE, sources=SCAN_SOURCES):
     """(bytes per launch, note) from the committed counter summary, or (None,
     reason) when it is missing or the kernel sources changed since."""
@@ -266,8 +287,12 @@ def bench_scan(args, dev):
     opu = OPS_PER_UPDATE_DELTA_B if args.delta_b else OPS_PER_UPDATE
     ops = cfg.updates * opu
     achieved_tops = ops / (kern_ms * 1e-3) / 1e12
-    traffic, traffic_note = (recorded_traffic() if cfg.name == "mamba2.8b_layer" and not args.delta_b
-                             else (None, "not measured"))
+    kernel = scan_kernel_name(cfg, args)
+    if cfg.name in SCAN_TRAFFIC and not args.delta_b and getattr(args, "scan_kernel", "planner") == "planner":
+        traffic, traffic_note = recorded_traffic(*SCAN_TRAFFIC[cfg.name])
+    else:
+        traffic, traffic_note = None, "not measured for this variant"
+    clock = measured_clock_ghz()
     p10, p50, p90 = (float(v) for v in np.percentile(per_launch_ms, [10, 50, 90]))
     line = {
         "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -276,7 +301,7 @@ def bench_scan(args, dev):
         "config": {"workload": cfg.name, "B": cfg.B, "D": cfg.D, "N": cfg.N, "L": cfg.L,
                    "final_state": cfg.final_state, "global_batch": cfg.B, "seq_len": cfg.L,
                    "discretization": "delta_b" if args.delta_b else "zoh", "parallelism": "none (1 GPU)",
-                   "scan_kernel": scan_kernel_name(cfg, args)},
+                   "scan_kernel": kernel},
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "elems_per_s": round(cfg.elements / (ms_step * 1e-3), 1),
         "kernel_ms_mean": round(kern_ms, 5), "kernel_ms_min": round(float(np.min(per_launch_ms)), 5),
@@ -293,6 +318,9 @@ def bench_scan(args, dev):
                      "ops_per_update": opu, "updates_per_launch": cfg.updates,
                      "op": "fp32 VALU lane-operations (%d per state update + 1 exp2); peak = 256 CUs x 64 "
                            "lanes x 2.4 GHz, non-packed" % (opu - 1),
+                     "clock_ghz_measured": clock,
+                     "frac_at_measured_clock": (round(achieved_tops / (VALU_PEAK_TOPS * clock / CLOCK_GHZ), 4)
+                                                if clock else None),
                      "hbm_achieved_gbs_kernel": round(nbytes / (kern_ms * 1e-3) / 1e9, 2)},
     }
     return line, cfg, x

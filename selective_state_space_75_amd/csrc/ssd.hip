@@ -96,6 +96,18 @@ __device__ __forceinline__ uint2 ld_row4(const uint16_t* row, int64_t t, bool ve
   return make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
 }
 
+// Work item of workgroup `id` out of `n`, so that each of the 8 XCDs (which
+// take workgroups round-robin: id % 8) gets a contiguous range of work items:
+// the heads of one (batch row, segment) then share that XCD's L2, and its
+// copy of B_t/C_t (1 MB per batch row at N = 128) is read from HBM once
+// rather than by every XCD.  The tail past the last multiple of 8 keeps its
+// index.
+__device__ __forceinline__ int64_t xcd_item(int64_t id, int64_t n) {
+  const int64_t per = n / 8;
+  if (id >= 8 * per) return id;
+  return (id % 8) * per + id / 8;
+}
+
 template <int kN, bool kOutBF16, bool kDeltaB>
 __global__ __launch_bounds__(256, 3) void ssd_chunk_kernel(SsdParams p) {
   __shared__ SsdLds<kN> S;
@@ -105,7 +117,7 @@ __global__ __launch_bounds__(256, 3) void ssd_chunk_kernel(SsdParams p) {
   const int w = tid >> 6, l = tid & 63;
   const int g = l >> 4, r = l & 15;
   const int64_t pblocks = p.P / kP;
-  const int64_t wg = blockIdx.x;                             // ((b S + seg) H + h) pblocks + pb
+  const int64_t wg = xcd_item(blockIdx.x, gridDim.x);      // ((b S + seg) H + h) pblocks + pb
   const int64_t pb = wg % pblocks;
   const int64_t h = (wg / pblocks) % p.H;
   const int64_t bs = wg / (pblocks * p.H);
@@ -465,7 +477,7 @@ __global__ __launch_bounds__(256, 4) void ssd_state_kernel(SsdParams p) {
   const int lr = tid >> 2, lq = tid & 3;                     // staging: row lr (+ 64 i), steps 8 lq .. + 7
   const int64_t pblocks = p.P / kP;
   const int64_t segs = p.S - 1;                              // the last segment needs no end state
-  const int64_t wg = blockIdx.x;                             // ((b segs + seg) H + h) pblocks + pb
+  const int64_t wg = xcd_item(blockIdx.x, gridDim.x);      // ((b segs + seg) H + h) pblocks + pb
   const int64_t pb = wg % pblocks;
   const int64_t h = (wg / pblocks) % p.H;
   const int64_t bs = wg / (pblocks * p.H);
