@@ -49,6 +49,11 @@ __device__ __forceinline__ float row_bcast(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x150 + k, 0xF, 0xF, true));
 }
 
+// Value v of lane `src` of the wave (ds_bpermute: the LDS crossbar, no LDS memory).
+__device__ __forceinline__ uint32_t lane_read(uint32_t v, int src) {
+  return (uint32_t)__builtin_amdgcn_ds_bpermute(src << 2, (int)v);
+}
+
 template <bool kBF16> struct Raw2;                       // 2 consecutive elements
 template <> struct Raw2<true> { uint32_t w; };
 template <> struct Raw2<false> { float2 v; };
@@ -166,6 +171,22 @@ __device__ __forceinline__ void row_scan(const ScanParams& p, RowLds& s, int64_t
     gv[par][j] = want_z ? gz : 1.0f;
     if constexpr (kMode == kDeltaB) duv[par][j] = dv[par][j] * uv[par][j];
   };
+  // bf16 outputs leave in whole 128-byte lines: a lane packs its 2 outputs of
+  // an even chunk (`held`) and of the following odd chunk, then lane j of a
+  // row stores steps 4j .. 4j+3 of that 64-step window, gathered from lanes
+  // 2j mod 16 and 2j+1 mod 16 of its row (the even chunk for j < 8, the odd
+  // one for j >= 8).  Half lines written a chunk apart were evicted between
+  // the halves at the batch-1 long sequence (1.33x the output bytes).
+  uint32_t held = 0;
+  auto put_pair = [&](int64_t t_even, uint32_t cur) {
+    const int s1 = 16 * r + ((2 * n) & 15);
+    const uint32_t h1 = lane_read(held, s1), c1 = lane_read(cur, s1);
+    const uint32_t h2 = lane_read(held, s1 + 1), c2 = lane_read(cur, s1 + 1);
+    const bool first = n < 8;
+    if (c_ok)
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.y) + row + t_even + 4 * n) =
+          make_uint2(first ? h1 : c1, first ? h2 : c2);
+  };
   float* prow = &s.part[w * kPWave + r * (16 * kPRowR + 8) + n * kPRowR];   // this lane's product row
   const float* pread = &s.part[w * kPWave + r * (16 * kPRowR + 8) + 2 * n]; // its outputs' column pair
 
@@ -236,10 +257,14 @@ __device__ __forceinline__ void row_scan(const ScanParams& p, RowLds& s, int64_t
         else o[j] = __builtin_fmaf(dskip, uv[Q][j], o[j] + (s0 + s1)) * gv[Q][j];
       }
       if constexpr (G == 4) {
-        if (c_ok && ck > 0) {
-          const int64_t at = row + t0 - kRCT + 2 * n;
-          if constexpr (kOutBF16) *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(p.y) + at) = pack_bf16x2(o[0], o[1]);
-          else *reinterpret_cast<float2*>(static_cast<float*>(p.y) + at) = make_float2(o[0], o[1]);
+        if constexpr (kOutBF16) {
+          // chunk ck-1 is even for P = 1 (keep its outputs), odd for P = 0 (store the pair)
+          if constexpr (P == 1) held = pack_bf16x2(o[0], o[1]);
+          else if (ck > 0) put_pair(t0 - 2 * kRCT, pack_bf16x2(o[0], o[1]));
+        } else {
+          // fp32: one chunk of a row is already a whole 128-byte line
+          if (c_ok && ck > 0)
+            *reinterpret_cast<float2*>(static_cast<float*>(p.y) + row + t0 - kRCT + 2 * n) = make_float2(o[0], o[1]);
         }
       }
       // unpack the next chunk (parity Q) in the second half, after its u and gate were used above
@@ -279,7 +304,7 @@ __device__ __forceinline__ void row_scan(const ScanParams& p, RowLds& s, int64_t
       for (int m = 0; m < 16; ++m) { o0 += q[2 * m]; o1 += q[2 * m + 1]; }
       o0 = __builtin_fmaf(dskip, uv[0][0], o0) * gv[0][0];
       o1 = __builtin_fmaf(dskip, uv[0][1], o1) * gv[0][1];
-      if (c_ok) {
+      if (c_ok) {   // an even last chunk: no partner, a half line
         const int64_t at = row + ck * kRCT + 2 * n;
         if constexpr (kOutBF16) *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(p.y) + at) = pack_bf16x2(o0, o1);
         else *reinterpret_cast<float2*>(static_cast<float*>(p.y) + at) = make_float2(o0, o1);
@@ -293,10 +318,10 @@ __device__ __forceinline__ void row_scan(const ScanParams& p, RowLds& s, int64_t
       for (int m = 0; m < 16; ++m) { o0 += q[2 * m]; o1 += q[2 * m + 1]; }
       o0 = __builtin_fmaf(dskip, uv[1][0], o0) * gv[1][0];
       o1 = __builtin_fmaf(dskip, uv[1][1], o1) * gv[1][1];
-      if (c_ok) {
-        const int64_t at = row + (ck + 1) * kRCT + 2 * n;
-        if constexpr (kOutBF16) *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(p.y) + at) = pack_bf16x2(o0, o1);
-        else *reinterpret_cast<float2*>(static_cast<float*>(p.y) + at) = make_float2(o0, o1);
+      if constexpr (kOutBF16) {
+        put_pair(ck * kRCT, pack_bf16x2(o0, o1));   // an odd last chunk pairs with the held even one
+      } else if (c_ok) {
+        *reinterpret_cast<float2*>(static_cast<float*>(p.y) + row + (ck + 1) * kRCT + 2 * n) = make_float2(o0, o1);
       }
       break;
     }

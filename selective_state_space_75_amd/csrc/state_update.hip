@@ -139,8 +139,7 @@ __global__ __launch_bounds__(kStreamBlock) void state_update_stream_kernel(Updat
 
   f4 h[kStreamR], a[kStreamR];
   typename Vec4In<kInBF16>::T bn[kStreamR], cn[kStreamR];
-  float uu[kStreamR], dr[kStreamR], bias[kStreamR];
-  uint32_t dd[kStreamR];
+  float uu[kStreamR], dr[kStreamR], bias[kStreamR], zz[kStreamR], dsk[kStreamR];
   // Issue every load first.  Out-of-range channels read the last channel
   // (always valid) and store nothing.
 #pragma unroll
@@ -151,7 +150,6 @@ __global__ __launch_bounds__(kStreamBlock) void state_update_stream_kernel(Updat
     uint32_t b = (uint32_t)((double)ch * p.inv_d);
     b += (ch - b * D >= D) ? 1u : 0u;
     const uint32_t d = ch - b * D;
-    dd[r] = d;
     h[r] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(p.state + (size_t)ch * 16 + 4 * q));
     a[r] = *reinterpret_cast<const f4*>(p.A + (size_t)d * 16 + 4 * q);
     bn[r] = ld4<kInBF16>(p.Bt, b * 16 + 4 * q);
@@ -159,6 +157,10 @@ __global__ __launch_bounds__(kStreamBlock) void state_update_stream_kernel(Updat
     uu[r] = ld<kInBF16>(p.u, ch);
     dr[r] = ld<kInBF16>(p.delta, ch);
     bias[r] = p.bias ? p.bias[d] : 0.0f;
+    // the gate's input and the skip weight with the others, so that no load is
+    // left after the arithmetic
+    zz[r] = p.z ? ld<kInBF16>(p.z, ch) : 0.0f;
+    dsk[r] = p.Dskip ? p.Dskip[d] : 0.0f;
   }
   // The arithmetic is cheap next to the state traffic, so ZOH always takes
   // the cancellation-free (Abar - 1) / A (measured: no cost on B=128 D=4096).
@@ -194,15 +196,14 @@ __global__ __launch_bounds__(kStreamBlock) void state_update_stream_kernel(Updat
   for (int r = 0; r < kStreamR; ++r) {
     const uint32_t ch0 = first + kStreamStride * r;
     const uint32_t ch = ch0 < BD ? ch0 : BD - 1;
-    const uint32_t d = dd[r];
     float sum = acc[r];
     sum += __shfl_xor(sum, 1, 4);
     sum += __shfl_xor(sum, 2, 4);
     if (ch0 < BD) {
       __builtin_nontemporal_store(h[r], reinterpret_cast<f4*>(p.state + (size_t)ch * 16 + 4 * q));
       if (q == 0) {
-        float v = sum + (p.Dskip ? p.Dskip[d] : 0.0f) * uu[r];
-        if (p.z) v *= silu(ld<kInBF16>(p.z, ch));
+        float v = sum + dsk[r] * uu[r];
+        if (p.z) v *= silu(zz[r]);
         if constexpr (kOutBF16) static_cast<uint16_t*>(p.y)[ch] = f32_to_bf16(v);
         else static_cast<float*>(p.y)[ch] = v;
       }
