@@ -228,6 +228,15 @@ struct Segment {
       const float gz = silu(at8<kInBF16>(z, j));
       return want_z ? gz : 1.0f;
     };
+    auto pack8 = [&](const float (&o)[8]) {
+      return make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                        pack_bf16x2(o[6], o[7]));
+    };
+    auto store_w = [&](int64_t t0, const uint4& wv) {
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.y) + row + t0 + 8 * g) = wv;
+    };
+    uint4 held = make_uint4(0, 0, 0, 0);   // bf16 outputs of the last even chunk, not yet stored
+    int64_t held_at = 0;
     auto store_out = [&](int64_t t0, const float (&o)[8]) {
       const int64_t at = row + t0 + 8 * g;
       if constexpr (kOutBF16) {
@@ -337,7 +346,21 @@ struct Segment {
           // chunk's outputs go when it is the only one), which the real
           // outputs overwrite later (same lane, same address, program order).
           if constexpr (kReadout && t == 16) {
-            if constexpr (kRagged) {
+            if constexpr (kOutBF16) {
+              // bf16: a quad writes 64 bytes of a channel per chunk, half a
+              // 128-byte line.  An even chunk's outputs are held and stored
+              // right before the next chunk's, so each line's halves reach the
+              // L2 back to back; a chunk apart they were evicted in between
+              // (1.2x the output bytes).
+              const uint4 wv = pack8(o);
+              if constexpr (P == 1) {
+                held = wv;
+                held_at = t0 - kCT;
+              } else if (ck > 0 && c_ok) {
+                store_w(held_at, held);
+                store_w(t0 - kCT, wv);
+              }
+            } else if constexpr (kRagged) {
               if (ck > 0 || nck > 1 ? c_ok : out_last) store_out(ck > 0 ? t0 - kCT : (nck > 1 ? t0 : t_last), o);
             } else {
               if (c_ok) store_out(ck > 0 ? t0 - kCT : t0, o);
@@ -398,7 +421,14 @@ struct Segment {
             const float y = (q[j] + q[8 + j]) + (q[16 + j] + q[24 + j]);
             o[j] = __builtin_fmaf(k.dskip, uv[P][j], y) * gv[P][j];
           }
-          if (out_last) store_out(t_last, o);
+          if constexpr (kOutBF16) {
+            if constexpr (P == 1) {   // an odd last chunk: the held even one goes first
+              if (c_ok) store_w(held_at, held);
+            }
+            if (out_last) store_w(t_last, pack8(o));
+          } else {
+            if (out_last) store_out(t_last, o);
+          }
         }
       };
       for (int64_t ck = 0;; ck += 2) {
