@@ -69,18 +69,21 @@ double v4_chunk_cost(int64_t tiles, int64_t k) {
 
 // Relative time of the row kernel (one state per lane, a 16-channel tile per
 // 4-wave workgroup, up to three workgroups per CU) in the units of
-// v4_chunk_cost.  Measured per 2048 steps on MI355X: 68 us with one workgroup
-// per CU, 156 us with three, against 190 us for a wave-tile pass of one tile
-// per SIMD; in between about 24 + 44 k us for k workgroups per CU.
+// v4_chunk_cost.  Measured per 2048 steps on MI355X, against 190 us for a
+// wave-tile pass of one tile per SIMD: 68, 110 and 153 us with one, two and
+// three workgroups per CU; from four on about 52 + 40.9 us per workgroup per
+// CU (a fit over 5, 10, 12 and 20 per CU, within 6% of each).
 double row_cost(int64_t wgs) {
   const int64_t per_cu = (wgs + kCUsPlan - 1) / kCUsPlan;
-  const int64_t full = per_cu / 3, rem = per_cu % 3;
-  return (full * 156.0 + (rem ? 24.0 + 44.0 * rem : 0.0)) / 190.0;
+  static const double kFew[3] = {68.0, 110.0, 153.0};
+  const double us = per_cu <= 3 ? kFew[per_cu - 1] : 52.0 + 40.9 * double(per_cu);
+  return us / 190.0;
 }
 
 // Shape-only plan (no device query).  The row kernel when L is a multiple of
-// 32 and its cost model beats the wave-tile kernel's (few 16-channel tiles:
-// the 130M layer, the batch-1 long sequence); else one pass per channel tile
+// 32 and its cost model beats the wave-tile kernel's (few 16-channel tiles,
+// as in the 130M layer and the batch-1 long sequence, or eight and more
+// workgroups per CU); else one pass per channel tile
 // while there are enough tiles to occupy the GPU; otherwise (few channels,
 // long L) split L into chunks of at least 2048 steps: for the wave-tile
 // kernel the number of chunks that minimises v4_chunk_cost, for the general

@@ -337,15 +337,22 @@ def scan_noalloc(**kw):
 def test_scan_kernel_choice():
     """The planner's kernel per workload: the row kernel where 16-channel wave
     tiles would leave SIMDs idle or need chunking (130M layer, batch-1 long
-    sequence), the wave-tile kernel's balanced split at the 2.8B layer and for
-    ragged lengths, chunking of the wave-tile kernel for very few tiles, the
-    general kernel for L % 8 != 0."""
+    sequence) and from eight row workgroups per CU on, the wave-tile kernel's
+    balanced split at the 2.8B layer and for ragged lengths, chunking of the
+    wave-tile kernel for very few tiles over long L, the general kernel for
+    L % 8 != 0.  (Each choice was the faster kernel in an interleaved timing of
+    both on MI355X.)"""
     k = _lib.scan_kernel
     assert k(8, 1536, 16, 2048) == "row"
     assert k(1, 4096, 16, 131072) == "row"
     assert k(4, 5120, 16, 2048) == "wave_tile"
     assert k(1, 4096, 16, 131072 - 8) == "wave_tile"
     assert k(1, 1024, 16, 65536) == "wave_tile"
+    assert k(1, 2048, 16, 16384) == "wave_tile"
+    assert k(1, 5120, 16, 8192) == "wave_tile"
+    assert k(2, 2560, 16, 4096) == "row"
+    assert k(8, 5120, 16, 2048) == "row"
+    assert k(32, 1536, 16, 2048) == "row"
     assert k(2, 100, 16, 100) == "general"
     assert k(1, 16, 16, 16) == "general"
     with _lib.test_knobs(scan_kernel="wave_tile"):
