@@ -53,12 +53,18 @@ SCAN_SOURCES = ["selective_state_space_75_amd/csrc/scan_v4.hpp", "selective_stat
                 "selective_state_space_75_amd/csrc/device_math.hpp", "selective_state_space_75_amd/csrc/abi.hip"]
 ROW_SOURCES = ["selective_state_space_75_amd/csrc/scan_row.hip", "selective_state_space_75_amd/csrc/kernels.hpp",
                "selective_state_space_75_amd/csrc/device_math.hpp", "selective_state_space_75_amd/csrc/abi.hip"]
-# Counter summaries per scan workload (taken with the kernel the planner picks for it).
+# Counter summaries per scan workload (taken with the kernel the planner picks
+# for it; the sources hashed are those of that kernel).
 SCAN_TRAFFIC = {
-    "mamba2.8b_layer": (TRAFFIC_FILE, SCAN_SOURCES),
-    "mamba130m_layer": (os.path.join(ROOT, "profiles", "scan_mamba130m_layer_traffic.txt"), ROW_SOURCES),
-    "long_b1": (os.path.join(ROOT, "profiles", "scan_long_b1_traffic.txt"), ROW_SOURCES),
+    "mamba2.8b_layer": TRAFFIC_FILE,
+    "mamba130m_layer": os.path.join(ROOT, "profiles", "scan_mamba130m_layer_traffic.txt"),
+    "long_b1": os.path.join(ROOT, "profiles", "scan_long_b1_traffic.txt"),
 }
+
+
+def kernel_sources(kernel):
+    """Source files of a scan kernel (by its mamba_scan_kernel name)."""
+    return ROW_SOURCES if kernel.startswith("row") else SCAN_SOURCES
 # Shader clock measured on the 2.8B-layer scan (rocprofv3 GRBM counters over
 # the kernel's duration); the ALU peak is also given at this clock.
 CLOCK_FILE = os.path.join(ROOT, "profiles", "scan_mamba2.8b_layer_sq_counters.txt")
@@ -289,7 +295,7 @@ def bench_scan(args, dev):
     achieved_tops = ops / (kern_ms * 1e-3) / 1e12
     kernel = scan_kernel_name(cfg, args)
     if cfg.name in SCAN_TRAFFIC and not args.delta_b and getattr(args, "scan_kernel", "planner") == "planner":
-        traffic, traffic_note = recorded_traffic(*SCAN_TRAFFIC[cfg.name])
+        traffic, traffic_note = recorded_traffic(SCAN_TRAFFIC[cfg.name], kernel_sources(kernel))
     else:
         traffic, traffic_note = None, "not measured for this variant"
     clock = measured_clock_ghz()
@@ -724,7 +730,7 @@ def main():
                     help="scan workloads: another sequence length L (same B, D, N, dtype, seed)")
     ap.add_argument("--delta-b", action="store_true",
                     help="scan workloads: the simplified rule B-bar = delta B instead of zero-order hold")
-    ap.add_argument("--scan-kernel", default="planner", choices=["planner", "wave_tile", "row", "general"],
+    ap.add_argument("--scan-kernel", default="planner", choices=["planner", "wave_tile", "row", "row_lean", "general"],
                     help="diagnostic: force a scan kernel through the library's test knob")
     args = ap.parse_args()
     if args.gpus != 1:

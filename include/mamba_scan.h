@@ -109,11 +109,16 @@ size_t mamba_scan_workspace_size(int64_t B, int64_t D, int64_t N, int64_t L);
  *                           SIMDs with state hand-over (L % 8 == 0, L >= 32);
  *   MAMBA_KERNEL_ROW        16 channels per 4-wave workgroup, one state per
  *                           lane, one pass (L % 32 == 0), chosen when the
- *                           wave tiles would leave SIMDs idle or need chunking.
+ *                           wave tiles would leave SIMDs idle or need chunking;
+ *   MAMBA_KERNEL_ROW_LEAN   the same layout with fewer registers and less LDS
+ *                           per workgroup (five workgroups per CU instead of
+ *                           three), chosen from nine 16-channel workgroups per
+ *                           CU on (L % 32 == 0).
  */
 #define MAMBA_KERNEL_GENERAL 1
 #define MAMBA_KERNEL_WAVE_TILE 2
 #define MAMBA_KERNEL_ROW 3
+#define MAMBA_KERNEL_ROW_LEAN 4
 int mamba_scan_kernel(int64_t B, int64_t D, int64_t N, int64_t L);
 
 /*
@@ -335,7 +340,7 @@ size_t mamba_ssd_workspace_size(int64_t B, int64_t H, int64_t P, int64_t N, int6
  *                         only for L % 8 != 0 or L < 32); 2 the wave-tile
  *                         kernel with 16 states per lane (L % 8 == 0, L >= 32);
  *                         3 the row kernel with one state per lane
- *                         (L % 32 == 0).  A kernel that cannot take the shape
+ *                         (L % 32 == 0); 4 its lean variant (L % 32 == 0).  A kernel that cannot take the shape
  *                         gives way to the planner's choice.
  *   scan_no_balance       != 0: no balanced split with state hand-over.
  *   handover_spin         >= 0: bound of a workgroup's wait for the state handed

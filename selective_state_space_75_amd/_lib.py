@@ -89,14 +89,14 @@ def status_string(status: int) -> str:
         return "?"
 
 
-SCAN_KERNELS = {"planner": 0, "general": 1, "wave_tile": 2, "row": 3}
+SCAN_KERNELS = {"planner": 0, "general": 1, "wave_tile": 2, "row": 3, "row_lean": 4}
 
 
 def set_test_knobs(scan_chunks: int = 0, scan_kernel: str = "planner", scan_no_balance: bool = False,
                    handover_spin: int = -1, ssd_segments: int = 0) -> None:
     """Process-wide test knobs of the library (mamba_set_test_knobs); no
     arguments restores the defaults.  scan_kernel: planner, general,
-    wave_tile or row."""
+    wave_tile, row or row_lean."""
     k = TestKnobs(scan_chunks, SCAN_KERNELS[scan_kernel], int(scan_no_balance), handover_spin, ssd_segments)
     st = lib().mamba_set_test_knobs(ctypes.byref(k))
     if st != 0:
@@ -125,7 +125,7 @@ def scan_kernel(B: int, D: int, N: int, L: int) -> str:
     k = lib().mamba_scan_kernel(B, D, N, L)
     if k < 0:
         raise MambaError(k, "mamba_scan_kernel")
-    return {1: "general", 2: "wave_tile", 3: "row"}[k]
+    return {1: "general", 2: "wave_tile", 3: "row", 4: "row_lean"}[k]
 
 
 def workspace_size(B: int, D: int, N: int, L: int) -> int:

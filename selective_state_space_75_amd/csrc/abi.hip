@@ -28,6 +28,7 @@ struct Plan {
   int64_t chunk_len = 0;
   bool v4 = false;          // the wave-tile kernel (L a multiple of 8, L >= 32)
   bool row = false;         // the row kernel (one state per lane, L a multiple of 32)
+  bool row_lean = false;    // its lean variant (five workgroups per CU)
   bool balanced = false;    // equal (tile x time) ranges with state hand-over
   size_t ws_bytes = 0;
   size_t off_local = 0, off_start = 0, off_sum = 0;
@@ -80,10 +81,10 @@ double row_cost(int64_t wgs) {
   return us / 190.0;
 }
 
-// Shape-only plan (no device query).  The row kernel when L is a multiple of
-// 32 and its cost model beats the wave-tile kernel's (few 16-channel tiles,
-// as in the 130M layer and the batch-1 long sequence, or eight and more
-// workgroups per CU); else one pass per channel tile
+// Shape-only plan (no device query).  When L is a multiple of 32: the lean
+// row kernel from nine 16-channel workgroups per CU on, the row kernel when
+// its cost model beats the wave-tile kernel's (few 16-channel tiles, as in
+// the 130M layer and the batch-1 long sequence); else one pass per channel tile
 // while there are enough tiles to occupy the GPU; otherwise (few channels,
 // long L) split L into chunks of at least 2048 steps: for the wave-tile
 // kernel the number of chunks that minimises v4_chunk_cost, for the general
@@ -95,7 +96,14 @@ Plan make_plan(int64_t B, int64_t D, int64_t N, int64_t L, const mamba_test_knob
   const bool row_ok = L % kRowStep == 0 && kn.scan_kernel != 1 && kn.scan_kernel != 2 && kn.scan_chunks == 0;
   if (row_ok) {
     const int64_t tiles16 = B * ((D + kV4Tile - 1) / kV4Tile);
-    bool row = kn.scan_kernel == 3;
+    const int64_t per_cu = (tiles16 + kCUsPlan - 1) / kCUsPlan;
+    // The lean row kernel from nine 16-channel workgroups per CU on: timed on
+    // MI355X it beat both other kernels by 5 to 9% at 10, 12 and 20 per CU;
+    // from 5 to 8 per CU it was within 2% of the wave-tile kernel's balanced
+    // split either way (at 5, the 2.8B layer, 1% slower in the streaming
+    // benchmark), and at 4 it lost by 4%.
+    const bool lean = kn.scan_kernel == 4 || (kn.scan_kernel == 0 && per_cu >= 9);
+    bool row = kn.scan_kernel == 3 || lean;
     if (!row) {
       double best = v4_chunk_cost(tiles16, 1);
       const int64_t kmax = L >= 4096 && tiles16 < kGroupsPlan ? (L / 2048 < 64 ? L / 2048 : 64) : 1;
@@ -104,6 +112,7 @@ Plan make_plan(int64_t B, int64_t D, int64_t N, int64_t L, const mamba_test_knob
     }
     if (row) {
       p.row = true;
+      p.row_lean = lean;
       p.v4 = false;
       p.tiles_d = (D + kV4Tile - 1) / kV4Tile;
       return p;   // one pass, no workspace
@@ -327,7 +336,7 @@ int scan_fwd_run(const void* u, const void* delta, const void* z, const void* Bt
     if (e != hipSuccess) return MAMBA_ERR_HIP;
     if (mamba::launch_scan_carry(p, stream) != hipSuccess) return MAMBA_ERR_HIP;
   }
-  const hipError_t e = plan.row ? mamba::launch_scan_row(p, in, out, stream)
+  const hipError_t e = plan.row ? mamba::launch_scan_row(p, in, out, plan.row_lean, stream)
                        : plan.v4 ? mamba::launch_scan_v4(p, q, in, out, false, stream)
                                  : mamba::launch_scan_full(p, in, out, stream);
   if (e != hipSuccess) return MAMBA_ERR_HIP;
@@ -371,7 +380,7 @@ int mamba_scan_kernel(int64_t B, int64_t D, int64_t N, int64_t L) {
   if (!shape_ok(B, D, N, L)) return MAMBA_ERR_SHAPE;
   if (N > 16) return MAMBA_ERR_UNSUPPORTED;
   const Plan p = make_plan(B, D, N, L, knobs());
-  return p.row ? MAMBA_KERNEL_ROW : p.v4 ? MAMBA_KERNEL_WAVE_TILE : MAMBA_KERNEL_GENERAL;
+  return p.row ? (p.row_lean ? MAMBA_KERNEL_ROW_LEAN : MAMBA_KERNEL_ROW) : p.v4 ? MAMBA_KERNEL_WAVE_TILE : MAMBA_KERNEL_GENERAL;
 }
 
 int mamba_set_test_knobs(const mamba_test_knobs_t* k) {

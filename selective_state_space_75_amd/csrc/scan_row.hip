@@ -329,6 +329,239 @@ __device__ __forceinline__ void row_scan(const ScanParams& p, RowLds& s, int64_t
   if (p.final_state != nullptr && c_ok && n_ok) p.final_state[(b * D + d) * N + n] = h;
 }
 
+// ---------------------------------------------------------------------------
+// Lean variant: the same lane layout and arithmetic with registers and LDS cut
+// so that five workgroups (five waves per SIMD) fit on a CU, for shapes with
+// four or more workgroups per CU, where other waves rather than lookahead
+// inside a wave hide latencies.  Differences from row_scan:
+//  * lane n of a row holds steps n and n + 16 of a chunk (two 2-byte loads
+//    per input for bf16), so that in each 16-step half lane n also owns the
+//    output of step n;
+//  * the readout goes through LDS every 16 steps (16 products per lane, read
+//    back as one 16-state column: 15 adds per output), in a per-wave buffer
+//    half the size;
+//  * B_t/C_t are read one 4-step group ahead and the step-dependent terms are
+//    formed in the step that uses them (inputs are still fetched two chunks
+//    ahead, as in row_scan).
+// bf16 outputs of two chunks (one 128-byte line per channel) are gathered
+// with ds_bpermute so that lane n writes steps 4n .. 4n+3 of the line.
+
+constexpr int kLPitch = 20;                            // floats per product row (16 + padding)
+constexpr int kLRowBlk = 16 * kLPitch + 16;            // floats per DPP row (+16: bank skew between rows)
+constexpr int kLWave = 3 * kLRowBlk + 16 * kLPitch;    // floats per wave
+
+struct alignas(16) RowLeanLds {
+  float bc[2][2][16 * kBCRow];    // [buffer][B, C][state * kBCRow + step], as in RowLds
+  float part[4 * kLWave];         // [wave][row][state][step of the half] products
+};
+static_assert(sizeof(RowLeanLds) <= 32768, "five workgroups per CU need at most 32 KiB of LDS each");
+
+template <bool kBF16> struct Raw1;
+template <> struct Raw1<true> { uint32_t h; };   // bf16 pattern in the low half
+template <> struct Raw1<false> { float v; };
+
+template <bool kBF16>
+__device__ __forceinline__ Raw1<kBF16> load1(const void* base, int64_t off) {
+  Raw1<kBF16> r;
+  if constexpr (kBF16) r.h = *(static_cast<const uint16_t*>(base) + off);
+  else r.v = *(static_cast<const float*>(base) + off);
+  return r;
+}
+template <bool kBF16>
+__device__ __forceinline__ float at1(const Raw1<kBF16>& r) {
+  if constexpr (kBF16) return __builtin_bit_cast(float, r.h << 16);
+  else return r.v;
+}
+
+template <bool kInBF16>
+struct LeanRaw {
+  Raw1<kInBF16> u[2], d[2], z[2];   // steps n and n + 16 of this lane's channel
+  Raw4<kInBF16> bc;                 // 4 steps of one B or C row (staging role)
+};
+
+__device__ __forceinline__ float comp4(const float4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+template <bool kInBF16, bool kOutBF16, int kMode>
+__device__ __forceinline__ void row_scan_lean(const ScanParams& p, RowLeanLds& s, int64_t b, int64_t d0) {
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63;
+  const int r = lane >> 4, n = lane & 15;
+  const int64_t D = p.D, N = p.N, L = p.L;
+  const int64_t d = d0 + 4 * w + r;
+  const bool c_ok = d < D;
+  const bool n_ok = n < N;
+  const int64_t row = (b * D + (c_ok ? d : 0)) * L;
+
+  float a = (c_ok && n_ok) ? p.A[(c_ok ? d : 0) * N + n] : -1.0f;
+  if (__builtin_fabsf(a) < 0x1p-40f) a = (a > 0.0f) ? 0x1p-40f : -0x1p-40f;
+  const float a2 = a * kLog2e, ia = 1.0f / a;
+  const float bias = !c_ok ? -__builtin_inff() : (p.bias ? p.bias[d] : 0.0f);
+  const float dskip = (c_ok && p.Dskip) ? p.Dskip[d] : 0.0f;
+  const bool want_z = p.z != nullptr;
+  const void* z_src = p.z ? p.z : p.u;
+
+  const int s_arr = tid >> 7, sn = (tid >> 3) & 15, sg = tid & 7;
+  const bool s_ok = sn < N;
+  const void* s_base = s_arr ? p.Ct : p.Bt;
+  const int64_t s_row = (b * N + (s_ok ? sn : 0)) * L;
+
+  const int64_t nck = L / kRCT;
+  LeanRaw<kInBF16> raw[2];           // inputs of chunks of each parity, fetched two chunks ahead
+  auto fetch = [&](int64_t ck, LeanRaw<kInBF16>& rr) {
+    const int64_t c = ck < nck ? ck : nck - 1;     // clamp: the prefetch past the end re-reads the last chunk
+    const int64_t at = row + c * kRCT + n;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      rr.u[e] = load1<kInBF16>(p.u, at + 16 * e);
+      rr.d[e] = load1<kInBF16>(p.delta, at + 16 * e);
+      rr.z[e] = load1<kInBF16>(z_src, at + 16 * e);
+    }
+    rr.bc = load4<kInBF16>(s_base, s_row + c * kRCT + 4 * sg, s_ok);
+  };
+  float dv[2], uv[2], gv[2], duv[2];    // [element]: delta, u, gate (and delta * u) of steps n, n + 16
+  auto prep = [&](const LeanRaw<kInBF16>& rr) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      dv[e] = softplus(at1<kInBF16>(rr.d[e]) + bias);
+      uv[e] = at1<kInBF16>(rr.u[e]);
+      const float gz = silu(at1<kInBF16>(rr.z[e]));
+      gv[e] = want_z ? gz : 1.0f;
+      if constexpr (kMode == kDeltaB) duv[e] = dv[e] * uv[e];
+    }
+  };
+  auto stage = [&](const LeanRaw<kInBF16>& rr, int buf) {
+    *reinterpret_cast<float4*>(&s.bc[buf][s_arr][sn * kBCRow + 4 * sg]) = widen4<kInBF16>(rr.bc);
+  };
+
+  float* prow = &s.part[w * kLWave + r * kLRowBlk + n * kLPitch];   // this lane's product row
+  const float* pcol = &s.part[w * kLWave + r * kLRowBlk + n];       // column of its output step
+
+  // Outputs.  bf16: packed per chunk (held[chunk parity]: steps n, n+16), a
+  // 64-step line stored after every odd chunk.  fp32: a 32-step line per chunk.
+  uint32_t held[2] = {0u, 0u};
+  auto put_bf16 = [&](int64_t t_line, bool whole) {
+    const int qh = n >> 2;                        // half of the line's 4 halves that steps 4n.. lie in
+    const int src = 16 * r + 4 * (n & 3);         // lanes holding steps 4n .. 4n+3
+    uint32_t v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t x0 = lane_read(held[0], src + j), x1 = lane_read(held[1], src + j);
+      v[j] = qh < 2 ? x0 : x1;
+    }
+    const bool hi = qh & 1;
+    const uint32_t w01 = hi ? ((v[0] >> 16) | (v[1] & 0xffff0000u)) : ((v[0] & 0xffffu) | (v[1] << 16));
+    const uint32_t w23 = hi ? ((v[2] >> 16) | (v[3] & 0xffff0000u)) : ((v[2] & 0xffffu) | (v[3] << 16));
+    if (c_ok && (whole || qh < 2))
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.y) + row + t_line + 4 * n) = make_uint2(w01, w23);
+  };
+  auto put_f32 = [&](int64_t t0, float o0, float o1) {
+    const int src = 16 * r + ((2 * n) & 15);      // lanes holding steps 2n, 2n+1 (half n >> 3)
+    const bool second = n >= 8;
+    const float a0 = __builtin_bit_cast(float, lane_read(__builtin_bit_cast(uint32_t, o0), src));
+    const float b0 = __builtin_bit_cast(float, lane_read(__builtin_bit_cast(uint32_t, o1), src));
+    const float a1 = __builtin_bit_cast(float, lane_read(__builtin_bit_cast(uint32_t, o0), src + 1));
+    const float b1 = __builtin_bit_cast(float, lane_read(__builtin_bit_cast(uint32_t, o1), src + 1));
+    if (c_ok)
+      *reinterpret_cast<float2*>(static_cast<float*>(p.y) + row + t0 + 2 * n) =
+          make_float2(second ? b0 : a0, second ? b1 : a1);
+  };
+
+  float h = 0.0f;
+  fetch(0, raw[0]);
+  fetch(1, raw[1]);
+  stage(raw[0], 0);
+  prep(raw[0]);
+  lds_barrier();
+
+  auto chunk = [&](auto ptag, int64_t ck) {
+    constexpr int P = decltype(ptag)::kValue;
+    const int64_t t0 = ck * kRCT;
+    fetch(ck + 2, raw[P]);          // raw[P] held chunk ck, already unpacked and staged
+    const float* Bs = &s.bc[P][0][n * kBCRow];
+    const float* Cs = &s.bc[P][1][n * kBCRow];
+    float oh[2];
+    unroll<0, 2>([&](auto ht) {
+      constexpr int hf = decltype(ht)::kValue;
+      float4 Bq = *reinterpret_cast<const float4*>(Bs + 16 * hf);
+      float4 Cq = *reinterpret_cast<const float4*>(Cs + 16 * hf);
+      unroll<0, 4>([&](auto gt) {
+        constexpr int g = decltype(gt)::kValue;
+        float4 Bn = Bq, Cn = Cq;
+        if constexpr (g < 3) {
+          Bn = *reinterpret_cast<const float4*>(Bs + 16 * hf + 4 * g + 4);
+          Cn = *reinterpret_cast<const float4*>(Cs + 16 * hf + 4 * g + 4);
+        }
+        float pt[4];
+        unroll<0, 4>([&](auto it) {
+          constexpr int i = decltype(it)::kValue;
+          constexpr int k = 4 * g + i;     // step 16 hf + k: element hf of lane k of the row
+          const float bn = comp4(Bq, i);
+          const float x = row_bcast<k>(dv[hf]) * a2;
+          const float ee = hw_exp2(x);
+          float ii;
+          if constexpr (kMode == kDeltaB) {
+            ii = row_bcast<k>(duv[hf]) * bn;
+          } else {
+            const float kc = (kMode == kZohFast) ? __builtin_fmaf(ee, ia, -ia) : expm1_from_exp2(x, ee) * ia;
+            ii = kc * (row_bcast<k>(uv[hf]) * bn);
+          }
+          h = __builtin_fmaf(ee, h, ii);
+          pt[i] = comp4(Cq, i) * h;
+        });
+        *reinterpret_cast<float4*>(prow + 4 * g) = make_float4(pt[0], pt[1], pt[2], pt[3]);
+        Bq = Bn;
+        Cq = Cn;
+      });
+      // readout of step 16 hf + n: the 16 states' products of this row (this
+      // wave's own LDS writes, which the LDS performs in order)
+      float v[16];
+#pragma unroll
+      for (int m = 0; m < 16; ++m) v[m] = pcol[m * kLPitch];
+      const float y = (((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]))) +
+                      (((v[8] + v[9]) + (v[10] + v[11])) + ((v[12] + v[13]) + (v[14] + v[15])));
+      oh[hf] = __builtin_fmaf(dskip, uv[hf], y) * gv[hf];
+    });
+    if constexpr (kOutBF16) {
+      held[P] = pack_bf16x2(oh[0], oh[1]);
+      if constexpr (P == 1) put_bf16(t0 - kRCT, true);
+      else if (ck + 1 == nck) put_bf16(t0, false);   // an even last chunk: the first half of a line
+    } else {
+      put_f32(t0, oh[0], oh[1]);
+    }
+    if (ck + 1 < nck) {
+      prep(raw[P ^ 1]);
+      stage(raw[P ^ 1], P ^ 1);
+    }
+    lds_barrier();
+  };
+  for (int64_t ck = 0;; ck += 2) {
+    chunk(Tag<0>{}, ck);
+    if (ck + 1 >= nck) break;
+    chunk(Tag<1>{}, ck + 1);
+    if (ck + 2 >= nck) break;
+  }
+  if (p.final_state != nullptr && c_ok && n_ok) p.final_state[(b * D + d) * N + n] = h;
+}
+
+template <bool kInBF16, bool kOutBF16>
+__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(5)))
+scan_row_lean_kernel(ScanParams p) {
+  __shared__ RowLeanLds s;
+  const int64_t tiles_d = (p.D + 15) / 16;
+  const int64_t b = (int64_t)blockIdx.x / tiles_d;
+  const int64_t d0 = ((int64_t)blockIdx.x - b * tiles_d) * 16;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t d = d0 + 4 * w + (lane >> 4);
+  const int n = lane & 15;
+  const bool small_a = d < p.D && n < p.N && __builtin_fabsf(p.A[d * p.N + n]) < kFastZohMinAbsA;
+  const int any_small = __syncthreads_or(small_a ? 1 : 0);
+  if (p.delta_b) row_scan_lean<kInBF16, kOutBF16, kDeltaB>(p, s, b, d0);
+  else if (p.accurate || any_small) row_scan_lean<kInBF16, kOutBF16, kZohAccurate>(p, s, b, d0);
+  else row_scan_lean<kInBF16, kOutBF16, kZohFast>(p, s, b, d0);
+}
+
 template <bool kInBF16, bool kOutBF16>
 __global__ __launch_bounds__(256) void scan_row_kernel(ScanParams p) {
   __shared__ RowLds s;
@@ -348,18 +581,19 @@ __global__ __launch_bounds__(256) void scan_row_kernel(ScanParams p) {
 }
 
 template <bool kInBF16, bool kOutBF16>
-hipError_t launch_row_t(const ScanParams& p, hipStream_t st) {
+hipError_t launch_row_t(const ScanParams& p, bool lean, hipStream_t st) {
   const int64_t grid = p.B * ((p.D + 15) / 16);
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((scan_row_kernel<kInBF16, kOutBF16>), dim3((unsigned)grid), dim3(256), 0, st, p);
+  if (lean) hipLaunchKernelGGL((scan_row_lean_kernel<kInBF16, kOutBF16>), dim3((unsigned)grid), dim3(256), 0, st, p);
+  else hipLaunchKernelGGL((scan_row_kernel<kInBF16, kOutBF16>), dim3((unsigned)grid), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_scan_row(const ScanParams& p, Dt in, Dt out, hipStream_t s) {
-  if (in == Dt::BF16) return out == Dt::BF16 ? launch_row_t<true, true>(p, s) : launch_row_t<true, false>(p, s);
-  return out == Dt::BF16 ? launch_row_t<false, true>(p, s) : launch_row_t<false, false>(p, s);
+hipError_t launch_scan_row(const ScanParams& p, Dt in, Dt out, bool lean, hipStream_t s) {
+  if (in == Dt::BF16) return out == Dt::BF16 ? launch_row_t<true, true>(p, lean, s) : launch_row_t<true, false>(p, lean, s);
+  return out == Dt::BF16 ? launch_row_t<false, true>(p, lean, s) : launch_row_t<false, false>(p, lean, s);
 }
 
 }  // namespace mamba

@@ -49,9 +49,11 @@ def test_workspace_size_plan():
     ws = _lib.workspace_size
     assert ws(1, 16, 16, 256) == 0
     assert ws(8, 1536, 16, 2048) == 0
+    # 2560 tiles of 16 channels, ten per CU: the lean row kernel, no workspace
+    assert ws(8, 5120, 16, 2048) == 0
     # >= 1024 tiles of 16 channels: balanced split over 1024 waves, one
     # hand-over slot per wave (an 8-byte flag each, then 16 x 16 fp32 states each)
-    assert ws(4, 5120, 16, 2048) == 1024 * 8 + 1024 * 16 * 16 * 4
+    assert ws(4, 4096, 16, 2048) == 1024 * 8 + 1024 * 16 * 16 * 4
     # L % 32 != 0 but L % 8 == 0: the same kernel, its last chunk shifted back
     assert ws(4, 5120, 16, 2040) == 1024 * 8 + 1024 * 16 * 16 * 4
     assert ws(4, 5120, 16, 2044) == 0      # L % 8 != 0: general kernel, no hand-over
@@ -100,8 +102,8 @@ def test_knob_defaults_and_errors():
     import pytest as _pt
     # the general kernel takes 64-channel tiles; no balance drops the hand-over area
     with _lib.test_knobs(scan_no_balance=True):
-        assert _lib.workspace_size(4, 5120, 16, 2048) == 0
-    assert _lib.workspace_size(4, 5120, 16, 2048) == 1024 * 8 + 1024 * 16 * 16 * 4
+        assert _lib.workspace_size(4, 4096, 16, 2048) == 0
+    assert _lib.workspace_size(4, 4096, 16, 2048) == 1024 * 8 + 1024 * 16 * 16 * 4
     with _pt.raises(_lib.MambaError):
         _lib.set_test_knobs(scan_chunks=-1)
     with _lib.test_knobs(ssd_segments=3):
@@ -143,9 +145,9 @@ def update(**kw):
     (dict(A=None), NULL), (dict(y=None), NULL), (dict(fs=None), NULL),
     (dict(u=P + 2), ALIGN), (dict(z=P + 8), ALIGN), (dict(y=P + 4), ALIGN), (dict(Ct=P + 2), ALIGN),
     (dict(A=P + 2), ALIGN), (dict(fs=P + 1), ALIGN),
-    # the 2.8B layer's balanced split needs a workspace (hand-over slots)
-    (dict(B=4, D=5120, L=2048), WS),
-    (dict(B=4, D=5120, L=2048, ws=P, wsb=1024), WS),
+    # the balanced split of the wave-tile kernel needs a workspace (hand-over slots)
+    (dict(B=4, D=4096, L=2048), WS),
+    (dict(B=4, D=4096, L=2048, ws=P, wsb=1024), WS),
 ])
 def test_scan_rejects_bad_arguments(kw, code):
     assert scan(**kw) == code
@@ -155,7 +157,7 @@ def test_scan_optional_pointers_do_not_trigger_errors_early():
     # z, Dskip, bias may be NULL and final state is ignored when not requested;
     # with everything else valid but the workspace missing, the workspace error
     # is what comes back (so no launch happens).
-    st = scan(z=None, Dskip=None, bias=None, fs=None, rfs=0, B=4, D=5120, L=2048)
+    st = scan(z=None, Dskip=None, bias=None, fs=None, rfs=0, B=4, D=4096, L=2048)
     assert st == WS
 
 
@@ -335,31 +337,40 @@ def scan_noalloc(**kw):
 
 
 def test_scan_kernel_choice():
-    """The planner's kernel per workload: the row kernel where 16-channel wave
+    """The planner's kernel per workload: the lean row kernel from nine
+    16-channel workgroups per CU on, the row kernel where 16-channel wave
     tiles would leave SIMDs idle or need chunking (130M layer, batch-1 long
-    sequence) and from eight row workgroups per CU on, the wave-tile kernel's
-    balanced split at the 2.8B layer and for ragged lengths, chunking of the
-    wave-tile kernel for very few tiles over long L, the general kernel for
-    L % 8 != 0.  (Each choice was the faster kernel in an interleaved timing of
-    both on MI355X.)"""
+    sequence), the wave-tile kernel's balanced split from four to eight
+    workgroups per CU (the 2.8B layer) and for ragged lengths, chunking of the wave-tile kernel for very few
+    tiles over long L, the general kernel for L % 8 != 0.  (Each choice was
+    the fastest kernel in an interleaved timing of all of them on MI355X.)"""
     k = _lib.scan_kernel
     assert k(8, 1536, 16, 2048) == "row"
     assert k(1, 4096, 16, 131072) == "row"
     assert k(4, 5120, 16, 2048) == "wave_tile"
+    assert k(5, 4096, 16, 2048) == "wave_tile"
+    assert k(7, 4096, 16, 2048) == "wave_tile"
+    assert k(4, 4096, 16, 2048) == "wave_tile"
+    assert k(3, 5120, 16, 2048) == "wave_tile"
+    assert k(4, 5120, 16, 2040) == "wave_tile"
     assert k(1, 4096, 16, 131072 - 8) == "wave_tile"
     assert k(1, 1024, 16, 65536) == "wave_tile"
     assert k(1, 2048, 16, 16384) == "wave_tile"
     assert k(1, 5120, 16, 8192) == "wave_tile"
     assert k(2, 2560, 16, 4096) == "row"
-    assert k(8, 5120, 16, 2048) == "row"
-    assert k(32, 1536, 16, 2048) == "row"
+    assert k(8, 5120, 16, 2048) == "row_lean"
+    assert k(32, 1536, 16, 2048) == "row_lean"
+    assert k(9, 4096, 16, 2048) == "row_lean"
     assert k(2, 100, 16, 100) == "general"
     assert k(1, 16, 16, 16) == "general"
     with _lib.test_knobs(scan_kernel="wave_tile"):
         assert k(8, 1536, 16, 2048) == "wave_tile"
     with _lib.test_knobs(scan_kernel="row"):
         assert k(4, 5120, 16, 2048) == "row"
-        assert k(4, 5120, 16, 2040) == "wave_tile"    # the row kernel needs L % 32 == 0
+        assert k(4, 5120, 16, 2040) == "wave_tile"    # the row kernels need L % 32 == 0
+    with _lib.test_knobs(scan_kernel="row_lean"):
+        assert k(8, 1536, 16, 2048) == "row_lean"
+        assert k(4, 5120, 16, 2040) == "wave_tile"
     with _lib.test_knobs(scan_kernel="general"):
         assert k(4, 5120, 16, 2048) == "general"
     assert _lib.lib().mamba_scan_kernel(1, 1, 17, 1) == UNSUP

@@ -280,16 +280,17 @@ def _ragged_case(case, dev):
 def test_handover_fallback_matches(shape, dev):
     """With the hand-over wait forced to zero every split tile recomputes its
     state at the cut (from the start of its chunk) instead of receiving it;
-    the output must not change."""
+    the output must not change.  (The wave-tile kernel is forced: the planner
+    gives some of these shapes to a row kernel, which splits no tile.)"""
     import torch
     import selective_state_space_75_amd as m
     B, D, N, L, chunks = shape
     x = W.custom_scan_inputs(B, D, N, L, "bf16", seed=31337)
     t = upload_scan(x, dev)
-    with m.test_knobs(scan_chunks=chunks or 0):
+    with m.test_knobs(scan_chunks=chunks or 0, scan_kernel="wave_tile"):
         assert m.workspace_size(B, D, N, L) > 0
         y1, h1 = gpu_scan(t, return_final_state=True)
-    with m.test_knobs(scan_chunks=chunks or 0, handover_spin=0):
+    with m.test_knobs(scan_chunks=chunks or 0, scan_kernel="wave_tile", handover_spin=0):
         y2, h2 = gpu_scan(t, return_final_state=True)
     torch.cuda.synchronize()
     assert torch.equal(y1, y2) and torch.equal(h1, h2)

@@ -1,7 +1,8 @@
-"""GPU parity of the one-state-per-lane (row) scan kernel against the oracle.
+"""GPU parity of the one-state-per-lane (row) scan kernels against the oracle.
 
-The kernel is selected with the scan_kernel test knob, so every case runs it
-whatever the planner would choose: ragged channel counts (a workgroup's 16
+Both variants (row, and row_lean with fewer registers and less LDS per
+workgroup) are selected with the scan_kernel test knob, so every case runs
+them whatever the planner would choose: ragged channel counts (a workgroup's 16
 channels and a wave's 4 only partly present), N < 16 (lanes holding no
 state), one and two 32-step chunks, fp32 and bf16 inputs and outputs, the
 simplified rule, the accurate flag, A = 0 and denormal A, small |A| in one
@@ -32,13 +33,17 @@ CASES = [
 ]
 
 
+ROW_KERNELS = ["row", "row_lean"]
+
+
+@pytest.mark.parametrize("kernel", ROW_KERNELS)
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "B%dD%dN%dL%d_%s_%s_%s" % (
     c[0], c[1], c[2], c[3], c[4], c[5], "-".join(sorted(c[6])) or "plain"))
-def test_row_kernel_cases(case, dev):
+def test_row_kernel_cases(case, kernel, dev):
     import torch
     import selective_state_space_75_amd as m
     B, D, N, L, dt, odt, opts = case
-    log("[row] %s" % (case,))
+    log("[%s] %s" % (kernel, case))
     x = W.custom_scan_inputs(B, D, N, L, dt, seed=6000 + B * 131 + D * 7 + L + N)
     if opts.get("zero_A"):
         A = x["A"].copy()
@@ -58,7 +63,8 @@ def test_row_kernel_cases(case, dev):
     if opts.get("no_bias"):
         t["delta_bias"] = None
     out_dtype = torch.float32 if odt == "f32" else torch.bfloat16
-    with m.test_knobs(scan_kernel="row"):
+    with m.test_knobs(scan_kernel=kernel):
+        assert m.scan_kernel(B, D, N, L) == kernel
         assert m.workspace_size(B, D, N, L) == 0
         y, hN = gpu_scan(t, return_final_state=True, out_dtype=out_dtype, delta_b=opts.get("delta_b", False),
                          accurate_expm1=opts.get("accurate", False))
@@ -67,55 +73,59 @@ def test_row_kernel_cases(case, dev):
                          use_bias=not opts.get("no_bias"),
                          discretization="delta_b" if opts.get("delta_b") else "zoh")
     bf16 = dt == "bf16" or odt == "bf16"
-    assert_close(from_dev(y), yr, bf16, "row y")
+    assert_close(from_dev(y), yr, bf16, "%s y" % kernel)
     e = rel_l2(from_dev(hN), hr)
     log("  final state rel_l2=%.3e" % e)
     assert e <= (2e-3 if dt == "bf16" else 1e-5)
 
 
-def test_row_kernel_matches_wave_tile_kernel(dev):
-    """Both kernels compute each state update with the same operations in the
-    same order; only the readout's summation order over the 16 states
-    differs, so y agrees to fp32 rounding and the final state bit for bit."""
+@pytest.mark.parametrize("kernel", ROW_KERNELS)
+def test_row_kernel_matches_wave_tile_kernel(kernel, dev):
+    """The row kernels compute each state update with the same operations in
+    the same order as the wave-tile kernel; only the readout's summation
+    order over the 16 states differs, so y agrees to fp32 rounding and the
+    final state bit for bit."""
     import torch
     import selective_state_space_75_amd as m
     x = W.custom_scan_inputs(2, 256, 16, 1024, "bf16", seed=6500)
     t = upload_scan(x, dev)
-    with m.test_knobs(scan_kernel="row"):
+    with m.test_knobs(scan_kernel=kernel):
         y1, h1 = gpu_scan(t, return_final_state=True, out_dtype=torch.float32)
     with m.test_knobs(scan_kernel="wave_tile"):
         y2, h2 = gpu_scan(t, return_final_state=True, out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert torch.equal(h1, h2), "final states differ"
     e = rel_l2(from_dev(y1), from_dev(y2))
-    log("  row vs wave-tile y: rel_l2=%.3e" % e)
+    log("  %s vs wave-tile y: rel_l2=%.3e" % (kernel, e))
     assert e <= 1e-6
 
 
 @pytest.mark.parametrize("name", ["mamba130m_layer", "long_b1"])
 def test_row_kernel_full_workload(name, dev):
-    """Every output of a full workload on the row kernel, bf16 and fp32
-    output, against the oracle (run in 256-channel blocks)."""
+    """Every output of a full workload on both row kernels, bf16 and fp32
+    output, against the oracle (run once, in 256-channel blocks)."""
     import torch
     import selective_state_space_75_amd as m
     cfg = W.SCAN_CONFIGS[name]
     x = W.scan_inputs(cfg)
     t = upload_scan(x, dev)
     outs = {}
-    with m.test_knobs(scan_kernel="row"):
-        for odt in (torch.bfloat16, torch.float32):
-            outs[odt] = gpu_scan(t, return_final_state=True, out_dtype=odt)
+    for kernel in ROW_KERNELS:
+        with m.test_knobs(scan_kernel=kernel):
+            for odt in (torch.bfloat16, torch.float32):
+                outs[(kernel, odt)] = gpu_scan(t, return_final_state=True, out_dtype=odt)
     torch.cuda.synchronize()
     del t
-    errs = {odt: (BlockErr(), BlockErr()) for odt in outs}
+    errs = {key: (BlockErr(), BlockErr()) for key in outs}
     for b, d0, d1, yr, hr in oracle_scan_blocks(x, block=256):
-        for odt, (ey, eh) in errs.items():
-            y, hN = outs[odt]
+        for key, (ey, eh) in errs.items():
+            y, hN = outs[key]
             ey.add(from_dev(y[b, d0:d1]), yr)
             eh.add(from_dev(hN[b, d0:d1]), hr)
-    ey, eh = errs[torch.bfloat16]
-    log("  %s row y bf16: rel_l2=%.3e max_abs/max|y|=%.3e" % (name, ey.rel_l2, ey.max_abs_frac))
-    assert ey.rel_l2 <= BF16_REL_L2 and ey.max_abs_frac <= BF16_MAX_ABS_FRAC
-    ey, eh = errs[torch.float32]
-    log("  %s row y fp32: rel_l2=%.3e; final state rel_l2=%.3e" % (name, ey.rel_l2, eh.rel_l2))
-    assert ey.rel_l2 <= F32_OUT_REL_L2 and eh.rel_l2 <= F32_OUT_REL_L2
+    for kernel in ROW_KERNELS:
+        ey, eh = errs[(kernel, torch.bfloat16)]
+        log("  %s %s y bf16: rel_l2=%.3e max_abs/max|y|=%.3e" % (name, kernel, ey.rel_l2, ey.max_abs_frac))
+        assert ey.rel_l2 <= BF16_REL_L2 and ey.max_abs_frac <= BF16_MAX_ABS_FRAC
+        ey, eh = errs[(kernel, torch.float32)]
+        log("  %s %s y fp32: rel_l2=%.3e; final state rel_l2=%.3e" % (name, kernel, ey.rel_l2, eh.rel_l2))
+        assert ey.rel_l2 <= F32_OUT_REL_L2 and eh.rel_l2 <= F32_OUT_REL_L2
