@@ -213,7 +213,7 @@ constexpr unsigned kKnownFlags = MAMBA_FLAG_DELTA_B | MAMBA_FLAG_ACCURATE_EXPM1;
 }  // namespace
 
 struct BwdPlan {
-  int64_t tiles_d = 0, nck = 0, S = 0, seg_len = 0;
+  int64_t tiles_d = 0, groups = 0, nck = 0, S = 0, seg_len = 0;
   size_t off_ckh = 0, off_ckd = 0, off_sp = 0, off_sh = 0, off_sH = 0, off_hin = 0, off_gin = 0;
   size_t off_pb = 0, off_pc = 0, off_pa = 0, off_pd = 0, off_pbias = 0, bytes = 0;
 };
@@ -228,6 +228,7 @@ BwdPlan make_bwd_plan(int64_t B, int64_t D, int64_t L) {
   BwdPlan q;
   constexpr int64_t kC = mamba::kBwdChunk;
   q.tiles_d = (D + 15) / 16;
+  q.groups = (q.tiles_d + mamba::kBwdGroup - 1) / mamba::kBwdGroup;
   q.nck = (L + kC - 1) / kC;
   const int64_t rows = B * q.tiles_d;
   int64_t S = (8192 + rows - 1) / rows;
@@ -251,8 +252,8 @@ BwdPlan make_bwd_plan(int64_t B, int64_t D, int64_t L) {
   q.off_sH = o; o += align256(bsd * 16 * sizeof(float));
   q.off_hin = o; o += align256(bsd * 16 * sizeof(float));
   q.off_gin = o; o += align256(bsd * 16 * sizeof(float));
-  q.off_pb = o; o += align256(size_t(B) * size_t(q.tiles_d) * 16 * size_t(L) * sizeof(float));
-  q.off_pc = o; o += align256(size_t(B) * size_t(q.tiles_d) * 16 * size_t(L) * sizeof(float));
+  q.off_pb = o; o += align256(size_t(B) * size_t(q.groups) * 16 * size_t(L) * sizeof(float));
+  q.off_pc = o; o += align256(size_t(B) * size_t(q.groups) * 16 * size_t(L) * sizeof(float));
   q.off_pa = o; o += align256(bsd * 16 * sizeof(float));
   q.off_pd = o; o += align256(bsd * sizeof(float));
   q.off_pbias = o; o += align256(bsd * sizeof(float));
@@ -517,7 +518,7 @@ int mamba_scan_bwd(const void* u, const void* delta, const void* z, const void* 
   p.part_dA = at(plan.off_pa);
   p.part_dD = at(plan.off_pd);
   p.part_dbias = at(plan.off_pbias);
-  p.B = B; p.D = D; p.N = N; p.L = L; p.tiles_d = plan.tiles_d; p.nck = plan.nck;
+  p.B = B; p.D = D; p.N = N; p.L = L; p.tiles_d = plan.tiles_d; p.groups = plan.groups; p.nck = plan.nck;
   p.S = plan.S; p.seg_len = plan.seg_len;
   p.delta_b = (flags & MAMBA_FLAG_DELTA_B) ? 1 : 0;
   p.accurate = (flags & MAMBA_FLAG_ACCURATE_EXPM1) ? 1 : 0;

@@ -90,6 +90,9 @@ struct ConvParams {
 // kBwdChunk); each segment is cut into chunks of kBwdChunk steps, the unit
 // that is recomputed on chip.
 constexpr int kBwdChunk = 8;
+// 16-channel tiles per workgroup of the backward segment pass; the workgroup
+// sums its tiles' dB_t / dC_t contributions before storing one partial.
+constexpr int kBwdGroup = 4;
 
 struct BwdParams {
   const void *u, *delta, *z, *Bt, *Ct, *dy;
@@ -100,9 +103,10 @@ struct BwdParams {
   float *ckpt_cd;                               // (B, D, nck) sum of delta from the segment start to the chunk
   float *seg_P, *seg_h, *seg_H;                 // (B, S, D, 16) segment summaries
   float *h_in, *g_in;                           // (B, S, D, 16) state entering / adjoint leaving each segment
-  float *part_dB, *part_dC;                     // (B, tiles_d, 16, L) per-tile sums over channels
+  float *part_dB, *part_dC;                     // (B, groups, 16, L) sums over a workgroup's channels
   float *part_dA, *part_dD, *part_dbias;        // (B, S, D, 16), (B, S, D), (B, S, D) per-segment sums
   int64_t B, D, N, L, tiles_d, nck, S, seg_len;
+  int64_t groups;                               // ceil(tiles_d / kBwdGroup)
   int delta_b;
   int accurate; // cancellation-free (Abar - 1)/A for bf16 inputs too
   int vec;      // L % 8 == 0 and every (B, D, L) / (B, N, L) array 16-byte aligned

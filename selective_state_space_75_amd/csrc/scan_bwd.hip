@@ -191,15 +191,15 @@ struct Wave {
     Raw8<kGradBF16> dy;
   };
 
-  __device__ explicit Wave(const BwdParams& pp) : p(pp) {
-    lane = threadIdx.x;
+  // lane of the wave; tile td (tiles past the last have no channel), segment
+  // ss, batch row bb
+  __device__ Wave(const BwdParams& pp, int lane_, int64_t td_, int64_t ss, int64_t bb) : p(pp) {
+    lane = lane_;
     c = lane >> 2;
     g = lane & 3;
-    const int64_t w = blockIdx.x;
-    td = w % p.tiles_d;
-    const int64_t rest = w / p.tiles_d;
-    s = rest % p.S;
-    b = rest / p.S;
+    td = td_;
+    s = ss;
+    b = bb;
     d = td * 16 + c;
     c_ok = d < p.D;
     dd = c_ok ? d : 0;          // channels past D read channel 0 and contribute nothing
@@ -361,7 +361,8 @@ __device__ __forceinline__ void summary_body(const BwdParams& p, const Wave<kInB
 template <bool kInBF16, bool kGradBF16, int M>
 __global__ __launch_bounds__(64) void bwd_summary_kernel(BwdParams p) {
   __shared__ Stage st;
-  const Wave<kInBF16, kGradBF16> w(p);
+  const int64_t task = blockIdx.x, rest = task / p.tiles_d;
+  const Wave<kInBF16, kGradBF16> w(p, (int)threadIdx.x, task % p.tiles_d, rest % p.S, rest / p.S);
   if (M == kZohFast && __any(w.small_a)) summary_body<kInBF16, kGradBF16, kZohAccurate>(p, w, st);
   else summary_body<kInBF16, kGradBF16, M>(p, w, st);
 }
@@ -392,8 +393,10 @@ __global__ __launch_bounds__(256) void bwd_carry_kernel(BwdParams p) {
 // and the segment's entering state, rerun its steps keeping h_t and
 // (Abar_t - 1) in registers, then walk them in reverse with the adjoint.
 template <bool kInBF16, bool kGradBF16, int M>
-__device__ __forceinline__ void segment_body(const BwdParams& p, const Wave<kInBF16, kGradBF16>& w, Stage& st) {
+__device__ __forceinline__ void segment_body(const BwdParams& p, const Wave<kInBF16, kGradBF16>& w,
+                                             Stage (&sts)[kBwdGroup], int wv, int64_t tg) {
   using W = Wave<kInBF16, kGradBF16>;
+  Stage& st = sts[wv];
   const int lane = w.lane, c = w.c, g = w.g;
   const bool red_c = lane >= 32;
   const bool bit3 = (lane >> 3) & 1, bit2 = (lane >> 2) & 1;
@@ -594,16 +597,19 @@ __device__ __forceinline__ void segment_body(const BwdParams& p, const Wave<kInB
         st8<kGradBF16>(p.ddelta, w.row + t0 + 8 * g, vec, valid, dr);
         if (w.has_z) st8<kGradBF16>(p.dz, w.row + t0 + 8 * g, vec, valid, dz);
       }
-      if (w.sn_ok) {
-        float vb[8], vcc[8];
+      // the workgroup's dB_t (wave 0) and dC_t (wave 1) for state c: the
+      // tiles' partials summed in tile order
+      if (wv < 2 && w.sn_ok) {
+        float v[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          vb[j] = st.B[8 * g + j][c];
-          vcc[j] = st.C[8 * g + j][c];
+          float acc = wv == 0 ? sts[0].B[8 * g + j][c] : sts[0].C[8 * g + j][c];
+#pragma unroll
+          for (int q = 1; q < kBwdGroup; ++q) acc += wv == 0 ? sts[q].B[8 * g + j][c] : sts[q].C[8 * g + j][c];
+          v[j] = acc;
         }
-        const int64_t o = ((w.b * p.tiles_d + w.td) * 16 + c) * p.L + t0 + 8 * g;
-        st8<false>(p.part_dB, o, vec, valid, vb);
-        st8<false>(p.part_dC, o, vec, valid, vcc);
+        const int64_t o = ((w.b * p.groups + tg) * 16 + c) * p.L + t0 + 8 * g;
+        st8<false>(wv == 0 ? p.part_dB : p.part_dC, o, vec, valid, v);
       }
     }
     if (more) {
@@ -628,15 +634,21 @@ __device__ __forceinline__ void segment_body(const BwdParams& p, const Wave<kInB
   }
 }
 
+// A workgroup is kBwdGroup waves, one per 16-channel tile of a group of
+// adjacent tiles, all on the same segment and batch row (so they pass the
+// same barriers).  The cancellation-free quotient is chosen per wave.
 template <bool kInBF16, bool kGradBF16, int M>
-__global__ __launch_bounds__(64) void bwd_segment_kernel(BwdParams p) {
-  __shared__ Stage st;
-  const Wave<kInBF16, kGradBF16> w(p);
-  if (M == kZohFast && __any(w.small_a)) segment_body<kInBF16, kGradBF16, kZohAccurate>(p, w, st);
-  else segment_body<kInBF16, kGradBF16, M>(p, w, st);
+__global__ __launch_bounds__(64 * kBwdGroup) void bwd_segment_kernel(BwdParams p) {
+  __shared__ Stage st[kBwdGroup];
+  const int wv = (int)(threadIdx.x >> 6);
+  const int64_t task = blockIdx.x, rest = task / p.groups;
+  const int64_t tg = task % p.groups;
+  const Wave<kInBF16, kGradBF16> w(p, (int)(threadIdx.x & 63), tg * kBwdGroup + wv, rest % p.S, rest / p.S);
+  if (M == kZohFast && __any(w.small_a)) segment_body<kInBF16, kGradBF16, kZohAccurate>(p, w, st, wv, tg);
+  else segment_body<kInBF16, kGradBF16, M>(p, w, st, wv, tg);
 }
 
-// dB_t, dC_t: sum of the per-tile partials, in tile order.
+// dB_t, dC_t: sum of the per-workgroup partials, in tile order.
 __global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(BwdParams p) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t total = p.B * p.N * p.L;
@@ -644,14 +656,14 @@ __global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(BwdParams p) {
   const int64_t b = i / (p.N * p.L);
   const int64_t rem = i - b * p.N * p.L;
   const int64_t n = rem / p.L, t = rem - n * p.L;
-  const float* pb = p.part_dB + (b * p.tiles_d * 16 + n) * p.L + t;
-  const float* pc = p.part_dC + (b * p.tiles_d * 16 + n) * p.L + t;
+  const float* pb = p.part_dB + (b * p.groups * 16 + n) * p.L + t;
+  const float* pc = p.part_dC + (b * p.groups * 16 + n) * p.L + t;
   const int64_t stride = 16 * p.L;
   float sb = 0.0f, sc = 0.0f;
 #pragma unroll 8
-  for (int64_t td = 0; td < p.tiles_d; ++td) {
-    sb += pb[td * stride];
-    sc += pc[td * stride];
+  for (int64_t q = 0; q < p.groups; ++q) {
+    sb += pb[q * stride];
+    sc += pc[q * stride];
   }
   p.dBt[i] = sb;
   p.dCt[i] = sc;
@@ -691,7 +703,8 @@ hipError_t bwd_t(const BwdParams& p, hipStream_t s) {
   hipLaunchKernelGGL(bwd_carry_kernel, dim3((unsigned)((p.B * p.D * 16 + 255) / 256)), dim3(256), 0, s, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_segment_kernel<kInBF16, kGradBF16, M>), tasks, dim3(64), 0, s, p);
+  hipLaunchKernelGGL((bwd_segment_kernel<kInBF16, kGradBF16, M>), dim3((unsigned)(p.B * p.groups * p.S)),
+                     dim3(64 * kBwdGroup), 0, s, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t nbc = p.B * p.N * p.L;

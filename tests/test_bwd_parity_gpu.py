@@ -77,6 +77,7 @@ CASES = [
     (3, 33, 5, 41, "bf16", "f32", {"accurate": True}),
     (2, 48, 16, 96, "bf16", "f32", {"small_A": True}),   # tile 0 on the accurate quotient, tiles 1-2 fast
     (2, 48, 16, 96, "bf16", "f32", {"small_A": True, "accurate": True}),
+    (1, 150, 16, 96, "bf16", "f32", {"small_A": True}),  # 10 tiles: workgroups of 4, 4 and 2 (+2 empty)
 ]
 
 
