@@ -7,7 +7,8 @@ channels and a wave's 4 only partly present), N < 16 (lanes holding no
 state), one and two 32-step chunks, fp32 and bf16 inputs and outputs, the
 simplified rule, the accurate flag, A = 0 and denormal A, small |A| in one
 tile (the cancellation-free quotient for that workgroup only), absent z, D
-and bias, and the full 130M-layer and batch-1 long workloads (every output).
+and bias, the full 130M-layer and batch-1 long workloads (every output), and a
+shape the planner itself gives to the lean kernel.
 """
 import numpy as np
 import pytest
@@ -129,3 +130,31 @@ def test_row_kernel_full_workload(name, dev):
         ey, eh = errs[(kernel, torch.float32)]
         log("  %s %s y fp32: rel_l2=%.3e; final state rel_l2=%.3e" % (name, kernel, ey.rel_l2, eh.rel_l2))
         assert ey.rel_l2 <= F32_OUT_REL_L2 and eh.rel_l2 <= F32_OUT_REL_L2
+
+
+def test_lean_row_kernel_on_planner_shape(dev):
+    """A shape the planner gives to the lean row kernel (ten 16-channel tiles
+    per CU: B=8, D=5120, L=1024), through the planner, every output and the
+    final state against the oracle, bf16 and fp32 output."""
+    import torch
+    import selective_state_space_75_amd as m
+    B, D, N, L = 8, 5120, 16, 1024
+    assert m.scan_kernel(B, D, N, L) == "row_lean"
+    assert m.workspace_size(B, D, N, L) == 0
+    x = W.custom_scan_inputs(B, D, N, L, "bf16", seed=6700)
+    t = upload_scan(x, dev)
+    outs = {odt: gpu_scan(t, return_final_state=True, out_dtype=odt) for odt in (torch.bfloat16, torch.float32)}
+    torch.cuda.synchronize()
+    del t
+    errs = {odt: (BlockErr(), BlockErr()) for odt in outs}
+    for b, d0, d1, yr, hr in oracle_scan_blocks(x, block=1024):
+        for odt, (ey, eh) in errs.items():
+            y, hN = outs[odt]
+            ey.add(from_dev(y[b, d0:d1]), yr)
+            eh.add(from_dev(hN[b, d0:d1]), hr)
+    ey, _ = errs[torch.bfloat16]
+    log("  lean planner shape y bf16: rel_l2=%.3e max_abs/max|y|=%.3e" % (ey.rel_l2, ey.max_abs_frac))
+    assert ey.rel_l2 <= BF16_REL_L2 and ey.max_abs_frac <= BF16_MAX_ABS_FRAC
+    ey, eh = errs[torch.float32]
+    log("  lean planner shape y fp32: rel_l2=%.3e; final state rel_l2=%.3e" % (ey.rel_l2, eh.rel_l2))
+    assert ey.rel_l2 <= F32_OUT_REL_L2 and eh.rel_l2 <= F32_OUT_REL_L2
