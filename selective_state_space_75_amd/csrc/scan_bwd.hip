@@ -40,8 +40,10 @@
 // are evaluated once there, not once per lane of a channel.
 // dB_t and dC_t are shared by the D channels of a batch row: each step, the
 // wave sums its 16 channels' contributions with cross-lane swaps (permlane32,
-// permlane16, two DPP row rotations) into one per-tile partial per state; a
-// second kernel adds the partials of all tiles in a fixed order, and the
+// permlane16, two DPP row rotations) into one value per state; the segment
+// pass runs four such waves per workgroup (four adjacent tiles), which add
+// their values in tile order after each block and store one partial; a
+// second kernel adds the workgroups' partials in a fixed order, and the
 // per-batch-row partials of dA, dD and the bias gradient likewise, so results
 // are deterministic.
 #include <type_traits>

@@ -1,9 +1,11 @@
-// scan_row.hip -- selective-scan kernel with one state per lane (gfx950), for
-// shapes with few channel tiles: the batch-1 long sequence and other layers
-// whose 16-channel tiles do not fill the chip.  Same computation as
-// scan_v4.hpp ("Mamba 模型", full-step flowchart nodes H to M; ZOH per
-// "Mamba模型：高效序列建模的新突破" 3.1): softplus step, ZOH discretisation,
-// recurrence, readout, skip, gate.
+// scan_row.hip -- selective-scan kernels with one state per lane (gfx950).
+// Same computation as scan_v4.hpp ("Mamba 模型", full-step flowchart nodes H
+// to M; ZOH per "Mamba模型：高效序列建模的新突破" 3.1): softplus step, ZOH
+// discretisation, recurrence, readout, skip, gate.  Two variants:
+// scan_row_kernel for shapes whose 16-channel tiles do not fill the chip (the
+// batch-1 long sequence, the 130M layer), and scan_row_lean_kernel, which
+// trades in-wave lookahead for five workgroups per CU, for shapes with many
+// tiles per CU.
 //
 // Layout -- a workgroup of 4 waves owns 16 channels of one batch row:
 //  * wave w holds channels 4w .. 4w+3, one per 16-lane DPP row; lane n of a
@@ -23,7 +25,9 @@
 //    addresses).  One workgroup barrier per chunk guards the buffers;
 //  * the readout's per-state products C_t,n h_t,n go through LDS once per
 //    chunk: each lane writes its 32 products, then reads the 16 products of
-//    each of its 2 output steps and sums them (15 adds per output).
+//    each of its 2 output steps and sums them (15 adds per output);
+//  * outputs leave in whole 128-byte lines, gathered across the lanes of a
+//    row with ds_bpermute.
 // Per state update: 6 fp32 VALU + 1 v_exp_f32, as in the 4-states-per-lane
 // kernel, plus a quarter of a 16-byte LDS read each for B_t and C_t.
 #include "device_math.hpp"
