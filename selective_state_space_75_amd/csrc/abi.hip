@@ -93,7 +93,8 @@ Plan make_plan(int64_t B, int64_t D, int64_t N, int64_t L, const mamba_test_knob
   Plan p;
   p.tiles_d = (D + kTile - 1) / kTile;
   p.v4 = (L % 8 == 0) && L >= kV4Step && kn.scan_kernel != 1;
-  const bool row_ok = L % kRowStep == 0 && kn.scan_kernel != 1 && kn.scan_kernel != 2 && kn.scan_chunks == 0;
+  const bool row_ok = L % kRowStep == 0 && kn.scan_kernel != 1 && kn.scan_kernel != 2 &&
+                      (kn.scan_chunks == 0 || kn.scan_kernel == 3);
   if (row_ok) {
     const int64_t tiles16 = B * ((D + kV4Tile - 1) / kV4Tile);
     const int64_t per_cu = (tiles16 + kCUsPlan - 1) / kCUsPlan;
@@ -103,7 +104,26 @@ Plan make_plan(int64_t B, int64_t D, int64_t N, int64_t L, const mamba_test_knob
     // split either way (at 5, the 2.8B layer, 1% slower in the streaming
     // benchmark), and at 4 it lost by 4%.
     const bool lean = kn.scan_kernel == 4 || (kn.scan_kernel == 0 && per_cu >= 9);
-    bool row = kn.scan_kernel == 3 || lean;
+    // With 64 to 384 tiles (1.5 per CU at most) the row kernel cuts L into K
+    // chunks so that each of its two passes puts K - 1 workgroups on every
+    // tile, about three per CU: the first pass runs chunk 0 in full and
+    // chunks 1 .. K-2 as summaries, the second chunks 1 .. K-1 from the
+    // carried states.  Chunks of at least 2048 steps, a multiple of 64.
+    // Timed on MI355X this beat the wave-tile kernel's chunked path at every
+    // shape tried (B = 1 with D = 1024, 2048, 4096 and 5120, L = 8192 to
+    // 131072: by 1 to 14%), so it is taken whenever it applies.
+    int64_t k = 1;
+    if (!lean) {
+      if (kn.scan_chunks > 0) {
+        k = kn.scan_chunks;
+      } else if (tiles16 >= 64 && tiles16 <= 384) {
+        k = 768 / tiles16 + 1;
+        if (k > L / 2048) k = L / 2048;
+        if (k > 16) k = 16;
+        if (k < 3) k = 1;
+      }
+    }
+    bool row = kn.scan_kernel == 3 || lean || (kn.scan_kernel == 0 && k >= 3);
     if (!row) {
       double best = v4_chunk_cost(tiles16, 1);
       const int64_t kmax = L >= 4096 && tiles16 < kGroupsPlan ? (L / 2048 < 64 ? L / 2048 : 64) : 1;
@@ -115,7 +135,21 @@ Plan make_plan(int64_t B, int64_t D, int64_t N, int64_t L, const mamba_test_knob
       p.row_lean = lean;
       p.v4 = false;
       p.tiles_d = (D + kV4Tile - 1) / kV4Tile;
-      return p;   // one pass, no workspace
+      if (k > 1) {
+        int64_t len = (L + k - 1) / k;
+        len = (len + 2 * kRowStep - 1) / (2 * kRowStep) * (2 * kRowStep);
+        p.chunk_len = len;
+        p.n_chunks = (L + len - 1) / len;
+      }
+      if (p.n_chunks > 1) {
+        const size_t state = size_t(p.n_chunks) * size_t(B) * size_t(D) * size_t(N) * sizeof(float);
+        const size_t sums = size_t(p.n_chunks) * size_t(B) * size_t(D) * sizeof(float);
+        p.off_local = 0;
+        p.off_start = align256(state);
+        p.off_sum = p.off_start + align256(state);
+        p.ws_bytes = p.off_sum + align256(sums);
+      }
+      return p;   // one pass, or two over chunks with the carry between them
     }
   }
   // Units of independent sequential work: 16-channel tiles (wave-tile
@@ -332,12 +366,13 @@ int scan_fwd_run(const void* u, const void* delta, const void* z, const void* Bt
     p.s_sum = reinterpret_cast<float*>(ws + plan.off_sum);
     mamba::V2Params qs = q;   // the summary pass runs one workgroup per (chunk, tile)
     qs.balanced = 0;
-    const hipError_t e = plan.v4 ? mamba::launch_scan_v4(p, qs, in, out, true, stream)
-                                 : mamba::launch_scan_summary(p, in, stream);
+    const hipError_t e = plan.row ? mamba::launch_scan_row(p, in, out, false, 1, stream)
+                         : plan.v4 ? mamba::launch_scan_v4(p, qs, in, out, true, stream)
+                                   : mamba::launch_scan_summary(p, in, stream);
     if (e != hipSuccess) return MAMBA_ERR_HIP;
     if (mamba::launch_scan_carry(p, stream) != hipSuccess) return MAMBA_ERR_HIP;
   }
-  const hipError_t e = plan.row ? mamba::launch_scan_row(p, in, out, plan.row_lean, stream)
+  const hipError_t e = plan.row ? mamba::launch_scan_row(p, in, out, plan.row_lean, plan.n_chunks > 1 ? 2 : 0, stream)
                        : plan.v4 ? mamba::launch_scan_v4(p, q, in, out, false, stream)
                                  : mamba::launch_scan_full(p, in, out, stream);
   if (e != hipSuccess) return MAMBA_ERR_HIP;

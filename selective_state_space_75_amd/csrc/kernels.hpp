@@ -132,7 +132,9 @@ hipError_t launch_scan_summary(const ScanParams& p, Dt in, hipStream_t s);
 hipError_t launch_scan_carry(const ScanParams& p, hipStream_t s);
 hipError_t launch_clear_u64(uint64_t* p, int64_t n, hipStream_t s);
 hipError_t launch_scan_v4(const ScanParams& p, const V2Params& q, Dt in, Dt out, bool summary, hipStream_t s);
-hipError_t launch_scan_row(const ScanParams& p, Dt in, Dt out, bool lean, hipStream_t s);
+// phase 0: whole sequences; 1 and 2: the two passes over L in p.n_chunks
+// chunks (before and after the carry kernel), not for the lean variant.
+hipError_t launch_scan_row(const ScanParams& p, Dt in, Dt out, bool lean, int phase, hipStream_t s);
 hipError_t launch_state_update(const UpdateParams& p, Dt in, Dt out, hipStream_t s);
 hipError_t launch_scan_bwd(const BwdParams& p, Dt in, Dt grad, hipStream_t s);
 hipError_t launch_conv1d_fwd(const ConvParams& p, Dt in, Dt out, bool vec, hipStream_t s);

@@ -124,8 +124,23 @@ struct RowRaw {
   Raw4<kInBF16> bc;          // 4 steps of one B or C row (staging role)
 };
 
-template <bool kInBF16, bool kOutBF16, int kMode>
-__device__ __forceinline__ void row_scan(const ScanParams& p, RowLds& s, int64_t b, int64_t d0) {
+// What one workgroup scans: steps t_begin .. t_begin + 32 nck - 1 of its 16
+// channels, from the states h0 (null: a zero start).  h_end / s_sum (when not
+// null) receive the end state and the sum of delta over the range (a chunk's
+// summary for the carry); final_state says whether the end state is also the
+// scan's final state.
+struct RowTask {
+  int64_t t_begin, nck;
+  const float* h0;      // (B, D, N)
+  float* h_end;         // (B, D, N)
+  float* s_sum;         // (B, D)
+  bool final_state;
+};
+
+// kSum: the summary role -- the recurrence alone (no readout, outputs or
+// gate), for the end state of a chunk that starts from zero.
+template <bool kInBF16, bool kOutBF16, int kMode, bool kSum>
+__device__ __forceinline__ void row_scan(const ScanParams& p, RowLds& s, int64_t b, int64_t d0, const RowTask& task) {
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63;
   const int r = lane >> 4, n = lane & 15;
@@ -150,20 +165,22 @@ __device__ __forceinline__ void row_scan(const ScanParams& p, RowLds& s, int64_t
   const void* s_base = s_arr ? p.Ct : p.Bt;
   const int64_t s_row = (b * N + (s_ok ? sn : 0)) * L;
 
-  const int64_t nck = L / kRCT;
+  const int64_t nck = task.nck, tb = task.t_begin;
   auto fetch = [&](int64_t ck, RowRaw<kInBF16>& raw) {
     const int64_t c = ck < nck ? ck : nck - 1;     // clamp: prefetch past the end re-reads the last chunk
-    const int64_t t0 = c * kRCT;
+    const int64_t t0 = tb + c * kRCT;
     raw.u = load2<kInBF16>(p.u, row + t0 + 2 * n);
     raw.d = load2<kInBF16>(p.delta, row + t0 + 2 * n);
-    raw.z = load2<kInBF16>(z_src, row + t0 + 2 * n);
-    raw.bc = load4<kInBF16>(s_base, s_row + t0 + 4 * sg, s_ok);
+    if constexpr (!kSum) raw.z = load2<kInBF16>(z_src, row + t0 + 2 * n);
+    // the summary role reads no C_t (its staging threads stage zeros)
+    raw.bc = load4<kInBF16>(s_base, s_row + t0 + 4 * sg, s_ok && !(kSum && s_arr == 1));
   };
   auto stage = [&](const RowRaw<kInBF16>& raw, int buf) {
     *reinterpret_cast<float4*>(&s.bc[buf][s_arr][sn * kBCRow + 4 * sg]) = widen4<kInBF16>(raw.bc);
   };
 
-  float h = 0.0f;
+  float h = (task.h0 != nullptr && c_ok && n_ok) ? task.h0[(b * D + d) * N + n] : 0.0f;
+  float dsum = 0.0f;                     // this lane's 2 elements of delta per chunk, summed
   RowRaw<kInBF16> raw[2];
   float dv[2][2], uv[2][2], gv[2][2];   // [chunk parity][element]: delta, u, gate of this lane's 2 elements
   float duv[2][2];                       // delta * u (the simplified rule's per-step factor)
@@ -171,8 +188,10 @@ __device__ __forceinline__ void row_scan(const ScanParams& p, RowLds& s, int64_t
   auto prep = [&](const RowRaw<kInBF16>& rr, int par, int j) {
     dv[par][j] = softplus(at2<kInBF16>(rr.d, j) + bias);
     uv[par][j] = at2<kInBF16>(rr.u, j);
-    const float gz = silu(at2<kInBF16>(rr.z, j));
-    gv[par][j] = want_z ? gz : 1.0f;
+    if constexpr (!kSum) {
+      const float gz = silu(at2<kInBF16>(rr.z, j));
+      gv[par][j] = want_z ? gz : 1.0f;
+    }
     if constexpr (kMode == kDeltaB) duv[par][j] = dv[par][j] * uv[par][j];
   };
   // bf16 outputs leave in whole 128-byte lines: a lane packs its 2 outputs of
@@ -207,8 +226,9 @@ __device__ __forceinline__ void row_scan(const ScanParams& p, RowLds& s, int64_t
   auto chunk = [&](auto ptag, int64_t ck) {
     constexpr int P = decltype(ptag)::kValue;
     constexpr int Q = P ^ 1;
-    const int64_t t0 = ck * kRCT;
+    const int64_t t0 = tb + ck * kRCT;
     fetch(ck + 2, raw[P]);          // chunk ck+2 has the parity of ck; raw[P] was consumed by chunk ck-1
+    dsum += dv[P][0] + dv[P][1];
     const float* Bs = &s.bc[P][0][n * kBCRow];
     const float* Cs = &s.bc[P][1][n * kBCRow];
     float4 Bq[3], Cq[3];            // B, C of 4-step groups g, g+1, g+2 (rotating)
@@ -252,7 +272,7 @@ __device__ __forceinline__ void row_scan(const ScanParams& p, RowLds& s, int64_t
       }
       // outputs of the previous chunk (parity Q) in the first half: output j
       // over groups 2j, 2j+1, 8 of its 16 products per group
-      if constexpr (G < 4) {
+      if constexpr (!kSum && G < 4) {
         constexpr int j = G / 2;            // output j: step 2n + j of chunk ck-1
         constexpr int m0 = 8 * (G % 2);     // products of states m0 .. m0+7
         const float s0 = (q[2 * m0 + j] + q[2 * (m0 + 1) + j]) + (q[2 * (m0 + 2) + j] + q[2 * (m0 + 3) + j]);
@@ -260,7 +280,7 @@ __device__ __forceinline__ void row_scan(const ScanParams& p, RowLds& s, int64_t
         if constexpr (G % 2 == 0) o[j] = s0 + s1;
         else o[j] = __builtin_fmaf(dskip, uv[Q][j], o[j] + (s0 + s1)) * gv[Q][j];
       }
-      if constexpr (G == 4) {
+      if constexpr (!kSum && G == 4) {
         if constexpr (kOutBF16) {
           // chunk ck-1 is even for P = 1 (keep its outputs), odd for P = 0 (store the pair)
           if constexpr (P == 1) held = pack_bf16x2(o[0], o[1]);
@@ -277,31 +297,41 @@ __device__ __forceinline__ void row_scan(const ScanParams& p, RowLds& s, int64_t
       if constexpr (G == 6) stage(raw[Q], Q);
       // the next group's state-independent part, then this group's recurrence and products
       if constexpr (G + 1 < kRCT / 4) pre_group(Tag<G + 1>{});
-      const float4& C4 = Cq[G % 3];
-      float pt[4];
-      h = __builtin_fmaf(e[G & 1][0], h, in[G & 1][0]);
-      pt[0] = C4.x * h;
-      h = __builtin_fmaf(e[G & 1][1], h, in[G & 1][1]);
-      pt[1] = C4.y * h;
-      h = __builtin_fmaf(e[G & 1][2], h, in[G & 1][2]);
-      pt[2] = C4.z * h;
-      h = __builtin_fmaf(e[G & 1][3], h, in[G & 1][3]);
-      pt[3] = C4.w * h;
-      *reinterpret_cast<float4*>(prow + 4 * G) = make_float4(pt[0], pt[1], pt[2], pt[3]);
+      if constexpr (kSum) {
+        h = __builtin_fmaf(e[G & 1][0], h, in[G & 1][0]);
+        h = __builtin_fmaf(e[G & 1][1], h, in[G & 1][1]);
+        h = __builtin_fmaf(e[G & 1][2], h, in[G & 1][2]);
+        h = __builtin_fmaf(e[G & 1][3], h, in[G & 1][3]);
+      } else {
+        const float4& C4 = Cq[G % 3];
+        float pt[4];
+        h = __builtin_fmaf(e[G & 1][0], h, in[G & 1][0]);
+        pt[0] = C4.x * h;
+        h = __builtin_fmaf(e[G & 1][1], h, in[G & 1][1]);
+        pt[1] = C4.y * h;
+        h = __builtin_fmaf(e[G & 1][2], h, in[G & 1][2]);
+        pt[2] = C4.z * h;
+        h = __builtin_fmaf(e[G & 1][3], h, in[G & 1][3]);
+        pt[3] = C4.w * h;
+        *reinterpret_cast<float4*>(prow + 4 * G) = make_float4(pt[0], pt[1], pt[2], pt[3]);
+      }
     });
     // all of this chunk's B/C reads and the next chunk's staging are done by
     // every wave; this wave's products are in LDS (in order before the reads below)
     lds_barrier();
+    if constexpr (!kSum) {
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      const float2 v = *reinterpret_cast<const float2*>(pread + m * kPRowR);
-      q[2 * m] = v.x;
-      q[2 * m + 1] = v.y;
+      for (int m = 0; m < 16; ++m) {
+        const float2 v = *reinterpret_cast<const float2*>(pread + m * kPRowR);
+        q[2 * m] = v.x;
+        q[2 * m + 1] = v.y;
+      }
     }
   };
   for (int64_t ck = 0;; ck += 2) {
     chunk(Tag<0>{}, ck);
     if (ck + 1 >= nck) {
+      if constexpr (kSum) break;
       // outputs of the last chunk (parity 0)
       float o0 = 0.0f, o1 = 0.0f;
 #pragma unroll
@@ -309,7 +339,7 @@ __device__ __forceinline__ void row_scan(const ScanParams& p, RowLds& s, int64_t
       o0 = __builtin_fmaf(dskip, uv[0][0], o0) * gv[0][0];
       o1 = __builtin_fmaf(dskip, uv[0][1], o1) * gv[0][1];
       if (c_ok) {   // an even last chunk: no partner, a half line
-        const int64_t at = row + ck * kRCT + 2 * n;
+        const int64_t at = row + tb + ck * kRCT + 2 * n;
         if constexpr (kOutBF16) *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(p.y) + at) = pack_bf16x2(o0, o1);
         else *reinterpret_cast<float2*>(static_cast<float*>(p.y) + at) = make_float2(o0, o1);
       }
@@ -317,20 +347,29 @@ __device__ __forceinline__ void row_scan(const ScanParams& p, RowLds& s, int64_t
     }
     chunk(Tag<1>{}, ck + 1);
     if (ck + 2 >= nck) {
+      if constexpr (kSum) break;
       float o0 = 0.0f, o1 = 0.0f;
 #pragma unroll
       for (int m = 0; m < 16; ++m) { o0 += q[2 * m]; o1 += q[2 * m + 1]; }
       o0 = __builtin_fmaf(dskip, uv[1][0], o0) * gv[1][0];
       o1 = __builtin_fmaf(dskip, uv[1][1], o1) * gv[1][1];
       if constexpr (kOutBF16) {
-        put_pair(ck * kRCT, pack_bf16x2(o0, o1));   // an odd last chunk pairs with the held even one
+        put_pair(tb + ck * kRCT, pack_bf16x2(o0, o1));   // an odd last chunk pairs with the held even one
       } else if (c_ok) {
-        *reinterpret_cast<float2*>(static_cast<float*>(p.y) + row + (ck + 1) * kRCT + 2 * n) = make_float2(o0, o1);
+        *reinterpret_cast<float2*>(static_cast<float*>(p.y) + row + tb + (ck + 1) * kRCT + 2 * n) = make_float2(o0, o1);
       }
       break;
     }
   }
-  if (p.final_state != nullptr && c_ok && n_ok) p.final_state[(b * D + d) * N + n] = h;
+  if (task.h_end != nullptr && c_ok && n_ok) task.h_end[(b * D + d) * N + n] = h;
+  if (task.s_sum != nullptr) {
+    // the channel's sum over the 16 lanes of its row (each lane summed 2 elements per chunk)
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1)
+      dsum += __builtin_bit_cast(float, lane_read(__builtin_bit_cast(uint32_t, dsum), lane ^ off));
+    if (c_ok && n == 0) task.s_sum[b * D + d] = dsum;
+  }
+  if (task.final_state && p.final_state != nullptr && c_ok && n_ok) p.final_state[(b * D + d) * N + n] = h;
 }
 
 // ---------------------------------------------------------------------------
@@ -566,12 +605,38 @@ scan_row_lean_kernel(ScanParams p) {
   else row_scan_lean<kInBF16, kOutBF16, kZohFast>(p, s, b, d0);
 }
 
+// phase 0: the whole sequence, one workgroup per 16-channel tile.  With L in
+// K chunks of p.chunk_len steps (p.n_chunks = K): phase 1 runs chunk 0 in
+// full and chunks 1 .. K-2 as summaries (workgroup index = chunk x tiles +
+// tile), each storing its end state and sum of delta from a zero start; the
+// carry kernel then chains them into start states; phase 2 runs chunks
+// 1 .. K-1 in full from those.  Both phases put (K - 1) workgroups on every
+// tile, so a sequence with one tile per CU runs three or more per CU.
 template <bool kInBF16, bool kOutBF16>
-__global__ __launch_bounds__(256) void scan_row_kernel(ScanParams p) {
+__global__ __launch_bounds__(256) void scan_row_kernel(ScanParams p, int phase) {
   __shared__ RowLds s;
   const int64_t tiles_d = (p.D + 15) / 16;
-  const int64_t b = (int64_t)blockIdx.x / tiles_d;
-  const int64_t d0 = ((int64_t)blockIdx.x - b * tiles_d) * 16;
+  const int64_t bt = p.B * tiles_d;
+  const int64_t tile = (int64_t)blockIdx.x % bt, c = (int64_t)blockIdx.x / bt;
+  const int64_t b = tile / tiles_d;
+  const int64_t d0 = (tile - b * tiles_d) * 16;
+  const int64_t bdn = p.B * p.D * p.N, bd = p.B * p.D;
+  RowTask task{0, p.L / kRCT, nullptr, nullptr, nullptr, true};
+  bool sum_role = false;
+  if (phase == 1) {
+    task.t_begin = c * p.chunk_len;
+    task.nck = p.chunk_len / kRCT;
+    task.h_end = p.h_local + c * bdn;
+    task.s_sum = p.s_sum + c * bd;
+    task.final_state = false;
+    sum_role = c > 0;
+  } else if (phase == 2) {
+    const int64_t ch = c + 1;
+    task.t_begin = ch * p.chunk_len;
+    task.nck = (p.L - task.t_begin < p.chunk_len ? p.L - task.t_begin : p.chunk_len) / kRCT;
+    task.h0 = p.h_start + ch * bdn;
+    task.final_state = ch == p.n_chunks - 1;
+  }
   // the discretisation loop, uniform over the workgroup: the cancellation-free
   // quotient when asked for or when any |A| of the tile is small
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -579,25 +644,33 @@ __global__ __launch_bounds__(256) void scan_row_kernel(ScanParams p) {
   const int n = lane & 15;
   const bool small_a = d < p.D && n < p.N && __builtin_fabsf(p.A[d * p.N + n]) < kFastZohMinAbsA;
   const int any_small = __syncthreads_or(small_a ? 1 : 0);
-  if (p.delta_b) row_scan<kInBF16, kOutBF16, kDeltaB>(p, s, b, d0);
-  else if (p.accurate || any_small) row_scan<kInBF16, kOutBF16, kZohAccurate>(p, s, b, d0);
-  else row_scan<kInBF16, kOutBF16, kZohFast>(p, s, b, d0);
+  if (sum_role) {
+    if (p.delta_b) row_scan<kInBF16, kOutBF16, kDeltaB, true>(p, s, b, d0, task);
+    else if (p.accurate || any_small) row_scan<kInBF16, kOutBF16, kZohAccurate, true>(p, s, b, d0, task);
+    else row_scan<kInBF16, kOutBF16, kZohFast, true>(p, s, b, d0, task);
+  } else {
+    if (p.delta_b) row_scan<kInBF16, kOutBF16, kDeltaB, false>(p, s, b, d0, task);
+    else if (p.accurate || any_small) row_scan<kInBF16, kOutBF16, kZohAccurate, false>(p, s, b, d0, task);
+    else row_scan<kInBF16, kOutBF16, kZohFast, false>(p, s, b, d0, task);
+  }
 }
 
 template <bool kInBF16, bool kOutBF16>
-hipError_t launch_row_t(const ScanParams& p, bool lean, hipStream_t st) {
-  const int64_t grid = p.B * ((p.D + 15) / 16);
+hipError_t launch_row_t(const ScanParams& p, bool lean, int phase, hipStream_t st) {
+  const int64_t tiles = p.B * ((p.D + 15) / 16);
+  const int64_t grid = phase == 0 ? tiles : (p.n_chunks - 1) * tiles;
   if (grid <= 0) return hipSuccess;
   if (lean) hipLaunchKernelGGL((scan_row_lean_kernel<kInBF16, kOutBF16>), dim3((unsigned)grid), dim3(256), 0, st, p);
-  else hipLaunchKernelGGL((scan_row_kernel<kInBF16, kOutBF16>), dim3((unsigned)grid), dim3(256), 0, st, p);
+  else hipLaunchKernelGGL((scan_row_kernel<kInBF16, kOutBF16>), dim3((unsigned)grid), dim3(256), 0, st, p, phase);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_scan_row(const ScanParams& p, Dt in, Dt out, bool lean, hipStream_t s) {
-  if (in == Dt::BF16) return out == Dt::BF16 ? launch_row_t<true, true>(p, lean, s) : launch_row_t<true, false>(p, lean, s);
-  return out == Dt::BF16 ? launch_row_t<false, true>(p, lean, s) : launch_row_t<false, false>(p, lean, s);
+hipError_t launch_scan_row(const ScanParams& p, Dt in, Dt out, bool lean, int phase, hipStream_t s) {
+  if (lean && phase != 0) return hipErrorInvalidValue;   // the lean variant runs whole sequences only
+  if (in == Dt::BF16) return out == Dt::BF16 ? launch_row_t<true, true>(p, lean, phase, s) : launch_row_t<true, false>(p, lean, phase, s);
+  return out == Dt::BF16 ? launch_row_t<false, true>(p, lean, phase, s) : launch_row_t<false, false>(p, lean, phase, s);
 }
 
 }  // namespace mamba

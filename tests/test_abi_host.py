@@ -57,8 +57,10 @@ def test_workspace_size_plan():
     # L % 32 != 0 but L % 8 == 0: the same kernel, its last chunk shifted back
     assert ws(4, 5120, 16, 2040) == 1024 * 8 + 1024 * 16 * 16 * 4
     assert ws(4, 5120, 16, 2044) == 0      # L % 8 != 0: general kernel, no hand-over
-    # the batch-1 long sequence: the row kernel, one pass, no workspace
-    assert ws(1, 4096, 16, 131072) == 0
+    # the batch-1 long sequence (256 tiles): the row kernel over 4 chunks of
+    # 32768 steps, its two passes with h_local and h_start (K, B, D, N) fp32
+    # and the sums of delta (K, B, D) fp32 between them
+    assert ws(1, 4096, 16, 131072) == 2 * 4 * 4096 * 16 * 4 + 4 * 4096 * 4
     assert ws(2, 4096, 16, 65536) == 0      # 512 tiles: the row kernel too
     with _lib.test_knobs(scan_kernel="wave_tile"):
         n = ws(1, 4096, 16, 131072)
@@ -71,9 +73,12 @@ def test_workspace_size_plan():
         assert ws(2, 4096, 16, 65536) == 2 * 3 * 2 * 4096 * 16 * 4 + 3 * 2 * 4096 * 4 + 1024 * 8 + \
             1024 * 16 * 16 * 4
         assert ws(8, 1536, 16, 65536) == 0
-    # 64 tiles: few enough that chunking the wave-tile kernel (17 chunks) beats
-    # the row kernel's 64 workgroups on 256 CUs
-    assert ws(1, 1024, 16, 65536) == 2 * 17 * 1024 * 16 * 4 + 17 * 1024 * 4 + 1024 * 8 + 1024 * 16 * 16 * 4
+    # 64 tiles: the row kernel over 13 chunks (768 / 64 + 1) of 5056 steps
+    # (65536 / 13 rounded up to a multiple of 64), no hand-over area
+    assert ws(1, 1024, 16, 65536) == 2 * 13 * 1024 * 16 * 4 + 13 * 1024 * 4
+    # the same shape on the wave-tile kernel: 17 chunks, a balanced full pass
+    with _lib.test_knobs(scan_kernel="wave_tile"):
+        assert ws(1, 1024, 16, 65536) == 2 * 17 * 1024 * 16 * 4 + 17 * 1024 * 4 + 1024 * 8 + 1024 * 16 * 16 * 4
     # a ragged last chunk (L % 32 == 24) cannot take the row kernel: 5 chunks as above
     assert ws(1, 4096, 16, 131072 - 8) == n
     # the general kernel (L % 8 != 0) plans with 64-channel tiles: 16 chunks
@@ -346,7 +351,7 @@ def test_scan_kernel_choice():
     the fastest kernel in an interleaved timing of all of them on MI355X.)"""
     k = _lib.scan_kernel
     assert k(8, 1536, 16, 2048) == "row"
-    assert k(1, 4096, 16, 131072) == "row"
+    assert k(1, 4096, 16, 131072) == "row"     # in 4 chunks
     assert k(4, 5120, 16, 2048) == "wave_tile"
     assert k(5, 4096, 16, 2048) == "wave_tile"
     assert k(7, 4096, 16, 2048) == "wave_tile"
@@ -354,9 +359,10 @@ def test_scan_kernel_choice():
     assert k(3, 5120, 16, 2048) == "wave_tile"
     assert k(4, 5120, 16, 2040) == "wave_tile"
     assert k(1, 4096, 16, 131072 - 8) == "wave_tile"
-    assert k(1, 1024, 16, 65536) == "wave_tile"
-    assert k(1, 2048, 16, 16384) == "wave_tile"
-    assert k(1, 5120, 16, 8192) == "wave_tile"
+    assert k(1, 1024, 16, 65536) == "row"     # 13 chunks
+    assert k(1, 2048, 16, 16384) == "row"     # 7 chunks (L / 2048 caps 768 / 128 + 1)
+    assert k(1, 5120, 16, 8192) == "row"      # 3 chunks
+    assert k(1, 256, 16, 65536) == "wave_tile"
     assert k(2, 2560, 16, 4096) == "row"
     assert k(8, 5120, 16, 2048) == "row_lean"
     assert k(32, 1536, 16, 2048) == "row_lean"

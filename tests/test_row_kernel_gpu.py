@@ -36,6 +36,20 @@ CASES = [
 
 ROW_KERNELS = ["row", "row_lean"]
 
+# The row kernel over L in chunks (forced chunk counts): chunk 0 in full and
+# the middle chunks as summaries in one pass, the carry, then the other
+# chunks from their carried states; ragged last chunks of 32 steps.
+CHUNK_CASES = [
+    # B, D, N, L, dtype, out, chunks, opts
+    (1, 64, 16, 320, "bf16", "bf16", 3, {}),                      # chunks of 128, 128, 64
+    (2, 70, 16, 640, "bf16", "f32", 4, {}),                       # 192 x 3 + 64, ragged channels
+    (1, 33, 5, 96, "f32", "f32", 2, {}),                          # 64 + 32, N < 16
+    (2, 48, 16, 256, "f32", "f32", 3, {"delta_b": True}),
+    (1, 100, 16, 384, "bf16", "f32", 5, {"accurate": True}),      # 3 chunks of 128
+    (2, 48, 16, 512, "bf16", "f32", 4, {"small_A": True}),
+    (1, 40, 16, 448, "bf16", "bf16", 7, {"no_z": True, "no_dskip": True, "no_bias": True}),
+]
+
 
 @pytest.mark.parametrize("kernel", ROW_KERNELS)
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "B%dD%dN%dL%d_%s_%s_%s" % (
@@ -80,6 +94,44 @@ def test_row_kernel_cases(case, kernel, dev):
     assert e <= (2e-3 if dt == "bf16" else 1e-5)
 
 
+@pytest.mark.parametrize("case", CHUNK_CASES, ids=lambda c: "B%dD%dN%dL%d_%s_%s_k%d_%s" % (
+    c[0], c[1], c[2], c[3], c[4], c[5], c[6], "-".join(sorted(c[7])) or "plain"))
+def test_row_kernel_chunked(case, dev):
+    import torch
+    import selective_state_space_75_amd as m
+    B, D, N, L, dt, odt, chunks, opts = case
+    log("[row chunked] %s" % (case,))
+    x = W.custom_scan_inputs(B, D, N, L, dt, seed=6800 + B * 131 + D * 7 + L + N + chunks)
+    if opts.get("small_A"):
+        A = x["A"].copy()
+        A[:16, :] *= np.float32(1e-5)
+        x["A"] = A
+    t = upload_scan(x, dev)
+    if opts.get("no_z"):
+        t["z"] = None
+    if opts.get("no_dskip"):
+        t["Dskip"] = None
+    if opts.get("no_bias"):
+        t["delta_bias"] = None
+    out_dtype = torch.float32 if odt == "f32" else torch.bfloat16
+    with m.test_knobs(scan_kernel="row", scan_chunks=chunks):
+        assert m.scan_kernel(B, D, N, L) == "row"
+        wsb = m.workspace_size(B, D, N, L)
+        assert wsb > 0
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        y, hN = gpu_scan(t, return_final_state=True, out_dtype=out_dtype, delta_b=opts.get("delta_b", False),
+                         accurate_expm1=opts.get("accurate", False), workspace=ws)
+    torch.cuda.synchronize()
+    yr, hr = oracle_scan(x, use_z=not opts.get("no_z"), use_dskip=not opts.get("no_dskip"),
+                         use_bias=not opts.get("no_bias"),
+                         discretization="delta_b" if opts.get("delta_b") else "zoh")
+    bf16 = dt == "bf16" or odt == "bf16"
+    assert_close(from_dev(y), yr, bf16, "row chunked y")
+    e = rel_l2(from_dev(hN), hr)
+    log("  final state rel_l2=%.3e" % e)
+    assert e <= (2e-3 if dt == "bf16" else 1e-5)
+
+
 @pytest.mark.parametrize("kernel", ROW_KERNELS)
 def test_row_kernel_matches_wave_tile_kernel(kernel, dev):
     """The row kernels compute each state update with the same operations in
@@ -104,17 +156,23 @@ def test_row_kernel_matches_wave_tile_kernel(kernel, dev):
 @pytest.mark.parametrize("name", ["mamba130m_layer", "long_b1"])
 def test_row_kernel_full_workload(name, dev):
     """Every output of a full workload on both row kernels, bf16 and fp32
-    output, against the oracle (run once, in 256-channel blocks)."""
+    output, against the oracle (run once, in 256-channel blocks); the batch-1
+    long sequence also on the row kernel in one pass (its planned form is
+    four chunks)."""
     import torch
     import selective_state_space_75_amd as m
     cfg = W.SCAN_CONFIGS[name]
     x = W.scan_inputs(cfg)
     t = upload_scan(x, dev)
     outs = {}
-    for kernel in ROW_KERNELS:
-        with m.test_knobs(scan_kernel=kernel):
+    variants = [(k, 0) for k in ROW_KERNELS] + ([("row", 1)] if name == "long_b1" else [])
+    for kernel, chunks in variants:
+        with m.test_knobs(scan_kernel=kernel, scan_chunks=chunks):
+            wsb = m.workspace_size(cfg.B, cfg.D, cfg.N, cfg.L)
+            ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
             for odt in (torch.bfloat16, torch.float32):
-                outs[(kernel, odt)] = gpu_scan(t, return_final_state=True, out_dtype=odt)
+                outs[("%s/%d" % (kernel, chunks), odt)] = gpu_scan(t, return_final_state=True, out_dtype=odt,
+                                                                   workspace=ws)
     torch.cuda.synchronize()
     del t
     errs = {key: (BlockErr(), BlockErr()) for key in outs}
@@ -123,7 +181,7 @@ def test_row_kernel_full_workload(name, dev):
             y, hN = outs[key]
             ey.add(from_dev(y[b, d0:d1]), yr)
             eh.add(from_dev(hN[b, d0:d1]), hr)
-    for kernel in ROW_KERNELS:
+    for kernel in sorted({k for k, _ in outs}):
         ey, eh = errs[(kernel, torch.bfloat16)]
         log("  %s %s y bf16: rel_l2=%.3e max_abs/max|y|=%.3e" % (name, kernel, ey.rel_l2, ey.max_abs_frac))
         assert ey.rel_l2 <= BF16_REL_L2 and ey.max_abs_frac <= BF16_MAX_ABS_FRAC
