@@ -4,9 +4,11 @@ The entry point without a workspace takes its scratch memory from the
 library's own per-GPU buffer.  Two calls in a row, the second on a smaller
 input, must each equal mamba_scan_fwd on the same inputs bit for bit (the same
 kernels run on the same values; only where the scratch lives differs), and
-the oracle to the bf16 bar.  The first call takes the chunked path (summary,
-carry, a balanced full pass), the second the balanced split alone, so both
-use the scratch.  A shape whose plan needs more scratch than the buffer holds
+the oracle to the bf16 bar.  On the wave-tile kernel the first call takes the
+chunked path (summary, carry, a balanced full pass), the second the balanced
+split alone; on the planner's kernel both calls take the row kernel's two
+passes over chunks with the carry between them.  All of them use the
+scratch.  A shape whose plan needs more scratch than the buffer holds
 is refused before any launch (a host-side check, tested with the CPU tests).
 """
 import pytest
@@ -21,11 +23,18 @@ NOALLOC_BYTES = 8 << 20
 
 def test_noalloc_matches_workspace_entry_point(dev):
     import selective_state_space_75_amd as m
-    # the wave-tile kernel (the planner would scan the first shape with the
-    # row kernel, which needs no scratch)
+    # the wave-tile kernel forced (the planner scans the first shape with the
+    # row kernel over chunks, tested below)
     for i, (B, D, N, L) in enumerate([(1, 4096, 16, 16384), (2, 10240, 16, 128)]):
         with m.test_knobs(scan_kernel="wave_tile"):
             _call(m, i, B, D, N, L, dev)
+
+
+def test_noalloc_matches_workspace_entry_point_row_chunks(dev):
+    import selective_state_space_75_amd as m
+    for i, (B, D, N, L) in enumerate([(1, 4096, 16, 16384), (1, 2048, 16, 8192)]):
+        assert m.scan_kernel(B, D, N, L) == "row"
+        _call(m, 10 + i, B, D, N, L, dev)
 
 
 def _call(m, i, B, D, N, L, dev):
