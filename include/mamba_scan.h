@@ -103,13 +103,16 @@ size_t mamba_scan_workspace_size(int64_t B, int64_t D, int64_t N, int64_t L);
  * device query; callable without a GPU), or a negative status for an invalid
  * shape:
  *   MAMBA_KERNEL_GENERAL    64 channels per 4-wave workgroup, L staged in
- *                           32-step chunks through LDS (L % 8 != 0 or L < 32);
+ *                           32-step chunks through LDS (L < 32);
  *   MAMBA_KERNEL_WAVE_TILE  16 channels per wave, 16 states per lane-quad,
  *                           optionally chunked along L or balanced over the
  *                           SIMDs with state hand-over (L % 8 == 0, L >= 32);
  *   MAMBA_KERNEL_ROW        16 channels per 4-wave workgroup, one state per
- *                           lane, one pass (L % 32 == 0), chosen when the
- *                           wave tiles would leave SIMDs idle or need chunking;
+ *                           lane, one pass or two over chunks of L with a
+ *                           carry between them; chosen when the wave tiles
+ *                           would leave SIMDs idle or need chunking
+ *                           (L % 32 == 0), and for every L >= 32 that is not
+ *                           a multiple of 8;
  *   MAMBA_KERNEL_ROW_LEAN   the same layout with fewer registers and less LDS
  *                           per workgroup (five workgroups per CU instead of
  *                           three), chosen from nine 16-channel workgroups per
@@ -337,11 +340,12 @@ size_t mamba_ssd_workspace_size(int64_t B, int64_t H, int64_t P, int64_t N, int6
  *                         0: the planner decides.
  *   scan_kernel           which kernel mamba_scan_fwd runs: 0 the planner's
  *                         choice; 1 the general 64-channel kernel (normally
- *                         only for L % 8 != 0 or L < 32); 2 the wave-tile
- *                         kernel with 16 states per lane (L % 8 == 0, L >= 32);
- *                         3 the row kernel with one state per lane
- *                         (L % 32 == 0); 4 its lean variant (L % 32 == 0).  A kernel that cannot take the shape
- *                         gives way to the planner's choice.
+ *                         only for L < 32); 2 the wave-tile kernel with 16
+ *                         states per lane (L % 8 == 0, L >= 32); 3 the row
+ *                         kernel with one state per lane (L >= 32); 4 its
+ *                         lean variant (L % 32 == 0; the row kernel at other
+ *                         L).  A kernel that cannot take the shape gives way
+ *                         to the planner's choice.
  *   scan_no_balance       != 0: no balanced split with state hand-over.
  *   handover_spin         >= 0: bound of a workgroup's wait for the state handed
  *                         over by the previous one, in polls (0: every split

@@ -18,7 +18,7 @@ constexpr int64_t kMaxElems = int64_t(1) << 46;
 constexpr int64_t kV4Step = 32;       // the wave-tile kernel's chunk: L at least this, and a multiple of 8
 constexpr int64_t kV4Tile = 16;       // channels per wave in the wave-tile kernel
 constexpr int64_t kGroupsPlan = 1024; // waves of the balanced split (one per SIMD on MI355X)
-constexpr int64_t kRowStep = 32;      // the row kernel's chunk: L a multiple of this
+constexpr int64_t kRowStep = 32;      // the row kernel's chunk (its fast form: L a multiple of this)
 constexpr int64_t kCUsPlan = 256;     // compute units the plan assumes (MI355X)
 constexpr size_t kHandOverBytes = kV4Tile * 16 * sizeof(float);
 
@@ -81,7 +81,9 @@ double row_cost(int64_t wgs) {
   return us / 190.0;
 }
 
-// Shape-only plan (no device query).  When L is a multiple of 32: the lean
+// Shape-only plan (no device query).  When L is not a multiple of 8 (and at
+// least 32): the row kernel, in chunks when there are few tiles.  When L is a
+// multiple of 32: the lean
 // row kernel from nine 16-channel workgroups per CU on, the row kernel when
 // its cost model beats the wave-tile kernel's (few 16-channel tiles, as in
 // the 130M layer and the batch-1 long sequence); else one pass per channel tile
@@ -93,7 +95,13 @@ Plan make_plan(int64_t B, int64_t D, int64_t N, int64_t L, const mamba_test_knob
   Plan p;
   p.tiles_d = (D + kTile - 1) / kTile;
   p.v4 = (L % 8 == 0) && L >= kV4Step && kn.scan_kernel != 1;
-  const bool row_ok = L % kRowStep == 0 && kn.scan_kernel != 1 && kn.scan_kernel != 2 &&
+  // The row kernel takes any L >= 32 (element loads and a shifted last chunk
+  // when L is not a multiple of 32, about 10% slower); the planner sends it
+  // such an L only where the wave-tile kernel cannot go (L not a multiple of
+  // 8), in place of the general kernel, which is about 3x slower.
+  const bool aligned = L % kRowStep == 0;
+  const bool row_ok = L >= kRowStep && (aligned || !p.v4 || kn.scan_kernel >= 3) && kn.scan_kernel != 1 &&
+                      kn.scan_kernel != 2 &&
                       (kn.scan_chunks == 0 || kn.scan_kernel == 3);
   if (row_ok) {
     const int64_t tiles16 = B * ((D + kV4Tile - 1) / kV4Tile);
@@ -103,7 +111,8 @@ Plan make_plan(int64_t B, int64_t D, int64_t N, int64_t L, const mamba_test_knob
     // from 5 to 8 per CU it was within 2% of the wave-tile kernel's balanced
     // split either way (at 5, the 2.8B layer, 1% slower in the streaming
     // benchmark), and at 4 it lost by 4%.
-    const bool lean = kn.scan_kernel == 4 || (kn.scan_kernel == 0 && per_cu >= 9);
+    // (the lean variant has no ragged form: a forced lean at such an L runs the row kernel)
+    const bool lean = aligned && (kn.scan_kernel == 4 || (kn.scan_kernel == 0 && per_cu >= 9));
     // With 64 to 384 tiles (1.5 per CU at most) the row kernel cuts L into K
     // chunks so that each of its two passes puts K - 1 workgroups on every
     // tile, about three per CU: the first pass runs chunk 0 in full and
@@ -116,14 +125,14 @@ Plan make_plan(int64_t B, int64_t D, int64_t N, int64_t L, const mamba_test_knob
     if (!lean) {
       if (kn.scan_chunks > 0) {
         k = kn.scan_chunks;
-      } else if (tiles16 >= 64 && tiles16 <= 384) {
+      } else if ((tiles16 >= 64 || !aligned) && tiles16 <= 384) {
         k = 768 / tiles16 + 1;
         if (k > L / 2048) k = L / 2048;
         if (k > 16) k = 16;
         if (k < 3) k = 1;
       }
     }
-    bool row = kn.scan_kernel == 3 || lean || (kn.scan_kernel == 0 && k >= 3);
+    bool row = kn.scan_kernel >= 3 || lean || (kn.scan_kernel == 0 && (k >= 3 || !p.v4));
     if (!row) {
       double best = v4_chunk_cost(tiles16, 1);
       const int64_t kmax = L >= 4096 && tiles16 < kGroupsPlan ? (L / 2048 < 64 ? L / 2048 : 64) : 1;

@@ -118,19 +118,47 @@ __device__ __forceinline__ void unroll(F&& f) {
   }
 }
 
+// The same values from element loads (rows that are not 4- or 8-byte aligned:
+// L not a multiple of 32).
+template <bool kBF16>
+__device__ __forceinline__ Raw2<kBF16> load2e(const void* base, int64_t off) {
+  Raw2<kBF16> r;
+  if constexpr (kBF16) {
+    const uint16_t* q = static_cast<const uint16_t*>(base) + off;
+    r.w = (uint32_t)q[0] | ((uint32_t)q[1] << 16);
+  } else {
+    const float* q = static_cast<const float*>(base) + off;
+    r.v = make_float2(q[0], q[1]);
+  }
+  return r;
+}
+template <bool kBF16>
+__device__ __forceinline__ Raw4<kBF16> load4e(const void* base, int64_t off, bool ok) {
+  Raw4<kBF16> r;
+  if constexpr (kBF16) {
+    const uint16_t* q = static_cast<const uint16_t*>(base) + off;
+    r.w = ok ? make_uint2((uint32_t)q[0] | ((uint32_t)q[1] << 16), (uint32_t)q[2] | ((uint32_t)q[3] << 16))
+             : make_uint2(0, 0);
+  } else {
+    const float* q = static_cast<const float*>(base) + off;
+    r.v = ok ? make_float4(q[0], q[1], q[2], q[3]) : make_float4(0, 0, 0, 0);
+  }
+  return r;
+}
+
 template <bool kInBF16>
 struct RowRaw {
   Raw2<kInBF16> u, d, z;     // this lane's 2 elements of its channel
   Raw4<kInBF16> bc;          // 4 steps of one B or C row (staging role)
 };
 
-// What one workgroup scans: steps t_begin .. t_begin + 32 nck - 1 of its 16
-// channels, from the states h0 (null: a zero start).  h_end / s_sum (when not
+// What one workgroup scans: steps t_begin .. t_end - 1 of its 16 channels,
+// from the states h0 (null: a zero start).  h_end / s_sum (when not
 // null) receive the end state and the sum of delta over the range (a chunk's
 // summary for the carry); final_state says whether the end state is also the
 // scan's final state.
 struct RowTask {
-  int64_t t_begin, nck;
+  int64_t t_begin, t_end;
   const float* h0;      // (B, D, N)
   float* h_end;         // (B, D, N)
   float* s_sum;         // (B, D)
@@ -139,7 +167,12 @@ struct RowTask {
 
 // kSum: the summary role -- the recurrence alone (no readout, outputs or
 // gate), for the end state of a chunk that starts from zero.
-template <bool kInBF16, bool kOutBF16, int kMode, bool kSum>
+// kRag: L not a multiple of 32.  Loads and stores go element by element, and
+// the range's last 32-step chunk is shifted back to end at t_end: its steps
+// before the previous chunk's end are scanned again with delta = 0 (Abar = 1
+// and Bbar u = 0 exactly, so the state is unchanged) and their outputs are
+// not stored.
+template <bool kInBF16, bool kOutBF16, int kMode, bool kSum, bool kRag>
 __device__ __forceinline__ void row_scan(const ScanParams& p, RowLds& s, int64_t b, int64_t d0, const RowTask& task) {
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63;
@@ -165,15 +198,29 @@ __device__ __forceinline__ void row_scan(const ScanParams& p, RowLds& s, int64_t
   const void* s_base = s_arr ? p.Ct : p.Bt;
   const int64_t s_row = (b * N + (s_ok ? sn : 0)) * L;
 
-  const int64_t nck = task.nck, tb = task.t_begin;
+  const int64_t tb = task.t_begin, te = task.t_end;
+  const int64_t nck = (te - tb + kRCT - 1) / kRCT;
+  const int64_t rep_end = tb + (nck - 1) * kRCT;   // kRag: the last chunk's steps before this repeat
+  auto cstart = [&](int64_t c) -> int64_t {        // first step of chunk c
+    const int64_t t = tb + c * kRCT;
+    if constexpr (kRag) return c + 1 < nck ? t : te - kRCT;
+    else return t;
+  };
   auto fetch = [&](int64_t ck, RowRaw<kInBF16>& raw) {
-    const int64_t c = ck < nck ? ck : nck - 1;     // clamp: prefetch past the end re-reads the last chunk
-    const int64_t t0 = tb + c * kRCT;
-    raw.u = load2<kInBF16>(p.u, row + t0 + 2 * n);
-    raw.d = load2<kInBF16>(p.delta, row + t0 + 2 * n);
-    if constexpr (!kSum) raw.z = load2<kInBF16>(z_src, row + t0 + 2 * n);
+    const int64_t t0 = cstart(ck < nck ? ck : nck - 1);   // clamp: prefetch past the end re-reads the last chunk
     // the summary role reads no C_t (its staging threads stage zeros)
-    raw.bc = load4<kInBF16>(s_base, s_row + t0 + 4 * sg, s_ok && !(kSum && s_arr == 1));
+    const bool bc_ok = s_ok && !(kSum && s_arr == 1);
+    if constexpr (kRag) {
+      raw.u = load2e<kInBF16>(p.u, row + t0 + 2 * n);
+      raw.d = load2e<kInBF16>(p.delta, row + t0 + 2 * n);
+      if constexpr (!kSum) raw.z = load2e<kInBF16>(z_src, row + t0 + 2 * n);
+      raw.bc = load4e<kInBF16>(s_base, s_row + t0 + 4 * sg, bc_ok);
+    } else {
+      raw.u = load2<kInBF16>(p.u, row + t0 + 2 * n);
+      raw.d = load2<kInBF16>(p.delta, row + t0 + 2 * n);
+      if constexpr (!kSum) raw.z = load2<kInBF16>(z_src, row + t0 + 2 * n);
+      raw.bc = load4<kInBF16>(s_base, s_row + t0 + 4 * sg, bc_ok);
+    }
   };
   auto stage = [&](const RowRaw<kInBF16>& raw, int buf) {
     *reinterpret_cast<float4*>(&s.bc[buf][s_arr][sn * kBCRow + 4 * sg]) = widen4<kInBF16>(raw.bc);
@@ -185,8 +232,11 @@ __device__ __forceinline__ void row_scan(const ScanParams& p, RowLds& s, int64_t
   float dv[2][2], uv[2][2], gv[2][2];   // [chunk parity][element]: delta, u, gate of this lane's 2 elements
   float duv[2][2];                       // delta * u (the simplified rule's per-step factor)
   float q[32];                           // partial readouts of the previous chunk: q[2 * n' + j]
-  auto prep = [&](const RowRaw<kInBF16>& rr, int par, int j) {
+  auto prep = [&](const RowRaw<kInBF16>& rr, int par, int j, int64_t ckx) {   // ckx: rr's chunk
     dv[par][j] = softplus(at2<kInBF16>(rr.d, j) + bias);
+    if constexpr (kRag) {
+      if (ckx >= nck - 1 && cstart(nck - 1) + 2 * n + j < rep_end) dv[par][j] = 0.0f;
+    }
     uv[par][j] = at2<kInBF16>(rr.u, j);
     if constexpr (!kSum) {
       const float gz = silu(at2<kInBF16>(rr.z, j));
@@ -216,8 +266,8 @@ __device__ __forceinline__ void row_scan(const ScanParams& p, RowLds& s, int64_t
   fetch(0, raw[0]);
   fetch(1, raw[1]);
   stage(raw[0], 0);
-  prep(raw[0], 0, 0);
-  prep(raw[0], 0, 1);
+  prep(raw[0], 0, 0, 0);
+  prep(raw[0], 0, 1, 0);
 #pragma unroll
   for (int i = 0; i < 32; ++i) q[i] = 0.0f;
   uv[1][0] = uv[1][1] = gv[1][0] = gv[1][1] = 0.0f;
@@ -280,7 +330,20 @@ __device__ __forceinline__ void row_scan(const ScanParams& p, RowLds& s, int64_t
         if constexpr (G % 2 == 0) o[j] = s0 + s1;
         else o[j] = __builtin_fmaf(dskip, uv[Q][j], o[j] + (s0 + s1)) * gv[Q][j];
       }
-      if constexpr (!kSum && G == 4) {
+      if constexpr (!kSum && kRag && G == 4) {
+        // chunk ck-1 is not the last: element stores at its unshifted place
+        if (c_ok && ck > 0) {
+          const int64_t at = row + t0 - kRCT + 2 * n;
+          if constexpr (kOutBF16) {
+            static_cast<uint16_t*>(p.y)[at] = f32_to_bf16(o[0]);
+            static_cast<uint16_t*>(p.y)[at + 1] = f32_to_bf16(o[1]);
+          } else {
+            static_cast<float*>(p.y)[at] = o[0];
+            static_cast<float*>(p.y)[at + 1] = o[1];
+          }
+        }
+      }
+      if constexpr (!kSum && !kRag && G == 4) {
         if constexpr (kOutBF16) {
           // chunk ck-1 is even for P = 1 (keep its outputs), odd for P = 0 (store the pair)
           if constexpr (P == 1) held = pack_bf16x2(o[0], o[1]);
@@ -292,8 +355,8 @@ __device__ __forceinline__ void row_scan(const ScanParams& p, RowLds& s, int64_t
         }
       }
       // unpack the next chunk (parity Q) in the second half, after its u and gate were used above
-      if constexpr (G == 4) prep(raw[Q], Q, 0);
-      if constexpr (G == 5) prep(raw[Q], Q, 1);
+      if constexpr (G == 4) prep(raw[Q], Q, 0, ck + 1);
+      if constexpr (G == 5) prep(raw[Q], Q, 1, ck + 1);
       if constexpr (G == 6) stage(raw[Q], Q);
       // the next group's state-independent part, then this group's recurrence and products
       if constexpr (G + 1 < kRCT / 4) pre_group(Tag<G + 1>{});
@@ -328,6 +391,18 @@ __device__ __forceinline__ void row_scan(const ScanParams& p, RowLds& s, int64_t
       }
     }
   };
+  // kRag: the last chunk's outputs, element by element, its repeated steps left out
+  auto put_last = [&](float o0, float o1) {
+    const int64_t t = cstart(nck - 1) + 2 * n;
+    if (!c_ok) return;
+    if constexpr (kOutBF16) {
+      if (t >= rep_end) static_cast<uint16_t*>(p.y)[row + t] = f32_to_bf16(o0);
+      if (t + 1 >= rep_end) static_cast<uint16_t*>(p.y)[row + t + 1] = f32_to_bf16(o1);
+    } else {
+      if (t >= rep_end) static_cast<float*>(p.y)[row + t] = o0;
+      if (t + 1 >= rep_end) static_cast<float*>(p.y)[row + t + 1] = o1;
+    }
+  };
   for (int64_t ck = 0;; ck += 2) {
     chunk(Tag<0>{}, ck);
     if (ck + 1 >= nck) {
@@ -338,7 +413,9 @@ __device__ __forceinline__ void row_scan(const ScanParams& p, RowLds& s, int64_t
       for (int m = 0; m < 16; ++m) { o0 += q[2 * m]; o1 += q[2 * m + 1]; }
       o0 = __builtin_fmaf(dskip, uv[0][0], o0) * gv[0][0];
       o1 = __builtin_fmaf(dskip, uv[0][1], o1) * gv[0][1];
-      if (c_ok) {   // an even last chunk: no partner, a half line
+      if constexpr (kRag) {
+        put_last(o0, o1);
+      } else if (c_ok) {   // an even last chunk: no partner, a half line
         const int64_t at = row + tb + ck * kRCT + 2 * n;
         if constexpr (kOutBF16) *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(p.y) + at) = pack_bf16x2(o0, o1);
         else *reinterpret_cast<float2*>(static_cast<float*>(p.y) + at) = make_float2(o0, o1);
@@ -353,7 +430,9 @@ __device__ __forceinline__ void row_scan(const ScanParams& p, RowLds& s, int64_t
       for (int m = 0; m < 16; ++m) { o0 += q[2 * m]; o1 += q[2 * m + 1]; }
       o0 = __builtin_fmaf(dskip, uv[1][0], o0) * gv[1][0];
       o1 = __builtin_fmaf(dskip, uv[1][1], o1) * gv[1][1];
-      if constexpr (kOutBF16) {
+      if constexpr (kRag) {
+        put_last(o0, o1);
+      } else if constexpr (kOutBF16) {
         put_pair(tb + ck * kRCT, pack_bf16x2(o0, o1));   // an odd last chunk pairs with the held even one
       } else if (c_ok) {
         *reinterpret_cast<float2*>(static_cast<float*>(p.y) + row + tb + (ck + 1) * kRCT + 2 * n) = make_float2(o0, o1);
@@ -621,11 +700,11 @@ __global__ __launch_bounds__(256) void scan_row_kernel(ScanParams p, int phase) 
   const int64_t b = tile / tiles_d;
   const int64_t d0 = (tile - b * tiles_d) * 16;
   const int64_t bdn = p.B * p.D * p.N, bd = p.B * p.D;
-  RowTask task{0, p.L / kRCT, nullptr, nullptr, nullptr, true};
+  RowTask task{0, p.L, nullptr, nullptr, nullptr, true};
   bool sum_role = false;
   if (phase == 1) {
     task.t_begin = c * p.chunk_len;
-    task.nck = p.chunk_len / kRCT;
+    task.t_end = task.t_begin + p.chunk_len;
     task.h_end = p.h_local + c * bdn;
     task.s_sum = p.s_sum + c * bd;
     task.final_state = false;
@@ -633,7 +712,7 @@ __global__ __launch_bounds__(256) void scan_row_kernel(ScanParams p, int phase) 
   } else if (phase == 2) {
     const int64_t ch = c + 1;
     task.t_begin = ch * p.chunk_len;
-    task.nck = (p.L - task.t_begin < p.chunk_len ? p.L - task.t_begin : p.chunk_len) / kRCT;
+    task.t_end = p.L - task.t_begin < p.chunk_len ? p.L : task.t_begin + p.chunk_len;
     task.h0 = p.h_start + ch * bdn;
     task.final_state = ch == p.n_chunks - 1;
   }
@@ -644,14 +723,25 @@ __global__ __launch_bounds__(256) void scan_row_kernel(ScanParams p, int phase) 
   const int n = lane & 15;
   const bool small_a = d < p.D && n < p.N && __builtin_fabsf(p.A[d * p.N + n]) < kFastZohMinAbsA;
   const int any_small = __syncthreads_or(small_a ? 1 : 0);
-  if (sum_role) {
-    if (p.delta_b) row_scan<kInBF16, kOutBF16, kDeltaB, true>(p, s, b, d0, task);
-    else if (p.accurate || any_small) row_scan<kInBF16, kOutBF16, kZohAccurate, true>(p, s, b, d0, task);
-    else row_scan<kInBF16, kOutBF16, kZohFast, true>(p, s, b, d0, task);
+  // L not a multiple of 32: rows start at any element (element loads), and a
+  // range that ends at L has a shifted last chunk
+  const bool rag = p.L % kRCT != 0;
+  if (sum_role && rag) {
+    if (p.delta_b) row_scan<kInBF16, kOutBF16, kDeltaB, true, true>(p, s, b, d0, task);
+    else if (p.accurate || any_small) row_scan<kInBF16, kOutBF16, kZohAccurate, true, true>(p, s, b, d0, task);
+    else row_scan<kInBF16, kOutBF16, kZohFast, true, true>(p, s, b, d0, task);
+  } else if (sum_role) {
+    if (p.delta_b) row_scan<kInBF16, kOutBF16, kDeltaB, true, false>(p, s, b, d0, task);
+    else if (p.accurate || any_small) row_scan<kInBF16, kOutBF16, kZohAccurate, true, false>(p, s, b, d0, task);
+    else row_scan<kInBF16, kOutBF16, kZohFast, true, false>(p, s, b, d0, task);
+  } else if (rag) {
+    if (p.delta_b) row_scan<kInBF16, kOutBF16, kDeltaB, false, true>(p, s, b, d0, task);
+    else if (p.accurate || any_small) row_scan<kInBF16, kOutBF16, kZohAccurate, false, true>(p, s, b, d0, task);
+    else row_scan<kInBF16, kOutBF16, kZohFast, false, true>(p, s, b, d0, task);
   } else {
-    if (p.delta_b) row_scan<kInBF16, kOutBF16, kDeltaB, false>(p, s, b, d0, task);
-    else if (p.accurate || any_small) row_scan<kInBF16, kOutBF16, kZohAccurate, false>(p, s, b, d0, task);
-    else row_scan<kInBF16, kOutBF16, kZohFast, false>(p, s, b, d0, task);
+    if (p.delta_b) row_scan<kInBF16, kOutBF16, kDeltaB, false, false>(p, s, b, d0, task);
+    else if (p.accurate || any_small) row_scan<kInBF16, kOutBF16, kZohAccurate, false, false>(p, s, b, d0, task);
+    else row_scan<kInBF16, kOutBF16, kZohFast, false, false>(p, s, b, d0, task);
   }
 }
 

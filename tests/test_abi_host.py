@@ -56,7 +56,7 @@ def test_workspace_size_plan():
     assert ws(4, 4096, 16, 2048) == 1024 * 8 + 1024 * 16 * 16 * 4
     # L % 32 != 0 but L % 8 == 0: the same kernel, its last chunk shifted back
     assert ws(4, 5120, 16, 2040) == 1024 * 8 + 1024 * 16 * 16 * 4
-    assert ws(4, 5120, 16, 2044) == 0      # L % 8 != 0: general kernel, no hand-over
+    assert ws(4, 5120, 16, 2044) == 0      # L % 8 != 0: the row kernel in one pass, no hand-over
     # the batch-1 long sequence (256 tiles): the row kernel over 4 chunks of
     # 32768 steps, its two passes with h_local and h_start (K, B, D, N) fp32
     # and the sums of delta (K, B, D) fp32 between them
@@ -81,8 +81,12 @@ def test_workspace_size_plan():
         assert ws(1, 1024, 16, 65536) == 2 * 17 * 1024 * 16 * 4 + 17 * 1024 * 4 + 1024 * 8 + 1024 * 16 * 16 * 4
     # a ragged last chunk (L % 32 == 24) cannot take the row kernel: 5 chunks as above
     assert ws(1, 4096, 16, 131072 - 8) == n
-    # the general kernel (L % 8 != 0) plans with 64-channel tiles: 16 chunks
-    assert ws(1, 4096, 16, 131072 - 4) == 2 * 16 * 4096 * 16 * 4 + 16 * 4096 * 4
+    # L % 8 != 0: the row kernel over 4 chunks of 32768 steps as at 131072
+    # (the last one 4 steps short)
+    assert ws(1, 4096, 16, 131072 - 4) == 2 * 4 * 4096 * 16 * 4 + 4 * 4096 * 4
+    # the general kernel plans with 64-channel tiles: 16 chunks
+    with _lib.test_knobs(scan_kernel="general"):
+        assert ws(1, 4096, 16, 131072 - 4) == 2 * 16 * 4096 * 16 * 4 + 16 * 4096 * 4
     assert _lib.lib().mamba_scan_workspace_size(0, 1, 1, 1) == ctypes.c_size_t(-1).value
     assert _lib.lib().mamba_scan_workspace_size(1, 1, 17, 1) == ctypes.c_size_t(-1).value
 
@@ -346,9 +350,11 @@ def test_scan_kernel_choice():
     16-channel workgroups per CU on, the row kernel where 16-channel wave
     tiles would leave SIMDs idle or need chunking (130M layer, batch-1 long
     sequence), the wave-tile kernel's balanced split from four to eight
-    workgroups per CU (the 2.8B layer) and for ragged lengths, chunking of the wave-tile kernel for very few
-    tiles over long L, the general kernel for L % 8 != 0.  (Each choice was
-    the fastest kernel in an interleaved timing of all of them on MI355X.)"""
+    workgroups per CU (the 2.8B layer) and for L % 32 != 0 with L % 8 == 0,
+    chunking of the wave-tile kernel for very few tiles over long L, the row
+    kernel for every L >= 32 that is not a multiple of 8, the general kernel
+    only below 32 steps.  (Each choice was the fastest kernel in an
+    interleaved timing of all of them on MI355X.)"""
     k = _lib.scan_kernel
     assert k(8, 1536, 16, 2048) == "row"
     assert k(1, 4096, 16, 131072) == "row"     # in 4 chunks
@@ -367,16 +373,21 @@ def test_scan_kernel_choice():
     assert k(8, 5120, 16, 2048) == "row_lean"
     assert k(32, 1536, 16, 2048) == "row_lean"
     assert k(9, 4096, 16, 2048) == "row_lean"
-    assert k(2, 100, 16, 100) == "general"
+    assert k(2, 100, 16, 100) == "row"
+    assert k(4, 5120, 16, 2044) == "row"
+    assert k(1, 4096, 16, 131072 - 4) == "row"
+    assert k(1, 16, 16, 33) == "row"
+    assert k(1, 16, 16, 31) == "general"
     assert k(1, 16, 16, 16) == "general"
     with _lib.test_knobs(scan_kernel="wave_tile"):
         assert k(8, 1536, 16, 2048) == "wave_tile"
     with _lib.test_knobs(scan_kernel="row"):
         assert k(4, 5120, 16, 2048) == "row"
-        assert k(4, 5120, 16, 2040) == "wave_tile"    # the row kernels need L % 32 == 0
+        assert k(4, 5120, 16, 2040) == "row"          # forced: any L >= 32
+        assert k(4, 5120, 16, 16) == "general"
     with _lib.test_knobs(scan_kernel="row_lean"):
         assert k(8, 1536, 16, 2048) == "row_lean"
-        assert k(4, 5120, 16, 2040) == "wave_tile"
+        assert k(4, 5120, 16, 2040) == "row"          # the lean variant needs L % 32 == 0
     with _lib.test_knobs(scan_kernel="general"):
         assert k(4, 5120, 16, 2048) == "general"
     assert _lib.lib().mamba_scan_kernel(1, 1, 17, 1) == UNSUP

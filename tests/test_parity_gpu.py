@@ -176,7 +176,7 @@ def test_decode_options(case, dev):
 CASES = [
     # B, D, N, L, dtype, out, chunks, opts
     (1, 1, 1, 1, "f32", "f32", None, {}),
-    (3, 70, 16, 100, "bf16", "bf16", None, {}),          # L % 8 != 0: element path; D ragged
+    (3, 70, 16, 100, "bf16", "bf16", None, {}),          # L % 8 != 0: element loads; D ragged
     (2, 130, 16, 96, "f32", "bf16", None, {}),
     (2, 64, 5, 64, "bf16", "f32", None, {}),
     (1, 200, 16, 257, "f32", "f32", None, {"no_z": True, "no_dskip": True, "no_bias": True}),
@@ -226,12 +226,14 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("kernel", ["planner", "wave_tile"])
+@pytest.mark.parametrize("kernel", ["planner", "wave_tile", "row"])
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "B%dD%dN%dL%d_%s_%s_k%s_%s" % (
     c[0], c[1], c[2], c[3], c[4], c[5], c[6], "-".join(sorted(c[7])) or "plain"))
 def test_ragged_and_options(case, kernel, dev):
     """Each case with the planner's kernel (the row kernel for small shapes
-    with L % 32 == 0) and with the wave-tile kernel forced."""
+    with L % 32 == 0 and for L % 8 != 0), with the wave-tile kernel forced
+    (the general kernel where L % 8 != 0) and with the row kernel forced
+    (the general kernel below 32 steps)."""
     import selective_state_space_75_amd as m
     B, D, N, L, dt, odt, chunks, opts = case
     log("[ragged] %s %s" % (kernel, case))
