@@ -53,6 +53,13 @@ __device__ __forceinline__ float row_bcast(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x150 + k, 0xF, 0xF, true));
 }
 
+// Value of lane n + k of this lane's 16-lane row, 0 past the row's end (DPP
+// row_shl with bound control).
+template <int k>
+__device__ __forceinline__ float row_shl(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x100 + k, 0xF, 0xF, true));
+}
+
 // Value v of lane `src` of the wave (ds_bpermute: the LDS crossbar, no LDS memory).
 __device__ __forceinline__ uint32_t lane_read(uint32_t v, int src) {
   return (uint32_t)__builtin_amdgcn_ds_bpermute(src << 2, (int)v);
@@ -165,8 +172,14 @@ struct RowTask {
   bool final_state;
 };
 
-// kSum: the summary role -- the recurrence alone (no readout, outputs or
-// gate), for the end state of a chunk that starts from zero.
+// kSum: the summary role -- the end state of a range that starts from zero,
+// without readout, outputs or gate.  With the fast ZOH quotient it is not run
+// as a recurrence: over a 32-step chunk with F_t = exp(A * (delta_t + ... +
+// delta_31)) (F_32 = 1), unrolling h_t = Abar_t h_{t-1} + (Abar_t - 1)/A B_t u_t
+// gives h_31 = F_0 h_{-1} + (1/A) sum_t (F_t - F_{t+1}) B_t u_t, since
+// Abar_t F_{t+1} = F_t.  A step then costs 4 VALU + exp instead of 5 + exp;
+// the suffix sums of delta come from a 16-lane scan once per chunk, and
+// F_t - F_{t+1} cancels to the same degree as the quotient fma(Abar, 1/A, -1/A).
 // kRag: L not a multiple of 32.  Loads and stores go element by element, and
 // the range's last 32-step chunk is shifted back to end at t_end: its steps
 // before the previous chunk's end are scanned again with delta = 0 (Abar = 1
@@ -232,6 +245,7 @@ __device__ __forceinline__ void row_scan(const ScanParams& p, RowLds& s, int64_t
   float dv[2][2], uv[2][2], gv[2][2];   // [chunk parity][element]: delta, u, gate of this lane's 2 elements
   float duv[2][2];                       // delta * u (the simplified rule's per-step factor)
   float q[32];                           // partial readouts of the previous chunk: q[2 * n' + j]
+  constexpr bool kW = kSum && kMode == kZohFast;   // the weighted summary (above)
   auto prep = [&](const RowRaw<kInBF16>& rr, int par, int j, int64_t ckx) {   // ckx: rr's chunk
     dv[par][j] = softplus(at2<kInBF16>(rr.d, j) + bias);
     if constexpr (kRag) {
@@ -278,7 +292,19 @@ __device__ __forceinline__ void row_scan(const ScanParams& p, RowLds& s, int64_t
     constexpr int Q = P ^ 1;
     const int64_t t0 = tb + ck * kRCT;
     fetch(ck + 2, raw[P]);          // chunk ck+2 has the parity of ck; raw[P] was consumed by chunk ck-1
-    dsum += dv[P][0] + dv[P][1];
+    const float dpair = dv[P][0] + dv[P][1];
+    dsum += dpair;
+    // kW: sf[j] = sum of delta from this lane's step 2n + j to the chunk's end
+    float sf[2] = {0.0f, 0.0f};
+    if constexpr (kW) {
+      float x = row_shl<1>(dpair);   // exclusive suffix over the row: lanes n+1 .. 15
+      x += row_shl<1>(x);
+      x += row_shl<2>(x);
+      x += row_shl<4>(x);
+      x += row_shl<8>(x);
+      sf[1] = x + dv[P][1];
+      sf[0] = sf[1] + dv[P][0];
+    }
     const float* Bs = &s.bc[P][0][n * kBCRow];
     const float* Cs = &s.bc[P][1][n * kBCRow];
     float4 Bq[3], Cq[3];            // B, C of 4-step groups g, g+1, g+2 (rotating)
@@ -292,6 +318,11 @@ __device__ __forceinline__ void row_scan(const ScanParams& p, RowLds& s, int64_t
       constexpr int t = decltype(tt)::kValue;
       const float4& B4 = Bq[(t / 4) % 3];
       const float bn = (t % 4 == 0) ? B4.x : (t % 4 == 1) ? B4.y : (t % 4 == 2) ? B4.z : B4.w;
+      if constexpr (kW) {             // ee = F_t, ii = B_t u_t
+        ee = hw_exp2(row_bcast<t / 2>(sf[t % 2]) * a2);
+        ii = row_bcast<t / 2>(uv[P][t % 2]) * bn;
+        return;
+      }
       const float x = row_bcast<t / 2>(dv[P][t % 2]) * a2;
       ee = hw_exp2(x);
       if constexpr (kMode == kDeltaB) {
@@ -311,6 +342,8 @@ __device__ __forceinline__ void row_scan(const ScanParams& p, RowLds& s, int64_t
       });
     };
     pre_group(Tag<0>{});
+    const float f0 = e[0][0];       // kW: F_0, the chunk's decay
+    float wacc[2] = {0.0f, 0.0f};   // kW: sum of (F_t - F_{t+1}) B_t u_t, even and odd steps
     unroll<0, kRCT / 4>([&](auto gc) {
       constexpr int G = decltype(gc)::kValue;
       // (no scheduling fence here: the compiler's own interleaving of the
@@ -360,7 +393,13 @@ __device__ __forceinline__ void row_scan(const ScanParams& p, RowLds& s, int64_t
       if constexpr (G == 6) stage(raw[Q], Q);
       // the next group's state-independent part, then this group's recurrence and products
       if constexpr (G + 1 < kRCT / 4) pre_group(Tag<G + 1>{});
-      if constexpr (kSum) {
+      if constexpr (kW) {
+        const float f4 = (G + 1 < kRCT / 4) ? e[(G + 1) & 1][0] : 1.0f;   // F of the next group's first step
+        wacc[0] = __builtin_fmaf(e[G & 1][0] - e[G & 1][1], in[G & 1][0], wacc[0]);
+        wacc[1] = __builtin_fmaf(e[G & 1][1] - e[G & 1][2], in[G & 1][1], wacc[1]);
+        wacc[0] = __builtin_fmaf(e[G & 1][2] - e[G & 1][3], in[G & 1][2], wacc[0]);
+        wacc[1] = __builtin_fmaf(e[G & 1][3] - f4, in[G & 1][3], wacc[1]);
+      } else if constexpr (kSum) {
         h = __builtin_fmaf(e[G & 1][0], h, in[G & 1][0]);
         h = __builtin_fmaf(e[G & 1][1], h, in[G & 1][1]);
         h = __builtin_fmaf(e[G & 1][2], h, in[G & 1][2]);
@@ -379,6 +418,7 @@ __device__ __forceinline__ void row_scan(const ScanParams& p, RowLds& s, int64_t
         *reinterpret_cast<float4*>(prow + 4 * G) = make_float4(pt[0], pt[1], pt[2], pt[3]);
       }
     });
+    if constexpr (kW) h = __builtin_fmaf(f0, h, (wacc[0] + wacc[1]) * ia);
     // all of this chunk's B/C reads and the next chunk's staging are done by
     // every wave; this wave's products are in LDS (in order before the reads below)
     lds_barrier();

@@ -101,6 +101,7 @@ def test_small_abs_A_fast_quotient(dev):
     largest states, which are those of the smallest delta |A|).  Bars: 6e-5
     for y and 1e-4 for the final state."""
     import torch
+    import selective_state_space_75_amd as m
     B, D, N, L = 2, 256, 16, 2048
     x = W.custom_scan_inputs(B, D, N, L, "bf16", seed=8123)
     rng = np.random.default_rng(8124)
@@ -109,14 +110,18 @@ def test_small_abs_A_fast_quotient(dev):
     dt = np.exp(rng.uniform(np.log(1e-3), np.log(3e-3), size=D))
     x["delta_bias"] = np.log(np.expm1(dt)).astype(np.float32)
     t = upload_scan(x, dev)
-    y, hN = gpu_scan(t, return_final_state=True, out_dtype=torch.float32)
-    yb = gpu_scan(t, out_dtype=torch.bfloat16)
-    torch.cuda.synchronize()
     yr, hr = oracle_scan(x)
-    e, eh = rel_l2(from_dev(y), yr), rel_l2(from_dev(hN), hr)
-    log("  small |A|: y fp32 rel_l2=%.3e, final state rel_l2=%.3e" % (e, eh))
-    assert e <= 6e-5 and eh <= 1e-4
-    assert_close(from_dev(yb), yr, True, "small |A| y bf16")
+    # the planner's kernel, and the row kernel over four chunks (the middle
+    # two as weighted summaries on the same fast quotient)
+    for name, knobs in (("planner", {}), ("row, 4 chunks", {"scan_kernel": "row", "scan_chunks": 4})):
+        with m.test_knobs(**knobs):
+            y, hN = gpu_scan(t, return_final_state=True, out_dtype=torch.float32)
+            yb = gpu_scan(t, out_dtype=torch.bfloat16)
+            torch.cuda.synchronize()
+        e, eh = rel_l2(from_dev(y), yr), rel_l2(from_dev(hN), hr)
+        log("  small |A| (%s): y fp32 rel_l2=%.3e, final state rel_l2=%.3e" % (name, e, eh))
+        assert e <= 6e-5 and eh <= 1e-4
+        assert_close(from_dev(yb), yr, True, "small |A| y bf16 (%s)" % name)
 
 
 # ----------------------------------------------------------------------------- step-size limits
@@ -148,11 +153,26 @@ def _perturb_before(x, dt, t0, seed):
     return y
 
 
+# The scan plans the limits run on: the planner's (one pass at these shapes),
+# and the row kernel over four chunks of 64 steps, whose middle chunks are
+# summaries that the carry chains into start states.
+PLANS = [{}, {"scan_kernel": "row", "scan_chunks": 4}]
+PLAN_IDS = ["planner", "row_chunks"]
+
+
+@pytest.mark.parametrize("plan", PLANS, ids=PLAN_IDS)
 @pytest.mark.parametrize("loop", LOOPS, ids=LOOP_IDS)
-def test_large_delta_resets_state(loop, dev):
+def test_large_delta_resets_state(loop, plan, dev):
     """delta_raw + bias >= 40 at t0: the state at t0 is B/(-A) u_t0 (ZOH) or
     delta B u_t0 (simplified rule) up to e^-40, so outputs from t0 on do not
     change when any earlier input changes."""
+    import torch
+    import selective_state_space_75_amd as m
+    with m.test_knobs(**plan):
+        _large_delta_resets_state(loop, dev)
+
+
+def _large_delta_resets_state(loop, dev):
     import torch
     dt, odt, flags = loop
     B, D, N, L, t0 = 2, 96, 16, 256, 127
@@ -190,11 +210,18 @@ def test_large_delta_resets_state(loop, dev):
     assert rel_l2(g1, yr) <= bar and rel_l2(from_dev(h1), hr) <= bar
 
 
+@pytest.mark.parametrize("plan", PLANS, ids=PLAN_IDS)
 @pytest.mark.parametrize("loop", LOOPS, ids=LOOP_IDS)
-def test_small_delta_holds_state(loop, dev):
+def test_small_delta_holds_state(loop, plan, dev):
     """delta_raw + bias <= -40 over [t1, t2): delta ~ 4e-18, so the state is
     held (the final state after t2 equals the one after t1) and, from a zero
     state, y = D u silu(z)."""
+    import selective_state_space_75_amd as m
+    with m.test_knobs(**plan):
+        _small_delta_holds_state(loop, dev)
+
+
+def _small_delta_holds_state(loop, dev):
     import torch
     dt, odt, flags = loop
     B, D, N, L, t1, t2 = 2, 96, 16, 256, 96, 192
