@@ -44,6 +44,7 @@ constexpr int kPWave = 4 * 16 * kPRowR + 32;   // floats per wave of partial rea
 struct alignas(16) RowLds {
   float bc[2][2][16 * kBCRow];    // [buffer][B, C][state * kBCRow + step]
   float part[4 * kPWave];         // [wave][row][state][step] partial readouts
+  float ia[16 * 16];              // [channel][state] 1/A (the fast quotient's scaled state)
 };
 
 // Value of lane k of this lane's 16-lane row (DPP row_newbcast); folded by
@@ -58,6 +59,13 @@ __device__ __forceinline__ float row_bcast(float v) {
 template <int k>
 __device__ __forceinline__ float row_shl(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x100 + k, 0xF, 0xF, true));
+}
+
+// a + b rounded on its own: not contracted with the product that forms b, so
+// that b's DPP broadcast operand keeps a single use and stays folded.
+__device__ __forceinline__ float add_nc(float a, float b) {
+#pragma clang fp contract(off)
+  return a + b;
 }
 
 // Value v of lane `src` of the wave (ds_bpermute: the LDS crossbar, no LDS memory).
@@ -180,6 +188,12 @@ struct RowTask {
 // Abar_t F_{t+1} = F_t.  A step then costs 4 VALU + exp instead of 5 + exp;
 // the suffix sums of delta come from a 16-lane scan once per chunk, and
 // F_t - F_{t+1} cancels to the same degree as the quotient fma(Abar, 1/A, -1/A).
+// The full role on the fast quotient keeps g = A h instead of h: the step
+// g_t = Abar_t (g_{t-1} + B_t u_t) - B_t u_t is 5 VALU + exp instead of 6 + exp,
+// the readout's sum over the row's 16 states weights each product C_t,n g_t,n
+// by 1/A_n (an fma in place of an add, about a quarter of a VALU per update),
+// and the state is scaled back at the end.  Its rounding error per step,
+// 2^-24 max(|g|, |B u|), is that of the fast quotient's coefficient.
 // kRag: L not a multiple of 32.  Loads and stores go element by element, and
 // the range's last 32-step chunk is shifted back to end at t_end: its steps
 // before the previous chunk's end are scanned again with delta = 0 (Abar = 1
@@ -239,7 +253,19 @@ __device__ __forceinline__ void row_scan(const ScanParams& p, RowLds& s, int64_t
     *reinterpret_cast<float4*>(&s.bc[buf][s_arr][sn * kBCRow + 4 * sg]) = widen4<kInBF16>(raw.bc);
   };
 
+  constexpr bool kG = !kSum && kMode == kZohFast;  // the scaled state g = A h (above)
   float h = (task.h0 != nullptr && c_ok && n_ok) ? task.h0[(b * D + d) * N + n] : 0.0f;
+  if constexpr (kG) h *= a;
+  // kG: 1/A of the row's 16 states, staged once in LDS (the barrier before the
+  // first chunk orders it) and read 8 at a time where the readout sums need them
+  const float* ia_row = &s.ia[(4 * w + r) * 16];
+  if constexpr (kG) s.ia[(4 * w + r) * 16 + n] = ia;
+  auto ia8 = [&](int m0, float (&wv)[8]) {
+    const float4 lo = *reinterpret_cast<const float4*>(ia_row + m0);
+    const float4 hi = *reinterpret_cast<const float4*>(ia_row + m0 + 4);
+    wv[0] = lo.x; wv[1] = lo.y; wv[2] = lo.z; wv[3] = lo.w;
+    wv[4] = hi.x; wv[5] = hi.y; wv[6] = hi.z; wv[7] = hi.w;
+  };
   float dsum = 0.0f;                     // this lane's 2 elements of delta per chunk, summed
   RowRaw<kInBF16> raw[2];
   float dv[2][2], uv[2][2], gv[2][2];   // [chunk parity][element]: delta, u, gate of this lane's 2 elements
@@ -323,6 +349,11 @@ __device__ __forceinline__ void row_scan(const ScanParams& p, RowLds& s, int64_t
         ii = row_bcast<t / 2>(uv[P][t % 2]) * bn;
         return;
       }
+      if constexpr (kG) {             // ee = Abar_t, ii = B_t u_t
+        ee = hw_exp2(row_bcast<t / 2>(dv[P][t % 2]) * a2);
+        ii = row_bcast<t / 2>(uv[P][t % 2]) * bn;
+        return;
+      }
       const float x = row_bcast<t / 2>(dv[P][t % 2]) * a2;
       ee = hw_exp2(x);
       if constexpr (kMode == kDeltaB) {
@@ -358,10 +389,20 @@ __device__ __forceinline__ void row_scan(const ScanParams& p, RowLds& s, int64_t
       if constexpr (!kSum && G < 4) {
         constexpr int j = G / 2;            // output j: step 2n + j of chunk ck-1
         constexpr int m0 = 8 * (G % 2);     // products of states m0 .. m0+7
-        const float s0 = (q[2 * m0 + j] + q[2 * (m0 + 1) + j]) + (q[2 * (m0 + 2) + j] + q[2 * (m0 + 3) + j]);
-        const float s1 = (q[2 * (m0 + 4) + j] + q[2 * (m0 + 5) + j]) + (q[2 * (m0 + 6) + j] + q[2 * (m0 + 7) + j]);
-        if constexpr (G % 2 == 0) o[j] = s0 + s1;
-        else o[j] = __builtin_fmaf(dskip, uv[Q][j], o[j] + (s0 + s1)) * gv[Q][j];
+        if constexpr (kG) {   // products of g, each weighted by 1/A of its state
+          float wv[8];
+          ia8(m0, wv);
+          float acc = (G % 2 == 0) ? wv[0] * q[2 * m0 + j] : __builtin_fmaf(wv[0], q[2 * m0 + j], o[j]);
+#pragma unroll
+          for (int i = 1; i < 8; ++i) acc = __builtin_fmaf(wv[i], q[2 * (m0 + i) + j], acc);
+          if constexpr (G % 2 == 0) o[j] = acc;
+          else o[j] = __builtin_fmaf(dskip, uv[Q][j], acc) * gv[Q][j];
+        } else {
+          const float s0 = (q[2 * m0 + j] + q[2 * (m0 + 1) + j]) + (q[2 * (m0 + 2) + j] + q[2 * (m0 + 3) + j]);
+          const float s1 = (q[2 * (m0 + 4) + j] + q[2 * (m0 + 5) + j]) + (q[2 * (m0 + 6) + j] + q[2 * (m0 + 7) + j]);
+          if constexpr (G % 2 == 0) o[j] = s0 + s1;
+          else o[j] = __builtin_fmaf(dskip, uv[Q][j], o[j] + (s0 + s1)) * gv[Q][j];
+        }
       }
       if constexpr (!kSum && kRag && G == 4) {
         // chunk ck-1 is not the last: element stores at its unshifted place
@@ -404,6 +445,18 @@ __device__ __forceinline__ void row_scan(const ScanParams& p, RowLds& s, int64_t
         h = __builtin_fmaf(e[G & 1][1], h, in[G & 1][1]);
         h = __builtin_fmaf(e[G & 1][2], h, in[G & 1][2]);
         h = __builtin_fmaf(e[G & 1][3], h, in[G & 1][3]);
+      } else if constexpr (kG) {
+        const float4& C4 = Cq[G % 3];
+        float pt[4];
+        h = __builtin_fmaf(e[G & 1][0], add_nc(h, in[G & 1][0]), -in[G & 1][0]);
+        pt[0] = C4.x * h;
+        h = __builtin_fmaf(e[G & 1][1], add_nc(h, in[G & 1][1]), -in[G & 1][1]);
+        pt[1] = C4.y * h;
+        h = __builtin_fmaf(e[G & 1][2], add_nc(h, in[G & 1][2]), -in[G & 1][2]);
+        pt[2] = C4.z * h;
+        h = __builtin_fmaf(e[G & 1][3], add_nc(h, in[G & 1][3]), -in[G & 1][3]);
+        pt[3] = C4.w * h;
+        *reinterpret_cast<float4*>(prow + 4 * G) = make_float4(pt[0], pt[1], pt[2], pt[3]);
       } else {
         const float4& C4 = Cq[G % 3];
         float pt[4];
@@ -449,8 +502,13 @@ __device__ __forceinline__ void row_scan(const ScanParams& p, RowLds& s, int64_t
       if constexpr (kSum) break;
       // outputs of the last chunk (parity 0)
       float o0 = 0.0f, o1 = 0.0f;
+      float wv[16];
+      if constexpr (kG) { ia8(0, *reinterpret_cast<float(*)[8]>(&wv[0])); ia8(8, *reinterpret_cast<float(*)[8]>(&wv[8])); }
 #pragma unroll
-      for (int m = 0; m < 16; ++m) { o0 += q[2 * m]; o1 += q[2 * m + 1]; }
+      for (int m = 0; m < 16; ++m) {
+        if constexpr (kG) { o0 = __builtin_fmaf(wv[m], q[2 * m], o0); o1 = __builtin_fmaf(wv[m], q[2 * m + 1], o1); }
+        else { o0 += q[2 * m]; o1 += q[2 * m + 1]; }
+      }
       o0 = __builtin_fmaf(dskip, uv[0][0], o0) * gv[0][0];
       o1 = __builtin_fmaf(dskip, uv[0][1], o1) * gv[0][1];
       if constexpr (kRag) {
@@ -466,8 +524,13 @@ __device__ __forceinline__ void row_scan(const ScanParams& p, RowLds& s, int64_t
     if (ck + 2 >= nck) {
       if constexpr (kSum) break;
       float o0 = 0.0f, o1 = 0.0f;
+      float wv[16];
+      if constexpr (kG) { ia8(0, *reinterpret_cast<float(*)[8]>(&wv[0])); ia8(8, *reinterpret_cast<float(*)[8]>(&wv[8])); }
 #pragma unroll
-      for (int m = 0; m < 16; ++m) { o0 += q[2 * m]; o1 += q[2 * m + 1]; }
+      for (int m = 0; m < 16; ++m) {
+        if constexpr (kG) { o0 = __builtin_fmaf(wv[m], q[2 * m], o0); o1 = __builtin_fmaf(wv[m], q[2 * m + 1], o1); }
+        else { o0 += q[2 * m]; o1 += q[2 * m + 1]; }
+      }
       o0 = __builtin_fmaf(dskip, uv[1][0], o0) * gv[1][0];
       o1 = __builtin_fmaf(dskip, uv[1][1], o1) * gv[1][1];
       if constexpr (kRag) {
@@ -480,6 +543,7 @@ __device__ __forceinline__ void row_scan(const ScanParams& p, RowLds& s, int64_t
       break;
     }
   }
+  if constexpr (kG) h *= ia;     // back from g = A h
   if (task.h_end != nullptr && c_ok && n_ok) task.h_end[(b * D + d) * N + n] = h;
   if (task.s_sum != nullptr) {
     // the channel's sum over the 16 lanes of its row (each lane summed 2 elements per chunk)
@@ -757,7 +821,8 @@ __global__ __launch_bounds__(256) void scan_row_kernel(ScanParams p, int phase) 
     task.final_state = ch == p.n_chunks - 1;
   }
   // the discretisation loop, uniform over the workgroup: the cancellation-free
-  // quotient when asked for or when any |A| of the tile is small
+  // quotient when asked for or when any |A| of the tile is small; fp32 inputs
+  // always ask for it, so their instance has no fast-quotient loop at all
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int64_t d = d0 + 4 * w + (lane >> 4);
   const int n = lane & 15;
@@ -768,19 +833,19 @@ __global__ __launch_bounds__(256) void scan_row_kernel(ScanParams p, int phase) 
   const bool rag = p.L % kRCT != 0;
   if (sum_role && rag) {
     if (p.delta_b) row_scan<kInBF16, kOutBF16, kDeltaB, true, true>(p, s, b, d0, task);
-    else if (p.accurate || any_small) row_scan<kInBF16, kOutBF16, kZohAccurate, true, true>(p, s, b, d0, task);
+    else if (!kInBF16 || p.accurate || any_small) row_scan<kInBF16, kOutBF16, kZohAccurate, true, true>(p, s, b, d0, task);
     else row_scan<kInBF16, kOutBF16, kZohFast, true, true>(p, s, b, d0, task);
   } else if (sum_role) {
     if (p.delta_b) row_scan<kInBF16, kOutBF16, kDeltaB, true, false>(p, s, b, d0, task);
-    else if (p.accurate || any_small) row_scan<kInBF16, kOutBF16, kZohAccurate, true, false>(p, s, b, d0, task);
+    else if (!kInBF16 || p.accurate || any_small) row_scan<kInBF16, kOutBF16, kZohAccurate, true, false>(p, s, b, d0, task);
     else row_scan<kInBF16, kOutBF16, kZohFast, true, false>(p, s, b, d0, task);
   } else if (rag) {
     if (p.delta_b) row_scan<kInBF16, kOutBF16, kDeltaB, false, true>(p, s, b, d0, task);
-    else if (p.accurate || any_small) row_scan<kInBF16, kOutBF16, kZohAccurate, false, true>(p, s, b, d0, task);
+    else if (!kInBF16 || p.accurate || any_small) row_scan<kInBF16, kOutBF16, kZohAccurate, false, true>(p, s, b, d0, task);
     else row_scan<kInBF16, kOutBF16, kZohFast, false, true>(p, s, b, d0, task);
   } else {
     if (p.delta_b) row_scan<kInBF16, kOutBF16, kDeltaB, false, false>(p, s, b, d0, task);
-    else if (p.accurate || any_small) row_scan<kInBF16, kOutBF16, kZohAccurate, false, false>(p, s, b, d0, task);
+    else if (!kInBF16 || p.accurate || any_small) row_scan<kInBF16, kOutBF16, kZohAccurate, false, false>(p, s, b, d0, task);
     else row_scan<kInBF16, kOutBF16, kZohFast, false, false>(p, s, b, d0, task);
   }
 }
