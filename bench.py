@@ -186,6 +186,28 @@ def cpu_baseline_decode(cfg, layers=(0, 47), steps: int = 128):
             "layer_step_ms": round(t_run * 1e3 / (len(layers) * steps), 3)}
 
 
+def settle(step, ms):
+    """Untimed launches of the step for `ms` milliseconds of wall time, before
+    the counted warm-up steps.  Timed right after the GPU sat idle (input
+    generation, a CPU baseline) the first launches on MI355X run up to 1.6x
+    slower for about 20-30 ms while the clocks come up (measured at the
+    2.8B-layer scan: 0.40 ms per launch over the first 25 launches, 0.243 ms
+    from the 50th on); a short timed region would measure that ramp instead of
+    the steady state.  Returns what ran, for the JSON line."""
+    import torch
+    if ms <= 0:
+        return {"ms": 0, "launches": 0}
+    n = 0
+    t_end = time.perf_counter() + ms / 1e3
+    while time.perf_counter() < t_end:
+        step(n)
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()   # keep the queue short, so wall time is GPU time
+    torch.cuda.synchronize()
+    return {"ms": ms, "launches": n}
+
+
 def source_digest(files):
     """sha256 over the sources with comments and whitespace removed, so that
     only a change of the code itself invalidates a recorded measurement."""
@@ -272,6 +294,7 @@ def bench_scan(args, dev):
                    return_final_state=cfg.final_state, y=ys[i % len(sets)], final_state=hs[i % len(sets)],
                    workspace=ws if wsb else None, stream=stream, delta_b=args.delta_b)
 
+    settled = settle(step, args.settle_ms)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -302,8 +325,8 @@ def bench_scan(args, dev):
     p10, p50, p90 = (float(v) for v in np.percentile(per_launch_ms, [10, 50, 90]))
     line = {
         "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32", "io_dtype": cfg.dtype, "data": "synthetic",
+        "warmup": args.warmup, "settle": settled, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "io_dtype": cfg.dtype, "data": "synthetic",
         "config": {"workload": cfg.name, "B": cfg.B, "D": cfg.D, "N": cfg.N, "L": cfg.L,
                    "final_state": cfg.final_state, "global_batch": cfg.B, "seq_len": cfg.L,
                    "discretization": "delta_b" if args.delta_b else "zoh", "parallelism": "none (1 GPU)",
@@ -364,6 +387,7 @@ def bench_decode(args, dev):
                                L_["Dskip"], L_["bias"], y=L_["y"], stream=stream)
         graphs.append(g)
     # capture does not execute; restore the states it did not touch anyway
+    settled = settle(lambda i: graphs[i % pool].replay(), args.settle_ms)
     for i in range(args.warmup):
         graphs[i % pool].replay()
     torch.cuda.synchronize()
@@ -386,8 +410,8 @@ def bench_decode(args, dev):
     line = {
         "metric": "decode state-update HBM GB/s, 48 layers x 128 steps (B=128, D=4096, N=16)",
         "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": args.warmup,
-        "ms_per_step": round(wall * 1e3 / steps, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32", "io_dtype": "bf16", "data": "synthetic",
+        "settle": settled, "ms_per_step": round(wall * 1e3 / steps, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "io_dtype": "bf16", "data": "synthetic",
         "config": {"workload": "decode48", "layers": cfg.layers, "steps": steps, "B": cfg.B, "D": cfg.D,
                    "N": cfg.N, "order": "step-major, 48-layer step replayed as a HIP graph"},
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
@@ -422,6 +446,7 @@ def bench_conv(args, dev):
         m.conv1d_fwd(t["x"], t["w"], t["bias"], return_final_state=True, y=ys[i % len(sets)],
                      final_state=fss[i % len(sets)], stream=stream)
 
+    settled = settle(step, args.settle_ms)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -442,7 +467,7 @@ def bench_conv(args, dev):
     return {
         "metric": "causal conv1d + SiLU HBM GB/s (% of MI355X peak) at Mamba-2.8B layer shape",
         "value": round(nbytes / (ms_step * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "settle": settled, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "io_dtype": cfg.dtype, "data": "synthetic",
         "config": {"workload": cfg.name, "B": cfg.B, "D": cfg.D, "L": cfg.L, "K": cfg.K, "input_sets": len(sets)},
         "elems_per_s": round(cfg.elements / (ms_step * 1e-3), 1),
@@ -478,6 +503,7 @@ def bench_conv_decode(args, dev):
             for L_ in layers:
                 m.conv1d_update(L_["state"], L_["x"][s], L_["w"], L_["bias"], y=L_["y"], stream=stream)
         graphs.append(g)
+    settled = settle(lambda i: graphs[i % pool].replay(), args.settle_ms)
     for i in range(args.warmup):
         graphs[i % pool].replay()
     torch.cuda.synchronize()
@@ -496,7 +522,7 @@ def bench_conv_decode(args, dev):
     return {
         "metric": "conv1d one-token update HBM GB/s, 48 layers x 128 steps (B=128, D=4096, K=4)",
         "value": round(per_ls * cfg.layers * steps / wall / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps,
-        "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / steps, 5), "higher_is_better": True,
+        "warmup": args.warmup, "settle": settled, "ms_per_step": round(wall * 1e3 / steps, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "io_dtype": "bf16", "data": "synthetic",
         "config": {"workload": cfg.name, "layers": cfg.layers, "steps": steps, "B": cfg.B, "D": cfg.D, "K": cfg.K,
                    "order": "step-major, 48-layer step replayed as a HIP graph"},
@@ -537,6 +563,7 @@ def bench_bwd(args, dev):
         m.scan_bwd(t["u"], t["delta_raw"], t["z"], t["Bt"], t["Ct"], t["A"], t["Dskip"], t["delta_bias"], t["dy"],
                    workspace=ws, stream=stream)
 
+    settled = settle(step, args.settle_ms)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -559,7 +586,7 @@ def bench_bwd(args, dev):
     return {
         "metric": "scan backward: algorithmic GB/s and fp32 lane-op rate at Mamba-2.8B layer shape",
         "value": round(nbytes / (wall / steps) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps,
-        "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / steps, 5), "higher_is_better": True,
+        "warmup": args.warmup, "settle": settled, "ms_per_step": round(wall * 1e3 / steps, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "io_dtype": "bf16", "data": "synthetic",
         "config": {"workload": "bwd_2.8b_layer", "B": cfg.B, "D": cfg.D, "N": cfg.N, "L": cfg.L,
                    "grads": "du, ddelta, dz bf16; dB, dC, dA, dD, dbias fp32"},
@@ -609,6 +636,7 @@ def bench_ssd(args, dev):
         m.ssd_fwd(t["x"], t["delta_raw"], t["z"], t["Bt"], t["Ct"], t["A"], t["Dskip"], t["delta_bias"], P=cfg.P,
                   y=ys[i % len(sets)], stream=stream)
 
+    settled = settle(step, args.settle_ms)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -630,7 +658,7 @@ def bench_ssd(args, dev):
     return {
         "metric": "Mamba-2 SSD layer HBM GB/s (% of MI355X peak) at a 2.7B-shaped layer",
         "value": round(nbytes / (ms_step * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "settle": settled, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": cfg.name, "B": cfg.B, "H": cfg.H, "P": cfg.P, "N": cfg.N, "L": cfg.L,
                    "gate": cfg.gate, "input_sets": len(sets)},
@@ -715,6 +743,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="untimed launches for this long before the warm-up steps (clock ramp; 0 = none)")
     ap.add_argument("--workload", default=None,
                     help="one workload only (default: the 2.8B-layer line with the decode, 130M-layer and "
                          "batch-1 long workloads nested)")

@@ -106,13 +106,13 @@ Plan make_plan(int64_t B, int64_t D, int64_t N, int64_t L, const mamba_test_knob
   if (row_ok) {
     const int64_t tiles16 = B * ((D + kV4Tile - 1) / kV4Tile);
     const int64_t per_cu = (tiles16 + kCUsPlan - 1) / kCUsPlan;
-    // The lean row kernel from nine 16-channel workgroups per CU on: timed on
-    // MI355X it beat both other kernels by 5 to 9% at 10, 12 and 20 per CU;
-    // from 5 to 8 per CU it was within 2% of the wave-tile kernel's balanced
-    // split either way (at 5, the 2.8B layer, 1% slower in the streaming
-    // benchmark), and at 4 it lost by 4%.
+    // The lean row kernel from four 16-channel workgroups per CU on (the count
+    // rounded up): timed on MI355X at steady clocks it beat the wave-tile
+    // kernel's balanced split by 2% at 3.75 and 4 per CU, by 7 to 10% from 5
+    // (the 2.8B layer) to 12 per CU, and the row kernel by 6 to 7%; at 3 per
+    // CU (the 130M layer) the row kernel is 3% faster.
     // (the lean variant has no ragged form: a forced lean at such an L runs the row kernel)
-    const bool lean = aligned && (kn.scan_kernel == 4 || (kn.scan_kernel == 0 && per_cu >= 9));
+    const bool lean = aligned && (kn.scan_kernel == 4 || (kn.scan_kernel == 0 && per_cu >= 4));
     // With 64 to 384 tiles (1.5 per CU at most) the row kernel cuts L into K
     // chunks so that each of its two passes puts K - 1 workgroups on every
     // tile, about three per CU: the first pass runs chunk 0 in full and

@@ -694,6 +694,12 @@ __device__ __forceinline__ void row_scan_lean(const ScanParams& p, RowLeanLds& s
           make_float2(second ? b0 : a0, second ? b1 : a1);
   };
 
+  // On the fast quotient the state is kept scaled by A, as in row_scan: g = A h,
+  // g_t = Abar_t (g_{t-1} + B_t u_t) - B_t u_t, and the readout weights each
+  // state's product by 1/A (the row's 16 values, held in registers).
+  constexpr bool kG = kMode == kZohFast;
+  float iam[16];
+  if constexpr (kG) unroll<0, 16>([&](auto mt) { iam[decltype(mt)::kValue] = row_bcast<decltype(mt)::kValue>(ia); });
   float h = 0.0f;
   fetch(0, raw[0]);
   fetch(1, raw[1]);
@@ -727,13 +733,17 @@ __device__ __forceinline__ void row_scan_lean(const ScanParams& p, RowLeanLds& s
           const float x = row_bcast<k>(dv[hf]) * a2;
           const float ee = hw_exp2(x);
           float ii;
-          if constexpr (kMode == kDeltaB) {
-            ii = row_bcast<k>(duv[hf]) * bn;
+          if constexpr (kG) {
+            ii = row_bcast<k>(uv[hf]) * bn;
+            h = __builtin_fmaf(ee, add_nc(h, ii), -ii);
           } else {
-            const float kc = (kMode == kZohFast) ? __builtin_fmaf(ee, ia, -ia) : expm1_from_exp2(x, ee) * ia;
-            ii = kc * (row_bcast<k>(uv[hf]) * bn);
+            if constexpr (kMode == kDeltaB) {
+              ii = row_bcast<k>(duv[hf]) * bn;
+            } else {
+              ii = (expm1_from_exp2(x, ee) * ia) * (row_bcast<k>(uv[hf]) * bn);
+            }
+            h = __builtin_fmaf(ee, h, ii);
           }
-          h = __builtin_fmaf(ee, h, ii);
           pt[i] = comp4(Cq, i) * h;
         });
         *reinterpret_cast<float4*>(prow + 4 * g) = make_float4(pt[0], pt[1], pt[2], pt[3]);
@@ -745,8 +755,19 @@ __device__ __forceinline__ void row_scan_lean(const ScanParams& p, RowLeanLds& s
       float v[16];
 #pragma unroll
       for (int m = 0; m < 16; ++m) v[m] = pcol[m * kLPitch];
-      const float y = (((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]))) +
-                      (((v[8] + v[9]) + (v[10] + v[11])) + ((v[12] + v[13]) + (v[14] + v[15])));
+      float y;
+      if constexpr (kG) {
+        float y0 = iam[0] * v[0], y1 = iam[8] * v[8];
+#pragma unroll
+        for (int m = 1; m < 8; ++m) {
+          y0 = __builtin_fmaf(iam[m], v[m], y0);
+          y1 = __builtin_fmaf(iam[8 + m], v[8 + m], y1);
+        }
+        y = y0 + y1;
+      } else {
+        y = (((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]))) +
+            (((v[8] + v[9]) + (v[10] + v[11])) + ((v[12] + v[13]) + (v[14] + v[15])));
+      }
       oh[hf] = __builtin_fmaf(dskip, uv[hf], y) * gv[hf];
     });
     if constexpr (kOutBF16) {
@@ -768,6 +789,7 @@ __device__ __forceinline__ void row_scan_lean(const ScanParams& p, RowLeanLds& s
     chunk(Tag<1>{}, ck + 1);
     if (ck + 2 >= nck) break;
   }
+  if constexpr (kG) h *= ia;     // back from g = A h
   if (p.final_state != nullptr && c_ok && n_ok) p.final_state[(b * D + d) * N + n] = h;
 }
 
@@ -784,7 +806,7 @@ scan_row_lean_kernel(ScanParams p) {
   const bool small_a = d < p.D && n < p.N && __builtin_fabsf(p.A[d * p.N + n]) < kFastZohMinAbsA;
   const int any_small = __syncthreads_or(small_a ? 1 : 0);
   if (p.delta_b) row_scan_lean<kInBF16, kOutBF16, kDeltaB>(p, s, b, d0);
-  else if (p.accurate || any_small) row_scan_lean<kInBF16, kOutBF16, kZohAccurate>(p, s, b, d0);
+  else if (!kInBF16 || p.accurate || any_small) row_scan_lean<kInBF16, kOutBF16, kZohAccurate>(p, s, b, d0);
   else row_scan_lean<kInBF16, kOutBF16, kZohFast>(p, s, b, d0);
 }
 

@@ -51,9 +51,13 @@ def test_workspace_size_plan():
     assert ws(8, 1536, 16, 2048) == 0
     # 2560 tiles of 16 channels, ten per CU: the lean row kernel, no workspace
     assert ws(8, 5120, 16, 2048) == 0
-    # >= 1024 tiles of 16 channels: balanced split over 1024 waves, one
-    # hand-over slot per wave (an 8-byte flag each, then 16 x 16 fp32 states each)
-    assert ws(4, 4096, 16, 2048) == 1024 * 8 + 1024 * 16 * 16 * 4
+    # four or more tiles of 16 channels per CU: the lean row kernel, no workspace
+    assert ws(4, 4096, 16, 2048) == 0
+    # the wave-tile kernel at >= 1024 tiles of 16 channels: balanced split over
+    # 1024 waves, one hand-over slot per wave (an 8-byte flag each, then 16 x 16
+    # fp32 states each)
+    with _lib.test_knobs(scan_kernel="wave_tile"):
+        assert ws(4, 4096, 16, 2048) == 1024 * 8 + 1024 * 16 * 16 * 4
     # L % 32 != 0 but L % 8 == 0: the same kernel, its last chunk shifted back
     assert ws(4, 5120, 16, 2040) == 1024 * 8 + 1024 * 16 * 16 * 4
     assert ws(4, 5120, 16, 2044) == 0      # L % 8 != 0: the row kernel in one pass, no hand-over
@@ -109,10 +113,11 @@ def test_forced_chunks_knob():
 
 def test_knob_defaults_and_errors():
     import pytest as _pt
-    # the general kernel takes 64-channel tiles; no balance drops the hand-over area
-    with _lib.test_knobs(scan_no_balance=True):
+    # on the wave-tile kernel, no balance drops the hand-over area
+    with _lib.test_knobs(scan_kernel="wave_tile", scan_no_balance=True):
         assert _lib.workspace_size(4, 4096, 16, 2048) == 0
-    assert _lib.workspace_size(4, 4096, 16, 2048) == 1024 * 8 + 1024 * 16 * 16 * 4
+    with _lib.test_knobs(scan_kernel="wave_tile"):
+        assert _lib.workspace_size(4, 4096, 16, 2048) == 1024 * 8 + 1024 * 16 * 16 * 4
     with _pt.raises(_lib.MambaError):
         _lib.set_test_knobs(scan_chunks=-1)
     with _lib.test_knobs(ssd_segments=3):
@@ -154,9 +159,12 @@ def update(**kw):
     (dict(A=None), NULL), (dict(y=None), NULL), (dict(fs=None), NULL),
     (dict(u=P + 2), ALIGN), (dict(z=P + 8), ALIGN), (dict(y=P + 4), ALIGN), (dict(Ct=P + 2), ALIGN),
     (dict(A=P + 2), ALIGN), (dict(fs=P + 1), ALIGN),
-    # the balanced split of the wave-tile kernel needs a workspace (hand-over slots)
-    (dict(B=4, D=4096, L=2048), WS),
-    (dict(B=4, D=4096, L=2048, ws=P, wsb=1024), WS),
+    # the balanced split of the wave-tile kernel needs a workspace (hand-over
+    # slots; L = 2040 keeps the planner on it), and so does the row kernel over
+    # chunks (the carried states of the batch-1 long sequence)
+    (dict(B=4, D=5120, L=2040), WS),
+    (dict(B=4, D=5120, L=2040, ws=P, wsb=1024), WS),
+    (dict(B=1, D=4096, L=131072), WS),
 ])
 def test_scan_rejects_bad_arguments(kw, code):
     assert scan(**kw) == code
@@ -166,7 +174,7 @@ def test_scan_optional_pointers_do_not_trigger_errors_early():
     # z, Dskip, bias may be NULL and final state is ignored when not requested;
     # with everything else valid but the workspace missing, the workspace error
     # is what comes back (so no launch happens).
-    st = scan(z=None, Dskip=None, bias=None, fs=None, rfs=0, B=4, D=4096, L=2048)
+    st = scan(z=None, Dskip=None, bias=None, fs=None, rfs=0, B=4, D=5120, L=2040)
     assert st == WS
 
 
@@ -346,23 +354,24 @@ def scan_noalloc(**kw):
 
 
 def test_scan_kernel_choice():
-    """The planner's kernel per workload: the lean row kernel from nine
-    16-channel workgroups per CU on, the row kernel where 16-channel wave
-    tiles would leave SIMDs idle or need chunking (130M layer, batch-1 long
-    sequence), the wave-tile kernel's balanced split from four to eight
-    workgroups per CU (the 2.8B layer) and for L % 32 != 0 with L % 8 == 0,
-    chunking of the wave-tile kernel for very few tiles over long L, the row
-    kernel for every L >= 32 that is not a multiple of 8, the general kernel
-    only below 32 steps.  (Each choice was the fastest kernel in an
-    interleaved timing of all of them on MI355X.)"""
+    """The planner's kernel per workload: the lean row kernel from four
+    16-channel workgroups per CU on (the 2.8B layer has five) when L % 32 ==
+    0, the row kernel where 16-channel wave tiles would leave SIMDs idle or
+    need chunking (130M layer, batch-1 long sequence), the wave-tile kernel's
+    balanced split for L % 32 != 0 with L % 8 == 0, chunking of the wave-tile
+    kernel for very few tiles over long L, the row kernel for every L >= 32
+    that is not a multiple of 8, the general kernel only below 32 steps.
+    (Each choice was the fastest kernel in an interleaved timing of all of
+    them on MI355X.)"""
     k = _lib.scan_kernel
     assert k(8, 1536, 16, 2048) == "row"
     assert k(1, 4096, 16, 131072) == "row"     # in 4 chunks
-    assert k(4, 5120, 16, 2048) == "wave_tile"
-    assert k(5, 4096, 16, 2048) == "wave_tile"
-    assert k(7, 4096, 16, 2048) == "wave_tile"
-    assert k(4, 4096, 16, 2048) == "wave_tile"
-    assert k(3, 5120, 16, 2048) == "wave_tile"
+    assert k(4, 5120, 16, 2048) == "row_lean"
+    assert k(5, 4096, 16, 2048) == "row_lean"
+    assert k(7, 4096, 16, 2048) == "row_lean"
+    assert k(4, 4096, 16, 2048) == "row_lean"
+    assert k(3, 5120, 16, 2048) == "row_lean"  # 960 tiles: 3.75 per CU, rounded up to 4
+    assert k(3, 4096, 16, 2048) == "row"       # 768 tiles: 3 per CU
     assert k(4, 5120, 16, 2040) == "wave_tile"
     assert k(1, 4096, 16, 131072 - 8) == "wave_tile"
     assert k(1, 1024, 16, 65536) == "row"     # 13 chunks
