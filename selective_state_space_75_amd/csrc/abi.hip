@@ -72,36 +72,38 @@ double v4_chunk_cost(int64_t tiles, int64_t k) {
 // 4-wave workgroup, up to three workgroups per CU) in the units of
 // v4_chunk_cost.  Measured per 2048 steps on MI355X, against 190 us for a
 // wave-tile pass of one tile per SIMD: 68, 110 and 153 us with one, two and
-// three workgroups per CU; from four on about 52 + 40.9 us per workgroup per
-// CU (a fit over 5, 10, 12 and 20 per CU, within 6% of each).
+// three workgroups per CU; from four on about 26.6 + 41.9 us per workgroup
+// per CU (a fit over 5, 7, 8, 10 and 12 per CU at steady clocks, with the
+// state scaled by A, within 1.5% of each).
 double row_cost(int64_t wgs) {
   const int64_t per_cu = (wgs + kCUsPlan - 1) / kCUsPlan;
   static const double kFew[3] = {68.0, 110.0, 153.0};
-  const double us = per_cu <= 3 ? kFew[per_cu - 1] : 52.0 + 40.9 * double(per_cu);
+  const double us = per_cu <= 3 ? kFew[per_cu - 1] : 26.6 + 41.9 * double(per_cu);
   return us / 190.0;
 }
 
-// Shape-only plan (no device query).  When L is not a multiple of 8 (and at
-// least 32): the row kernel, in chunks when there are few tiles.  When L is a
-// multiple of 32: the lean
-// row kernel from nine 16-channel workgroups per CU on, the row kernel when
-// its cost model beats the wave-tile kernel's (few 16-channel tiles, as in
-// the 130M layer and the batch-1 long sequence); else one pass per channel tile
-// while there are enough tiles to occupy the GPU; otherwise (few channels,
-// long L) split L into chunks of at least 2048 steps: for the wave-tile
-// kernel the number of chunks that minimises v4_chunk_cost, for the general
-// kernel about 1024 workgroups.
+// Shape-only plan (no device query).  When L is a multiple of 32: the lean
+// row kernel from four 16-channel workgroups per CU on.  Otherwise, and for
+// any other L >= 32: the row kernel (element loads when L is not a multiple
+// of 32), in chunks when there are few tiles, or when its cost model beats
+// the wave-tile kernel's (few 16-channel tiles, as in the 130M layer and the
+// batch-1 long sequence); else the wave-tile kernel, one pass per channel
+// tile while there are enough tiles to occupy the GPU, otherwise (few
+// channels, long L) split L into chunks of at least 2048 steps, their number
+// minimising v4_chunk_cost.  The general kernel takes L < 32 (and plans about
+// 1024 workgroups when forced on a long L).
 Plan make_plan(int64_t B, int64_t D, int64_t N, int64_t L, const mamba_test_knobs_t& kn) {
   Plan p;
   p.tiles_d = (D + kTile - 1) / kTile;
   p.v4 = (L % 8 == 0) && L >= kV4Step && kn.scan_kernel != 1;
   // The row kernel takes any L >= 32 (element loads and a shifted last chunk
-  // when L is not a multiple of 32, about 10% slower); the planner sends it
-  // such an L only where the wave-tile kernel cannot go (L not a multiple of
-  // 8), in place of the general kernel, which is about 3x slower.
+  // when L is not a multiple of 32).  With the state scaled by A its ragged
+  // form beats the wave-tile kernel's shifted chunk as well (timed at steady
+  // clocks: the 130M layer at L = 2040 153 against 191 us, the batch-1 long
+  // sequence at L = 131064 4.1 against 4.68 ms, the 2.8B layer at L = 2040
+  // within 2%), so the same rules apply to every L >= 32.
   const bool aligned = L % kRowStep == 0;
-  const bool row_ok = L >= kRowStep && (aligned || !p.v4 || kn.scan_kernel >= 3) && kn.scan_kernel != 1 &&
-                      kn.scan_kernel != 2 &&
+  const bool row_ok = L >= kRowStep && kn.scan_kernel != 1 && kn.scan_kernel != 2 &&
                       (kn.scan_chunks == 0 || kn.scan_kernel == 3);
   if (row_ok) {
     const int64_t tiles16 = B * ((D + kV4Tile - 1) / kV4Tile);
@@ -125,7 +127,7 @@ Plan make_plan(int64_t B, int64_t D, int64_t N, int64_t L, const mamba_test_knob
     if (!lean) {
       if (kn.scan_chunks > 0) {
         k = kn.scan_chunks;
-      } else if ((tiles16 >= 64 || !aligned) && tiles16 <= 384) {
+      } else if ((tiles16 >= 64 || !p.v4) && tiles16 <= 384) {   // below 64 tiles only where the wave-tile kernel cannot go
         k = 768 / tiles16 + 1;
         if (k > L / 2048) k = L / 2048;
         if (k > 16) k = 16;

@@ -58,9 +58,12 @@ def test_workspace_size_plan():
     # fp32 states each)
     with _lib.test_knobs(scan_kernel="wave_tile"):
         assert ws(4, 4096, 16, 2048) == 1024 * 8 + 1024 * 16 * 16 * 4
-    # L % 32 != 0 but L % 8 == 0: the same kernel, its last chunk shifted back
-    assert ws(4, 5120, 16, 2040) == 1024 * 8 + 1024 * 16 * 16 * 4
-    assert ws(4, 5120, 16, 2044) == 0      # L % 8 != 0: the row kernel in one pass, no hand-over
+    # L % 32 != 0: the row kernel's ragged form in one pass, no hand-over; on
+    # the wave-tile kernel (L % 8 == 0) the balanced split, its last chunk shifted back
+    assert ws(4, 5120, 16, 2040) == 0
+    assert ws(4, 5120, 16, 2044) == 0
+    with _lib.test_knobs(scan_kernel="wave_tile"):
+        assert ws(4, 5120, 16, 2040) == 1024 * 8 + 1024 * 16 * 16 * 4
     # the batch-1 long sequence (256 tiles): the row kernel over 4 chunks of
     # 32768 steps, its two passes with h_local and h_start (K, B, D, N) fp32
     # and the sums of delta (K, B, D) fp32 between them
@@ -83,11 +86,13 @@ def test_workspace_size_plan():
     # the same shape on the wave-tile kernel: 17 chunks, a balanced full pass
     with _lib.test_knobs(scan_kernel="wave_tile"):
         assert ws(1, 1024, 16, 65536) == 2 * 17 * 1024 * 16 * 4 + 17 * 1024 * 4 + 1024 * 8 + 1024 * 16 * 16 * 4
-    # a ragged last chunk (L % 32 == 24) cannot take the row kernel: 5 chunks as above
-    assert ws(1, 4096, 16, 131072 - 8) == n
-    # L % 8 != 0: the row kernel over 4 chunks of 32768 steps as at 131072
-    # (the last one 4 steps short)
+    # a ragged last chunk (L % 32 == 24 or 28): the row kernel over 4 chunks of
+    # 32768 steps as at 131072 (the last one 8 or 4 steps short); on the
+    # wave-tile kernel 5 chunks as above
+    assert ws(1, 4096, 16, 131072 - 8) == 2 * 4 * 4096 * 16 * 4 + 4 * 4096 * 4
     assert ws(1, 4096, 16, 131072 - 4) == 2 * 4 * 4096 * 16 * 4 + 4 * 4096 * 4
+    with _lib.test_knobs(scan_kernel="wave_tile"):
+        assert ws(1, 4096, 16, 131072 - 8) == n
     # the general kernel plans with 64-channel tiles: 16 chunks
     with _lib.test_knobs(scan_kernel="general"):
         assert ws(1, 4096, 16, 131072 - 4) == 2 * 16 * 4096 * 16 * 4 + 16 * 4096 * 4
@@ -159,12 +164,11 @@ def update(**kw):
     (dict(A=None), NULL), (dict(y=None), NULL), (dict(fs=None), NULL),
     (dict(u=P + 2), ALIGN), (dict(z=P + 8), ALIGN), (dict(y=P + 4), ALIGN), (dict(Ct=P + 2), ALIGN),
     (dict(A=P + 2), ALIGN), (dict(fs=P + 1), ALIGN),
-    # the balanced split of the wave-tile kernel needs a workspace (hand-over
-    # slots; L = 2040 keeps the planner on it), and so does the row kernel over
-    # chunks (the carried states of the batch-1 long sequence)
-    (dict(B=4, D=5120, L=2040), WS),
-    (dict(B=4, D=5120, L=2040, ws=P, wsb=1024), WS),
+    # the row kernel over chunks needs a workspace (the carried states of the
+    # batch-1 long sequence, aligned or ragged)
     (dict(B=1, D=4096, L=131072), WS),
+    (dict(B=1, D=4096, L=131072, ws=P, wsb=1024), WS),
+    (dict(B=1, D=4096, L=131064), WS),
 ])
 def test_scan_rejects_bad_arguments(kw, code):
     assert scan(**kw) == code
@@ -174,7 +178,7 @@ def test_scan_optional_pointers_do_not_trigger_errors_early():
     # z, Dskip, bias may be NULL and final state is ignored when not requested;
     # with everything else valid but the workspace missing, the workspace error
     # is what comes back (so no launch happens).
-    st = scan(z=None, Dskip=None, bias=None, fs=None, rfs=0, B=4, D=5120, L=2040)
+    st = scan(z=None, Dskip=None, bias=None, fs=None, rfs=0, B=1, D=4096, L=131072)
     assert st == WS
 
 
@@ -357,12 +361,11 @@ def test_scan_kernel_choice():
     """The planner's kernel per workload: the lean row kernel from four
     16-channel workgroups per CU on (the 2.8B layer has five) when L % 32 ==
     0, the row kernel where 16-channel wave tiles would leave SIMDs idle or
-    need chunking (130M layer, batch-1 long sequence), the wave-tile kernel's
-    balanced split for L % 32 != 0 with L % 8 == 0, chunking of the wave-tile
-    kernel for very few tiles over long L, the row kernel for every L >= 32
-    that is not a multiple of 8, the general kernel only below 32 steps.
-    (Each choice was the fastest kernel in an interleaved timing of all of
-    them on MI355X.)"""
+    need chunking (130M layer, batch-1 long sequence) and, by its cost model,
+    at L % 32 != 0 (its ragged form), chunking of the wave-tile kernel for
+    very few tiles over long L when L % 8 == 0, the general kernel only below
+    32 steps.  (Each choice was the fastest kernel in an interleaved timing
+    of all of them on MI355X.)"""
     k = _lib.scan_kernel
     assert k(8, 1536, 16, 2048) == "row"
     assert k(1, 4096, 16, 131072) == "row"     # in 4 chunks
@@ -372,8 +375,10 @@ def test_scan_kernel_choice():
     assert k(4, 4096, 16, 2048) == "row_lean"
     assert k(3, 5120, 16, 2048) == "row_lean"  # 960 tiles: 3.75 per CU, rounded up to 4
     assert k(3, 4096, 16, 2048) == "row"       # 768 tiles: 3 per CU
-    assert k(4, 5120, 16, 2040) == "wave_tile"
-    assert k(1, 4096, 16, 131072 - 8) == "wave_tile"
+    assert k(4, 5120, 16, 2040) == "row"       # the lean kernel has no ragged form
+    assert k(8, 1536, 16, 2040) == "row"
+    assert k(1, 4096, 16, 131072 - 8) == "row"   # in 4 chunks
+    assert k(1, 256, 16, 65536 - 8) == "wave_tile"   # 16 tiles: the wave-tile kernel's chunks
     assert k(1, 1024, 16, 65536) == "row"     # 13 chunks
     assert k(1, 2048, 16, 16384) == "row"     # 7 chunks (L / 2048 caps 768 / 128 + 1)
     assert k(1, 5120, 16, 8192) == "row"      # 3 chunks

@@ -83,8 +83,8 @@ def test_long_b1_all_channels(dev):
 def test_layer_fp32_output(name, dev):
     """The full layer with fp32 output: kernel arithmetic against the fp64 oracle."""
     import torch
-    # the 2.8B layer also on the wave-tile kernel (its balanced split), which
-    # the planner keeps for L % 32 != 0
+    # the 2.8B layer also on the wave-tile kernel (its balanced split and
+    # hand-over at full size)
     kernels = ("planner", "wave_tile") if name == "mamba2.8b_layer" else ("planner",)
     errs, _ = _full_compare(name, dev, (torch.float32,), kernels=kernels)
     for kern in kernels:

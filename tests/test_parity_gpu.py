@@ -65,8 +65,8 @@ def test_mamba28b_layer(dev):
 
 def test_mamba28b_layer_wave_tile(dev):
     """The same layer on the wave-tile kernel (balanced split over 1024 waves
-    with state hand-over between them), which the planner keeps for lengths
-    with L % 32 != 0."""
+    with state hand-over between them), which the planner keeps for very few
+    tiles over a long L."""
     import selective_state_space_75_amd as m
     with m.test_knobs(scan_kernel="wave_tile"):
         _run_config("mamba2.8b_layer", dev)
