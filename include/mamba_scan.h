@@ -107,16 +107,19 @@ size_t mamba_scan_workspace_size(int64_t B, int64_t D, int64_t N, int64_t L);
  *   MAMBA_KERNEL_WAVE_TILE  16 channels per wave, 16 states per lane-quad,
  *                           optionally chunked along L or balanced over the
  *                           SIMDs with state hand-over (L % 8 == 0, L >= 32);
+ *                           chosen for very few 16-channel tiles over a long L;
  *   MAMBA_KERNEL_ROW        16 channels per 4-wave workgroup, one state per
  *                           lane, one pass or two over chunks of L with a
  *                           carry between them; chosen when the wave tiles
- *                           would leave SIMDs idle or need chunking
- *                           (L % 32 == 0), and for every L >= 32 that is not
- *                           a multiple of 8;
+ *                           would leave SIMDs idle or need chunking, and,
+ *                           by a cost model, for L % 32 != 0 (element loads
+ *                           and a shifted last chunk);
  *   MAMBA_KERNEL_ROW_LEAN   the same layout with fewer registers and less LDS
  *                           per workgroup (five workgroups per CU instead of
- *                           three), chosen from nine 16-channel workgroups per
- *                           CU on (L % 32 == 0).
+ *                           three), chosen from four 16-channel workgroups
+ *                           per CU on (L % 32 == 0).
+ * The choice depends on the shape only; every kernel computes the same
+ * result to fp32 rounding.
  */
 #define MAMBA_KERNEL_GENERAL 1
 #define MAMBA_KERNEL_WAVE_TILE 2
@@ -330,8 +333,9 @@ size_t mamba_ssd_workspace_size(int64_t B, int64_t H, int64_t P, int64_t N, int6
 
 /*
  * Test and diagnostic knobs.  They change how a call is carried out, never
- * what it computes (every setting gives the same result up to floating-point
- * summation order, and the hand-over settings bit for bit).  Process-wide:
+ * what it computes (every setting gives the same result to fp32 rounding --
+ * summation order, and on the fast ZOH quotient the row kernels' state scaled
+ * by A -- and the hand-over settings bit for bit).  Process-wide:
  * every later call uses them, so a workspace size queried before a change
  * does not fit a launch after it.  Not for production use.
  *
