@@ -22,13 +22,17 @@ from selective_state_space_75_amd import workloads as W
 pytestmark = pytest.mark.gpu
 
 
-def _full_compare(name, dev, out_dtypes, kernels=("planner",)):
+def _full_compare(name, dev, out_dtypes, kernels=("planner",), seq_len=0):
     """Runs the workload once per output dtype (and kernel) and compares every
     output and the final state against the oracle, which runs once in channel
-    blocks.  Keys of the result: the output dtype, or (kernel, dtype)."""
+    blocks.  Keys of the result: the output dtype, or (kernel, dtype).
+    seq_len > 0: the same workload at another sequence length."""
     import torch
     import selective_state_space_75_amd as m
     cfg = W.SCAN_CONFIGS[name]
+    if seq_len:
+        cfg = W.ScanConfig("%s_L%d" % (name, seq_len), cfg.B, cfg.D, cfg.N, seq_len, cfg.dtype, cfg.seed,
+                           cfg.dskip, cfg.final_state)
     log("[%s full] B=%d D=%d N=%d L=%d: drawing inputs" % (name, cfg.B, cfg.D, cfg.N, cfg.L))
     x = W.scan_inputs(cfg)
     t = upload_scan(x, dev)
@@ -93,6 +97,23 @@ def test_layer_fp32_output(name, dev):
             % (name, kern, ey.rel_l2, ey.max_abs_frac, eh.rel_l2))
         assert ey.rel_l2 <= F32_OUT_REL_L2
         assert eh.rel_l2 <= F32_OUT_REL_L2
+
+
+@pytest.mark.parametrize("name", ["mamba2.8b_layer", "mamba130m_layer"])
+def test_layer_ragged_length_fp32_output(name, dev):
+    """The full layer at L = 2040 (L % 32 != 0) on the planner's kernel, the
+    row kernel's ragged form (element loads, a shifted last chunk), with fp32
+    output: every output and the final state against the oracle."""
+    import torch
+    import selective_state_space_75_amd as m
+    cfg = W.SCAN_CONFIGS[name]
+    assert m.scan_kernel(cfg.B, cfg.D, cfg.N, 2040) == "row"
+    errs, _ = _full_compare(name, dev, (torch.float32,), seq_len=2040)
+    ey, eh = errs[torch.float32]
+    log("  %s at L = 2040 y fp32: rel_l2=%.3e max_abs/max|y|=%.3e; final state rel_l2=%.3e"
+        % (name, ey.rel_l2, ey.max_abs_frac, eh.rel_l2))
+    assert ey.rel_l2 <= F32_OUT_REL_L2
+    assert eh.rel_l2 <= F32_OUT_REL_L2
 
 
 # ----------------------------------------------------------------------------- small |A| on the fast quotient
