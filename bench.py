@@ -72,6 +72,9 @@ DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "state_update_decode48_traf
 CONV_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "conv1d_2.8b_layer_traffic.txt")
 CONV_SOURCES = ["selective_state_space_75_amd/csrc/conv1d.hip", "selective_state_space_75_amd/csrc/kernels.hpp",
                 "selective_state_space_75_amd/csrc/device_math.hpp", "selective_state_space_75_amd/csrc/abi.hip"]
+BWD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_bwd_2.8b_layer_traffic.txt")
+BWD_SOURCES = ["selective_state_space_75_amd/csrc/scan_bwd.hip", "selective_state_space_75_amd/csrc/kernels.hpp",
+               "selective_state_space_75_amd/csrc/device_math.hpp", "selective_state_space_75_amd/csrc/abi.hip"]
 DECODE_SOURCES = ["selective_state_space_75_amd/csrc/state_update.hip", "selective_state_space_75_amd/csrc/kernels.hpp",
                   "selective_state_space_75_amd/csrc/device_math.hpp", "selective_state_space_75_amd/csrc/abi.hip"]
 
@@ -583,6 +586,7 @@ def bench_bwd(args, dev):
     nbytes = e * 2 * 4 + bc * 2 * 2 + e * 2 * 3 + bc * 4 * 2 + cfg.D * (cfg.N + 3) * 4 * 2
     ops = cfg.updates * OPS_PER_UPDATE_BWD
     ach = ops / (call_ms * 1e-3) / 1e12
+    traffic, traffic_note = recorded_traffic(BWD_TRAFFIC_FILE, BWD_SOURCES)
     return {
         "metric": "scan backward: algorithmic GB/s and fp32 lane-op rate at Mamba-2.8B layer shape",
         "value": round(nbytes / (wall / steps) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps,
@@ -592,7 +596,8 @@ def bench_bwd(args, dev):
                    "grads": "du, ddelta, dz bf16; dB, dC, dA, dD, dbias fp32"},
         "call_ms_mean": round(call_ms, 5), "algorithmic_bytes": nbytes,
         "roofline": {"bound": "alu", "achieved": round(ach, 3), "peak": round(VALU_PEAK_TOPS, 2), "unit": "TOP/s",
-                     "frac": round(ach / VALU_PEAK_TOPS, 4), "traffic": None, "ops_per_update": OPS_PER_UPDATE_BWD,
+                     "frac": round(ach / VALU_PEAK_TOPS, 4), "traffic": traffic, "traffic_note": traffic_note,
+                     "ops_per_update": OPS_PER_UPDATE_BWD,
                      "launch_time": "whole call: segment summary, carry, segment recompute and two reduce kernels"},
     }
 

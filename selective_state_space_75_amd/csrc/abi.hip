@@ -271,7 +271,7 @@ struct BwdPlan {
 // layer: 8 segments of 256 steps rather than 6 of 320 and one of 128).
 BwdPlan make_bwd_plan(int64_t B, int64_t D, int64_t L) {
   BwdPlan q;
-  constexpr int64_t kC = mamba::kBwdChunk;
+  constexpr int64_t kC = mamba::kBwdBlock;
   q.tiles_d = (D + 15) / 16;
   q.groups = (q.tiles_d + mamba::kBwdGroup - 1) / mamba::kBwdGroup;
   q.nck = (L + kC - 1) / kC;

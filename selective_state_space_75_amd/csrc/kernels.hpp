@@ -90,6 +90,9 @@ struct ConvParams {
 // kBwdChunk); each segment is cut into chunks of kBwdChunk steps, the unit
 // that is recomputed on chip.
 constexpr int kBwdChunk = 8;
+// Steps staged at a time (four chunks); the summary pass stores one state per
+// channel at the start of each such block.
+constexpr int kBwdBlock = 4 * kBwdChunk;
 // 16-channel tiles per workgroup of the backward segment pass; the workgroup
 // sums its tiles' dB_t / dC_t contributions before storing one partial.
 constexpr int kBwdGroup = 4;
@@ -99,13 +102,13 @@ struct BwdParams {
   const float *A, *Dskip, *bias;
   void *du, *ddelta, *dz;                       // grad dtype, (B, D, L)
   float *dBt, *dCt, *dA, *dDskip, *dbias;       // fp32 results
-  float *ckpt_h;                                // (B, D, nck, 16) chunk-start states from a zero segment start
-  float *ckpt_cd;                               // (B, D, nck) sum of delta from the segment start to the chunk
+  float *ckpt_h;                                // (B, nck, D, 16) block-start states from a zero segment start
+  float *ckpt_cd;                               // (B, nck, D) sum of delta from the segment start to the block
   float *seg_P, *seg_h, *seg_H;                 // (B, S, D, 16) segment summaries
   float *h_in, *g_in;                           // (B, S, D, 16) state entering / adjoint leaving each segment
   float *part_dB, *part_dC;                     // (B, groups, 16, L) sums over a workgroup's channels
   float *part_dA, *part_dD, *part_dbias;        // (B, S, D, 16), (B, S, D), (B, S, D) per-segment sums
-  int64_t B, D, N, L, tiles_d, nck, S, seg_len;
+  int64_t B, D, N, L, tiles_d, nck, S, seg_len;   // nck: kBwdBlock-step blocks over L
   int64_t groups;                               // ceil(tiles_d / kBwdGroup)
   int delta_b;
   int accurate; // cancellation-free (Abar - 1)/A for bf16 inputs too

@@ -11,15 +11,17 @@
 // L is cut into segments (2.8B layer: 8 of 256 steps), each segment into
 // 8-step chunks, and five launches run:
 //   summary:  each segment's recurrence from a zero start; stores the state
-//             and the running sum of delta at every chunk start, and per
-//             segment the end state, the product of Abar and the adjoint term
-//             it passes to the previous segment;
+//             and the running sum of delta at the start of every 32-step
+//             block, and per segment the end state, the product of Abar and
+//             the adjoint term it passes to the previous segment;
 //   carry:    one thread per (batch row, channel, state) chains the segments:
 //             the state entering each segment and the adjoint leaving it;
-//   segment:  walks the segment's chunks from the last: rebuilds the chunk's
-//             start state (stored state + decayed entering state), reruns its
-//             8 steps keeping h_t in registers, then walks them in reverse
-//             with the state adjoint g_t = dyc_t C_t + Abar_(t+1) g_(t+1):
+//   segment:  walks the segment's blocks from the last: rebuilds the
+//             block's start state (stored state + decayed entering state),
+//             runs the recurrence over its first three chunks for the chunk
+//             starts, then per chunk from the last reruns its 8 steps keeping
+//             h_t in registers and walks them in reverse with the state
+//             adjoint g_t = dyc_t C_t + Abar_(t+1) g_(t+1):
 //             dyc  = dy * silu(z)            dz = dy * yc * s (1 + z (1 - s))
 //             dAbar = g h_(t-1)              dcoef = g B u
 //             du   = dyc D + sum_n g coef B
@@ -55,7 +57,7 @@ namespace mamba {
 namespace {
 
 constexpr int kT = kBwdChunk;      // steps recomputed at a time
-constexpr int kBlk = 4 * kT;       // steps staged at a time
+constexpr int kBlk = kBwdBlock;     // steps staged at a time (four chunks)
 
 // Sum over the four lanes of a quad (DPP quad permutations).
 __device__ __forceinline__ float quad_sum4(float v) {
@@ -230,7 +232,8 @@ struct Wave {
   }
 
   __device__ int64_t nblocks() const { return (t_end - t_begin + kBlk - 1) / kBlk; }
-  __device__ int64_t ckpt_index(int64_t t) const { return (b * p.D + d) * p.nck + t / kT; }
+  // block-major: a wave's 16 channels of one block are 1 KB of contiguous states
+  __device__ int64_t ckpt_index(int64_t t) const { return (b * p.nck + t / kBlk) * p.D + d; }
 
   // global loads of the block at t0 (z / dy / C_t only when `adjoint`)
   __device__ void fetch(int64_t t0, Raw& x, bool adjoint) const {
@@ -276,7 +279,7 @@ struct Wave {
 };
 
 // Segment pass 1: per segment, the recurrence from a zero start.  Stores
-// the chunk-start states and the running sum of delta at every chunk start,
+// the state and the running sum of delta at every block start,
 // and per segment the end state h, the product P of Abar over the segment,
 // and H = sum_t (prod_(r <= t) Abar_r) dyc_t C_t, which carry the state into
 // the next segment and the adjoint into the previous one.
@@ -294,16 +297,17 @@ __device__ __forceinline__ void summary_body(const BwdParams& p, const Wave<kInB
     const int64_t t0 = w.t_begin + ib * kBlk;
     const bool more = ib + 1 < nb;
     if (more) w.fetch(t0 + kBlk, x, true);
-    float4 ckh[4];
-    float ckc[4];
+    // the block's start state: 64 contiguous bytes per channel
+    if (w.c_ok) {
+      *reinterpret_cast<float4*>(p.ckpt_h + w.ckpt_index(t0) * 16 + 4 * w.g) = make_float4(h[0], h[1], h[2], h[3]);
+      if (w.g == 0) p.ckpt_cd[w.ckpt_index(t0)] = cum;
+    }
     // whole blocks take a copy of the steps with every count known at compile time
     auto steps = [&](auto whole) {
       constexpr bool kWhole = decltype(whole)::value;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int64_t tk = t0 + k * kT;
-        ckh[k] = make_float4(h[0], h[1], h[2], h[3]);
-        ckc[k] = cum;
         if (kWhole || tk < w.t_end) {
           const int len = kWhole ? kT : ((w.t_end - tk) < kT ? (int)(w.t_end - tk) : kT);
 #pragma unroll
@@ -333,17 +337,6 @@ __device__ __forceinline__ void summary_body(const BwdParams& p, const Wave<kInB
     };
     if (t0 + kBlk <= w.t_end) steps(std::true_type{});
     else steps(std::false_type{});
-    // the block's chunk-start states: 4 x 64 contiguous bytes per channel
-    if (w.c_ok) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int64_t tk = t0 + k * kT;
-        if (tk < w.t_end) {
-          *reinterpret_cast<float4*>(p.ckpt_h + w.ckpt_index(tk) * 16 + 4 * w.g) = ckh[k];
-          if (w.g == k) p.ckpt_cd[w.ckpt_index(tk)] = ckc[k];
-        }
-      }
-    }
     if (more) {
       __syncthreads();
       w.stage(x, st, true, sg, accD);
@@ -391,9 +384,10 @@ __global__ __launch_bounds__(256) void bwd_carry_kernel(BwdParams p) {
 }
 
 // Segment pass 2: blocks of the segment from the last, and the chunks of a
-// block from the last: rebuild the chunk's start state from the stored one
-// and the segment's entering state, rerun its steps keeping h_t and
-// (Abar_t - 1) in registers, then walk them in reverse with the adjoint.
+// block from the last: rebuild the block's start state from the stored one
+// and the segment's entering state, run the recurrence forward for the
+// starts of its chunks, then per chunk rerun its steps keeping h_t and
+// (Abar_t - 1) in registers and walk them in reverse with the adjoint.
 template <bool kInBF16, bool kGradBF16, int M>
 __device__ __forceinline__ void segment_body(const BwdParams& p, const Wave<kInBF16, kGradBF16>& w,
                                              Stage (&sts)[kBwdGroup], int wv, int64_t tg) {
@@ -421,19 +415,14 @@ __device__ __forceinline__ void segment_body(const BwdParams& p, const Wave<kInB
   float dAacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   float accD = 0.0f, accBias = 0.0f;
   float sg_cur[8], sg_next[8];
-  float4 ckh_cur[4], ckh_next[4];
-  float ckc_cur[4], ckc_next[4];
+  float4 ckh_cur, ckh_next;
+  float ckc_cur, ckc_next;
   const int64_t nb = w.nblocks();
-  // the chunk-start states of the block at t0 (4 x 64 contiguous bytes per channel)
-  auto fetch_ckpt = [&](int64_t t0, float4 (&ckh)[4], float (&ckc)[4]) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int64_t tk = t0 + k * kT;
-      const bool ok = w.c_ok && tk < w.t_end;
-      ckh[k] = ok ? *reinterpret_cast<const float4*>(p.ckpt_h + w.ckpt_index(tk) * 16 + 4 * g)
-                  : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-      ckc[k] = ok ? p.ckpt_cd[w.ckpt_index(tk)] : 0.0f;
-    }
+  // the start state of the block at t0 (64 contiguous bytes per channel)
+  auto fetch_ckpt = [&](int64_t t0, float4& ckh, float& ckc) {
+    ckh = w.c_ok ? *reinterpret_cast<const float4*>(p.ckpt_h + w.ckpt_index(t0) * 16 + 4 * g)
+                 : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    ckc = w.c_ok ? p.ckpt_cd[w.ckpt_index(t0)] : 0.0f;
   };
   typename W::Raw x;
   {
@@ -449,28 +438,54 @@ __device__ __forceinline__ void segment_body(const BwdParams& p, const Wave<kInB
     const bool more = ib > 0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) sg_cur[j] = sg_next[j];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      ckh_cur[k] = ckh_next[k];
-      ckc_cur[k] = ckc_next[k];
-    }
+    ckh_cur = ckh_next;
+    ckc_cur = ckc_next;
     if (more) {
       w.fetch(t0 - kBlk, x, true);
       fetch_ckpt(t0 - kBlk, ckh_next, ckc_next);
     }
     const int blen = (w.t_end - t0) < kBlk ? (int)(w.t_end - t0) : kBlk;
+    // chunk-start states: the block's start is the stored state (from a zero
+    // segment start) + P(segment start .. block) h_in; every chunk but the
+    // last is then run forward for the next chunk's start (a chunk that is
+    // followed by another is whole)
+    float hs[4][4];
+    {
+      const float hl[4] = {ckh_cur.x, ckh_cur.y, ckh_cur.z, ckh_cur.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) hs[0][i] = __builtin_fmaf(hw_exp2(w.a2[i] * ckc_cur), hin[i], hl[i]);
+    }
+#pragma unroll
+    for (int k = 1; k < 4; ++k) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) hs[k][i] = hs[k - 1][i];
+      if (k * kT < blen) {
+#pragma unroll
+        for (int tl = 0; tl < kT; ++tl) {
+          const int ts = (k - 1) * kT + tl;
+          const float2 v = *reinterpret_cast<const float2*>(&st.V[ts][c]);
+          const float4 Bq = *reinterpret_cast<const float4*>(&st.B[ts][4 * g]);
+          const float bv[4] = {Bq.x, Bq.y, Bq.z, Bq.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float xx = v.y * w.a2[i];
+            const float e = hw_exp2(xx);
+            const float coef = M == kDeltaB ? v.y
+                               : M == kZohFast ? __builtin_fmaf(e, w.ia[i], -w.ia[i])
+                                               : expm1_from_exp2(xx, e) * w.ia[i];
+            hs[k][i] = __builtin_fmaf(e, hs[k][i], coef * (bv[i] * v.x));
+          }
+        }
+      }
+    }
 #pragma unroll
     for (int k = 3; k >= 0; --k) {
       if (k * kT < blen) {
         const int len = (blen - k * kT) < kT ? blen - k * kT : kT;
-        // chunk start state: stored (zero segment start) + P(start .. chunk) h_in
         // er: Abar - 1 (cancellation-free quotient) or Abar (the other rules)
         float hist[kT + 1][4], er[kT][4];
-        {
-          const float hl[4] = {ckh_cur[k].x, ckh_cur[k].y, ckh_cur[k].z, ckh_cur[k].w};
 #pragma unroll
-          for (int i = 0; i < 4; ++i) hist[0][i] = __builtin_fmaf(hw_exp2(w.a2[i] * ckc_cur[k]), hin[i], hl[i]);
-        }
+        for (int i = 0; i < 4; ++i) hist[0][i] = hs[k][i];
 #pragma unroll
         for (int tl = 0; tl < kT; ++tl) {
           if (tl < len) {

@@ -247,10 +247,10 @@ def test_bwd_workspace_size():
     ws = _lib.scan_bwd_workspace_size
     a = lambda x: (x + 255) // 256 * 256  # noqa: E731
     B, D, N, L = 2, 70, 5, 100
-    # 5 channel tiles in 2 workgroups of up to 4; 8-step chunks -> 13;
-    # segments: 10 (row, tile) pairs want 820 segments, at most
-    # ceil(100 / 64) = 2 -> 50 steps, rounded up to 64 -> 2 segments
-    groups, nck, S = 2, 13, 2
+    # 5 channel tiles in 2 workgroups of up to 4; one stored state per
+    # 32-step block -> 4 blocks; segments: 10 (row, tile) pairs want 820
+    # segments, at most ceil(100 / 64) = 2 -> 50 steps, rounded up to 64 -> 2
+    groups, nck, S = 2, 4, 2
     bd, bsd = B * D, B * D * S
     assert ws(B, D, N, L) == (a(bd * nck * 16 * 4) + a(bd * nck * 4) + 5 * a(bsd * 16 * 4)
                               + 2 * a(B * groups * 16 * L * 4) + a(bsd * 16 * 4) + 2 * a(bsd * 4))
