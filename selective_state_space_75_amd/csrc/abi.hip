@@ -83,7 +83,7 @@ double row_cost(int64_t wgs) {
 }
 
 // Shape-only plan (no device query).  When L is a multiple of 32: the lean
-// row kernel from four 16-channel workgroups per CU on.  Otherwise, and for
+// row kernel from three 16-channel workgroups per CU on.  Otherwise, and for
 // any other L >= 32: the row kernel (element loads when L is not a multiple
 // of 32), in chunks when there are few tiles, or when its cost model beats
 // the wave-tile kernel's (few 16-channel tiles, as in the 130M layer and the
@@ -108,13 +108,14 @@ Plan make_plan(int64_t B, int64_t D, int64_t N, int64_t L, const mamba_test_knob
   if (row_ok) {
     const int64_t tiles16 = B * ((D + kV4Tile - 1) / kV4Tile);
     const int64_t per_cu = (tiles16 + kCUsPlan - 1) / kCUsPlan;
-    // The lean row kernel from four 16-channel workgroups per CU on (the count
-    // rounded up): timed on MI355X at steady clocks it beat the wave-tile
-    // kernel's balanced split by 2% at 3.75 and 4 per CU, by 7 to 10% from 5
-    // (the 2.8B layer) to 12 per CU, and the row kernel by 6 to 7%; at 3 per
-    // CU (the 130M layer) the row kernel is 3% faster.
+    // The lean row kernel from three 16-channel workgroups per CU on (the
+    // count rounded up).  With its issue priority stepped down by progress
+    // (ProgressPrio) it was timed on MI355X at steady clocks against the row
+    // kernel: 135 against 147 us at 3 per CU (the 130M layer), 164 against
+    // 193 us at 4, 199 against 233 us at 5 (the 2.8B layer); at 2 per CU they
+    // tie (111 us), and below that the row kernel's in-wave lookahead wins.
     // (the lean variant has no ragged form: a forced lean at such an L runs the row kernel)
-    const bool lean = aligned && (kn.scan_kernel == 4 || (kn.scan_kernel == 0 && per_cu >= 4));
+    const bool lean = aligned && (kn.scan_kernel == 4 || (kn.scan_kernel == 0 && per_cu >= 3));
     // With 64 to 384 tiles (1.5 per CU at most) the row kernel cuts L into K
     // chunks so that each of its two passes puts K - 1 workgroups on every
     // tile, about three per CU: the first pass runs chunk 0 in full and

@@ -85,6 +85,29 @@ struct ConvParams {
   int64_t rows, D, L, K;  // rows = B * D
 };
 
+// Issue priority from progress (s_setprio).  A SIMD issues to the oldest
+// ready wave first, so co-resident workgroups that run the same long loop
+// finish one after another, and the last one runs its end alone, with its
+// latencies uncovered.  A wave that steps its priority down as it advances
+// through its range (3 before 1/2, 2 before 3/4, 1 before 7/8, then 0)
+// lets the workgroups behind it catch up at each step, so that they stay
+// within an eighth of the range of each other and finish nearly together.
+// It changes only the order of issue, never what is computed.
+struct ProgressPrio {
+  int lvl = 0;
+  __device__ __forceinline__ void begin() { __builtin_amdgcn_s_setprio(3); }
+  // done of total units of the wave's range are behind it (uniform over the wave)
+  __device__ __forceinline__ void at(int64_t done, int64_t total) {
+    const int l = (int)((8 * done >= 4 * total) + (8 * done >= 6 * total) + (8 * done >= 7 * total));
+    if (l != lvl) {
+      lvl = l;
+      if (l == 1) __builtin_amdgcn_s_setprio(2);
+      else if (l == 2) __builtin_amdgcn_s_setprio(1);
+      else __builtin_amdgcn_s_setprio(0);
+    }
+  }
+};
+
 // Backward pass of the scan.
 // Backward pass: L is cut into segments of seg_len steps (a multiple of
 // kBwdChunk); each segment is cut into chunks of kBwdChunk steps, the unit

@@ -783,7 +783,10 @@ __device__ __forceinline__ void row_scan_lean(const ScanParams& p, RowLeanLds& s
     }
     lds_barrier();
   };
+  ProgressPrio prio;    // co-resident workgroups finish together (kernels.hpp)
+  prio.begin();
   for (int64_t ck = 0;; ck += 2) {
+    prio.at(ck, nck);
     chunk(Tag<0>{}, ck);
     if (ck + 1 >= nck) break;
     chunk(Tag<1>{}, ck + 1);
