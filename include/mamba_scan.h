@@ -116,9 +116,10 @@ size_t mamba_scan_workspace_size(int64_t B, int64_t D, int64_t N, int64_t L);
  *                           and a shifted last chunk);
  *   MAMBA_KERNEL_ROW_LEAN   the same layout with fewer registers and less LDS
  *                           per workgroup (five workgroups per CU instead of
- *                           three) and an issue priority stepped down as
- *                           each workgroup advances, chosen from three
- *                           16-channel workgroups per CU on (L % 32 == 0).
+ *                           three), chosen from four 16-channel workgroups
+ *                           per CU on (L % 32 == 0).
+ * The row kernels step each workgroup's issue priority down as it advances
+ * through L, so that the workgroups sharing a CU finish together.
  * The choice depends on the shape only; every kernel computes the same
  * result to fp32 rounding.
  */

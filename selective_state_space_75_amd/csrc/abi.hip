@@ -71,19 +71,21 @@ double v4_chunk_cost(int64_t tiles, int64_t k) {
 // Relative time of the row kernel (one state per lane, a 16-channel tile per
 // 4-wave workgroup, up to three workgroups per CU) in the units of
 // v4_chunk_cost.  Measured per 2048 steps on MI355X, against 190 us for a
-// wave-tile pass of one tile per SIMD: 68, 110 and 153 us with one, two and
-// three workgroups per CU; from four on about 26.6 + 41.9 us per workgroup
-// per CU (a fit over 5, 7, 8, 10 and 12 per CU at steady clocks, with the
-// state scaled by A, within 1.5% of each).
+// wave-tile pass of one tile per SIMD: 68, 103 and 133 us with one, two and
+// three workgroups per CU (the last two with the issue priority stepped down
+// by progress); from four on about 26.6 + 41.9 us per workgroup per CU (a
+// fit over 5, 7, 8, 10 and 12 per CU at steady clocks, with the state scaled
+// by A, within 1.5% of each; 198, 228 and 262 us at 4, 5 and 6 per CU with
+// the priority).
 double row_cost(int64_t wgs) {
   const int64_t per_cu = (wgs + kCUsPlan - 1) / kCUsPlan;
-  static const double kFew[3] = {68.0, 110.0, 153.0};
+  static const double kFew[3] = {68.0, 103.0, 133.0};
   const double us = per_cu <= 3 ? kFew[per_cu - 1] : 26.6 + 41.9 * double(per_cu);
   return us / 190.0;
 }
 
 // Shape-only plan (no device query).  When L is a multiple of 32: the lean
-// row kernel from three 16-channel workgroups per CU on.  Otherwise, and for
+// row kernel from four 16-channel workgroups per CU on.  Otherwise, and for
 // any other L >= 32: the row kernel (element loads when L is not a multiple
 // of 32), in chunks when there are few tiles, or when its cost model beats
 // the wave-tile kernel's (few 16-channel tiles, as in the 130M layer and the
@@ -108,14 +110,14 @@ Plan make_plan(int64_t B, int64_t D, int64_t N, int64_t L, const mamba_test_knob
   if (row_ok) {
     const int64_t tiles16 = B * ((D + kV4Tile - 1) / kV4Tile);
     const int64_t per_cu = (tiles16 + kCUsPlan - 1) / kCUsPlan;
-    // The lean row kernel from three 16-channel workgroups per CU on (the
-    // count rounded up).  With its issue priority stepped down by progress
-    // (ProgressPrio) it was timed on MI355X at steady clocks against the row
-    // kernel: 135 against 147 us at 3 per CU (the 130M layer), 164 against
-    // 193 us at 4, 199 against 233 us at 5 (the 2.8B layer); at 2 per CU they
-    // tie (111 us), and below that the row kernel's in-wave lookahead wins.
+    // The lean row kernel from four 16-channel workgroups per CU on (the
+    // count rounded up).  Both kernels step their issue priority down by
+    // progress (ProgressPrio); timed on MI355X at steady clocks (B = 4,
+    // L = 2048, lean against row): 3 per CU 136 against 133 us, 3.5 per CU
+    // 162 against 196 us, 4 per CU 164 against 198 us, 5 per CU (the 2.8B
+    // layer) 200 against 228 us, 6 per CU 269 against 262 us.
     // (the lean variant has no ragged form: a forced lean at such an L runs the row kernel)
-    const bool lean = aligned && (kn.scan_kernel == 4 || (kn.scan_kernel == 0 && per_cu >= 3));
+    const bool lean = aligned && (kn.scan_kernel == 4 || (kn.scan_kernel == 0 && per_cu >= 4));
     // With 64 to 384 tiles (1.5 per CU at most) the row kernel cuts L into K
     // chunks so that each of its two passes puts K - 1 workgroups on every
     // tile, about three per CU: the first pass runs chunk 0 in full and

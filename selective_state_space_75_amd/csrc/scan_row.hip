@@ -496,7 +496,10 @@ __device__ __forceinline__ void row_scan(const ScanParams& p, RowLds& s, int64_t
       if (t + 1 >= rep_end) static_cast<float*>(p.y)[row + t + 1] = o1;
     }
   };
+  ProgressPrio prio;    // co-resident workgroups finish together (kernels.hpp)
+  prio.begin();
   for (int64_t ck = 0;; ck += 2) {
+    prio.at(ck, nck);
     chunk(Tag<0>{}, ck);
     if (ck + 1 >= nck) {
       if constexpr (kSum) break;
@@ -821,7 +824,10 @@ scan_row_lean_kernel(ScanParams p) {
 // 1 .. K-1 in full from those.  Both phases put (K - 1) workgroups on every
 // tile, so a sequence with one tile per CU runs three or more per CU.
 template <bool kInBF16, bool kOutBF16>
-__global__ __launch_bounds__(256) void scan_row_kernel(ScanParams p, int phase) {
+// Three workgroups per CU (the LDS allows three): the register budget is held
+// to the 168 VGPRs that three waves per SIMD leave.
+__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(3)))
+scan_row_kernel(ScanParams p, int phase) {
   __shared__ RowLds s;
   const int64_t tiles_d = (p.D + 15) / 16;
   const int64_t bt = p.B * tiles_d;

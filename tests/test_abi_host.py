@@ -358,26 +358,25 @@ def scan_noalloc(**kw):
 
 
 def test_scan_kernel_choice():
-    """The planner's kernel per workload: the lean row kernel from three
-    16-channel workgroups per CU on (the 130M layer has three, the 2.8B layer
-    five) when L % 32 == 0, the row kernel where fewer would leave SIMDs idle
-    or need chunking (the batch-1 long sequence) and, by its cost model,
+    """The planner's kernel per workload: the lean row kernel from four
+    16-channel workgroups per CU on (the 2.8B layer has five) when L % 32 ==
+    0, the row kernel where 16-channel wave tiles would leave SIMDs idle or
+    need chunking (130M layer, batch-1 long sequence) and, by its cost model,
     at L % 32 != 0 (its ragged form), chunking of the wave-tile kernel for
     very few tiles over long L when L % 8 == 0, the general kernel only below
     32 steps.  (Each choice was the fastest kernel in an interleaved timing
     of all of them on MI355X.)"""
     k = _lib.scan_kernel
-    assert k(8, 1536, 16, 2048) == "row_lean"  # 768 tiles: 3 per CU
+    assert k(8, 1536, 16, 2048) == "row"       # 768 tiles: 3 per CU
     assert k(1, 4096, 16, 131072) == "row"     # in 4 chunks
     assert k(4, 5120, 16, 2048) == "row_lean"
     assert k(5, 4096, 16, 2048) == "row_lean"
     assert k(7, 4096, 16, 2048) == "row_lean"
     assert k(4, 4096, 16, 2048) == "row_lean"
     assert k(3, 5120, 16, 2048) == "row_lean"  # 960 tiles: 3.75 per CU, rounded up to 4
-    assert k(3, 4096, 16, 2048) == "row_lean"  # 768 tiles: 3 per CU
+    assert k(3, 4096, 16, 2048) == "row"       # 768 tiles: 3 per CU
     assert k(2, 4096, 16, 2048) == "row"       # 512 tiles: 2 per CU
-    assert k(5, 1536, 16, 2048) == "row"       # 480 tiles: 1.875 per CU, rounded up to 2
-    assert k(3, 3072, 16, 2048) == "row_lean"  # 576 tiles: 2.25 per CU, rounded up to 3
+    assert k(4, 3584, 16, 2048) == "row_lean"  # 896 tiles: 3.5 per CU, rounded up to 4
     assert k(4, 5120, 16, 2040) == "row"       # the lean kernel has no ragged form
     assert k(8, 1536, 16, 2040) == "row"
     assert k(1, 4096, 16, 131072 - 8) == "row"   # in 4 chunks
