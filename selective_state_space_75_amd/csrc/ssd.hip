@@ -518,6 +518,8 @@ __global__ __launch_bounds__(256, 4) void ssd_state_kernel(SsdParams p) {
 
   float after = 0.0f;   // sum of delta over the segment's steps after the current piece
   const int64_t npieces = (p.seg_len + kPiece - 1) / kPiece;
+  ProgressPrio prio;    // one round of workgroups: they finish together (kernels.hpp)
+  prio.begin();
   for (int64_t pi = npieces - 1; pi >= 0; --pi) {
     const int64_t p0 = t_begin + pi * kPiece;
     const int plen = (int)((p.seg_len - pi * kPiece) < kPiece ? (p.seg_len - pi * kPiece) : kPiece);
@@ -595,6 +597,7 @@ __global__ __launch_bounds__(256, 4) void ssd_state_kernel(SsdParams p) {
     unroll_for<0, kAhead>([&](auto jc) { fetch(blk_t(decltype(jc)::kValue), o[decltype(jc)::kValue]); });
     const int ngroups = nblk / kSets;
     for (int gi = 0; gi < ngroups; ++gi) {
+      prio.at((npieces - 1 - pi) * kPiece + gi * kSets * 32, p.seg_len);
       unroll_for<0, kSets>([&](auto jc) {
         constexpr int j = decltype(jc)::kValue;
         const int k = gi * kSets + j;
