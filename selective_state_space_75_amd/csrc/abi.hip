@@ -116,8 +116,10 @@ Plan make_plan(int64_t B, int64_t D, int64_t N, int64_t L, const mamba_test_knob
     // L = 2048, lean against row): 3 per CU 136 against 133 us, 3.5 per CU
     // 162 against 196 us, 4 per CU 164 against 198 us, 5 per CU (the 2.8B
     // layer) 200 against 228 us, 6 per CU 269 against 262 us.
-    // (the lean variant has no ragged form: a forced lean at such an L runs the row kernel)
-    const bool lean = aligned && (kn.scan_kernel == 4 || (kn.scan_kernel == 0 && per_cu >= 4));
+    // (the lean variant has no ragged form: a forced lean at such an L runs the row
+    // kernel; it counts chunks in 32 bits, so it takes L < 2^33 only)
+    const bool lean = aligned && L < (int64_t(1) << 33) &&
+                      (kn.scan_kernel == 4 || (kn.scan_kernel == 0 && per_cu >= 4));
     // With 64 to 384 tiles (1.5 per CU at most) the row kernel cuts L into K
     // chunks so that each of its two passes puts K - 1 workgroups on every
     // tile, about three per CU: the first pass runs chunk 0 in full and

@@ -96,9 +96,13 @@ struct ConvParams {
 struct ProgressPrio {
   int lvl = 0;
   __device__ __forceinline__ void begin() { __builtin_amdgcn_s_setprio(3); }
-  // done of total units of the wave's range are behind it (uniform over the wave)
-  __device__ __forceinline__ void at(int64_t done, int64_t total) {
-    const int l = (int)((8 * done >= 4 * total) + (8 * done >= 6 * total) + (8 * done >= 7 * total));
+  // done of total units of the wave's range are behind it (uniform over the
+  // wave).  With 32-bit unsigned counts (total < 2^29) the compares run on the
+  // scalar unit; 64-bit signed ones need the vector unit.
+  template <typename T>
+  __device__ __forceinline__ void at(T done, T total) {
+    const T a = 8 * done;
+    const int l = a >= 7 * total ? 3 : a >= 6 * total ? 2 : a >= 4 * total ? 1 : 0;   // scalar selects
     if (l != lvl) {
       lvl = l;
       if (l == 1) __builtin_amdgcn_s_setprio(2);

@@ -636,11 +636,13 @@ __device__ __forceinline__ void row_scan_lean(const ScanParams& p, RowLeanLds& s
   const void* s_base = s_arr ? p.Ct : p.Bt;
   const int64_t s_row = (b * N + (s_ok ? sn : 0)) * L;
 
-  const int64_t nck = L / kRCT;
+  // chunk counts in 32 bits (the planner gives this kernel L < 2^33), so that
+  // the loop's uniform compares stay on the scalar unit
+  const int nck = (int)(L / kRCT);
   LeanRaw<kInBF16> raw[2];           // inputs of chunks of each parity, fetched two chunks ahead
-  auto fetch = [&](int64_t ck, LeanRaw<kInBF16>& rr) {
-    const int64_t c = ck < nck ? ck : nck - 1;     // clamp: the prefetch past the end re-reads the last chunk
-    const int64_t at = row + c * kRCT + n;
+  auto fetch = [&](int ck, LeanRaw<kInBF16>& rr) {
+    const int c = ck < nck ? ck : nck - 1;     // clamp: the prefetch past the end re-reads the last chunk
+    const int64_t at = row + (int64_t)c * kRCT + n;
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       rr.u[e] = load1<kInBF16>(p.u, at + 16 * e);
@@ -710,9 +712,9 @@ __device__ __forceinline__ void row_scan_lean(const ScanParams& p, RowLeanLds& s
   prep(raw[0]);
   lds_barrier();
 
-  auto chunk = [&](auto ptag, int64_t ck) {
+  auto chunk = [&](auto ptag, int ck) {
     constexpr int P = decltype(ptag)::kValue;
-    const int64_t t0 = ck * kRCT;
+    const int64_t t0 = (int64_t)ck * kRCT;
     fetch(ck + 2, raw[P]);          // raw[P] held chunk ck, already unpacked and staged
     const float* Bs = &s.bc[P][0][n * kBCRow];
     const float* Cs = &s.bc[P][1][n * kBCRow];
@@ -788,8 +790,8 @@ __device__ __forceinline__ void row_scan_lean(const ScanParams& p, RowLeanLds& s
   };
   ProgressPrio prio;    // co-resident workgroups finish together (kernels.hpp)
   prio.begin();
-  for (int64_t ck = 0;; ck += 2) {
-    prio.at(ck, nck);
+  for (int ck = 0;; ck += 2) {
+    prio.at((uint32_t)ck, (uint32_t)nck);
     chunk(Tag<0>{}, ck);
     if (ck + 1 >= nck) break;
     chunk(Tag<1>{}, ck + 1);
