@@ -404,6 +404,10 @@ def test_scan_kernel_choice():
     with _lib.test_knobs(scan_kernel="row_lean"):
         assert k(8, 1536, 16, 2048) == "row_lean"
         assert k(4, 5120, 16, 2040) == "row"          # the lean variant needs L % 32 == 0
+        # it counts chunks in 32 bits: L < 2^33 only (the planner's own choice
+        # of it implies L < 2^32, since it needs B D >= 12,304)
+        assert k(1, 16, 16, (1 << 33) - 32) == "row_lean"
+        assert k(1, 16, 16, 1 << 33) == "row"
     with _lib.test_knobs(scan_kernel="general"):
         assert k(4, 5120, 16, 2048) == "general"
     assert _lib.lib().mamba_scan_kernel(1, 1, 17, 1) == UNSUP
